@@ -1,0 +1,88 @@
+"""The five synthetic workloads the step is tested and measured on.
+
+Each workload is a set of weight matrices with transformer-layer shapes, a
+block shape, the optimizer's hyper-parameters and the distribution of the
+synthetic gradients. The pages measure on CIFAR ResNets, LM1B and 360M-660M
+language models (podcast "Preconditioned Optimization Without the Full Matrix
+Cost", cue 36; SOAP record); the optimizer step only ever sees gradient
+tensors, so seeded synthetic gradients with the shapes of a GPT-small layer
+set and of a 1B-class decoder layer set stand in for those models.
+
+Where a workload leaves a hyper-parameter open, beta2 = 0.999, eps = 1e-6 and
+lr = 1e-3 (the values given for the single-matrix case) are used. "N(0, x)"
+means standard deviation x.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+GPT_SMALL_LAYER = ((768, 2304), (768, 768), (768, 3072), (3072, 768))
+DECODER_1B_LAYER = ((2048, 6144), (2048, 2048), (2048, 8192), (8192, 2048))
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    shapes: tuple                 # (rows, cols) per matrix, registration order
+    block_rows: int
+    block_cols: int
+    beta2: float = 0.999
+    eps: float = 1e-6
+    lr: float = 1e-3
+    root_every: int = 10
+    steps: int = 10
+    dtype: str = "f32"            # gradient and parameter storage: f32 | bf16
+    grad: str = "iid"             # iid | row_scaled | col_scaled | low_rank
+    grad_std: float = 1.0
+    noise_std: float = 0.0        # low_rank: additive noise
+    rank: int = 0                 # low_rank: rank of the factor product
+    diag_fraction: float = 0.0    # fraction of blocks whose gradient is diagonal
+    newton_max_iters: int = 25
+    newton_tol: float = 1e-6      # <= 0: exactly newton_max_iters iterations
+    newton_scale_mode: int = 1
+    init_std: float = 0.02
+    seed: int = 0
+    notes: str = field(default="", compare=False)
+
+
+def _layers(layer, n):
+    return tuple(s for _ in range(n) for s in layer)
+
+
+WORKLOADS = {
+    "single_64x32": Workload(
+        name="single_64x32", shapes=((64, 32),), block_rows=64, block_cols=32,
+        root_every=1, steps=10, grad="iid", grad_std=1.0, seed=1001,
+        notes="one 64x32 matrix, one block, roots every step"),
+    "gpt_small_b256": Workload(
+        name="gpt_small_b256", shapes=_layers(GPT_SMALL_LAYER, 12), block_rows=256,
+        block_cols=256, root_every=10, steps=100, grad="row_scaled", grad_std=1e-2,
+        seed=1002, notes="12 GPT-small layers, 1296 blocks of 256x256, no tails"),
+    "gpt_small_b512_lowrank": Workload(
+        name="gpt_small_b512_lowrank", shapes=_layers(GPT_SMALL_LAYER, 12), block_rows=512,
+        block_cols=512, eps=1e-12, root_every=10, steps=100, grad="low_rank", rank=16,
+        grad_std=0.05, noise_std=1e-3, seed=1003,
+        notes="12 GPT-small layers, 456 blocks of 512x512 (252 tails), ill-conditioned"),
+    "decoder_1b_b1024_f32": Workload(
+        name="decoder_1b_b1024_f32", shapes=_layers(DECODER_1B_LAYER, 24), block_rows=1024,
+        block_cols=1024, root_every=10, steps=50, grad="col_scaled", grad_std=1e-2,
+        seed=1004, notes="24 1B-class decoder layers, 1152 blocks of 1024x1024, fp32"),
+    "decoder_1b_b1024_bf16": Workload(
+        name="decoder_1b_b1024_bf16", shapes=_layers(DECODER_1B_LAYER, 24), block_rows=1024,
+        block_cols=1024, root_every=10, steps=50, dtype="bf16", grad="col_scaled",
+        grad_std=1e-2, diag_fraction=0.1, newton_max_iters=10, newton_tol=0.0, seed=1005,
+        notes="as decoder_1b_b1024_f32 with bf16 gradients and parameters, 10 fixed "
+              "Newton iterations, 10% diagonal blocks"),
+}
+
+# Short aliases in the order the workloads are listed.
+ORDER = ("single_64x32", "gpt_small_b256", "gpt_small_b512_lowrank",
+         "decoder_1b_b1024_f32", "decoder_1b_b1024_bf16")
+
+
+def get(name) -> Workload:
+    return WORKLOADS[name]
+
+
+def n_blocks(w: Workload) -> int:
+    return sum(-(-r // w.block_rows) * -(-c // w.block_cols) for r, c in w.shapes)

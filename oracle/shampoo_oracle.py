@@ -1,0 +1,349 @@
+"""Oracle for the blocked Shampoo step: plain, slow, fp64, CPU only.
+
+TEST INFRASTRUCTURE. Only the test suite, the package's smoke check and the
+CPU-baseline leg of the benchmark may import this module. The product path
+(the HIP library and its Python binding) never calls it, and this module
+imports nothing from the product path. It shares no code with the kernels.
+
+What it computes, and where the pages define it:
+
+* Matrix Shampoo ("Shampoo optimizer" page, section "Key Components" and the
+  simplified matrix-case loop under it; podcast "Preconditioned Optimization
+  Without the Full Matrix Cost", cue 20): for a weight block W (m x n) with
+  gradient G, keep a left statistic L (m x m) and a right statistic R (n x n),
+  both started at eps * identity, accumulate G G^T into L and G^T G into R,
+  and move W by -lr * L^(-1/4) G R^(-1/4).
+* The statistics are an exponential moving average with weight beta2 on the
+  old value and stat_scale (default 1 - beta2) on the new outer product, the
+  form the SOAP record sweeps as beta_shampoo. beta2 = stat_scale = 1 gives
+  the plain running sum of the "Shampoo optimizer" loop.
+* The quarter power on each side (podcast cue 22) makes the two-sided product
+  equal to the Kronecker preconditioner (L kron R)^(-1/4) applied to the
+  row-major flattening of G. The oracle never uses that identity; the tests
+  use it as an independent check.
+* Roots are recomputed only every k steps and reused in between (podcast
+  cue 28). Reading taken: the first step always computes roots, so refresh
+  happens at steps t = 1, 1 + k, 1 + 2k, ...
+* Gradients are cut into blocks that are stacked into a batch (DASH page,
+  abstract). Reading taken: blocks of block_rows x block_cols in row-major
+  block order inside a matrix, matrices in registration order; a tail block
+  keeps its real (smaller) extent here, since zero padding decouples exactly.
+
+Roots are the plain definition: the principal inverse p-th root of a
+symmetric positive definite matrix from its symmetric eigendecomposition
+(numpy.linalg.eigh, i.e. LAPACK). The GPU reaches the same matrix by an
+iteration; the oracle also carries that iteration, written from its
+published definition (coupled Newton for the inverse p-th root, Guo and
+Higham, SIAM J. Matrix Anal. Appl. 28(3), 2006), for the fixed-iteration
+workload and for tests of the iteration itself.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "BlockInfo",
+    "block_table",
+    "pack_blocks",
+    "unpack_blocks",
+    "update_statistics",
+    "inverse_root_eigh",
+    "newton_scale",
+    "inverse_root_coupled_newton",
+    "precondition",
+    "round_to_bf16",
+    "is_refresh_step",
+    "ShampooOracle",
+]
+
+
+# ---------------------------------------------------------------------------
+# Block map (DASH page, abstract: preconditioner blocks stacked into a batch)
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class BlockInfo:
+    """One block of one registered matrix.
+
+    id:     position in the stacked batch.
+    mat:    index of the matrix in registration order.
+    bi, bj: block row / block column inside that matrix.
+    r0, c0: first row / column of the block in the matrix.
+    m, n:   real extent of the block (smaller than the block shape for tails).
+    """
+
+    id: int
+    mat: int
+    bi: int
+    bj: int
+    r0: int
+    c0: int
+    m: int
+    n: int
+
+
+def block_table(shapes, block_rows, block_cols):
+    """Enumerate the blocks of every matrix.
+
+    Matrices keep registration order; inside a matrix, blocks go in row-major
+    block order; a tail block keeps its real extent.
+    """
+    table = []
+    for mat, (rows, cols) in enumerate(shapes):
+        nbr = -(-rows // block_rows)
+        nbc = -(-cols // block_cols)
+        for bi in range(nbr):
+            for bj in range(nbc):
+                r0, c0 = bi * block_rows, bj * block_cols
+                table.append(BlockInfo(len(table), mat, bi, bj, r0, c0,
+                                       min(block_rows, rows - r0),
+                                       min(block_cols, cols - c0)))
+    return table
+
+
+def pack_blocks(mats, table, block_rows, block_cols):
+    """Stack every block into a [B, block_rows, block_cols] array.
+
+    Values are copied unchanged (same dtype as the inputs); entries outside
+    a tail block's real extent are +0.0.
+    """
+    dtype = mats[0].dtype if mats else np.float32
+    out = np.zeros((len(table), block_rows, block_cols), dtype=dtype)
+    for b in table:
+        out[b.id, :b.m, :b.n] = mats[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n]
+    return out
+
+
+def unpack_blocks(packed, table, shapes):
+    """Inverse of pack_blocks: write each block's real extent back."""
+    mats = [np.zeros(s, dtype=packed.dtype) for s in shapes]
+    for b in table:
+        mats[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n] = packed[b.id, :b.m, :b.n]
+    return mats
+
+
+# ---------------------------------------------------------------------------
+# Statistics ("Shampoo optimizer" page, matrix-case loop; podcast cue 20;
+# EMA weight as in the SOAP record's beta_shampoo sweep)
+# ---------------------------------------------------------------------------
+def update_statistics(L, R, G, beta2, stat_scale):
+    """L <- beta2 L + stat_scale G G^T ;  R <- beta2 R + stat_scale G^T G."""
+    G = np.asarray(G, dtype=np.float64)
+    L_new = beta2 * L + stat_scale * (G @ G.T)
+    R_new = beta2 * R + stat_scale * (G.T @ G)
+    return L_new, R_new
+
+
+# ---------------------------------------------------------------------------
+# Inverse roots
+# ---------------------------------------------------------------------------
+def inverse_root_eigh(A, p=4):
+    """Principal inverse p-th root of a symmetric positive definite matrix.
+
+    A = Q diag(lam) Q^T  =>  A^(-1/p) = Q diag(lam^(-1/p)) Q^T.  A matrix
+    that is not positive definite is an error, never silently clamped.
+    """
+    A = np.asarray(A, dtype=np.float64)
+    lam, Q = np.linalg.eigh(A)
+    if not lam.min() > 0.0:
+        raise np.linalg.LinAlgError(
+            f"inverse root of a matrix that is not positive definite "
+            f"(smallest eigenvalue {lam.min():.3e})")
+    return (Q * lam ** (-1.0 / p)) @ Q.T
+
+
+def newton_scale(A, p=4, mode=1):
+    """Norm used to scale A before the coupled Newton iteration.
+
+    mode 0: s = ||A||_F, which puts the spectrum of A/s in (0, 1].
+    mode 1: s = min(||A||_F, ||A||_inf) * 2 / (p + 1), which puts the
+            spectrum of A/s in (0, (p + 1) / 2]; both norms bound the
+            largest eigenvalue of a symmetric matrix.
+    The DASH page (abstract) stresses that this scaling decides how fast
+    Shampoo's root solver converges; the limit reached does not depend on it.
+    """
+    A = np.asarray(A, dtype=np.float64)
+    fro = math.sqrt(float(np.sum(A * A)))
+    if mode == 0:
+        return fro
+    if mode == 1:
+        inf = float(np.max(np.sum(np.abs(A), axis=1)))
+        return min(fro, inf) * 2.0 / (p + 1)
+    raise ValueError(f"unknown scale mode {mode}")
+
+
+@dataclass
+class NewtonInfo:
+    iters: int
+    residuals: list = field(default_factory=list)
+    status: str = "capped"  # converged | stalled | diverged | capped
+
+
+def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
+                                divergence_factor=1.2):
+    """Coupled Newton iteration for A^(-1/p) (Guo and Higham 2006).
+
+    Start from M = A / s and X = s^(-1/p) I. Each iteration forms
+    T = ((p + 1) I - M) / p, then X <- X T and M <- T^p M; X tends to
+    A^(-1/p) while M tends to I. The spectrum of M must start in (0, p + 1).
+
+    Stopping: after each iteration the residual r = ||M - I||_F / sqrt(n) is
+    compared with tol (stop, keep this X), with the previous residual (no
+    decrease: stop, keep the previous X) and with divergence_factor times
+    the previous residual or a non-finite value (diverged: keep the previous
+    X). tol <= 0 runs exactly max_iters iterations, with no early stop.
+    """
+    A = np.asarray(A, dtype=np.float64)
+    n = A.shape[0]
+    eye = np.eye(n)
+    s = newton_scale(A, p, scale_mode)
+    M = A / s
+    X = s ** (-1.0 / p) * eye
+    info = NewtonInfo(0)
+    r_prev = math.inf
+    for k in range(max_iters):
+        T = ((p + 1) * eye - M) / p
+        X_new = X @ T
+        M_new = np.linalg.matrix_power(T, p) @ M
+        r = float(np.sqrt(np.sum((M_new - eye) ** 2)) / math.sqrt(n))
+        info.residuals.append(r)
+        if tol > 0.0:
+            if not math.isfinite(r) or r > divergence_factor * r_prev:
+                info.status = "diverged"
+                break
+            if r >= r_prev:
+                info.status = "stalled"
+                break
+        X, M, r_prev = X_new, M_new, r
+        info.iters = k + 1
+        if tol > 0.0 and r <= tol:
+            info.status = "converged"
+            break
+    return X, info
+
+
+# ---------------------------------------------------------------------------
+# Preconditioned update ("Shampoo optimizer" page, last line of the loop;
+# podcast cue 20)
+# ---------------------------------------------------------------------------
+def precondition(XL, G, XR):
+    """U = L^(-1/4) G R^(-1/4), given the two roots."""
+    return np.asarray(XL, np.float64) @ np.asarray(G, np.float64) @ np.asarray(XR, np.float64)
+
+
+def round_to_bf16(x):
+    """Round fp64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits: write x = f * 2^e with f in [0.5, 1),
+    round f * 256 to an integer with ties to even, scale back. Finite normal
+    range only (the parameters here are far from under- and overflow).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    f, e = np.frexp(x)
+    return np.ldexp(np.rint(f * 256.0) / 256.0, e)
+
+
+def is_refresh_step(t, root_every):
+    """Roots are recomputed at t = 1, 1 + k, 1 + 2k, ... (k = root_every)."""
+    return root_every > 0 and (t - 1) % root_every == 0
+
+
+# ---------------------------------------------------------------------------
+# The whole step over a set of matrices
+# ---------------------------------------------------------------------------
+@dataclass
+class _BlockState:
+    L: np.ndarray
+    R: np.ndarray
+    XL: np.ndarray | None = None
+    XR: np.ndarray | None = None
+    newton_L: NewtonInfo | None = None
+    newton_R: NewtonInfo | None = None
+
+
+class ShampooOracle:
+    """Blocked Shampoo over a list of matrices, block by block, in fp64.
+
+    shapes:       (rows, cols) of each matrix, in registration order.
+    block_rows, block_cols: the block shape.
+    beta2, stat_scale: EMA weights of the statistics (stat_scale None means
+                  1 - beta2).
+    eps:          L and R start at eps * I.
+    lr:           step size.
+    root_every:   k of the refresh schedule (0: only explicit refresh).
+    blocks:       optional subset of block ids to track (blocks are
+                  independent, so a sample can be run alone).
+    root_method:  "eigh" (the definition) or "newton" (the iteration, with
+                  newton_iters / newton_tol / newton_scale_mode).
+    param_bf16:   parameters are stored in bfloat16 after every update.
+    """
+
+    def __init__(self, shapes, block_rows, block_cols, beta2, eps, lr, root_every,
+                 stat_scale=None, blocks=None, root_method="eigh", newton_iters=25,
+                 newton_tol=0.0, newton_scale_mode=1, param_bf16=False, p=4):
+        self.shapes = [tuple(s) for s in shapes]
+        self.table = block_table(self.shapes, block_rows, block_cols)
+        self.ids = list(range(len(self.table))) if blocks is None else sorted(set(blocks))
+        self.beta2 = float(beta2)
+        self.stat_scale = 1.0 - self.beta2 if stat_scale is None else float(stat_scale)
+        self.eps = float(eps)
+        self.lr = float(lr)
+        self.root_every = int(root_every)
+        self.root_method = root_method
+        self.newton_iters = newton_iters
+        self.newton_tol = newton_tol
+        self.newton_scale_mode = newton_scale_mode
+        self.param_bf16 = param_bf16
+        self.p = p
+        self.t = 0
+        self.state = {}
+        for i in self.ids:
+            b = self.table[i]
+            self.state[i] = _BlockState(self.eps * np.eye(b.m), self.eps * np.eye(b.n))
+
+    def _root(self, A):
+        if self.root_method == "eigh":
+            return inverse_root_eigh(A, self.p), None
+        if self.root_method == "newton":
+            return inverse_root_coupled_newton(A, self.p, self.newton_iters, self.newton_tol,
+                                               self.newton_scale_mode)
+        raise ValueError(self.root_method)
+
+    def refresh_roots(self):
+        for i in self.ids:
+            st = self.state[i]
+            st.XL, st.newton_L = self._root(st.L)
+            st.XR, st.newton_R = self._root(st.R)
+
+    def step(self, grads, params, force_refresh=False, auto_refresh=True):
+        """One step. grads/params are lists of full matrices (any float dtype).
+
+        Returns (new params as fp64 arrays, {block id: U}). Only tracked
+        blocks of the params change.
+        """
+        self.t += 1
+        new_params = [np.array(p, dtype=np.float64) for p in params]
+        blocks_g = {}
+        for i in self.ids:
+            b = self.table[i]
+            G = np.asarray(grads[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n], dtype=np.float64)
+            blocks_g[i] = G
+            st = self.state[i]
+            st.L, st.R = update_statistics(st.L, st.R, G, self.beta2, self.stat_scale)
+        if force_refresh or (auto_refresh and is_refresh_step(self.t, self.root_every)):
+            self.refresh_roots()
+        updates = {}
+        for i in self.ids:
+            b = self.table[i]
+            st = self.state[i]
+            if st.XL is None:
+                raise RuntimeError("step before any root refresh")
+            U = precondition(st.XL, blocks_g[i], st.XR)
+            updates[i] = U
+            W = new_params[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n] - self.lr * U
+            if self.param_bf16:
+                W = round_to_bf16(W)
+            new_params[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n] = W
+        return new_params, updates

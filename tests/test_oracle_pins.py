@@ -1,0 +1,410 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix.
+
+None of these compare the oracle with itself: each check uses a closed form,
+an identity, an independent library routine (SVD, Kronecker eigendecomposition,
+torch's bfloat16 cast) or brute force on tiny inputs. Every part of the
+oracle is covered by at least one check that a dropped term, a wrong sign or
+index, or a transposed operand would fail (see test_planted_mistakes).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (ShampooOracle, block_table, inverse_root_coupled_newton, inverse_root_eigh,
+                    is_refresh_step, newton_scale, pack_blocks, precondition, round_to_bf16,
+                    unpack_blocks, update_statistics)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rel(a, b):
+    return float(np.linalg.norm(np.asarray(a) - np.asarray(b)) / np.linalg.norm(np.asarray(b)))
+
+
+def run_oracle(G_steps, W0, beta2, eps, lr, root_every=1, stat_scale=None, **kw):
+    m, n = np.asarray(G_steps[0]).shape
+    o = ShampooOracle([(m, n)], m, n, beta2, eps, lr, root_every, stat_scale=stat_scale, **kw)
+    W = [np.asarray(W0, dtype=np.float64)]
+    Us = []
+    for G in G_steps:
+        W, U = o.step([np.asarray(G, dtype=np.float64)], W)
+        Us.append(U[0])
+    return o, W[0], Us
+
+
+# ---------------------------------------------------------------------------
+# The 2x2 example of the "Shampoo optimizer" page (no numbers printed there)
+# ---------------------------------------------------------------------------
+def test_two_by_two_example_all_ones():
+    case = json.load(open(os.path.join(GOLDEN, "two_by_two.json")))["cases"][0]
+    G = np.array(case["G"])
+    W0 = np.array(case["W0"])
+    b2, eps, lr = case["beta2"], case["eps"], case["lr"]
+    _, W1, Us = run_oracle([G], W0, b2, eps, lr)
+    U_cf = G / math.sqrt(b2 * eps + 4 * (1 - b2))
+    assert rel(Us[0], U_cf) < 1e-12
+    assert rel(W1, W0 - lr * U_cf) < 1e-14
+
+
+def test_two_by_two_example_diagonal_sum_form():
+    case = json.load(open(os.path.join(GOLDEN, "two_by_two.json")))["cases"][1]
+    Gs = [np.array(g) for g in case["G_steps"]]
+    eps = case["eps"]
+    _, _, Us = run_oracle(Gs, np.zeros((2, 2)), case["beta2"], eps, case["lr"],
+                          stat_scale=case["stat_scale"])
+    acc = np.full(2, eps)
+    for G, U in zip(Gs, Us):
+        g = np.diag(G)
+        acc = acc + g * g
+        assert np.allclose(U, np.diag(g / np.sqrt(acc)), rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Diagonal gradients: every root is elementwise (closed form)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n", [(5, 5), (6, 3), (3, 7)])
+def test_diagonal_gradients_closed_form(m, n):
+    rng = np.random.default_rng(3)
+    b2, eps, lr, k = 0.9, 1e-3, 0.1, 1
+    d = min(m, n)
+    Gs = []
+    for _ in range(6):
+        G = np.zeros((m, n))
+        G[np.arange(d), np.arange(d)] = rng.standard_normal(d)
+        Gs.append(G)
+    _, _, Us = run_oracle(Gs, np.zeros((m, n)), b2, eps, lr, root_every=k)
+    ell = np.full(d, eps)
+    for G, U in zip(Gs, Us):
+        g = np.diag(G)[:d] if m == n else G[np.arange(d), np.arange(d)]
+        ell = b2 * ell + (1 - b2) * g * g
+        expect = np.zeros((m, n))
+        expect[np.arange(d), np.arange(d)] = g / np.sqrt(ell)
+        assert np.allclose(U, expect, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Kronecker brute force (podcast cue 22): vec_r(U) = (L kron R)^(-1/4) vec_r(G)
+# ---------------------------------------------------------------------------
+def kron_update(L, R, G):
+    K = np.kron(L, R)
+    lam, Q = np.linalg.eigh(K)
+    return ((Q * lam ** -0.25) @ Q.T @ G.reshape(-1)).reshape(G.shape)
+
+
+@pytest.mark.parametrize("m,n", [(1, 1), (2, 3), (4, 5), (6, 6), (7, 2)])
+def test_kronecker_bruteforce_tiny(m, n):
+    rng = np.random.default_rng(m * 10 + n)
+    b2, eps = 0.95, 1e-2
+    Gs = [rng.standard_normal((m, n)) for _ in range(4)]
+    o, _, Us = run_oracle(Gs, np.zeros((m, n)), b2, eps, 1e-3, root_every=1)
+    L = eps * np.eye(m)
+    R = eps * np.eye(n)
+    for G, U in zip(Gs, Us):
+        L = b2 * L + (1 - b2) * G @ G.T
+        R = b2 * R + (1 - b2) * G.T @ G
+        assert rel(U, kron_update(L, R, G)) < 1e-10
+
+
+def test_kronecker_bruteforce_single_64x32():
+    """The whole single-matrix workload (64x32, 10 steps, roots every step)."""
+    rng = np.random.default_rng(1001)
+    Gs = [rng.standard_normal((64, 32)) for _ in range(10)]
+    b2, eps = 0.999, 1e-6
+    _, _, Us = run_oracle(Gs, np.zeros((64, 32)), b2, eps, 1e-3, root_every=1)
+    L, R = eps * np.eye(64), eps * np.eye(32)
+    for t, (G, U) in enumerate(zip(Gs, Us)):
+        L = b2 * L + (1 - b2) * G @ G.T
+        R = b2 * R + (1 - b2) * G.T @ G
+        if t in (0, 1, 9):
+            assert rel(U, kron_update(L, R, G)) < 1e-9
+
+
+# ---------------------------------------------------------------------------
+# First step from the SVD (independent LAPACK routine)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n", [(8, 8), (9, 4), (3, 10)])
+def test_first_step_svd_closed_form(m, n):
+    rng = np.random.default_rng(7)
+    G = rng.standard_normal((m, n))
+    b2, eps = 0.999, 1e-6
+    _, _, Us = run_oracle([G], np.zeros((m, n)), b2, eps, 1e-3)
+    P, s, Qt = np.linalg.svd(G, full_matrices=False)
+    U_cf = (P * (s / np.sqrt(b2 * eps + (1 - b2) * s * s))) @ Qt
+    assert rel(Us[0], U_cf) < 1e-11
+
+
+def test_shared_singular_vectors_multistep():
+    rng = np.random.default_rng(11)
+    n = 6
+    P, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    Q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    b2, eps = 0.9, 1e-4
+    sv = [np.abs(rng.standard_normal(n)) + 0.1 for _ in range(5)]
+    Gs = [(P * s) @ Q.T for s in sv]
+    _, _, Us = run_oracle(Gs, np.zeros((n, n)), b2, eps, 1e-3, root_every=1)
+    ell = np.full(n, eps)
+    for s, U in zip(sv, Us):
+        ell = b2 * ell + (1 - b2) * s * s
+        assert rel(U, (P * (s / np.sqrt(ell))) @ Q.T) < 1e-11
+
+
+# ---------------------------------------------------------------------------
+# Statistics: the recursion equals the closed sum
+# ---------------------------------------------------------------------------
+def test_statistics_closed_sum():
+    rng = np.random.default_rng(5)
+    m, n, T = 5, 3, 7
+    b2, eps, gam = 0.8, 0.3, 0.45
+    L, R = eps * np.eye(m), eps * np.eye(n)
+    Gs = [rng.standard_normal((m, n)) for _ in range(T)]
+    for G in Gs:
+        L, R = update_statistics(L, R, G, b2, gam)
+    L_cf = b2 ** T * eps * np.eye(m) + gam * sum(b2 ** (T - 1 - s) * Gs[s] @ Gs[s].T for s in range(T))
+    R_cf = b2 ** T * eps * np.eye(n) + gam * sum(b2 ** (T - 1 - s) * Gs[s].T @ Gs[s] for s in range(T))
+    assert rel(L, L_cf) < 1e-14 and rel(R, R_cf) < 1e-14
+
+
+def test_scalar_one_by_one():
+    b2, eps, lr = 0.99, 1e-5, 0.5
+    gs = [0.3, -1.2, 2.0, 0.0, -0.7]
+    _, _, Us = run_oracle([[[g]] for g in gs], [[0.0]], b2, eps, lr)
+    for t, (g, U) in enumerate(zip(gs, Us), start=1):
+        ell = b2 ** t * eps + (1 - b2) * sum(b2 ** (t - s) * gs[s - 1] ** 2 for s in range(1, t + 1))
+        assert abs(U[0, 0] - g * ell ** -0.5) <= 1e-12 * max(1.0, abs(g * ell ** -0.5))
+
+
+# ---------------------------------------------------------------------------
+# Invariants: symmetric PSD statistics, X^4 A = I
+# ---------------------------------------------------------------------------
+def test_invariants():
+    rng = np.random.default_rng(9)
+    o = ShampooOracle([(12, 20), (20, 12)], 8, 8, 0.999, 1e-6, 1e-3, 2)
+    W = [np.zeros((12, 20)), np.zeros((20, 12))]
+    for _ in range(3):
+        W, _ = o.step([rng.standard_normal((12, 20)), rng.standard_normal((20, 12))], W)
+    for st in o.state.values():
+        for A, X in ((st.L, st.XL), (st.R, st.XR)):
+            assert np.array_equal(A, A.T)
+            assert np.linalg.eigvalsh(A).min() > 0
+            X4 = np.linalg.matrix_power(X, 4)
+            assert np.linalg.norm(X4 @ A - np.eye(A.shape[0])) / math.sqrt(A.shape[0]) < 1e-10
+
+
+def test_inverse_root_rejects_indefinite():
+    with pytest.raises(np.linalg.LinAlgError):
+        inverse_root_eigh(np.diag([1.0, -1e-3]))
+    with pytest.raises(np.linalg.LinAlgError):
+        inverse_root_eigh(np.zeros((3, 3)))
+
+
+def test_inverse_root_2x2_analytic():
+    a, b, c = 3.0, 1.25, 2.0
+    A = np.array([[a, b], [b, c]])
+    disc = math.sqrt(((a - c) / 2) ** 2 + b * b)
+    lam = np.array([(a + c) / 2 - disc, (a + c) / 2 + disc])
+    # eigenvector of the larger eigenvalue, by hand
+    v = np.array([b, lam[1] - a])
+    v /= np.linalg.norm(v)
+    w = np.array([-v[1], v[0]])
+    X_cf = lam[1] ** -0.25 * np.outer(v, v) + lam[0] ** -0.25 * np.outer(w, w)
+    assert rel(inverse_root_eigh(A), X_cf) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# Refresh schedule (podcast cue 28: roots reused between refreshes)
+# ---------------------------------------------------------------------------
+def test_refresh_schedule():
+    assert [t for t in range(1, 32) if is_refresh_step(t, 10)] == [1, 11, 21, 31]
+    assert all(is_refresh_step(t, 1) for t in range(1, 5))
+    assert not any(is_refresh_step(t, 0) for t in range(1, 5))
+
+
+def test_stale_roots_between_refreshes():
+    """With G_t = c_t G0 and roots frozen after step 1, U_t = (c_t / c_1) U_1;
+    at the refresh step the SVD closed form with accumulated scales holds."""
+    rng = np.random.default_rng(21)
+    n = 5
+    G0 = rng.standard_normal((n, n))
+    cs = [1.0, 0.5, -2.0, 3.0, 0.25]
+    b2, eps, k = 0.9, 1e-3, 3
+    _, _, Us = run_oracle([c * G0 for c in cs], np.zeros((n, n)), b2, eps, 1e-3, root_every=k)
+    for t in (1, 2):
+        assert rel(Us[t], cs[t] * Us[0]) < 1e-13
+    # step 4 (t index 3) refreshes: L_4 = b2^4 eps I + (1-b2) S P Sigma^2 P^T
+    P, s, Qt = np.linalg.svd(G0)
+    S = sum(b2 ** (3 - j) * cs[j] ** 2 for j in range(4))
+    U_cf = (P * (cs[3] * s / np.sqrt(b2 ** 4 * eps + (1 - b2) * S * s * s))) @ Qt
+    assert rel(Us[3], U_cf) < 1e-11
+    # step 5 is stale again: scaled copy of step 4
+    assert rel(Us[4], cs[4] / cs[3] * Us[3]) < 1e-13
+
+
+def test_update_sign_and_step_size():
+    rng = np.random.default_rng(4)
+    G = rng.standard_normal((4, 3))
+    W0 = rng.standard_normal((4, 3))
+    _, W1a, Ua = run_oracle([G], W0, 0.9, 1e-3, 0.0)
+    assert np.array_equal(W1a, W0)
+    _, W1, U = run_oracle([G], W0, 0.9, 1e-3, 0.25)
+    assert rel(W1, W0 - 0.25 * U[0]) < 1e-15
+    # the update points along the gradient (preconditioner is positive definite)
+    assert float(np.sum(U[0] * G)) > 0
+
+
+# ---------------------------------------------------------------------------
+# Block map: row-major blocks, zero-padded tails, exact round trip
+# ---------------------------------------------------------------------------
+def test_block_counts_of_the_workloads():
+    gpt = [(768, 2304), (768, 768), (768, 3072), (3072, 768)] * 12
+    dec = [(2048, 6144), (2048, 2048), (2048, 8192), (8192, 2048)] * 24
+    assert len(block_table([(64, 32)], 64, 32)) == 1
+    assert len(block_table(gpt, 256, 256)) == 1296
+    t512 = block_table(gpt, 512, 512)
+    assert len(t512) == 456
+    assert sum(1 for b in t512 if (b.m, b.n) != (512, 512)) == 252
+    assert len(block_table(dec, 1024, 1024)) == 1152
+
+
+def test_pack_matches_elementwise_enumeration():
+    rng = np.random.default_rng(2)
+    shapes = [(7, 5), (3, 9), (8, 8)]
+    mats = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    br, bc = 4, 3
+    table = block_table(shapes, br, bc)
+    P = pack_blocks(mats, table, br, bc)
+    # independent enumeration: walk every element of the packed array
+    base = 0
+    for mat, (rows, cols) in enumerate(shapes):
+        nbr, nbc = -(-rows // br), -(-cols // bc)
+        for idx in range(nbr * nbc * br * bc):
+            blk, rem = divmod(idx, br * bc)
+            r, c = divmod(rem, bc)
+            bi, bj = divmod(blk, nbc)
+            gr, gc = bi * br + r, bj * bc + c
+            v = P[base + blk, r, c]
+            if gr < rows and gc < cols:
+                assert v == mats[mat][gr, gc]
+            else:
+                assert v == 0.0 and not np.signbit(v)
+        base += nbr * nbc
+    assert base == P.shape[0]
+    back = unpack_blocks(P, table, shapes)
+    for a, b in zip(mats, back):
+        assert np.array_equal(a, b)
+
+
+def test_tail_blocks_equal_padded_blocks():
+    """Zero padding decouples exactly: the padded block's update restricted to
+    the real extent equals the update of the real block."""
+    rng = np.random.default_rng(8)
+    m, n, bm, bn = 5, 3, 8, 4
+    Gs = [rng.standard_normal((m, n)) for _ in range(3)]
+    _, _, Us = run_oracle(Gs, np.zeros((m, n)), 0.9, 1e-2, 1e-3)
+    Gp = [np.pad(G, ((0, bm - m), (0, bn - n))) for G in Gs]
+    _, _, Up = run_oracle(Gp, np.zeros((bm, bn)), 0.9, 1e-2, 1e-3)
+    for U, V in zip(Us, Up):
+        assert rel(V[:m, :n], U) < 1e-12
+        assert np.abs(V[m:, :]).max() == 0 and np.abs(V[:, n:]).max() == 0
+
+
+# ---------------------------------------------------------------------------
+# Coupled Newton iteration (the GPU's method) against the definition
+# ---------------------------------------------------------------------------
+def spd(n, cond, rng):
+    Q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    lam = np.geomspace(1.0, 1.0 / cond, n)
+    return (Q * lam) @ Q.T, Q, lam
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_newton_converges_to_eigh(mode):
+    rng = np.random.default_rng(13)
+    A, _, _ = spd(24, 1e3, rng)
+    A *= 7.5
+    X, info = inverse_root_coupled_newton(A, 4, max_iters=60, tol=1e-13, scale_mode=mode)
+    assert info.status in ("converged", "stalled")
+    assert rel(X, inverse_root_eigh(A)) < 1e-11
+
+
+def test_newton_orthogonal_similarity():
+    """Newton commutes with an orthogonal change of basis: on Q diag(a) Q^T it
+    returns Q diag(x) Q^T with x from the diagonal matrix (fixed 5 iterations,
+    far from converged, so this checks the iteration itself)."""
+    rng = np.random.default_rng(17)
+    A, Q, lam = spd(6, 50.0, rng)
+    Xa, _ = inverse_root_coupled_newton(A, 4, max_iters=5, tol=0.0, scale_mode=0)
+    Xd, _ = inverse_root_coupled_newton(np.diag(lam), 4, max_iters=5, tol=0.0, scale_mode=0)
+    assert np.allclose(Xd, np.diag(np.diag(Xd)), atol=0)
+    assert rel(Xa, Q @ Xd @ Q.T) < 1e-12
+
+
+def test_newton_scalar_fixed_point_and_monotone():
+    """On a 1x1 matrix the iteration is the scalar map x -> x (5 - m)/4,
+    m -> m ((5 - m)/4)^4, whose fixed point is a^(-1/4) and whose residual
+    |m - 1| decreases every step for m in (0, 5)."""
+    a = 3.7e-4
+    # scale mode 1 maps a 1x1 matrix to m0 = 5/2, away from the fixed point
+    X, info = inverse_root_coupled_newton(np.array([[a]]), 4, max_iters=30, tol=0.0, scale_mode=1)
+    r = info.residuals
+    assert r[0] == pytest.approx(abs(2.5 * (2.5 / 4) ** 4 - 1), rel=1e-14)
+    assert all(r2 < r1 for r1, r2 in zip(r, r[1:]) if r1 > 1e-15)
+    assert abs(X[0, 0] - a ** -0.25) < 1e-12 * a ** -0.25
+
+
+def test_newton_scale_bounds_spectrum():
+    rng = np.random.default_rng(19)
+    A, _, lam = spd(10, 20.0, rng)
+    A *= 3.0
+    lam = lam * 3.0
+    # ||A||_F^2 = sum of squared eigenvalues (symmetric A)
+    assert abs(newton_scale(A, 4, 0) ** 2 - float(np.sum(lam ** 2))) < 1e-12 * float(np.sum(lam ** 2))
+    s1 = newton_scale(A, 4, 1)
+    assert lam.max() / s1 <= 2.5 + 1e-12
+    D = np.diag([4.0, 1.0, 0.5])
+    assert abs(newton_scale(D, 4, 1) - 4.0 * 2 / 5) < 1e-15  # inf-norm 4 < fro
+    with pytest.raises(ValueError):
+        newton_scale(D, 4, 7)
+
+
+def test_newton_guard_keeps_finite_iterate():
+    """An indefinite input makes the iteration blow up; with a tolerance the
+    guard stops and keeps the last finite iterate."""
+    A = np.diag([1.0, 0.5, -0.4])
+    X, info = inverse_root_coupled_newton(A, 4, max_iters=60, tol=1e-12, scale_mode=0)
+    assert np.all(np.isfinite(X))
+    assert info.status in ("diverged", "stalled")
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 rounding against torch's cast (round to nearest, ties to even)
+# ---------------------------------------------------------------------------
+def test_round_to_bf16_matches_torch():
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal(20000) * 0.05).astype(np.float32).astype(np.float64)
+    # add exact ties: values halfway between two bf16 numbers
+    ties = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(0.5 + 2 ** -9), 0.02 + 0.0])
+    x = np.concatenate([x, ties.astype(np.float32).astype(np.float64)])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(round_to_bf16(x), ref)
+    assert round_to_bf16(np.array([1.0 + 2 ** -8]))[0] == 1.0           # tie to even
+    assert round_to_bf16(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
+
+
+def test_bf16_params_are_rounded_after_each_step():
+    rng = np.random.default_rng(29)
+    G = rng.standard_normal((4, 4))
+    W0 = round_to_bf16(rng.standard_normal((4, 4)) * 0.02)
+    _, W1, U = run_oracle([G], W0, 0.999, 1e-6, 1e-3, param_bf16=True)
+    assert np.array_equal(W1, round_to_bf16(W0 - 1e-3 * U[0]))
+    assert np.array_equal(round_to_bf16(W1), W1)
+
+
+def test_precondition_is_left_then_right():
+    XL = np.array([[2.0, 0.0], [0.0, 3.0]])
+    XR = np.array([[5.0, 0.0, 0.0], [0.0, 7.0, 0.0], [0.0, 0.0, 11.0]])
+    G = np.ones((2, 3))
+    assert np.array_equal(precondition(XL, G, XR), np.outer([2.0, 3.0], [5.0, 7.0, 11.0]))
