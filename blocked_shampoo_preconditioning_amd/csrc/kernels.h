@@ -1,0 +1,114 @@
+// Internal interface between the runtime (runtime.cpp) and the HIP kernels
+// (kernels.hip). Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace shp {
+
+// One block of one registered matrix (device copy of the block map).
+struct BlockMeta {
+  int32_t mat;     // matrix index, registration order
+  int32_t r0, c0;  // origin of the block inside the matrix
+  int32_t m, n;    // real extent (block shape minus the zero-padded tail)
+  int32_t pad_;
+};
+
+// Per registered matrix; the pointers are refreshed whenever a step passes
+// different ones.
+struct MatMeta {
+  const void* grad;
+  void* param;
+  int64_t ld;
+};
+
+// C[m][n] = sum_k P'[k][m] * Q'[k][n] for every element of a batch of
+// independent matrices, all stored row-major and contiguous:
+//   P: K x M (element stride sP between batch members), Q: K x N, C: M x N.
+// P' = pa * P + pd * I (on the k == m diagonal), Q' likewise with qa/qd; the
+// identity shift is what forms T = (5 I - M) / 4 inside the Newton loads.
+struct GemmProblem {
+  const float* P;
+  const float* Q;
+  float* C;
+  int64_t sP, sQ, sC;
+  int32_t M, N, K;
+  int32_t batch;
+  float pa, pd, qa, qd;
+  // epilogue of symmetric products: C = alpha * acc + beta * C_old
+  float alpha, beta;
+  // factors with status[f0 + i] != 0 are skipped (Newton early exit)
+  const int32_t* status;
+  int32_t f0;
+  // residual partials: resid[(f0 + i) * resid_stride + tile] = sum (C - I)^2
+  float* resid;
+  int32_t resid_stride;
+};
+
+constexpr int kMaxProblems = 4;
+
+struct GemmLaunch {
+  GemmProblem p[kMaxProblems];
+  int32_t n_problems;
+};
+
+// Parameter update epilogue of the second apply product.
+struct UpdateArgs {
+  const BlockMeta* blocks;
+  const MatMeta* mats;
+  float lr;
+  int32_t param_bf16;
+  float* out_packed;  // non-null: store U packed instead of updating params
+};
+
+// Factor addressing for the per-factor kernels: factors [0, B) are left
+// statistics of side nl, [B, 2B) right statistics of side nr; left factors
+// start at baseL, right factors at baseR (element offsets into a buffer).
+struct FactorSet {
+  int32_t B;
+  int32_t nl, nr;
+  int64_t offL, offR;  // element offsets of the first left / right factor
+  const int32_t* nreal;
+};
+
+struct NewtonCtl {
+  int32_t* status;
+  int32_t* final_iter;
+  float* scale;
+  float* rprev;
+  float* cfac;          // s^(-1/4)
+  float* resid;         // partials [2B][resid_stride]
+  int32_t resid_stride;
+  int32_t ntiles_l, ntiles_r;  // tiles actually written per left / right factor
+  int32_t* active_count;       // [iter][2] factors active during the iteration
+  double* flops_acc;           // algorithmic flops of the Newton products run
+  float tol;
+  int32_t max_iters;
+  int32_t scale_mode;
+};
+
+// ---- launchers (return hipGetLastError()) ----
+hipError_t launch_pack(const BlockMeta* blocks, const MatMeta* mats, int32_t B, int32_t br, int32_t bc,
+                       int32_t grad_bf16, float* Gp, float* GpT, hipStream_t s);
+hipError_t launch_unpack(const BlockMeta* blocks, const MatMeta* dst, int32_t B, int32_t br,
+                         int32_t bc, const float* Gp, hipStream_t s);
+hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nelemR, int32_t nr,
+                             int32_t B, float eps, hipStream_t s);
+hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, hipStream_t s);
+hipError_t launch_gemm_full(const GemmLaunch& g, int tile, hipStream_t s);
+hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, hipStream_t s);
+hipError_t launch_norms(const float* A, FactorSet fs, NewtonCtl c, hipStream_t s);
+hipError_t launch_newton_init(const float* A, float* M0, float* X1, FactorSet fs, NewtonCtl c,
+                              hipStream_t s);
+hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, hipStream_t s);
+hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, NewtonCtl c,
+                               hipStream_t s);
+
+// Tiles written by a symmetric product of side n with square tile t.
+inline int32_t sym_tiles(int32_t n, int32_t t) {
+  int32_t T = n / t;
+  return T * (T + 1) / 2;
+}
+
+}  // namespace shp

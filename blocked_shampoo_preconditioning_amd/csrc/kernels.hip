@@ -1,0 +1,725 @@
+// HIP kernels of the blocked Shampoo step for CDNA4 (gfx950).
+//
+// Steps of one optimizer step (page "Shampoo optimizer", matrix-case loop;
+// DASH page, abstract, for the stacked block batch):
+//   pack      gradient blocks -> Gp [B][br][bc] and its transpose GpT
+//   stats     L <- beta2 L + g Gp Gp^T,  R <- beta2 R + g Gp^T Gp  (MFMA, SYRK)
+//   norms     s = ||A||_F or min(||A||_F, ||A||_inf) * 2/5 per factor
+//   newton    coupled Newton for A^(-1/4): T = (5I - M)/4, X <- X T,
+//             M <- T^4 M (MFMA GEMM chains, symmetric outputs)
+//   apply     W -= lr * X_L Gp X_R (two MFMA products, update in the epilogue)
+//
+// Every dense product here has the form C = P^T Q with P (K x M) and Q
+// (K x N) stored row-major, so both operands stream along K in contiguous
+// rows ("k-major") and go to LDS without a transpose. The statistics read
+// GpT / Gp, the Newton products read symmetric matrices (P^T = P), the
+// apply reads Gp and the transposed intermediate it writes itself.
+//
+// MFMA: v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate). Operand layout
+// for one 32x32x2 step: lane l supplies A[m = l % 32][k = l / 32] and
+// B[k = l / 32][n = l % 32]; accumulator register r of lane l holds
+// D[m = 8 (r / 4) + 4 (l / 32) + r % 4][n = l % 32].
+#include "kernels.h"
+
+#include <math.h>
+
+namespace shp {
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Tile shape: WM x WN waves, each owning FM x FN 32x32 MFMA fragments.
+template <int WM_, int WN_, int FM_, int FN_>
+struct Cfg {
+  static constexpr int WM = WM_, WN = WN_, FM = FM_, FN = FN_;
+  static constexpr int NT = 64 * WM * WN;
+  static constexpr int BM = 32 * FM * WM;
+  static constexpr int BN = 32 * FN * WN;
+  static constexpr int BK = 16;
+  // LDS row pitch: the two half-waves of an operand read rows k and k+1;
+  // a pitch of 32 (mod 64) banks keeps them on disjoint banks.
+  static constexpr int LDP = BM + ((BM % 64) == 0 ? 32 : 0);
+  static constexpr int LDQ = BN + ((BN % 64) == 0 ? 32 : 0);
+  static constexpr int LDS_FLOATS = 2 * BK * (LDP + LDQ);
+  static constexpr int PV = BM / 4, QV = BN / 4;           // float4 per operand row
+  static constexpr int PPT = BK * PV / NT, QPT = BK * QV / NT;  // float4 per thread
+  static_assert(PPT >= 1 && QPT >= 1, "tile too small for the thread count");
+  static_assert((BK * PV) % NT == 0 && (BK * QV) % NT == 0, "uneven operand load");
+};
+
+using Cfg128 = Cfg<2, 2, 2, 2>;  // 128 x 128, 256 threads
+using Cfg64 = Cfg<2, 2, 1, 1>;   //  64 x  64, 256 threads
+using Cfg32 = Cfg<1, 1, 1, 1>;   //  32 x  32,  64 threads
+
+// Workgroups are dispatched round-robin over the 8 XCDs. Give every XCD a
+// contiguous range of logical tiles so the tiles of one matrix share an L2.
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int xcd = w % 8, idx = w / 8;
+  return xcd * per + min(xcd, rem) + idx;
+}
+
+__device__ __forceinline__ float4 shift_diag(float4 x, float a, float d, int k, int m) {
+  // x holds columns m..m+3 of row k: x * a + d on the diagonal
+  x.x = x.x * a + (k == m ? d : 0.f);
+  x.y = x.y * a + (k == m + 1 ? d : 0.f);
+  x.z = x.z * a + (k == m + 2 ? d : 0.f);
+  x.w = x.w * a + (k == m + 3 ? d : 0.f);
+  return x;
+}
+
+// acc[fm][fn] += sum over K of P'[k][m0 + ...] * Q'[k][n0 + ...]
+template <class C>
+__device__ __forceinline__ void mainloop(const float* __restrict__ P, const float* __restrict__ Q,
+                                         int M, int N, int K, int m0, int n0, float pa, float pd,
+                                         bool tp, float qa, float qd, bool tq,
+                                         floatx16 (&acc)[C::FM][C::FN], float* lds) {
+  float* sP = lds;
+  float* sQ = lds + 2 * C::BK * C::LDP;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % C::WM, wn = wave / C::WM;
+  const int half = lane >> 5, l32 = lane & 31;
+
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  float4 pr[C::PPT], qr[C::QPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < C::PPT; ++i) {
+      const int v = tid + i * C::NT;
+      const int row = v / C::PV, c4 = v % C::PV;
+      const int k = k0 + row, m = m0 + c4 * 4;
+      float4 x = *reinterpret_cast<const float4*>(P + (size_t)k * M + m);
+      pr[i] = tp ? shift_diag(x, pa, pd, k, m) : x;
+    }
+#pragma unroll
+    for (int i = 0; i < C::QPT; ++i) {
+      const int v = tid + i * C::NT;
+      const int row = v / C::QV, c4 = v % C::QV;
+      const int k = k0 + row, n = n0 + c4 * 4;
+      float4 x = *reinterpret_cast<const float4*>(Q + (size_t)k * N + n);
+      qr[i] = tq ? shift_diag(x, qa, qd, k, n) : x;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::PPT; ++i) {
+      const int v = tid + i * C::NT;
+      const int row = v / C::PV, c4 = v % C::PV;
+      *reinterpret_cast<float4*>(sP + (buf * C::BK + row) * C::LDP + c4 * 4) = pr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::QPT; ++i) {
+      const int v = tid + i * C::NT;
+      const int row = v / C::QV, c4 = v % C::QV;
+      *reinterpret_cast<float4*>(sQ + (buf * C::BK + row) * C::LDQ + c4 * 4) = qr[i];
+    }
+  };
+
+  const int nk = K / C::BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * C::BK);
+    const float* p = sP + buf * C::BK * C::LDP + wm * 32 * C::FM + l32;
+    const float* q = sQ + buf * C::BK * C::LDQ + wn * 32 * C::FN + l32;
+#pragma unroll
+    for (int kk = 0; kk < C::BK; kk += 2) {
+      float a[C::FM], b[C::FN];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) a[i] = p[(kk + half) * C::LDP + i * 32];
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) b[j] = q[(kk + half) * C::LDQ + j * 32];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+// Row / column of accumulator register r of fragment (i, j).
+template <class C>
+__device__ __forceinline__ int frag_row(int m0, int i, int r) {
+  const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) % C::WM;
+  return m0 + wm * 32 * C::FM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+template <class C>
+__device__ __forceinline__ int frag_col(int n0, int j) {
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) / C::WM;
+  return n0 + wn * 32 * C::FN + j * 32 + (lane & 31);
+}
+
+// ---------------------------------------------------------------------------
+// Symmetric product: only tiles on or above the diagonal are computed; each
+// is written to its place and mirrored, so the stored result is exactly
+// symmetric. Used by the statistics (EMA epilogue) and the Newton chain.
+// ---------------------------------------------------------------------------
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_sym_kernel(GemmLaunch g) {
+  __shared__ float lds[C::LDS_FLOATS];
+  __shared__ float red[C::NT / 64];
+  const GemmProblem& pb = g.p[blockIdx.y];
+  const int T = pb.M / C::BM;
+  const int ntile = T * (T + 1) / 2;
+  const int total = ntile * pb.batch;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  if (logical >= total) return;
+  const int f = logical / ntile;
+  const int tile = logical - f * ntile;
+  if (pb.status != nullptr && pb.status[pb.f0 + f] != 0) return;
+  int t = tile, ti = 0;
+  while (t >= T - ti) {
+    t -= T - ti;
+    ++ti;
+  }
+  const int tj = ti + t;
+  const int m0 = ti * C::BM, n0 = tj * C::BN;
+
+  floatx16 acc[C::FM][C::FN];
+  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, pb.pa,
+              pb.pd, pb.pa != 1.f || pb.pd != 0.f, pb.qa, pb.qd, pb.qa != 1.f || pb.qd != 0.f, acc,
+              lds);
+
+  float* Cb = pb.C + (size_t)f * pb.sC;
+  const int N = pb.N;
+  const bool diag = (ti == tj);
+  float rs = 0.f;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = frag_col<C>(n0, j);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = frag_row<C>(m0, i, r);
+        if (diag && row > col) continue;
+        float v = pb.alpha * acc[i][j][r];
+        if (pb.beta != 0.f) v += pb.beta * Cb[(size_t)row * N + col];
+        Cb[(size_t)row * N + col] = v;
+        if (row != col) Cb[(size_t)col * N + row] = v;
+        const float d = v - (row == col ? 1.f : 0.f);
+        rs += (row == col ? 1.f : 2.f) * d * d;
+      }
+    }
+  if (pb.resid != nullptr) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) rs += __shfl_xor(rs, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = rs;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float s = 0.f;
+      for (int w = 0; w < C::NT / 64; ++w) s += red[w];
+      pb.resid[(size_t)(pb.f0 + f) * pb.resid_stride + tile] = s;
+    }
+  }
+}
+
+// Plain product, every tile, C = acc (first apply product).
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_full_kernel(GemmLaunch g) {
+  __shared__ float lds[C::LDS_FLOATS];
+  const GemmProblem& pb = g.p[blockIdx.y];
+  const int TM = pb.M / C::BM, TN = pb.N / C::BN;
+  const int ntile = TM * TN;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  if (logical >= ntile * pb.batch) return;
+  const int f = logical / ntile;
+  const int tile = logical - f * ntile;
+  const int m0 = (tile / TN) * C::BM, n0 = (tile % TN) * C::BN;
+  floatx16 acc[C::FM][C::FN];
+  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, 1.f,
+              0.f, false, 1.f, 0.f, false, acc, lds);
+  float* Cb = pb.C + (size_t)f * pb.sC;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = frag_col<C>(n0, j);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Cb[(size_t)frag_row<C>(m0, i, r) * pb.N + col] = acc[i][j][r];
+    }
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bfloat16, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Second apply product with the parameter update in the epilogue:
+// W[r0 + row][c0 + col] -= lr * U[row][col] on the block's real extent.
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_update_kernel(GemmLaunch g, UpdateArgs u) {
+  __shared__ float lds[C::LDS_FLOATS];
+  const GemmProblem& pb = g.p[0];
+  const int TM = pb.M / C::BM, TN = pb.N / C::BN;
+  const int ntile = TM * TN;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  if (logical >= ntile * pb.batch) return;
+  const int f = logical / ntile;
+  const int tile = logical - f * ntile;
+  const int m0 = (tile / TN) * C::BM, n0 = (tile % TN) * C::BN;
+  floatx16 acc[C::FM][C::FN];
+  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, 1.f,
+              0.f, false, 1.f, 0.f, false, acc, lds);
+  if (u.out_packed != nullptr) {
+    float* Ub = u.out_packed + (size_t)f * pb.M * pb.N;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const int col = frag_col<C>(n0, j);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Ub[(size_t)frag_row<C>(m0, i, r) * pb.N + col] = acc[i][j][r];
+      }
+    return;
+  }
+  const BlockMeta bm = u.blocks[f];
+  const MatMeta mm = u.mats[bm.mat];
+  const float lr = u.lr;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = frag_col<C>(n0, j);
+      if (col >= bm.n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = frag_row<C>(m0, i, r);
+        if (row >= bm.m) continue;
+        const size_t off = (size_t)(bm.r0 + row) * mm.ld + bm.c0 + col;
+        if (u.param_bf16) {
+          uint16_t* w = reinterpret_cast<uint16_t*>(mm.param) + off;
+          *w = f32_to_bf16(bf16_to_f32(*w) - lr * acc[i][j][r]);
+        } else {
+          float* w = reinterpret_cast<float*>(mm.param) + off;
+          *w = *w - lr * acc[i][j][r];
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pack / unpack: 64 x 64 tiles of a block, 256 threads, 16-byte accesses.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float4 load4(const void* base, int64_t off, int bf16) {
+  if (bf16) {
+    const uint2 h = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+    return make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
+                       __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
+  }
+  return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+}
+__device__ __forceinline__ float load1(const void* base, int64_t off, int bf16) {
+  if (bf16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[off]);
+  return reinterpret_cast<const float*>(base)[off];
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__ blocks,
+                                                   const MatMeta* __restrict__ mats, int br, int bc,
+                                                   int bf16, float* __restrict__ Gp,
+                                                   float* __restrict__ GpT) {
+  __shared__ float tile[64][65];
+  const int b = blockIdx.y;
+  const BlockMeta bm = blocks[b];
+  const MatMeta mm = mats[bm.mat];
+  const int tcn = (bc + 63) / 64;
+  const int rr0 = (blockIdx.x / tcn) * 64, cc0 = (blockIdx.x % tcn) * 64;
+  const int tid = threadIdx.x;
+  // 4-element vector loads need ld % 4 == 0 and a 4-element-aligned base
+  const bool vec = (mm.ld & 3) == 0 &&
+                   (reinterpret_cast<uintptr_t>(mm.grad) & (bf16 ? 7u : 15u)) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = tid / 16 + 16 * i;
+    const int c = (tid % 16) * 4;
+    const int pr = rr0 + row, pc = cc0 + c;  // position inside the packed block
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (pr < bm.m && pc < bm.n) {
+      const int64_t off = (int64_t)(bm.r0 + pr) * mm.ld + bm.c0 + pc;
+      if (vec && pc + 3 < bm.n) {
+        v = load4(mm.grad, off, bf16);
+      } else {
+        v.x = load1(mm.grad, off, bf16);
+        if (pc + 1 < bm.n) v.y = load1(mm.grad, off + 1, bf16);
+        if (pc + 2 < bm.n) v.z = load1(mm.grad, off + 2, bf16);
+        if (pc + 3 < bm.n) v.w = load1(mm.grad, off + 3, bf16);
+      }
+    }
+    if (pr < br && pc < bc)
+      *reinterpret_cast<float4*>(Gp + ((size_t)b * br + pr) * bc + pc) = v;
+    tile[row][c] = v.x;
+    tile[row][c + 1] = v.y;
+    tile[row][c + 2] = v.z;
+    tile[row][c + 3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tc = tid / 16 + 16 * i;  // column of the tile = row of GpT
+    const int r = (tid % 16) * 4;
+    if (cc0 + tc < bc && rr0 + r < br) {
+      const float4 v = make_float4(tile[r][tc], tile[r + 1][tc], tile[r + 2][tc], tile[r + 3][tc]);
+      *reinterpret_cast<float4*>(GpT + ((size_t)b * bc + cc0 + tc) * br + rr0 + r) = v;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void unpack_kernel(const BlockMeta* __restrict__ blocks,
+                                                     const MatMeta* __restrict__ dst, int br, int bc,
+                                                     const float* __restrict__ Gp) {
+  const int b = blockIdx.y;
+  const BlockMeta bm = blocks[b];
+  const MatMeta mm = dst[bm.mat];
+  const int tcn = (bc + 63) / 64;
+  const int rr0 = (blockIdx.x / tcn) * 64, cc0 = (blockIdx.x % tcn) * 64;
+  const int tid = threadIdx.x;
+  float* out = reinterpret_cast<float*>(mm.param);
+  const bool vec = (mm.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pr = rr0 + tid / 16 + 16 * i;
+    const int pc = cc0 + (tid % 16) * 4;
+    if (pr >= bm.m || pc >= bm.n) continue;
+    const float4 v = *reinterpret_cast<const float4*>(Gp + ((size_t)b * br + pr) * bc + pc);
+    const int64_t off = (int64_t)(bm.r0 + pr) * mm.ld + bm.c0 + pc;
+    if (vec && pc + 3 < bm.n) {
+      *reinterpret_cast<float4*>(out + off) = v;
+    } else {
+      out[off] = v.x;
+      if (pc + 1 < bm.n) out[off + 1] = v.y;
+      if (pc + 2 < bm.n) out[off + 2] = v.z;
+      if (pc + 3 < bm.n) out[off + 3] = v.w;
+    }
+  }
+}
+
+// L = R = eps * I over the whole padded factor (left factors, then right).
+__global__ __launch_bounds__(256) void init_state_kernel(float* LR, int64_t nelemL, int nl,
+                                                         int64_t nelemR, int nr, float eps) {
+  const int64_t total = nelemL + nelemR;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const bool left = e < nelemL;
+    const int n = left ? nl : nr;
+    const int64_t w = (left ? e : e - nelemL) % ((int64_t)n * n);
+    LR[e] = (w / n == w % n) ? eps : 0.f;
+  }
+}
+
+__device__ __forceinline__ const float* factor_ptr(const float* base, const FactorSet& fs, int f,
+                                                   int& n) {
+  if (f < fs.B) {
+    n = fs.nl;
+    return base + fs.offL + (int64_t)f * fs.nl * fs.nl;
+  }
+  n = fs.nr;
+  return base + fs.offR + (int64_t)(f - fs.B) * fs.nr * fs.nr;
+}
+
+// ---------------------------------------------------------------------------
+// Norm scaling: one workgroup per factor, fp64 accumulation in a fixed order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A, FactorSet fs,
+                                                    NewtonCtl c) {
+  __shared__ double red_sq[4];
+  __shared__ double red_inf[4];
+  const int f = blockIdx.x;
+  int n;
+  const float* Af = factor_ptr(A, fs, f, n);
+  const int nr = fs.nreal[f];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double sq = 0.0, rowmax = 0.0;
+  for (int r = wave; r < nr; r += 4) {
+    const float* row = Af + (int64_t)r * n;
+    double as = 0.0;
+    const int n4 = nr & ~3;
+    for (int j = lane * 4; j < n4; j += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(row + j);
+      as += fabs((double)v.x) + fabs((double)v.y) + fabs((double)v.z) + fabs((double)v.w);
+      sq += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+    }
+    for (int j = n4 + lane; j < nr; j += 64) {
+      const double v = row[j];
+      as += fabs(v);
+      sq += v * v;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) as += __shfl_xor(as, o);
+    rowmax = fmax(rowmax, as);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o);
+  if (lane == 0) {
+    red_sq[wave] = sq;
+    red_inf[wave] = rowmax;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double fro = sqrt(red_sq[0] + red_sq[1] + red_sq[2] + red_sq[3]);
+    const double inf = fmax(fmax(red_inf[0], red_inf[1]), fmax(red_inf[2], red_inf[3]));
+    const double s = c.scale_mode == 0 ? fro : fmin(fro, inf) * 0.4;
+    const bool ok = s > 0.0 && isfinite(s) && isfinite(fro);
+    c.scale[f] = (float)s;
+    c.cfac[f] = ok ? (float)pow(s, -0.25) : 0.f;
+    c.status[f] = ok ? 0 : 3;
+    c.final_iter[f] = 0;
+    c.rprev[f] = INFINITY;
+  }
+}
+
+// M0 = A / s (identity on the padded part), X1 = s^(-1/4) (5 I - M0) / 4.
+__global__ __launch_bounds__(256) void newton_init_kernel(const float* __restrict__ A,
+                                                          float* __restrict__ M0,
+                                                          float* __restrict__ X1, FactorSet fs,
+                                                          NewtonCtl c) {
+  const int f = blockIdx.y;
+  if (c.status[f] != 0) return;
+  int n;
+  const float* Af = factor_ptr(A, fs, f, n);
+  const int64_t base = Af - A;
+  const int nr = fs.nreal[f];
+  const float s = c.scale[f], cf = c.cfac[f];
+  const int64_t nn = (int64_t)n * n;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(e / n), col = (int)(e % n);
+    const float id = (r == col) ? 1.f : 0.f;
+    const float m = (r < nr && col < nr) ? Af[e] / s : id;
+    M0[base + e] = m;
+    X1[base + e] = cf * (1.25f * id - 0.25f * m);
+  }
+}
+
+// After iteration `iter` (which produced M_{iter+1} and X_{iter+1}): residual
+// and stopping rule per factor; counts the factors that took part in the
+// iteration and adds the algorithmic flops of its symmetric products
+// (three at the first iteration, where X_1 needs no product, four after;
+// n^2 (n + 1) each).
+__global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, NewtonCtl c, int iter) {
+  __shared__ int cnt[2];
+  if (threadIdx.x < 2) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int nf = 2 * fs.B;
+  for (int f = threadIdx.x; f < nf; f += blockDim.x) {
+    if (c.status[f] != 0) continue;
+    const bool left = f < fs.B;
+    atomicAdd(&cnt[left ? 0 : 1], 1);
+    const int nt = left ? c.ntiles_l : c.ntiles_r;
+    const float* p = c.resid + (size_t)f * c.resid_stride;
+    float s = 0.f;
+    for (int t = 0; t < nt; ++t) s += p[t];
+    const float r = sqrtf(s) / sqrtf((float)fs.nreal[f]);
+    const float rp = c.rprev[f];
+    int st = 0;
+    if (!isfinite(r)) {
+      st = 3;
+    } else if (c.tol > 0.f && r > 1.2f * rp) {
+      st = 3;
+    } else if (c.tol > 0.f && r >= rp) {
+      st = 2;
+    } else {
+      c.rprev[f] = r;
+      c.final_iter[f] = iter + 1;
+      if (c.tol > 0.f && r <= c.tol)
+        st = 1;
+      else if (iter + 1 >= c.max_iters)
+        st = 4;
+    }
+    c.status[f] = st;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) c.active_count[iter * 2 + threadIdx.x] = cnt[threadIdx.x];
+  if (threadIdx.x == 0) {
+    const double nl = fs.nl, nr = fs.nr, g = iter == 0 ? 3.0 : 4.0;
+    c.flops_acc[0] += g * (cnt[0] * nl * nl * (nl + 1.0) + cnt[1] * nr * nr * (nr + 1.0));
+  }
+}
+
+// Put the kept iterate into the root buffer: X_k lives in Xroot for even k
+// and in Xalt for odd k; X_0 = s^(-1/4) I is never stored.
+__global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ Xroot,
+                                                           const float* __restrict__ Xalt,
+                                                           FactorSet fs, NewtonCtl c) {
+  const int f = blockIdx.y;
+  const int k = c.final_iter[f];
+  if (k > 0 && (k & 1) == 0) return;
+  int n;
+  const float* xf = factor_ptr(Xroot, fs, f, n);
+  const int64_t base = xf - Xroot;
+  const float cf = c.cfac[f];
+  const int64_t nn = (int64_t)n * n;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    Xroot[base + e] = (k == 0) ? ((e / n == e % n) ? cf : 0.f) : Xalt[base + e];
+  }
+}
+
+template <class C>
+int grid_sym(const GemmLaunch& g) {
+  int mx = 0;
+  for (int i = 0; i < g.n_problems; ++i) {
+    const int T = g.p[i].M / C::BM;
+    mx = max(mx, T * (T + 1) / 2 * g.p[i].batch);
+  }
+  return mx;
+}
+template <class C>
+int grid_full(const GemmLaunch& g) {
+  int mx = 0;
+  for (int i = 0; i < g.n_problems; ++i)
+    mx = max(mx, (g.p[i].M / C::BM) * (g.p[i].N / C::BN) * g.p[i].batch);
+  return mx;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_pack(const BlockMeta* blocks, const MatMeta* mats, int32_t B, int32_t br,
+                       int32_t bc, int32_t grad_bf16, float* Gp, float* GpT, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  dim3 grid(((br + 63) / 64) * ((bc + 63) / 64), B);
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, blocks, mats, br, bc, grad_bf16, Gp, GpT);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const BlockMeta* blocks, const MatMeta* dst, int32_t B, int32_t br,
+                         int32_t bc, const float* Gp, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  dim3 grid(((br + 63) / 64) * ((bc + 63) / 64), B);
+  hipLaunchKernelGGL(unpack_kernel, grid, dim3(256), 0, s, blocks, dst, br, bc, Gp);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nelemR, int32_t nr,
+                             int32_t B, float eps, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const int64_t total = nelemL + nelemR;
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(init_state_kernel, dim3(blocks), dim3(256), 0, s, LR, nelemL, nl, nelemR, nr,
+                     eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, hipStream_t s) {
+  if (g.n_problems == 0) return hipSuccess;
+  switch (tile) {
+    case 128: {
+      const int gx = grid_sym<Cfg128>(g);
+      if (gx) hipLaunchKernelGGL(gemm_sym_kernel<Cfg128>, dim3(gx, g.n_problems), dim3(Cfg128::NT), 0, s, g);
+      break;
+    }
+    case 64: {
+      const int gx = grid_sym<Cfg64>(g);
+      if (gx) hipLaunchKernelGGL(gemm_sym_kernel<Cfg64>, dim3(gx, g.n_problems), dim3(Cfg64::NT), 0, s, g);
+      break;
+    }
+    case 32: {
+      const int gx = grid_sym<Cfg32>(g);
+      if (gx) hipLaunchKernelGGL(gemm_sym_kernel<Cfg32>, dim3(gx, g.n_problems), dim3(Cfg32::NT), 0, s, g);
+      break;
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_full(const GemmLaunch& g, int tile, hipStream_t s) {
+  if (g.n_problems == 0) return hipSuccess;
+  switch (tile) {
+    case 128: {
+      const int gx = grid_full<Cfg128>(g);
+      if (gx) hipLaunchKernelGGL(gemm_full_kernel<Cfg128>, dim3(gx, g.n_problems), dim3(Cfg128::NT), 0, s, g);
+      break;
+    }
+    case 64: {
+      const int gx = grid_full<Cfg64>(g);
+      if (gx) hipLaunchKernelGGL(gemm_full_kernel<Cfg64>, dim3(gx, g.n_problems), dim3(Cfg64::NT), 0, s, g);
+      break;
+    }
+    case 32: {
+      const int gx = grid_full<Cfg32>(g);
+      if (gx) hipLaunchKernelGGL(gemm_full_kernel<Cfg32>, dim3(gx, g.n_problems), dim3(Cfg32::NT), 0, s, g);
+      break;
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, hipStream_t s) {
+  if (g.n_problems != 1) return hipErrorInvalidValue;
+  switch (tile) {
+    case 128: {
+      const int gx = grid_full<Cfg128>(g);
+      if (gx) hipLaunchKernelGGL(gemm_update_kernel<Cfg128>, dim3(gx), dim3(Cfg128::NT), 0, s, g, u);
+      break;
+    }
+    case 64: {
+      const int gx = grid_full<Cfg64>(g);
+      if (gx) hipLaunchKernelGGL(gemm_update_kernel<Cfg64>, dim3(gx), dim3(Cfg64::NT), 0, s, g, u);
+      break;
+    }
+    case 32: {
+      const int gx = grid_full<Cfg32>(g);
+      if (gx) hipLaunchKernelGGL(gemm_update_kernel<Cfg32>, dim3(gx), dim3(Cfg32::NT), 0, s, g, u);
+      break;
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_norms(const float* A, FactorSet fs, NewtonCtl c, hipStream_t s) {
+  if (fs.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(norms_kernel, dim3(2 * fs.B), dim3(256), 0, s, A, fs, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_newton_init(const float* A, float* M0, float* X1, FactorSet fs, NewtonCtl c,
+                              hipStream_t s) {
+  if (fs.B == 0) return hipSuccess;
+  const int nmax = std::max(fs.nl, fs.nr);
+  const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
+  hipLaunchKernelGGL(newton_init_kernel, dim3(chunks, 2 * fs.B), dim3(256), 0, s, A, M0, X1, fs, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, hipStream_t s) {
+  if (fs.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(newton_check_kernel, dim3(1), dim3(1024), 0, s, fs, c, iter);
+  return hipGetLastError();
+}
+
+hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, NewtonCtl c,
+                               hipStream_t s) {
+  if (fs.B == 0) return hipSuccess;
+  const int nmax = std::max(fs.nl, fs.nr);
+  const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
+  hipLaunchKernelGGL(newton_final_kernel, dim3(chunks, 2 * fs.B), dim3(256), 0, s, Xroot, Xalt, fs,
+                     c);
+  return hipGetLastError();
+}
+
+}  // namespace shp

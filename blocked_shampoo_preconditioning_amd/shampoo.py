@@ -1,0 +1,326 @@
+"""ctypes binding of libshampoo_mi355x.so (the C ABI in include/shampoo.h).
+
+The functions keep the C names and only marshal arguments: every step of the
+method runs in the HIP library. PyTorch provides device memory (the
+workspace, parameters and gradients) and the stream. A missing library is an
+error; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libshampoo_mi355x.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "shampoo.h")
+
+SHAMPOO_OK = 0
+SHAMPOO_ERR_INVALID_ARG = 1
+SHAMPOO_ERR_UNSUPPORTED = 2
+SHAMPOO_ERR_WORKSPACE_TOO_SMALL = 3
+SHAMPOO_ERR_MISALIGNED = 4
+SHAMPOO_ERR_NO_ROOTS = 5
+SHAMPOO_ERR_HIP = 6
+SHAMPOO_F32 = 0
+SHAMPOO_BF16 = 1
+SHAMPOO_FORCE_REFRESH = 1
+SHAMPOO_NO_AUTO_REFRESH = 2
+TIMING_CLASSES = ("pack", "stats", "norms", "newton_gemm", "newton_aux", "apply")
+
+
+class MatrixDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ld", ctypes.c_int64)]
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("block_rows", ctypes.c_int32), ("block_cols", ctypes.c_int32),
+                ("beta2", ctypes.c_double), ("stat_scale", ctypes.c_double),
+                ("eps", ctypes.c_double), ("lr", ctypes.c_double),
+                ("root_every", ctypes.c_int32), ("newton_max_iters", ctypes.c_int32),
+                ("newton_tol", ctypes.c_double), ("newton_scale_mode", ctypes.c_int32),
+                ("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("n_blocks", "grad_packed", "stats", "roots",
+                                              "newton_status", "newton_iters", "newton_scale",
+                                              "workspace_bytes")]
+
+
+class Timing(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * 6), ("flops", ctypes.c_double * 6),
+                ("bytes", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6)]
+
+
+class ShampooError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"shampoo error {code}: {message}")
+        self.code = code
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(ctypes.c_void_p)
+_SIGNATURES = {
+    "shampoo_config_default": [ctypes.POINTER(Config)],
+    "shampoo_workspace_size": [ctypes.POINTER(Config), ctypes.POINTER(MatrixDesc), ctypes.c_int32,
+                               ctypes.POINTER(ctypes.c_size_t)],
+    "shampoo_init": [ctypes.POINTER(Config), ctypes.POINTER(MatrixDesc), ctypes.c_int32, _P,
+                     ctypes.c_size_t, _P, ctypes.POINTER(_P)],
+    "shampoo_step": [_P, _PP, _PP, ctypes.c_uint32, _P],
+    "shampoo_refresh_roots": [_P, _P],
+    "shampoo_destroy": [_P],
+    "shampoo_state_layout": [_P, ctypes.POINTER(Layout)],
+    "shampoo_get_step": [_P, ctypes.POINTER(ctypes.c_int64)],
+    "shampoo_set_step": [_P, ctypes.c_int64],
+    "shampoo_pack": [_P, _PP, _P],
+    "shampoo_unpack": [_P, _PP, _P],
+    "shampoo_precondition": [_P, _P, _P],
+    "shampoo_get_status": [_P, _P, ctypes.POINTER(ctypes.c_int32)],
+    "shampoo_set_timing": [_P, ctypes.c_int32, _P],
+    "shampoo_get_timing": [_P, ctypes.POINTER(Timing)],
+    "shampoo_status_string": [ctypes.c_int],
+    "shampoo_last_error": [],
+}
+
+
+def load_library(path=LIB_PATH):
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          f"`python -m blocked_shampoo_preconditioning_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, argtypes in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_char_p if name in ("shampoo_status_string", "shampoo_last_error") \
+            else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def header_functions(path=HEADER_PATH):
+    """Names of the functions include/shampoo.h declares."""
+    text = open(path).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(shampoo_\w+)\s*\(", text, re.M)))
+
+
+def _check(code):
+    if code != SHAMPOO_OK:
+        lib = load_library()
+        raise ShampooError(code, lib.shampoo_last_error().decode())
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*[ctypes.c_void_p(p) for p in ptrs])
+    return ctypes.cast(arr, _PP), arr
+
+
+# ---------------------------------------------------------------------------
+# Functions with the C names (argument marshalling only)
+# ---------------------------------------------------------------------------
+def shampoo_config_default():
+    cfg = Config()
+    _check(load_library().shampoo_config_default(ctypes.byref(cfg)))
+    return cfg
+
+
+def make_descs(shapes, lds=None):
+    descs = (MatrixDesc * max(1, len(shapes)))()
+    for i, (r, c) in enumerate(shapes):
+        descs[i] = MatrixDesc(r, c, c if lds is None else lds[i])
+    return descs
+
+
+def shampoo_workspace_size(cfg, descs, n_mats):
+    out = ctypes.c_size_t(0)
+    _check(load_library().shampoo_workspace_size(ctypes.byref(cfg), descs, n_mats, ctypes.byref(out)))
+    return out.value
+
+
+def shampoo_init(cfg, descs, n_mats, workspace_ptr, workspace_bytes, stream):
+    h = ctypes.c_void_p()
+    _check(load_library().shampoo_init(ctypes.byref(cfg), descs, n_mats, ctypes.c_void_p(workspace_ptr),
+                                       workspace_bytes, ctypes.c_void_p(stream), ctypes.byref(h)))
+    return h
+
+
+def shampoo_step(h, param_ptrs, grad_ptrs, flags, stream):
+    p, _pk = _ptr_array(param_ptrs)
+    g, _gk = _ptr_array(grad_ptrs)
+    _check(load_library().shampoo_step(h, p, g, flags, ctypes.c_void_p(stream)))
+
+
+def shampoo_refresh_roots(h, stream):
+    _check(load_library().shampoo_refresh_roots(h, ctypes.c_void_p(stream)))
+
+
+def shampoo_destroy(h):
+    _check(load_library().shampoo_destroy(h))
+
+
+def shampoo_state_layout(h):
+    out = Layout()
+    _check(load_library().shampoo_state_layout(h, ctypes.byref(out)))
+    return out
+
+
+def shampoo_get_step(h):
+    t = ctypes.c_int64()
+    _check(load_library().shampoo_get_step(h, ctypes.byref(t)))
+    return t.value
+
+
+def shampoo_set_step(h, t):
+    _check(load_library().shampoo_set_step(h, t))
+
+
+def shampoo_pack(h, grad_ptrs, stream):
+    g, _gk = _ptr_array(grad_ptrs)
+    _check(load_library().shampoo_pack(h, g, ctypes.c_void_p(stream)))
+
+
+def shampoo_unpack(h, dst_ptrs, stream):
+    d, _dk = _ptr_array(dst_ptrs)
+    _check(load_library().shampoo_unpack(h, d, ctypes.c_void_p(stream)))
+
+
+def shampoo_precondition(h, out_ptr, stream):
+    _check(load_library().shampoo_precondition(h, ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)))
+
+
+def shampoo_get_status(h, stream):
+    n = ctypes.c_int32()
+    _check(load_library().shampoo_get_status(h, ctypes.c_void_p(stream), ctypes.byref(n)))
+    return n.value
+
+
+def shampoo_set_timing(h, enable, stream):
+    _check(load_library().shampoo_set_timing(h, int(enable), ctypes.c_void_p(stream)))
+
+
+def shampoo_get_timing(h):
+    t = Timing()
+    _check(load_library().shampoo_get_timing(h, ctypes.byref(t)))
+    return {name: {"ms": t.ms[i], "flops": t.flops[i], "bytes": t.bytes[i],
+                   "launches": t.launches[i]} for i, name in enumerate(TIMING_CLASSES)}
+
+
+# ---------------------------------------------------------------------------
+# Convenience wrapper over torch tensors
+# ---------------------------------------------------------------------------
+class Shampoo:
+    """Blocked Shampoo over a list of 2-D CUDA tensors (parameters).
+
+    The workspace is one uint8 tensor allocated here with torch; the library
+    keeps all state in it. Every call runs on torch's current stream.
+    """
+
+    def __init__(self, shapes, block_rows=1024, block_cols=1024, beta2=0.999, eps=1e-6, lr=1e-3,
+                 root_every=10, stat_scale=None, newton_max_iters=25, newton_tol=1e-6,
+                 newton_scale_mode=1, dtype="f32", device="cuda", lds=None):
+        import torch
+        self.torch = torch
+        self.shapes = [tuple(int(v) for v in s) for s in shapes]
+        self.lds = [c for (_, c) in self.shapes] if lds is None else list(lds)
+        cfg = shampoo_config_default()
+        cfg.block_rows, cfg.block_cols = block_rows, block_cols
+        cfg.beta2, cfg.eps, cfg.lr = beta2, eps, lr
+        cfg.stat_scale = -1.0 if stat_scale is None else stat_scale
+        cfg.root_every = root_every
+        cfg.newton_max_iters, cfg.newton_tol = newton_max_iters, newton_tol
+        cfg.newton_scale_mode = newton_scale_mode
+        dt = {"f32": SHAMPOO_F32, "bf16": SHAMPOO_BF16}[dtype]
+        cfg.param_dtype = cfg.grad_dtype = dt
+        self.cfg = cfg
+        self.descs = make_descs(self.shapes, self.lds)
+        self.n = len(self.shapes)
+        nbytes = shampoo_workspace_size(cfg, self.descs, self.n)
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        base = self.workspace.data_ptr()
+        self._ws_ptr = (base + 255) // 256 * 256
+        self._ws_off = self._ws_ptr - base
+        self.handle = shampoo_init(cfg, self.descs, self.n, self._ws_ptr, nbytes, self._stream())
+        self.layout = shampoo_state_layout(self.handle)
+
+    def _stream(self):
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def close(self):
+        if self.handle is not None:
+            self.torch.cuda.current_stream().synchronize()
+            shampoo_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def step(self, params, grads, flags=0):
+        shampoo_step(self.handle, [p.data_ptr() for p in params], [g.data_ptr() for g in grads],
+                     flags, self._stream())
+
+    def refresh_roots(self):
+        shampoo_refresh_roots(self.handle, self._stream())
+
+    def pack(self, grads):
+        shampoo_pack(self.handle, [g.data_ptr() for g in grads], self._stream())
+
+    def unpack(self, dsts):
+        shampoo_unpack(self.handle, [d.data_ptr() for d in dsts], self._stream())
+
+    def precondition(self, out):
+        shampoo_precondition(self.handle, out.data_ptr(), self._stream())
+
+    def n_diverged(self):
+        return shampoo_get_status(self.handle, self._stream())
+
+    def set_timing(self, enable):
+        shampoo_set_timing(self.handle, enable, self._stream())
+
+    def timing(self):
+        return shampoo_get_timing(self.handle)
+
+    @property
+    def t(self):
+        return shampoo_get_step(self.handle)
+
+    # --- views of the state inside the workspace (no copies) ---
+    def _view(self, off, count, dtype):
+        torch = self.torch
+        esz = torch.tensor([], dtype=dtype).element_size()
+        start = self._ws_off + off
+        return self.workspace[start:start + count * esz].view(dtype)
+
+    @property
+    def n_blocks(self):
+        return int(self.layout.n_blocks)
+
+    def grad_packed(self):
+        B, br, bc = self.n_blocks, self.cfg.block_rows, self.cfg.block_cols
+        return self._view(self.layout.grad_packed, B * br * bc, self.torch.float32).view(B, br, bc)
+
+    def _factors(self, off):
+        B, br, bc = self.n_blocks, self.cfg.block_rows, self.cfg.block_cols
+        flat = self._view(off, B * (br * br + bc * bc), self.torch.float32)
+        return flat[:B * br * br].view(B, br, br), flat[B * br * br:].view(B, bc, bc)
+
+    def stats(self):
+        return self._factors(self.layout.stats)
+
+    def roots(self):
+        return self._factors(self.layout.roots)
+
+    def newton_info(self):
+        B = self.n_blocks
+        st = self._view(self.layout.newton_status, 2 * B, self.torch.int32)
+        it = self._view(self.layout.newton_iters, 2 * B, self.torch.int32)
+        sc = self._view(self.layout.newton_scale, 2 * B, self.torch.float32)
+        return st, it, sc

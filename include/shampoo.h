@@ -1,0 +1,202 @@
+/*
+ * shampoo.h - C ABI of the blocked Shampoo optimizer step for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (page "Shampoo optimizer", section "Key Components" and the
+ * matrix-case loop under it; podcast "Preconditioned Optimization Without
+ * the Full Matrix Cost", cues 20-22): every weight matrix W (m x n) keeps a
+ * left statistic L (m x m) and a right statistic R (n x n), both started at
+ * eps * I. Each step takes the gradient G and
+ *     L <- beta2 L + stat_scale G G^T,   R <- beta2 R + stat_scale G^T G,
+ *     W <- W - lr * L^(-1/4) G R^(-1/4).
+ * The inverse fourth roots are recomputed only every root_every steps and
+ * reused in between (podcast cue 28). Matrices are cut into blocks of
+ * block_rows x block_cols that are preconditioned independently and stacked
+ * into one batch (DASH page, abstract); tail blocks are zero-padded.
+ *
+ * Roots come from a norm-scaled coupled Newton iteration for the inverse
+ * p-th root, p = 4 (Guo and Higham, SIAM J. Matrix Anal. Appl. 28(3), 2006):
+ * M = A / s, X = s^(-1/4) I, then repeatedly T = (5 I - M) / 4, X <- X T,
+ * M <- T^4 M, until ||M - I||_F / sqrt(n) <= newton_tol, the residual stops
+ * decreasing, or newton_max_iters iterations have run.
+ *
+ * Conventions of every entry point:
+ *  - Return value: SHAMPOO_OK (0) or one of the SHAMPOO_ERR_* codes below.
+ *    No C++ exception crosses this boundary. On error a message is kept per
+ *    thread (shampoo_last_error) and no device work has been enqueued unless
+ *    the code is SHAMPOO_ERR_HIP.
+ *  - Pointers named "device" are device (HBM) addresses owned by the caller;
+ *    the library never allocates or frees device memory. "host" pointers are
+ *    read during the call only.
+ *  - hip_stream is a hipStream_t (NULL = the default stream). All device
+ *    work is enqueued on it asynchronously; calls return before it runs,
+ *    except the ones documented as synchronising.
+ *  - Matrices are row-major with a leading dimension ld (elements) >= cols.
+ *  - A handle is not thread-safe; separate handles are independent.
+ *  - Device faults surface as SHAMPOO_ERR_HIP at a later synchronising call.
+ */
+#ifndef SHAMPOO_MI355X_H
+#define SHAMPOO_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ codes */
+enum {
+  SHAMPOO_OK = 0,
+  SHAMPOO_ERR_INVALID_ARG = 1,        /* NULL handle/pointer, bad size or value    */
+  SHAMPOO_ERR_UNSUPPORTED = 2,        /* dtype, block shape or mode not supported   */
+  SHAMPOO_ERR_WORKSPACE_TOO_SMALL = 3,
+  SHAMPOO_ERR_MISALIGNED = 4,         /* pointer not aligned as documented          */
+  SHAMPOO_ERR_NO_ROOTS = 5,           /* step needs roots but none were computed    */
+  SHAMPOO_ERR_HIP = 6                 /* a HIP runtime call failed (message kept)   */
+};
+
+/* Storage types of gradients and parameters. Statistics and roots are fp32. */
+typedef enum { SHAMPOO_F32 = 0, SHAMPOO_BF16 = 1 } shampoo_dtype_t;
+
+/* Flags of shampoo_step. */
+enum {
+  SHAMPOO_FORCE_REFRESH = 1u,   /* recompute roots this step whatever the schedule */
+  SHAMPOO_NO_AUTO_REFRESH = 2u  /* never recompute roots this step                 */
+};
+
+/* One registered matrix: rows x cols, row-major, leading dimension ld
+ * (elements, >= cols). Parameters and gradients of a matrix share this shape
+ * and ld. Pointers must be aligned to their element size; 16-byte aligned
+ * matrices with ld % 4 == 0 are read with vector loads. */
+typedef struct {
+  int64_t rows, cols, ld;
+} shampoo_matrix_desc_t;
+
+/* Hyper-parameters. shampoo_config_default fills every field. The real
+ * values are given in double and rounded once to fp32, the precision every
+ * kernel computes in. */
+typedef struct {
+  int32_t block_rows, block_cols; /* block shape; each a multiple of 32, <= 4096 */
+  double beta2;                   /* weight of the old statistic                 */
+  double stat_scale;              /* weight of the new outer product; a negative
+                                     value means 1 - beta2 (formed in double)    */
+  double eps;                     /* L and R start at eps * I (> 0)              */
+  double lr;                      /* step size                                   */
+  int32_t root_every;             /* refresh at t = 1, 1+k, 1+2k...; 0 = only on
+                                     SHAMPOO_FORCE_REFRESH / refresh_roots       */
+  int32_t newton_max_iters;       /* iteration cap, 1..64                        */
+  double newton_tol;              /* stop when ||M - I||_F / sqrt(n) <= tol; a
+                                     value <= 0 runs exactly newton_max_iters     */
+  int32_t newton_scale_mode;      /* 0: s = ||A||_F (spectrum of A/s in (0,1]);
+                                     1: s = min(||A||_F, ||A||_inf) * 2/5
+                                        (spectrum in (0, 5/2])                   */
+  int32_t param_dtype;            /* shampoo_dtype_t of the parameters           */
+  int32_t grad_dtype;             /* shampoo_dtype_t of the gradients            */
+} shampoo_config_t;
+
+/* Byte offsets of the state inside the caller's workspace (for inspection
+ * and checkpointing). Square blocks of side b: stats holds B left
+ * statistics [B][b][b] followed by B right statistics; roots likewise.
+ * For rectangular blocks the left part has side block_rows and the right
+ * part side block_cols. grad_packed is [B][block_rows][block_cols] fp32,
+ * the last packed gradient. */
+typedef struct {
+  int64_t n_blocks;
+  int64_t grad_packed;    /* fp32 [B][br][bc]                                   */
+  int64_t stats;          /* fp32 [B][br][br] then [B][bc][bc]                  */
+  int64_t roots;          /* fp32, same layout as stats                         */
+  int64_t newton_status;  /* int32 [2B]: per factor, 0 none 1 converged 2 stalled
+                             3 diverged 4 capped (left factors first)            */
+  int64_t newton_iters;   /* int32 [2B]: iterations behind the kept root         */
+  int64_t newton_scale;   /* fp32 [2B]: the scale s of the last refresh           */
+  int64_t workspace_bytes;
+} shampoo_layout_t;
+
+/* Accumulated kernel time per class while timing is enabled (milliseconds,
+ * measured with HIP events on the stream the kernels run on) and the
+ * algorithmic flop count of the launches timed. Classes: 0 pack, 1
+ * statistics, 2 norms, 3 Newton GEMMs, 4 Newton bookkeeping (init, checks,
+ * final copy), 5 apply (two-sided product and parameter update). */
+#define SHAMPOO_TIMING_CLASSES 6
+typedef struct {
+  double ms[SHAMPOO_TIMING_CLASSES];
+  double flops[SHAMPOO_TIMING_CLASSES];
+  double bytes[SHAMPOO_TIMING_CLASSES];
+  int64_t launches[SHAMPOO_TIMING_CLASSES];
+} shampoo_timing_t;
+
+typedef struct shampoo_ctx* shampoo_t;
+
+/* Fill *cfg with the defaults: square blocks of 1024, beta2 0.999,
+ * stat_scale 1 - beta2, eps 1e-6, lr 1e-3, root_every 10, 25 Newton
+ * iterations at most, tol 1e-6, scale mode 1, fp32 parameters and gradients. */
+int shampoo_config_default(shampoo_config_t* cfg);
+
+/* Bytes of device workspace needed for these matrices (host only, no HIP
+ * call). mats: host array of n_mats descriptors. */
+int shampoo_workspace_size(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats,
+                           int32_t n_mats, size_t* bytes_out);
+
+/* Create a handle. workspace: device buffer of at least workspace_size
+ * bytes, 256-byte aligned, owned by the caller and kept alive and unmoved
+ * until shampoo_destroy. Enqueues on hip_stream the upload of the block map
+ * and the start state L = R = eps I; the step counter starts at 0 with no
+ * roots. *out receives the handle. */
+int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats, int32_t n_mats,
+                 void* workspace, size_t workspace_bytes, void* hip_stream, shampoo_t* out);
+
+/* One optimizer step (page "Shampoo optimizer", matrix-case loop).
+ * params: host array of n_mats device pointers, updated in place.
+ * grads:  host array of n_mats device pointers, read only.
+ * Packs the gradient blocks, updates L and R, recomputes the roots when the
+ * schedule (or SHAMPOO_FORCE_REFRESH) asks, then applies
+ * W -= lr * L^(-1/4) G R^(-1/4) on every block's real extent.
+ * SHAMPOO_ERR_NO_ROOTS if roots are needed and SHAMPOO_NO_AUTO_REFRESH
+ * forbids computing them. The step counter t is incremented on success. */
+int shampoo_step(shampoo_t h, void* const* params, const void* const* grads, uint32_t flags,
+                 void* hip_stream);
+
+/* Recompute the roots from the current L and R (coupled Newton). */
+int shampoo_refresh_roots(shampoo_t h, void* hip_stream);
+
+/* Release the handle (host memory only; the workspace stays the caller's).
+ * Waits for nothing: the caller must not free the workspace while work that
+ * uses it is still queued. */
+int shampoo_destroy(shampoo_t h);
+
+/* ------------------------------------------------------ inspection hooks */
+int shampoo_state_layout(shampoo_t h, shampoo_layout_t* out);
+int shampoo_get_step(shampoo_t h, int64_t* t_out);
+int shampoo_set_step(shampoo_t h, int64_t t);
+
+/* Pack alone: gather the gradient blocks into grad_packed (zero-padded). */
+int shampoo_pack(shampoo_t h, const void* const* grads, void* hip_stream);
+
+/* Unpack alone: write every block's real extent of grad_packed into dst
+ * (host array of n_mats device pointers, fp32, the registered shapes/ld). */
+int shampoo_unpack(shampoo_t h, void* const* dst, void* hip_stream);
+
+/* Two-sided product alone: out (device, fp32 [B][br][bc]) receives
+ * L^(-1/4) Gp R^(-1/4) of every block from the current packed gradient and
+ * roots; parameters are not touched. */
+int shampoo_precondition(shampoo_t h, void* out, void* hip_stream);
+
+/* Number of factors whose last Newton run diverged (non-finite or growing
+ * residual). Synchronises hip_stream. */
+int shampoo_get_status(shampoo_t h, void* hip_stream, int32_t* n_diverged_out);
+
+/* Kernel timing with HIP events recorded on the stream of each launch (off
+ * by default). Enabling clears the accumulators (the device flop counter is
+ * cleared on hip_stream). shampoo_get_timing waits for the recorded events
+ * and then reads the device flop counter of the Newton products. */
+int shampoo_set_timing(shampoo_t h, int32_t enable, void* hip_stream);
+int shampoo_get_timing(shampoo_t h, shampoo_timing_t* out);
+
+const char* shampoo_status_string(int status);
+const char* shampoo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SHAMPOO_MI355X_H */

@@ -192,8 +192,9 @@ def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
     Stopping: after each iteration the residual r = ||M - I||_F / sqrt(n) is
     compared with tol (stop, keep this X), with the previous residual (no
     decrease: stop, keep the previous X) and with divergence_factor times
-    the previous residual or a non-finite value (diverged: keep the previous
-    X). tol <= 0 runs exactly max_iters iterations, with no early stop.
+    the previous residual (diverged: keep the previous X). tol <= 0 runs
+    exactly max_iters iterations and skips those three tests; in both modes
+    a non-finite residual stops the iteration and keeps the previous X.
     """
     A = np.asarray(A, dtype=np.float64)
     n = A.shape[0]
@@ -209,8 +210,11 @@ def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
         M_new = np.linalg.matrix_power(T, p) @ M
         r = float(np.sqrt(np.sum((M_new - eye) ** 2)) / math.sqrt(n))
         info.residuals.append(r)
+        if not math.isfinite(r):
+            info.status = "diverged"
+            break
         if tol > 0.0:
-            if not math.isfinite(r) or r > divergence_factor * r_prev:
+            if r > divergence_factor * r_prev:
                 info.status = "diverged"
                 break
             if r >= r_prev:
@@ -317,33 +321,49 @@ class ShampooOracle:
             st.XL, st.newton_L = self._root(st.L)
             st.XR, st.newton_R = self._root(st.R)
 
-    def step(self, grads, params, force_refresh=False, auto_refresh=True):
-        """One step. grads/params are lists of full matrices (any float dtype).
+    def step_blocks(self, block_grads, block_params=None, force_refresh=False, auto_refresh=True):
+        """One step on the tracked blocks.
 
-        Returns (new params as fp64 arrays, {block id: U}). Only tracked
-        blocks of the params change.
+        block_grads:  {block id: gradient block (real extent)} for every
+                      tracked block.
+        block_params: optional {block id: parameter block}; when given, each
+                      is moved by -lr * U (and rounded to bfloat16 when the
+                      parameters are bfloat16).
+        Returns ({block id: new parameter block} or None, {block id: U}).
         """
         self.t += 1
-        new_params = [np.array(p, dtype=np.float64) for p in params]
-        blocks_g = {}
+        G = {i: np.asarray(block_grads[i], dtype=np.float64) for i in self.ids}
         for i in self.ids:
-            b = self.table[i]
-            G = np.asarray(grads[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n], dtype=np.float64)
-            blocks_g[i] = G
             st = self.state[i]
-            st.L, st.R = update_statistics(st.L, st.R, G, self.beta2, self.stat_scale)
+            st.L, st.R = update_statistics(st.L, st.R, G[i], self.beta2, self.stat_scale)
         if force_refresh or (auto_refresh and is_refresh_step(self.t, self.root_every)):
             self.refresh_roots()
         updates = {}
         for i in self.ids:
-            b = self.table[i]
             st = self.state[i]
             if st.XL is None:
                 raise RuntimeError("step before any root refresh")
-            U = precondition(st.XL, blocks_g[i], st.XR)
-            updates[i] = U
-            W = new_params[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n] - self.lr * U
-            if self.param_bf16:
-                W = round_to_bf16(W)
-            new_params[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n] = W
+            updates[i] = precondition(st.XL, G[i], st.XR)
+        if block_params is None:
+            return None, updates
+        new = {}
+        for i in self.ids:
+            W = np.asarray(block_params[i], dtype=np.float64) - self.lr * updates[i]
+            new[i] = round_to_bf16(W) if self.param_bf16 else W
+        return new, updates
+
+    def step(self, grads, params, force_refresh=False, auto_refresh=True):
+        """One step over full matrices (lists, any float dtype).
+
+        Returns (new params as fp64 arrays, {block id: U}); only the tracked
+        blocks of the parameters change.
+        """
+        sl = {i: (self.table[i].mat, slice(self.table[i].r0, self.table[i].r0 + self.table[i].m),
+                  slice(self.table[i].c0, self.table[i].c0 + self.table[i].n)) for i in self.ids}
+        gb = {i: grads[m][r, c] for i, (m, r, c) in sl.items()}
+        new_params = [np.array(p, dtype=np.float64) for p in params]
+        wb = {i: new_params[m][r, c] for i, (m, r, c) in sl.items()}
+        new_blocks, updates = self.step_blocks(gb, wb, force_refresh, auto_refresh)
+        for i, (m, r, c) in sl.items():
+            new_params[m][r, c] = new_blocks[i]
         return new_params, updates
