@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the blocked Shampoo step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is the whole optimizer step on one batch of gradients: pack, EMA
+statistics, the coupled-Newton roots when the refresh schedule asks (every
+root_every steps, so K = 20 after W = 10 holds exactly two refreshes), and the
+two-sided apply with the parameter update. Gradients are seeded synthetic
+tensors resident in HBM before the timed region (a few distinct sets, used in
+turn). Prints one JSON line with steps/s, blocks/s, per-kernel-class times
+and TFLOP/s measured with HIP events on the stream the kernels run on, the
+roofline fraction of the dominant kernel (the Newton products) against the
+fp32 MFMA peak, and the fp64 oracle timed on the host cores on a bounded
+sample of blocks.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Shampoo optimizer steps/sec + batched GEMM TFLOP/s vs MFMA peak, 1 GPU"
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+DEFAULT_WORKLOAD = "decoder_1b_b1024_f32"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, grad_sets, budget_s=15.0, max_blocks=32, seed=0):
+    """Time the oracle (as it stands) on a sample of blocks: one refresh step
+    and one non-refresh step per block, extrapolated linearly to all blocks
+    over one root cycle (blocks are independent)."""
+    import numpy as np
+
+    from oracle import ShampooOracle, block_table
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    table = block_table(w.shapes, w.block_rows, w.block_cols)
+    rng = np.random.default_rng(seed)
+    by_shape = {}
+    for b in table:
+        by_shape.setdefault(w.shapes[b.mat], []).append(b.id)
+    order = [int(rng.choice(v)) for v in by_shape.values()]
+    rest = [int(i) for i in rng.permutation(len(table)) if int(i) not in order]
+    order += rest
+    g1, g2 = grad_sets[0], grad_sets[1 % len(grad_sets)]
+    t_ref = t_non = 0.0
+    used = 0
+    start = time.perf_counter()
+    for i in order[:max_blocks]:
+        b = table[i]
+        blk = lambda g: g[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n].float().cpu().numpy()
+        G1, G2 = blk(g1), blk(g2)
+        o = ShampooOracle(w.shapes, w.block_rows, w.block_cols, w.beta2, w.eps, w.lr,
+                          w.root_every, blocks=[i])
+        a = time.perf_counter()
+        o.step_blocks({i: G1})          # t = 1: refresh step
+        bt = time.perf_counter()
+        o.step_blocks({i: G2})          # t = 2: stale roots
+        c = time.perf_counter()
+        t_ref += bt - a
+        t_non += c - bt
+        used += 1
+        if time.perf_counter() - start > budget_s and used >= 4:
+            break
+    k = max(1, w.root_every)
+    per_block_cycle = (t_ref + (k - 1) * t_non) / used
+    steps_per_s = k / (per_block_cycle * len(table))
+    return {
+        "value": steps_per_s, "unit": "steps/s", "cores": cores, "kind": "oracle",
+        "sample": (f"fp64 oracle (numpy/LAPACK, eigh roots) on {used} of {len(table)} blocks "
+                   f"(every matrix shape): one refresh step ({t_ref / used * 1e3:.1f} ms/block) and "
+                   f"one non-refresh step ({t_non / used * 1e3:.1f} ms/block), extrapolated "
+                   f"linearly to all blocks over a {k}-step root cycle"),
+        "blocks_per_s": steps_per_s * len(table),
+        "cpu_seconds": t_ref + t_non,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--grad-sets", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the blocked step shards by blocks with no communication but the parameter "
+              "all-gather, which this build does not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from blocked_shampoo_preconditioning_amd import configs, synth
+    from blocked_shampoo_preconditioning_amd import shampoo as S
+
+    if not os.path.exists(S.LIB_PATH):
+        from blocked_shampoo_preconditioning_amd import build
+        build.build()
+    S.load_library()
+    w = configs.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {w.name}: {len(w.shapes)} matrices, blocks {w.block_rows}x{w.block_cols}")
+    src = synth.GradientSource(w, device=dev)
+    params = src.init_params()
+    n_sets = max(1, min(args.grad_sets, args.steps + args.warmup))
+    grad_sets = [src.grads(t) for t in range(1, n_sets + 1)]
+    sh = S.Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
+                   root_every=w.root_every, newton_max_iters=w.newton_max_iters,
+                   newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype)
+    B = sh.n_blocks
+    log(f"{B} blocks, workspace {sh.workspace.numel() / 2**30:.1f} GiB")
+    for t in range(args.warmup):
+        sh.step(params, grad_sets[t % n_sets])
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    stream = torch.cuda.current_stream()
+    sh.set_timing(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for t in range(args.steps):
+        sh.step(params, grad_sets[(args.warmup + t) % n_sets])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed = e0.elapsed_time(e1) / 1e3
+    tm = sh.timing()
+    sh.set_timing(False)
+    n_div = sh.n_diverged()
+    st, it, _ = sh.newton_info()
+    iters = it.cpu().tolist()
+    log(f"timed {args.steps} steps: {elapsed * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms)")
+
+    steps_per_s = args.steps / elapsed
+    kernels = {}
+    for name, d in tm.items():
+        entry = {"ms": round(d["ms"], 3), "launches": d["launches"]}
+        if d["flops"] > 0 and d["ms"] > 0:
+            tf = d["flops"] / (d["ms"] * 1e-3) / 1e12
+            entry["tflops"] = round(tf, 2)
+            entry["frac_fp32_mfma"] = round(tf / PEAK_FP32_MFMA_TFLOPS, 4)
+        if d["bytes"] > 0 and d["ms"] > 0:
+            gbs = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+            entry["gbs"] = round(gbs, 1)
+            entry["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
+        kernels[name] = entry
+    nw = tm["newton_gemm"]
+    achieved = nw["flops"] / (nw["ms"] * 1e-3) / 1e12 if nw["ms"] > 0 else 0.0
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None,
+        "kernel": "newton_sym_kernel (fp32 MFMA 32x32x2, 128x128 tiles, symmetric outputs)",
+        "launches": nw["launches"],
+        "flops_per_launch": nw["flops"] / max(1, nw["launches"]),
+        "avg_launch_ms": nw["ms"] / max(1, nw["launches"]),
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        cpu = cpu_baseline(w, grad_sets)
+    out = {
+        "metric": METRIC, "value": round(steps_per_s, 4), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 gradients and parameters)",
+        "data": "synthetic (seeded gradients with transformer-layer shapes)",
+        "config": {"workload": w.name, "matrices": len(w.shapes), "blocks": B,
+                   "block": [w.block_rows, w.block_cols], "root_every": w.root_every,
+                   "newton_max_iters": w.newton_max_iters, "newton_tol": w.newton_tol,
+                   "newton_scale_mode": w.newton_scale_mode, "grad_sets": n_sets},
+        "blocks_per_s": round(steps_per_s * B, 1),
+        "gemm_tflops": {k: kernels[k].get("tflops") for k in ("stats", "newton_gemm", "apply")},
+        "kernels": kernels,
+        "newton": {"iters_last_refresh_max": max(iters) if iters else 0,
+                   "iters_last_refresh_min": min(iters) if iters else 0, "n_diverged": n_div},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    sh.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

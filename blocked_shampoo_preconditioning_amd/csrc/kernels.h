@@ -95,7 +95,7 @@ hipError_t launch_unpack(const BlockMeta* blocks, const MatMeta* dst, int32_t B,
                          int32_t bc, const float* Gp, hipStream_t s);
 hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nelemR, int32_t nr,
                              int32_t B, float eps, hipStream_t s);
-hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, hipStream_t s);
+hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, hipStream_t s);
 hipError_t launch_gemm_full(const GemmLaunch& g, int tile, hipStream_t s);
 hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, hipStream_t s);
 hipError_t launch_norms(const float* A, FactorSet fs, NewtonCtl c, hipStream_t s);

@@ -167,7 +167,7 @@ __device__ __forceinline__ int frag_col(int n0, int j) {
 // symmetric. Used by the statistics (EMA epilogue) and the Newton chain.
 // ---------------------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_sym_kernel(GemmLaunch g) {
+__device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   __shared__ float lds[C::LDS_FLOATS];
   __shared__ float red[C::NT / 64];
   const GemmProblem& pb = g.p[blockIdx.y];
@@ -226,9 +226,21 @@ __global__ __launch_bounds__(C::NT) void gemm_sym_kernel(GemmLaunch g) {
   }
 }
 
+// Statistics: L <- beta2 L + g GpT^T GpT, R <- beta2 R + g Gp^T Gp.
+template <class C>
+__global__ __launch_bounds__(C::NT) void syrk_ema_kernel(GemmLaunch g) {
+  sym_product<C>(g);
+}
+
+// One product of the coupled Newton chain (T T, X T, T2 T2 or T4 M).
+template <class C>
+__global__ __launch_bounds__(C::NT) void newton_sym_kernel(GemmLaunch g) {
+  sym_product<C>(g);
+}
+
 // Plain product, every tile, C = acc (first apply product).
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_full_kernel(GemmLaunch g) {
+__global__ __launch_bounds__(C::NT) void apply_left_kernel(GemmLaunch g) {
   __shared__ float lds[C::LDS_FLOATS];
   const GemmProblem& pb = g.p[blockIdx.y];
   const int TM = pb.M / C::BM, TN = pb.N / C::BN;
@@ -265,7 +277,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 // Second apply product with the parameter update in the epilogue:
 // W[r0 + row][c0 + col] -= lr * U[row][col] on the block's real extent.
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_update_kernel(GemmLaunch g, UpdateArgs u) {
+__global__ __launch_bounds__(C::NT) void apply_update_kernel(GemmLaunch g, UpdateArgs u) {
   __shared__ float lds[C::LDS_FLOATS];
   const GemmProblem& pb = g.p[0];
   const int TM = pb.M / C::BM, TN = pb.N / C::BN;
@@ -619,24 +631,23 @@ hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nele
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, hipStream_t s) {
+hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, hipStream_t s) {
   if (g.n_problems == 0) return hipSuccess;
   switch (tile) {
-    case 128: {
-      const int gx = grid_sym<Cfg128>(g);
-      if (gx) hipLaunchKernelGGL(gemm_sym_kernel<Cfg128>, dim3(gx, g.n_problems), dim3(Cfg128::NT), 0, s, g);
-      break;
-    }
-    case 64: {
-      const int gx = grid_sym<Cfg64>(g);
-      if (gx) hipLaunchKernelGGL(gemm_sym_kernel<Cfg64>, dim3(gx, g.n_problems), dim3(Cfg64::NT), 0, s, g);
-      break;
-    }
-    case 32: {
-      const int gx = grid_sym<Cfg32>(g);
-      if (gx) hipLaunchKernelGGL(gemm_sym_kernel<Cfg32>, dim3(gx, g.n_problems), dim3(Cfg32::NT), 0, s, g);
-      break;
-    }
+#define SHP_SYM_CASE(T, CFG)                                                                   \
+  case T: {                                                                                    \
+    const int gx = grid_sym<CFG>(g);                                                           \
+    if (!gx) break;                                                                            \
+    if (newton)                                                                                \
+      hipLaunchKernelGGL(newton_sym_kernel<CFG>, dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g); \
+    else                                                                                       \
+      hipLaunchKernelGGL(syrk_ema_kernel<CFG>, dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g);   \
+    break;                                                                                     \
+  }
+    SHP_SYM_CASE(128, Cfg128)
+    SHP_SYM_CASE(64, Cfg64)
+    SHP_SYM_CASE(32, Cfg32)
+#undef SHP_SYM_CASE
     default:
       return hipErrorInvalidValue;
   }
@@ -648,17 +659,17 @@ hipError_t launch_gemm_full(const GemmLaunch& g, int tile, hipStream_t s) {
   switch (tile) {
     case 128: {
       const int gx = grid_full<Cfg128>(g);
-      if (gx) hipLaunchKernelGGL(gemm_full_kernel<Cfg128>, dim3(gx, g.n_problems), dim3(Cfg128::NT), 0, s, g);
+      if (gx) hipLaunchKernelGGL(apply_left_kernel<Cfg128>, dim3(gx, g.n_problems), dim3(Cfg128::NT), 0, s, g);
       break;
     }
     case 64: {
       const int gx = grid_full<Cfg64>(g);
-      if (gx) hipLaunchKernelGGL(gemm_full_kernel<Cfg64>, dim3(gx, g.n_problems), dim3(Cfg64::NT), 0, s, g);
+      if (gx) hipLaunchKernelGGL(apply_left_kernel<Cfg64>, dim3(gx, g.n_problems), dim3(Cfg64::NT), 0, s, g);
       break;
     }
     case 32: {
       const int gx = grid_full<Cfg32>(g);
-      if (gx) hipLaunchKernelGGL(gemm_full_kernel<Cfg32>, dim3(gx, g.n_problems), dim3(Cfg32::NT), 0, s, g);
+      if (gx) hipLaunchKernelGGL(apply_left_kernel<Cfg32>, dim3(gx, g.n_problems), dim3(Cfg32::NT), 0, s, g);
       break;
     }
     default:
@@ -672,17 +683,17 @@ hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile
   switch (tile) {
     case 128: {
       const int gx = grid_full<Cfg128>(g);
-      if (gx) hipLaunchKernelGGL(gemm_update_kernel<Cfg128>, dim3(gx), dim3(Cfg128::NT), 0, s, g, u);
+      if (gx) hipLaunchKernelGGL(apply_update_kernel<Cfg128>, dim3(gx), dim3(Cfg128::NT), 0, s, g, u);
       break;
     }
     case 64: {
       const int gx = grid_full<Cfg64>(g);
-      if (gx) hipLaunchKernelGGL(gemm_update_kernel<Cfg64>, dim3(gx), dim3(Cfg64::NT), 0, s, g, u);
+      if (gx) hipLaunchKernelGGL(apply_update_kernel<Cfg64>, dim3(gx), dim3(Cfg64::NT), 0, s, g, u);
       break;
     }
     case 32: {
       const int gx = grid_full<Cfg32>(g);
-      if (gx) hipLaunchKernelGGL(gemm_update_kernel<Cfg32>, dim3(gx), dim3(Cfg32::NT), 0, s, g, u);
+      if (gx) hipLaunchKernelGGL(apply_update_kernel<Cfg32>, dim3(gx), dim3(Cfg32::NT), 0, s, g, u);
       break;
     }
     default:

@@ -337,7 +337,7 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
   for (const auto& b : h->blocks) flops += sym_flops(b.m, b.n) + sym_flops(b.n, b.m);
   const double bytes = 4.0 * (double)p.B * (2.0 * p.br * p.bc + 2.0 * (double)p.br * p.br +
                                             2.0 * (double)p.bc * p.bc);
-  return timed(h, kStats, flops, bytes, s, [&] { return shp::launch_gemm_sym(g, p.tile, s); });
+  return timed(h, kStats, flops, bytes, s, [&] { return shp::launch_gemm_sym(g, p.tile, false, s); });
 }
 
 // One batched symmetric product over all factors (left and right problems).
@@ -401,11 +401,11 @@ int do_refresh(shampoo_ctx* h, hipStream_t s) {
     factor_problems(h, g2, T2, T2, T4, false, false, false);            // T4 = T2 T2
     shp::GemmLaunch g3{};
     factor_problems(h, g3, T4, Mk, T2, false, false, true);             // M' = T4 M
-    rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g1, p.tile, s); });
+    rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g1, p.tile, true, s); });
     if (rc) return rc;
-    rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g2, p.tile, s); });
+    rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g2, p.tile, true, s); });
     if (rc) return rc;
-    rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g3, p.tile, s); });
+    rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g3, p.tile, true, s); });
     if (rc) return rc;
     rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] { return shp::launch_newton_check(fs, c, k, s); });
     if (rc) return rc;
