@@ -39,7 +39,7 @@ class Workload:
     diag_fraction: float = 0.0    # fraction of blocks whose gradient is diagonal
     newton_max_iters: int = 25
     newton_tol: float = 1e-6      # <= 0: exactly newton_max_iters iterations
-    newton_scale_mode: int = 1
+    newton_scale_mode: int = 2
     init_std: float = 0.02
     seed: int = 0
     notes: str = field(default="", compare=False)

@@ -23,21 +23,22 @@ struct MatMeta {
   int64_t ld;
 };
 
-// C[m][n] = sum_k P'[k][m] * Q'[k][n] for every element of a batch of
-// independent matrices, all stored row-major and contiguous:
-//   P: K x M (element stride sP between batch members), Q: K x N, C: M x N.
-// P' = pa * P + pd * I (on the k == m diagonal), Q' likewise with qa/qd; the
-// identity shift is what forms T = (5 I - M) / 4 inside the Newton loads.
+// C[m][n] = alpha * sum_k P[k][m] Q[k][n] + beta * D[m][n] + gamma * I[m][n]
+// for every element of a batch of independent matrices, all stored row-major
+// and contiguous: P is K x M (element stride sP between batch members), Q is
+// K x N, C and D are M x N. D may be C itself (the statistics' EMA reads the
+// old value). The Newton products use the affine part to form
+// T = (5 I - M) / 4 without touching the operands:
+//   T T = M M / 16 - 5 M / 8 + 25 I / 16,   X T = 5 X / 4 - X M / 4.
 struct GemmProblem {
   const float* P;
   const float* Q;
   float* C;
-  int64_t sP, sQ, sC;
+  const float* D;
+  int64_t sP, sQ, sC, sD;
   int32_t M, N, K;
   int32_t batch;
-  float pa, pd, qa, qd;
-  // epilogue of symmetric products: C = alpha * acc + beta * C_old
-  float alpha, beta;
+  float alpha, beta, gamma;
   // factors with status[f0 + i] != 0 are skipped (Newton early exit)
   const int32_t* status;
   int32_t f0;
@@ -71,6 +72,10 @@ struct FactorSet {
   int64_t offL, offR;  // element offsets of the first left / right factor
   const int32_t* nreal;
 };
+
+// Power-iteration steps of scale mode 2 (the first shares the norm pass).
+constexpr int kPowerIters = 8;
+constexpr int kMaxSide = 4096;
 
 struct NewtonCtl {
   int32_t* status;

@@ -27,6 +27,9 @@ namespace shp {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+// Native 4-wide vector: HIP's float4 is a union-based struct that the
+// compiler has kept in scratch memory when held in register arrays.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Tile shape: WM x WN waves, each owning FM x FN 32x32 MFMA fragments.
 template <int WM_, int WN_, int FM_, int FN_>
@@ -59,20 +62,14 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   return xcd * per + min(xcd, rem) + idx;
 }
 
-__device__ __forceinline__ float4 shift_diag(float4 x, float a, float d, int k, int m) {
-  // x holds columns m..m+3 of row k: x * a + d on the diagonal
-  x.x = x.x * a + (k == m ? d : 0.f);
-  x.y = x.y * a + (k == m + 1 ? d : 0.f);
-  x.z = x.z * a + (k == m + 2 ? d : 0.f);
-  x.w = x.w * a + (k == m + 3 ? d : 0.f);
-  return x;
-}
-
-// acc[fm][fn] += sum over K of P'[k][m0 + ...] * Q'[k][n0 + ...]
+// acc[fm][fn] = sum over K of P[k][m0 + ...] * Q[k][n0 + ...]
+// Double-buffered LDS: the global loads of K-tile kt+1 are issued before the
+// MFMAs of tile kt and written to the other LDS buffer after them, so their
+// latency hides behind the matrix work. No lambdas here: captured register
+// arrays have been demoted to scratch memory by the compiler.
 template <class C>
 __device__ __forceinline__ void mainloop(const float* __restrict__ P, const float* __restrict__ Q,
-                                         int M, int N, int K, int m0, int n0, float pa, float pd,
-                                         bool tp, float qa, float qd, bool tq,
+                                         int M, int N, int K, int m0, int n0,
                                          floatx16 (&acc)[C::FM][C::FN], float* lds) {
   float* sP = lds;
   float* sQ = lds + 2 * C::BK * C::LDP;
@@ -88,63 +85,65 @@ __device__ __forceinline__ void mainloop(const float* __restrict__ P, const floa
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  float4 pr[C::PPT], qr[C::QPT];
-  auto gload = [&](int k0) {
+  // this thread's float4 slots of a K-tile: global row offset and LDS offset
+  const float* gp = P + m0;
+  const float* gq = Q + n0;
+  const int p_row0 = tid / C::PV, p_c4 = (tid % C::PV) * 4;
+  const int q_row0 = tid / C::QV, q_c4 = (tid % C::QV) * 4;
+  constexpr int P_ROWS = C::NT / C::PV, Q_ROWS = C::NT / C::QV;  // rows per slot step
+  const size_t p_tile = (size_t)C::BK * M, q_tile = (size_t)C::BK * N;
+  gp += (size_t)p_row0 * M + p_c4;
+  gq += (size_t)q_row0 * N + q_c4;
+  const int lp = p_row0 * C::LDP + p_c4, lq = q_row0 * C::LDQ + q_c4;
+
+  f32x4 pr[C::PPT], qr[C::QPT];
 #pragma unroll
-    for (int i = 0; i < C::PPT; ++i) {
-      const int v = tid + i * C::NT;
-      const int row = v / C::PV, c4 = v % C::PV;
-      const int k = k0 + row, m = m0 + c4 * 4;
-      float4 x = *reinterpret_cast<const float4*>(P + (size_t)k * M + m);
-      pr[i] = tp ? shift_diag(x, pa, pd, k, m) : x;
-    }
+  for (int i = 0; i < C::PPT; ++i) pr[i] = *reinterpret_cast<const f32x4*>(gp + (size_t)i * P_ROWS * M);
 #pragma unroll
-    for (int i = 0; i < C::QPT; ++i) {
-      const int v = tid + i * C::NT;
-      const int row = v / C::QV, c4 = v % C::QV;
-      const int k = k0 + row, n = n0 + c4 * 4;
-      float4 x = *reinterpret_cast<const float4*>(Q + (size_t)k * N + n);
-      qr[i] = tq ? shift_diag(x, qa, qd, k, n) : x;
-    }
-  };
-  auto sstore = [&](int buf) {
+  for (int i = 0; i < C::QPT; ++i) qr[i] = *reinterpret_cast<const f32x4*>(gq + (size_t)i * Q_ROWS * N);
 #pragma unroll
-    for (int i = 0; i < C::PPT; ++i) {
-      const int v = tid + i * C::NT;
-      const int row = v / C::PV, c4 = v % C::PV;
-      *reinterpret_cast<float4*>(sP + (buf * C::BK + row) * C::LDP + c4 * 4) = pr[i];
-    }
+  for (int i = 0; i < C::PPT; ++i) *reinterpret_cast<f32x4*>(sP + lp + i * P_ROWS * C::LDP) = pr[i];
 #pragma unroll
-    for (int i = 0; i < C::QPT; ++i) {
-      const int v = tid + i * C::NT;
-      const int row = v / C::QV, c4 = v % C::QV;
-      *reinterpret_cast<float4*>(sQ + (buf * C::BK + row) * C::LDQ + c4 * 4) = qr[i];
-    }
-  };
+  for (int i = 0; i < C::QPT; ++i) *reinterpret_cast<f32x4*>(sQ + lq + i * Q_ROWS * C::LDQ) = qr[i];
+  __syncthreads();
 
   const int nk = K / C::BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * C::BK);
-    const float* p = sP + buf * C::BK * C::LDP + wm * 32 * C::FM + l32;
-    const float* q = sQ + buf * C::BK * C::LDQ + wn * 32 * C::FN + l32;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      gp += p_tile;
+      gq += q_tile;
+#pragma unroll
+      for (int i = 0; i < C::PPT; ++i)
+        pr[i] = *reinterpret_cast<const f32x4*>(gp + (size_t)i * P_ROWS * M);
+#pragma unroll
+      for (int i = 0; i < C::QPT; ++i)
+        qr[i] = *reinterpret_cast<const f32x4*>(gq + (size_t)i * Q_ROWS * N);
+    }
+    const float* p = sP + buf * C::BK * C::LDP + wm * 32 * C::FM + l32 + half * C::LDP;
+    const float* q = sQ + buf * C::BK * C::LDQ + wn * 32 * C::FN + l32 + half * C::LDQ;
 #pragma unroll
     for (int kk = 0; kk < C::BK; kk += 2) {
       float a[C::FM], b[C::FN];
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) a[i] = p[(kk + half) * C::LDP + i * 32];
+      for (int i = 0; i < C::FM; ++i) a[i] = p[kk * C::LDP + i * 32];
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) b[j] = q[(kk + half) * C::LDQ + j * 32];
+      for (int j = 0; j < C::FN; ++j) b[j] = q[kk * C::LDQ + j * 32];
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    if (more) {
+      float* dP = sP + (buf ^ 1) * C::BK * C::LDP + lp;
+      float* dQ = sQ + (buf ^ 1) * C::BK * C::LDQ + lq;
+#pragma unroll
+      for (int i = 0; i < C::PPT; ++i) *reinterpret_cast<f32x4*>(dP + i * P_ROWS * C::LDP) = pr[i];
+#pragma unroll
+      for (int i = 0; i < C::QPT; ++i) *reinterpret_cast<f32x4*>(dQ + i * Q_ROWS * C::LDQ) = qr[i];
+    }
     __syncthreads();
   }
 }
@@ -188,11 +187,11 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const int m0 = ti * C::BM, n0 = tj * C::BN;
 
   floatx16 acc[C::FM][C::FN];
-  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, pb.pa,
-              pb.pd, pb.pa != 1.f || pb.pd != 0.f, pb.qa, pb.qd, pb.qa != 1.f || pb.qd != 0.f, acc,
+  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, acc,
               lds);
 
   float* Cb = pb.C + (size_t)f * pb.sC;
+  const float* Db = pb.D != nullptr ? pb.D + (size_t)f * pb.sD : nullptr;
   const int N = pb.N;
   const bool diag = (ti == tj);
   float rs = 0.f;
@@ -206,7 +205,8 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
         const int row = frag_row<C>(m0, i, r);
         if (diag && row > col) continue;
         float v = pb.alpha * acc[i][j][r];
-        if (pb.beta != 0.f) v += pb.beta * Cb[(size_t)row * N + col];
+        if (Db != nullptr) v += pb.beta * Db[(size_t)row * N + col];
+        if (row == col) v += pb.gamma;
         Cb[(size_t)row * N + col] = v;
         if (row != col) Cb[(size_t)col * N + row] = v;
         const float d = v - (row == col ? 1.f : 0.f);
@@ -251,8 +251,8 @@ __global__ __launch_bounds__(C::NT) void apply_left_kernel(GemmLaunch g) {
   const int tile = logical - f * ntile;
   const int m0 = (tile / TN) * C::BM, n0 = (tile % TN) * C::BN;
   floatx16 acc[C::FM][C::FN];
-  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, 1.f,
-              0.f, false, 1.f, 0.f, false, acc, lds);
+  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, acc,
+              lds);
   float* Cb = pb.C + (size_t)f * pb.sC;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -288,8 +288,8 @@ __global__ __launch_bounds__(C::NT) void apply_update_kernel(GemmLaunch g, Updat
   const int tile = logical - f * ntile;
   const int m0 = (tile / TN) * C::BM, n0 = (tile % TN) * C::BN;
   floatx16 acc[C::FM][C::FN];
-  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, 1.f,
-              0.f, false, 1.f, 0.f, false, acc, lds);
+  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, acc,
+              lds);
   if (u.out_packed != nullptr) {
     float* Ub = u.out_packed + (size_t)f * pb.M * pb.N;
 #pragma unroll
@@ -446,47 +446,100 @@ __device__ __forceinline__ const float* factor_ptr(const float* base, const Fact
 }
 
 // ---------------------------------------------------------------------------
-// Norm scaling: one workgroup per factor, fp64 accumulation in a fixed order.
+// Norm scaling: one workgroup per factor, fixed-order reductions.
+//   mode 0: s = ||A||_F
+//   mode 1: s = min(||A||_F, ||A||_inf) * 2/5
+//   mode 2: s = max(lam / 2, min(||A||_F, ||A||_inf) / 4.5), lam the power
+//           iteration estimate ||A v_k|| of the largest eigenvalue after
+//           kPowerIters products from v_0 = 1 / sqrt(n). lam never exceeds the
+//           largest eigenvalue and both norms bound it from above, so the
+//           spectrum of A / s stays below 4.5, inside the iteration's
+//           convergence region (0, 5).
+// Only the real extent of a factor enters.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
 __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A, FactorSet fs,
                                                     NewtonCtl c) {
-  __shared__ double red_sq[4];
+  __shared__ double red[4];
   __shared__ double red_inf[4];
+  __shared__ float v[kMaxSide];
+  __shared__ float w[kMaxSide];
   const int f = blockIdx.x;
   int n;
   const float* Af = factor_ptr(A, fs, f, n);
   const int nr = fs.nreal[f];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n4 = nr & ~3;
+  // pass 1: squares, absolute row sums and w = A 1 (row sums)
   double sq = 0.0, rowmax = 0.0;
   for (int r = wave; r < nr; r += 4) {
     const float* row = Af + (int64_t)r * n;
-    double as = 0.0;
-    const int n4 = nr & ~3;
+    double as = 0.0, rs = 0.0;
     for (int j = lane * 4; j < n4; j += 256) {
-      const float4 v = *reinterpret_cast<const float4*>(row + j);
-      as += fabs((double)v.x) + fabs((double)v.y) + fabs((double)v.z) + fabs((double)v.w);
-      sq += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+      const float4 x = *reinterpret_cast<const float4*>(row + j);
+      as += fabs((double)x.x) + fabs((double)x.y) + fabs((double)x.z) + fabs((double)x.w);
+      rs += (double)x.x + (double)x.y + (double)x.z + (double)x.w;
+      sq += (double)x.x * x.x + (double)x.y * x.y + (double)x.z * x.z + (double)x.w * x.w;
     }
     for (int j = n4 + lane; j < nr; j += 64) {
-      const double v = row[j];
-      as += fabs(v);
-      sq += v * v;
+      const double x = row[j];
+      as += fabs(x);
+      rs += x;
+      sq += x * x;
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) as += __shfl_xor(as, o);
+    for (int o = 32; o > 0; o >>= 1) {
+      as += __shfl_xor(as, o);
+      rs += __shfl_xor(rs, o);
+    }
     rowmax = fmax(rowmax, as);
+    if (lane == 0 && c.scale_mode == 2) w[r] = (float)rs;
   }
+  if (lane == 0) red_inf[wave] = rowmax;
+  const double fro = sqrt(block_sum(sq, red));
+  const double inf = fmax(fmax(red_inf[0], red_inf[1]), fmax(red_inf[2], red_inf[3]));
+  const double bound = fmin(fro, inf);
+  double s = c.scale_mode == 0 ? fro : bound * 0.4;
+  if (c.scale_mode == 2) {
+    double lam = 0.0;
+    for (int it = 0; it < kPowerIters; ++it) {
+      if (it > 0) {
+        // w = A v
+        for (int r = wave; r < nr; r += 4) {
+          const float* row = Af + (int64_t)r * n;
+          float d = 0.f;
+          for (int j = lane * 4; j < n4; j += 256) {
+            const float4 x = *reinterpret_cast<const float4*>(row + j);
+            d += x.x * v[j] + x.y * v[j + 1] + x.z * v[j + 2] + x.w * v[j + 3];
+          }
+          for (int j = n4 + lane; j < nr; j += 64) d += row[j] * v[j];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o);
-  if (lane == 0) {
-    red_sq[wave] = sq;
-    red_inf[wave] = rowmax;
+          for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
+          if (lane == 0) w[r] = d;
+        }
+      }
+      __syncthreads();
+      double nn = 0.0;
+      for (int r = threadIdx.x; r < nr; r += 256) nn += (double)w[r] * w[r];
+      // v_0 = 1 / sqrt(nr) is folded in: the first product is the row sum
+      nn = block_sum(nn, red) / (it == 0 ? (double)nr : 1.0);
+      lam = sqrt(nn);
+      const float inv = lam > 0.0 ? (float)(1.0 / (lam * (it == 0 ? sqrt((double)nr) : 1.0))) : 0.f;
+      for (int r = threadIdx.x; r < nr; r += 256) v[r] = w[r] * inv;
+      __syncthreads();
+    }
+    s = fmax(lam * 0.5, bound / 4.5);
   }
-  __syncthreads();
   if (threadIdx.x == 0) {
-    const double fro = sqrt(red_sq[0] + red_sq[1] + red_sq[2] + red_sq[3]);
-    const double inf = fmax(fmax(red_inf[0], red_inf[1]), fmax(red_inf[2], red_inf[3]));
-    const double s = c.scale_mode == 0 ? fro : fmin(fro, inf) * 0.4;
     const bool ok = s > 0.0 && isfinite(s) && isfinite(fro);
     c.scale[f] = (float)s;
     c.cfac[f] = ok ? (float)pow(s, -0.25) : 0.f;

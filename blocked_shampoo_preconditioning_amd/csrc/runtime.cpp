@@ -79,8 +79,8 @@ int validate_config(const shampoo_config_t* c) {
     return fail(SHAMPOO_ERR_INVALID_ARG, "newton_max_iters must be in 1..64");
   if (!std::isfinite(c->newton_tol))
     return fail(SHAMPOO_ERR_INVALID_ARG, "newton_tol must be finite");
-  if (c->newton_scale_mode != 0 && c->newton_scale_mode != 1)
-    return fail(SHAMPOO_ERR_UNSUPPORTED, "newton_scale_mode must be 0 or 1");
+  if (c->newton_scale_mode < 0 || c->newton_scale_mode > 2)
+    return fail(SHAMPOO_ERR_UNSUPPORTED, "newton_scale_mode must be 0, 1 or 2");
   if ((c->param_dtype != SHAMPOO_F32 && c->param_dtype != SHAMPOO_BF16) ||
       (c->grad_dtype != SHAMPOO_F32 && c->grad_dtype != SHAMPOO_BF16))
     return fail(SHAMPOO_ERR_UNSUPPORTED, "dtypes must be SHAMPOO_F32 or SHAMPOO_BF16");
@@ -313,10 +313,9 @@ shp::GemmProblem sym_problem(const float* P, const float* Q, float* C, int64_t s
   g.N = n;
   g.K = k;
   g.batch = batch;
-  g.pa = g.qa = 1.f;
-  g.pd = g.qd = 0.f;
   g.alpha = 1.f;
   g.beta = 0.f;
+  g.gamma = 0.f;
   return g;
 }
 
@@ -331,6 +330,8 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
   for (int i = 0; i < 2; ++i) {
     g.p[i].alpha = h->stat_scale;
     g.p[i].beta = (float)h->cfg.beta2;
+    g.p[i].D = g.p[i].C;  // EMA: reads the old statistic in place
+    g.p[i].sD = g.p[i].sC;
   }
   g.n_problems = 2;
   double flops = 0.0;
@@ -340,21 +341,20 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
   return timed(h, kStats, flops, bytes, s, [&] { return shp::launch_gemm_sym(g, p.tile, false, s); });
 }
 
-// One batched symmetric product over all factors (left and right problems).
+// One batched symmetric product over all factors (left and right problems):
+// C = alpha P Q + beta D + gamma I.
 void factor_problems(const shampoo_ctx* h, shp::GemmLaunch& g, const float* P, const float* Q,
-                     float* C, bool tP, bool tQ, bool resid) {
+                     float* C, const float* D, float alpha, float beta, float gamma, bool resid) {
   const Plan& p = h->plan;
   const shp::NewtonCtl c = h->newton_ctl();
-  const bool square = p.br == p.bc;
   auto add = [&](int64_t off, int n, int batch, int f0) {
     shp::GemmProblem q = sym_problem(P + off, Q + off, C + off, (int64_t)n * n, n, n, batch);
-    if (tP) {
-      q.pa = -0.25f;
-      q.pd = 1.25f;
-    }
-    if (tQ) {
-      q.qa = -0.25f;
-      q.qd = 1.25f;
+    q.alpha = alpha;
+    q.beta = beta;
+    q.gamma = gamma;
+    if (D != nullptr) {
+      q.D = D + off;
+      q.sD = (int64_t)n * n;
     }
     q.status = c.status;
     q.f0 = f0;
@@ -364,7 +364,7 @@ void factor_problems(const shampoo_ctx* h, shp::GemmLaunch& g, const float* P, c
     }
     g.p[g.n_problems++] = q;
   };
-  if (square) {
+  if (p.br == p.bc) {
     add(0, p.br, (int)(2 * p.B), 0);
   } else {
     add(0, p.br, (int)p.B, 0);
@@ -394,13 +394,14 @@ int do_refresh(shampoo_ctx* h, hipStream_t s) {
     float* T4 = h->s(2);
     float* Xcur = (k % 2 == 0) ? h->xroot() : h->xalt();
     float* Xnext = (k % 2 == 0) ? h->xalt() : h->xroot();
+    // T = (5 I - M) / 4 enters through the affine epilogue:
     shp::GemmLaunch g1{};
-    factor_problems(h, g1, Mk, Mk, T2, true, true, false);             // T2 = T T
-    if (k > 0) factor_problems(h, g1, Xcur, Mk, Xnext, false, true, false);  // X T
+    factor_problems(h, g1, Mk, Mk, T2, Mk, 0.0625f, -0.625f, 1.5625f, false);  // T2 = T T
+    if (k > 0) factor_problems(h, g1, Xcur, Mk, Xnext, Xcur, -0.25f, 1.25f, 0.f, false);  // X T
     shp::GemmLaunch g2{};
-    factor_problems(h, g2, T2, T2, T4, false, false, false);            // T4 = T2 T2
+    factor_problems(h, g2, T2, T2, T4, nullptr, 1.f, 0.f, 0.f, false);      // T4 = T2 T2
     shp::GemmLaunch g3{};
-    factor_problems(h, g3, T4, Mk, T2, false, false, true);             // M' = T4 M
+    factor_problems(h, g3, T4, Mk, T2, nullptr, 1.f, 0.f, 0.f, true);       // M' = T4 M
     rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g1, p.tile, true, s); });
     if (rc) return rc;
     rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g2, p.tile, true, s); });
@@ -434,7 +435,7 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   a.N = p.br;
   a.K = p.br;
   a.batch = (int)p.B;
-  a.pa = a.qa = a.alpha = 1.f;
+  a.alpha = 1.f;
   g1.p[0] = a;
   g1.n_problems = 1;
   // U[m][n] = sum_k TmpT[k][m] X_R[k][n]   (= X_L Gp X_R, br x bc)
@@ -449,7 +450,7 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   b.N = p.bc;
   b.K = p.bc;
   b.batch = (int)p.B;
-  b.pa = b.qa = b.alpha = 1.f;
+  b.alpha = 1.f;
   g2.p[0] = b;
   g2.n_problems = 1;
   shp::UpdateArgs u{};
@@ -486,7 +487,7 @@ int shampoo_config_default(shampoo_config_t* cfg) {
   cfg->root_every = 10;
   cfg->newton_max_iters = 25;
   cfg->newton_tol = 1e-6;
-  cfg->newton_scale_mode = 1;
+  cfg->newton_scale_mode = 2;
   cfg->param_dtype = SHAMPOO_F32;
   cfg->grad_dtype = SHAMPOO_F32;
   return SHAMPOO_OK;

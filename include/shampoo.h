@@ -90,7 +90,11 @@ typedef struct {
                                      value <= 0 runs exactly newton_max_iters     */
   int32_t newton_scale_mode;      /* 0: s = ||A||_F (spectrum of A/s in (0,1]);
                                      1: s = min(||A||_F, ||A||_inf) * 2/5
-                                        (spectrum in (0, 5/2])                   */
+                                        (spectrum in (0, 5/2]);
+                                     2: s = max(lam/2, min(||A||_F,||A||_inf)/4.5)
+                                        with lam = ||A v_8||, eight power-
+                                        iteration products from v_0 = 1/sqrt(n)
+                                        (spectrum in (0, 4.5), mostly (0, ~2.2]) */
   int32_t param_dtype;            /* shampoo_dtype_t of the parameters           */
   int32_t grad_dtype;             /* shampoo_dtype_t of the gradients            */
 } shampoo_config_t;
@@ -130,7 +134,7 @@ typedef struct shampoo_ctx* shampoo_t;
 
 /* Fill *cfg with the defaults: square blocks of 1024, beta2 0.999,
  * stat_scale 1 - beta2, eps 1e-6, lr 1e-3, root_every 10, 25 Newton
- * iterations at most, tol 1e-6, scale mode 1, fp32 parameters and gradients. */
+ * iterations at most, tol 1e-6, scale mode 2, fp32 parameters and gradients. */
 int shampoo_config_default(shampoo_config_t* cfg);
 
 /* Bytes of device workspace needed for these matrices (host only, no HIP

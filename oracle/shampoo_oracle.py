@@ -154,7 +154,7 @@ def inverse_root_eigh(A, p=4):
     return (Q * lam ** (-1.0 / p)) @ Q.T
 
 
-def newton_scale(A, p=4, mode=1):
+def newton_scale(A, p=4, mode=1, power_iters=8):
     """Norm used to scale A before the coupled Newton iteration.
 
     mode 0: s = ||A||_F, which puts the spectrum of A/s in (0, 1].
@@ -163,14 +163,31 @@ def newton_scale(A, p=4, mode=1):
             largest eigenvalue of a symmetric matrix.
     The DASH page (abstract) stresses that this scaling decides how fast
     Shampoo's root solver converges; the limit reached does not depend on it.
+    mode 2: s = max(lam / 2, min(||A||_F, ||A||_inf) / 4.5), where lam is the
+            power-iteration estimate of the largest eigenvalue: from
+            v_0 = (1, ..., 1) / sqrt(n), repeat w = A v, lam = ||w||, v = w / lam
+            power_iters times. lam never exceeds the largest eigenvalue of a
+            symmetric positive semi-definite A, so the spectrum of A / s stays
+            below 4.5, inside the (0, p + 1) region where the iteration
+            converges.
     """
     A = np.asarray(A, dtype=np.float64)
     fro = math.sqrt(float(np.sum(A * A)))
     if mode == 0:
         return fro
+    inf = float(np.max(np.sum(np.abs(A), axis=1)))
     if mode == 1:
-        inf = float(np.max(np.sum(np.abs(A), axis=1)))
         return min(fro, inf) * 2.0 / (p + 1)
+    if mode == 2:
+        v = np.full(A.shape[0], 1.0 / math.sqrt(A.shape[0]))
+        lam = 0.0
+        for _ in range(power_iters):
+            w = A @ v
+            lam = float(np.sqrt(np.sum(w * w)))
+            if lam == 0.0:
+                break
+            v = w / lam
+        return max(lam / 2.0, min(fro, inf) / 4.5)
     raise ValueError(f"unknown scale mode {mode}")
 
 

@@ -91,6 +91,8 @@ def run_parity(w, steps, ids=None, root_method="eigh", check_update=True, on_ste
     U_out = torch.empty(B * br * bc, dtype=torch.float32, device=dev) if check_update else None
     records = []
     for t in range(1, steps + 1):
+        if on_step is not None:
+            on_step(t - 1, sh, orc, params, None, None, None)
         grads = src.grads(t)
         G = {i: block_of(grads[table[i].mat], table[i]) for i in ids}
         sh.step(params, grads)
@@ -99,6 +101,7 @@ def run_parity(w, steps, ids=None, root_method="eigh", check_update=True, on_ste
         Lg, Rg = sh.stats()
         per = {}
         se = ue = 0.0
+        Ugpu = {}
         if check_update:
             sh.precondition(U_out)
             Ug = U_out.view(B, br, bc)
@@ -107,14 +110,16 @@ def run_parity(w, steps, ids=None, root_method="eigh", check_update=True, on_ste
             st = orc.state[i]
             eL = rel(Lg[i, :b.m, :b.m].cpu().numpy(), st.L)
             eR = rel(Rg[i, :b.n, :b.n].cpu().numpy(), st.R)
-            eU = rel(Ug[i, :b.m, :b.n].cpu().numpy(), U[i]) if check_update else float("nan")
+            if check_update:
+                Ugpu[i] = Ug[i, :b.m, :b.n].cpu().numpy().astype(np.float64)
+            eU = rel(Ugpu[i], U[i]) if check_update else float("nan")
             per[i] = (eL, eR, eU)
             se = max(se, eL, eR)
             if check_update:
                 ue = max(ue, eU)
         records.append(Record(t, se, ue, per))
         if on_step is not None:
-            on_step(t, sh, orc, params, grads)
+            on_step(t, sh, orc, params, grads, U, Ugpu)
         log(f"  {w.name} t={t}: stats {se:.2e} update {ue:.2e}")
     return records, sh, orc, params, W
 

@@ -236,3 +236,80 @@ def test_nan_gradient_block_is_flagged_and_contained():
     st = sh.newton_info()[0].tolist()  # factors: L0, L1, R0, R1
     assert st[1] == 3 and st[3] == 3 and st[0] in (1, 2) and st[2] in (1, 2), st
     sh.close()
+
+
+# ---------------------------------------------------------------------------
+# Norm scaling and the fixed-iteration bf16 workload
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_newton_scale_matches_oracle(mode):
+    """The per-factor scale s of the norms kernel against the oracle's
+    definition evaluated on the oracle's statistics (real extents, tails)."""
+    from oracle import newton_scale
+    w = workload("gpt_small_b256", shapes=((300, 520), (256, 256), (512, 96)), root_every=1,
+                 newton_scale_mode=mode, seed=21)
+    recs, sh, orc, params, W = run_parity(w, 2, check_update=False)
+    _, _, sc = sh.newton_info()
+    sc = sc.cpu().numpy()
+    B = sh.n_blocks
+    for i in range(B):
+        st = orc.state[i]
+        for f, A in ((i, st.L), (B + i, st.R)):
+            ref = newton_scale(A, 4, mode)
+            assert abs(sc[f] - ref) <= 2e-5 * ref, (i, f, sc[f], ref)
+    sh.close()
+
+
+def test_decoder_1b_bf16_fixed_newton_sampled():
+    """bf16 gradients and parameters, fp32 statistics and roots, exactly 10
+    Newton iterations, 10% diagonal blocks. The update is compared with the
+    same fixed-count iteration run in fp64 by the oracle, and the bf16
+    parameters after 10 steps with the oracle's (rounded to bf16 each step)."""
+    from oracle import round_to_bf16
+    w = workload("decoder_1b_b1024_bf16")
+    table = block_table(w.shapes, w.block_rows, w.block_cols)
+    diag = synth.diagonal_blocks(w)
+    diag_ids = sorted(b.id for b in table if (b.mat, b.bi, b.bj) in diag)
+    assert len(diag_ids) == round(0.1 * len(table))
+    ids = sorted(set(sample_blocks(w, 4, seed=6)) | set(diag_ids[:3]))
+    prev = {}
+    counts = {"elements": 0, "one_ulp": 0}
+
+    def check_rounding(t, sh, orc, params, grads, U, Ug):
+        cur = {i: block_of(params[table[i].mat], table[i]) for i in ids}
+        if U is not None:
+            for i in ids:
+                assert np.array_equal(round_to_bf16(cur[i]), cur[i])  # stored as bf16
+                # the step from the GPU's own previous parameters with the
+                # oracle's update, rounded to nearest even in bf16; the GPU
+                # rounds prev - lr * U_gpu computed in fp32, so it may differ by
+                # one ulp plus lr |U_gpu - U| plus the fp32 rounding
+                pred = round_to_bf16(prev[i] - w.lr * U[i])
+                d = np.abs(cur[i] - pred)
+                _, e = np.frexp(np.maximum(np.abs(pred), np.abs(cur[i])))
+                allow = (np.ldexp(1.0, e - 8) + w.lr * np.abs(Ug[i] - U[i])
+                         + 2.0 ** -23 * np.maximum(np.abs(prev[i]), w.lr * np.abs(Ug[i])))
+                assert np.all(d <= allow), (t, i, float((d - allow).max()))
+                counts["elements"] += d.size
+                counts["one_ulp"] += int(np.count_nonzero(d))
+        prev.update(cur)
+
+    recs, sh, orc, params, W = run_parity(w, 10, ids=ids, root_method="newton",
+                                          on_step=check_rounding)
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    frac = counts["one_ulp"] / counts["elements"]
+    log(f"  bf16 parameters that differ from the rounded oracle step: {frac:.2e}")
+    assert frac < 1e-3
+    # cumulative change of the parameters against the oracle's
+    W0 = {i: block_of(synth.GradientSource(w, device="cuda").init_params()[table[i].mat], table[i])
+          for i in ids}
+    for i in ids:
+        dW = rel(block_of(params[table[i].mat], table[i]) - W0[i], W[i] - W0[i])
+        log(f"  block {i}: relative error of the 10-step parameter change {dW:.2e}")
+    for i in diag_ids[:3]:
+        Xl, Xr = sh.roots()
+        X = Xl[i].cpu().numpy()
+        assert np.count_nonzero(X - np.diag(np.diag(X))) == 0  # stays exactly diagonal
+    sh.close()

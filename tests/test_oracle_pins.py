@@ -408,3 +408,24 @@ def test_precondition_is_left_then_right():
     XR = np.array([[5.0, 0.0, 0.0], [0.0, 7.0, 0.0], [0.0, 0.0, 11.0]])
     G = np.ones((2, 3))
     assert np.array_equal(precondition(XL, G, XR), np.outer([2.0, 3.0], [5.0, 7.0, 11.0]))
+
+
+def test_newton_scale_mode2_power_iteration():
+    """Mode 2 on a diagonal matrix: v_k is proportional to A^k 1, so the
+    estimate after k products is ||A^k 1|| / ||A^(k-1) 1|| (closed form)."""
+    a = np.array([3.0, 1.0, 0.5, 2.5, 0.1])
+    A = np.diag(a)
+    k = 8
+    lam = math.sqrt(np.sum(a ** (2 * k))) / math.sqrt(np.sum(a ** (2 * (k - 1))))
+    bound = min(math.sqrt(np.sum(a * a)), a.max())
+    assert newton_scale(A, 4, 2) == pytest.approx(max(lam / 2, bound / 4.5), rel=1e-13)
+    assert lam <= a.max()
+    # random SPD: spectrum of A / s below 4.5, lam from below
+    rng = np.random.default_rng(31)
+    for _ in range(5):
+        B, _, lam_true = spd(40, 1e4, rng)
+        s = newton_scale(B, 4, 2)
+        assert lam_true.max() / s < 4.5
+        assert lam_true.max() / s > 1.5  # the estimate is close to the top eigenvalue
+    X, info = inverse_root_coupled_newton(B, 4, max_iters=60, tol=1e-13, scale_mode=2)
+    assert rel(X, inverse_root_eigh(B)) < 1e-10
