@@ -90,6 +90,23 @@ def cpu_baseline(w, grad_sets, budget_s=15.0, max_blocks=32, seed=0):
     }
 
 
+def newton_traffic(workload):
+    """HBM bytes per Newton-product launch from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source (its
+    SHA-256 is recorded with the counters); None otherwise."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    src = os.path.join(ROOT, "blocked_shampoo_preconditioning_amd", "csrc", "kernels.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return round(rec["kernels"]["newton_sym_kernel"]["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +115,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--grad-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="end with one plain 1 GiB device copy (a known-size kernel that "
+                         "calibrates the HBM traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -168,9 +188,10 @@ def main():
         kernels[name] = entry
     nw = tm["newton_gemm"]
     achieved = nw["flops"] / (nw["ms"] * 1e-3) / 1e12 if nw["ms"] > 0 else 0.0
+    traffic = newton_traffic(w.name)
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": traffic,
         "kernel": "newton_sym_kernel (fp32 MFMA 32x32x2, 128x128 tiles, symmetric outputs)",
         "launches": nw["launches"],
         "flops_per_launch": nw["flops"] / max(1, nw["launches"]),
@@ -199,6 +220,14 @@ def main():
         "cpu_baseline": cpu,
     }
     sh.close()
+    if args.copy_probe:
+        n = 1 << 28  # 1 GiB of fp32
+        src_t = torch.ones(n, dtype=torch.float32, device=dev)
+        dst_t = torch.empty_like(src_t)
+        torch.cuda.synchronize()
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = 4 * n
     print(json.dumps(out), flush=True)
 
 

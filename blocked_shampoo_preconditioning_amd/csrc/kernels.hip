@@ -67,7 +67,9 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 // MFMAs of tile kt and written to the other LDS buffer after them, so their
 // latency hides behind the matrix work. No lambdas here: captured register
 // arrays have been demoted to scratch memory by the compiler.
-template <class C>
+// MASK selects the fragments (bit i * FN + j) whose MFMAs run; the others
+// only take part in the loads and barriers.
+template <class C, int MASK = -1>
 __device__ __forceinline__ void mainloop(const float* __restrict__ P, const float* __restrict__ Q,
                                          int M, int N, int K, int m0, int n0,
                                          floatx16 (&acc)[C::FM][C::FN], float* lds) {
@@ -134,7 +136,8 @@ __device__ __forceinline__ void mainloop(const float* __restrict__ P, const floa
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+          if (MASK & (1 << (i * C::FN + j)))
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     if (more) {
       float* dP = sP + (buf ^ 1) * C::BK * C::LDP + lp;
@@ -146,6 +149,36 @@ __device__ __forceinline__ void mainloop(const float* __restrict__ P, const floa
     }
     __syncthreads();
   }
+}
+
+template <int FM, int FN>
+constexpr int upper_mask() {
+  int m = 0;
+  for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j)
+      if (i <= j) m |= 1 << (i * FN + j);
+  return m;
+}
+
+// Main loop of a symmetric product's tile. On a diagonal tile, fragments
+// strictly below the diagonal are not needed: a wave whose block lies below
+// it runs no MFMA, a wave on it runs the upper fragments only. The choice is
+// made once per wave (the wave index is uniform; readfirstlane tells the
+// compiler so), outside the K loop.
+template <class C>
+__device__ __forceinline__ void mainloop_sym(const float* __restrict__ P,
+                                             const float* __restrict__ Q, int M, int N, int K,
+                                             int m0, int n0, floatx16 (&acc)[C::FM][C::FN],
+                                             float* lds, bool diag) {
+  static_assert(C::FM == C::FN && C::WM == C::WN, "symmetric tiles are square");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % C::WM, wn = wave / C::WM;
+  if (!diag || wm < wn)
+    mainloop<C>(P, Q, M, N, K, m0, n0, acc, lds);
+  else if (wm == wn)
+    mainloop<C, upper_mask<C::FM, C::FN>()>(P, Q, M, N, K, m0, n0, acc, lds);
+  else
+    mainloop<C, 0>(P, Q, M, N, K, m0, n0, acc, lds);
 }
 
 // Row / column of accumulator register r of fragment (i, j).
@@ -186,31 +219,51 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const int tj = ti + t;
   const int m0 = ti * C::BM, n0 = tj * C::BN;
 
+  const bool diag = (ti == tj);
   floatx16 acc[C::FM][C::FN];
-  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, acc,
-              lds);
+  mainloop_sym<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0,
+                  acc, lds, diag);
 
+  // Epilogue: C = alpha acc + beta D + gamma I on and above the diagonal, and
+  // the mirror below it. The four registers 4g..4g+3 of a lane hold four
+  // consecutive rows of one column, i.e. four consecutive columns of the
+  // mirrored row, written as one 16-byte store.
   float* Cb = pb.C + (size_t)f * pb.sC;
   const float* Db = pb.D != nullptr ? pb.D + (size_t)f * pb.sD : nullptr;
   const int N = pb.N;
-  const bool diag = (ti == tj);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % C::WM, wn = wave / C::WM;
   float rs = 0.f;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
+      if (diag && wm * C::FM + i > wn * C::FN + j) continue;  // wave-uniform
       const int col = frag_col<C>(n0, j);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = frag_row<C>(m0, i, r);
-        if (diag && row > col) continue;
-        float v = pb.alpha * acc[i][j][r];
-        if (Db != nullptr) v += pb.beta * Db[(size_t)row * N + col];
-        if (row == col) v += pb.gamma;
-        Cb[(size_t)row * N + col] = v;
-        if (row != col) Cb[(size_t)col * N + row] = v;
-        const float d = v - (row == col ? 1.f : 0.f);
-        rs += (row == col ? 1.f : 2.f) * d * d;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int row0 = frag_row<C>(m0, i, 4 * g4);
+        f32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = row0 + q;
+          float x = pb.alpha * acc[i][j][4 * g4 + q];
+          if (Db != nullptr) x += pb.beta * Db[(size_t)row * N + col];
+          if (row == col) x += pb.gamma;
+          v[q] = x;
+          if (!diag || row <= col) {
+            Cb[(size_t)row * N + col] = x;
+            const float d = x - (row == col ? 1.f : 0.f);
+            rs += (row == col ? 1.f : 2.f) * d * d;
+          }
+        }
+        if (!diag || row0 + 3 < col) {
+          *reinterpret_cast<f32x4*>(Cb + (size_t)col * N + row0) = v;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (row0 + q < col) Cb[(size_t)col * N + row0 + q] = v[q];
+        }
       }
     }
   if (pb.resid != nullptr) {
