@@ -7,8 +7,8 @@ A step is the whole optimizer step on one batch of gradients: pack, EMA
 statistics, the coupled-Newton roots when the refresh schedule asks (every
 root_every steps, so K = 20 after W = 10 holds exactly two refreshes), and the
 two-sided apply with the parameter update. Gradients are seeded synthetic
-tensors resident in HBM before the timed region (a few distinct sets, used in
-turn). Prints one JSON line with steps/s, blocks/s, per-kernel-class times
+tensors resident in HBM before the timed region (by default one distinct
+set per step, as the workload's distribution prescribes). Prints one JSON line with steps/s, blocks/s, per-kernel-class times
 and TFLOP/s measured with HIP events on the stream the kernels run on, the
 roofline fraction of the dominant kernel (the Newton products) against the
 fp32 MFMA peak, and the fp64 oracle timed on the host cores on a bounded
@@ -113,7 +113,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--grad-sets", type=int, default=4)
+    ap.add_argument("--grad-sets", type=int, default=0,
+                    help="distinct gradient sets held in HBM, used in turn (0: one per step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one plain 1 GiB device copy (a known-size kernel that "
@@ -141,7 +142,8 @@ def main():
     log(f"workload {w.name}: {len(w.shapes)} matrices, blocks {w.block_rows}x{w.block_cols}")
     src = synth.GradientSource(w, device=dev)
     params = src.init_params()
-    n_sets = max(1, min(args.grad_sets, args.steps + args.warmup))
+    total = args.steps + args.warmup
+    n_sets = total if args.grad_sets <= 0 else max(1, min(args.grad_sets, total))
     grad_sets = [src.grads(t) for t in range(1, n_sets + 1)]
     sh = S.Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
                    root_every=w.root_every, newton_max_iters=w.newton_max_iters,
@@ -171,6 +173,18 @@ def main():
     n_div = sh.n_diverged()
     st, it, _ = sh.newton_info()
     iters = it.cpu().tolist()
+    status = st.cpu().tolist()
+    resid = sh.newton_residual().cpu()
+    B_ = len(iters) // 2
+    newton_stats = {
+        "status_counts": {name: status.count(code) for code, name in
+                          ((1, "converged"), (2, "stalled"), (3, "diverged"), (4, "capped"))},
+        "iters_left_mean": sum(iters[:B_]) / max(1, B_),
+        "iters_right_mean": sum(iters[B_:]) / max(1, B_),
+        "iters_min": min(iters) if iters else 0, "iters_max": max(iters) if iters else 0,
+        "residual_median": float(resid.median()) if len(resid) else 0.0,
+        "residual_max": float(resid.max()) if len(resid) else 0.0,
+    }
     log(f"timed {args.steps} steps: {elapsed * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms)")
 
     steps_per_s = args.steps / elapsed
@@ -214,8 +228,7 @@ def main():
         "blocks_per_s": round(steps_per_s * B, 1),
         "gemm_tflops": {k: kernels[k].get("tflops") for k in ("stats", "newton_gemm", "apply")},
         "kernels": kernels,
-        "newton": {"iters_last_refresh_max": max(iters) if iters else 0,
-                   "iters_last_refresh_min": min(iters) if iters else 0, "n_diverged": n_div},
+        "newton": dict(newton_stats, n_diverged=n_div),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

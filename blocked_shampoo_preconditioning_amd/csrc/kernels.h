@@ -73,8 +73,8 @@ struct FactorSet {
   const int32_t* nreal;
 };
 
-// Power-iteration steps of scale mode 2 (the first shares the norm pass).
-constexpr int kPowerIters = 8;
+// Power-iteration products of scale mode 2 (the first shares the norm pass).
+constexpr int kPowerIters = 16;
 constexpr int kMaxSide = 4096;
 
 struct NewtonCtl {

@@ -31,14 +31,15 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // compiler has kept in scratch memory when held in register arrays.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Tile shape: WM x WN waves, each owning FM x FN 32x32 MFMA fragments.
-template <int WM_, int WN_, int FM_, int FN_>
+// Tile shape: WM x WN waves, each owning FM x FN 32x32 MFMA fragments; K
+// advances BK at a time.
+template <int WM_, int WN_, int FM_, int FN_, int BK_ = 16>
 struct Cfg {
   static constexpr int WM = WM_, WN = WN_, FM = FM_, FN = FN_;
   static constexpr int NT = 64 * WM * WN;
   static constexpr int BM = 32 * FM * WM;
   static constexpr int BN = 32 * FN * WN;
-  static constexpr int BK = 16;
+  static constexpr int BK = BK_;
   // LDS row pitch: the two half-waves of an operand read rows k and k+1;
   // a pitch of 32 (mod 64) banks keeps them on disjoint banks.
   static constexpr int LDP = BM + ((BM % 64) == 0 ? 32 : 0);
@@ -54,8 +55,9 @@ using Cfg128 = Cfg<2, 2, 2, 2>;  // 128 x 128, 256 threads
 using Cfg64 = Cfg<2, 2, 1, 1>;   //  64 x  64, 256 threads
 using Cfg32 = Cfg<1, 1, 1, 1>;   //  32 x  32,  64 threads
 
-// Workgroups are dispatched round-robin over the 8 XCDs. Give every XCD a
-// contiguous range of logical tiles so the tiles of one matrix share an L2.
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
+// XCD w % 8). xcd_remap gives every XCD a contiguous range of logical tiles so
+// the tiles of one matrix share an L2.
 __device__ __forceinline__ int xcd_remap(int w, int total) {
   const int per = total / 8, rem = total % 8;
   const int xcd = w % 8, idx = w / 8;
@@ -201,15 +203,19 @@ __device__ __forceinline__ int frag_col(int n0, int j) {
 template <class C>
 __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   __shared__ float lds[C::LDS_FLOATS];
-  __shared__ float red[C::NT / 64];
+  float* red = lds;  // residual partials reuse the operand tiles after the K loop
   const GemmProblem& pb = g.p[blockIdx.y];
   const int T = pb.M / C::BM;
   const int ntile = T * (T + 1) / 2;
-  const int total = ntile * pb.batch;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  if (logical >= total) return;
-  const int f = logical / ntile;
-  const int tile = logical - f * ntile;
+  // Matrices are dealt to the XCDs round-robin (matrix f on XCD f % 8) and
+  // each XCD runs the tiles of its matrices one matrix after the other, so an
+  // L2 serves all tiles of a matrix and, when converged factors drop out of a
+  // Newton launch, every XCD keeps its share of the remaining ones.
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int j = idx / ntile;
+  const int tile = idx - j * ntile;
+  const int f = j * 8 + xcd;
+  if (f >= pb.batch) return;
   if (pb.status != nullptr && pb.status[pb.f0 + f] != 0) return;
   int t = tile, ti = 0;
   while (t >= T - ti) {
@@ -281,13 +287,13 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
 
 // Statistics: L <- beta2 L + g GpT^T GpT, R <- beta2 R + g Gp^T Gp.
 template <class C>
-__global__ __launch_bounds__(C::NT) void syrk_ema_kernel(GemmLaunch g) {
+__global__ __launch_bounds__(C::NT, 4) void syrk_ema_kernel(GemmLaunch g) {
   sym_product<C>(g);
 }
 
 // One product of the coupled Newton chain (T T, X T, T2 T2 or T4 M).
 template <class C>
-__global__ __launch_bounds__(C::NT) void newton_sym_kernel(GemmLaunch g) {
+__global__ __launch_bounds__(C::NT, 4) void newton_sym_kernel(GemmLaunch g) {
   sym_product<C>(g);
 }
 
@@ -330,7 +336,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 // Second apply product with the parameter update in the epilogue:
 // W[r0 + row][c0 + col] -= lr * U[row][col] on the block's real extent.
 template <class C>
-__global__ __launch_bounds__(C::NT) void apply_update_kernel(GemmLaunch g, UpdateArgs u) {
+__global__ __launch_bounds__(C::NT, 4) void apply_update_kernel(GemmLaunch g, UpdateArgs u) {
   __shared__ float lds[C::LDS_FLOATS];
   const GemmProblem& pb = g.p[0];
   const int TM = pb.M / C::BM, TN = pb.N / C::BN;
@@ -502,12 +508,13 @@ __device__ __forceinline__ const float* factor_ptr(const float* base, const Fact
 // Norm scaling: one workgroup per factor, fixed-order reductions.
 //   mode 0: s = ||A||_F
 //   mode 1: s = min(||A||_F, ||A||_inf) * 2/5
-//   mode 2: s = max(lam / 2, min(||A||_F, ||A||_inf) / 4.5), lam the power
-//           iteration estimate ||A v_k|| of the largest eigenvalue after
-//           kPowerIters products from v_0 = 1 / sqrt(n). lam never exceeds the
-//           largest eigenvalue and both norms bound it from above, so the
-//           spectrum of A / s stays below 4.5, inside the iteration's
-//           convergence region (0, 5).
+//   mode 2: s = lam / 2, lam the power-iteration estimate ||A v_k|| of the
+//           largest eigenvalue after kPowerIters (16) products from
+//           v_0 = 1 / sqrt(n). For symmetric A the ratios ||A^(j+1) v|| /
+//           ||A^j v|| never decrease, so lam >= lam_max |c_1|^(1/16) with c_1
+//           the component of v_0 on the top eigenvector: the spectrum of A / s
+//           stays inside the iteration's convergence region (0, 5) unless
+//           |c_1| < 4.3e-7. lam = 0 falls back to mode 1.
 // Only the real extent of a factor enters.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double block_sum(double v, double* red) {
@@ -590,7 +597,7 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
       for (int r = threadIdx.x; r < nr; r += 256) v[r] = w[r] * inv;
       __syncthreads();
     }
-    s = fmax(lam * 0.5, bound / 4.5);
+    s = lam > 0.0 ? lam * 0.5 : bound * 0.4;
   }
   if (threadIdx.x == 0) {
     const bool ok = s > 0.0 && isfinite(s) && isfinite(fro);
@@ -694,7 +701,7 @@ int grid_sym(const GemmLaunch& g) {
   int mx = 0;
   for (int i = 0; i < g.n_problems; ++i) {
     const int T = g.p[i].M / C::BM;
-    mx = max(mx, T * (T + 1) / 2 * g.p[i].batch);
+    mx = max(mx, T * (T + 1) / 2 * 8 * ((g.p[i].batch + 7) / 8));
   }
   return mx;
 }

@@ -630,6 +630,7 @@ int shampoo_state_layout(shampoo_t h, shampoo_layout_t* out) {
   out->newton_status = h->plan.off_status;
   out->newton_iters = h->plan.off_final;
   out->newton_scale = h->plan.off_scale;
+  out->newton_residual = h->plan.off_rprev;
   out->workspace_bytes = h->plan.total;
   return SHAMPOO_OK;
 }

@@ -45,7 +45,7 @@ class Config(ctypes.Structure):
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("n_blocks", "grad_packed", "stats", "roots",
                                               "newton_status", "newton_iters", "newton_scale",
-                                              "workspace_bytes")]
+                                              "newton_residual", "workspace_bytes")]
 
 
 class Timing(ctypes.Structure):
@@ -86,11 +86,21 @@ _SIGNATURES = {
 }
 
 
-def load_library(path=LIB_PATH):
-    """Load the HIP library (once). Raises if it has not been built."""
+def load_library(path=None):
+    """Load the HIP library (once). Raises if it has not been built.
+
+    torch is imported first when it is installed: PyTorch-ROCm brings its own
+    HIP runtime, and the library must bind to that one; a second runtime
+    loaded next to it does not see the device.
+    """
     global _lib
     if _lib is not None:
         return _lib
+    path = LIB_PATH if path is None else path
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
                           f"`python -m blocked_shampoo_preconditioning_amd.build`")
@@ -324,3 +334,6 @@ class Shampoo:
         it = self._view(self.layout.newton_iters, 2 * B, self.torch.int32)
         sc = self._view(self.layout.newton_scale, 2 * B, self.torch.float32)
         return st, it, sc
+
+    def newton_residual(self):
+        return self._view(self.layout.newton_residual, 2 * self.n_blocks, self.torch.float32)

@@ -91,10 +91,12 @@ typedef struct {
   int32_t newton_scale_mode;      /* 0: s = ||A||_F (spectrum of A/s in (0,1]);
                                      1: s = min(||A||_F, ||A||_inf) * 2/5
                                         (spectrum in (0, 5/2]);
-                                     2: s = max(lam/2, min(||A||_F,||A||_inf)/4.5)
-                                        with lam = ||A v_8||, eight power-
-                                        iteration products from v_0 = 1/sqrt(n)
-                                        (spectrum in (0, 4.5), mostly (0, ~2.2]) */
+                                     2: s = lam/2 with lam = ||A v_16||, sixteen
+                                        power-iteration products from
+                                        v_0 = 1/sqrt(n) (lam <= lam_max, so the
+                                        spectrum of A/s is in (0, ~2.2] unless v_0
+                                        is almost orthogonal to the top
+                                        eigenvector); lam = 0 falls back to 1     */
   int32_t param_dtype;            /* shampoo_dtype_t of the parameters           */
   int32_t grad_dtype;             /* shampoo_dtype_t of the gradients            */
 } shampoo_config_t;
@@ -114,6 +116,7 @@ typedef struct {
                              3 diverged 4 capped (left factors first)            */
   int64_t newton_iters;   /* int32 [2B]: iterations behind the kept root         */
   int64_t newton_scale;   /* fp32 [2B]: the scale s of the last refresh           */
+  int64_t newton_residual; /* fp32 [2B]: ||M - I||_F / sqrt(n) of the kept iterate  */
   int64_t workspace_bytes;
 } shampoo_layout_t;
 

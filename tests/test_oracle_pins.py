@@ -415,17 +415,20 @@ def test_newton_scale_mode2_power_iteration():
     estimate after k products is ||A^k 1|| / ||A^(k-1) 1|| (closed form)."""
     a = np.array([3.0, 1.0, 0.5, 2.5, 0.1])
     A = np.diag(a)
-    k = 8
+    k = 16
     lam = math.sqrt(np.sum(a ** (2 * k))) / math.sqrt(np.sum(a ** (2 * (k - 1))))
-    bound = min(math.sqrt(np.sum(a * a)), a.max())
-    assert newton_scale(A, 4, 2) == pytest.approx(max(lam / 2, bound / 4.5), rel=1e-13)
+    assert newton_scale(A, 4, 2) == pytest.approx(lam / 2, rel=1e-13)
     assert lam <= a.max()
-    # random SPD: spectrum of A / s below 4.5, lam from below
+    # zero matrix: falls back to the norm bound (0 here)
+    assert newton_scale(np.zeros((3, 3)), 4, 2) == 0.0
+    # random SPD: the estimate is within the bound of the proof and the scaled
+    # spectrum lies inside the convergence region
     rng = np.random.default_rng(31)
     for _ in range(5):
-        B, _, lam_true = spd(40, 1e4, rng)
+        B, Q, lam_true = spd(40, 1e4, rng)
+        c1 = abs(Q[:, 0] @ np.full(40, 1 / math.sqrt(40)))  # top eigenvector first in spd()
         s = newton_scale(B, 4, 2)
-        assert lam_true.max() / s < 4.5
-        assert lam_true.max() / s > 1.5  # the estimate is close to the top eigenvalue
+        assert 2 * s >= lam_true.max() * c1 ** (1 / 16) * (1 - 1e-12)
+        assert 1.0 < lam_true.max() / s < 5.0
     X, info = inverse_root_coupled_newton(B, 4, max_iters=60, tol=1e-13, scale_mode=2)
     assert rel(X, inverse_root_eigh(B)) < 1e-10
