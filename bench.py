@@ -65,7 +65,7 @@ def cpu_baseline(w, grad_sets, budget_s=15.0, max_blocks=32, seed=0):
         blk = lambda g: g[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n].float().cpu().numpy()
         G1, G2 = blk(g1), blk(g2)
         o = ShampooOracle(w.shapes, w.block_rows, w.block_cols, w.beta2, w.eps, w.lr,
-                          w.root_every, blocks=[i])
+                          w.root_every, blocks=[i], momentum=w.momentum)
         a = time.perf_counter()
         o.step_blocks({i: G1})          # t = 1: refresh step
         bt = time.perf_counter()
@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--grad-sets", type=int, default=0,
                     help="distinct gradient sets held in HBM, used in turn (0: one per step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--momentum", type=float, default=None,
+                    help="momentum folded in before preconditioning (default: the workload's, 0)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one plain 1 GiB device copy (a known-size kernel that "
                          "calibrates the HBM traffic counters)")
@@ -137,6 +139,9 @@ def main():
         build.build()
     S.load_library()
     w = configs.get(args.workload)
+    if args.momentum is not None:
+        import dataclasses
+        w = dataclasses.replace(w, momentum=args.momentum)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {w.name}: {len(w.shapes)} matrices, blocks {w.block_rows}x{w.block_cols}")
@@ -147,7 +152,8 @@ def main():
     grad_sets = [src.grads(t) for t in range(1, n_sets + 1)]
     sh = S.Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
                    root_every=w.root_every, newton_max_iters=w.newton_max_iters,
-                   newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype)
+                   newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype,
+                   momentum=w.momentum)
     B = sh.n_blocks
     log(f"{B} blocks, workspace {sh.workspace.numel() / 2**30:.1f} GiB")
     for t in range(args.warmup):
@@ -224,7 +230,8 @@ def main():
         "config": {"workload": w.name, "matrices": len(w.shapes), "blocks": B,
                    "block": [w.block_rows, w.block_cols], "root_every": w.root_every,
                    "newton_max_iters": w.newton_max_iters, "newton_tol": w.newton_tol,
-                   "newton_scale_mode": w.newton_scale_mode, "grad_sets": n_sets},
+                   "newton_scale_mode": w.newton_scale_mode, "momentum": w.momentum,
+                   "grad_sets": n_sets},
         "blocks_per_s": round(steps_per_s * B, 1),
         "gemm_tflops": {k: kernels[k].get("tflops") for k in ("stats", "newton_gemm", "apply")},
         "kernels": kernels,

@@ -94,8 +94,10 @@ struct NewtonCtl {
 };
 
 // ---- launchers (return hipGetLastError()) ----
+// Mom (nullable): momentum buffer [B][br][bc], updated as Mom = momentum * Mom + Gp.
 hipError_t launch_pack(const BlockMeta* blocks, const MatMeta* mats, int32_t B, int32_t br, int32_t bc,
-                       int32_t grad_bf16, float* Gp, float* GpT, hipStream_t s);
+                       int32_t grad_bf16, float* Gp, float* GpT, float* Mom, float momentum,
+                       hipStream_t s);
 hipError_t launch_unpack(const BlockMeta* blocks, const MatMeta* dst, int32_t B, int32_t br,
                          int32_t bc, const float* Gp, hipStream_t s);
 hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nelemR, int32_t nr,

@@ -405,7 +405,8 @@ __device__ __forceinline__ float load1(const void* base, int64_t off, int bf16) 
 __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__ blocks,
                                                    const MatMeta* __restrict__ mats, int br, int bc,
                                                    int bf16, float* __restrict__ Gp,
-                                                   float* __restrict__ GpT) {
+                                                   float* __restrict__ GpT, float* __restrict__ Mom,
+                                                   float momentum) {
   __shared__ float tile[64][65];
   const int b = blockIdx.y;
   const BlockMeta bm = blocks[b];
@@ -433,8 +434,18 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
         if (pc + 3 < bm.n) v.w = load1(mm.grad, off + 3, bf16);
       }
     }
-    if (pr < br && pc < bc)
-      *reinterpret_cast<float4*>(Gp + ((size_t)b * br + pr) * bc + pc) = v;
+    if (pr < br && pc < bc) {
+      const size_t o = ((size_t)b * br + pr) * bc + pc;
+      *reinterpret_cast<float4*>(Gp + o) = v;
+      if (Mom != nullptr) {  // momentum folded in before preconditioning
+        float4 m = *reinterpret_cast<const float4*>(Mom + o);
+        m.x = momentum * m.x + v.x;
+        m.y = momentum * m.y + v.y;
+        m.z = momentum * m.z + v.z;
+        m.w = momentum * m.w + v.w;
+        *reinterpret_cast<float4*>(Mom + o) = m;
+      }
+    }
     tile[row][c] = v.x;
     tile[row][c + 1] = v.y;
     tile[row][c + 2] = v.z;
@@ -719,10 +730,12 @@ int grid_full(const GemmLaunch& g) {
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_pack(const BlockMeta* blocks, const MatMeta* mats, int32_t B, int32_t br,
-                       int32_t bc, int32_t grad_bf16, float* Gp, float* GpT, hipStream_t s) {
+                       int32_t bc, int32_t grad_bf16, float* Gp, float* GpT, float* Mom,
+                       float momentum, hipStream_t s) {
   if (B == 0) return hipSuccess;
   dim3 grid(((br + 63) / 64) * ((bc + 63) / 64), B);
-  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, blocks, mats, br, bc, grad_bf16, Gp, GpT);
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, blocks, mats, br, bc, grad_bf16, Gp, GpT,
+                     Mom, momentum);
   return hipGetLastError();
 }
 

@@ -57,8 +57,9 @@ struct Plan {
   int ntiles_l = 0, ntiles_r = 0, resid_stride = 0;
   int64_t fl = 0, fr = 0;  // elements of all left / right factors
   int64_t off_blocks, off_mats, off_umats, off_nreal, off_status, off_final, off_scale, off_rprev,
-      off_cfac, off_active, off_flops, off_resid, off_gp, off_lr, off_xroot, off_xalt, off_s0,
-      off_s1, off_s2, total;
+      off_cfac, off_active, off_flops, off_resid, off_gp, off_mom, off_lr, off_xroot, off_xalt,
+      off_s0, off_s1, off_s2, total;
+  bool momentum = false;
 };
 
 int validate_config(const shampoo_config_t* c) {
@@ -81,6 +82,8 @@ int validate_config(const shampoo_config_t* c) {
     return fail(SHAMPOO_ERR_INVALID_ARG, "newton_tol must be finite");
   if (c->newton_scale_mode < 0 || c->newton_scale_mode > 2)
     return fail(SHAMPOO_ERR_UNSUPPORTED, "newton_scale_mode must be 0, 1 or 2");
+  if (!std::isfinite(c->momentum) || c->momentum < 0.0 || c->momentum >= 1.0)
+    return fail(SHAMPOO_ERR_INVALID_ARG, "momentum must be in [0, 1)");
   if ((c->param_dtype != SHAMPOO_F32 && c->param_dtype != SHAMPOO_BF16) ||
       (c->grad_dtype != SHAMPOO_F32 && c->grad_dtype != SHAMPOO_BF16))
     return fail(SHAMPOO_ERR_UNSUPPORTED, "dtypes must be SHAMPOO_F32 or SHAMPOO_BF16");
@@ -133,6 +136,8 @@ Plan make_plan(const shampoo_config_t* c, const shampoo_matrix_desc_t* m, int32_
   p.off_flops = take(8);
   p.off_resid = take(2 * p.B * p.resid_stride * 4);
   p.off_gp = take(p.B * p.br * p.bc * 4);
+  p.momentum = c->momentum > 0.0;
+  p.off_mom = p.momentum ? take(p.B * p.br * p.bc * 4) : -1;
   p.off_lr = take(fbytes);
   p.off_xroot = take(fbytes);
   p.off_xalt = take(fbytes);
@@ -174,6 +179,7 @@ struct shampoo_ctx {
   template <class T>
   T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
   float* gp() const { return at<float>(plan.off_gp); }
+  float* mom() const { return plan.momentum ? at<float>(plan.off_mom) : nullptr; }
   float* lr() const { return at<float>(plan.off_lr); }
   float* xroot() const { return at<float>(plan.off_xroot); }
   float* xalt() const { return at<float>(plan.off_xalt); }
@@ -292,11 +298,11 @@ int do_pack(shampoo_ctx* h, hipStream_t s) {
   double real = 0.0;
   for (const auto& b : h->blocks) real += (double)b.m * b.n;
   const double esz = h->cfg.grad_dtype == SHAMPOO_BF16 ? 2.0 : 4.0;
-  const double bytes = real * esz + 2.0 * 4.0 * (double)p.B * p.br * p.bc;
+  const double bytes = real * esz + (p.momentum ? 4.0 : 2.0) * 4.0 * (double)p.B * p.br * p.bc;
   return timed(h, kPack, 0.0, bytes, s, [&] {
     return shp::launch_pack(h->at<shp::BlockMeta>(p.off_blocks), h->at<shp::MatMeta>(p.off_mats),
                             (int32_t)p.B, p.br, p.bc, h->cfg.grad_dtype == SHAMPOO_BF16, h->gp(),
-                            h->gpT(), s);
+                            h->gpT(), h->mom(), (float)h->cfg.momentum, s);
   });
 }
 
@@ -422,10 +428,11 @@ int do_refresh(shampoo_ctx* h, hipStream_t s) {
 int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   const Plan& p = h->plan;
   if (p.B == 0) return SHAMPOO_OK;
-  // TmpT[m][n] = sum_k Gp[k][m] X_L[k][n]   (= (X_L Gp)^T, bc x br)
+  // TmpT[m][n] = sum_k Gp[k][m] X_L[k][n]   (= (X_L Gp)^T, bc x br); with
+  // momentum the preconditioned matrix is the momentum buffer
   shp::GemmLaunch g1{};
   shp::GemmProblem a{};
-  a.P = h->gp();
+  a.P = p.momentum ? h->mom() : h->gp();
   a.sP = (int64_t)p.br * p.bc;
   a.Q = h->xroot();
   a.sQ = (int64_t)p.br * p.br;
@@ -490,6 +497,7 @@ int shampoo_config_default(shampoo_config_t* cfg) {
   cfg->newton_scale_mode = 2;
   cfg->param_dtype = SHAMPOO_F32;
   cfg->grad_dtype = SHAMPOO_F32;
+  cfg->momentum = 0.0;
   return SHAMPOO_OK;
 }
 
@@ -566,6 +574,8 @@ int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats,
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(plan.off_final), 0, 2 * plan.B * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(plan.off_scale), 0, 2 * plan.B * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(plan.off_flops), 0, 8, s);
+    if (e == hipSuccess && plan.momentum)
+      e = hipMemsetAsync(h->at<void>(plan.off_mom), 0, plan.B * plan.br * plan.bc * 4, s);
     if (e == hipSuccess)
       e = shp::launch_init_state(h->lr(), plan.fl, plan.br, plan.fr, plan.bc, (int32_t)plan.B,
                                  (float)cfg->eps, s);
@@ -631,6 +641,7 @@ int shampoo_state_layout(shampoo_t h, shampoo_layout_t* out) {
   out->newton_iters = h->plan.off_final;
   out->newton_scale = h->plan.off_scale;
   out->newton_residual = h->plan.off_rprev;
+  out->momentum = h->plan.off_mom;
   out->workspace_bytes = h->plan.total;
   return SHAMPOO_OK;
 }

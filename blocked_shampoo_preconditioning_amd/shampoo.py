@@ -39,13 +39,14 @@ class Config(ctypes.Structure):
                 ("eps", ctypes.c_double), ("lr", ctypes.c_double),
                 ("root_every", ctypes.c_int32), ("newton_max_iters", ctypes.c_int32),
                 ("newton_tol", ctypes.c_double), ("newton_scale_mode", ctypes.c_int32),
-                ("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32)]
+                ("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+                ("momentum", ctypes.c_double)]
 
 
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("n_blocks", "grad_packed", "stats", "roots",
                                               "newton_status", "newton_iters", "newton_scale",
-                                              "newton_residual", "workspace_bytes")]
+                                              "newton_residual", "momentum", "workspace_bytes")]
 
 
 class Timing(ctypes.Structure):
@@ -233,7 +234,7 @@ class Shampoo:
 
     def __init__(self, shapes, block_rows=1024, block_cols=1024, beta2=0.999, eps=1e-6, lr=1e-3,
                  root_every=10, stat_scale=None, newton_max_iters=25, newton_tol=1e-6,
-                 newton_scale_mode=1, dtype="f32", device="cuda", lds=None):
+                 newton_scale_mode=2, dtype="f32", device="cuda", lds=None, momentum=0.0):
         import torch
         self.torch = torch
         self.shapes = [tuple(int(v) for v in s) for s in shapes]
@@ -245,6 +246,7 @@ class Shampoo:
         cfg.root_every = root_every
         cfg.newton_max_iters, cfg.newton_tol = newton_max_iters, newton_tol
         cfg.newton_scale_mode = newton_scale_mode
+        cfg.momentum = momentum
         dt = {"f32": SHAMPOO_F32, "bf16": SHAMPOO_BF16}[dtype]
         cfg.param_dtype = cfg.grad_dtype = dt
         self.cfg = cfg
@@ -324,6 +326,12 @@ class Shampoo:
 
     def stats(self):
         return self._factors(self.layout.stats)
+
+    def momentum_buffer(self):
+        if self.layout.momentum < 0:
+            return None
+        B, br, bc = self.n_blocks, self.cfg.block_rows, self.cfg.block_cols
+        return self._view(self.layout.momentum, B * br * bc, self.torch.float32).view(B, br, bc)
 
     def roots(self):
         return self._factors(self.layout.roots)

@@ -99,6 +99,10 @@ typedef struct {
                                         eigenvector); lam = 0 falls back to 1     */
   int32_t param_dtype;            /* shampoo_dtype_t of the parameters           */
   int32_t grad_dtype;             /* shampoo_dtype_t of the gradients            */
+  double momentum;                /* alpha of ordinary momentum folded in before
+                                     preconditioning (podcast cue 28):
+                                     m = alpha m + G, W -= lr L^(-1/4) m R^(-1/4);
+                                     statistics use the raw G. 0 = off (default) */
 } shampoo_config_t;
 
 /* Byte offsets of the state inside the caller's workspace (for inspection
@@ -117,6 +121,7 @@ typedef struct {
   int64_t newton_iters;   /* int32 [2B]: iterations behind the kept root         */
   int64_t newton_scale;   /* fp32 [2B]: the scale s of the last refresh           */
   int64_t newton_residual; /* fp32 [2B]: ||M - I||_F / sqrt(n) of the kept iterate  */
+  int64_t momentum;       /* fp32 [B][br][bc] momentum, or -1 when it is off         */
   int64_t workspace_bytes;
 } shampoo_layout_t;
 
@@ -137,7 +142,8 @@ typedef struct shampoo_ctx* shampoo_t;
 
 /* Fill *cfg with the defaults: square blocks of 1024, beta2 0.999,
  * stat_scale 1 - beta2, eps 1e-6, lr 1e-3, root_every 10, 25 Newton
- * iterations at most, tol 1e-6, scale mode 2, fp32 parameters and gradients. */
+ * iterations at most, tol 1e-6, scale mode 2, fp32 parameters and gradients,
+ * no momentum. */
 int shampoo_config_default(shampoo_config_t* cfg);
 
 /* Bytes of device workspace needed for these matrices (host only, no HIP
@@ -185,8 +191,9 @@ int shampoo_pack(shampoo_t h, const void* const* grads, void* hip_stream);
 int shampoo_unpack(shampoo_t h, void* const* dst, void* hip_stream);
 
 /* Two-sided product alone: out (device, fp32 [B][br][bc]) receives
- * L^(-1/4) Gp R^(-1/4) of every block from the current packed gradient and
- * roots; parameters are not touched. */
+ * L^(-1/4) Gp R^(-1/4) of every block from the current packed gradient (the
+ * momentum buffer when momentum is on) and roots; parameters are not
+ * touched. */
 int shampoo_precondition(shampoo_t h, void* out, void* hip_stream);
 
 /* Number of factors whose last Newton run diverged (non-finite or growing

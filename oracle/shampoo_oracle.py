@@ -24,6 +24,10 @@ What it computes, and where the pages define it:
 * Roots are recomputed only every k steps and reused in between (podcast
   cue 28). Reading taken: the first step always computes roots, so refresh
   happens at steps t = 1, 1 + k, 1 + 2k, ...
+* Optional momentum (podcast cue 28: ordinary momentum, alpha = 0.9, folded in
+  before preconditioning). Reading taken: m_t = alpha m_{t-1} + G_t per block,
+  statistics still accumulate the raw G_t, and the update is
+  -lr L^(-1/4) m_t R^(-1/4).
 * Gradients are cut into blocks that are stacked into a batch (DASH page,
   abstract). Reading taken: blocks of block_rows x block_cols in row-major
   block order inside a matrix, matrices in registration order; a tail block
@@ -281,6 +285,7 @@ class _BlockState:
     R: np.ndarray
     XL: np.ndarray | None = None
     XR: np.ndarray | None = None
+    mom: np.ndarray | None = None
     newton_L: NewtonInfo | None = None
     newton_R: NewtonInfo | None = None
 
@@ -300,11 +305,13 @@ class ShampooOracle:
     root_method:  "eigh" (the definition) or "newton" (the iteration, with
                   newton_iters / newton_tol / newton_scale_mode).
     param_bf16:   parameters are stored in bfloat16 after every update.
+    momentum:     alpha of the momentum folded in before preconditioning
+                  (0: none).
     """
 
     def __init__(self, shapes, block_rows, block_cols, beta2, eps, lr, root_every,
                  stat_scale=None, blocks=None, root_method="eigh", newton_iters=25,
-                 newton_tol=0.0, newton_scale_mode=1, param_bf16=False, p=4):
+                 newton_tol=0.0, newton_scale_mode=1, param_bf16=False, p=4, momentum=0.0):
         self.shapes = [tuple(s) for s in shapes]
         self.table = block_table(self.shapes, block_rows, block_cols)
         self.ids = list(range(len(self.table))) if blocks is None else sorted(set(blocks))
@@ -319,11 +326,13 @@ class ShampooOracle:
         self.newton_scale_mode = newton_scale_mode
         self.param_bf16 = param_bf16
         self.p = p
+        self.momentum = float(momentum)
         self.t = 0
         self.state = {}
         for i in self.ids:
             b = self.table[i]
-            self.state[i] = _BlockState(self.eps * np.eye(b.m), self.eps * np.eye(b.n))
+            self.state[i] = _BlockState(self.eps * np.eye(b.m), self.eps * np.eye(b.n),
+                                        mom=np.zeros((b.m, b.n)))
 
     def _root(self, A):
         if self.root_method == "eigh":
@@ -361,7 +370,11 @@ class ShampooOracle:
             st = self.state[i]
             if st.XL is None:
                 raise RuntimeError("step before any root refresh")
-            updates[i] = precondition(st.XL, G[i], st.XR)
+            D = G[i]
+            if self.momentum != 0.0:
+                st.mom = self.momentum * st.mom + G[i]
+                D = st.mom
+            updates[i] = precondition(st.XL, D, st.XR)
         if block_params is None:
             return None, updates
         new = {}

@@ -313,3 +313,32 @@ def test_decoder_1b_bf16_fixed_newton_sampled():
         X = Xl[i].cpu().numpy()
         assert np.count_nonzero(X - np.diag(np.diag(X))) == 0  # stays exactly diagonal
     sh.close()
+
+
+# ---------------------------------------------------------------------------
+# Momentum folded in before preconditioning (podcast cue 28)
+# ---------------------------------------------------------------------------
+def test_momentum_small_ragged_every_block():
+    w = workload("gpt_small_b256", shapes=((300, 520), (256, 256), (130, 71)), root_every=3,
+                 momentum=0.9, seed=88)
+    recs, sh, orc, params, W = run_parity(w, 7)
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    # the momentum buffer itself against the oracle's, every block
+    Mg = sh.momentum_buffer()
+    table = block_table(w.shapes, w.block_rows, w.block_cols)
+    for b in table:
+        assert rel(Mg[b.id, :b.m, :b.n].cpu().numpy(), orc.state[b.id].mom) <= 1e-6
+        assert torch.count_nonzero(Mg[b.id, b.m:, :]) == 0 and torch.count_nonzero(Mg[b.id, :, b.n:]) == 0
+    sh.close()
+
+
+def test_momentum_decoder_1b_sampled():
+    w = workload("decoder_1b_b1024_f32", momentum=0.9)
+    ids = sample_blocks(w, 5, seed=9)
+    recs, sh, orc, params, W = run_parity(w, 10, ids=ids)
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    sh.close()

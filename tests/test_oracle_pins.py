@@ -432,3 +432,37 @@ def test_newton_scale_mode2_power_iteration():
         assert 1.0 < lam_true.max() / s < 5.0
     X, info = inverse_root_coupled_newton(B, 4, max_iters=60, tol=1e-13, scale_mode=2)
     assert rel(X, inverse_root_eigh(B)) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# Momentum before preconditioning (podcast cue 28)
+# ---------------------------------------------------------------------------
+def test_momentum_constant_gradient_closed_form():
+    """Constant gradient, roots frozen after step 1: the momentum after t steps
+    is G (1 - a^t) / (1 - a), so U_t = (1 - a^t) / (1 - a) U_1."""
+    rng = np.random.default_rng(41)
+    G = rng.standard_normal((5, 3))
+    a = 0.9
+    _, _, Us = run_oracle([G] * 6, np.zeros((5, 3)), 0.99, 1e-3, 1e-2, root_every=100, momentum=a)
+    for t, U in enumerate(Us, start=1):
+        assert rel(U, (1 - a ** t) / (1 - a) * Us[0]) < 1e-13
+
+
+def test_momentum_is_linear_sum_of_past_updates():
+    """With frozen roots the preconditioner is linear: U_t = sum_s a^(t-s) P(G_s)
+    where P is the plain (momentum-free) update with the same roots."""
+    rng = np.random.default_rng(43)
+    Gs = [rng.standard_normal((4, 6)) for _ in range(5)]
+    a = 0.9
+    _, _, Um = run_oracle(Gs, np.zeros((4, 6)), 0.95, 1e-2, 1e-3, root_every=100, momentum=a)
+    # momentum-free run with the same statistics gives the same roots (k = 100)
+    o, _, _ = run_oracle(Gs[:1], np.zeros((4, 6)), 0.95, 1e-2, 1e-3, root_every=100)
+    XL, XR = o.state[0].XL, o.state[0].XR
+    for t in range(5):
+        ref = sum(a ** (t - s) * XL @ Gs[s] @ XR for s in range(t + 1))
+        assert rel(Um[t], ref) < 1e-12
+    # momentum 0 is the plain method
+    _, _, U0 = run_oracle(Gs, np.zeros((4, 6)), 0.95, 1e-2, 1e-3, root_every=1, momentum=0.0)
+    _, _, Up = run_oracle(Gs, np.zeros((4, 6)), 0.95, 1e-2, 1e-3, root_every=1)
+    for u, v in zip(U0, Up):
+        assert np.array_equal(u, v)
