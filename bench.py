@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--momentum", type=float, default=None,
                     help="momentum folded in before preconditioning (default: the workload's, 0)")
+    ap.add_argument("--root-method", default=None, choices=("newton", "newton_db"),
+                    help="inverse-root solver (default: the workload's, coupled Newton)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one plain 1 GiB device copy (a known-size kernel that "
                          "calibrates the HBM traffic counters)")
@@ -139,9 +141,11 @@ def main():
         build.build()
     S.load_library()
     w = configs.get(args.workload)
+    import dataclasses
     if args.momentum is not None:
-        import dataclasses
         w = dataclasses.replace(w, momentum=args.momentum)
+    if args.root_method is not None:
+        w = dataclasses.replace(w, root_method=args.root_method)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {w.name}: {len(w.shapes)} matrices, blocks {w.block_rows}x{w.block_cols}")
@@ -153,7 +157,7 @@ def main():
     sh = S.Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
                    root_every=w.root_every, newton_max_iters=w.newton_max_iters,
                    newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype,
-                   momentum=w.momentum)
+                   momentum=w.momentum, root_method=w.root_method)
     B = sh.n_blocks
     log(f"{B} blocks, workspace {sh.workspace.numel() / 2**30:.1f} GiB")
     for t in range(args.warmup):
@@ -212,7 +216,8 @@ def main():
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": traffic,
-        "kernel": "newton_sym_kernel (fp32 MFMA 32x32x2, 128x128 tiles, symmetric outputs)",
+        "kernel": "newton_sym_kernel (fp32 MFMA 32x32x2, 128x128 tiles, symmetric outputs; "
+                  f"{w.root_method} root products)",
         "launches": nw["launches"],
         "flops_per_launch": nw["flops"] / max(1, nw["launches"]),
         "avg_launch_ms": nw["ms"] / max(1, nw["launches"]),
@@ -231,6 +236,7 @@ def main():
                    "block": [w.block_rows, w.block_cols], "root_every": w.root_every,
                    "newton_max_iters": w.newton_max_iters, "newton_tol": w.newton_tol,
                    "newton_scale_mode": w.newton_scale_mode, "momentum": w.momentum,
+                   "root_method": w.root_method,
                    "grad_sets": n_sets},
         "blocks_per_s": round(steps_per_s * B, 1),
         "gemm_tflops": {k: kernels[k].get("tflops") for k in ("stats", "newton_gemm", "apply")},

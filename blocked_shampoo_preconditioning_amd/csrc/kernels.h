@@ -77,7 +77,13 @@ struct FactorSet {
 constexpr int kPowerIters = 16;
 constexpr int kMaxSide = 4096;
 
+enum RootSolver { kCoupledNewton = 0, kNewtonDB = 1 };
+
+// A residual that grows from below this value is the fp32 floor, not divergence.
+constexpr float kFloorGuard = 1e-3f;
+
 struct NewtonCtl {
+  int32_t solver;       // RootSolver
   int32_t* status;
   int32_t* final_iter;
   float* scale;
@@ -108,9 +114,20 @@ hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile
 hipError_t launch_norms(const float* A, FactorSet fs, NewtonCtl c, hipStream_t s);
 hipError_t launch_newton_init(const float* A, float* M0, float* X1, FactorSet fs, NewtonCtl c,
                               hipStream_t s);
-hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, hipStream_t s);
+// shift: the residual just computed belongs to iterate iter + shift (1 for
+// coupled Newton, whose products first make the next iterate; 0 for the
+// Denman-Beavers pair, whose residual product comes first). prod_before /
+// prod_after: symmetric products per factor launched before the check (all
+// factors entering it) and after it (those still running), for the flop count.
+hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, int32_t shift,
+                               int32_t prod_before, int32_t prod_after, hipStream_t s);
+// scale: multiply the kept iterate by s^(-1/4) (Denman-Beavers result).
 hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, NewtonCtl c,
-                               hipStream_t s);
+                               int32_t scale, hipStream_t s);
+// Between the two Denman-Beavers stages: Y1 (kept pair of stage 1, in Ybuf0 or
+// Ybuf1 by parity) becomes stage 2's Y0 in Ybuf0, Z0 = I goes to Z0buf.
+hipError_t launch_db_stage2_init(float* Ybuf0, const float* Ybuf1, float* Z0buf, FactorSet fs,
+                                 NewtonCtl c, hipStream_t s);
 
 // Tiles written by a symmetric product of side n with square tile t.
 inline int32_t sym_tiles(int32_t n, int32_t t) {

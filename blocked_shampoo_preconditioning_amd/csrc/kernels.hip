@@ -579,7 +579,9 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   const double fro = sqrt(block_sum(sq, red));
   const double inf = fmax(fmax(red_inf[0], red_inf[1]), fmax(red_inf[2], red_inf[3]));
   const double bound = fmin(fro, inf);
-  double s = c.scale_mode == 0 ? fro : bound * 0.4;
+  // spectral target: Newton converges on (0, 5), the Denman-Beavers pair on (0, 2)
+  const bool db = c.solver == kNewtonDB;
+  double s = c.scale_mode == 0 ? fro : bound * (db ? 1.0 : 0.4);
   if (c.scale_mode == 2) {
     double lam = 0.0;
     for (int it = 0; it < kPowerIters; ++it) {
@@ -608,7 +610,7 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
       for (int r = threadIdx.x; r < nr; r += 256) v[r] = w[r] * inv;
       __syncthreads();
     }
-    s = lam > 0.0 ? lam * 0.5 : bound * 0.4;
+    s = lam > 0.0 ? lam * (db ? 1.0 : 0.5) : bound * (db ? 1.0 : 0.4);
   }
   if (threadIdx.x == 0) {
     const bool ok = s > 0.0 && isfinite(s) && isfinite(fro);
@@ -620,7 +622,9 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   }
 }
 
-// M0 = A / s (identity on the padded part), X1 = s^(-1/4) (5 I - M0) / 4.
+// Coupled Newton: M0 = A / s (identity on the padded part) and
+// X1 = s^(-1/4) (5 I - M0) / 4. Denman-Beavers: Y0 = A / s (into M0) and Z0 = I
+// (into X1).
 __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restrict__ A,
                                                           float* __restrict__ M0,
                                                           float* __restrict__ X1, FactorSet fs,
@@ -639,7 +643,7 @@ __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restric
     const float id = (r == col) ? 1.f : 0.f;
     const float m = (r < nr && col < nr) ? Af[e] / s : id;
     M0[base + e] = m;
-    X1[base + e] = cf * (1.25f * id - 0.25f * m);
+    X1[base + e] = c.solver == kNewtonDB ? id : cf * (1.25f * id - 0.25f * m);
   }
 }
 
@@ -648,10 +652,17 @@ __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restric
 // iteration and adds the algorithmic flops of its symmetric products
 // (three at the first iteration, where X_1 needs no product, four after;
 // n^2 (n + 1) each).
-__global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, NewtonCtl c, int iter) {
+__global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, NewtonCtl c, int iter,
+                                                            int shift, int prod_before,
+                                                            int prod_after) {
   __shared__ int cnt[2];
-  if (threadIdx.x < 2) cnt[threadIdx.x] = 0;
+  __shared__ int cnt_out[2];
+  if (threadIdx.x < 2) {
+    cnt[threadIdx.x] = 0;
+    cnt_out[threadIdx.x] = 0;
+  }
   __syncthreads();
+  const int cur = iter + shift;  // the iterate whose residual was just formed
   const int nf = 2 * fs.B;
   for (int f = threadIdx.x; f < nf; f += blockDim.x) {
     if (c.status[f] != 0) continue;
@@ -663,39 +674,49 @@ __global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, Newton
     for (int t = 0; t < nt; ++t) s += p[t];
     const float r = sqrtf(s) / sqrtf((float)fs.nreal[f]);
     const float rp = c.rprev[f];
+    // In exact arithmetic both iterations shrink the residual every step, so a
+    // growth means trouble: from a residual above kFloorGuard it is divergence,
+    // below it the fp32 floor has been reached (stalled, the previous iterate
+    // is kept and is as good).
     int st = 0;
     if (!isfinite(r)) {
       st = 3;
-    } else if (c.tol > 0.f && r > 1.2f * rp) {
+    } else if (c.tol > 0.f && r > 1.2f * rp && rp > kFloorGuard) {
       st = 3;
     } else if (c.tol > 0.f && r >= rp) {
       st = 2;
     } else {
       c.rprev[f] = r;
-      c.final_iter[f] = iter + 1;
+      c.final_iter[f] = cur;
       if (c.tol > 0.f && r <= c.tol)
         st = 1;
-      else if (iter + 1 >= c.max_iters)
+      else if (cur >= c.max_iters)
         st = 4;
     }
+    // a rejected iterate leaves final_iter at the previous (accepted) one
     c.status[f] = st;
+    if (st == 0) atomicAdd(&cnt_out[left ? 0 : 1], 1);
   }
   __syncthreads();
   if (threadIdx.x < 2) c.active_count[iter * 2 + threadIdx.x] = cnt[threadIdx.x];
   if (threadIdx.x == 0) {
-    const double nl = fs.nl, nr = fs.nr, g = iter == 0 ? 3.0 : 4.0;
-    c.flops_acc[0] += g * (cnt[0] * nl * nl * (nl + 1.0) + cnt[1] * nr * nr * (nr + 1.0));
+    const double nl = fs.nl, nr = fs.nr;
+    const double fl = nl * nl * (nl + 1.0), fr = nr * nr * (nr + 1.0);
+    c.flops_acc[0] += prod_before * (cnt[0] * fl + cnt[1] * fr) +
+                      prod_after * (cnt_out[0] * fl + cnt_out[1] * fr);
   }
 }
 
 // Put the kept iterate into the root buffer: X_k lives in Xroot for even k
 // and in Xalt for odd k; X_0 = s^(-1/4) I is never stored.
+// scale = 1 (Denman-Beavers): the kept Z is multiplied by s^(-1/4), and Z_0 = I
+// is stored in Xroot by the stage-2 init.
 __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ Xroot,
                                                            const float* __restrict__ Xalt,
-                                                           FactorSet fs, NewtonCtl c) {
+                                                           FactorSet fs, NewtonCtl c, int scale) {
   const int f = blockIdx.y;
   const int k = c.final_iter[f];
-  if (k > 0 && (k & 1) == 0) return;
+  if (!scale && k > 0 && (k & 1) == 0) return;
   int n;
   const float* xf = factor_ptr(Xroot, fs, f, n);
   const int64_t base = xf - Xroot;
@@ -703,8 +724,43 @@ __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ X
   const int64_t nn = (int64_t)n * n;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
        e += (int64_t)gridDim.x * blockDim.x) {
-    Xroot[base + e] = (k == 0) ? ((e / n == e % n) ? cf : 0.f) : Xalt[base + e];
+    if (scale)
+      Xroot[base + e] = cf * ((k & 1) ? Xalt[base + e] : Xroot[base + e]);
+    else
+      Xroot[base + e] = (k == 0) ? ((e / n == e % n) ? cf : 0.f) : Xalt[base + e];
   }
+}
+
+// Stage 1's kept Y (index final_iter, Ybuf0 for even, Ybuf1 for odd) becomes
+// stage 2's Y0 in Ybuf0, and Z0 = I goes to Z0buf. A factor whose stage 1
+// diverged keeps its status and gets no stage 2 (its root becomes s^(-1/4) I).
+__global__ __launch_bounds__(256) void db_stage2_init_kernel(float* __restrict__ Ybuf0,
+                                                             const float* __restrict__ Ybuf1,
+                                                             float* __restrict__ Z0buf,
+                                                             FactorSet fs, NewtonCtl c) {
+  const int f = blockIdx.y;
+  const int k = c.final_iter[f];
+  const bool dead = c.status[f] == 3;
+  int n;
+  const float* yf = factor_ptr(Ybuf0, fs, f, n);
+  const int64_t base = yf - Ybuf0;
+  const int64_t nn = (int64_t)n * n;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    if (!dead && (k & 1)) Ybuf0[base + e] = Ybuf1[base + e];
+    Z0buf[base + e] = (e / n == e % n) ? 1.f : 0.f;
+  }
+}
+
+// After the copy above has read every factor's final_iter: stage 2 starts.
+__global__ __launch_bounds__(256) void db_stage2_reset_kernel(FactorSet fs, NewtonCtl c) {
+  const int f = blockIdx.x * blockDim.x + threadIdx.x;
+  if (f >= 2 * fs.B) return;
+  if (c.status[f] != 3) {
+    c.status[f] = 0;
+    c.rprev[f] = INFINITY;
+  }
+  c.final_iter[f] = 0;
 }
 
 template <class C>
@@ -843,19 +899,32 @@ hipError_t launch_newton_init(const float* A, float* M0, float* X1, FactorSet fs
   return hipGetLastError();
 }
 
-hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, hipStream_t s) {
+hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, int32_t shift,
+                               int32_t prod_before, int32_t prod_after, hipStream_t s) {
   if (fs.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(newton_check_kernel, dim3(1), dim3(1024), 0, s, fs, c, iter);
+  hipLaunchKernelGGL(newton_check_kernel, dim3(1), dim3(1024), 0, s, fs, c, iter, shift,
+                     prod_before, prod_after);
   return hipGetLastError();
 }
 
 hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, NewtonCtl c,
-                               hipStream_t s) {
+                               int32_t scale, hipStream_t s) {
   if (fs.B == 0) return hipSuccess;
   const int nmax = std::max(fs.nl, fs.nr);
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
   hipLaunchKernelGGL(newton_final_kernel, dim3(chunks, 2 * fs.B), dim3(256), 0, s, Xroot, Xalt, fs,
-                     c);
+                     c, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_db_stage2_init(float* Ybuf0, const float* Ybuf1, float* Z0buf, FactorSet fs,
+                                 NewtonCtl c, hipStream_t s) {
+  if (fs.B == 0) return hipSuccess;
+  const int nmax = std::max(fs.nl, fs.nr);
+  const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
+  hipLaunchKernelGGL(db_stage2_init_kernel, dim3(chunks, 2 * fs.B), dim3(256), 0, s, Ybuf0, Ybuf1,
+                     Z0buf, fs, c);
+  hipLaunchKernelGGL(db_stage2_reset_kernel, dim3((2 * fs.B + 255) / 256), dim3(256), 0, s, fs, c);
   return hipGetLastError();
 }
 

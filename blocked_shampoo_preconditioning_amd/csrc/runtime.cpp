@@ -82,6 +82,8 @@ int validate_config(const shampoo_config_t* c) {
     return fail(SHAMPOO_ERR_INVALID_ARG, "newton_tol must be finite");
   if (c->newton_scale_mode < 0 || c->newton_scale_mode > 2)
     return fail(SHAMPOO_ERR_UNSUPPORTED, "newton_scale_mode must be 0, 1 or 2");
+  if (c->root_method != shp::kCoupledNewton && c->root_method != shp::kNewtonDB)
+    return fail(SHAMPOO_ERR_UNSUPPORTED, "root_method must be 0 (coupled Newton) or 1 (Newton-DB)");
   if (!std::isfinite(c->momentum) || c->momentum < 0.0 || c->momentum >= 1.0)
     return fail(SHAMPOO_ERR_INVALID_ARG, "momentum must be in [0, 1)");
   if ((c->param_dtype != SHAMPOO_F32 && c->param_dtype != SHAMPOO_BF16) ||
@@ -201,6 +203,7 @@ struct shampoo_ctx {
   }
   shp::NewtonCtl newton_ctl() const {
     shp::NewtonCtl c;
+    c.solver = cfg.root_method;
     c.status = at<int32_t>(plan.off_status);
     c.final_iter = at<int32_t>(plan.off_final);
     c.scale = at<float>(plan.off_scale);
@@ -378,12 +381,15 @@ void factor_problems(const shampoo_ctx* h, shp::GemmLaunch& g, const float* P, c
   }
 }
 
+int do_refresh_db(shampoo_ctx* h, hipStream_t s);
+
 int do_refresh(shampoo_ctx* h, hipStream_t s) {
   const Plan& p = h->plan;
   if (p.B == 0) {
     h->roots_valid = true;
     return SHAMPOO_OK;
   }
+  if (h->cfg.root_method == shp::kNewtonDB) return do_refresh_db(h, s);
   const shp::FactorSet fs = h->factors();
   const shp::NewtonCtl c = h->newton_ctl();
   double nbytes = 0.0;
@@ -414,12 +420,67 @@ int do_refresh(shampoo_ctx* h, hipStream_t s) {
     if (rc) return rc;
     rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g3, p.tile, true, s); });
     if (rc) return rc;
-    rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] { return shp::launch_newton_check(fs, c, k, s); });
+    const int before = k == 0 ? 3 : 4;
+    rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+               [&] { return shp::launch_newton_check(fs, c, k, 1, before, 0, s); });
     if (rc) return rc;
     mi = 1 - mi;
   }
   rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_newton_final(h->xroot(), h->xalt(), fs, c, s); });
+             [&] { return shp::launch_newton_final(h->xroot(), h->xalt(), fs, c, 0, s); });
+  if (rc) return rc;
+  h->roots_valid = true;
+  return SHAMPOO_OK;
+}
+
+// Newton-DB: two Denman-Beavers square-root stages in inverse-free form on
+// the symmetric GEMM core. Y ping-pongs between S0 (even k) and S1 (odd), Z
+// between Xroot and Xalt, M = Z Y goes to S2. Per iteration: M (with the
+// residual partials), the check, then Y' = 3Y/2 - Y M/2 and Z' = 3Z/2 - M Z/2
+// in one launch. Stage 2 restarts from stage 1's kept Y with Z = I; the root
+// is s^(-1/4) times stage 2's kept Z.
+int do_refresh_db(shampoo_ctx* h, hipStream_t s) {
+  const Plan& p = h->plan;
+  const shp::FactorSet fs = h->factors();
+  const shp::NewtonCtl c = h->newton_ctl();
+  double nbytes = 0.0;
+  for (const auto& b : h->blocks) nbytes += 4.0 * ((double)b.m * b.m + (double)b.n * b.n);
+  int rc = timed(h, kNorms, 0.0, nbytes, s, [&] { return shp::launch_norms(h->lr(), fs, c, s); });
+  if (rc) return rc;
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+             [&] { return shp::launch_newton_init(h->lr(), h->s(0), h->xroot(), fs, c, s); });
+  if (rc) return rc;
+  const int kmax = h->cfg.newton_max_iters;
+  for (int stage = 0; stage < 2; ++stage) {
+    for (int k = 0; k <= kmax; ++k) {
+      float* Y = h->s(k & 1);
+      float* Z = (k & 1) ? h->xalt() : h->xroot();
+      float* Yn = h->s((k + 1) & 1);
+      float* Zn = ((k + 1) & 1) ? h->xalt() : h->xroot();
+      shp::GemmLaunch g1{};
+      factor_problems(h, g1, Z, Y, h->s(2), nullptr, 1.f, 0.f, 0.f, true);  // M = Z Y
+      rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g1, p.tile, true, s); });
+      if (rc) return rc;
+      const int after = k < kmax ? 2 : 0;
+      rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+                 [&] { return shp::launch_newton_check(fs, c, k, 0, 1, after, s); });
+      if (rc) return rc;
+      if (k == kmax) break;
+      shp::GemmLaunch g2{};
+      factor_problems(h, g2, Y, h->s(2), Yn, Y, -0.5f, 1.5f, 0.f, false);  // Y (3I - M) / 2
+      factor_problems(h, g2, h->s(2), Z, Zn, Z, -0.5f, 1.5f, 0.f, false);  // (3I - M) Z / 2
+      rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g2, p.tile, true, s); });
+      if (rc) return rc;
+    }
+    if (stage == 0) {
+      rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
+        return shp::launch_db_stage2_init(h->s(0), h->s(1), h->xroot(), fs, c, s);
+      });
+      if (rc) return rc;
+    }
+  }
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+             [&] { return shp::launch_newton_final(h->xroot(), h->xalt(), fs, c, 1, s); });
   if (rc) return rc;
   h->roots_valid = true;
   return SHAMPOO_OK;
@@ -498,6 +559,7 @@ int shampoo_config_default(shampoo_config_t* cfg) {
   cfg->param_dtype = SHAMPOO_F32;
   cfg->grad_dtype = SHAMPOO_F32;
   cfg->momentum = 0.0;
+  cfg->root_method = shp::kCoupledNewton;
   return SHAMPOO_OK;
 }
 

@@ -103,6 +103,14 @@ typedef struct {
                                      preconditioning (podcast cue 28):
                                      m = alpha m + G, W -= lr L^(-1/4) m R^(-1/4);
                                      statistics use the raw G. 0 = off (default) */
+  int32_t root_method;            /* 0: coupled Newton for the inverse 4th root
+                                        (default);
+                                     1: Newton-DB: two Denman-Beavers square-root
+                                        stages in inverse-free form, Y1 ~ A~^(1/2),
+                                        then Z2 ~ Y1^(-1/2) = A~^(-1/4) (a reading
+                                        of the DASH page's solver); newton_*
+                                        settings apply to each stage and the
+                                        spectral targets of the scale modes are 1 */
 } shampoo_config_t;
 
 /* Byte offsets of the state inside the caller's workspace (for inspection
@@ -143,7 +151,7 @@ typedef struct shampoo_ctx* shampoo_t;
 /* Fill *cfg with the defaults: square blocks of 1024, beta2 0.999,
  * stat_scale 1 - beta2, eps 1e-6, lr 1e-3, root_every 10, 25 Newton
  * iterations at most, tol 1e-6, scale mode 2, fp32 parameters and gradients,
- * no momentum. */
+ * no momentum, coupled Newton roots. */
 int shampoo_config_default(shampoo_config_t* cfg);
 
 /* Bytes of device workspace needed for these matrices (host only, no HIP

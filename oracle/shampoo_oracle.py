@@ -57,6 +57,9 @@ __all__ = [
     "inverse_root_eigh",
     "newton_scale",
     "inverse_root_coupled_newton",
+    "db_scale",
+    "sqrt_pair_db",
+    "inverse_root_newton_db",
     "precondition",
     "round_to_bf16",
     "is_refresh_step",
@@ -203,6 +206,9 @@ class NewtonInfo:
     status: str = "capped"  # converged | stalled | diverged | capped
 
 
+FLOOR_GUARD = 1e-3  # a residual that grows from below this is at the rounding floor
+
+
 def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
                                 divergence_factor=1.2):
     """Coupled Newton iteration for A^(-1/p) (Guo and Higham 2006).
@@ -214,9 +220,12 @@ def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
     Stopping: after each iteration the residual r = ||M - I||_F / sqrt(n) is
     compared with tol (stop, keep this X), with the previous residual (no
     decrease: stop, keep the previous X) and with divergence_factor times
-    the previous residual (diverged: keep the previous X). tol <= 0 runs
-    exactly max_iters iterations and skips those three tests; in both modes
-    a non-finite residual stops the iteration and keeps the previous X.
+    the previous residual (diverged: keep the previous X; only when the
+    previous residual exceeds FLOOR_GUARD, since in exact arithmetic the
+    residual shrinks every step and a growth from a small residual is the
+    rounding floor). tol <= 0 runs exactly max_iters iterations and skips
+    those tests; in both modes a non-finite residual stops the iteration and
+    keeps the previous X.
     """
     A = np.asarray(A, dtype=np.float64)
     n = A.shape[0]
@@ -236,7 +245,7 @@ def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
             info.status = "diverged"
             break
         if tol > 0.0:
-            if r > divergence_factor * r_prev:
+            if r > divergence_factor * r_prev and r_prev > FLOOR_GUARD:
                 info.status = "diverged"
                 break
             if r >= r_prev:
@@ -248,6 +257,85 @@ def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
             info.status = "converged"
             break
     return X, info
+
+
+def db_scale(A, mode=2, power_iters=16):
+    """Scale for the Denman-Beavers stages: the iteration converges for a
+    spectrum inside (0, 2), so the spectral target is 1 instead of Newton's:
+    mode 0 ||A||_F, mode 1 min(||A||_F, ||A||_inf), mode 2 the power estimate
+    lam itself (norm bound when lam is 0)."""
+    A = np.asarray(A, dtype=np.float64)
+    fro = math.sqrt(float(np.sum(A * A)))
+    if mode == 0:
+        return fro
+    bound = min(fro, float(np.max(np.sum(np.abs(A), axis=1))))
+    if mode == 1:
+        return bound
+    if mode == 2:
+        lam = 2.0 * newton_scale(A, 4, 2, power_iters)  # newton_scale returns lam / 2
+        return lam if lam > 0.0 else bound
+    raise ValueError(f"unknown scale mode {mode}")
+
+
+def sqrt_pair_db(A, max_iters=25, tol=0.0, divergence_factor=1.2):
+    """Denman-Beavers pair iteration for the square root, inverse-free form
+    (Newton-Schulz): Y_0 = A, Z_0 = I, M_k = Z_k Y_k,
+    Y_{k+1} = Y_k (3 I - M_k) / 2, Z_{k+1} = (3 I - M_k) Z_k / 2.
+    Y tends to A^(1/2) and Z to A^(-1/2) when the spectrum of A lies in (0, 2).
+
+    The residual r_k = ||M_k - I||_F / sqrt(n) belongs to the pair k. Stops
+    at r_k <= tol (keep pair k), on r_k >= r_(k-1) (stalled, or diverged for a
+    growth beyond divergence_factor from r_(k-1) > FLOOR_GUARD; keep pair
+    k - 1), on a non-finite r_k (keep pair k - 1), or after max_iters updates.
+    tol <= 0: exactly max_iters updates (only the non-finite guard)."""
+    A = np.asarray(A, dtype=np.float64)
+    n = A.shape[0]
+    eye = np.eye(n)
+    Y, Z = A.copy(), eye.copy()
+    info = NewtonInfo(0)
+    prev = (Y, Z)
+    r_prev = math.inf
+    for k in range(max_iters + 1):
+        M = Z @ Y
+        r = float(np.sqrt(np.sum((M - eye) ** 2)) / math.sqrt(n))
+        info.residuals.append(r)
+        if not math.isfinite(r):
+            info.status = "diverged"
+            Y, Z = prev
+            break
+        if tol > 0.0:
+            if r <= tol:
+                info.status = "converged"
+                break
+            if r > divergence_factor * r_prev and r_prev > FLOOR_GUARD:
+                info.status = "diverged"
+                Y, Z = prev
+                break
+            if r >= r_prev:
+                info.status = "stalled"
+                Y, Z = prev
+                break
+        if k == max_iters:
+            break
+        prev = (Y, Z)
+        r_prev = r
+        T = (3.0 * eye - M) / 2.0
+        Y, Z = Y @ T, T @ Z
+        info.iters = k + 1
+    return Y, Z, info
+
+
+def inverse_root_newton_db(A, max_iters=25, tol=0.0, scale_mode=2):
+    """A^(-1/4) by two Denman-Beavers square-root stages (a reading of the
+    DASH page's "Newton-DB" solver, whose formula the page does not give):
+    with A~ = A / s, the first stage gives Y1 ~ A~^(1/2); the second, run on
+    Y1, gives Z2 ~ Y1^(-1/2) = A~^(-1/4); the root is s^(-1/4) Z2.
+    Returns (X, (info_stage1, info_stage2))."""
+    A = np.asarray(A, dtype=np.float64)
+    s = db_scale(A, scale_mode)
+    Y1, _, info1 = sqrt_pair_db(A / s, max_iters, tol)
+    _, Z2, info2 = sqrt_pair_db(Y1, max_iters, tol)
+    return s ** -0.25 * Z2, (info1, info2)
 
 
 # ---------------------------------------------------------------------------
@@ -302,8 +390,9 @@ class ShampooOracle:
     root_every:   k of the refresh schedule (0: only explicit refresh).
     blocks:       optional subset of block ids to track (blocks are
                   independent, so a sample can be run alone).
-    root_method:  "eigh" (the definition) or "newton" (the iteration, with
-                  newton_iters / newton_tol / newton_scale_mode).
+    root_method:  "eigh" (the definition), "newton" (coupled Newton) or
+                  "newton_db" (two Denman-Beavers stages), the iterations with
+                  newton_iters / newton_tol / newton_scale_mode.
     param_bf16:   parameters are stored in bfloat16 after every update.
     momentum:     alpha of the momentum folded in before preconditioning
                   (0: none).
@@ -340,6 +429,9 @@ class ShampooOracle:
         if self.root_method == "newton":
             return inverse_root_coupled_newton(A, self.p, self.newton_iters, self.newton_tol,
                                                self.newton_scale_mode)
+        if self.root_method == "newton_db":
+            return inverse_root_newton_db(A, self.newton_iters, self.newton_tol,
+                                          self.newton_scale_mode)
         raise ValueError(self.root_method)
 
     def refresh_roots(self):

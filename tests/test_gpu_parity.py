@@ -342,3 +342,50 @@ def test_momentum_decoder_1b_sampled():
         assert r.stats_err <= STATS_TOL, r
         assert r.update_err <= UPDATE_TOL, r
     sh.close()
+
+
+# ---------------------------------------------------------------------------
+# Newton-DB roots (two Denman-Beavers square-root stages)
+# ---------------------------------------------------------------------------
+def test_newton_db_small_ragged_every_block():
+    w = workload("gpt_small_b256", shapes=((300, 520), (256, 256), (130, 71), (512, 96)),
+                 root_every=3, root_method="newton_db", seed=91)
+    recs, sh, orc, params, W = run_parity(w, 7)
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    st = sh.newton_info()[0].cpu().tolist()
+    assert set(st) <= {1, 2}, st
+    sh.close()
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_newton_db_scale_and_fixed_count_match_oracle(mode):
+    """Fixed 6 updates per stage: the GPU runs the same iteration as the fp64
+    oracle; the scale of every factor is the oracle's db_scale."""
+    from oracle import db_scale
+    w = workload("gpt_small_b256", shapes=((300, 520), (256, 256)), root_every=1,
+                 root_method="newton_db", newton_max_iters=6, newton_tol=0.0,
+                 newton_scale_mode=mode, seed=93)
+    recs, sh, orc, params, W = run_parity(w, 2, root_method="newton_db")
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= 1e-4, r  # same algorithm on both sides
+    sc = sh.newton_info()[2].cpu().numpy()
+    B = sh.n_blocks
+    for i in range(B):
+        st = orc.state[i]
+        for f, A in ((i, st.L), (B + i, st.R)):
+            ref = db_scale(A, mode)
+            assert abs(sc[f] - ref) <= 2e-5 * ref, (f, sc[f], ref)
+    sh.close()
+
+
+def test_newton_db_decoder_1b_sampled():
+    w = workload("decoder_1b_b1024_f32", root_method="newton_db")
+    ids = sample_blocks(w, 4, seed=10)
+    recs, sh, orc, params, W = run_parity(w, 10, ids=ids)
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    sh.close()

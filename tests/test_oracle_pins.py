@@ -466,3 +466,65 @@ def test_momentum_is_linear_sum_of_past_updates():
     _, _, Up = run_oracle(Gs, np.zeros((4, 6)), 0.95, 1e-2, 1e-3, root_every=1)
     for u, v in zip(U0, Up):
         assert np.array_equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# Newton-DB: two Denman-Beavers square-root stages
+# ---------------------------------------------------------------------------
+from oracle import db_scale, inverse_root_newton_db, sqrt_pair_db  # noqa: E402
+
+
+def test_db_pair_gives_square_root_and_inverse():
+    rng = np.random.default_rng(51)
+    A, Q, lam = spd(20, 50.0, rng)
+    A *= 1.5  # spectrum in (0.03, 1.5], inside (0, 2)
+    Y, Z, info = sqrt_pair_db(A, 40, 1e-13)
+    assert info.status in ("converged", "stalled")
+    sq = (Q * np.sqrt(1.5 * lam)) @ Q.T  # square root from the eigenpairs
+    assert rel(Y, sq) < 1e-11 and rel(Z, np.linalg.inv(sq)) < 1e-11
+    assert rel(Y @ Y, A) < 1e-11
+
+
+def test_db_scalar_map():
+    """1x1: y <- y (3 - zy) / 2, z <- (3 - zy) z / 2 from (a, 1); z y tends to 1
+    and y to sqrt(a); one step by hand."""
+    a = 0.3
+    Y, Z, info = sqrt_pair_db(np.array([[a]]), 1, 0.0)
+    t = (3 - a) / 2
+    assert Y[0, 0] == pytest.approx(a * t, rel=1e-15) and Z[0, 0] == pytest.approx(t, rel=1e-15)
+    Y, Z, _ = sqrt_pair_db(np.array([[a]]), 40, 1e-14)
+    assert Y[0, 0] == pytest.approx(math.sqrt(a), rel=1e-13)
+    assert Z[0, 0] == pytest.approx(1 / math.sqrt(a), rel=1e-13)
+
+
+def test_newton_db_root_matches_eigh():
+    rng = np.random.default_rng(53)
+    for mode in (0, 1, 2):
+        A, _, _ = spd(24, 300.0, rng)
+        A *= 3e-3
+        X, (i1, i2) = inverse_root_newton_db(A, 60, 1e-13, mode)
+        assert rel(X, inverse_root_eigh(A)) < 1e-10
+    assert db_scale(np.diag([4.0, 1.0]), 1) == pytest.approx(4.0)
+
+
+def test_newton_db_orthogonal_similarity():
+    rng = np.random.default_rng(57)
+    A, Q, lam = spd(6, 20.0, rng)
+    Xa, _ = inverse_root_newton_db(A, 4, 0.0, 0)
+    Xd, _ = inverse_root_newton_db(np.diag(lam), 4, 0.0, 0)
+    assert np.allclose(Xd, np.diag(np.diag(Xd)), atol=0)
+    assert rel(Xa, Q @ Xd @ Q.T) < 1e-12
+
+
+def test_growth_at_the_floor_is_a_stall_not_divergence():
+    """A residual that grows from below the floor guard stops the iteration as
+    'stalled' and keeps the previous iterate; from above it, 'diverged'."""
+    # fp32-like floor emulated on a diagonal matrix: the iteration reaches the
+    # fp64 floor (~1e-16) and stalls there, never reported as divergence
+    A = np.diag(np.geomspace(1.0, 1e-3, 30))
+    for tol in (1e-20, 1e-30):
+        X, info = inverse_root_coupled_newton(A, 4, max_iters=60, tol=tol, scale_mode=2)
+        assert info.status == "stalled", info
+        assert rel(X, inverse_root_eigh(A)) < 1e-12
+    _, _, i_db = sqrt_pair_db(A / db_scale(A, 2), 60, 1e-30)
+    assert i_db.status == "stalled"
