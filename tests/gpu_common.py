@@ -74,9 +74,12 @@ class Record:
     per_block: dict
 
 
-def run_parity(w, steps, ids=None, root_method="eigh", check_update=True, on_step=None):
+def run_parity(w, steps, ids=None, root_method="eigh", check_update=True, on_step=None,
+               compare=None):
     """Run `steps` steps of workload w on the GPU and in the oracle (tracked
-    blocks `ids`, default all). Returns (records, shampoo, oracle, params)."""
+    blocks `ids`, default all), comparing after every step t with
+    compare(t) true (default: all). Returns (records, shampoo, oracle,
+    params, oracle parameter blocks)."""
     dev = torch.device("cuda")
     table = block_table(w.shapes, w.block_rows, w.block_cols)
     ids = list(range(len(table))) if ids is None else list(ids)
@@ -98,6 +101,8 @@ def run_parity(w, steps, ids=None, root_method="eigh", check_update=True, on_ste
         G = {i: block_of(grads[table[i].mat], table[i]) for i in ids}
         sh.step(params, grads)
         W, U = orc.step_blocks(G, W)
+        if compare is not None and not compare(t):
+            continue
         torch.cuda.synchronize()
         Lg, Rg = sh.stats()
         per = {}
