@@ -118,8 +118,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--momentum", type=float, default=None,
                     help="momentum folded in before preconditioning (default: the workload's, 0)")
-    ap.add_argument("--root-method", default=None, choices=("newton", "newton_db"),
+    ap.add_argument("--root-method", default=None, choices=("newton", "newton_db", "chebyshev"),
                     help="inverse-root solver (default: the workload's, coupled Newton)")
+    ap.add_argument("--cheb-degree", type=int, default=None,
+                    help="Chebyshev degree (default: the workload's, 128)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one plain 1 GiB device copy (a known-size kernel that "
                          "calibrates the HBM traffic counters)")
@@ -146,6 +148,8 @@ def main():
         w = dataclasses.replace(w, momentum=args.momentum)
     if args.root_method is not None:
         w = dataclasses.replace(w, root_method=args.root_method)
+    if args.cheb_degree is not None:
+        w = dataclasses.replace(w, cheb_degree=args.cheb_degree)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {w.name}: {len(w.shapes)} matrices, blocks {w.block_rows}x{w.block_cols}")
@@ -157,7 +161,7 @@ def main():
     sh = S.Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
                    root_every=w.root_every, newton_max_iters=w.newton_max_iters,
                    newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype,
-                   momentum=w.momentum, root_method=w.root_method)
+                   momentum=w.momentum, root_method=w.root_method, cheb_degree=w.cheb_degree)
     B = sh.n_blocks
     log(f"{B} blocks, workspace {sh.workspace.numel() / 2**30:.1f} GiB")
     for t in range(args.warmup):
@@ -237,6 +241,7 @@ def main():
                    "newton_max_iters": w.newton_max_iters, "newton_tol": w.newton_tol,
                    "newton_scale_mode": w.newton_scale_mode, "momentum": w.momentum,
                    "root_method": w.root_method,
+                   "cheb_degree": w.cheb_degree if w.root_method == "chebyshev" else None,
                    "grad_sets": n_sets},
         "blocks_per_s": round(steps_per_s * B, 1),
         "gemm_tflops": {k: kernels[k].get("tflops") for k in ("stats", "newton_gemm", "apply")},

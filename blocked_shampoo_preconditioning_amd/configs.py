@@ -41,7 +41,8 @@ class Workload:
     newton_tol: float = 1e-6      # <= 0: exactly newton_max_iters iterations
     newton_scale_mode: int = 2
     momentum: float = 0.0         # ordinary momentum folded in before preconditioning
-    root_method: str = "newton"   # newton (coupled) | newton_db (Denman-Beavers stages)
+    root_method: str = "newton"   # newton (coupled) | newton_db (Denman-Beavers) | chebyshev
+    cheb_degree: int = 128        # degree of the Chebyshev interpolant (chebyshev only)
     init_std: float = 0.02
     seed: int = 0
     notes: str = field(default="", compare=False)

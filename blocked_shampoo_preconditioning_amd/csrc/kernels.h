@@ -23,7 +23,8 @@ struct MatMeta {
   int64_t ld;
 };
 
-// C[m][n] = alpha * sum_k P[k][m] Q[k][n] + beta * D[m][n] + gamma * I[m][n]
+// C[m][n] = alpha * sum_k P[k][m] Q[k][n] + beta * D[m][n] + beta2 * D2[m][n]
+//           + gamma * I[m][n]
 // for every element of a batch of independent matrices, all stored row-major
 // and contiguous: P is K x M (element stride sP between batch members), Q is
 // K x N, C and D are M x N. D may be C itself (the statistics' EMA reads the
@@ -35,10 +36,15 @@ struct GemmProblem {
   const float* Q;
   float* C;
   const float* D;
-  int64_t sP, sQ, sC, sD;
+  const float* D2;  // second affine term (Clenshaw's B_(k+2)), weight beta2
+  int64_t sP, sQ, sC, sD, sD2;
   int32_t M, N, K;
   int32_t batch;
-  float alpha, beta, gamma;
+  float alpha, beta, gamma, beta2;
+  // per-factor epilogue coefficients: if set, alpha, beta, beta2, gamma are
+  // coef[(f0 + i) * coef_stride + 0..3]
+  const float* coef;
+  int32_t coef_stride;
   // factors with status[f0 + i] != 0 are skipped (Newton early exit)
   const int32_t* status;
   int32_t f0;
@@ -77,13 +83,16 @@ struct FactorSet {
 constexpr int kPowerIters = 16;
 constexpr int kMaxSide = 4096;
 
-enum RootSolver { kCoupledNewton = 0, kNewtonDB = 1 };
+enum RootSolver { kCoupledNewton = 0, kNewtonDB = 1, kChebyshev = 2 };
 
 // A residual that grows from below this value is the fp32 floor, not divergence.
 constexpr float kFloorGuard = 1e-3f;
 
 struct NewtonCtl {
   int32_t solver;       // RootSolver
+  float floor;          // lower bound of every statistic's spectrum: beta2^t eps
+  float* cheb;          // Chebyshev coefficient quadruples [2B][degree + 1][4]
+  int32_t degree;
   int32_t* status;
   int32_t* final_iter;
   float* scale;
@@ -124,6 +133,12 @@ hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, int32_t 
 // scale: multiply the kept iterate by s^(-1/4) (Denman-Beavers result).
 hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, NewtonCtl c,
                                int32_t scale, hipStream_t s);
+// Chebyshev: per factor, the interval [r, 1] (r = floor / s), the interpolant's
+// coefficients and the Clenshaw epilogue quadruples; status = capped.
+hipError_t launch_cheb_setup(FactorSet fs, NewtonCtl c, hipStream_t s);
+// B_d = c_d I and B_(d-1) = c_(d-1) I + 2 c_d T(Ahat), T = (2 Ahat - (1 + r) I) / (1 - r).
+hipError_t launch_cheb_init(const float* Ahat, float* Bd, float* Bd1, FactorSet fs, NewtonCtl c,
+                            hipStream_t s);
 // Between the two Denman-Beavers stages: Y1 (kept pair of stage 1, in Ybuf0 or
 // Ybuf1 by parity) becomes stage 2's Y0 in Ybuf0, Z0 = I goes to Z0buf.
 hipError_t launch_db_stage2_init(float* Ybuf0, const float* Ybuf1, float* Z0buf, FactorSet fs,

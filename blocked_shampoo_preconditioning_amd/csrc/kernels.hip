@@ -236,6 +236,15 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   // mirrored row, written as one 16-byte store.
   float* Cb = pb.C + (size_t)f * pb.sC;
   const float* Db = pb.D != nullptr ? pb.D + (size_t)f * pb.sD : nullptr;
+  const float* D2b = pb.D2 != nullptr ? pb.D2 + (size_t)f * pb.sD2 : nullptr;
+  float e_alpha = pb.alpha, e_beta = pb.beta, e_beta2 = pb.beta2, e_gamma = pb.gamma;
+  if (pb.coef != nullptr) {
+    const float* cf = pb.coef + (size_t)(pb.f0 + f) * pb.coef_stride;
+    e_alpha = cf[0];
+    e_beta = cf[1];
+    e_beta2 = cf[2];
+    e_gamma = cf[3];
+  }
   const int N = pb.N;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave % C::WM, wn = wave / C::WM;
@@ -253,9 +262,10 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = row0 + q;
-          float x = pb.alpha * acc[i][j][4 * g4 + q];
-          if (Db != nullptr) x += pb.beta * Db[(size_t)row * N + col];
-          if (row == col) x += pb.gamma;
+          float x = e_alpha * acc[i][j][4 * g4 + q];
+          if (Db != nullptr) x += e_beta * Db[(size_t)row * N + col];
+          if (D2b != nullptr) x += e_beta2 * D2b[(size_t)row * N + col];
+          if (row == col) x += e_gamma;
           v[q] = x;
           if (!diag || row <= col) {
             Cb[(size_t)row * N + col] = x;
@@ -581,8 +591,9 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   const double bound = fmin(fro, inf);
   // spectral target: Newton converges on (0, 5), the Denman-Beavers pair on (0, 2)
   const bool db = c.solver == kNewtonDB;
+  const bool cheb = c.solver == kChebyshev;
   double s = c.scale_mode == 0 ? fro : bound * (db ? 1.0 : 0.4);
-  if (c.scale_mode == 2) {
+  if (c.scale_mode == 2 || cheb) {
     double lam = 0.0;
     for (int it = 0; it < kPowerIters; ++it) {
       if (it > 0) {
@@ -611,6 +622,10 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
       __syncthreads();
     }
     s = lam > 0.0 ? lam * (db ? 1.0 : 0.5) : bound * (db ? 1.0 : 0.4);
+    // Chebyshev needs an upper bound of the spectrum: lam >= 0.55 lam_max
+    // unless v_0 is almost orthogonal to the top eigenvector; the norm bound
+    // holds always
+    if (cheb) s = lam > 0.0 ? fmin(lam / 0.55, bound) : bound;
   }
   if (threadIdx.x == 0) {
     const bool ok = s > 0.0 && isfinite(s) && isfinite(fro);
@@ -643,7 +658,8 @@ __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restric
     const float id = (r == col) ? 1.f : 0.f;
     const float m = (r < nr && col < nr) ? Af[e] / s : id;
     M0[base + e] = m;
-    X1[base + e] = c.solver == kNewtonDB ? id : cf * (1.25f * id - 0.25f * m);
+    if (c.solver != kChebyshev)
+      X1[base + e] = c.solver == kNewtonDB ? id : cf * (1.25f * id - 0.25f * m);
   }
 }
 
@@ -717,6 +733,8 @@ __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ X
   const int f = blockIdx.y;
   const int k = c.final_iter[f];
   if (!scale && k > 0 && (k & 1) == 0) return;
+  const bool odd = scale == 1 && (k & 1);  // scale 2: the result is in Xroot
+  const bool dead = scale == 2 && c.status[f] == 3;  // no valid scale: the root is 0
   int n;
   const float* xf = factor_ptr(Xroot, fs, f, n);
   const int64_t base = xf - Xroot;
@@ -724,8 +742,10 @@ __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ X
   const int64_t nn = (int64_t)n * n;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
        e += (int64_t)gridDim.x * blockDim.x) {
-    if (scale)
-      Xroot[base + e] = cf * ((k & 1) ? Xalt[base + e] : Xroot[base + e]);
+    if (dead)
+      Xroot[base + e] = 0.f;
+    else if (scale)
+      Xroot[base + e] = cf * (odd ? Xalt[base + e] : Xroot[base + e]);
     else
       Xroot[base + e] = (k == 0) ? ((e / n == e % n) ? cf : 0.f) : Xalt[base + e];
   }
@@ -761,6 +781,66 @@ __global__ __launch_bounds__(256) void db_stage2_reset_kernel(FactorSet fs, Newt
     c.rprev[f] = INFINITY;
   }
   c.final_iter[f] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Chebyshev inverse root: X = s^(-1/4) p(A / s), p the degree-d interpolant of
+// x^(-1/4) on [r, 1] at the Chebyshev points, r = floor / s; Clenshaw in
+// matrices, one symmetric product per degree.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void cheb_setup_kernel(FactorSet fs, NewtonCtl c) {
+  __shared__ double fx[1025];
+  const int f = blockIdx.x;
+  const int d = c.degree, N = d + 1;
+  float* q = c.cheb + (size_t)f * N * 4;
+  const double s = c.scale[f];
+  const bool ok = c.status[f] == 0 && s > 0.0;
+  const double r = ok ? fmin((double)c.floor / s, 0.999) : 0.5;
+  const double pi = 3.14159265358979323846;
+  for (int j = threadIdx.x; j < N; j += blockDim.x) {
+    const double th = pi * (j + 0.5) / N;
+    const double x = ((1.0 - r) * cos(th) + 1.0 + r) * 0.5;
+    fx[j] = pow(x, -0.25);
+  }
+  __syncthreads();
+  const float a = (float)(4.0 / (1.0 - r)), b = (float)(-2.0 * (1.0 + r) / (1.0 - r));
+  for (int k = threadIdx.x; k < N; k += blockDim.x) {
+    double ck = 0.0;
+    for (int j = 0; j < N; ++j) ck += fx[j] * cos(k * pi * (j + 0.5) / N);
+    ck *= 2.0 / N;
+    // slot k: the epilogue of the product forming B_k (k = 1 .. d-2) or p (k = 0)
+    q[k * 4 + 0] = k == 0 ? 0.5f * a : a;
+    q[k * 4 + 1] = k == 0 ? 0.5f * b : b;
+    q[k * 4 + 2] = -1.f;
+    q[k * 4 + 3] = (float)(k == 0 ? 0.5 * ck : ck);
+  }
+  if (threadIdx.x == 0) {
+    c.status[f] = ok ? 4 : 3;
+    c.final_iter[f] = 0;
+    c.rprev[f] = 0.f;
+  }
+}
+
+// B_d = c_d I; B_(d-1) = c_(d-1) I + c_d (a Ahat + b I) with a, b from slot 1.
+__global__ __launch_bounds__(256) void cheb_init_kernel(const float* __restrict__ Ahat,
+                                                        float* __restrict__ Bd,
+                                                        float* __restrict__ Bd1, FactorSet fs,
+                                                        NewtonCtl c) {
+  const int f = blockIdx.y;
+  int n;
+  const float* af = factor_ptr(Ahat, fs, f, n);
+  const int64_t base = af - Ahat;
+  const int d = c.degree;
+  const float* q = c.cheb + (size_t)f * (d + 1) * 4;
+  const float cd = q[d * 4 + 3], cd1 = q[(d - 1) * 4 + 3];
+  const float a = q[1 * 4 + 0], b = q[1 * 4 + 1];
+  const int64_t nn = (int64_t)n * n;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const float id = (e / n == e % n) ? 1.f : 0.f;
+    Bd[base + e] = cd * id;
+    Bd1[base + e] = cd * a * af[e] + (cd1 + cd * b) * id;
+  }
 }
 
 template <class C>
@@ -914,6 +994,22 @@ hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, Ne
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
   hipLaunchKernelGGL(newton_final_kernel, dim3(chunks, 2 * fs.B), dim3(256), 0, s, Xroot, Xalt, fs,
                      c, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_cheb_setup(FactorSet fs, NewtonCtl c, hipStream_t s) {
+  if (fs.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(cheb_setup_kernel, dim3(2 * fs.B), dim3(256), 0, s, fs, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_cheb_init(const float* Ahat, float* Bd, float* Bd1, FactorSet fs, NewtonCtl c,
+                            hipStream_t s) {
+  if (fs.B == 0) return hipSuccess;
+  const int nmax = std::max(fs.nl, fs.nr);
+  const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
+  hipLaunchKernelGGL(cheb_init_kernel, dim3(chunks, 2 * fs.B), dim3(256), 0, s, Ahat, Bd, Bd1, fs,
+                     c);
   return hipGetLastError();
 }
 

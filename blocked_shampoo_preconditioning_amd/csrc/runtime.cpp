@@ -58,7 +58,7 @@ struct Plan {
   int64_t fl = 0, fr = 0;  // elements of all left / right factors
   int64_t off_blocks, off_mats, off_umats, off_nreal, off_status, off_final, off_scale, off_rprev,
       off_cfac, off_active, off_flops, off_resid, off_gp, off_mom, off_lr, off_xroot, off_xalt,
-      off_s0, off_s1, off_s2, total;
+      off_s0, off_s1, off_s2, off_cheb, total;
   bool momentum = false;
 };
 
@@ -82,8 +82,12 @@ int validate_config(const shampoo_config_t* c) {
     return fail(SHAMPOO_ERR_INVALID_ARG, "newton_tol must be finite");
   if (c->newton_scale_mode < 0 || c->newton_scale_mode > 2)
     return fail(SHAMPOO_ERR_UNSUPPORTED, "newton_scale_mode must be 0, 1 or 2");
-  if (c->root_method != shp::kCoupledNewton && c->root_method != shp::kNewtonDB)
-    return fail(SHAMPOO_ERR_UNSUPPORTED, "root_method must be 0 (coupled Newton) or 1 (Newton-DB)");
+  if (c->root_method != shp::kCoupledNewton && c->root_method != shp::kNewtonDB &&
+      c->root_method != shp::kChebyshev)
+    return fail(SHAMPOO_ERR_UNSUPPORTED,
+                "root_method must be 0 (coupled Newton), 1 (Newton-DB) or 2 (Chebyshev)");
+  if (c->root_method == shp::kChebyshev && (c->cheb_degree < 2 || c->cheb_degree > 1024))
+    return fail(SHAMPOO_ERR_INVALID_ARG, "cheb_degree must be in 2..1024");
   if (!std::isfinite(c->momentum) || c->momentum < 0.0 || c->momentum >= 1.0)
     return fail(SHAMPOO_ERR_INVALID_ARG, "momentum must be in [0, 1)");
   if ((c->param_dtype != SHAMPOO_F32 && c->param_dtype != SHAMPOO_BF16) ||
@@ -136,6 +140,9 @@ Plan make_plan(const shampoo_config_t* c, const shampoo_matrix_desc_t* m, int32_
   p.off_cfac = take(2 * p.B * 4);
   p.off_active = take((int64_t)(p.max_iters + 1) * 2 * 4);
   p.off_flops = take(8);
+  p.off_cheb = c->root_method == shp::kChebyshev
+                   ? take(2 * p.B * (int64_t)(c->cheb_degree + 1) * 4 * 4)
+                   : -1;
   p.off_resid = take(2 * p.B * p.resid_stride * 4);
   p.off_gp = take(p.B * p.br * p.bc * 4);
   p.momentum = c->momentum > 0.0;
@@ -216,6 +223,9 @@ struct shampoo_ctx {
     c.active_count = at<int32_t>(plan.off_active);
     c.flops_acc = at<double>(plan.off_flops);
     c.tol = (float)cfg.newton_tol;
+    c.floor = 0.f;
+    c.cheb = plan.off_cheb >= 0 ? at<float>(plan.off_cheb) : nullptr;
+    c.degree = cfg.cheb_degree;
     c.max_iters = cfg.newton_max_iters;
     c.scale_mode = cfg.newton_scale_mode;
     return c;
@@ -382,14 +392,18 @@ void factor_problems(const shampoo_ctx* h, shp::GemmLaunch& g, const float* P, c
 }
 
 int do_refresh_db(shampoo_ctx* h, hipStream_t s);
+int do_refresh_cheb(shampoo_ctx* h, int64_t t_stats, hipStream_t s);
 
-int do_refresh(shampoo_ctx* h, hipStream_t s) {
+// t_stats: the step whose statistics the roots are taken of (for the
+// Chebyshev interval's lower end beta2^t eps).
+int do_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
   const Plan& p = h->plan;
   if (p.B == 0) {
     h->roots_valid = true;
     return SHAMPOO_OK;
   }
   if (h->cfg.root_method == shp::kNewtonDB) return do_refresh_db(h, s);
+  if (h->cfg.root_method == shp::kChebyshev) return do_refresh_cheb(h, t_stats, s);
   const shp::FactorSet fs = h->factors();
   const shp::NewtonCtl c = h->newton_ctl();
   double nbytes = 0.0;
@@ -486,6 +500,54 @@ int do_refresh_db(shampoo_ctx* h, hipStream_t s) {
   return SHAMPOO_OK;
 }
 
+int do_refresh_cheb(shampoo_ctx* h, int64_t t_stats, hipStream_t s) {
+  const Plan& p = h->plan;
+  const shp::FactorSet fs = h->factors();
+  shp::NewtonCtl c = h->newton_ctl();
+  c.floor = (float)(std::pow(h->cfg.beta2, (double)t_stats) * h->cfg.eps);
+  const int d = h->cfg.cheb_degree;
+  double nbytes = 0.0;
+  for (const auto& b : h->blocks) nbytes += 4.0 * ((double)b.m * b.m + (double)b.n * b.n);
+  int rc = timed(h, kNorms, 0.0, nbytes, s, [&] { return shp::launch_norms(h->lr(), fs, c, s); });
+  if (rc) return rc;
+  // Ahat = A / s in Xalt (identity on tail padding); then the coefficients
+  // (which mark every factor as a fixed-degree result); B_d, B_(d-1) in S0, S1
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+             [&] { return shp::launch_newton_init(h->lr(), h->xalt(), nullptr, fs, c, s); });
+  if (rc) return rc;
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] { return shp::launch_cheb_setup(fs, c, s); });
+  if (rc) return rc;
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+             [&] { return shp::launch_cheb_init(h->xalt(), h->s(0), h->s(1), fs, c, s); });
+  if (rc) return rc;
+  double fprod = 0.0;
+  for (const auto& b : h->blocks)
+    fprod += (double)b.m * b.m * (b.m + 1.0) + (double)b.n * b.n * (b.n + 1.0);
+  // B_k = a Ahat B_(k+1) + b B_(k+1) - B_(k+2) + c_k I, buffer of B_k: S[(d - k) % 3];
+  // the last product (k = 0) forms p into Xroot
+  for (int k = d - 2; k >= 0; --k) {
+    float* Bk1 = h->s((d - k - 1) % 3);
+    float* Bk2 = h->s((d - k - 2) % 3);
+    float* Bk = k == 0 ? h->xroot() : h->s((d - k) % 3);
+    shp::GemmLaunch g{};
+    factor_problems(h, g, h->xalt(), Bk1, Bk, Bk1, 1.f, 0.f, 0.f, false);
+    for (int i = 0; i < g.n_problems; ++i) {
+      g.p[i].D2 = Bk2 + (g.p[i].D - Bk1);
+      g.p[i].sD2 = g.p[i].sD;
+      g.p[i].status = nullptr;  // every factor runs the whole recurrence
+      g.p[i].coef = c.cheb + (size_t)k * 4;
+      g.p[i].coef_stride = (d + 1) * 4;
+    }
+    rc = timed(h, kNewtonGemm, fprod, 0.0, s, [&] { return shp::launch_gemm_sym(g, p.tile, true, s); });
+    if (rc) return rc;
+  }
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+             [&] { return shp::launch_newton_final(h->xroot(), h->xalt(), fs, c, 2, s); });
+  if (rc) return rc;
+  h->roots_valid = true;
+  return SHAMPOO_OK;
+}
+
 int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   const Plan& p = h->plan;
   if (p.B == 0) return SHAMPOO_OK;
@@ -560,6 +622,7 @@ int shampoo_config_default(shampoo_config_t* cfg) {
   cfg->grad_dtype = SHAMPOO_F32;
   cfg->momentum = 0.0;
   cfg->root_method = shp::kCoupledNewton;
+  cfg->cheb_degree = 128;
   return SHAMPOO_OK;
 }
 
@@ -670,7 +733,7 @@ int shampoo_step(shampoo_t h, void* const* params, const void* const* grads, uin
   if (rc) return rc;
   if ((rc = do_pack(h, s))) return rc;
   if ((rc = do_stats(h, s))) return rc;
-  if (refresh && (rc = do_refresh(h, s))) return rc;
+  if (refresh && (rc = do_refresh(h, s, t))) return rc;
   if ((rc = do_apply(h, s, nullptr))) return rc;
   h->t = t;
   return SHAMPOO_OK;
@@ -678,7 +741,7 @@ int shampoo_step(shampoo_t h, void* const* params, const void* const* grads, uin
 
 int shampoo_refresh_roots(shampoo_t h, void* hip_stream) {
   if (!h) return fail(SHAMPOO_ERR_INVALID_ARG, "handle is NULL");
-  return do_refresh(h, static_cast<hipStream_t>(hip_stream));
+  return do_refresh(h, static_cast<hipStream_t>(hip_stream), h->t);
 }
 
 int shampoo_destroy(shampoo_t h) {
@@ -808,7 +871,7 @@ int shampoo_get_timing(shampoo_t h, shampoo_timing_t* out) {
   // recorded event).
   double nf = 0.0;
   HIP_CHECK(hipMemcpy(&nf, h->at<void>(h->plan.off_flops), sizeof(double), hipMemcpyDeviceToHost));
-  out->flops[kNewtonGemm] = nf;
+  out->flops[kNewtonGemm] += nf;  // the Chebyshev products are counted on the host
   return SHAMPOO_OK;
 }
 

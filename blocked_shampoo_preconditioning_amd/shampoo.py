@@ -27,7 +27,7 @@ SHAMPOO_BF16 = 1
 SHAMPOO_FORCE_REFRESH = 1
 SHAMPOO_NO_AUTO_REFRESH = 2
 TIMING_CLASSES = ("pack", "stats", "norms", "newton_gemm", "newton_aux", "apply")
-ROOT_METHODS = {"newton": 0, "newton_db": 1}
+ROOT_METHODS = {"newton": 0, "newton_db": 1, "chebyshev": 2}
 
 
 class MatrixDesc(ctypes.Structure):
@@ -41,7 +41,8 @@ class Config(ctypes.Structure):
                 ("root_every", ctypes.c_int32), ("newton_max_iters", ctypes.c_int32),
                 ("newton_tol", ctypes.c_double), ("newton_scale_mode", ctypes.c_int32),
                 ("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
-                ("momentum", ctypes.c_double), ("root_method", ctypes.c_int32)]
+                ("momentum", ctypes.c_double), ("root_method", ctypes.c_int32),
+                ("cheb_degree", ctypes.c_int32)]
 
 
 class Layout(ctypes.Structure):
@@ -236,7 +237,7 @@ class Shampoo:
     def __init__(self, shapes, block_rows=1024, block_cols=1024, beta2=0.999, eps=1e-6, lr=1e-3,
                  root_every=10, stat_scale=None, newton_max_iters=25, newton_tol=1e-6,
                  newton_scale_mode=2, dtype="f32", device="cuda", lds=None, momentum=0.0,
-                 root_method="newton"):
+                 root_method="newton", cheb_degree=128):
         import torch
         self.torch = torch
         self.shapes = [tuple(int(v) for v in s) for s in shapes]
@@ -250,6 +251,7 @@ class Shampoo:
         cfg.newton_scale_mode = newton_scale_mode
         cfg.momentum = momentum
         cfg.root_method = ROOT_METHODS[root_method]
+        cfg.cheb_degree = cheb_degree
         dt = {"f32": SHAMPOO_F32, "bf16": SHAMPOO_BF16}[dtype]
         cfg.param_dtype = cfg.grad_dtype = dt
         self.cfg = cfg

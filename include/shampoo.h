@@ -110,7 +110,15 @@ typedef struct {
                                         then Z2 ~ Y1^(-1/2) = A~^(-1/4) (a reading
                                         of the DASH page's solver); newton_*
                                         settings apply to each stage and the
-                                        spectral targets of the scale modes are 1 */
+                                        spectral targets of the scale modes are 1;
+                                     2: Chebyshev: X = s^(-1/4) p(A/s), p the
+                                        degree-cheb_degree interpolant of x^(-1/4)
+                                        on [beta2^t eps / s, 1] at the Chebyshev
+                                        points, s an upper bound of the spectrum
+                                        (min(lam/0.55, ||A||_F, ||A||_inf)),
+                                        Clenshaw recurrence: cheb_degree - 1
+                                        products, no iteration, no early exit    */
+  int32_t cheb_degree;            /* 2..1024, default 128                        */
 } shampoo_config_t;
 
 /* Byte offsets of the state inside the caller's workspace (for inspection
@@ -151,7 +159,7 @@ typedef struct shampoo_ctx* shampoo_t;
 /* Fill *cfg with the defaults: square blocks of 1024, beta2 0.999,
  * stat_scale 1 - beta2, eps 1e-6, lr 1e-3, root_every 10, 25 Newton
  * iterations at most, tol 1e-6, scale mode 2, fp32 parameters and gradients,
- * no momentum, coupled Newton roots. */
+ * no momentum, coupled Newton roots (Chebyshev degree 128 if selected). */
 int shampoo_config_default(shampoo_config_t* cfg);
 
 /* Bytes of device workspace needed for these matrices (host only, no HIP

@@ -60,6 +60,9 @@ __all__ = [
     "db_scale",
     "sqrt_pair_db",
     "inverse_root_newton_db",
+    "chebyshev_interval",
+    "chebyshev_coefficients",
+    "inverse_root_chebyshev",
     "precondition",
     "round_to_bf16",
     "is_refresh_step",
@@ -338,6 +341,59 @@ def inverse_root_newton_db(A, max_iters=25, tol=0.0, scale_mode=2):
     return s ** -0.25 * Z2, (info1, info2)
 
 
+def chebyshev_interval(A, floor, power_iters=16):
+    """Scale s and lower end r of the Chebyshev interval [r, 1] for A / s.
+
+    s = min(lam / 0.55, min(||A||_F, ||A||_inf)) bounds the largest eigenvalue
+    from above (lam is mode 2's power estimate, which is at least 0.55 lam_max
+    unless v_0 is almost orthogonal to the top eigenvector; the norms bound it
+    always). floor is a lower bound of the smallest eigenvalue: for a Shampoo
+    statistic, beta2^t eps (the decayed eps I start plus a PSD sum). r =
+    floor / s, kept below 0.999."""
+    A = np.asarray(A, dtype=np.float64)
+    fro = math.sqrt(float(np.sum(A * A)))
+    bound = min(fro, float(np.max(np.sum(np.abs(A), axis=1))))
+    lam = 2.0 * newton_scale(A, 4, 2, power_iters)
+    s = min(lam / 0.55, bound) if lam > 0.0 else bound
+    r = min(floor / s, 0.999) if s > 0.0 else 0.999
+    return s, r
+
+
+def chebyshev_coefficients(r, degree):
+    """Coefficients c_0..c_d of the Chebyshev interpolant of x^(-1/4) on
+    [r, 1] at the d + 1 Chebyshev points (first kind): with
+    theta_j = pi (j + 1/2) / (d + 1) and x_j = ((1 - r) cos theta_j + 1 + r) / 2,
+    c_k = 2 / (d + 1) sum_j x_j^(-1/4) cos(k theta_j); the interpolant is
+    c_0 / 2 + sum_{k>=1} c_k T_k(t), t = (2 x - 1 - r) / (1 - r)."""
+    N = degree + 1
+    theta = math.pi * (np.arange(N) + 0.5) / N
+    x = ((1.0 - r) * np.cos(theta) + 1.0 + r) / 2.0
+    fx = x ** -0.25
+    return np.array([2.0 / N * float(np.sum(fx * np.cos(k * theta))) for k in range(N)])
+
+
+def inverse_root_chebyshev(A, floor, degree=128, power_iters=16, interval=None):
+    """A^(-1/4) as s^(-1/4) p(A / s), p the degree-d Chebyshev interpolant of
+    x^(-1/4) on [r, 1] (chebyshev_interval), evaluated by the Clenshaw
+    recurrence in matrices: B_(d+1) = B_(d+2) = 0,
+    B_k = c_k I + 2 T B_(k+1) - B_(k+2), p = c_0 / 2 I + T B_1 - B_2 with
+    T = (2 A / s - (1 + r) I) / (1 - r). A reading of the DASH page's
+    Chebyshev inverse-root solver (the page gives no formula). interval, if
+    given, is the (s, r) to use instead of chebyshev_interval's."""
+    A = np.asarray(A, dtype=np.float64)
+    n = A.shape[0]
+    eye = np.eye(n)
+    s, r = chebyshev_interval(A, floor, power_iters) if interval is None else interval
+    c = chebyshev_coefficients(r, degree)
+    T = (2.0 * A / s - (1.0 + r) * eye) / (1.0 - r)
+    b1 = np.zeros((n, n))
+    b2 = np.zeros((n, n))
+    for k in range(degree, 0, -1):
+        b1, b2 = c[k] * eye + 2.0 * T @ b1 - b2, b1
+    P = 0.5 * c[0] * eye + T @ b1 - b2
+    return s ** -0.25 * P, (s, r)
+
+
 # ---------------------------------------------------------------------------
 # Preconditioned update ("Shampoo optimizer" page, last line of the loop;
 # podcast cue 20)
@@ -390,9 +446,10 @@ class ShampooOracle:
     root_every:   k of the refresh schedule (0: only explicit refresh).
     blocks:       optional subset of block ids to track (blocks are
                   independent, so a sample can be run alone).
-    root_method:  "eigh" (the definition), "newton" (coupled Newton) or
+    root_method:  "eigh" (the definition), "newton" (coupled Newton),
                   "newton_db" (two Denman-Beavers stages), the iterations with
-                  newton_iters / newton_tol / newton_scale_mode.
+                  newton_iters / newton_tol / newton_scale_mode, or "chebyshev"
+                  (degree cheb_degree on [beta2^t eps / s, 1]).
     param_bf16:   parameters are stored in bfloat16 after every update.
     momentum:     alpha of the momentum folded in before preconditioning
                   (0: none).
@@ -400,7 +457,8 @@ class ShampooOracle:
 
     def __init__(self, shapes, block_rows, block_cols, beta2, eps, lr, root_every,
                  stat_scale=None, blocks=None, root_method="eigh", newton_iters=25,
-                 newton_tol=0.0, newton_scale_mode=1, param_bf16=False, p=4, momentum=0.0):
+                 newton_tol=0.0, newton_scale_mode=1, param_bf16=False, p=4, momentum=0.0,
+                 cheb_degree=128):
         self.shapes = [tuple(s) for s in shapes]
         self.table = block_table(self.shapes, block_rows, block_cols)
         self.ids = list(range(len(self.table))) if blocks is None else sorted(set(blocks))
@@ -416,6 +474,7 @@ class ShampooOracle:
         self.param_bf16 = param_bf16
         self.p = p
         self.momentum = float(momentum)
+        self.cheb_degree = int(cheb_degree)
         self.t = 0
         self.state = {}
         for i in self.ids:
@@ -432,6 +491,9 @@ class ShampooOracle:
         if self.root_method == "newton_db":
             return inverse_root_newton_db(A, self.newton_iters, self.newton_tol,
                                           self.newton_scale_mode)
+        if self.root_method == "chebyshev":
+            floor = (self.beta2 ** self.t) * self.eps
+            return inverse_root_chebyshev(A, floor, self.cheb_degree)
         raise ValueError(self.root_method)
 
     def refresh_roots(self):

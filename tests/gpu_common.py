@@ -38,7 +38,7 @@ def make_shampoo(w):
     return Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
                    root_every=w.root_every, newton_max_iters=w.newton_max_iters,
                    newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype,
-                   momentum=w.momentum, root_method=w.root_method)
+                   momentum=w.momentum, root_method=w.root_method, cheb_degree=w.cheb_degree)
 
 
 def sample_blocks(w, k, seed=0):
@@ -89,7 +89,8 @@ def run_parity(w, steps, ids=None, root_method="eigh", check_update=True, on_ste
     orc = ShampooOracle(w.shapes, w.block_rows, w.block_cols, w.beta2, w.eps, w.lr, w.root_every,
                         blocks=ids, root_method=root_method, newton_iters=w.newton_max_iters,
                         newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode,
-                        param_bf16=(w.dtype == "bf16"), momentum=w.momentum)
+                        param_bf16=(w.dtype == "bf16"), momentum=w.momentum,
+                        cheb_degree=w.cheb_degree)
     W = {i: block_of(params[table[i].mat], table[i]) for i in ids}
     B, br, bc = sh.n_blocks, w.block_rows, w.block_cols
     U_out = torch.empty(B * br * bc, dtype=torch.float32, device=dev) if check_update else None

@@ -389,3 +389,32 @@ def test_newton_db_decoder_1b_sampled():
         assert r.stats_err <= STATS_TOL, r
         assert r.update_err <= UPDATE_TOL, r
     sh.close()
+
+
+# ---------------------------------------------------------------------------
+# Chebyshev roots (degree-d interpolant of x^(-1/4), Clenshaw recurrence)
+# ---------------------------------------------------------------------------
+def test_chebyshev_same_algorithm_small_ragged():
+    """Degree 24 on a ragged set: the GPU evaluates the same interpolant as the
+    fp64 oracle (its interval comes from the oracle's own statistics)."""
+    w = workload("gpt_small_b256", shapes=((300, 520), (256, 256), (130, 71)), root_every=2,
+                 root_method="chebyshev", cheb_degree=24, seed=95)
+    recs, sh, orc, params, W = run_parity(w, 4, root_method="chebyshev")
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= 1e-4, r
+    assert set(sh.newton_info()[0].cpu().tolist()) == {4}
+    sh.close()
+
+
+def test_chebyshev_decoder_1b_against_eigh():
+    """Degree 128 on the 1B-class set: the interpolant's own error on the
+    interval [beta2^t eps / s, 1] (~4e-4 at this conditioning) stays inside
+    the update bar against the definition (eigh roots)."""
+    w = workload("decoder_1b_b1024_f32", root_method="chebyshev", cheb_degree=128)
+    ids = sample_blocks(w, 3, seed=11)
+    recs, sh, orc, params, W = run_parity(w, 3, ids=ids)
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    sh.close()

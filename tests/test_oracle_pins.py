@@ -528,3 +528,55 @@ def test_growth_at_the_floor_is_a_stall_not_divergence():
         assert rel(X, inverse_root_eigh(A)) < 1e-12
     _, _, i_db = sqrt_pair_db(A / db_scale(A, 2), 60, 1e-30)
     assert i_db.status == "stalled"
+
+
+# ---------------------------------------------------------------------------
+# Chebyshev inverse root (interpolant of x^(-1/4), Clenshaw in matrices)
+# ---------------------------------------------------------------------------
+from oracle import chebyshev_coefficients, chebyshev_interval, inverse_root_chebyshev  # noqa: E402
+
+
+def test_chebyshev_matches_numpy_interpolant_on_scalars():
+    """1x1 and diagonal matrices: the matrix Clenshaw result equals numpy's own
+    Chebyshev interpolant of x^(-1/4) (an independent routine) evaluated at
+    a / s, times s^(-1/4)."""
+    a = np.array([3e-3, 0.02, 0.5, 1.0, 0.7])
+    floor = 1e-3
+    for deg in (8, 33):
+        X, (s, r) = inverse_root_chebyshev(np.diag(a), floor, deg)
+        p = np.polynomial.Chebyshev.interpolate(lambda t: t ** -0.25, deg, domain=[r, 1.0])
+        assert np.allclose(np.diag(X), s ** -0.25 * p(a / s), rtol=1e-11, atol=0)
+        assert np.count_nonzero(X - np.diag(np.diag(X))) == 0
+
+
+def test_chebyshev_coefficients_reproduce_the_function_at_the_nodes():
+    r, d = 0.05, 20
+    c = chebyshev_coefficients(r, d)
+    theta = math.pi * (np.arange(d + 1) + 0.5) / (d + 1)
+    x = ((1 - r) * np.cos(theta) + 1 + r) / 2
+    vals = 0.5 * c[0] + sum(c[k] * np.cos(k * theta) for k in range(1, d + 1))
+    assert np.allclose(vals, x ** -0.25, rtol=1e-13)
+
+
+def test_chebyshev_converges_to_eigh_and_interval_is_valid():
+    rng = np.random.default_rng(61)
+    A, Q, lam = spd(16, 30.0, rng)
+    A = 2e-3 * A + 1e-5 * np.eye(16)
+    floor = 1e-5
+    s, r = chebyshev_interval(A, floor)
+    lam = np.linalg.eigvalsh(A)
+    assert lam.max() <= s * (1 + 1e-12) and lam.min() >= r * s * (1 - 1e-12)
+    errs = [rel(inverse_root_chebyshev(A, floor, d)[0], inverse_root_eigh(A)) for d in (16, 48, 128)]
+    assert errs[0] > errs[1] > errs[2] and errs[2] < 1e-8
+
+
+def test_chebyshev_orthogonal_similarity():
+    rng = np.random.default_rng(63)
+    A, Q, lam = spd(6, 20.0, rng)
+    # the interval is not rotation-invariant (power iteration from the
+    # all-ones vector, inf-norm), the polynomial is: use one interval for both
+    iv = chebyshev_interval(A, 0.01)
+    Xa, _ = inverse_root_chebyshev(A, 0.01, 12, interval=iv)
+    Xd, _ = inverse_root_chebyshev(np.diag(lam), 0.01, 12, interval=iv)
+    assert np.count_nonzero(Xd - np.diag(np.diag(Xd))) == 0
+    assert rel(Xa, Q @ Xd @ Q.T) < 1e-12
