@@ -2,8 +2,9 @@
 
     python -m blocked_shampoo_preconditioning_amd.build
 
-Compiles csrc/kernels.hip and csrc/runtime.cpp with hipcc into one shared
-library next to this file. Packed fp32 instructions are disabled for the
+Compiles the HIP kernels (csrc/kernels.hip, csrc/tensor_kernels.hip) and the
+host runtime (csrc/runtime.cpp, roots.cpp, tensor_runtime.cpp) with hipcc into
+one shared library next to this file. Packed fp32 instructions are disabled for the
 device code (-packed-fp32-ops); hipcc's host pass warns that it does not know
 that feature, which is harmless.
 """
@@ -19,7 +20,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libshampoo_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "runtime.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "tensor_kernels.hip", "runtime.cpp",
+                                            "roots.cpp", "tensor_runtime.cpp")]
 ARCH = "gfx950"
 
 

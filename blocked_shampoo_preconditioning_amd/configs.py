@@ -78,6 +78,68 @@ WORKLOADS = {
               "Newton iterations, 10% diagonal blocks"),
 }
 
+# ---------------------------------------------------------------------------
+# Order-k tensors (podcast cue 26): conv filters [out, in, kh, kw]. The
+# podcast's image test bed is CIFAR-10 on a 32-layer ResNet (cue 36); its
+# convolution filters are 3 x 3 with 16, 32 and 64 channels in three stages
+# of five residual blocks (two convolutions each) after a 3 -> 16 stem.
+# ---------------------------------------------------------------------------
+def resnet_cifar_convs(n_blocks_per_stage=5, width=1):
+    """Conv filter shapes of a CIFAR ResNet (6n + 2 layers) at width x."""
+    c = [16 * width, 32 * width, 64 * width]
+    shapes = [(c[0], 3, 3, 3)]
+    cin = c[0]
+    for cout in c:
+        for _ in range(n_blocks_per_stage):
+            shapes.append((cout, cin, 3, 3))
+            shapes.append((cout, cout, 3, 3))
+            cin = cout
+    return tuple(shapes)
+
+
+@dataclass(frozen=True)
+class TensorWorkload:
+    name: str
+    shapes: tuple                 # per tensor, all of one order k
+    block_dims: tuple             # block size of every dimension
+    beta2: float = 0.999
+    eps: float = 1e-6
+    lr: float = 1e-3
+    root_every: int = 10
+    steps: int = 10
+    dtype: str = "f32"
+    grad: str = "iid"             # iid | row_scaled (one scale per index of dimension 0)
+    grad_std: float = 1.0
+    newton_max_iters: int = 25
+    newton_tol: float = 1e-6
+    newton_scale_mode: int = 2
+    momentum: float = 0.0
+    root_method: str = "newton"
+    cheb_degree: int = 128
+    init_std: float = 0.02
+    seed: int = 0
+    notes: str = field(default="", compare=False)
+
+
+TENSOR_WORKLOADS = {
+    "resnet32_cifar_convs": TensorWorkload(
+        name="resnet32_cifar_convs", shapes=resnet_cifar_convs(5, 1), block_dims=(64, 64, 3, 3),
+        root_every=10, steps=20, grad="row_scaled", grad_std=1e-2, seed=2001,
+        notes="the 31 conv filters of ResNet-32 for CIFAR-10, one block each (channels "
+              "zero-padded to 64)"),
+    "resnet32_x8_convs_b128": TensorWorkload(
+        name="resnet32_x8_convs_b128", shapes=resnet_cifar_convs(5, 8),
+        block_dims=(128, 128, 3, 3), root_every=10, steps=20, grad="row_scaled", grad_std=1e-2,
+        seed=2002,
+        notes="ResNet-32's conv filters at 8x channel width (128 / 256 / 512), blocks of "
+              "128 x 128 x 3 x 3: 201 blocks"),
+}
+
+
+def get_tensor(name) -> TensorWorkload:
+    return TENSOR_WORKLOADS[name]
+
+
 # Short aliases in the order the workloads are listed.
 ORDER = ("single_64x32", "gpt_small_b256", "gpt_small_b512_lowrank",
          "decoder_1b_b1024_f32", "decoder_1b_b1024_bf16")

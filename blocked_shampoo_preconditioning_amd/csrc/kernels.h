@@ -53,7 +53,7 @@ struct GemmProblem {
   int32_t resid_stride;
 };
 
-constexpr int kMaxProblems = 4;
+constexpr int kMaxProblems = 8;
 
 struct GemmLaunch {
   GemmProblem p[kMaxProblems];
@@ -69,14 +69,24 @@ struct UpdateArgs {
   float* out_packed;  // non-null: store U packed instead of updating params
 };
 
-// Factor addressing for the per-factor kernels: factors [0, B) are left
-// statistics of side nl, [B, 2B) right statistics of side nr; left factors
-// start at baseL, right factors at baseR (element offsets into a buffer).
+// Factor addressing for the per-factor kernels: factors come in groups (the
+// left and right statistics of a matrix block, or one statistic per tensor
+// dimension), B factors per group; factor f = g * B + i is the i-th factor
+// of group g, side side[g], stored at element offset off[g] + i * side[g]^2.
+constexpr int kMaxGroups = 4;
+
 struct FactorSet {
   int32_t B;
-  int32_t nl, nr;
-  int64_t offL, offR;  // element offsets of the first left / right factor
-  const int32_t* nreal;
+  int32_t n_groups;
+  int32_t side[kMaxGroups];
+  int64_t off[kMaxGroups];
+  const int32_t* nreal;  // real extent of every factor [n_groups * B]
+  __host__ __device__ int32_t count() const { return n_groups * B; }
+  __host__ __device__ int32_t max_side() const {
+    int32_t m = 0;
+    for (int g = 0; g < n_groups; ++g) m = side[g] > m ? side[g] : m;
+    return m;
+  }
 };
 
 // Power-iteration products of scale mode 2 (the first shares the norm pass).
@@ -91,21 +101,22 @@ constexpr float kFloorGuard = 1e-3f;
 struct NewtonCtl {
   int32_t solver;       // RootSolver
   float floor;          // lower bound of every statistic's spectrum: beta2^t eps
-  float* cheb;          // Chebyshev coefficient quadruples [2B][degree + 1][4]
+  float* cheb;          // Chebyshev coefficient quadruples [factor][degree + 1][4]
   int32_t degree;
   int32_t* status;
   int32_t* final_iter;
   float* scale;
   float* rprev;
-  float* cfac;          // s^(-1/4)
-  float* resid;         // partials [2B][resid_stride]
+  float* cfac;          // s^(-1/p)
+  float* resid;         // partials [factor][resid_stride]
   int32_t resid_stride;
-  int32_t ntiles_l, ntiles_r;  // tiles actually written per left / right factor
-  int32_t* active_count;       // [iter][2] factors active during the iteration
+  int32_t ntiles[kMaxGroups];  // tiles actually written per factor of each group
+  int32_t* active_count;       // [iter][kMaxGroups] factors active during the iteration
   double* flops_acc;           // algorithmic flops of the Newton products run
   float tol;
   int32_t max_iters;
   int32_t scale_mode;
+  int32_t p;            // the root is A^(-1/p)
 };
 
 // ---- launchers (return hipGetLastError()) ----
@@ -130,7 +141,7 @@ hipError_t launch_newton_init(const float* A, float* M0, float* X1, FactorSet fs
 // factors entering it) and after it (those still running), for the flop count.
 hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, int32_t shift,
                                int32_t prod_before, int32_t prod_after, hipStream_t s);
-// scale: multiply the kept iterate by s^(-1/4) (Denman-Beavers result).
+// scale: multiply the kept iterate by s^(-1/p) (Denman-Beavers result).
 hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, NewtonCtl c,
                                int32_t scale, hipStream_t s);
 // Chebyshev: per factor, the interval [r, 1] (r = floor / s), the interpolant's
@@ -149,5 +160,70 @@ inline int32_t sym_tiles(int32_t n, int32_t t) {
   int32_t T = n / t;
   return T * (T + 1) / 2;
 }
+
+}  // namespace shp
+
+// ===========================================================================
+// Order-k tensors (podcast "Preconditioned Optimization Without the Full
+// Matrix Cost", cue 26): one statistic per dimension. A packed block is a
+// dense row-major [b_0][b_1]...[b_(k-1)] array (E elements), zero past the
+// block's real extent.
+// ===========================================================================
+namespace shp {
+
+constexpr int kMaxOrder = 4;
+constexpr int kMaxSmallSide = 8;  // dimensions blocked at <= 8 take the small-side kernels
+
+struct TensorMeta {
+  const void* grad;
+  void* param;
+  int64_t stride[kMaxOrder];  // element strides of the tensor
+};
+
+struct TBlockMeta {
+  int32_t tensor;
+  int32_t origin[kMaxOrder];
+  int32_t extent[kMaxOrder];
+  int32_t pad_;
+};
+
+struct TensorGeom {
+  int32_t order;
+  int32_t b[kMaxOrder];  // packed extent of every dimension
+  int32_t E;             // elements of a packed block
+};
+
+// Gp[blk][e] (+ Mom = momentum Mom + Gp) from the tensors.
+hipError_t launch_tensor_pack(const TBlockMeta* blocks, const TensorMeta* tensors, TensorGeom g,
+                              int32_t B, int32_t grad_bf16, float* Gp, float* Mom, float momentum,
+                              hipStream_t s);
+// mode 0: dst[...] = Src (unpack into the param pointers of `tensors`);
+// mode 1: param -= lr * Src (update; bf16 parameters rounded to nearest even).
+hipError_t launch_tensor_scatter(const TBlockMeta* blocks, const TensorMeta* tensors, TensorGeom g,
+                                 int32_t B, const float* Src, float lr, int32_t param_bf16,
+                                 int32_t update, hipStream_t s);
+// Out[blk] = transpose of In[blk] viewed as R x C (Out is C x R); each Out
+// block holds out_stride elements, the R * C of the transpose then zeros.
+hipError_t launch_transpose(const float* In, int64_t in_stride, float* Out, int64_t out_stride,
+                            int32_t R, int32_t C, int32_t B, hipStream_t s);
+// Small-side statistic of dimension with extent n (<= 8) of In[blk] viewed as
+// [A][n][C]: H <- beta2 H + gamma sum_(a, c) In[a][l][c] In[a][l'][c].
+// partial: scratch of B * chunks * 36 floats.
+hipError_t launch_small_gram(const float* In, int64_t in_stride, int32_t A, int32_t n, int32_t C,
+                             int32_t B, float* partial, int32_t chunks, float* H, float beta2,
+                             float gamma, hipStream_t s);
+// Out[blk][r][j] = sum_l X[blk][j][l] In[blk][l][r]: the product along the
+// leading dimension (extent n), which moves that dimension last. FMA kernel
+// for small n or a row count R that the MFMA tiles do not divide.
+hipError_t launch_mode_product(const float* In, int64_t in_stride, const float* X, int64_t x_stride,
+                               float* Out, int64_t out_stride, int32_t n, int32_t R, int32_t B,
+                               hipStream_t s);
+// Small-side roots: per factor (count factors of side n, real extent nreal[f]),
+// fp64 cyclic Jacobi of H, X = V diag(max(lam, floor)^(-1/p)) V^T on the real
+// extent, zero elsewhere. status / final_iter / resid of each factor are written
+// (1 / sweeps / relative off-diagonal norm left; 3 if H is not finite).
+hipError_t launch_small_root(const float* H, float* X, int32_t n, int32_t count,
+                             const int32_t* nreal, float floor, int32_t p, int32_t* status,
+                             int32_t* final_iter, float* resid, hipStream_t s);
 
 }  // namespace shp

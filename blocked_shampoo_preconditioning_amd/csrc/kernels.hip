@@ -517,25 +517,23 @@ __global__ __launch_bounds__(256) void init_state_kernel(float* LR, int64_t nele
 
 __device__ __forceinline__ const float* factor_ptr(const float* base, const FactorSet& fs, int f,
                                                    int& n) {
-  if (f < fs.B) {
-    n = fs.nl;
-    return base + fs.offL + (int64_t)f * fs.nl * fs.nl;
-  }
-  n = fs.nr;
-  return base + fs.offR + (int64_t)(f - fs.B) * fs.nr * fs.nr;
+  const int g = f / fs.B, i = f - g * fs.B;
+  n = fs.side[g];
+  return base + fs.off[g] + (int64_t)i * n * n;
 }
 
 // ---------------------------------------------------------------------------
 // Norm scaling: one workgroup per factor, fixed-order reductions.
 //   mode 0: s = ||A||_F
-//   mode 1: s = min(||A||_F, ||A||_inf) * 2/5
+//   mode 1: s = min(||A||_F, ||A||_inf) * 2 / (p + 1)
 //   mode 2: s = lam / 2, lam the power-iteration estimate ||A v_k|| of the
 //           largest eigenvalue after kPowerIters (16) products from
 //           v_0 = 1 / sqrt(n). For symmetric A the ratios ||A^(j+1) v|| /
 //           ||A^j v|| never decrease, so lam >= lam_max |c_1|^(1/16) with c_1
 //           the component of v_0 on the top eigenvector: the spectrum of A / s
-//           stays inside the iteration's convergence region (0, 5) unless
-//           |c_1| < 4.3e-7. lam = 0 falls back to mode 1.
+//           stays inside the iteration's convergence region (0, p + 1)
+//           unless |c_1| < 2^-16 (p + 1)^-16 (4.3e-7 for p = 4). lam = 0 falls
+//           back to mode 1.
 // Only the real extent of a factor enters.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double block_sum(double v, double* red) {
@@ -589,10 +587,11 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   const double fro = sqrt(block_sum(sq, red));
   const double inf = fmax(fmax(red_inf[0], red_inf[1]), fmax(red_inf[2], red_inf[3]));
   const double bound = fmin(fro, inf);
-  // spectral target: Newton converges on (0, 5), the Denman-Beavers pair on (0, 2)
+  // spectral target: Newton converges on (0, p + 1), the Denman-Beavers pair on (0, 2)
   const bool db = c.solver == kNewtonDB;
   const bool cheb = c.solver == kChebyshev;
-  double s = c.scale_mode == 0 ? fro : bound * (db ? 1.0 : 0.4);
+  const double mode1 = db ? 1.0 : 2.0 / (c.p + 1);
+  double s = c.scale_mode == 0 ? fro : bound * mode1;
   if (c.scale_mode == 2 || cheb) {
     double lam = 0.0;
     for (int it = 0; it < kPowerIters; ++it) {
@@ -621,7 +620,7 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
       for (int r = threadIdx.x; r < nr; r += 256) v[r] = w[r] * inv;
       __syncthreads();
     }
-    s = lam > 0.0 ? lam * (db ? 1.0 : 0.5) : bound * (db ? 1.0 : 0.4);
+    s = lam > 0.0 ? lam * (db ? 1.0 : 0.5) : bound * mode1;
     // Chebyshev needs an upper bound of the spectrum: lam >= 0.55 lam_max
     // unless v_0 is almost orthogonal to the top eigenvector; the norm bound
     // holds always
@@ -630,7 +629,7 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   if (threadIdx.x == 0) {
     const bool ok = s > 0.0 && isfinite(s) && isfinite(fro);
     c.scale[f] = (float)s;
-    c.cfac[f] = ok ? (float)pow(s, -0.25) : 0.f;
+    c.cfac[f] = ok ? (float)pow(s, -1.0 / c.p) : 0.f;
     c.status[f] = ok ? 0 : 3;
     c.final_iter[f] = 0;
     c.rprev[f] = INFINITY;
@@ -638,7 +637,7 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
 }
 
 // Coupled Newton: M0 = A / s (identity on the padded part) and
-// X1 = s^(-1/4) (5 I - M0) / 4. Denman-Beavers: Y0 = A / s (into M0) and Z0 = I
+// X1 = s^(-1/p) ((p + 1) I - M0) / p. Denman-Beavers: Y0 = A / s (into M0) and Z0 = I
 // (into X1).
 __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restrict__ A,
                                                           float* __restrict__ M0,
@@ -651,6 +650,7 @@ __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restric
   const int64_t base = Af - A;
   const int nr = fs.nreal[f];
   const float s = c.scale[f], cf = c.cfac[f];
+  const float ip = 1.f / (float)c.p, ip1 = (float)(c.p + 1) / (float)c.p;
   const int64_t nn = (int64_t)n * n;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
        e += (int64_t)gridDim.x * blockDim.x) {
@@ -659,32 +659,32 @@ __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restric
     const float m = (r < nr && col < nr) ? Af[e] / s : id;
     M0[base + e] = m;
     if (c.solver != kChebyshev)
-      X1[base + e] = c.solver == kNewtonDB ? id : cf * (1.25f * id - 0.25f * m);
+      X1[base + e] = c.solver == kNewtonDB ? id : cf * (ip1 * id - ip * m);
   }
 }
 
 // After iteration `iter` (which produced M_{iter+1} and X_{iter+1}): residual
-// and stopping rule per factor; counts the factors that took part in the
-// iteration and adds the algorithmic flops of its symmetric products
-// (three at the first iteration, where X_1 needs no product, four after;
-// n^2 (n + 1) each).
+// and stopping rule per factor; counts the factors of each group that took
+// part in the iteration and adds the algorithmic flops of its symmetric
+// products (prod_before for every factor that entered, prod_after for those
+// still running; n^2 (n + 1) each).
 __global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, NewtonCtl c, int iter,
                                                             int shift, int prod_before,
                                                             int prod_after) {
-  __shared__ int cnt[2];
-  __shared__ int cnt_out[2];
-  if (threadIdx.x < 2) {
+  __shared__ int cnt[kMaxGroups];
+  __shared__ int cnt_out[kMaxGroups];
+  if (threadIdx.x < kMaxGroups) {
     cnt[threadIdx.x] = 0;
     cnt_out[threadIdx.x] = 0;
   }
   __syncthreads();
   const int cur = iter + shift;  // the iterate whose residual was just formed
-  const int nf = 2 * fs.B;
+  const int nf = fs.count();
   for (int f = threadIdx.x; f < nf; f += blockDim.x) {
     if (c.status[f] != 0) continue;
-    const bool left = f < fs.B;
-    atomicAdd(&cnt[left ? 0 : 1], 1);
-    const int nt = left ? c.ntiles_l : c.ntiles_r;
+    const int g = f / fs.B;
+    atomicAdd(&cnt[g], 1);
+    const int nt = c.ntiles[g];
     const float* p = c.resid + (size_t)f * c.resid_stride;
     float s = 0.f;
     for (int t = 0; t < nt; ++t) s += p[t];
@@ -711,21 +711,23 @@ __global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, Newton
     }
     // a rejected iterate leaves final_iter at the previous (accepted) one
     c.status[f] = st;
-    if (st == 0) atomicAdd(&cnt_out[left ? 0 : 1], 1);
+    if (st == 0) atomicAdd(&cnt_out[g], 1);
   }
   __syncthreads();
-  if (threadIdx.x < 2) c.active_count[iter * 2 + threadIdx.x] = cnt[threadIdx.x];
+  if (threadIdx.x < fs.n_groups) c.active_count[iter * kMaxGroups + threadIdx.x] = cnt[threadIdx.x];
   if (threadIdx.x == 0) {
-    const double nl = fs.nl, nr = fs.nr;
-    const double fl = nl * nl * (nl + 1.0), fr = nr * nr * (nr + 1.0);
-    c.flops_acc[0] += prod_before * (cnt[0] * fl + cnt[1] * fr) +
-                      prod_after * (cnt_out[0] * fl + cnt_out[1] * fr);
+    double fl = 0.0;
+    for (int g = 0; g < fs.n_groups; ++g) {
+      const double n = fs.side[g];
+      fl += (prod_before * (double)cnt[g] + prod_after * (double)cnt_out[g]) * n * n * (n + 1.0);
+    }
+    c.flops_acc[0] += fl;
   }
 }
 
 // Put the kept iterate into the root buffer: X_k lives in Xroot for even k
-// and in Xalt for odd k; X_0 = s^(-1/4) I is never stored.
-// scale = 1 (Denman-Beavers): the kept Z is multiplied by s^(-1/4), and Z_0 = I
+// and in Xalt for odd k; X_0 = s^(-1/p) I is never stored.
+// scale = 1 (Denman-Beavers): the kept Z is multiplied by s^(-1/p), and Z_0 = I
 // is stored in Xroot by the stage-2 init.
 __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ Xroot,
                                                            const float* __restrict__ Xalt,
@@ -753,7 +755,7 @@ __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ X
 
 // Stage 1's kept Y (index final_iter, Ybuf0 for even, Ybuf1 for odd) becomes
 // stage 2's Y0 in Ybuf0, and Z0 = I goes to Z0buf. A factor whose stage 1
-// diverged keeps its status and gets no stage 2 (its root becomes s^(-1/4) I).
+// diverged keeps its status and gets no stage 2 (its root becomes s^(-1/p) I).
 __global__ __launch_bounds__(256) void db_stage2_init_kernel(float* __restrict__ Ybuf0,
                                                              const float* __restrict__ Ybuf1,
                                                              float* __restrict__ Z0buf,
@@ -775,7 +777,7 @@ __global__ __launch_bounds__(256) void db_stage2_init_kernel(float* __restrict__
 // After the copy above has read every factor's final_iter: stage 2 starts.
 __global__ __launch_bounds__(256) void db_stage2_reset_kernel(FactorSet fs, NewtonCtl c) {
   const int f = blockIdx.x * blockDim.x + threadIdx.x;
-  if (f >= 2 * fs.B) return;
+  if (f >= fs.count()) return;
   if (c.status[f] != 3) {
     c.status[f] = 0;
     c.rprev[f] = INFINITY;
@@ -784,8 +786,8 @@ __global__ __launch_bounds__(256) void db_stage2_reset_kernel(FactorSet fs, Newt
 }
 
 // ---------------------------------------------------------------------------
-// Chebyshev inverse root: X = s^(-1/4) p(A / s), p the degree-d interpolant of
-// x^(-1/4) on [r, 1] at the Chebyshev points, r = floor / s; Clenshaw in
+// Chebyshev inverse root: X = s^(-1/p) q(A / s), q the degree-d interpolant of
+// x^(-1/p) on [r, 1] at the Chebyshev points, r = floor / s; Clenshaw in
 // matrices, one symmetric product per degree.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void cheb_setup_kernel(FactorSet fs, NewtonCtl c) {
@@ -800,7 +802,7 @@ __global__ __launch_bounds__(256) void cheb_setup_kernel(FactorSet fs, NewtonCtl
   for (int j = threadIdx.x; j < N; j += blockDim.x) {
     const double th = pi * (j + 0.5) / N;
     const double x = ((1.0 - r) * cos(th) + 1.0 + r) * 0.5;
-    fx[j] = pow(x, -0.25);
+    fx[j] = pow(x, -1.0 / c.p);
   }
   __syncthreads();
   const float a = (float)(4.0 / (1.0 - r)), b = (float)(-2.0 * (1.0 + r) / (1.0 - r));
@@ -966,16 +968,16 @@ hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile
 
 hipError_t launch_norms(const float* A, FactorSet fs, NewtonCtl c, hipStream_t s) {
   if (fs.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(norms_kernel, dim3(2 * fs.B), dim3(256), 0, s, A, fs, c);
+  hipLaunchKernelGGL(norms_kernel, dim3(fs.count()), dim3(256), 0, s, A, fs, c);
   return hipGetLastError();
 }
 
 hipError_t launch_newton_init(const float* A, float* M0, float* X1, FactorSet fs, NewtonCtl c,
                               hipStream_t s) {
   if (fs.B == 0) return hipSuccess;
-  const int nmax = std::max(fs.nl, fs.nr);
+  const int nmax = fs.max_side();
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
-  hipLaunchKernelGGL(newton_init_kernel, dim3(chunks, 2 * fs.B), dim3(256), 0, s, A, M0, X1, fs, c);
+  hipLaunchKernelGGL(newton_init_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, A, M0, X1, fs, c);
   return hipGetLastError();
 }
 
@@ -990,25 +992,25 @@ hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, int32_t 
 hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, NewtonCtl c,
                                int32_t scale, hipStream_t s) {
   if (fs.B == 0) return hipSuccess;
-  const int nmax = std::max(fs.nl, fs.nr);
+  const int nmax = fs.max_side();
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
-  hipLaunchKernelGGL(newton_final_kernel, dim3(chunks, 2 * fs.B), dim3(256), 0, s, Xroot, Xalt, fs,
+  hipLaunchKernelGGL(newton_final_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, Xroot, Xalt, fs,
                      c, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_cheb_setup(FactorSet fs, NewtonCtl c, hipStream_t s) {
   if (fs.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(cheb_setup_kernel, dim3(2 * fs.B), dim3(256), 0, s, fs, c);
+  hipLaunchKernelGGL(cheb_setup_kernel, dim3(fs.count()), dim3(256), 0, s, fs, c);
   return hipGetLastError();
 }
 
 hipError_t launch_cheb_init(const float* Ahat, float* Bd, float* Bd1, FactorSet fs, NewtonCtl c,
                             hipStream_t s) {
   if (fs.B == 0) return hipSuccess;
-  const int nmax = std::max(fs.nl, fs.nr);
+  const int nmax = fs.max_side();
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
-  hipLaunchKernelGGL(cheb_init_kernel, dim3(chunks, 2 * fs.B), dim3(256), 0, s, Ahat, Bd, Bd1, fs,
+  hipLaunchKernelGGL(cheb_init_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, Ahat, Bd, Bd1, fs,
                      c);
   return hipGetLastError();
 }
@@ -1016,11 +1018,11 @@ hipError_t launch_cheb_init(const float* Ahat, float* Bd, float* Bd1, FactorSet 
 hipError_t launch_db_stage2_init(float* Ybuf0, const float* Ybuf1, float* Z0buf, FactorSet fs,
                                  NewtonCtl c, hipStream_t s) {
   if (fs.B == 0) return hipSuccess;
-  const int nmax = std::max(fs.nl, fs.nr);
+  const int nmax = fs.max_side();
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
-  hipLaunchKernelGGL(db_stage2_init_kernel, dim3(chunks, 2 * fs.B), dim3(256), 0, s, Ybuf0, Ybuf1,
+  hipLaunchKernelGGL(db_stage2_init_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, Ybuf0, Ybuf1,
                      Z0buf, fs, c);
-  hipLaunchKernelGGL(db_stage2_reset_kernel, dim3((2 * fs.B + 255) / 256), dim3(256), 0, s, fs, c);
+  hipLaunchKernelGGL(db_stage2_reset_kernel, dim3((fs.count() + 255) / 256), dim3(256), 0, s, fs, c);
   return hipGetLastError();
 }
 

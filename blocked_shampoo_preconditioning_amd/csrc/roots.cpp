@@ -1,0 +1,243 @@
+// Inverse roots A^(-1/p) of batches of symmetric statistics on the symmetric
+// MFMA product core: norm scaling, then the coupled Newton iteration (any
+// even p up to 8), the Denman-Beavers pair (p = 4) or the Chebyshev
+// interpolant (any p). Every launch goes to the caller's stream; per-factor
+// stop rules run on the device (no host synchronisation).
+#include <cmath>
+
+#include "runtime_common.h"
+
+namespace shp_rt {
+namespace {
+
+// Symmetric-product launches of one stage, one per MFMA tile size in use.
+struct SymLaunches {
+  int n = 0;
+  int tile[shp::kMaxGroups];
+  shp::GemmLaunch g[shp::kMaxGroups];
+};
+
+shp::GemmProblem sym_problem(const float* P, const float* Q, float* C, int64_t stride, int n, int k,
+                             int batch) {
+  shp::GemmProblem g{};
+  g.P = P;
+  g.Q = Q;
+  g.C = C;
+  g.sP = stride;
+  g.sQ = stride;
+  g.sC = (int64_t)n * n;
+  g.M = n;
+  g.N = n;
+  g.K = k;
+  g.batch = batch;
+  g.alpha = 1.f;
+  return g;
+}
+
+// C = alpha P Q + beta D + gamma I over every factor; groups of one side and
+// tile stored back to back share a problem.
+void factor_problems(const RootJob& j, SymLaunches& L, const float* P, const float* Q, float* C,
+                     const float* D, float alpha, float beta, float gamma, bool resid) {
+  const shp::FactorSet& fs = j.fs;
+  for (int g = 0; g < fs.n_groups;) {
+    int e = g + 1;
+    while (e < fs.n_groups && fs.side[e] == fs.side[g] && j.tile[e] == j.tile[g] &&
+           fs.off[e] == fs.off[e - 1] + (int64_t)fs.B * fs.side[g] * fs.side[g])
+      ++e;
+    const int n = fs.side[g];
+    const int64_t off = fs.off[g];
+    shp::GemmProblem q = sym_problem(P + off, Q + off, C + off, (int64_t)n * n, n, n,
+                                     (e - g) * fs.B);
+    q.alpha = alpha;
+    q.beta = beta;
+    q.gamma = gamma;
+    if (D != nullptr) {
+      q.D = D + off;
+      q.sD = (int64_t)n * n;
+    }
+    q.status = j.c.status;
+    q.f0 = g * fs.B;
+    if (resid) {
+      q.resid = j.c.resid;
+      q.resid_stride = j.c.resid_stride;
+    }
+    int li = 0;
+    while (li < L.n && L.tile[li] != j.tile[g]) ++li;
+    if (li == L.n) {
+      L.tile[L.n] = j.tile[g];
+      L.g[L.n] = shp::GemmLaunch{};
+      ++L.n;
+    }
+    L.g[li].p[L.g[li].n_problems++] = q;
+    g = e;
+  }
+}
+
+int launch_all(shampoo_ctx* h, const SymLaunches& L, double flops, hipStream_t s) {
+  for (int i = 0; i < L.n; ++i) {
+    const int rc = timed(h, kNewtonGemm, i == 0 ? flops : 0.0, 0.0, s,
+                         [&] { return shp::launch_gemm_sym(L.g[i], L.tile[i], true, s); });
+    if (rc) return rc;
+  }
+  return SHAMPOO_OK;
+}
+
+double norm_bytes(const RootJob& j) {
+  double b = 0.0;
+  for (int g = 0; g < j.fs.n_groups; ++g) b += 4.0 * j.fs.B * (double)j.fs.side[g] * j.fs.side[g];
+  return b;
+}
+
+// Coupled Newton for A^(-1/p), p in {4, 6, 8}: T = ((p + 1) I - M) / p enters
+// through the affine epilogues
+//   T T = (M M - 2 (p + 1) M + (p + 1)^2 I) / p^2,   X T = ((p + 1) X - X M) / p,
+// then T^p by squaring (T^6 = T^4 T^2, T^8 = T^4 T^4) and M <- T^p M.
+// Buffers: M in s[iM], T^2 in s[iT], T^4 in s[2], T^6 / T^8 in s[3]; the new M
+// overwrites T^2 and the two swap roles. X ping-pongs between xroot (even
+// iterates) and xalt (odd); X_1 is formed by the init kernel.
+int newton(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
+  const shp::FactorSet& fs = j.fs;
+  const shp::NewtonCtl& c = j.c;
+  int rc = timed(h, kNorms, 0.0, norm_bytes(j), s, [&] { return shp::launch_norms(j.A, fs, c, s); });
+  if (rc) return rc;
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+             [&] { return shp::launch_newton_init(j.A, j.s[0], j.xalt, fs, c, s); });
+  if (rc) return rc;
+  const double p = c.p;
+  const float a2 = (float)(1.0 / (p * p)), b2 = (float)(-2.0 * (p + 1.0) / (p * p)),
+              g2 = (float)((p + 1.0) * (p + 1.0) / (p * p));
+  const float xa = (float)(-1.0 / p), xb = (float)((p + 1.0) / p);
+  const int per_iter = c.p == 4 ? 4 : 5;  // symmetric products of one iteration
+  int iM = 0, iT = 1;
+  for (int k = 0; k < c.max_iters; ++k) {
+    float* M = j.s[iM];
+    float* T2 = j.s[iT];
+    float* T4 = j.s[2];
+    float* Xcur = (k % 2 == 0) ? j.xroot : j.xalt;
+    float* Xnext = (k % 2 == 0) ? j.xalt : j.xroot;
+    SymLaunches l1, l2, l3, l4;
+    factor_problems(j, l1, M, M, T2, M, a2, b2, g2, false);                      // T^2
+    if (k > 0) factor_problems(j, l1, Xcur, M, Xnext, Xcur, xa, xb, 0.f, false);  // X T
+    factor_problems(j, l2, T2, T2, T4, nullptr, 1.f, 0.f, 0.f, false);            // T^4
+    const float* Tp = T4;
+    if (c.p == 6 || c.p == 8) {
+      factor_problems(j, l3, T4, c.p == 6 ? T2 : T4, j.s[3], nullptr, 1.f, 0.f, 0.f, false);
+      Tp = j.s[3];
+    }
+    factor_problems(j, l4, Tp, M, T2, nullptr, 1.f, 0.f, 0.f, true);  // M <- T^p M
+    if ((rc = launch_all(h, l1, 0.0, s))) return rc;
+    if ((rc = launch_all(h, l2, 0.0, s))) return rc;
+    if ((rc = launch_all(h, l3, 0.0, s))) return rc;
+    if ((rc = launch_all(h, l4, 0.0, s))) return rc;
+    const int before = k == 0 ? per_iter - 1 : per_iter;
+    rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+               [&] { return shp::launch_newton_check(fs, c, k, 1, before, 0, s); });
+    if (rc) return rc;
+    std::swap(iM, iT);
+  }
+  return timed(h, kNewtonAux, 0.0, 0.0, s,
+               [&] { return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 0, s); });
+}
+
+// Newton-DB: two Denman-Beavers square-root stages in inverse-free form on
+// the symmetric GEMM core. Y ping-pongs between s[0] (even k) and s[1] (odd),
+// Z between xroot and xalt, M = Z Y goes to s[2]. Per iteration: M (with the
+// residual partials), the check, then Y' = 3Y/2 - Y M/2 and Z' = 3Z/2 - M Z/2
+// in one launch. Stage 2 restarts from stage 1's kept Y with Z = I; the root
+// is s^(-1/4) times stage 2's kept Z.
+int newton_db(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
+  const shp::FactorSet& fs = j.fs;
+  const shp::NewtonCtl& c = j.c;
+  int rc = timed(h, kNorms, 0.0, norm_bytes(j), s, [&] { return shp::launch_norms(j.A, fs, c, s); });
+  if (rc) return rc;
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+             [&] { return shp::launch_newton_init(j.A, j.s[0], j.xroot, fs, c, s); });
+  if (rc) return rc;
+  const int kmax = c.max_iters;
+  for (int stage = 0; stage < 2; ++stage) {
+    for (int k = 0; k <= kmax; ++k) {
+      float* Y = j.s[k & 1];
+      float* Z = (k & 1) ? j.xalt : j.xroot;
+      float* Yn = j.s[(k + 1) & 1];
+      float* Zn = ((k + 1) & 1) ? j.xalt : j.xroot;
+      SymLaunches l1;
+      factor_problems(j, l1, Z, Y, j.s[2], nullptr, 1.f, 0.f, 0.f, true);  // M = Z Y
+      if ((rc = launch_all(h, l1, 0.0, s))) return rc;
+      const int after = k < kmax ? 2 : 0;
+      rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+                 [&] { return shp::launch_newton_check(fs, c, k, 0, 1, after, s); });
+      if (rc) return rc;
+      if (k == kmax) break;
+      SymLaunches l2;
+      factor_problems(j, l2, Y, j.s[2], Yn, Y, -0.5f, 1.5f, 0.f, false);  // Y (3I - M) / 2
+      factor_problems(j, l2, j.s[2], Z, Zn, Z, -0.5f, 1.5f, 0.f, false);  // (3I - M) Z / 2
+      if ((rc = launch_all(h, l2, 0.0, s))) return rc;
+    }
+    if (stage == 0) {
+      rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
+        return shp::launch_db_stage2_init(j.s[0], j.s[1], j.xroot, fs, c, s);
+      });
+      if (rc) return rc;
+    }
+  }
+  return timed(h, kNewtonAux, 0.0, 0.0, s,
+               [&] { return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 1, s); });
+}
+
+// Chebyshev: X = s^(-1/p) q(Ahat), Ahat = A / s, by the Clenshaw recurrence
+// B_k = a Ahat B_(k+1) + b B_(k+1) - B_(k+2) + c_k I (per-factor epilogue
+// coefficients); B_k lives in s[(d - k) % 3], the last product (k = 0) forms
+// q into xroot.
+int chebyshev(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
+  const shp::FactorSet& fs = j.fs;
+  shp::NewtonCtl c = j.c;
+  c.floor = (float)(std::pow(h->cfg.beta2, (double)j.t_stats) * h->cfg.eps);
+  const int d = c.degree;
+  int rc = timed(h, kNorms, 0.0, norm_bytes(j), s, [&] { return shp::launch_norms(j.A, fs, c, s); });
+  if (rc) return rc;
+  // Ahat in xalt (identity on tail padding); the coefficients (which mark
+  // every factor as a fixed-degree result); B_d, B_(d-1) in s[0], s[1]
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+             [&] { return shp::launch_newton_init(j.A, j.xalt, nullptr, fs, c, s); });
+  if (rc) return rc;
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] { return shp::launch_cheb_setup(fs, c, s); });
+  if (rc) return rc;
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
+             [&] { return shp::launch_cheb_init(j.xalt, j.s[0], j.s[1], fs, c, s); });
+  if (rc) return rc;
+  for (int k = d - 2; k >= 0; --k) {
+    float* Bk1 = j.s[(d - k - 1) % 3];
+    float* Bk2 = j.s[(d - k - 2) % 3];
+    float* Bk = k == 0 ? j.xroot : j.s[(d - k) % 3];
+    SymLaunches L;
+    factor_problems(j, L, j.xalt, Bk1, Bk, Bk1, 1.f, 0.f, 0.f, false);
+    for (int li = 0; li < L.n; ++li)
+      for (int i = 0; i < L.g[li].n_problems; ++i) {
+        shp::GemmProblem& q = L.g[li].p[i];
+        q.D2 = Bk2 + (q.D - Bk1);
+        q.sD2 = q.sD;
+        q.status = nullptr;  // every factor runs the whole recurrence
+        q.coef = c.cheb + (size_t)k * 4;
+        q.coef_stride = (d + 1) * 4;
+      }
+    if ((rc = launch_all(h, L, j.real_cube, s))) return rc;
+  }
+  return timed(h, kNewtonAux, 0.0, 0.0, s,
+               [&] { return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 2, s); });
+}
+
+}  // namespace
+
+int run_roots(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
+  if (j.fs.B == 0 || j.fs.n_groups == 0) return SHAMPOO_OK;
+  switch (j.c.solver) {
+    case shp::kNewtonDB:
+      return newton_db(h, j, s);
+    case shp::kChebyshev:
+      return chebyshev(h, j, s);
+    default:
+      return newton(h, j, s);
+  }
+}
+
+}  // namespace shp_rt

@@ -15,8 +15,9 @@
 #include <vector>
 
 #include "kernels.h"
+#include "runtime_common.h"
 
-namespace {
+namespace shp_rt {
 
 thread_local std::string g_last_error;
 
@@ -28,15 +29,6 @@ int fail(int code, const std::string& msg) {
 int hip_fail(hipError_t e, const char* where) {
   return fail(SHAMPOO_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
-
-#define HIP_CHECK(expr)                            \
-  do {                                             \
-    hipError_t e_ = (expr);                        \
-    if (e_ != hipSuccess) return hip_fail(e_, #expr); \
-  } while (0)
-
-constexpr int64_t kAlign = 256;
-int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int pick_tile(int a, int b) {
   int g = a, h = b;
@@ -50,23 +42,14 @@ int pick_tile(int a, int b) {
   return 32;
 }
 
-// Layout of the caller's workspace (byte offsets, 256-byte aligned).
-struct Plan {
-  int64_t B = 0;
-  int br = 0, bc = 0, n_mats = 0, tile = 32, max_iters = 1;
-  int ntiles_l = 0, ntiles_r = 0, resid_stride = 0;
-  int64_t fl = 0, fr = 0;  // elements of all left / right factors
-  int64_t off_blocks, off_mats, off_umats, off_nreal, off_status, off_final, off_scale, off_rprev,
-      off_cfac, off_active, off_flops, off_resid, off_gp, off_mom, off_lr, off_xroot, off_xalt,
-      off_s0, off_s1, off_s2, off_cheb, total;
-  bool momentum = false;
-};
-
-int validate_config(const shampoo_config_t* c) {
+// tensor: the block shape comes with the tensor descriptors, block_rows /
+// block_cols are not read
+int validate_config(const shampoo_config_t* c, bool tensor) {
   if (!c) return fail(SHAMPOO_ERR_INVALID_ARG, "config is NULL");
-  if (c->block_rows <= 0 || c->block_cols <= 0 || c->block_rows > 4096 || c->block_cols > 4096)
+  if (!tensor && (c->block_rows <= 0 || c->block_cols <= 0 || c->block_rows > 4096 ||
+                  c->block_cols > 4096))
     return fail(SHAMPOO_ERR_INVALID_ARG, "block shape must be in 1..4096");
-  if (c->block_rows % 32 || c->block_cols % 32)
+  if (!tensor && (c->block_rows % 32 || c->block_cols % 32))
     return fail(SHAMPOO_ERR_UNSUPPORTED, "block_rows and block_cols must be multiples of 32");
   if (!std::isfinite(c->beta2) || c->beta2 < 0.0 || c->beta2 > 1.0)
     return fail(SHAMPOO_ERR_INVALID_ARG, "beta2 must be in [0, 1]");
@@ -138,7 +121,7 @@ Plan make_plan(const shampoo_config_t* c, const shampoo_matrix_desc_t* m, int32_
   p.off_scale = take(2 * p.B * 4);
   p.off_rprev = take(2 * p.B * 4);
   p.off_cfac = take(2 * p.B * 4);
-  p.off_active = take((int64_t)(p.max_iters + 1) * 2 * 4);
+  p.off_active = take((int64_t)(p.max_iters + 1) * shp::kMaxGroups * 4);
   p.off_flops = take(8);
   p.off_cheb = c->root_method == shp::kChebyshev
                    ? take(2 * p.B * (int64_t)(c->cheb_degree + 1) * 4 * 4)
@@ -157,111 +140,73 @@ Plan make_plan(const shampoo_config_t* c, const shampoo_matrix_desc_t* m, int32_
   return p;
 }
 
-enum { kPack = 0, kStats = 1, kNorms = 2, kNewtonGemm = 3, kNewtonAux = 4, kApply = 5 };
+}  // namespace shp_rt
 
-struct TimedLaunch {
-  int cls;
-  hipEvent_t start, stop;
-  double flops, bytes;
-};
-
-}  // namespace
-
-struct shampoo_ctx {
-  shampoo_config_t cfg;
-  Plan plan;
-  char* ws = nullptr;
-  std::vector<shampoo_matrix_desc_t> mats;
-  std::vector<shp::BlockMeta> blocks;
-  std::vector<shp::MatMeta> meta_host;   // what the device table holds
-  bool meta_valid = false;
-  hipEvent_t meta_copied = nullptr;      // the last upload of meta_host has finished
-  int64_t t = 0;
-  bool roots_valid = false;
-  float stat_scale = 0.f;
-  // timing
-  bool timing = false;
-  std::vector<TimedLaunch> timed;
-  std::vector<hipEvent_t> event_pool;
-  double newton_flops_base = 0.0;
-
-  template <class T>
-  T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
-  float* gp() const { return at<float>(plan.off_gp); }
-  float* mom() const { return plan.momentum ? at<float>(plan.off_mom) : nullptr; }
-  float* lr() const { return at<float>(plan.off_lr); }
-  float* xroot() const { return at<float>(plan.off_xroot); }
-  float* xalt() const { return at<float>(plan.off_xalt); }
-  float* s(int i) const {
-    return at<float>(i == 0 ? plan.off_s0 : i == 1 ? plan.off_s1 : plan.off_s2);
-  }
-  float* gpT() const { return s(2); }   // packed transpose lives in Newton scratch
-  float* tmpT() const { return s(1); }  // apply intermediate likewise
-
-  shp::FactorSet factors() const {
-    shp::FactorSet fs;
-    fs.B = (int32_t)plan.B;
-    fs.nl = plan.br;
-    fs.nr = plan.bc;
-    fs.offL = 0;
-    fs.offR = plan.fl;
-    fs.nreal = at<int32_t>(plan.off_nreal);
-    return fs;
-  }
-  shp::NewtonCtl newton_ctl() const {
-    shp::NewtonCtl c;
-    c.solver = cfg.root_method;
-    c.status = at<int32_t>(plan.off_status);
-    c.final_iter = at<int32_t>(plan.off_final);
-    c.scale = at<float>(plan.off_scale);
-    c.rprev = at<float>(plan.off_rprev);
-    c.cfac = at<float>(plan.off_cfac);
-    c.resid = at<float>(plan.off_resid);
-    c.resid_stride = plan.resid_stride;
-    c.ntiles_l = plan.ntiles_l;
-    c.ntiles_r = plan.ntiles_r;
-    c.active_count = at<int32_t>(plan.off_active);
-    c.flops_acc = at<double>(plan.off_flops);
-    c.tol = (float)cfg.newton_tol;
-    c.floor = 0.f;
-    c.cheb = plan.off_cheb >= 0 ? at<float>(plan.off_cheb) : nullptr;
-    c.degree = cfg.cheb_degree;
-    c.max_iters = cfg.newton_max_iters;
-    c.scale_mode = cfg.newton_scale_mode;
-    return c;
-  }
-
-  hipEvent_t get_event() {
-    if (!event_pool.empty()) {
-      hipEvent_t e = event_pool.back();
-      event_pool.pop_back();
-      return e;
-    }
-    hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+hipEvent_t shampoo_ctx::get_event() {
+  if (!event_pool.empty()) {
+    hipEvent_t e = event_pool.back();
+    event_pool.pop_back();
     return e;
   }
-};
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
 
+namespace shp_rt {
 namespace {
 
-// Run `launch` with HIP events around it when timing is enabled.
-template <class F>
-int timed(shampoo_ctx* h, int cls, double flops, double bytes, hipStream_t s, F&& launch) {
-  hipEvent_t a = nullptr, b = nullptr;
-  if (h->timing) {
-    a = h->get_event();
-    b = h->get_event();
-    if (!a || !b) return fail(SHAMPOO_ERR_HIP, "hipEventCreate failed");
-    HIP_CHECK(hipEventRecord(a, s));
-  }
-  hipError_t e = launch();
-  if (e != hipSuccess) return hip_fail(e, "kernel launch");
-  if (h->timing) {
-    HIP_CHECK(hipEventRecord(b, s));
-    h->timed.push_back({cls, a, b, flops, bytes});
-  }
-  return SHAMPOO_OK;
+// Matrix-handle buffers inside the workspace.
+float* m_gp(const shampoo_ctx* h) { return h->at<float>(h->plan.off_gp); }
+float* m_mom(const shampoo_ctx* h) {
+  return h->plan.momentum ? h->at<float>(h->plan.off_mom) : nullptr;
+}
+float* m_lr(const shampoo_ctx* h) { return h->at<float>(h->plan.off_lr); }
+float* m_xroot(const shampoo_ctx* h) { return h->at<float>(h->plan.off_xroot); }
+float* m_xalt(const shampoo_ctx* h) { return h->at<float>(h->plan.off_xalt); }
+float* m_s(const shampoo_ctx* h, int i) {
+  return h->at<float>(i == 0 ? h->plan.off_s0 : i == 1 ? h->plan.off_s1 : h->plan.off_s2);
+}
+float* m_gpT(const shampoo_ctx* h) { return m_s(h, 2); }   // packed transpose lives in Newton scratch
+float* m_tmpT(const shampoo_ctx* h) { return m_s(h, 1); }  // apply intermediate likewise
+
+shp::FactorSet m_factors(const shampoo_ctx* h) {
+  const Plan& plan = h->plan;
+  shp::FactorSet fs{};
+  fs.B = (int32_t)plan.B;
+  fs.n_groups = 2;
+  fs.side[0] = plan.br;
+  fs.side[1] = plan.bc;
+  fs.off[0] = 0;
+  fs.off[1] = plan.fl;
+  fs.nreal = h->at<int32_t>(plan.off_nreal);
+  return fs;
+}
+
+shp::NewtonCtl m_ctl(const shampoo_ctx* h) {
+  const Plan& plan = h->plan;
+  const shampoo_config_t& cfg = h->cfg;
+  shp::NewtonCtl c{};
+  c.solver = cfg.root_method;
+  c.status = h->at<int32_t>(plan.off_status);
+  c.final_iter = h->at<int32_t>(plan.off_final);
+  c.scale = h->at<float>(plan.off_scale);
+  c.rprev = h->at<float>(plan.off_rprev);
+  c.cfac = h->at<float>(plan.off_cfac);
+  c.resid = h->at<float>(plan.off_resid);
+  c.resid_stride = plan.resid_stride;
+  c.ntiles[0] = plan.ntiles_l;
+  c.ntiles[1] = plan.ntiles_r;
+  c.active_count = h->at<int32_t>(plan.off_active);
+  c.flops_acc = h->at<double>(plan.off_flops);
+  c.tol = (float)cfg.newton_tol;
+  c.floor = 0.f;
+  c.cheb = plan.off_cheb >= 0 ? h->at<float>(plan.off_cheb) : nullptr;
+  c.degree = cfg.cheb_degree;
+  c.max_iters = cfg.newton_max_iters;
+  c.scale_mode = cfg.newton_scale_mode;
+  c.p = 4;
+  return c;
 }
 
 int upload_meta(shampoo_ctx* h, const void* const* grads, void* const* params, hipStream_t s) {
@@ -289,11 +234,14 @@ int upload_meta(shampoo_ctx* h, const void* const* grads, void* const* params, h
   return SHAMPOO_OK;
 }
 
+}  // namespace
+
 int check_ptrs(const shampoo_ctx* h, const void* const* ptrs, int dtype, const char* what) {
-  if (h->plan.n_mats > 0 && !ptrs) return fail(SHAMPOO_ERR_INVALID_ARG, std::string(what) + " is NULL");
+  const int n = (int)h->empty_item.size();
+  if (n > 0 && !ptrs) return fail(SHAMPOO_ERR_INVALID_ARG, std::string(what) + " is NULL");
   const uintptr_t align = dtype == SHAMPOO_BF16 ? 2 : 4;
-  for (int i = 0; i < h->plan.n_mats; ++i) {
-    const bool empty = h->mats[i].rows == 0 || h->mats[i].cols == 0;
+  for (int i = 0; i < n; ++i) {
+    const bool empty = h->empty_item[i] != 0;
     if (!ptrs[i] && !empty)
       return fail(SHAMPOO_ERR_INVALID_ARG, std::string(what) + "[" + std::to_string(i) + "] is NULL");
     if (reinterpret_cast<uintptr_t>(ptrs[i]) % align)
@@ -303,6 +251,8 @@ int check_ptrs(const shampoo_ctx* h, const void* const* ptrs, int dtype, const c
   }
   return SHAMPOO_OK;
 }
+
+namespace {
 
 double sym_flops(double n, double k) { return n * (n + 1.0) * k; }
 
@@ -314,8 +264,8 @@ int do_pack(shampoo_ctx* h, hipStream_t s) {
   const double bytes = real * esz + (p.momentum ? 4.0 : 2.0) * 4.0 * (double)p.B * p.br * p.bc;
   return timed(h, kPack, 0.0, bytes, s, [&] {
     return shp::launch_pack(h->at<shp::BlockMeta>(p.off_blocks), h->at<shp::MatMeta>(p.off_mats),
-                            (int32_t)p.B, p.br, p.bc, h->cfg.grad_dtype == SHAMPOO_BF16, h->gp(),
-                            h->gpT(), h->mom(), (float)h->cfg.momentum, s);
+                            (int32_t)p.B, p.br, p.bc, h->cfg.grad_dtype == SHAMPOO_BF16, m_gp(h),
+                            m_gpT(h), m_mom(h), (float)h->cfg.momentum, s);
   });
 }
 
@@ -343,9 +293,9 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
   if (p.B == 0) return SHAMPOO_OK;
   shp::GemmLaunch g{};
   // L = beta2 L + g Gp Gp^T: C[m][n] = sum_k GpT[k][m] GpT[k][n]
-  g.p[0] = sym_problem(h->gpT(), h->gpT(), h->lr(), (int64_t)p.bc * p.br, p.br, p.bc, (int)p.B);
+  g.p[0] = sym_problem(m_gpT(h), m_gpT(h), m_lr(h), (int64_t)p.bc * p.br, p.br, p.bc, (int)p.B);
   // R = beta2 R + g Gp^T Gp: C[m][n] = sum_k Gp[k][m] Gp[k][n]
-  g.p[1] = sym_problem(h->gp(), h->gp(), h->lr() + p.fl, (int64_t)p.br * p.bc, p.bc, p.br, (int)p.B);
+  g.p[1] = sym_problem(m_gp(h), m_gp(h), m_lr(h) + p.fl, (int64_t)p.br * p.bc, p.bc, p.br, (int)p.B);
   for (int i = 0; i < 2; ++i) {
     g.p[i].alpha = h->stat_scale;
     g.p[i].beta = (float)h->cfg.beta2;
@@ -360,40 +310,6 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
   return timed(h, kStats, flops, bytes, s, [&] { return shp::launch_gemm_sym(g, p.tile, false, s); });
 }
 
-// One batched symmetric product over all factors (left and right problems):
-// C = alpha P Q + beta D + gamma I.
-void factor_problems(const shampoo_ctx* h, shp::GemmLaunch& g, const float* P, const float* Q,
-                     float* C, const float* D, float alpha, float beta, float gamma, bool resid) {
-  const Plan& p = h->plan;
-  const shp::NewtonCtl c = h->newton_ctl();
-  auto add = [&](int64_t off, int n, int batch, int f0) {
-    shp::GemmProblem q = sym_problem(P + off, Q + off, C + off, (int64_t)n * n, n, n, batch);
-    q.alpha = alpha;
-    q.beta = beta;
-    q.gamma = gamma;
-    if (D != nullptr) {
-      q.D = D + off;
-      q.sD = (int64_t)n * n;
-    }
-    q.status = c.status;
-    q.f0 = f0;
-    if (resid) {
-      q.resid = c.resid;
-      q.resid_stride = c.resid_stride;
-    }
-    g.p[g.n_problems++] = q;
-  };
-  if (p.br == p.bc) {
-    add(0, p.br, (int)(2 * p.B), 0);
-  } else {
-    add(0, p.br, (int)p.B, 0);
-    add(p.fl, p.bc, (int)p.B, (int)p.B);
-  }
-}
-
-int do_refresh_db(shampoo_ctx* h, hipStream_t s);
-int do_refresh_cheb(shampoo_ctx* h, int64_t t_stats, hipStream_t s);
-
 // t_stats: the step whose statistics the roots are taken of (for the
 // Chebyshev interval's lower end beta2^t eps).
 int do_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
@@ -402,147 +318,18 @@ int do_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
     h->roots_valid = true;
     return SHAMPOO_OK;
   }
-  if (h->cfg.root_method == shp::kNewtonDB) return do_refresh_db(h, s);
-  if (h->cfg.root_method == shp::kChebyshev) return do_refresh_cheb(h, t_stats, s);
-  const shp::FactorSet fs = h->factors();
-  const shp::NewtonCtl c = h->newton_ctl();
-  double nbytes = 0.0;
-  for (const auto& b : h->blocks) nbytes += 4.0 * ((double)b.m * b.m + (double)b.n * b.n);
-  int rc = timed(h, kNorms, 0.0, nbytes, s, [&] { return shp::launch_norms(h->lr(), fs, c, s); });
-  if (rc) return rc;
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_newton_init(h->lr(), h->s(0), h->xalt(), fs, c, s); });
-  if (rc) return rc;
-  int mi = 0;  // M_k lives in s(mi); T2 goes to s(1 - mi), T4 to s(2)
-  for (int k = 0; k < h->cfg.newton_max_iters; ++k) {
-    float* Mk = h->s(mi);
-    float* T2 = h->s(1 - mi);
-    float* T4 = h->s(2);
-    float* Xcur = (k % 2 == 0) ? h->xroot() : h->xalt();
-    float* Xnext = (k % 2 == 0) ? h->xalt() : h->xroot();
-    // T = (5 I - M) / 4 enters through the affine epilogue:
-    shp::GemmLaunch g1{};
-    factor_problems(h, g1, Mk, Mk, T2, Mk, 0.0625f, -0.625f, 1.5625f, false);  // T2 = T T
-    if (k > 0) factor_problems(h, g1, Xcur, Mk, Xnext, Xcur, -0.25f, 1.25f, 0.f, false);  // X T
-    shp::GemmLaunch g2{};
-    factor_problems(h, g2, T2, T2, T4, nullptr, 1.f, 0.f, 0.f, false);      // T4 = T2 T2
-    shp::GemmLaunch g3{};
-    factor_problems(h, g3, T4, Mk, T2, nullptr, 1.f, 0.f, 0.f, true);       // M' = T4 M
-    rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g1, p.tile, true, s); });
-    if (rc) return rc;
-    rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g2, p.tile, true, s); });
-    if (rc) return rc;
-    rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g3, p.tile, true, s); });
-    if (rc) return rc;
-    const int before = k == 0 ? 3 : 4;
-    rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-               [&] { return shp::launch_newton_check(fs, c, k, 1, before, 0, s); });
-    if (rc) return rc;
-    mi = 1 - mi;
-  }
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_newton_final(h->xroot(), h->xalt(), fs, c, 0, s); });
-  if (rc) return rc;
-  h->roots_valid = true;
-  return SHAMPOO_OK;
-}
-
-// Newton-DB: two Denman-Beavers square-root stages in inverse-free form on
-// the symmetric GEMM core. Y ping-pongs between S0 (even k) and S1 (odd), Z
-// between Xroot and Xalt, M = Z Y goes to S2. Per iteration: M (with the
-// residual partials), the check, then Y' = 3Y/2 - Y M/2 and Z' = 3Z/2 - M Z/2
-// in one launch. Stage 2 restarts from stage 1's kept Y with Z = I; the root
-// is s^(-1/4) times stage 2's kept Z.
-int do_refresh_db(shampoo_ctx* h, hipStream_t s) {
-  const Plan& p = h->plan;
-  const shp::FactorSet fs = h->factors();
-  const shp::NewtonCtl c = h->newton_ctl();
-  double nbytes = 0.0;
-  for (const auto& b : h->blocks) nbytes += 4.0 * ((double)b.m * b.m + (double)b.n * b.n);
-  int rc = timed(h, kNorms, 0.0, nbytes, s, [&] { return shp::launch_norms(h->lr(), fs, c, s); });
-  if (rc) return rc;
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_newton_init(h->lr(), h->s(0), h->xroot(), fs, c, s); });
-  if (rc) return rc;
-  const int kmax = h->cfg.newton_max_iters;
-  for (int stage = 0; stage < 2; ++stage) {
-    for (int k = 0; k <= kmax; ++k) {
-      float* Y = h->s(k & 1);
-      float* Z = (k & 1) ? h->xalt() : h->xroot();
-      float* Yn = h->s((k + 1) & 1);
-      float* Zn = ((k + 1) & 1) ? h->xalt() : h->xroot();
-      shp::GemmLaunch g1{};
-      factor_problems(h, g1, Z, Y, h->s(2), nullptr, 1.f, 0.f, 0.f, true);  // M = Z Y
-      rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g1, p.tile, true, s); });
-      if (rc) return rc;
-      const int after = k < kmax ? 2 : 0;
-      rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-                 [&] { return shp::launch_newton_check(fs, c, k, 0, 1, after, s); });
-      if (rc) return rc;
-      if (k == kmax) break;
-      shp::GemmLaunch g2{};
-      factor_problems(h, g2, Y, h->s(2), Yn, Y, -0.5f, 1.5f, 0.f, false);  // Y (3I - M) / 2
-      factor_problems(h, g2, h->s(2), Z, Zn, Z, -0.5f, 1.5f, 0.f, false);  // (3I - M) Z / 2
-      rc = timed(h, kNewtonGemm, 0.0, 0.0, s, [&] { return shp::launch_gemm_sym(g2, p.tile, true, s); });
-      if (rc) return rc;
-    }
-    if (stage == 0) {
-      rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
-        return shp::launch_db_stage2_init(h->s(0), h->s(1), h->xroot(), fs, c, s);
-      });
-      if (rc) return rc;
-    }
-  }
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_newton_final(h->xroot(), h->xalt(), fs, c, 1, s); });
-  if (rc) return rc;
-  h->roots_valid = true;
-  return SHAMPOO_OK;
-}
-
-int do_refresh_cheb(shampoo_ctx* h, int64_t t_stats, hipStream_t s) {
-  const Plan& p = h->plan;
-  const shp::FactorSet fs = h->factors();
-  shp::NewtonCtl c = h->newton_ctl();
-  c.floor = (float)(std::pow(h->cfg.beta2, (double)t_stats) * h->cfg.eps);
-  const int d = h->cfg.cheb_degree;
-  double nbytes = 0.0;
-  for (const auto& b : h->blocks) nbytes += 4.0 * ((double)b.m * b.m + (double)b.n * b.n);
-  int rc = timed(h, kNorms, 0.0, nbytes, s, [&] { return shp::launch_norms(h->lr(), fs, c, s); });
-  if (rc) return rc;
-  // Ahat = A / s in Xalt (identity on tail padding); then the coefficients
-  // (which mark every factor as a fixed-degree result); B_d, B_(d-1) in S0, S1
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_newton_init(h->lr(), h->xalt(), nullptr, fs, c, s); });
-  if (rc) return rc;
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] { return shp::launch_cheb_setup(fs, c, s); });
-  if (rc) return rc;
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_cheb_init(h->xalt(), h->s(0), h->s(1), fs, c, s); });
-  if (rc) return rc;
-  double fprod = 0.0;
+  RootJob j;
+  j.fs = m_factors(h);
+  j.c = m_ctl(h);
+  j.A = m_lr(h);
+  j.xroot = m_xroot(h);
+  j.xalt = m_xalt(h);
+  for (int i = 0; i < 3; ++i) j.s[i] = m_s(h, i);
+  j.tile[0] = j.tile[1] = p.tile;
   for (const auto& b : h->blocks)
-    fprod += (double)b.m * b.m * (b.m + 1.0) + (double)b.n * b.n * (b.n + 1.0);
-  // B_k = a Ahat B_(k+1) + b B_(k+1) - B_(k+2) + c_k I, buffer of B_k: S[(d - k) % 3];
-  // the last product (k = 0) forms p into Xroot
-  for (int k = d - 2; k >= 0; --k) {
-    float* Bk1 = h->s((d - k - 1) % 3);
-    float* Bk2 = h->s((d - k - 2) % 3);
-    float* Bk = k == 0 ? h->xroot() : h->s((d - k) % 3);
-    shp::GemmLaunch g{};
-    factor_problems(h, g, h->xalt(), Bk1, Bk, Bk1, 1.f, 0.f, 0.f, false);
-    for (int i = 0; i < g.n_problems; ++i) {
-      g.p[i].D2 = Bk2 + (g.p[i].D - Bk1);
-      g.p[i].sD2 = g.p[i].sD;
-      g.p[i].status = nullptr;  // every factor runs the whole recurrence
-      g.p[i].coef = c.cheb + (size_t)k * 4;
-      g.p[i].coef_stride = (d + 1) * 4;
-    }
-    rc = timed(h, kNewtonGemm, fprod, 0.0, s, [&] { return shp::launch_gemm_sym(g, p.tile, true, s); });
-    if (rc) return rc;
-  }
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_newton_final(h->xroot(), h->xalt(), fs, c, 2, s); });
+    j.real_cube += (double)b.m * b.m * (b.m + 1.0) + (double)b.n * b.n * (b.n + 1.0);
+  j.t_stats = t_stats;
+  const int rc = run_roots(h, j, s);
   if (rc) return rc;
   h->roots_valid = true;
   return SHAMPOO_OK;
@@ -555,11 +342,11 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   // momentum the preconditioned matrix is the momentum buffer
   shp::GemmLaunch g1{};
   shp::GemmProblem a{};
-  a.P = p.momentum ? h->mom() : h->gp();
+  a.P = p.momentum ? m_mom(h) : m_gp(h);
   a.sP = (int64_t)p.br * p.bc;
-  a.Q = h->xroot();
+  a.Q = m_xroot(h);
   a.sQ = (int64_t)p.br * p.br;
-  a.C = h->tmpT();
+  a.C = m_tmpT(h);
   a.sC = (int64_t)p.bc * p.br;
   a.M = p.bc;
   a.N = p.br;
@@ -571,9 +358,9 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   // U[m][n] = sum_k TmpT[k][m] X_R[k][n]   (= X_L Gp X_R, br x bc)
   shp::GemmLaunch g2{};
   shp::GemmProblem b{};
-  b.P = h->tmpT();
+  b.P = m_tmpT(h);
   b.sP = (int64_t)p.bc * p.br;
-  b.Q = h->xroot() + p.fl;
+  b.Q = m_xroot(h) + p.fl;
   b.sQ = (int64_t)p.bc * p.bc;
   b.C = nullptr;
   b.M = p.br;
@@ -600,6 +387,9 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
 }
 
 }  // namespace
+}  // namespace shp_rt
+
+using namespace shp_rt;
 
 // ===========================================================================
 // C ABI
@@ -628,7 +418,7 @@ int shampoo_config_default(shampoo_config_t* cfg) {
 
 int shampoo_workspace_size(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats,
                            int32_t n_mats, size_t* bytes_out) {
-  int rc = validate_config(cfg);
+  int rc = validate_config(cfg, false);
   if (rc) return rc;
   rc = validate_mats(mats, n_mats);
   if (rc) return rc;
@@ -639,7 +429,7 @@ int shampoo_workspace_size(const shampoo_config_t* cfg, const shampoo_matrix_des
 
 int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats, int32_t n_mats,
                  void* workspace, size_t workspace_bytes, void* hip_stream, shampoo_t* out) {
-  int rc = validate_config(cfg);
+  int rc = validate_config(cfg, false);
   if (rc) return rc;
   rc = validate_mats(mats, n_mats);
   if (rc) return rc;
@@ -658,8 +448,10 @@ int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats,
   if (!h) return fail(SHAMPOO_ERR_INVALID_ARG, "out of host memory");
   h->cfg = *cfg;
   h->plan = plan;
+  h->off_flops = plan.off_flops;
   h->ws = static_cast<char*>(workspace);
   h->mats.assign(mats, mats + n_mats);
+  for (int i = 0; i < n_mats; ++i) h->empty_item.push_back(mats[i].rows == 0 || mats[i].cols == 0);
   h->stat_scale = (float)(cfg->stat_scale < 0.0 ? 1.0 - cfg->beta2 : cfg->stat_scale);
   // block map: matrices in registration order, row-major blocks inside each
   std::vector<int32_t> nreal;
@@ -702,7 +494,7 @@ int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats,
     if (e == hipSuccess && plan.momentum)
       e = hipMemsetAsync(h->at<void>(plan.off_mom), 0, plan.B * plan.br * plan.bc * 4, s);
     if (e == hipSuccess)
-      e = shp::launch_init_state(h->lr(), plan.fl, plan.br, plan.fr, plan.bc, (int32_t)plan.B,
+      e = shp::launch_init_state(m_lr(h), plan.fl, plan.br, plan.fr, plan.bc, (int32_t)plan.B,
                                  (float)cfg->eps, s);
     // the host copies above are from pageable memory; make sure they are done
     // before the temporaries go away
@@ -729,6 +521,11 @@ int shampoo_step(shampoo_t h, void* const* params, const void* const* grads, uin
     return fail(SHAMPOO_ERR_NO_ROOTS, "no roots yet: pass SHAMPOO_FORCE_REFRESH or call "
                                       "shampoo_refresh_roots first");
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (h->tensor) {
+    if ((rc = tensor_step(h, params, grads, refresh, t, s))) return rc;
+    h->t = t;
+    return SHAMPOO_OK;
+  }
   rc = upload_meta(h, grads, params, s);
   if (rc) return rc;
   if ((rc = do_pack(h, s))) return rc;
@@ -741,6 +538,7 @@ int shampoo_step(shampoo_t h, void* const* params, const void* const* grads, uin
 
 int shampoo_refresh_roots(shampoo_t h, void* hip_stream) {
   if (!h) return fail(SHAMPOO_ERR_INVALID_ARG, "handle is NULL");
+  if (h->tensor) return tensor_refresh(h, static_cast<hipStream_t>(hip_stream), h->t);
   return do_refresh(h, static_cast<hipStream_t>(hip_stream), h->t);
 }
 
@@ -758,6 +556,7 @@ int shampoo_destroy(shampoo_t h) {
 
 int shampoo_state_layout(shampoo_t h, shampoo_layout_t* out) {
   if (!h || !out) return fail(SHAMPOO_ERR_INVALID_ARG, "NULL argument");
+  if (h->tensor) return tensor_layout(h, out);
   out->n_blocks = h->plan.B;
   out->grad_packed = h->plan.off_gp;
   out->stats = h->plan.off_lr;
@@ -788,6 +587,7 @@ int shampoo_pack(shampoo_t h, const void* const* grads, void* hip_stream) {
   int rc = check_ptrs(h, grads, h->cfg.grad_dtype, "grads");
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (h->tensor) return tensor_pack(h, grads, s);
   rc = upload_meta(h, grads, nullptr, s);
   if (rc) return rc;
   return do_pack(h, s);
@@ -799,6 +599,7 @@ int shampoo_unpack(shampoo_t h, void* const* dst, void* hip_stream) {
   if (rc) return rc;
   const Plan& p = h->plan;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (h->tensor) return tensor_unpack(h, dst, s);
   std::vector<shp::MatMeta> m(p.n_mats);
   for (int i = 0; i < p.n_mats; ++i) {
     m[i].grad = nullptr;
@@ -810,7 +611,7 @@ int shampoo_unpack(shampoo_t h, void* const* dst, void* hip_stream) {
                              hipMemcpyHostToDevice, s));
   }
   HIP_CHECK(shp::launch_unpack(h->at<shp::BlockMeta>(p.off_blocks), h->at<shp::MatMeta>(p.off_umats),
-                               (int32_t)p.B, p.br, p.bc, h->gp(), s));
+                               (int32_t)p.B, p.br, p.bc, m_gp(h), s));
   // the descriptor copy is from pageable host memory that dies here
   HIP_CHECK(hipStreamSynchronize(s));
   return SHAMPOO_OK;
@@ -818,20 +619,25 @@ int shampoo_unpack(shampoo_t h, void* const* dst, void* hip_stream) {
 
 int shampoo_precondition(shampoo_t h, void* out, void* hip_stream) {
   if (!h) return fail(SHAMPOO_ERR_INVALID_ARG, "handle is NULL");
-  if (!out && h->plan.B) return fail(SHAMPOO_ERR_INVALID_ARG, "out is NULL");
+  shampoo_layout_t lay{};
+  if (h->tensor) tensor_layout(h, &lay);
+  const int64_t nb = h->tensor ? lay.n_blocks : h->plan.B;
+  if (!out && nb) return fail(SHAMPOO_ERR_INVALID_ARG, "out is NULL");
   if (reinterpret_cast<uintptr_t>(out) % 16) return fail(SHAMPOO_ERR_MISALIGNED, "out not 16-byte aligned");
   if (!h->roots_valid) return fail(SHAMPOO_ERR_NO_ROOTS, "no roots yet");
+  if (h->tensor)
+    return tensor_precondition(h, static_cast<float*>(out), static_cast<hipStream_t>(hip_stream));
   return do_apply(h, static_cast<hipStream_t>(hip_stream), static_cast<float*>(out));
 }
 
 int shampoo_get_status(shampoo_t h, void* hip_stream, int32_t* n_diverged_out) {
   if (!h || !n_diverged_out) return fail(SHAMPOO_ERR_INVALID_ARG, "NULL argument");
-  const Plan& p = h->plan;
-  std::vector<int32_t> st(2 * p.B);
+  int64_t off = h->plan.off_status, count = 2 * h->plan.B;
+  if (h->tensor) tensor_status_count(h, &off, &count);
+  std::vector<int32_t> st(count);
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if (p.B) {
-    HIP_CHECK(hipMemcpyAsync(st.data(), h->at<void>(p.off_status), st.size() * 4,
-                             hipMemcpyDeviceToHost, s));
+  if (count) {
+    HIP_CHECK(hipMemcpyAsync(st.data(), h->at<void>(off), st.size() * 4, hipMemcpyDeviceToHost, s));
   }
   HIP_CHECK(hipStreamSynchronize(s));
   int32_t n = 0;
@@ -849,7 +655,7 @@ int shampoo_set_timing(shampoo_t h, int32_t enable, void* hip_stream) {
   h->timed.clear();
   h->timing = enable != 0;
   if (h->timing)
-    HIP_CHECK(hipMemsetAsync(h->at<void>(h->plan.off_flops), 0, 8,
+    HIP_CHECK(hipMemsetAsync(h->at<void>(h->off_flops), 0, 8,
                              static_cast<hipStream_t>(hip_stream)));
   return SHAMPOO_OK;
 }
@@ -870,7 +676,7 @@ int shampoo_get_timing(shampoo_t h, shampoo_timing_t* out) {
   // kernels accumulate them on the device (all of them ran before the last
   // recorded event).
   double nf = 0.0;
-  HIP_CHECK(hipMemcpy(&nf, h->at<void>(h->plan.off_flops), sizeof(double), hipMemcpyDeviceToHost));
+  HIP_CHECK(hipMemcpy(&nf, h->at<void>(h->off_flops), sizeof(double), hipMemcpyDeviceToHost));
   out->flops[kNewtonGemm] += nf;  // the Chebyshev products are counted on the host
   return SHAMPOO_OK;
 }

@@ -1,0 +1,397 @@
+// HIP kernels of order-k tensor Shampoo (podcast "Preconditioned
+// Optimization Without the Full Matrix Cost", cue 26) that are not dense
+// contractions: gather / scatter of tensor blocks, the batched transpose that
+// makes a dimension's unfolding a k-major operand of the MFMA SYRK, the
+// statistics, roots and mode products of dimensions blocked at <= 8 (all
+// memory-bound or tiny: no MFMA), and the FMA mode product for row counts the
+// MFMA tiles do not divide.
+#include <math.h>
+
+#include "kernels.h"
+
+namespace shp {
+namespace {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bfloat16, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Position of packed element e inside the tensor: element offset and whether
+// it lies inside the block's real extent.
+__device__ __forceinline__ bool tensor_offset(const TensorGeom& g, const TBlockMeta& bm,
+                                              const TensorMeta& tm, int e, int64_t& off) {
+  off = 0;
+  bool in = true;
+  for (int d = g.order - 1; d >= 0; --d) {
+    const int n = g.b[d];
+    const int q = e / n;
+    const int i = e - q * n;
+    e = q;
+    in = in && i < bm.extent[d];
+    off += (int64_t)(bm.origin[d] + i) * tm.stride[d];
+  }
+  return in;
+}
+
+__global__ __launch_bounds__(256) void tensor_pack_kernel(const TBlockMeta* __restrict__ blocks,
+                                                          const TensorMeta* __restrict__ tensors,
+                                                          TensorGeom g, int bf16,
+                                                          float* __restrict__ Gp,
+                                                          float* __restrict__ Mom, float momentum) {
+  const int b = blockIdx.y;
+  const TBlockMeta bm = blocks[b];
+  const TensorMeta tm = tensors[bm.tensor];
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < g.E; e += gridDim.x * 256) {
+    int64_t off;
+    float v = 0.f;
+    if (tensor_offset(g, bm, tm, e, off))
+      v = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(tm.grad)[off])
+               : reinterpret_cast<const float*>(tm.grad)[off];
+    const size_t o = (size_t)b * g.E + e;
+    Gp[o] = v;
+    if (Mom != nullptr) Mom[o] = momentum * Mom[o] + v;
+  }
+}
+
+__global__ __launch_bounds__(256) void tensor_scatter_kernel(const TBlockMeta* __restrict__ blocks,
+                                                             const TensorMeta* __restrict__ tensors,
+                                                             TensorGeom g,
+                                                             const float* __restrict__ Src, float lr,
+                                                             int bf16, int update) {
+  const int b = blockIdx.y;
+  const TBlockMeta bm = blocks[b];
+  const TensorMeta tm = tensors[bm.tensor];
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < g.E; e += gridDim.x * 256) {
+    int64_t off;
+    if (!tensor_offset(g, bm, tm, e, off)) continue;
+    const float u = Src[(size_t)b * g.E + e];
+    if (!update) {
+      reinterpret_cast<float*>(tm.param)[off] = u;
+    } else if (bf16) {
+      uint16_t* w = reinterpret_cast<uint16_t*>(tm.param) + off;
+      *w = f32_to_bf16(bf16_to_f32(*w) - lr * u);
+    } else {
+      float* w = reinterpret_cast<float*>(tm.param) + off;
+      *w = *w - lr * u;
+    }
+  }
+}
+
+// Batched transpose through LDS. A tile is TH x TW of the input (TW <= 64,
+// TH * (TW | 1) <= 4096), elements taken in linear order on both sides so that
+// thin matrices (a handful of columns) still read and write whole lines.
+__global__ __launch_bounds__(256) void transpose_kernel(const float* __restrict__ In,
+                                                        int64_t in_stride, float* __restrict__ Out,
+                                                        int64_t out_stride, int R, int C, int TH,
+                                                        int TW) {
+  __shared__ float tile[4096 + 64];
+  const int b = blockIdx.y;
+  const int tcn = (C + TW - 1) / TW;
+  const int r0 = (blockIdx.x / tcn) * TH, c0 = (blockIdx.x % tcn) * TW;
+  const int th = min(TH, R - r0), tw = min(TW, C - c0);
+  const int pitch = tw | 1;  // odd pitch: column reads spread over the banks
+  const float* in = In + (size_t)b * in_stride;
+  float* out = Out + (size_t)b * out_stride;
+  for (int i = threadIdx.x; i < th * tw; i += 256) {
+    const int r = i / tw, c = i - r * tw;
+    tile[r * pitch + c] = in[(size_t)(r0 + r) * C + c0 + c];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < th * tw; i += 256) {
+    const int c = i / th, r = i - c * th;
+    out[(size_t)(c0 + c) * R + r0 + r] = tile[r * pitch + c];
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ Out, int64_t stride,
+                                                        int64_t from) {
+  float* out = Out + (size_t)blockIdx.y * stride;
+  for (int64_t e = from + blockIdx.x * 256 + threadIdx.x; e < stride; e += gridDim.x * 256)
+    out[e] = 0.f;
+}
+
+// Pair (l, l') with l <= l' of an n x n symmetric statistic, packed row by row.
+constexpr int kMaxPairs = kMaxSmallSide * (kMaxSmallSide + 1) / 2;
+
+template <int N>
+__global__ __launch_bounds__(256) void small_gram_kernel(const float* __restrict__ In,
+                                                         int64_t in_stride, int A, int C,
+                                                         float* __restrict__ partial) {
+  constexpr int NP = N * (N + 1) / 2;
+  __shared__ float red[4][NP];
+  const int b = blockIdx.y;
+  const float* in = In + (size_t)b * in_stride;
+  float acc[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) acc[q] = 0.f;
+  const int64_t total = (int64_t)A * C;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * 256) {
+    const int64_t a = q / C, c = q - a * C;
+    const float* src = in + (size_t)a * N * C + c;
+    float v[N];
+#pragma unroll
+    for (int l = 0; l < N; ++l) v[l] = src[(size_t)l * C];
+    int k = 0;
+#pragma unroll
+    for (int l = 0; l < N; ++l)
+#pragma unroll
+      for (int m = l; m < N; ++m) acc[k++] += v[l] * v[m];
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    float x = acc[q];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    if (lane == 0) red[wave][q] = x;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < NP; q += 256)
+    partial[((size_t)b * gridDim.x + blockIdx.x) * kMaxPairs + q] =
+        red[0][q] + red[1][q] + red[2][q] + red[3][q];
+}
+
+// H <- beta2 H + gamma * (sum of the chunk partials, in chunk order).
+__global__ __launch_bounds__(64) void small_gram_ema_kernel(const float* __restrict__ partial,
+                                                            int chunks, int n, float* __restrict__ H,
+                                                            float beta2, float gamma) {
+  const int b = blockIdx.x;
+  const int np = n * (n + 1) / 2;
+  float* h = H + (size_t)b * n * n;
+  for (int q = threadIdx.x; q < np; q += 64) {
+    double s = 0.0;
+    for (int c = 0; c < chunks; ++c) s += partial[((size_t)b * chunks + c) * kMaxPairs + q];
+    // pair q -> (l, m), l <= m
+    int l = 0, rem = q;
+    while (rem >= n - l) {
+      rem -= n - l;
+      ++l;
+    }
+    const int m = l + rem;
+    const float v = beta2 * h[l * n + m] + gamma * (float)s;
+    h[l * n + m] = v;
+    h[m * n + l] = v;
+  }
+}
+
+// Out[r][j] = sum_l X[j][l] In[l][r] for J output columns j0 .. j0 + J - 1 per
+// thread; X is uniform over the workgroup (scalar loads). When one workgroup
+// covers all n columns, the [256][n] output tile is contiguous and is staged
+// through LDS to leave as whole lines.
+template <int J>
+__global__ __launch_bounds__(256) void mode_product_kernel(const float* __restrict__ In,
+                                                           int64_t in_stride,
+                                                           const float* __restrict__ X,
+                                                           int64_t x_stride, float* __restrict__ Out,
+                                                           int64_t out_stride, int n, int R) {
+  __shared__ float stage[256 * J];
+  const int b = blockIdx.z;
+  const float* in = In + (size_t)b * in_stride;
+  const float* x = X + (size_t)b * x_stride;
+  float* out = Out + (size_t)b * out_stride;
+  const int r0 = blockIdx.x * 256;
+  const int r = r0 + threadIdx.x;
+  const int j0 = blockIdx.y * J;
+  float acc[J];
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) acc[jj] = 0.f;
+  if (r < R) {
+    for (int l = 0; l < n; ++l) {
+      const float v = in[(size_t)l * R + r];
+#pragma unroll
+      for (int jj = 0; jj < J; ++jj)
+        if (j0 + jj < n) acc[jj] += x[(j0 + jj) * n + l] * v;
+    }
+  }
+  if (gridDim.y == 1 && n == J) {
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) stage[threadIdx.x * J + jj] = acc[jj];
+    __syncthreads();
+    const int rows = min(256, R - r0);
+    float* dst = out + (size_t)r0 * J;
+    for (int i = threadIdx.x; i < rows * J; i += 256) dst[i] = stage[i];
+    return;
+  }
+  if (r < R) {
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj)
+      if (j0 + jj < n) out[(size_t)r * n + j0 + jj] = acc[jj];
+  }
+}
+
+// One thread per factor: cyclic Jacobi in fp64 on the factor's real extent,
+// matrix and eigenvectors in this thread's slice of LDS.
+constexpr int kJacobiThreads = 64;
+constexpr int kJacobiSweeps = 30;
+
+__global__ __launch_bounds__(kJacobiThreads) void small_root_kernel(
+    const float* __restrict__ H, float* __restrict__ X, int n, int count,
+    const int32_t* __restrict__ nreal, float floor, int p, int32_t* __restrict__ status,
+    int32_t* __restrict__ final_iter, float* __restrict__ resid) {
+  constexpr int S = kMaxSmallSide;
+  __shared__ double sa[kJacobiThreads][S * S];
+  __shared__ double sv[kJacobiThreads][S * S];
+  const int f = blockIdx.x * kJacobiThreads + threadIdx.x;
+  if (f >= count) return;
+  double* a = sa[threadIdx.x];
+  double* v = sv[threadIdx.x];
+  const float* h = H + (size_t)f * n * n;
+  float* x = X + (size_t)f * n * n;
+  const int m = nreal[f];
+  bool finite = true;
+  double diag2 = 0.0;
+  for (int i = 0; i < m; ++i)
+    for (int j = 0; j < m; ++j) {
+      // the stored statistic is symmetric up to fp32 rounding; use its average
+      const double y = 0.5 * ((double)h[i * n + j] + (double)h[j * n + i]);
+      finite = finite && isfinite(y);
+      a[i * S + j] = y;
+      v[i * S + j] = i == j ? 1.0 : 0.0;
+      if (i == j) diag2 += y * y;
+    }
+  int sweeps = 0;
+  double off = 0.0;
+  for (; finite && sweeps < kJacobiSweeps; ++sweeps) {
+    off = 0.0;
+    for (int i = 0; i < m; ++i)
+      for (int j = i + 1; j < m; ++j) off += a[i * S + j] * a[i * S + j];
+    if (off <= 1e-32 * diag2) break;
+    for (int P = 0; P < m; ++P)
+      for (int Q = P + 1; Q < m; ++Q) {
+        const double apq = a[P * S + Q];
+        if (apq == 0.0) continue;
+        // rotation in the (P, Q) plane that zeroes a[P][Q]
+        const double th = (a[Q * S + Q] - a[P * S + P]) / (2.0 * apq);
+        const double t = (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + sqrt(th * th + 1.0));
+        const double c = 1.0 / sqrt(t * t + 1.0), s = t * c;
+        for (int r = 0; r < m; ++r) {  // columns P, Q
+          const double arp = a[r * S + P], arq = a[r * S + Q];
+          a[r * S + P] = c * arp - s * arq;
+          a[r * S + Q] = s * arp + c * arq;
+        }
+        for (int r = 0; r < m; ++r) {  // rows P, Q
+          const double apr = a[P * S + r], aqr = a[Q * S + r];
+          a[P * S + r] = c * apr - s * aqr;
+          a[Q * S + r] = s * apr + c * aqr;
+        }
+        for (int r = 0; r < m; ++r) {
+          const double vrp = v[r * S + P], vrq = v[r * S + Q];
+          v[r * S + P] = c * vrp - s * vrq;
+          v[r * S + Q] = s * vrp + c * vrq;
+        }
+      }
+  }
+  double w[S];
+  // the spectrum of the exact statistic is >= floor = beta2^t eps; rounding
+  // below it (or an underflowed floor) is lifted to keep the root finite
+  const double lo = fmax((double)floor, 1e-30);
+  for (int i = 0; i < m; ++i) w[i] = pow(fmax(a[i * S + i], lo), -1.0 / p);
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) {
+      double y = 0.0;
+      if (i < m && j < m && finite)
+        for (int q = 0; q < m; ++q) y += v[i * S + q] * w[q] * v[j * S + q];
+      x[i * n + j] = (float)y;
+    }
+  status[f] = finite ? 1 : 3;
+  final_iter[f] = sweeps;
+  resid[f] = diag2 > 0.0 ? (float)sqrt(off / diag2) : 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_tensor_pack(const TBlockMeta* blocks, const TensorMeta* tensors, TensorGeom g,
+                              int32_t B, int32_t grad_bf16, float* Gp, float* Mom, float momentum,
+                              hipStream_t s) {
+  if (B == 0 || g.E == 0) return hipSuccess;
+  const int chunks = std::max(1, std::min(1024, (g.E + 1023) / 1024));
+  hipLaunchKernelGGL(tensor_pack_kernel, dim3(chunks, B), dim3(256), 0, s, blocks, tensors, g,
+                     grad_bf16, Gp, Mom, momentum);
+  return hipGetLastError();
+}
+
+hipError_t launch_tensor_scatter(const TBlockMeta* blocks, const TensorMeta* tensors, TensorGeom g,
+                                 int32_t B, const float* Src, float lr, int32_t param_bf16,
+                                 int32_t update, hipStream_t s) {
+  if (B == 0 || g.E == 0) return hipSuccess;
+  const int chunks = std::max(1, std::min(1024, (g.E + 1023) / 1024));
+  hipLaunchKernelGGL(tensor_scatter_kernel, dim3(chunks, B), dim3(256), 0, s, blocks, tensors, g,
+                     Src, lr, param_bf16, update);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const float* In, int64_t in_stride, float* Out, int64_t out_stride,
+                            int32_t R, int32_t C, int32_t B, hipStream_t s) {
+  if (B == 0 || R == 0 || C == 0) return hipSuccess;
+  const int TW = std::min(C, 64);
+  const int TH = std::min(R, 4096 / (TW | 1));  // TH rows of pitch <= (TW | 1) fit the tile
+  const int tiles = ((R + TH - 1) / TH) * ((C + TW - 1) / TW);
+  hipLaunchKernelGGL(transpose_kernel, dim3(tiles, B), dim3(256), 0, s, In, in_stride, Out,
+                     out_stride, R, C, TH, TW);
+  const int64_t used = (int64_t)R * C;
+  if (out_stride > used) {
+    const int chunks = (int)std::min<int64_t>(64, (out_stride - used + 255) / 256);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(chunks, B), dim3(256), 0, s, Out, out_stride, used);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_small_gram(const float* In, int64_t in_stride, int32_t A, int32_t n, int32_t C,
+                             int32_t B, float* partial, int32_t chunks, float* H, float beta2,
+                             float gamma, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid(chunks, B);
+  switch (n) {
+#define SHP_GRAM(N)                                                                              \
+  case N:                                                                                        \
+    hipLaunchKernelGGL(small_gram_kernel<N>, grid, dim3(256), 0, s, In, in_stride, A, C, partial); \
+    break;
+    SHP_GRAM(1) SHP_GRAM(2) SHP_GRAM(3) SHP_GRAM(4) SHP_GRAM(5) SHP_GRAM(6) SHP_GRAM(7) SHP_GRAM(8)
+#undef SHP_GRAM
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL(small_gram_ema_kernel, dim3(B), dim3(64), 0, s, partial, chunks, n, H, beta2,
+                     gamma);
+  return hipGetLastError();
+}
+
+hipError_t launch_mode_product(const float* In, int64_t in_stride, const float* X, int64_t x_stride,
+                               float* Out, int64_t out_stride, int32_t n, int32_t R, int32_t B,
+                               hipStream_t s) {
+  if (B == 0 || R == 0) return hipSuccess;
+  const int gx = (R + 255) / 256;
+  switch (n <= kMaxSmallSide ? n : 0) {
+#define SHP_MP(N)                                                                               \
+  case N:                                                                                       \
+    hipLaunchKernelGGL(mode_product_kernel<N>, dim3(gx, 1, B), dim3(256), 0, s, In, in_stride, X, \
+                       x_stride, Out, out_stride, n, R);                                        \
+    break;
+    SHP_MP(1) SHP_MP(2) SHP_MP(3) SHP_MP(4) SHP_MP(5) SHP_MP(6) SHP_MP(7) SHP_MP(8)
+#undef SHP_MP
+    default:
+      hipLaunchKernelGGL(mode_product_kernel<8>, dim3(gx, (n + 7) / 8, B), dim3(256), 0, s, In,
+                         in_stride, X, x_stride, Out, out_stride, n, R);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_small_root(const float* H, float* X, int32_t n, int32_t count,
+                             const int32_t* nreal, float floor, int32_t p, int32_t* status,
+                             int32_t* final_iter, float* resid, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  if (n < 1 || n > kMaxSmallSide) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(small_root_kernel, dim3((count + kJacobiThreads - 1) / kJacobiThreads),
+                     dim3(kJacobiThreads), 0, s, H, X, n, count, nreal, floor, p, status,
+                     final_iter, resid);
+  return hipGetLastError();
+}
+
+}  // namespace shp

@@ -56,6 +56,21 @@ class Timing(ctypes.Structure):
                 ("bytes", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6)]
 
 
+MAX_ORDER = 4
+
+
+class TensorDesc(ctypes.Structure):
+    _fields_ = [("order", ctypes.c_int32), ("dims", ctypes.c_int64 * MAX_ORDER),
+                ("strides", ctypes.c_int64 * MAX_ORDER)]
+
+
+class TensorInfo(ctypes.Structure):
+    _fields_ = [("order", ctypes.c_int32), ("block_dims", ctypes.c_int32 * MAX_ORDER),
+                ("n_blocks", ctypes.c_int64), ("block_elems", ctypes.c_int64),
+                ("stats", ctypes.c_int64 * MAX_ORDER), ("roots", ctypes.c_int64 * MAX_ORDER),
+                ("factor_group", ctypes.c_int32 * MAX_ORDER)]
+
+
 class ShampooError(RuntimeError):
     def __init__(self, code, message):
         super().__init__(f"shampoo error {code}: {message}")
@@ -86,6 +101,13 @@ _SIGNATURES = {
     "shampoo_get_timing": [_P, ctypes.POINTER(Timing)],
     "shampoo_status_string": [ctypes.c_int],
     "shampoo_last_error": [],
+    "shampoo_tensor_workspace_size": [ctypes.POINTER(Config), ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(TensorDesc),
+                                      ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)],
+    "shampoo_tensor_init": [ctypes.POINTER(Config), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                            ctypes.POINTER(TensorDesc), ctypes.c_int32, _P, ctypes.c_size_t, _P,
+                            ctypes.POINTER(_P)],
+    "shampoo_tensor_info": [_P, ctypes.POINTER(TensorInfo)],
 }
 
 
@@ -224,6 +246,52 @@ def shampoo_get_timing(h):
                    "launches": t.launches[i]} for i, name in enumerate(TIMING_CLASSES)}
 
 
+def make_tensor_descs(shapes, strides=None):
+    """Descriptors of tensors (row-major contiguous unless strides are given)."""
+    descs = (TensorDesc * max(1, len(shapes)))()
+    for i, shape in enumerate(shapes):
+        k = len(shape)
+        if strides is None:
+            st, acc = [0] * k, 1
+            for d in range(k - 1, -1, -1):
+                st[d] = acc
+                acc *= max(1, shape[d])
+        else:
+            st = strides[i]
+        descs[i].order = k
+        for d in range(k):
+            descs[i].dims[d] = shape[d]
+            descs[i].strides[d] = st[d]
+    return descs
+
+
+def _block_dims(block_dims):
+    arr = (ctypes.c_int32 * MAX_ORDER)(*[int(b) for b in block_dims])
+    return arr
+
+
+def shampoo_tensor_workspace_size(cfg, block_dims, descs, n_tensors):
+    out = ctypes.c_size_t(0)
+    _check(load_library().shampoo_tensor_workspace_size(
+        ctypes.byref(cfg), len(block_dims), _block_dims(block_dims), descs, n_tensors,
+        ctypes.byref(out)))
+    return out.value
+
+
+def shampoo_tensor_init(cfg, block_dims, descs, n_tensors, workspace_ptr, workspace_bytes, stream):
+    h = ctypes.c_void_p()
+    _check(load_library().shampoo_tensor_init(
+        ctypes.byref(cfg), len(block_dims), _block_dims(block_dims), descs, n_tensors,
+        ctypes.c_void_p(workspace_ptr), workspace_bytes, ctypes.c_void_p(stream), ctypes.byref(h)))
+    return h
+
+
+def shampoo_tensor_info(h):
+    out = TensorInfo()
+    _check(load_library().shampoo_tensor_info(h, ctypes.byref(out)))
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Convenience wrapper over torch tensors
 # ---------------------------------------------------------------------------
@@ -350,3 +418,85 @@ class Shampoo:
 
     def newton_residual(self):
         return self._view(self.layout.newton_residual, 2 * self.n_blocks, self.torch.float32)
+
+
+class TensorShampoo(Shampoo):
+    """Order-k tensor Shampoo over a list of CUDA tensors of one order k
+    (contiguous unless strides are given): one statistic per dimension, cut
+    into blocks of block_dims. Same calls as Shampoo; state views per
+    dimension."""
+
+    def __init__(self, shapes, block_dims, beta2=0.999, eps=1e-6, lr=1e-3, root_every=10,
+                 stat_scale=None, newton_max_iters=25, newton_tol=1e-6, newton_scale_mode=2,
+                 dtype="f32", device="cuda", strides=None, momentum=0.0, root_method="newton",
+                 cheb_degree=128):
+        import torch
+        self.torch = torch
+        self.shapes = [tuple(int(v) for v in s) for s in shapes]
+        self.block_dims = tuple(int(b) for b in block_dims)
+        cfg = shampoo_config_default()
+        cfg.beta2, cfg.eps, cfg.lr = beta2, eps, lr
+        cfg.stat_scale = -1.0 if stat_scale is None else stat_scale
+        cfg.root_every = root_every
+        cfg.newton_max_iters, cfg.newton_tol = newton_max_iters, newton_tol
+        cfg.newton_scale_mode = newton_scale_mode
+        cfg.momentum = momentum
+        cfg.root_method = ROOT_METHODS[root_method]
+        cfg.cheb_degree = cheb_degree
+        dt = {"f32": SHAMPOO_F32, "bf16": SHAMPOO_BF16}[dtype]
+        cfg.param_dtype = cfg.grad_dtype = dt
+        self.cfg = cfg
+        self.descs = make_tensor_descs(self.shapes, strides)
+        self.n = len(self.shapes)
+        nbytes = shampoo_tensor_workspace_size(cfg, self.block_dims, self.descs, self.n)
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        base = self.workspace.data_ptr()
+        self._ws_ptr = (base + 255) // 256 * 256
+        self._ws_off = self._ws_ptr - base
+        self.handle = shampoo_tensor_init(cfg, self.block_dims, self.descs, self.n, self._ws_ptr,
+                                          nbytes, self._stream())
+        self.layout = shampoo_state_layout(self.handle)
+        self.info = shampoo_tensor_info(self.handle)
+
+    @property
+    def order(self):
+        return len(self.block_dims)
+
+    def grad_packed(self):
+        B = self.n_blocks
+        E = int(self.info.block_elems)
+        return self._view(self.layout.grad_packed, B * E, self.torch.float32).view(B, *self.block_dims)
+
+    def momentum_buffer(self):
+        if self.layout.momentum < 0:
+            return None
+        B, E = self.n_blocks, int(self.info.block_elems)
+        return self._view(self.layout.momentum, B * E, self.torch.float32).view(B, *self.block_dims)
+
+    def _per_dim(self, offs):
+        B = self.n_blocks
+        return [self._view(offs[i], B * n * n, self.torch.float32).view(B, n, n)
+                for i, n in enumerate(self.block_dims)]
+
+    def stats(self):
+        """[B, n_i, n_i] statistic of every dimension i."""
+        return self._per_dim(self.info.stats)
+
+    def roots(self):
+        return self._per_dim(self.info.roots)
+
+    def _per_factor(self, off, dtype):
+        B, k = self.n_blocks, self.order
+        flat = self._view(off, k * B, dtype)
+        return [flat[self.info.factor_group[i] * B:(self.info.factor_group[i] + 1) * B]
+                for i in range(k)]
+
+    def newton_info(self):
+        """Per dimension: (status, iterations, scale) of every block's factor."""
+        st = self._per_factor(self.layout.newton_status, self.torch.int32)
+        it = self._per_factor(self.layout.newton_iters, self.torch.int32)
+        sc = self._per_factor(self.layout.newton_scale, self.torch.float32)
+        return list(zip(st, it, sc))
+
+    def newton_residual(self):
+        return self._per_factor(self.layout.newton_residual, self.torch.float32)

@@ -17,6 +17,10 @@ Distributions (per workload, see ``configs``):
               seeded permutation over all blocks of all matrices) carries a
               diagonal gradient: off-diagonal entries of the block are 0.
 Initial parameters: N(0, init_std^2), stored in the workload's dtype.
+
+Tensor workloads (TensorGradientSource): iid N(0, grad_std^2), or row_scaled
+with one log-uniform [1e-2, 1] scale per index of the first dimension (the
+output channel of a conv filter), fixed for every step.
 """
 from __future__ import annotations
 
@@ -24,12 +28,12 @@ import math
 
 import torch
 
-from .configs import Workload
+from .configs import TensorWorkload, Workload
 
 _DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
-def torch_dtype(w: Workload):
+def torch_dtype(w):
     return _DTYPES[w.dtype]
 
 
@@ -113,3 +117,38 @@ class GradientSource:
         g = _gen(self.device.type, self.seed * 1_000_003 + 5)
         return [(torch.randn(r, c, generator=g, device=self.device) * w.init_std)
                 .to(torch_dtype(w)).contiguous() for (r, c) in w.shapes]
+
+
+class TensorGradientSource:
+    """Deterministic per-step gradients of a tensor workload."""
+
+    def __init__(self, w: TensorWorkload, device="cpu", seed=None):
+        self.w = w
+        self.device = torch.device(device)
+        self.seed = w.seed if seed is None else int(seed)
+        g = _gen(self.device.type, self.seed * 1_000_003 + 19)
+        lo, hi = math.log(1e-2), 0.0
+        self._scale = []
+        for shape in w.shapes:
+            if w.grad == "row_scaled":
+                u = torch.rand((shape[0],) + (1,) * (len(shape) - 1), generator=g, device=self.device)
+                self._scale.append(torch.exp(lo + (hi - lo) * u))
+            else:
+                self._scale.append(None)
+
+    def grads(self, step):
+        w = self.w
+        g = _gen(self.device.type, self.seed * 1_000_003 + 101 * int(step) + 31)
+        out = []
+        for i, shape in enumerate(w.shapes):
+            G = torch.randn(shape, generator=g, device=self.device) * w.grad_std
+            if self._scale[i] is not None:
+                G *= self._scale[i]
+            out.append(G.to(torch_dtype(w)).contiguous())
+        return out
+
+    def init_params(self):
+        w = self.w
+        g = _gen(self.device.type, self.seed * 1_000_003 + 7)
+        return [(torch.randn(s, generator=g, device=self.device) * w.init_std)
+                .to(torch_dtype(w)).contiguous() for s in w.shapes]

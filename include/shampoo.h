@@ -226,6 +226,76 @@ int shampoo_get_timing(shampoo_t h, shampoo_timing_t* out);
 const char* shampoo_status_string(int status);
 const char* shampoo_last_error(void);
 
+/* ------------------------------------------------------ order-k tensors
+ * Podcast "Preconditioned Optimization Without the Full Matrix Cost", cue 26
+ * (the order-k algorithm): a parameter tensor of order k keeps one statistic
+ * per dimension i, H_i (n_i x n_i), started at eps * I and updated as
+ *     H_i <- beta2 H_i + stat_scale G_(i) G_(i)^T
+ * with G_(i) the mode-i unfolding of the gradient (rows: dimension i,
+ * columns: all the others); the update is
+ *     W <- W - lr * G x_1 H_1^(-1/2k) x_2 ... x_k H_k^(-1/2k),
+ * x_i the product along dimension i (the products commute). k = 2 is the
+ * matrix method above. Refresh schedule, momentum, dtypes and the root
+ * settings of shampoo_config_t apply unchanged, with p = 2k; block_rows and
+ * block_cols are not read.
+ *
+ * Blocks: dimension i is cut at block_dims[i]; a block is packed as a dense
+ * row-major [block_dims[0]]...[block_dims[k-1]] fp32 array, zero past its
+ * real extent. Every block_dims[i] is either 1..8 ("small": statistics and
+ * mode products by memory-bound kernels, roots by an fp64 eigendecomposition)
+ * or a multiple of 32 up to 4096 (statistics by the MFMA SYRK, roots by the
+ * selected solver on the MFMA core, products by MFMA when the product of
+ * the other block sizes is a multiple of 32). A packed block holds at most
+ * 2^30 elements. root_method 1 (Newton-DB) needs k = 2.
+ *
+ * Handles made by shampoo_tensor_init take the same calls as matrix handles:
+ * shampoo_step / refresh_roots / pack / unpack / precondition / get_status /
+ * timing / state_layout / destroy, with one pointer per registered tensor
+ * wherever the matrix calls take one per matrix. shampoo_precondition writes
+ * [B][E] fp32 (E = product of block_dims). In shampoo_layout_t, stats and
+ * roots point at the first statistic of the first dimension (see
+ * shampoo_tensor_info for each dimension's place) and the per-factor arrays
+ * hold k * B entries. */
+#define SHAMPOO_MAX_ORDER 4
+
+/* One registered tensor: extents and element strides (>= 1) of each of its
+ * `order` dimensions; parameters and gradients share them. */
+typedef struct {
+  int32_t order;
+  int64_t dims[SHAMPOO_MAX_ORDER];
+  int64_t strides[SHAMPOO_MAX_ORDER];
+} shampoo_tensor_desc_t;
+
+/* Where each dimension's state lives (byte offsets into the workspace). */
+typedef struct {
+  int32_t order;
+  int32_t block_dims[SHAMPOO_MAX_ORDER];
+  int64_t n_blocks;
+  int64_t block_elems;                    /* E                                   */
+  int64_t stats[SHAMPOO_MAX_ORDER];       /* fp32 [B][n_i][n_i], n_i = block_dims[i] */
+  int64_t roots[SHAMPOO_MAX_ORDER];       /* fp32 [B][n_i][n_i]                    */
+  int32_t factor_group[SHAMPOO_MAX_ORDER]; /* dimension i's factors sit at entries
+                                             [g B, (g + 1) B) of the per-factor
+                                             arrays, g = factor_group[i]         */
+} shampoo_tensor_info_t;
+
+/* Bytes of device workspace for these tensors (host only, no HIP call).
+ * block_dims: host array of `order` block sizes (2 <= order <= 4); tensors:
+ * host array of n_tensors descriptors, each of that order. */
+int shampoo_tensor_workspace_size(const shampoo_config_t* cfg, int32_t order,
+                                  const int32_t* block_dims, const shampoo_tensor_desc_t* tensors,
+                                  int32_t n_tensors, size_t* bytes_out);
+
+/* Create a tensor handle; workspace, stream and start state as shampoo_init
+ * (every H_i = eps I, t = 0, no roots). */
+int shampoo_tensor_init(const shampoo_config_t* cfg, int32_t order, const int32_t* block_dims,
+                        const shampoo_tensor_desc_t* tensors, int32_t n_tensors, void* workspace,
+                        size_t workspace_bytes, void* hip_stream, shampoo_t* out);
+
+/* Per-dimension layout of a tensor handle; SHAMPOO_ERR_INVALID_ARG for a
+ * matrix handle. */
+int shampoo_tensor_info(shampoo_t h, shampoo_tensor_info_t* out);
+
 #ifdef __cplusplus
 }
 #endif

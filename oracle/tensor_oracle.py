@@ -27,7 +27,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .shampoo_oracle import (inverse_root_coupled_newton, inverse_root_eigh, is_refresh_step,
-                             round_to_bf16, update_statistics)
+                             round_to_bf16)
 
 __all__ = ["TensorBlock", "tensor_block_table", "mode_unfold", "mode_product",
            "precondition_tensor", "pack_tensor_blocks", "TensorShampooOracle"]
@@ -155,9 +155,10 @@ class TensorShampooOracle:
         G = {i: np.asarray(block_grads[i], np.float64) for i in self.ids}
         for i in self.ids:
             for m in range(self.k):
-                # the statistic of dimension m: the matrices' EMA on G_(m) G_(m)^T
-                self.H[i][m], _ = update_statistics(self.H[i][m], np.eye(1), mode_unfold(G[i], m),
-                                                    self.beta2, self.stat_scale)
+                # the statistic of dimension m: the matrices' EMA (the left
+                # statistic's rule) on the unfolding, H <- beta2 H + g G_(m) G_(m)^T
+                Gm = mode_unfold(G[i], m)
+                self.H[i][m] = self.beta2 * self.H[i][m] + self.stat_scale * (Gm @ Gm.T)
         if force_refresh or (auto_refresh and is_refresh_step(self.t, self.root_every)):
             self.refresh_roots()
         updates, new = {}, {}

@@ -143,3 +143,68 @@ def test_product_path_has_no_oracle_or_fallback():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+# ---------------------------------------------------------------------------
+# Order-k tensor handles: sizes and validation (host only)
+# ---------------------------------------------------------------------------
+def _tws(cfg, block_dims, shapes, strides=None):
+    d = S.make_tensor_descs(shapes, strides)
+    out = ctypes.c_size_t(0)
+    bd = (ctypes.c_int32 * 4)(*block_dims)
+    code = S.load_library().shampoo_tensor_workspace_size(ctypes.byref(cfg), len(block_dims), bd, d,
+                                                          len(shapes), ctypes.byref(out))
+    return code, out.value
+
+
+def test_tensor_workspace_size(lib):
+    c = S.shampoo_config_default()
+    code, b = _tws(c, (64, 32, 3, 3), [(64, 32, 3, 3)])
+    E = 64 * 32 * 9
+    assert code == S.SHAMPOO_OK
+    # packed gradient, two apply buffers, statistics and roots of every dimension
+    assert b >= 3 * E * 4 + 2 * 4 * (64 * 64 + 32 * 32 + 9 + 9)
+    code2, b2 = _tws(c, (64, 32, 3, 3), [(64, 32, 3, 3), (130, 40, 3, 3)])  # 3 x 2 more blocks
+    assert code2 == S.SHAMPOO_OK and b2 >= b + 6 * 3 * E * 4 - 8192
+    code3, b3 = _tws(c, (64, 32, 3, 3), [(0, 32, 3, 3)])
+    assert code3 == S.SHAMPOO_OK and b3 < 1 << 16
+    code4, _ = _tws(c, (3, 3), [(5, 7)])  # two small dimensions: no MFMA factor at all
+    assert code4 == S.SHAMPOO_OK
+
+
+@pytest.mark.parametrize("block_dims,shapes,field,value,code", [
+    ((64, 16, 3), [(64, 16, 3)], None, None, S.SHAMPOO_ERR_UNSUPPORTED),   # 16: neither small nor x32
+    ((64, 32, 3, 3, 1), [(64, 32, 3, 3, 1)], None, None, S.SHAMPOO_ERR_UNSUPPORTED),  # order 5
+    ((64,), [(64,)], None, None, S.SHAMPOO_ERR_UNSUPPORTED),               # order 1
+    ((64, 32, 3), [(64, 32)], None, None, S.SHAMPOO_ERR_INVALID_ARG),      # order mismatch
+    ((64, 32, 3), [(64, 32, 3)], "root_method", 1, S.SHAMPOO_ERR_UNSUPPORTED),  # DB needs k = 2
+    ((64, 32, 3), [(64, 32, 3)], "eps", 0.0, S.SHAMPOO_ERR_INVALID_ARG),
+    ((4096, 4096, 128), [(4096, 4096, 128)], None, None, S.SHAMPOO_ERR_UNSUPPORTED),  # 2^31 per block
+])
+def test_tensor_validation(lib, block_dims, shapes, field, value, code):
+    c = S.shampoo_config_default()
+    if field:
+        setattr(c, field, value)
+    k = len(block_dims)
+    if k > 4 or len(shapes[0]) > 4:
+        # more than SHAMPOO_MAX_ORDER dimensions cannot be described; the order
+        # argument alone is rejected
+        d = S.make_tensor_descs([s[:4] for s in shapes])
+        out = ctypes.c_size_t(0)
+        bd = (ctypes.c_int32 * 5)(*block_dims)
+        got = lib.shampoo_tensor_workspace_size(ctypes.byref(c), k, ctypes.cast(bd, ctypes.POINTER(ctypes.c_int32)),
+                                                d, 1, ctypes.byref(out))
+    else:
+        got, _ = _tws(c, block_dims, shapes)
+    assert got == code
+
+
+def test_tensor_bad_strides(lib):
+    c = S.shampoo_config_default()
+    code, _ = _tws(c, (32, 3), [(40, 3)], strides=[(3, 0)])
+    assert code == S.SHAMPOO_ERR_INVALID_ARG
+
+
+def test_tensor_matrix_handle_info_rejected(lib):
+    out = S.TensorInfo()
+    assert lib.shampoo_tensor_info(None, ctypes.byref(out)) == S.SHAMPOO_ERR_INVALID_ARG
