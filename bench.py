@@ -3,6 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+NAME is a matrix workload (default decoder_1b_b1024_f32) or one of the
+order-k tensor workloads (resnet32_cifar_convs, resnet32_x8_convs_b128).
+
 A step is the whole optimizer step on one batch of gradients: pack, EMA
 statistics, the coupled-Newton roots when the refresh schedule asks (every
 root_every steps, so K = 20 after W = 10 holds exactly two refreshes), and the
@@ -90,6 +93,144 @@ def cpu_baseline(w, grad_sets, budget_s=15.0, max_blocks=32, seed=0):
     }
 
 
+def cpu_baseline_tensor(w, grad_sets, budget_s=15.0, max_blocks=16, seed=0):
+    """The tensor oracle (as it stands) on a sample of blocks, timed and
+    extrapolated like cpu_baseline."""
+    import numpy as np
+
+    from oracle.tensor_oracle import TensorShampooOracle, tensor_block_table
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    table = tensor_block_table(w.shapes, w.block_dims)
+    rng = np.random.default_rng(seed)
+    order = [int(i) for i in rng.permutation(len(table))]
+    g1, g2 = grad_sets[0], grad_sets[1 % len(grad_sets)]
+    t_ref = t_non = 0.0
+    used = 0
+    start = time.perf_counter()
+    for i in order[:max_blocks]:
+        b = table[i]
+        G1 = g1[b.tensor][b.slices()].float().cpu().numpy()
+        G2 = g2[b.tensor][b.slices()].float().cpu().numpy()
+        o = TensorShampooOracle(w.shapes, w.block_dims, w.beta2, w.eps, w.lr, w.root_every,
+                                blocks=[i], momentum=w.momentum)
+        a = time.perf_counter()
+        o.step_blocks({i: G1})
+        bt = time.perf_counter()
+        o.step_blocks({i: G2})
+        c = time.perf_counter()
+        t_ref += bt - a
+        t_non += c - bt
+        used += 1
+        if time.perf_counter() - start > budget_s and used >= 4:
+            break
+    k = max(1, w.root_every)
+    per_block_cycle = (t_ref + (k - 1) * t_non) / used
+    steps_per_s = k / (per_block_cycle * len(table))
+    return {
+        "value": steps_per_s, "unit": "steps/s", "cores": cores, "kind": "oracle",
+        "sample": (f"fp64 tensor oracle (numpy/LAPACK, eigh roots) on {used} of {len(table)} "
+                   f"blocks: one refresh step ({t_ref / used * 1e3:.1f} ms/block) and one "
+                   f"non-refresh step ({t_non / used * 1e3:.1f} ms/block), extrapolated "
+                   f"linearly to all blocks over a {k}-step root cycle"),
+        "blocks_per_s": steps_per_s * len(table),
+        "cpu_seconds": t_ref + t_non,
+    }
+
+
+def class_table(tm):
+    kernels = {}
+    for name, d in tm.items():
+        entry = {"ms": round(d["ms"], 3), "launches": d["launches"]}
+        if d["flops"] > 0 and d["ms"] > 0:
+            tf = d["flops"] / (d["ms"] * 1e-3) / 1e12
+            entry["tflops"] = round(tf, 2)
+            entry["frac_fp32_mfma"] = round(tf / PEAK_FP32_MFMA_TFLOPS, 4)
+        if d["bytes"] > 0 and d["ms"] > 0:
+            gbs = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+            entry["gbs"] = round(gbs, 1)
+            entry["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
+        kernels[name] = entry
+    return kernels
+
+
+def run_tensor(args, w, torch, S, synth):
+    """Order-k tensor workloads: the same step, timing and JSON line."""
+    import dataclasses
+    if args.momentum is not None:
+        w = dataclasses.replace(w, momentum=args.momentum)
+    if args.root_method is not None:
+        w = dataclasses.replace(w, root_method=args.root_method)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"tensor workload {w.name}: {len(w.shapes)} tensors, blocks {w.block_dims}")
+    src = synth.TensorGradientSource(w, device=dev)
+    params = src.init_params()
+    total = args.steps + args.warmup
+    n_sets = total if args.grad_sets <= 0 else max(1, min(args.grad_sets, total))
+    grad_sets = [src.grads(t) for t in range(1, n_sets + 1)]
+    sh = S.TensorShampoo(w.shapes, w.block_dims, beta2=w.beta2, eps=w.eps, lr=w.lr,
+                         root_every=w.root_every, newton_max_iters=w.newton_max_iters,
+                         newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode,
+                         dtype=w.dtype, momentum=w.momentum, root_method=w.root_method,
+                         cheb_degree=w.cheb_degree)
+    B = sh.n_blocks
+    log(f"{B} blocks of {int(sh.info.block_elems)} elements, workspace "
+        f"{sh.workspace.numel() / 2**30:.2f} GiB")
+    for t in range(args.warmup):
+        sh.step(params, grad_sets[t % n_sets])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sh.set_timing(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for t in range(args.steps):
+        sh.step(params, grad_sets[(args.warmup + t) % n_sets])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = e0.elapsed_time(e1) / 1e3
+    tm = sh.timing()
+    sh.set_timing(False)
+    n_div = sh.n_diverged()
+    kernels = class_table(tm)
+    # dominant class by kernel time; its roofline against HBM (bytes known)
+    # or the fp32 MFMA peak
+    dom = max(tm, key=lambda k: tm[k]["ms"])
+    d = tm[dom]
+    if d["bytes"] > 0 and (d["flops"] == 0 or d["bytes"] / max(d["flops"], 1.0) > 0.05):
+        ach = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    else:
+        ach = d["flops"] / (d["ms"] * 1e-3) / 1e12 if d["ms"] > 0 else 0.0
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4)}
+    roof.update({"traffic": None, "kernel": f"class {dom}", "launches": d["launches"],
+                 "avg_launch_ms": d["ms"] / max(1, d["launches"])})
+    cpu = None if args.no_cpu_baseline else cpu_baseline_tensor(w, grad_sets)
+    steps_per_s = args.steps / elapsed
+    out = {
+        "metric": METRIC, "value": round(steps_per_s, 4), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 gradients and parameters)",
+        "data": "synthetic (seeded gradients with conv-filter shapes)",
+        "config": {"workload": w.name, "tensors": len(w.shapes), "blocks": B,
+                   "block": list(w.block_dims), "root_every": w.root_every,
+                   "root_method": w.root_method, "momentum": w.momentum, "grad_sets": n_sets},
+        "blocks_per_s": round(steps_per_s * B, 1),
+        "kernels": kernels, "n_diverged": n_div, "roofline": roof, "cpu_baseline": cpu,
+    }
+    sh.close()
+    print(json.dumps(out), flush=True)
+
+
 def newton_traffic(workload):
     """HBM bytes per Newton-product launch from the committed rocprofv3
     counter summary, if it was taken on the current kernel source (its
@@ -142,6 +283,8 @@ def main():
         from blocked_shampoo_preconditioning_amd import build
         build.build()
     S.load_library()
+    if args.workload in configs.TENSOR_WORKLOADS:
+        return run_tensor(args, configs.get_tensor(args.workload), torch, S, synth)
     w = configs.get(args.workload)
     import dataclasses
     if args.momentum is not None:
@@ -202,18 +345,7 @@ def main():
     log(f"timed {args.steps} steps: {elapsed * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms)")
 
     steps_per_s = args.steps / elapsed
-    kernels = {}
-    for name, d in tm.items():
-        entry = {"ms": round(d["ms"], 3), "launches": d["launches"]}
-        if d["flops"] > 0 and d["ms"] > 0:
-            tf = d["flops"] / (d["ms"] * 1e-3) / 1e12
-            entry["tflops"] = round(tf, 2)
-            entry["frac_fp32_mfma"] = round(tf / PEAK_FP32_MFMA_TFLOPS, 4)
-        if d["bytes"] > 0 and d["ms"] > 0:
-            gbs = d["bytes"] / (d["ms"] * 1e-3) / 1e9
-            entry["gbs"] = round(gbs, 1)
-            entry["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
-        kernels[name] = entry
+    kernels = class_table(tm)
     nw = tm["newton_gemm"]
     achieved = nw["flops"] / (nw["ms"] * 1e-3) / 1e12 if nw["ms"] > 0 else 0.0
     traffic = newton_traffic(w.name)

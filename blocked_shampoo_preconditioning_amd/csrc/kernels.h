@@ -218,6 +218,12 @@ hipError_t launch_small_gram(const float* In, int64_t in_stride, int32_t A, int3
 hipError_t launch_mode_product(const float* In, int64_t in_stride, const float* X, int64_t x_stride,
                                float* Out, int64_t out_stride, int32_t n, int32_t R, int32_t B,
                                hipStream_t s);
+// The last product (leading dimension k-1, extent <= 8) with the update
+// W -= lr * U written straight into the parameters (no packed U).
+hipError_t launch_mode_product_update(const float* In, int64_t in_stride, const float* X,
+                                      int64_t x_stride, const TBlockMeta* blocks,
+                                      const TensorMeta* tensors, TensorGeom g, int32_t R, int32_t B,
+                                      float lr, int32_t param_bf16, hipStream_t s);
 // Small-side roots: per factor (count factors of side n, real extent nreal[f]),
 // fp64 cyclic Jacobi of H, X = V diag(max(lam, floor)^(-1/p)) V^T on the real
 // extent, zero elsewhere. status / final_iter / resid of each factor are written

@@ -22,23 +22,45 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return (uint16_t)(u >> 16);
 }
 
-// Position of packed element e inside the tensor: element offset and whether
-// it lies inside the block's real extent.
-__device__ __forceinline__ bool tensor_offset(const TensorGeom& g, const TBlockMeta& bm,
-                                              const TensorMeta& tm, int e, int64_t& off) {
-  off = 0;
-  bool in = true;
-  for (int d = g.order - 1; d >= 0; --d) {
-    const int n = g.b[d];
-    const int q = e / n;
-    const int i = e - q * n;
-    e = q;
-    in = in && i < bm.extent[d];
-    off += (int64_t)(bm.origin[d] + i) * tm.stride[d];
+// A block's geometry in registers: K is the order (compile-time, so every
+// per-dimension array is indexed by constants and stays in registers).
+template <int K>
+struct BlockGeo {
+  int b[K], ext[K];
+  int64_t base;        // element offset of the block's origin
+  int64_t stride[K];
+  __device__ __forceinline__ void load(const TensorGeom& g, const TBlockMeta& bm,
+                                       const TensorMeta& tm) {
+    base = 0;
+#pragma unroll
+    for (int d = 0; d < K; ++d) {
+      b[d] = g.b[d];
+      ext[d] = bm.extent[d];
+      stride[d] = tm.stride[d];
+      base += (int64_t)bm.origin[d] * tm.stride[d];
+    }
   }
-  return in;
-}
+  // Offset of packed element e from the tensor's start, and whether it lies
+  // inside the block's real extent.
+  __device__ __forceinline__ bool offset(int e, int64_t& off) const {
+    off = base;
+    bool in = true;
+#pragma unroll
+    for (int d = K - 1; d >= 0; --d) {
+      int i = e;
+      if (d > 0) {
+        const int q = e / b[d];
+        i = e - q * b[d];
+        e = q;
+      }
+      in = in && i < ext[d];
+      off += (int64_t)i * stride[d];
+    }
+    return in;
+  }
+};
 
+template <int K>
 __global__ __launch_bounds__(256) void tensor_pack_kernel(const TBlockMeta* __restrict__ blocks,
                                                           const TensorMeta* __restrict__ tensors,
                                                           TensorGeom g, int bf16,
@@ -46,19 +68,22 @@ __global__ __launch_bounds__(256) void tensor_pack_kernel(const TBlockMeta* __re
                                                           float* __restrict__ Mom, float momentum) {
   const int b = blockIdx.y;
   const TBlockMeta bm = blocks[b];
-  const TensorMeta tm = tensors[bm.tensor];
+  BlockGeo<K> geo;
+  geo.load(g, bm, tensors[bm.tensor]);
+  const void* grad = tensors[bm.tensor].grad;
   for (int e = blockIdx.x * 256 + threadIdx.x; e < g.E; e += gridDim.x * 256) {
     int64_t off;
     float v = 0.f;
-    if (tensor_offset(g, bm, tm, e, off))
-      v = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(tm.grad)[off])
-               : reinterpret_cast<const float*>(tm.grad)[off];
+    if (geo.offset(e, off))
+      v = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(grad)[off])
+               : reinterpret_cast<const float*>(grad)[off];
     const size_t o = (size_t)b * g.E + e;
     Gp[o] = v;
     if (Mom != nullptr) Mom[o] = momentum * Mom[o] + v;
   }
 }
 
+template <int K>
 __global__ __launch_bounds__(256) void tensor_scatter_kernel(const TBlockMeta* __restrict__ blocks,
                                                              const TensorMeta* __restrict__ tensors,
                                                              TensorGeom g,
@@ -66,18 +91,20 @@ __global__ __launch_bounds__(256) void tensor_scatter_kernel(const TBlockMeta* _
                                                              int bf16, int update) {
   const int b = blockIdx.y;
   const TBlockMeta bm = blocks[b];
-  const TensorMeta tm = tensors[bm.tensor];
+  BlockGeo<K> geo;
+  geo.load(g, bm, tensors[bm.tensor]);
+  void* param = tensors[bm.tensor].param;
   for (int e = blockIdx.x * 256 + threadIdx.x; e < g.E; e += gridDim.x * 256) {
     int64_t off;
-    if (!tensor_offset(g, bm, tm, e, off)) continue;
+    if (!geo.offset(e, off)) continue;
     const float u = Src[(size_t)b * g.E + e];
     if (!update) {
-      reinterpret_cast<float*>(tm.param)[off] = u;
+      reinterpret_cast<float*>(param)[off] = u;
     } else if (bf16) {
-      uint16_t* w = reinterpret_cast<uint16_t*>(tm.param) + off;
+      uint16_t* w = reinterpret_cast<uint16_t*>(param) + off;
       *w = f32_to_bf16(bf16_to_f32(*w) - lr * u);
     } else {
-      float* w = reinterpret_cast<float*>(tm.param) + off;
+      float* w = reinterpret_cast<float*>(param) + off;
       *w = *w - lr * u;
     }
   }
@@ -226,6 +253,51 @@ __global__ __launch_bounds__(256) void mode_product_kernel(const float* __restri
   }
 }
 
+// The last product of the chain (leading dimension k-1, extent J = n <= 8)
+// with the parameter update in its epilogue: output row r is the packed
+// position r * J of the block in its own order, so one offset per thread and
+// W[off + j * stride_(k-1)] -= lr * U[r][j] for j inside the real extent.
+template <int J, int K>
+__global__ __launch_bounds__(256) void mode_product_update_kernel(
+    const float* __restrict__ In, int64_t in_stride, const float* __restrict__ X, int64_t x_stride,
+    const TBlockMeta* __restrict__ blocks, const TensorMeta* __restrict__ tensors, TensorGeom g,
+    int R, float lr, int bf16) {
+  const int b = blockIdx.z;
+  const float* in = In + (size_t)b * in_stride;
+  const float* x = X + (size_t)b * x_stride;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= R) return;
+  const TBlockMeta bm = blocks[b];
+  BlockGeo<K> geo;
+  geo.load(g, bm, tensors[bm.tensor]);
+  int64_t off;
+  if (!geo.offset(r * J, off)) return;
+  float acc[J];
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) acc[jj] = 0.f;
+#pragma unroll
+  for (int l = 0; l < J; ++l) {
+    const float v = in[(size_t)l * R + r];
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj) acc[jj] += x[jj * J + l] * v;
+  }
+  const int64_t st = geo.stride[K - 1];
+  const int ext = geo.ext[K - 1];
+  void* param = tensors[bm.tensor].param;
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) {
+    if (jj >= ext) break;
+    const int64_t o = off + jj * st;
+    if (bf16) {
+      uint16_t* w = reinterpret_cast<uint16_t*>(param) + o;
+      *w = f32_to_bf16(bf16_to_f32(*w) - lr * acc[jj]);
+    } else {
+      float* w = reinterpret_cast<float*>(param) + o;
+      *w = *w - lr * acc[jj];
+    }
+  }
+}
+
 // One thread per factor: cyclic Jacobi in fp64 on the factor's real extent,
 // matrix and eigenvectors in this thread's slice of LDS.
 constexpr int kJacobiThreads = 64;
@@ -312,8 +384,23 @@ hipError_t launch_tensor_pack(const TBlockMeta* blocks, const TensorMeta* tensor
                               hipStream_t s) {
   if (B == 0 || g.E == 0) return hipSuccess;
   const int chunks = std::max(1, std::min(1024, (g.E + 1023) / 1024));
-  hipLaunchKernelGGL(tensor_pack_kernel, dim3(chunks, B), dim3(256), 0, s, blocks, tensors, g,
-                     grad_bf16, Gp, Mom, momentum);
+  const dim3 grid(chunks, B);
+  switch (g.order) {
+    case 2:
+      hipLaunchKernelGGL(tensor_pack_kernel<2>, grid, dim3(256), 0, s, blocks, tensors, g,
+                         grad_bf16, Gp, Mom, momentum);
+      break;
+    case 3:
+      hipLaunchKernelGGL(tensor_pack_kernel<3>, grid, dim3(256), 0, s, blocks, tensors, g,
+                         grad_bf16, Gp, Mom, momentum);
+      break;
+    case 4:
+      hipLaunchKernelGGL(tensor_pack_kernel<4>, grid, dim3(256), 0, s, blocks, tensors, g,
+                         grad_bf16, Gp, Mom, momentum);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -322,8 +409,23 @@ hipError_t launch_tensor_scatter(const TBlockMeta* blocks, const TensorMeta* ten
                                  int32_t update, hipStream_t s) {
   if (B == 0 || g.E == 0) return hipSuccess;
   const int chunks = std::max(1, std::min(1024, (g.E + 1023) / 1024));
-  hipLaunchKernelGGL(tensor_scatter_kernel, dim3(chunks, B), dim3(256), 0, s, blocks, tensors, g,
-                     Src, lr, param_bf16, update);
+  const dim3 grid(chunks, B);
+  switch (g.order) {
+    case 2:
+      hipLaunchKernelGGL(tensor_scatter_kernel<2>, grid, dim3(256), 0, s, blocks, tensors, g, Src,
+                         lr, param_bf16, update);
+      break;
+    case 3:
+      hipLaunchKernelGGL(tensor_scatter_kernel<3>, grid, dim3(256), 0, s, blocks, tensors, g, Src,
+                         lr, param_bf16, update);
+      break;
+    case 4:
+      hipLaunchKernelGGL(tensor_scatter_kernel<4>, grid, dim3(256), 0, s, blocks, tensors, g, Src,
+                         lr, param_bf16, update);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -381,6 +483,28 @@ hipError_t launch_mode_product(const float* In, int64_t in_stride, const float* 
                          in_stride, X, x_stride, Out, out_stride, n, R);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_mode_product_update(const float* In, int64_t in_stride, const float* X,
+                                      int64_t x_stride, const TBlockMeta* blocks,
+                                      const TensorMeta* tensors, TensorGeom g, int32_t R, int32_t B,
+                                      float lr, int32_t param_bf16, hipStream_t s) {
+  if (B == 0 || R == 0) return hipSuccess;
+  const int n = g.b[g.order - 1];
+  const dim3 grid((R + 255) / 256, 1, B);
+  if (n < 1 || n > kMaxSmallSide || g.order < 2 || g.order > 4) return hipErrorInvalidValue;
+#define SHP_MPU(N, K)                                                                          \
+  if (n == N && g.order == K) {                                                                \
+    hipLaunchKernelGGL((mode_product_update_kernel<N, K>), grid, dim3(256), 0, s, In, in_stride, \
+                       X, x_stride, blocks, tensors, g, R, lr, param_bf16);                    \
+    return hipGetLastError();                                                                  \
+  }
+#define SHP_MPU_K(N) SHP_MPU(N, 2) SHP_MPU(N, 3) SHP_MPU(N, 4)
+  SHP_MPU_K(1) SHP_MPU_K(2) SHP_MPU_K(3) SHP_MPU_K(4) SHP_MPU_K(5) SHP_MPU_K(6) SHP_MPU_K(7)
+  SHP_MPU_K(8)
+#undef SHP_MPU_K
+#undef SHP_MPU
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_small_root(const float* H, float* X, int32_t n, int32_t count,

@@ -14,7 +14,8 @@
 //   apply     k products along the leading dimension, each moving it last,
 //             so after k of them the block is back in its own order:
 //             MFMA (C = P^T X with P the block as [b_i][E / b_i]) or the FMA
-//             kernel; then the update scatter W -= lr U.
+//             kernel; the update W -= lr U in the last FMA product's epilogue
+//             when the last dimension is small, else a scatter kernel.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -66,6 +67,16 @@ void destroy_tensor_state(TensorState* t) {
 namespace {
 
 bool small_side(int n) { return n >= 1 && n <= shp::kMaxSmallSide; }
+
+// MFMA tile of the symmetric products of side n over `count` factors: the
+// largest whose launch still gives every CU several workgroups (a 128 x 128
+// factor is one tile at 128, ten at 32).
+int occupancy_tile(int n, int64_t count) {
+  for (int t : {128, 64}) {
+    if (n % t == 0 && count * shp::sym_tiles(n, t) >= 2048) return t;
+  }
+  return 32;
+}
 bool big_side(int n) { return n >= 32 && n <= shp::kMaxSide && n % 32 == 0; }
 
 int make_tensor_plan(const shampoo_config_t* cfg, int32_t order, const int32_t* bd,
@@ -161,7 +172,7 @@ int make_tensor_plan(const shampoo_config_t* cfg, int32_t order, const int32_t* 
     before *= ts.b[i];
     const int64_t after = E / before;
     if (ts.is_big[i]) {
-      ts.stat_tile[i] = pick_tile(ts.b[i], ts.b[i]);
+      ts.stat_tile[i] = occupancy_tile(ts.b[i], ts.B);
       ts.Kp[i] = (K + 15) / 16 * 16;
       ts.rotate[i] = !(after == 1 && K == ts.Kp[i]);
       if (ts.rotate[i]) ts.rot_stride = std::max<int64_t>(ts.rot_stride, ts.Kp[i] * ts.b[i]);
@@ -382,7 +393,18 @@ int do_tensor_apply(shampoo_ctx* h, hipStream_t s, float* out) {
     float* dst = (i == ts.k - 1 && out) ? out : ap[i & 1];
     const float* X = roots + ts.foff[i];
     const double fl = i == 0 ? ts.apply_flops : 0.0;
+    const double esz = h->cfg.param_dtype == SHAMPOO_BF16 ? 2.0 : 4.0;
     int rc;
+    if (i == ts.k - 1 && !out && !ts.is_big[i]) {
+      // last product of the chain with the update in its epilogue
+      rc = timed(h, kApply, fl, 4.0 * ts.B * ts.E + 2.0 * esz * ts.real_elems, s, [&] {
+        return shp::launch_mode_product_update(
+            cur, ts.E, X, (int64_t)n * n, h->at<shp::TBlockMeta>(ts.off_blocks),
+            h->at<shp::TensorMeta>(ts.off_meta), geom(ts), (int32_t)R, (int32_t)ts.B,
+            (float)h->cfg.lr, h->cfg.param_dtype == SHAMPOO_BF16, s);
+      });
+      return rc;
+    }
     if (ts.is_big[i] && ts.apply_tile[i] > 0) {
       // C[r][j] = sum_l cur[l][r] X[l][j]: the product along dimension i (X is
       // symmetric), which leaves dimension i last
