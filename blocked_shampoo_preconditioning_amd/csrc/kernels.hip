@@ -71,15 +71,16 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
 // arrays have been demoted to scratch memory by the compiler.
 // MASK selects the fragments (bit i * FN + j) whose MFMAs run; the others
 // only take part in the loads and barriers.
+// (wm, wn) is the wave's fragment block inside the tile; every wave loads its
+// share of the operand tiles whatever its block.
 template <class C, int MASK = -1>
-__device__ __forceinline__ void mainloop(const float* __restrict__ P, const float* __restrict__ Q,
-                                         int M, int N, int K, int m0, int n0,
-                                         floatx16 (&acc)[C::FM][C::FN], float* lds) {
+__device__ __forceinline__ void mainloop_w(const float* __restrict__ P, const float* __restrict__ Q,
+                                           int M, int N, int K, int m0, int n0, int wm, int wn,
+                                           floatx16 (&acc)[C::FM][C::FN], float* lds) {
   float* sP = lds;
   float* sQ = lds + 2 * C::BK * C::LDP;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % C::WM, wn = wave / C::WM;
+  const int lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
 
 #pragma unroll
@@ -153,6 +154,14 @@ __device__ __forceinline__ void mainloop(const float* __restrict__ P, const floa
   }
 }
 
+template <class C, int MASK = -1>
+__device__ __forceinline__ void mainloop(const float* __restrict__ P, const float* __restrict__ Q,
+                                         int M, int N, int K, int m0, int n0,
+                                         floatx16 (&acc)[C::FM][C::FN], float* lds) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  mainloop_w<C, MASK>(P, Q, M, N, K, m0, n0, wave % C::WM, wave / C::WM, acc, lds);
+}
+
 template <int FM, int FN>
 constexpr int upper_mask() {
   int m = 0;
@@ -162,37 +171,88 @@ constexpr int upper_mask() {
   return m;
 }
 
-// Main loop of a symmetric product's tile. On a diagonal tile, fragments
-// strictly below the diagonal are not needed: a wave whose block lies below
-// it runs no MFMA, a wave on it runs the upper fragments only. The choice is
-// made once per wave (the wave index is uniform; readfirstlane tells the
-// compiler so), outside the K loop.
+// Fragments of rows i < FM / 2 (top) or i >= FM / 2 (bottom).
+template <int FM, int FN>
+constexpr int half_mask(bool bottom) {
+  int m = 0;
+  for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j)
+      if ((i >= FM / 2) == bottom) m |= 1 << (i * FN + j);
+  return m;
+}
+
+// Which fragments a wave computes on a symmetric product's tile. Off the
+// diagonal: its own block, all fragments. On a diagonal tile only the upper
+// triangle is needed: a wave on the diagonal runs its upper fragments; the
+// block above the diagonal is split by rows between its own wave and the
+// mirror wave below the diagonal (which would otherwise idle), so the tile
+// takes 3 fragment times instead of 4 with 2 x 2 fragments per wave. The
+// choice is per wave (the wave index is uniform; readfirstlane tells the
+// compiler so) and made outside the K loop.
+template <class C>
+struct SymWave {
+  int wm, wn, mask;
+  __device__ __forceinline__ SymWave(bool diag) {
+    static_assert(C::FM == C::FN && C::WM == C::WN, "symmetric tiles are square");
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wm = wave % C::WM;
+    wn = wave / C::WM;
+    mask = -1;
+    if (!diag) return;
+    if (wm == wn) {
+      mask = upper_mask<C::FM, C::FN>();
+    } else if (C::FM >= 2) {
+      const bool below = wm > wn;
+      if (below) {
+        const int t = wm;
+        wm = wn;
+        wn = t;
+      }
+      mask = below ? half_mask<C::FM, C::FN>(true) : half_mask<C::FM, C::FN>(false);
+    } else if (wm > wn) {
+      mask = 0;
+    }
+  }
+};
+
 template <class C>
 __device__ __forceinline__ void mainloop_sym(const float* __restrict__ P,
                                              const float* __restrict__ Q, int M, int N, int K,
                                              int m0, int n0, floatx16 (&acc)[C::FM][C::FN],
-                                             float* lds, bool diag) {
-  static_assert(C::FM == C::FN && C::WM == C::WN, "symmetric tiles are square");
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave % C::WM, wn = wave / C::WM;
-  if (!diag || wm < wn)
-    mainloop<C>(P, Q, M, N, K, m0, n0, acc, lds);
-  else if (wm == wn)
-    mainloop<C, upper_mask<C::FM, C::FN>()>(P, Q, M, N, K, m0, n0, acc, lds);
+                                             float* lds, const SymWave<C>& sw) {
+  constexpr int kUpper = upper_mask<C::FM, C::FN>();
+  constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
+  if (sw.mask == -1)
+    mainloop_w<C>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else if (sw.mask == kUpper)
+    mainloop_w<C, kUpper>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else if (C::FM >= 2 && sw.mask == kTop)
+    mainloop_w<C, kTop>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else if (C::FM >= 2 && sw.mask == kBottom)
+    mainloop_w<C, kBottom>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
   else
-    mainloop<C, 0>(P, Q, M, N, K, m0, n0, acc, lds);
+    mainloop_w<C, 0>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
 }
 
-// Row / column of accumulator register r of fragment (i, j).
+// Row / column of accumulator register r of fragment (i, j) of the wave's
+// block (wm, wn).
 template <class C>
-__device__ __forceinline__ int frag_row(int m0, int i, int r) {
-  const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) % C::WM;
+__device__ __forceinline__ int frag_row_w(int m0, int wm, int i, int r) {
+  const int lane = threadIdx.x & 63;
   return m0 + wm * 32 * C::FM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 template <class C>
-__device__ __forceinline__ int frag_col(int n0, int j) {
-  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) / C::WM;
+__device__ __forceinline__ int frag_col_w(int n0, int wn, int j) {
+  const int lane = threadIdx.x & 63;
   return n0 + wn * 32 * C::FN + j * 32 + (lane & 31);
+}
+template <class C>
+__device__ __forceinline__ int frag_row(int m0, int i, int r) {
+  return frag_row_w<C>(m0, (threadIdx.x >> 6) % C::WM, i, r);
+}
+template <class C>
+__device__ __forceinline__ int frag_col(int n0, int j) {
+  return frag_col_w<C>(n0, (threadIdx.x >> 6) / C::WM, j);
 }
 
 // ---------------------------------------------------------------------------
@@ -226,9 +286,10 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const int m0 = ti * C::BM, n0 = tj * C::BN;
 
   const bool diag = (ti == tj);
+  const SymWave<C> sw(diag);
   floatx16 acc[C::FM][C::FN];
   mainloop_sym<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0,
-                  acc, lds, diag);
+                  acc, lds, sw);
 
   // Epilogue: C = alpha acc + beta D + gamma I on and above the diagonal, and
   // the mirror below it. The four registers 4g..4g+3 of a lane hold four
@@ -246,18 +307,16 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
     e_gamma = cf[3];
   }
   const int N = pb.N;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave % C::WM, wn = wave / C::WM;
   float rs = 0.f;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
-      if (diag && wm * C::FM + i > wn * C::FN + j) continue;  // wave-uniform
-      const int col = frag_col<C>(n0, j);
+      if (!((sw.mask >> (i * C::FN + j)) & 1)) continue;  // wave-uniform
+      const int col = frag_col_w<C>(n0, sw.wn, j);
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int row0 = frag_row<C>(m0, i, 4 * g4);
+        const int row0 = frag_row_w<C>(m0, sw.wm, i, 4 * g4);
         f32x4 v;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
