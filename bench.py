@@ -171,7 +171,12 @@ def run_tensor(args, w, torch, S, synth):
     params = src.init_params()
     total = args.steps + args.warmup
     n_sets = total if args.grad_sets <= 0 else max(1, min(args.grad_sets, total))
-    grad_sets = [src.grads(t) for t in range(1, n_sets + 1)]
+    grad_sets = []
+    for t in range(1, n_sets + 1):
+        grad_sets.append(src.grads(t))
+        if t % 10 == 0 or t == n_sets:
+            torch.cuda.synchronize()
+            log(f"gradient sets generated: {t}/{n_sets}")
     sh = S.TensorShampoo(w.shapes, w.block_dims, beta2=w.beta2, eps=w.eps, lr=w.lr,
                          root_every=w.root_every, newton_max_iters=w.newton_max_iters,
                          newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode,
@@ -300,7 +305,12 @@ def main():
     params = src.init_params()
     total = args.steps + args.warmup
     n_sets = total if args.grad_sets <= 0 else max(1, min(args.grad_sets, total))
-    grad_sets = [src.grads(t) for t in range(1, n_sets + 1)]
+    grad_sets = []
+    for t in range(1, n_sets + 1):
+        grad_sets.append(src.grads(t))
+        if t % 10 == 0 or t == n_sets:
+            torch.cuda.synchronize()
+            log(f"gradient sets generated: {t}/{n_sets}")
     sh = S.Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
                    root_every=w.root_every, newton_max_iters=w.newton_max_iters,
                    newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype,
