@@ -56,6 +56,10 @@ __all__ = [
     "update_statistics",
     "inverse_root_eigh",
     "newton_scale",
+    "newton_map",
+    "newton_balance",
+    "spectrum_floor_estimate",
+    "SCALED_PHASE_END",
     "inverse_root_coupled_newton",
     "db_scale",
     "sqrt_pair_db",
@@ -164,6 +168,19 @@ def inverse_root_eigh(A, p=4):
     return (Q * lam ** (-1.0 / p)) @ Q.T
 
 
+def _power_lambda(A, power_iters=16):
+    """||A v_k|| after power_iters products from v_0 = 1 / sqrt(n) (0 if A v = 0)."""
+    v = np.full(A.shape[0], 1.0 / math.sqrt(A.shape[0]))
+    lam = 0.0
+    for _ in range(power_iters):
+        w = A @ v
+        lam = float(np.sqrt(np.sum(w * w)))
+        if lam == 0.0:
+            break
+        v = w / lam
+    return lam
+
+
 def newton_scale(A, p=4, mode=1, power_iters=16):
     """Norm used to scale A before the coupled Newton iteration.
 
@@ -173,6 +190,8 @@ def newton_scale(A, p=4, mode=1, power_iters=16):
             largest eigenvalue of a symmetric matrix.
     The DASH page (abstract) stresses that this scaling decides how fast
     Shampoo's root solver converges; the limit reached does not depend on it.
+    mode 3: mode 2's s, and the iteration then scales itself every step
+            (see newton_balance).
     mode 2: s = lam / 2, where lam is the power-iteration estimate of the
             largest eigenvalue: from v_0 = (1, ..., 1) / sqrt(n), repeat
             w = A v, lam = ||w||, v = w / lam, power_iters (16) times. For a
@@ -190,16 +209,73 @@ def newton_scale(A, p=4, mode=1, power_iters=16):
     if mode == 1:
         return min(fro, inf) * 2.0 / (p + 1)
     if mode == 2:
-        v = np.full(A.shape[0], 1.0 / math.sqrt(A.shape[0]))
-        lam = 0.0
-        for _ in range(power_iters):
-            w = A @ v
-            lam = float(np.sqrt(np.sum(w * w)))
-            if lam == 0.0:
-                break
-            v = w / lam
+        lam = _power_lambda(A, power_iters)
         return lam / 2.0 if lam > 0.0 else min(fro, inf) * 2.0 / (p + 1)
+    if mode == 3:  # the start of mode 2; the iteration then scales itself
+        return newton_scale(A, p, 2, power_iters)
     raise ValueError(f"unknown scale mode {mode}")
+
+
+# ---------------------------------------------------------------------------
+# Per-iteration scaling (scale mode 3)
+#
+# One coupled Newton iteration acts on every eigenvalue m of M through the
+# scalar map f(m) = m ((p + 1 - m) / p)^p, which has its maximum 1 at m = 1
+# and maps (0, p + 1) into (0, 1]. After the first iteration the spectrum
+# lies in (0, 1], so M may be scaled by any mu in [1, 0.9 (p + 1)] (and X by
+# mu^(1/p), keeping X^p A = M) without leaving the convergence region; a
+# mu > 1 lifts the small eigenvalues, the slow ones, mu times faster, at the
+# price of pulling the eigenvalues near 1 down to f(mu). With an estimate a
+# of the bottom of the spectrum the best mu balances the two ends,
+# f(mu a) = f(mu). The estimate starts from spectrum_floor_estimate (Rayleigh
+# quotients, never below the smallest eigenvalue: the scaling can only err on
+# the cautious side) and follows the scalar map. Scaling stops once the estimate passes
+# SCALED_PHASE_END; the quadratic phase then runs unscaled. (A reading: the
+# pages name no iteration; scaling the coupled iteration this way follows
+# the scaled Newton methods for matrix roots in the numerical literature.)
+# ---------------------------------------------------------------------------
+SCALED_PHASE_END = 0.75
+BALANCE_STEPS = 40
+
+
+def spectrum_floor_estimate(A, lam, power_iters=16):
+    """Estimate of the smallest eigenvalue of a symmetric A that is never
+    below it: the smaller of the smallest diagonal entry and the Rayleigh
+    quotient v^T A v after power_iters steps of the power iteration on
+    lam I - A (whose top eigenvector is A's bottom one) from the alternating
+    vector v_0 = (1, -1, 1, ...) / sqrt(n). Both are Rayleigh quotients of A."""
+    A = np.asarray(A, dtype=np.float64)
+    n = A.shape[0]
+    v = np.array([1.0 if i % 2 == 0 else -1.0 for i in range(n)]) / math.sqrt(n)
+    for _ in range(power_iters):
+        w = lam * v - A @ v
+        nw = float(np.sqrt(np.sum(w * w)))
+        if nw == 0.0:
+            break
+        v = w / nw
+    return min(float(np.min(np.diag(A))), float(v @ (A @ v)))
+
+
+def newton_map(m, p, mu=1.0):
+    """f(mu m) = mu m ((p + 1 - mu m) / p)^p."""
+    y = mu * m
+    return y * ((p + 1 - y) / p) ** p
+
+
+def newton_balance(a, p):
+    """mu in [1, 0.9 (p + 1)] with f(mu a) = f(mu), by BALANCE_STEPS bisection
+    steps (the lower end of the last bracket); 0.9 (p + 1) when f(mu a) < f(mu)
+    holds even there."""
+    lo, hi = 1.0, 0.9 * (p + 1)
+    if newton_map(a, p, hi) < newton_map(1.0, p, hi):
+        return hi
+    for _ in range(BALANCE_STEPS):
+        mid = 0.5 * (lo + hi)
+        if newton_map(a, p, mid) < newton_map(1.0, p, mid):
+            lo = mid
+        else:
+            hi = mid
+    return lo
 
 
 @dataclass
@@ -207,6 +283,7 @@ class NewtonInfo:
     iters: int
     residuals: list = field(default_factory=list)
     status: str = "capped"  # converged | stalled | diverged | capped
+    mus: list = field(default_factory=list)  # scale of M at every iteration (1 unless mode 3)
 
 
 FLOOR_GUARD = 1e-3  # a residual that grows from below this is at the rounding floor
@@ -237,28 +314,44 @@ def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
     M = A / s
     X = s ** (-1.0 / p) * eye
     info = NewtonInfo(0)
+    scaled = scale_mode == 3
+    if scaled:
+        # lower estimate of the spectrum of M after the first (unscaled)
+        # iteration: f(a_0) for the smallest, f(b_0) for the largest eigenvalue
+        # (b_0 = lam / s = 2, or (p + 1) / 2 when the fallback norm was used)
+        lam = _power_lambda(A)
+        b0 = 2.0 if lam > 0.0 else (p + 1) / 2.0
+        a = min(newton_map(spectrum_floor_estimate(A, lam) / s, p), newton_map(b0, p))
+    mu = 1.0
     r_prev = math.inf
     for k in range(max_iters):
-        T = ((p + 1) * eye - M) / p
-        X_new = X @ T
-        M_new = np.linalg.matrix_power(T, p) @ M
+        Ms = mu * M
+        T = ((p + 1) * eye - Ms) / p
+        X_new = mu ** (1.0 / p) * X @ T
+        M_new = np.linalg.matrix_power(T, p) @ Ms
         r = float(np.sqrt(np.sum((M_new - eye) ** 2)) / math.sqrt(n))
         info.residuals.append(r)
+        info.mus.append(mu)
         if not math.isfinite(r):
             info.status = "diverged"
             break
-        if tol > 0.0:
+        if tol > 0.0 and mu == 1.0:
             if r > divergence_factor * r_prev and r_prev > FLOOR_GUARD:
                 info.status = "diverged"
                 break
             if r >= r_prev:
                 info.status = "stalled"
                 break
-        X, M, r_prev = X_new, M_new, r
+        # a scaled iterate need not shrink the residual: accept it and start
+        # the monotone checks afresh once the scaling has stopped
+        X, M, r_prev = X_new, M_new, (r if mu == 1.0 else math.inf)
         info.iters = k + 1
         if tol > 0.0 and r <= tol:
             info.status = "converged"
             break
+        if scaled:
+            mu = newton_balance(a, p) if a < SCALED_PHASE_END else 1.0
+            a = newton_map(a, p, mu)
     return X, info
 
 
@@ -274,8 +367,8 @@ def db_scale(A, mode=2, power_iters=16):
     bound = min(fro, float(np.max(np.sum(np.abs(A), axis=1))))
     if mode == 1:
         return bound
-    if mode == 2:
-        lam = 2.0 * newton_scale(A, 4, 2, power_iters)  # newton_scale returns lam / 2
+    if mode in (2, 3):  # mode 3's per-iteration scaling belongs to the coupled Newton iteration
+        lam = _power_lambda(A, power_iters)
         return lam if lam > 0.0 else bound
     raise ValueError(f"unknown scale mode {mode}")
 

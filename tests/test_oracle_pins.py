@@ -580,3 +580,59 @@ def test_chebyshev_orthogonal_similarity():
     Xd, _ = inverse_root_chebyshev(np.diag(lam), 0.01, 12, interval=iv)
     assert np.count_nonzero(Xd - np.diag(np.diag(Xd))) == 0
     assert rel(Xa, Q @ Xd @ Q.T) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Scale mode 3: the coupled Newton iteration that scales itself every step
+# ---------------------------------------------------------------------------
+def _rotated(n, cond, seed):
+    rng = np.random.default_rng(seed)
+    Q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    lam = np.geomspace(1.0, 1.0 / cond, n)
+    return (Q * lam) @ Q.T
+
+
+def _column_scaled_stat(n, seed):
+    rng = np.random.default_rng(seed)
+    cs = np.exp(rng.uniform(np.log(1e-2), 0.0, n))
+    G = rng.standard_normal((n, n)) * 1e-2 * cs[None, :]
+    return 1e-3 * G.T @ G + 1e-7 * np.eye(n)
+
+
+@pytest.mark.parametrize("p", [4, 6, 8])
+@pytest.mark.parametrize("kind,cond", [("rot", 1e2), ("rot", 1e4), ("colscaled", None)])
+def test_scaled_newton_reaches_the_root(p, kind, cond):
+    A = _rotated(96, cond, 3) if kind == "rot" else _column_scaled_stat(96, 5)
+    X, info = inverse_root_coupled_newton(A, p, 60, 1e-11, scale_mode=3)
+    ref = inverse_root_eigh(A, p)
+    assert info.status == "converged"
+    assert np.linalg.norm(X - ref) / np.linalg.norm(ref) < 1e-8
+    # the scales stay inside the safe range and the first iteration is unscaled
+    assert info.mus[0] == 1.0 and all(1.0 <= m <= 0.9 * (p + 1) for m in info.mus)
+
+
+@pytest.mark.parametrize("kind,cond", [("rot", 1e3), ("rot", 1e5), ("colscaled", None)])
+def test_scaled_newton_needs_fewer_iterations(kind, cond):
+    A = _rotated(96, cond, 7) if kind == "rot" else _column_scaled_stat(128, 9)
+    _, i2 = inverse_root_coupled_newton(A, 4, 60, 1e-10, scale_mode=2)
+    _, i3 = inverse_root_coupled_newton(A, 4, 60, 1e-10, scale_mode=3)
+    assert i3.iters < i2.iters, (i3.iters, i2.iters)
+    assert any(m > 1.0 for m in i3.mus)
+
+
+def test_scaled_newton_diagonal_closed_form():
+    lam = np.geomspace(3.0, 3e-4, 40)
+    X, info = inverse_root_coupled_newton(np.diag(lam), 4, 60, 1e-12, scale_mode=3)
+    assert np.abs(X - np.diag(lam ** -0.25)).max() / lam.min() ** -0.25 < 1e-9
+    assert np.abs(X - np.diag(np.diag(X))).max() == 0.0  # stays diagonal
+
+
+def test_spectrum_floor_estimate_bounds():
+    from oracle import spectrum_floor_estimate
+    for seed in range(4):
+        A = _rotated(64, 10.0 ** (seed + 1), seed)
+        lam = np.linalg.eigvalsh(A)
+        e = spectrum_floor_estimate(A, lam[-1])
+        assert lam[0] - 1e-12 <= e <= np.diag(A).min() + 1e-12
+    D = np.diag(np.linspace(2.0, 0.5, 9))
+    assert spectrum_floor_estimate(D, 2.0) == 0.5
