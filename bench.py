@@ -164,6 +164,8 @@ def run_tensor(args, w, torch, S, synth):
         w = dataclasses.replace(w, momentum=args.momentum)
     if args.root_method is not None:
         w = dataclasses.replace(w, root_method=args.root_method)
+    if args.scale_mode is not None:
+        w = dataclasses.replace(w, newton_scale_mode=args.scale_mode)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"tensor workload {w.name}: {len(w.shapes)} tensors, blocks {w.block_dims}")
@@ -266,6 +268,8 @@ def main():
                     help="momentum folded in before preconditioning (default: the workload's, 0)")
     ap.add_argument("--root-method", default=None, choices=("newton", "newton_db", "chebyshev"),
                     help="inverse-root solver (default: the workload's, coupled Newton)")
+    ap.add_argument("--scale-mode", type=int, default=None, choices=(0, 1, 2, 3),
+                    help="Newton scale mode (default: the workload's)")
     ap.add_argument("--cheb-degree", type=int, default=None,
                     help="Chebyshev degree (default: the workload's, 128)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -298,6 +302,8 @@ def main():
         w = dataclasses.replace(w, root_method=args.root_method)
     if args.cheb_degree is not None:
         w = dataclasses.replace(w, cheb_degree=args.cheb_degree)
+    if args.scale_mode is not None:
+        w = dataclasses.replace(w, newton_scale_mode=args.scale_mode)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {w.name}: {len(w.shapes)} matrices, blocks {w.block_rows}x{w.block_cols}")

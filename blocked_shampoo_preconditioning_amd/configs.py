@@ -39,7 +39,7 @@ class Workload:
     diag_fraction: float = 0.0    # fraction of blocks whose gradient is diagonal
     newton_max_iters: int = 25
     newton_tol: float = 1e-6      # <= 0: exactly newton_max_iters iterations
-    newton_scale_mode: int = 2
+    newton_scale_mode: int = 3    # 3: the iteration scales itself (fewer iterations)
     momentum: float = 0.0         # ordinary momentum folded in before preconditioning
     root_method: str = "newton"   # newton (coupled) | newton_db (Denman-Beavers) | chebyshev
     cheb_degree: int = 128        # degree of the Chebyshev interpolant (chebyshev only)
@@ -73,9 +73,10 @@ WORKLOADS = {
     "decoder_1b_b1024_bf16": Workload(
         name="decoder_1b_b1024_bf16", shapes=_layers(DECODER_1B_LAYER, 24), block_rows=1024,
         block_cols=1024, root_every=10, steps=50, dtype="bf16", grad="col_scaled",
-        grad_std=1e-2, diag_fraction=0.1, newton_max_iters=10, newton_tol=0.0, seed=1005,
+        grad_std=1e-2, diag_fraction=0.1, newton_max_iters=10, newton_tol=0.0,
+        newton_scale_mode=2, seed=1005,
         notes="as decoder_1b_b1024_f32 with bf16 gradients and parameters, 10 fixed "
-              "Newton iterations, 10% diagonal blocks"),
+              "(unscaled) Newton iterations, 10% diagonal blocks"),
 }
 
 # ---------------------------------------------------------------------------
@@ -112,7 +113,7 @@ class TensorWorkload:
     grad_std: float = 1.0
     newton_max_iters: int = 25
     newton_tol: float = 1e-6
-    newton_scale_mode: int = 2
+    newton_scale_mode: int = 3
     momentum: float = 0.0
     root_method: str = "newton"
     cheb_degree: int = 128

@@ -117,7 +117,17 @@ struct NewtonCtl {
   int32_t max_iters;
   int32_t scale_mode;
   int32_t p;            // the root is A^(-1/p)
+  // scale mode 3 (coupled Newton scaling itself every iteration):
+  float* lo;            // per factor: estimate of the bottom of the spectrum of the next M
+  float* coef;          // per factor kCoefRecord floats: epilogue quadruples of the next
+                        // iteration's T^2, X T and M' products, then the previous scale
 };
+
+// Scale mode 3 (see newton_check_kernel): record layout per factor.
+constexpr int kCoefRecord = 16;
+constexpr int kCoefT2 = 0, kCoefXT = 4, kCoefM = 8, kCoefPrevMu = 12;
+constexpr double kScaledPhaseEnd = 0.75;
+constexpr int kBalanceSteps = 40;
 
 // ---- launchers (return hipGetLastError()) ----
 // Mom (nullable): momentum buffer [B][br][bc], updated as Mom = momentum * Mom + Gp.

@@ -585,6 +585,9 @@ __device__ __forceinline__ const float* factor_ptr(const float* base, const Fact
 // Norm scaling: one workgroup per factor, fixed-order reductions.
 //   mode 0: s = ||A||_F
 //   mode 1: s = min(||A||_F, ||A||_inf) * 2 / (p + 1)
+//   mode 3: mode 2's s; the coupled Newton iteration then scales itself
+//           every step (newton_check_kernel), starting from an estimate of the
+//           spectrum's bottom made here
 //   mode 2: s = lam / 2, lam the power-iteration estimate ||A v_k|| of the
 //           largest eigenvalue after kPowerIters (16) products from
 //           v_0 = 1 / sqrt(n). For symmetric A the ratios ||A^(j+1) v|| /
@@ -605,10 +608,55 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+// Scalar map of one coupled Newton iteration on an eigenvalue m of M scaled
+// by mu: f(mu m) = mu m ((p + 1 - mu m) / p)^p.
+__device__ __forceinline__ double newton_map(double m, int p, double mu) {
+  const double y = mu * m, t = (p + 1 - y) / p;
+  double tp = 1.0;
+  for (int i = 0; i < p; ++i) tp *= t;
+  return y * tp;
+}
+
+// mu in [1, 0.9 (p + 1)] with f(mu a) = f(mu): bisection, kBalanceSteps steps.
+__device__ double newton_balance(double a, int p) {
+  double lo = 1.0, hi = 0.9 * (p + 1);
+  if (newton_map(a, p, hi) < newton_map(1.0, p, hi)) return hi;
+  for (int i = 0; i < kBalanceSteps; ++i) {
+    const double mid = 0.5 * (lo + hi);
+    if (newton_map(a, p, mid) < newton_map(1.0, p, mid))
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// Epilogue quadruples (alpha, beta, beta2, gamma) of one iteration at scale
+// mu: T = ((p + 1) I - mu M) / p,
+//   T^2   = (mu^2 M M - 2 (p + 1) mu M + (p + 1)^2 I) / p^2
+//   X' = mu^(1/p) X T = ((p + 1) mu^(1/p) X - mu^(1 + 1/p) X M) / p
+//   M' = T^p (mu M).
+__device__ void write_newton_coefs(float* rec, double mu, int p) {
+  const double pp = (double)p * p, q = p + 1.0, mr = pow(mu, 1.0 / p);
+  rec[kCoefT2 + 0] = (float)(mu * mu / pp);
+  rec[kCoefT2 + 1] = (float)(-2.0 * q * mu / pp);
+  rec[kCoefT2 + 2] = 0.f;
+  rec[kCoefT2 + 3] = (float)(q * q / pp);
+  rec[kCoefXT + 0] = (float)(-mu * mr / p);
+  rec[kCoefXT + 1] = (float)(q * mr / p);
+  rec[kCoefXT + 2] = 0.f;
+  rec[kCoefXT + 3] = 0.f;
+  rec[kCoefM + 0] = (float)mu;
+  rec[kCoefM + 1] = 0.f;
+  rec[kCoefM + 2] = 0.f;
+  rec[kCoefM + 3] = 0.f;
+}
+
 __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A, FactorSet fs,
                                                     NewtonCtl c) {
   __shared__ double red[4];
   __shared__ double red_inf[4];
+  __shared__ double red_min[4];
   __shared__ float v[kMaxSide];
   __shared__ float w[kMaxSide];
   const int f = blockIdx.x;
@@ -617,10 +665,16 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   const int nr = fs.nreal[f];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n4 = nr & ~3;
-  // pass 1: squares, absolute row sums and w = A 1 (row sums)
-  double sq = 0.0, rowmax = 0.0;
+  const bool db = c.solver == kNewtonDB;
+  const bool cheb = c.solver == kChebyshev;
+  const bool power = c.scale_mode >= 2 || cheb;
+  const bool scaled = c.scale_mode == 3 && c.solver == kCoupledNewton;
+  // pass 1: squares, absolute row sums, w = A 1 (row sums) and the smallest
+  // diagonal entry
+  double sq = 0.0, rowmax = 0.0, dmin = INFINITY;
   for (int r = wave; r < nr; r += 4) {
     const float* row = Af + (int64_t)r * n;
+    dmin = fmin(dmin, (double)row[r]);
     double as = 0.0, rs = 0.0;
     for (int j = lane * 4; j < n4; j += 256) {
       const float4 x = *reinterpret_cast<const float4*>(row + j);
@@ -640,19 +694,20 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
       rs += __shfl_xor(rs, o);
     }
     rowmax = fmax(rowmax, as);
-    if (lane == 0 && c.scale_mode == 2) w[r] = (float)rs;
+    if (lane == 0 && power) w[r] = (float)rs;
   }
-  if (lane == 0) red_inf[wave] = rowmax;
+  if (lane == 0) {
+    red_inf[wave] = rowmax;
+    red_min[wave] = dmin;
+  }
   const double fro = sqrt(block_sum(sq, red));
   const double inf = fmax(fmax(red_inf[0], red_inf[1]), fmax(red_inf[2], red_inf[3]));
   const double bound = fmin(fro, inf);
   // spectral target: Newton converges on (0, p + 1), the Denman-Beavers pair on (0, 2)
-  const bool db = c.solver == kNewtonDB;
-  const bool cheb = c.solver == kChebyshev;
   const double mode1 = db ? 1.0 : 2.0 / (c.p + 1);
   double s = c.scale_mode == 0 ? fro : bound * mode1;
-  if (c.scale_mode == 2 || cheb) {
-    double lam = 0.0;
+  double lam = 0.0;
+  if (power) {
     for (int it = 0; it < kPowerIters; ++it) {
       if (it > 0) {
         // w = A v
@@ -685,6 +740,45 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
     // holds always
     if (cheb) s = lam > 0.0 ? fmin(lam / 0.55, bound) : bound;
   }
+  double est = fmin(fmin(red_min[0], red_min[1]), fmin(red_min[2], red_min[3]));
+  if (scaled && lam > 0.0) {
+    // bottom of the spectrum: power iteration on lam I - A from the
+    // alternating vector, then the Rayleigh quotient v^T A v (never below the
+    // smallest eigenvalue, like every diagonal entry)
+    const float inv0 = (float)(1.0 / sqrt((double)nr));
+    for (int r = threadIdx.x; r < nr; r += 256) v[r] = (r & 1) ? -inv0 : inv0;
+    __syncthreads();
+    for (int it = 0; it <= kPowerIters; ++it) {
+      double rq = 0.0;
+      for (int r = wave; r < nr; r += 4) {
+        const float* row = Af + (int64_t)r * n;
+        float d = 0.f;
+        for (int j = lane * 4; j < n4; j += 256) {
+          const float4 x = *reinterpret_cast<const float4*>(row + j);
+          d += x.x * v[j] + x.y * v[j + 1] + x.z * v[j + 2] + x.w * v[j + 3];
+        }
+        for (int j = n4 + lane; j < nr; j += 64) d += row[j] * v[j];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
+        if (lane == 0) {
+          w[r] = (float)(lam * v[r] - d);
+          rq += (double)v[r] * d;
+        }
+      }
+      rq = block_sum(rq, red);  // v^T A v of the current v
+      if (it == kPowerIters) {
+        est = fmin(est, rq);
+        break;
+      }
+      double nn = 0.0;
+      for (int r = threadIdx.x; r < nr; r += 256) nn += (double)w[r] * w[r];
+      nn = block_sum(nn, red);
+      if (!(nn > 0.0)) break;
+      const float inv = (float)(1.0 / sqrt(nn));
+      for (int r = threadIdx.x; r < nr; r += 256) v[r] = w[r] * inv;
+      __syncthreads();
+    }
+  }
   if (threadIdx.x == 0) {
     const bool ok = s > 0.0 && isfinite(s) && isfinite(fro);
     c.scale[f] = (float)s;
@@ -692,6 +786,17 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
     c.status[f] = ok ? 0 : 3;
     c.final_iter[f] = 0;
     c.rprev[f] = INFINITY;
+    if (scaled) {
+      // the estimate for M after the first, unscaled iteration: f(a_0) for the
+      // bottom, f(b_0) for the top (b_0 = lam / s = 2, or (p + 1) / 2 when the
+      // norm bound was used)
+      const double b0 = lam > 0.0 ? 2.0 : 0.5 * (c.p + 1);
+      const double a0 = ok ? fmax(est, 0.0) / s : 0.0;
+      c.lo[f] = (float)fmin(newton_map(a0, c.p, 1.0), newton_map(b0, c.p, 1.0));
+      float* rec = c.coef + (size_t)f * kCoefRecord;
+      write_newton_coefs(rec, 1.0, c.p);
+      rec[kCoefPrevMu] = 1.f;
+    }
   }
 }
 
@@ -739,6 +844,7 @@ __global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, Newton
   __syncthreads();
   const int cur = iter + shift;  // the iterate whose residual was just formed
   const int nf = fs.count();
+  const bool scaled = c.scale_mode == 3 && c.solver == kCoupledNewton && c.coef != nullptr;
   for (int f = threadIdx.x; f < nf; f += blockDim.x) {
     if (c.status[f] != 0) continue;
     const int g = f / fs.B;
@@ -748,17 +854,25 @@ __global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, Newton
     float s = 0.f;
     for (int t = 0; t < nt; ++t) s += p[t];
     const float r = sqrtf(s) / sqrtf((float)fs.nreal[f]);
-    const float rp = c.rprev[f];
+    // Scale mode 3: this iterate was made with M scaled by mu (mu > 1 lifts
+    // the slow small eigenvalues and may raise the residual), the previous one
+    // with mu_prev; only unscaled iterates take the monotone tests, and the
+    // first of them after the scaled phase is compared with nothing.
+    float* rec = scaled ? c.coef + (size_t)f * kCoefRecord : nullptr;
+    const float mu = scaled ? rec[kCoefM] : 1.f;
+    const float mu_prev = scaled ? rec[kCoefPrevMu] : 1.f;
+    const float rp = mu_prev > 1.f ? INFINITY : c.rprev[f];
     // In exact arithmetic both iterations shrink the residual every step, so a
     // growth means trouble: from a residual above kFloorGuard it is divergence,
     // below it the fp32 floor has been reached (stalled, the previous iterate
     // is kept and is as good).
+    const bool monotone = c.tol > 0.f && mu == 1.f;
     int st = 0;
     if (!isfinite(r)) {
       st = 3;
-    } else if (c.tol > 0.f && r > 1.2f * rp && rp > kFloorGuard) {
+    } else if (monotone && r > 1.2f * rp && rp > kFloorGuard) {
       st = 3;
-    } else if (c.tol > 0.f && r >= rp) {
+    } else if (monotone && r >= rp) {
       st = 2;
     } else {
       c.rprev[f] = r;
@@ -770,7 +884,18 @@ __global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, Newton
     }
     // a rejected iterate leaves final_iter at the previous (accepted) one
     c.status[f] = st;
-    if (st == 0) atomicAdd(&cnt_out[g], 1);
+    if (st == 0) {
+      atomicAdd(&cnt_out[g], 1);
+      if (scaled) {
+        // the next scale balances the scalar map at the tracked estimate of the
+        // spectrum's bottom; the estimate follows the map
+        const double a = c.lo[f];
+        const double mun = a < kScaledPhaseEnd ? newton_balance(a, c.p) : 1.0;
+        c.lo[f] = (float)newton_map(a, c.p, mun);
+        write_newton_coefs(rec, mun, c.p);
+        rec[kCoefPrevMu] = mu;
+      }
+    }
   }
   __syncthreads();
   if (threadIdx.x < fs.n_groups) c.active_count[iter * kMaxGroups + threadIdx.x] = cnt[threadIdx.x];

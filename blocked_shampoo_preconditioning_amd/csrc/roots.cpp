@@ -35,9 +35,11 @@ shp::GemmProblem sym_problem(const float* P, const float* Q, float* C, int64_t s
 }
 
 // C = alpha P Q + beta D + gamma I over every factor; groups of one side and
-// tile stored back to back share a problem.
+// tile stored back to back share a problem. coef_slot >= 0: the epilogue
+// coefficients come per factor from that slot of the scale-mode-3 records.
 void factor_problems(const RootJob& j, SymLaunches& L, const float* P, const float* Q, float* C,
-                     const float* D, float alpha, float beta, float gamma, bool resid) {
+                     const float* D, float alpha, float beta, float gamma, bool resid,
+                     int coef_slot = -1) {
   const shp::FactorSet& fs = j.fs;
   for (int g = 0; g < fs.n_groups;) {
     int e = g + 1;
@@ -57,6 +59,10 @@ void factor_problems(const RootJob& j, SymLaunches& L, const float* P, const flo
     }
     q.status = j.c.status;
     q.f0 = g * fs.B;
+    if (coef_slot >= 0 && j.c.coef != nullptr) {
+      q.coef = j.c.coef + coef_slot;
+      q.coef_stride = shp::kCoefRecord;
+    }
     if (resid) {
       q.resid = j.c.resid;
       q.resid_stride = j.c.resid_stride;
@@ -88,8 +94,9 @@ double norm_bytes(const RootJob& j) {
   return b;
 }
 
-// Coupled Newton for A^(-1/p), p in {4, 6, 8}: T = ((p + 1) I - M) / p enters
-// through the affine epilogues
+// Coupled Newton for A^(-1/p), p in {4, 6, 8} (scale mode 3: M scaled by a
+// per-factor mu each iteration, X by mu^(1/p), folded into the same
+// epilogues): T = ((p + 1) I - M) / p enters through the affine epilogues
 //   T T = (M M - 2 (p + 1) M + (p + 1)^2 I) / p^2,   X T = ((p + 1) X - X M) / p,
 // then T^p by squaring (T^6 = T^4 T^2, T^8 = T^4 T^4) and M <- T^p M.
 // Buffers: M in s[iM], T^2 in s[iT], T^4 in s[2], T^6 / T^8 in s[3]; the new M
@@ -115,16 +122,22 @@ int newton(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
     float* T4 = j.s[2];
     float* Xcur = (k % 2 == 0) ? j.xroot : j.xalt;
     float* Xnext = (k % 2 == 0) ? j.xalt : j.xroot;
+    // scale mode 3: per-factor coefficients of the scaled iteration (the
+    // check kernel writes the next iteration's)
+    const bool sc = c.scale_mode == 3 && c.coef != nullptr;
     SymLaunches l1, l2, l3, l4;
-    factor_problems(j, l1, M, M, T2, M, a2, b2, g2, false);                      // T^2
-    if (k > 0) factor_problems(j, l1, Xcur, M, Xnext, Xcur, xa, xb, 0.f, false);  // X T
+    factor_problems(j, l1, M, M, T2, M, a2, b2, g2, false, sc ? shp::kCoefT2 : -1);  // T^2
+    if (k > 0)
+      factor_problems(j, l1, Xcur, M, Xnext, Xcur, xa, xb, 0.f, false,
+                      sc ? shp::kCoefXT : -1);                                  // X T
     factor_problems(j, l2, T2, T2, T4, nullptr, 1.f, 0.f, 0.f, false);            // T^4
     const float* Tp = T4;
     if (c.p == 6 || c.p == 8) {
       factor_problems(j, l3, T4, c.p == 6 ? T2 : T4, j.s[3], nullptr, 1.f, 0.f, 0.f, false);
       Tp = j.s[3];
     }
-    factor_problems(j, l4, Tp, M, T2, nullptr, 1.f, 0.f, 0.f, true);  // M <- T^p M
+    factor_problems(j, l4, Tp, M, T2, nullptr, 1.f, 0.f, 0.f, true,
+                    sc ? shp::kCoefM : -1);  // M <- T^p (mu M)
     if ((rc = launch_all(h, l1, 0.0, s))) return rc;
     if ((rc = launch_all(h, l2, 0.0, s))) return rc;
     if ((rc = launch_all(h, l3, 0.0, s))) return rc;

@@ -63,8 +63,8 @@ int validate_config(const shampoo_config_t* c, bool tensor) {
     return fail(SHAMPOO_ERR_INVALID_ARG, "newton_max_iters must be in 1..64");
   if (!std::isfinite(c->newton_tol))
     return fail(SHAMPOO_ERR_INVALID_ARG, "newton_tol must be finite");
-  if (c->newton_scale_mode < 0 || c->newton_scale_mode > 2)
-    return fail(SHAMPOO_ERR_UNSUPPORTED, "newton_scale_mode must be 0, 1 or 2");
+  if (c->newton_scale_mode < 0 || c->newton_scale_mode > 3)
+    return fail(SHAMPOO_ERR_UNSUPPORTED, "newton_scale_mode must be 0, 1, 2 or 3");
   if (c->root_method != shp::kCoupledNewton && c->root_method != shp::kNewtonDB &&
       c->root_method != shp::kChebyshev)
     return fail(SHAMPOO_ERR_UNSUPPORTED,
@@ -121,6 +121,8 @@ Plan make_plan(const shampoo_config_t* c, const shampoo_matrix_desc_t* m, int32_
   p.off_scale = take(2 * p.B * 4);
   p.off_rprev = take(2 * p.B * 4);
   p.off_cfac = take(2 * p.B * 4);
+  p.off_lo = take(2 * p.B * 4);
+  p.off_coef = take(2 * p.B * shp::kCoefRecord * 4);
   p.off_active = take((int64_t)(p.max_iters + 1) * shp::kMaxGroups * 4);
   p.off_flops = take(8);
   p.off_cheb = c->root_method == shp::kChebyshev
@@ -206,6 +208,8 @@ shp::NewtonCtl m_ctl(const shampoo_ctx* h) {
   c.max_iters = cfg.newton_max_iters;
   c.scale_mode = cfg.newton_scale_mode;
   c.p = 4;
+  c.lo = h->at<float>(plan.off_lo);
+  c.coef = h->at<float>(plan.off_coef);
   return c;
 }
 
@@ -407,7 +411,7 @@ int shampoo_config_default(shampoo_config_t* cfg) {
   cfg->root_every = 10;
   cfg->newton_max_iters = 25;
   cfg->newton_tol = 1e-6;
-  cfg->newton_scale_mode = 2;
+  cfg->newton_scale_mode = 3;
   cfg->param_dtype = SHAMPOO_F32;
   cfg->grad_dtype = SHAMPOO_F32;
   cfg->momentum = 0.0;

@@ -50,8 +50,8 @@ struct Plan {
   int ntiles_l = 0, ntiles_r = 0, resid_stride = 0;
   int64_t fl = 0, fr = 0;  // elements of all left / right factors
   int64_t off_blocks, off_mats, off_umats, off_nreal, off_status, off_final, off_scale, off_rprev,
-      off_cfac, off_active, off_flops, off_resid, off_gp, off_mom, off_lr, off_xroot, off_xalt,
-      off_s0, off_s1, off_s2, off_cheb, total;
+      off_cfac, off_lo, off_coef, off_active, off_flops, off_resid, off_gp, off_mom, off_lr,
+      off_xroot, off_xalt, off_s0, off_s1, off_s2, off_cheb, total;
   bool momentum = false;
 };
 

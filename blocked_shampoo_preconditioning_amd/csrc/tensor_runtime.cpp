@@ -54,7 +54,8 @@ struct TensorState {
   double real_cube = 0.0;                 // sum of n^2 (n + 1) over the large factors (real n)
   double stat_flops = 0.0, apply_flops = 0.0, real_elems = 0.0;
   int64_t off_blocks, off_meta, off_umeta, off_nreal, off_status, off_final, off_scale, off_rprev,
-      off_cfac, off_active, off_flops, off_cheb, off_resid, off_partial, off_gp, off_mom, off_ap0,
+      off_cfac, off_lo, off_coef, off_active, off_flops, off_cheb, off_resid, off_partial, off_gp,
+      off_mom, off_ap0,
       off_ap1, off_stats, off_xroot, off_xalt, off_s[4], total;
 };
 
@@ -207,6 +208,8 @@ int make_tensor_plan(const shampoo_config_t* cfg, int32_t order, const int32_t* 
   ts.off_scale = c.take(nf * 4);
   ts.off_rprev = c.take(nf * 4);
   ts.off_cfac = c.take(nf * 4);
+  ts.off_lo = c.take(nf * 4);
+  ts.off_coef = c.take(nf * shp::kCoefRecord * 4);
   ts.off_active = c.take((int64_t)(cfg->newton_max_iters + 1) * shp::kMaxGroups * 4);
   ts.off_flops = c.take(8);
   ts.off_cheb = cfg->root_method == shp::kChebyshev && ts.nbig
@@ -376,6 +379,8 @@ shp::NewtonCtl tensor_ctl(const shampoo_ctx* h) {
   c.max_iters = cfg.newton_max_iters;
   c.scale_mode = cfg.newton_scale_mode;
   c.p = ts.p;
+  c.lo = h->at<float>(ts.off_lo);
+  c.coef = h->at<float>(ts.off_coef);
   return c;
 }
 

@@ -304,7 +304,7 @@ class Shampoo:
 
     def __init__(self, shapes, block_rows=1024, block_cols=1024, beta2=0.999, eps=1e-6, lr=1e-3,
                  root_every=10, stat_scale=None, newton_max_iters=25, newton_tol=1e-6,
-                 newton_scale_mode=2, dtype="f32", device="cuda", lds=None, momentum=0.0,
+                 newton_scale_mode=3, dtype="f32", device="cuda", lds=None, momentum=0.0,
                  root_method="newton", cheb_degree=128):
         import torch
         self.torch = torch
@@ -427,7 +427,7 @@ class TensorShampoo(Shampoo):
     dimension."""
 
     def __init__(self, shapes, block_dims, beta2=0.999, eps=1e-6, lr=1e-3, root_every=10,
-                 stat_scale=None, newton_max_iters=25, newton_tol=1e-6, newton_scale_mode=2,
+                 stat_scale=None, newton_max_iters=25, newton_tol=1e-6, newton_scale_mode=3,
                  dtype="f32", device="cuda", strides=None, momentum=0.0, root_method="newton",
                  cheb_degree=128):
         import torch

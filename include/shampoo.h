@@ -96,7 +96,20 @@ typedef struct {
                                         v_0 = 1/sqrt(n) (lam <= lam_max, so the
                                         spectrum of A/s is in (0, ~2.2] unless v_0
                                         is almost orthogonal to the top
-                                        eigenvector); lam = 0 falls back to 1     */
+                                        eigenvector); lam = 0 falls back to 1;
+                                     3: mode 2's s, then the coupled Newton
+                                        iteration scales itself every step: from
+                                        the second iteration on M is scaled by
+                                        mu in [1, 0.9 (p + 1)] (X by mu^(1/p))
+                                        chosen to balance the scalar map at a
+                                        tracked estimate of the spectrum's bottom
+                                        (started from Rayleigh quotients, never
+                                        below the smallest eigenvalue), until the
+                                        estimate passes 0.75; residual stall and
+                                        divergence tests apply to unscaled
+                                        iterates only. Same limit, fewer
+                                        iterations on ill-conditioned factors.
+                                        Newton-DB treats 3 as 2               */
   int32_t param_dtype;            /* shampoo_dtype_t of the parameters           */
   int32_t grad_dtype;             /* shampoo_dtype_t of the gradients            */
   double momentum;                /* alpha of ordinary momentum folded in before
@@ -158,7 +171,7 @@ typedef struct shampoo_ctx* shampoo_t;
 
 /* Fill *cfg with the defaults: square blocks of 1024, beta2 0.999,
  * stat_scale 1 - beta2, eps 1e-6, lr 1e-3, root_every 10, 25 Newton
- * iterations at most, tol 1e-6, scale mode 2, fp32 parameters and gradients,
+ * iterations at most, tol 1e-6, scale mode 3, fp32 parameters and gradients,
  * no momentum, coupled Newton roots (Chebyshev degree 128 if selected). */
 int shampoo_config_default(shampoo_config_t* cfg);
 

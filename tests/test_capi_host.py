@@ -30,7 +30,7 @@ def test_config_default(lib):
     assert (c.block_rows, c.block_cols) == (1024, 1024)
     assert c.beta2 == pytest.approx(0.999) and c.eps == pytest.approx(1e-6)
     assert c.lr == pytest.approx(1e-3) and c.root_every == 10 and c.stat_scale < 0
-    assert c.newton_max_iters == 25 and c.newton_scale_mode == 2 and c.momentum == 0.0
+    assert c.newton_max_iters == 25 and c.newton_scale_mode == 3 and c.momentum == 0.0
     assert c.root_method == 0 and c.cheb_degree == 128
     assert lib.shampoo_config_default(None) == S.SHAMPOO_ERR_INVALID_ARG
 
@@ -70,7 +70,7 @@ def test_workspace_size_grows_with_blocks(lib):
     ("root_every", -1, S.SHAMPOO_ERR_INVALID_ARG),
     ("newton_max_iters", 0, S.SHAMPOO_ERR_INVALID_ARG),
     ("newton_max_iters", 65, S.SHAMPOO_ERR_INVALID_ARG),
-    ("newton_scale_mode", 3, S.SHAMPOO_ERR_UNSUPPORTED),
+    ("newton_scale_mode", 4, S.SHAMPOO_ERR_UNSUPPORTED),
     ("param_dtype", 7, S.SHAMPOO_ERR_UNSUPPORTED),
     ("momentum", 1.0, S.SHAMPOO_ERR_INVALID_ARG),
     ("root_method", 3, S.SHAMPOO_ERR_UNSUPPORTED),

@@ -241,7 +241,7 @@ def test_nan_gradient_block_is_flagged_and_contained():
 # ---------------------------------------------------------------------------
 # Norm scaling and the fixed-iteration bf16 workload
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
 def test_newton_scale_matches_oracle(mode):
     """The per-factor scale s of the norms kernel against the oracle's
     definition evaluated on the oracle's statistics (real extents, tails)."""
@@ -417,4 +417,63 @@ def test_chebyshev_decoder_1b_against_eigh():
     for r in recs:
         assert r.stats_err <= STATS_TOL, r
         assert r.update_err <= UPDATE_TOL, r
+    sh.close()
+
+
+# ---------------------------------------------------------------------------
+# Scale mode 3: the coupled Newton iteration scaling itself every step
+# ---------------------------------------------------------------------------
+def test_scaled_newton_small_ragged_every_block():
+    """Ragged multi-tile set, roots every 3 steps, every block compared at
+    every step against the eigh oracle; iteration counts close to the fp64
+    run of the same scaled iteration."""
+    from oracle import inverse_root_coupled_newton
+    w = workload("gpt_small_b256", shapes=((300, 520), (256, 256), (130, 71), (512, 96)),
+                 root_every=3, steps=7, seed=77, newton_scale_mode=3)
+    recs, sh, orc, params, W = run_parity(w, 7)
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    st, it, _ = sh.newton_info()
+    st, it = st.cpu().numpy(), it.cpu().numpy()
+    assert set(st.tolist()) <= {1, 2}, st
+    B = sh.n_blocks
+    for i in range(B):
+        for f, A in ((i, orc.state[i].L), (B + i, orc.state[i].R)):
+            _, info = inverse_root_coupled_newton(A, 4, 25, 1e-6, 3)
+            assert abs(int(it[f]) - info.iters) <= 2, (f, int(it[f]), info.iters)
+    sh.close()
+
+
+def test_scaled_newton_decoder_1b_sampled():
+    """The 1B-class set with scale mode 3: parity against eigh on sampled
+    blocks for 12 steps (refreshes at t = 1 and 11) and fewer iterations
+    than mode 2 on the column-scaled right factors."""
+    w = workload("decoder_1b_b1024_f32", newton_scale_mode=3)
+    ids = sample_blocks(w, 6, seed=2)
+    recs, sh, orc, params, W = run_parity(w, 12, ids=ids, compare=lambda t: t in (1, 2, 10, 11, 12))
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    st, it, _ = sh.newton_info()
+    st, it = st.cpu().numpy(), it.cpu().numpy()
+    B = sh.n_blocks
+    log(f"  mode 3 status {np.bincount(st, minlength=5).tolist()} left iters "
+        f"{np.bincount(it[:B]).tolist()} right iters {np.bincount(it[B:]).tolist()}")
+    assert set(st.tolist()) <= {1, 2}
+    assert it[B:].mean() <= 9.0  # mode 2 takes 11 on these factors
+    sh.close()
+
+
+def test_scaled_newton_lowrank_illconditioned():
+    w = workload("gpt_small_b512_lowrank", newton_scale_mode=3)
+    ids = sample_blocks(w, 9, seed=3)
+    recs, sh, orc, params, W = run_parity(w, 12, ids=ids)
+    Xl, Xr = sh.roots()
+    assert torch.isfinite(Xl).all() and torch.isfinite(Xr).all()
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+    for r in recs[10:]:
+        assert r.update_err <= UPDATE_TOL, r
+    assert sh.n_diverged() == 0
     sh.close()

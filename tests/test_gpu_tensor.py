@@ -173,6 +173,17 @@ def test_tensor_momentum_and_bf16(case):
     sh.close()
 
 
+def test_tensor_scaled_newton():
+    """Scale mode 3 at p = 8 (order 4) and p = 6 (order 3)."""
+    for case in ("conv4_64x32", "order3_mixed"):
+        w = dataclasses.replace(CASES[case], newton_scale_mode=3)
+        log(f"tensor scaled newton {case}")
+        s, u, wp, sh, _ = run_tensor_parity(w, 3)
+        assert s <= STATS_TOL and u <= UPDATE_TOL and wp <= UPDATE_TOL, (s, u, wp)
+        assert sh.n_diverged() == 0
+        sh.close()
+
+
 def test_tensor_chebyshev():
     w = dataclasses.replace(CASES["conv4_64x32"], root_method="chebyshev")
     log("tensor chebyshev")
