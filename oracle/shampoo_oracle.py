@@ -60,6 +60,7 @@ __all__ = [
     "newton_balance",
     "spectrum_floor_estimate",
     "SCALED_PHASE_END",
+    "final_step_bound",
     "inverse_root_coupled_newton",
     "db_scale",
     "sqrt_pair_db",
@@ -284,9 +285,27 @@ class NewtonInfo:
     residuals: list = field(default_factory=list)
     status: str = "capped"  # converged | stalled | diverged | capped
     mus: list = field(default_factory=list)  # scale of M at every iteration (1 unless mode 3)
+    last_x_only: bool = False  # the last iteration formed only X (final_step_bound met tol)
 
 
 FLOOR_GUARD = 1e-3  # a residual that grows from below this is at the rounding floor
+
+
+# Residual below which rounding, not the iteration, sets ||M - I||_F / sqrt(n)
+# (twice the unit roundoff of the precision computed in): a tolerance under it
+# is not attainable, and the final-step bound is not trusted there.
+ROUNDING_FLOOR = 2.0 * float(np.finfo(np.float64).eps)
+
+
+def final_step_bound(r, n, p):
+    """Bound on the residual after one more unscaled iteration from an
+    iterate with residual r = ||M - I||_F / sqrt(n). Near the fixed point the
+    scalar map sends 1 + e to 1 - C e^2 + O(e^3), C = (p + 1) / (2 p), and
+    sum e^4 <= (sum e^2)^2, so the new residual is at most C sqrt(n) r^2 (to
+    leading order). When this is already below tol the last iteration needs
+    only X <- X T: M would be formed only to be checked. (A reading: the stop
+    rule's tolerance is met by the bound instead of by a formed residual.)"""
+    return (p + 1) / (2.0 * p) * math.sqrt(n) * r * r
 
 
 def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
@@ -349,9 +368,20 @@ def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
         if tol > 0.0 and r <= tol:
             info.status = "converged"
             break
+        mu_next = 1.0
         if scaled:
-            mu = newton_balance(a, p) if a < SCALED_PHASE_END else 1.0
-            a = newton_map(a, p, mu)
+            mu_next = newton_balance(a, p) if a < SCALED_PHASE_END else 1.0
+            a = newton_map(a, p, mu_next)
+        if (tol > 0.0 and mu == 1.0 and mu_next == 1.0 and k + 1 < max_iters
+                and max(final_step_bound(r, n, p), ROUNDING_FLOOR) <= tol):
+            # the next iterate is certain to meet tol: form only its X
+            X = X @ (((p + 1) * eye - M) / p)
+            info.iters = k + 2
+            info.residuals.append(final_step_bound(r, n, p))
+            info.status = "converged"
+            info.last_x_only = True
+            break
+        mu = mu_next
     return X, info
 
 

@@ -636,3 +636,19 @@ def test_spectrum_floor_estimate_bounds():
         assert lam[0] - 1e-12 <= e <= np.diag(A).min() + 1e-12
     D = np.diag(np.linspace(2.0, 0.5, 9))
     assert spectrum_floor_estimate(D, 2.0) == 0.5
+
+
+@pytest.mark.parametrize("mode", [2, 3])
+def test_final_step_forms_only_x(mode):
+    """When the final-step bound already meets tol, the last iteration forms
+    only X: the result still meets the bound against the true root (the
+    root's relative error is about r / p), and it takes no more iterations
+    than the residual test would."""
+    for cond in (1e2, 1e4):
+        A = _rotated(64, cond, 11)
+        X, info = inverse_root_coupled_newton(A, 4, 40, 1e-9, scale_mode=mode)
+        assert info.status == "converged" and info.last_x_only
+        assert rel(X, inverse_root_eigh(A)) < 1e-9
+        M = np.linalg.matrix_power(X, 4) @ A  # the residual of the kept X, formed here
+        # (formed again here, so up to the rounding of X^4 A itself)
+        assert np.linalg.norm(M - np.eye(64)) / 8.0 <= info.residuals[-1] * 1.01 + 1e-11
