@@ -45,9 +45,11 @@ struct GemmProblem {
   // coef[(f0 + i) * coef_stride + 0..3]
   const float* coef;
   int32_t coef_stride;
-  // factors with status[f0 + i] != 0 are skipped (Newton early exit)
+  // factors with status[f0 + i] != 0 are skipped (Newton early exit), except
+  // those whose status equals also_status (when non-zero)
   const int32_t* status;
   int32_t f0;
+  int32_t also_status;
   // residual partials: resid[(f0 + i) * resid_stride + tile] = sum (C - I)^2
   float* resid;
   int32_t resid_stride;
@@ -97,6 +99,13 @@ enum RootSolver { kCoupledNewton = 0, kNewtonDB = 1, kChebyshev = 2 };
 
 // A residual that grows from below this value is the fp32 floor, not divergence.
 constexpr float kFloorGuard = 1e-3f;
+
+// Per-factor status of the root iterations: 0 running, 1 converged, 2 stalled,
+// 3 diverged, 4 capped, 5 converged once the next iteration has formed X
+// (the final-step bound met tol; that iteration runs only the X T product).
+constexpr int kStatusFinalX = 5;
+// Residual level below which fp32 rounding, not the iteration, decides.
+constexpr float kRoundingFloor = 2.f * 1.1920929e-7f;
 
 struct NewtonCtl {
   int32_t solver;       // RootSolver

@@ -276,7 +276,10 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const int tile = idx - j * ntile;
   const int f = j * 8 + xcd;
   if (f >= pb.batch) return;
-  if (pb.status != nullptr && pb.status[pb.f0 + f] != 0) return;
+  if (pb.status != nullptr) {
+    const int st = pb.status[pb.f0 + f];
+    if (st != 0 && !(pb.also_status != 0 && st == pb.also_status)) return;
+  }
   int t = tile, ti = 0;
   while (t >= T - ti) {
     t -= T - ti;
@@ -837,17 +840,26 @@ __global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, Newton
                                                             int prod_after) {
   __shared__ int cnt[kMaxGroups];
   __shared__ int cnt_out[kMaxGroups];
+  __shared__ int cnt_x[kMaxGroups];
   if (threadIdx.x < kMaxGroups) {
     cnt[threadIdx.x] = 0;
     cnt_out[threadIdx.x] = 0;
+    cnt_x[threadIdx.x] = 0;
   }
   __syncthreads();
   const int cur = iter + shift;  // the iterate whose residual was just formed
   const int nf = fs.count();
   const bool scaled = c.scale_mode == 3 && c.solver == kCoupledNewton && c.coef != nullptr;
   for (int f = threadIdx.x; f < nf; f += blockDim.x) {
-    if (c.status[f] != 0) continue;
     const int g = f / fs.B;
+    if (c.status[f] == kStatusFinalX) {
+      // the iteration just run formed only this factor's X: it is the result
+      c.status[f] = 1;
+      c.final_iter[f] = cur;
+      atomicAdd(&cnt_x[g], 1);
+      continue;
+    }
+    if (c.status[f] != 0) continue;
     atomicAdd(&cnt[g], 1);
     const int nt = c.ntiles[g];
     const float* p = c.resid + (size_t)f * c.resid_stride;
@@ -885,16 +897,29 @@ __global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, Newton
     // a rejected iterate leaves final_iter at the previous (accepted) one
     c.status[f] = st;
     if (st == 0) {
-      atomicAdd(&cnt_out[g], 1);
+      double mun = 1.0;
       if (scaled) {
         // the next scale balances the scalar map at the tracked estimate of the
         // spectrum's bottom; the estimate follows the map
         const double a = c.lo[f];
-        const double mun = a < kScaledPhaseEnd ? newton_balance(a, c.p) : 1.0;
+        mun = a < kScaledPhaseEnd ? newton_balance(a, c.p) : 1.0;
         c.lo[f] = (float)newton_map(a, c.p, mun);
         write_newton_coefs(rec, mun, c.p);
         rec[kCoefPrevMu] = mu;
       }
+      // Coupled Newton near the fixed point: the next residual is at most
+      // C sqrt(n) r^2, C = (p + 1) / (2 p). When that already meets tol, the
+      // next iteration forms only X (its M would be formed only to be checked).
+      if (shift == 1 && c.tol > 0.f && mu == 1.f && mun == 1.0 && cur < c.max_iters) {
+        const float bound = (float)((c.p + 1) / (2.0 * c.p) * sqrt((double)fs.nreal[f]) *
+                                    (double)r * r);
+        if (fmaxf(bound, kRoundingFloor) <= c.tol) {
+          st = kStatusFinalX;
+          c.status[f] = st;
+          c.rprev[f] = bound;
+        }
+      }
+      atomicAdd(&cnt_out[g], 1);
     }
   }
   __syncthreads();
@@ -903,7 +928,9 @@ __global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, Newton
     double fl = 0.0;
     for (int g = 0; g < fs.n_groups; ++g) {
       const double n = fs.side[g];
-      fl += (prod_before * (double)cnt[g] + prod_after * (double)cnt_out[g]) * n * n * (n + 1.0);
+      // factors that finished with an X-only iteration ran one product in it
+      fl += (prod_before * (double)cnt[g] + prod_after * (double)cnt_out[g] + (double)cnt_x[g]) *
+            n * n * (n + 1.0);
     }
     c.flops_acc[0] += fl;
   }

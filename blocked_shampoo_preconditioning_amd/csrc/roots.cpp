@@ -39,7 +39,7 @@ shp::GemmProblem sym_problem(const float* P, const float* Q, float* C, int64_t s
 // coefficients come per factor from that slot of the scale-mode-3 records.
 void factor_problems(const RootJob& j, SymLaunches& L, const float* P, const float* Q, float* C,
                      const float* D, float alpha, float beta, float gamma, bool resid,
-                     int coef_slot = -1) {
+                     int coef_slot = -1, int also_status = 0) {
   const shp::FactorSet& fs = j.fs;
   for (int g = 0; g < fs.n_groups;) {
     int e = g + 1;
@@ -59,6 +59,7 @@ void factor_problems(const RootJob& j, SymLaunches& L, const float* P, const flo
     }
     q.status = j.c.status;
     q.f0 = g * fs.B;
+    q.also_status = also_status;
     if (coef_slot >= 0 && j.c.coef != nullptr) {
       q.coef = j.c.coef + coef_slot;
       q.coef_stride = shp::kCoefRecord;
@@ -127,9 +128,11 @@ int newton(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
     const bool sc = c.scale_mode == 3 && c.coef != nullptr;
     SymLaunches l1, l2, l3, l4;
     factor_problems(j, l1, M, M, T2, M, a2, b2, g2, false, sc ? shp::kCoefT2 : -1);  // T^2
+    // X T runs also for the factors whose final-step bound met tol: their last
+    // iteration forms only X
     if (k > 0)
       factor_problems(j, l1, Xcur, M, Xnext, Xcur, xa, xb, 0.f, false,
-                      sc ? shp::kCoefXT : -1);                                  // X T
+                      sc ? shp::kCoefXT : -1, shp::kStatusFinalX);              // X T
     factor_problems(j, l2, T2, T2, T4, nullptr, 1.f, 0.f, 0.f, false);            // T^4
     const float* Tp = T4;
     if (c.p == 6 || c.p == 8) {
