@@ -660,8 +660,15 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   __shared__ double red[4];
   __shared__ double red_inf[4];
   __shared__ double red_min[4];
-  __shared__ float v[kMaxSide];
-  __shared__ float w[kMaxSide];
+  // four vectors of the largest side (dynamic LDS, sized at launch): the top
+  // power iteration's vector and product, the bottom one's (scale mode 3)
+  extern __shared__ float4 vecs4[];  // float4: 16-byte aligned for the vector loads
+  float* vecs = reinterpret_cast<float*>(vecs4);
+  const int ms = (fs.max_side() + 3) & ~3;
+  float* v = vecs;
+  float* w = vecs + ms;
+  float* u = vecs + 2 * ms;
+  float* wu = vecs + 3 * ms;
   const int f = blockIdx.x;
   int n;
   const float* Af = factor_ptr(A, fs, f, n);
@@ -672,33 +679,40 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   const bool cheb = c.solver == kChebyshev;
   const bool power = c.scale_mode >= 2 || cheb;
   const bool scaled = c.scale_mode == 3 && c.solver == kCoupledNewton;
-  // pass 1: squares, absolute row sums, w = A 1 (row sums) and the smallest
-  // diagonal entry
+  const float inv0 = (float)(1.0 / sqrt((double)nr));
+  // pass 1: squares, absolute row sums, w = A 1 (row sums), the smallest
+  // diagonal entry and (mode 3) wu = A u_0 with u_0 = (1, -1, 1, ...) / sqrt(n)
   double sq = 0.0, rowmax = 0.0, dmin = INFINITY;
   for (int r = wave; r < nr; r += 4) {
     const float* row = Af + (int64_t)r * n;
     dmin = fmin(dmin, (double)row[r]);
-    double as = 0.0, rs = 0.0;
+    double as = 0.0, rs = 0.0, alt = 0.0;
     for (int j = lane * 4; j < n4; j += 256) {
       const float4 x = *reinterpret_cast<const float4*>(row + j);
       as += fabs((double)x.x) + fabs((double)x.y) + fabs((double)x.z) + fabs((double)x.w);
       rs += (double)x.x + (double)x.y + (double)x.z + (double)x.w;
+      alt += (double)x.x - (double)x.y + (double)x.z - (double)x.w;
       sq += (double)x.x * x.x + (double)x.y * x.y + (double)x.z * x.z + (double)x.w * x.w;
     }
     for (int j = n4 + lane; j < nr; j += 64) {
       const double x = row[j];
       as += fabs(x);
       rs += x;
+      alt += (j & 1) ? -x : x;
       sq += x * x;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       as += __shfl_xor(as, o);
       rs += __shfl_xor(rs, o);
+      alt += __shfl_xor(alt, o);
     }
     rowmax = fmax(rowmax, as);
     if (lane == 0 && power) w[r] = (float)rs;
+    if (lane == 0 && scaled) wu[r] = (float)(alt * inv0);
   }
+  if (scaled)
+    for (int r = threadIdx.x; r < nr; r += 256) u[r] = (r & 1) ? -inv0 : inv0;
   if (lane == 0) {
     red_inf[wave] = rowmax;
     red_min[wave] = dmin;
@@ -709,22 +723,38 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   // spectral target: Newton converges on (0, p + 1), the Denman-Beavers pair on (0, 2)
   const double mode1 = db ? 1.0 : 2.0 / (c.p + 1);
   double s = c.scale_mode == 0 ? fro : bound * mode1;
-  double lam = 0.0;
+  double lam = 0.0, q = INFINITY;
   if (power) {
+    // Top power iteration from v_0 = 1 / sqrt(n); in mode 3 the bottom one
+    // runs beside it on lam_j I - A from u_0 (one pass over A per step serves
+    // both): q_j = u_j^T A u_j, u_(j+1) = normalised lam_j u_j - A u_j.
     for (int it = 0; it < kPowerIters; ++it) {
       if (it > 0) {
-        // w = A v
         for (int r = wave; r < nr; r += 4) {
           const float* row = Af + (int64_t)r * n;
-          float d = 0.f;
+          float d = 0.f, du = 0.f;
           for (int j = lane * 4; j < n4; j += 256) {
             const float4 x = *reinterpret_cast<const float4*>(row + j);
-            d += x.x * v[j] + x.y * v[j + 1] + x.z * v[j + 2] + x.w * v[j + 3];
+            const float4 y = *reinterpret_cast<const float4*>(v + j);
+            d += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+            if (scaled) {
+              const float4 z = *reinterpret_cast<const float4*>(u + j);
+              du += x.x * z.x + x.y * z.y + x.z * z.z + x.w * z.w;
+            }
           }
-          for (int j = n4 + lane; j < nr; j += 64) d += row[j] * v[j];
+          for (int j = n4 + lane; j < nr; j += 64) {
+            d += row[j] * v[j];
+            if (scaled) du += row[j] * u[j];
+          }
 #pragma unroll
-          for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
-          if (lane == 0) w[r] = d;
+          for (int o = 32; o > 0; o >>= 1) {
+            d += __shfl_xor(d, o);
+            du += __shfl_xor(du, o);
+          }
+          if (lane == 0) {
+            w[r] = d;
+            if (scaled) wu[r] = du;
+          }
         }
       }
       __syncthreads();
@@ -733,9 +763,25 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
       // v_0 = 1 / sqrt(nr) is folded in: the first product is the row sum
       nn = block_sum(nn, red) / (it == 0 ? (double)nr : 1.0);
       lam = sqrt(nn);
+      if (scaled) {
+        double qq = 0.0;
+        for (int r = threadIdx.x; r < nr; r += 256) qq += (double)u[r] * wu[r];
+        q = block_sum(qq, red);
+        double nu = 0.0;
+        for (int r = threadIdx.x; r < nr; r += 256) {
+          const float y = (float)(lam * u[r] - wu[r]);
+          wu[r] = y;
+          nu += (double)y * y;
+        }
+        nu = block_sum(nu, red);
+        const float invu = nu > 0.0 ? (float)(1.0 / sqrt(nu)) : 0.f;
+        if (nu > 0.0 && lam > 0.0)
+          for (int r = threadIdx.x; r < nr; r += 256) u[r] = wu[r] * invu;
+      }
       const float inv = lam > 0.0 ? (float)(1.0 / (lam * (it == 0 ? sqrt((double)nr) : 1.0))) : 0.f;
       for (int r = threadIdx.x; r < nr; r += 256) v[r] = w[r] * inv;
       __syncthreads();
+      if (lam == 0.0) break;
     }
     s = lam > 0.0 ? lam * (db ? 1.0 : 0.5) : bound * mode1;
     // Chebyshev needs an upper bound of the spectrum: lam >= 0.55 lam_max
@@ -743,45 +789,9 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
     // holds always
     if (cheb) s = lam > 0.0 ? fmin(lam / 0.55, bound) : bound;
   }
-  double est = fmin(fmin(red_min[0], red_min[1]), fmin(red_min[2], red_min[3]));
-  if (scaled && lam > 0.0) {
-    // bottom of the spectrum: power iteration on lam I - A from the
-    // alternating vector, then the Rayleigh quotient v^T A v (never below the
-    // smallest eigenvalue, like every diagonal entry)
-    const float inv0 = (float)(1.0 / sqrt((double)nr));
-    for (int r = threadIdx.x; r < nr; r += 256) v[r] = (r & 1) ? -inv0 : inv0;
-    __syncthreads();
-    for (int it = 0; it <= kPowerIters; ++it) {
-      double rq = 0.0;
-      for (int r = wave; r < nr; r += 4) {
-        const float* row = Af + (int64_t)r * n;
-        float d = 0.f;
-        for (int j = lane * 4; j < n4; j += 256) {
-          const float4 x = *reinterpret_cast<const float4*>(row + j);
-          d += x.x * v[j] + x.y * v[j + 1] + x.z * v[j + 2] + x.w * v[j + 3];
-        }
-        for (int j = n4 + lane; j < nr; j += 64) d += row[j] * v[j];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
-        if (lane == 0) {
-          w[r] = (float)(lam * v[r] - d);
-          rq += (double)v[r] * d;
-        }
-      }
-      rq = block_sum(rq, red);  // v^T A v of the current v
-      if (it == kPowerIters) {
-        est = fmin(est, rq);
-        break;
-      }
-      double nn = 0.0;
-      for (int r = threadIdx.x; r < nr; r += 256) nn += (double)w[r] * w[r];
-      nn = block_sum(nn, red);
-      if (!(nn > 0.0)) break;
-      const float inv = (float)(1.0 / sqrt(nn));
-      for (int r = threadIdx.x; r < nr; r += 256) v[r] = w[r] * inv;
-      __syncthreads();
-    }
-  }
+  // the bottom estimate: both the smallest diagonal entry and q are Rayleigh
+  // quotients, never below the smallest eigenvalue
+  const double est = fmin(fmin(fmin(red_min[0], red_min[1]), fmin(red_min[2], red_min[3])), q);
   if (threadIdx.x == 0) {
     const bool ok = s > 0.0 && isfinite(s) && isfinite(fro);
     c.scale[f] = (float)s;
@@ -1179,7 +1189,9 @@ hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile
 
 hipError_t launch_norms(const float* A, FactorSet fs, NewtonCtl c, hipStream_t s) {
   if (fs.B == 0) return hipSuccess;
-  hipLaunchKernelGGL(norms_kernel, dim3(fs.count()), dim3(256), 0, s, A, fs, c);
+  // sides are multiples of 4 or small, so the vectors stay 16-byte aligned
+  const int ms = (fs.max_side() + 3) & ~3;
+  hipLaunchKernelGGL(norms_kernel, dim3(fs.count()), dim3(256), 4 * ms * sizeof(float), s, A, fs, c);
   return hipGetLastError();
 }
 

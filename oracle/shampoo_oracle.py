@@ -59,6 +59,7 @@ __all__ = [
     "newton_map",
     "newton_balance",
     "spectrum_floor_estimate",
+    "power_pair",
     "SCALED_PHASE_END",
     "final_step_bound",
     "inverse_root_coupled_newton",
@@ -239,22 +240,41 @@ SCALED_PHASE_END = 0.75
 BALANCE_STEPS = 40
 
 
-def spectrum_floor_estimate(A, lam, power_iters=16):
-    """Estimate of the smallest eigenvalue of a symmetric A that is never
-    below it: the smaller of the smallest diagonal entry and the Rayleigh
-    quotient v^T A v after power_iters steps of the power iteration on
-    lam I - A (whose top eigenvector is A's bottom one) from the alternating
-    vector v_0 = (1, -1, 1, ...) / sqrt(n). Both are Rayleigh quotients of A."""
+def power_pair(A, power_iters=16):
+    """Top and bottom power iterations run side by side (one pass over A per
+    step serves both): v_0 = (1, ..., 1) / sqrt(n) for the top, u_0 = (1, -1,
+    1, ...) / sqrt(n) for the bottom; step j forms A v_j and A u_j, takes
+    lam_j = ||A v_j||, v_(j+1) = A v_j / lam_j, the Rayleigh quotient
+    q_j = u_j^T A u_j and u_(j+1) the normalised lam_j u_j - A u_j (a power
+    step on lam_j I - A, whose top eigenvector is A's bottom one). Returns
+    (lam_(P-1), q_(P-1)) for P = power_iters: lam is mode 2's estimate, q a
+    Rayleigh quotient (never below the smallest eigenvalue)."""
     A = np.asarray(A, dtype=np.float64)
     n = A.shape[0]
-    v = np.array([1.0 if i % 2 == 0 else -1.0 for i in range(n)]) / math.sqrt(n)
+    v = np.full(n, 1.0 / math.sqrt(n))
+    u = np.array([1.0 if i % 2 == 0 else -1.0 for i in range(n)]) / math.sqrt(n)
+    lam, q = 0.0, math.inf
     for _ in range(power_iters):
-        w = lam * v - A @ v
+        Av, Au = A @ v, A @ u
+        lam = float(np.sqrt(np.sum(Av * Av)))
+        q = float(u @ Au)
+        if lam == 0.0:
+            break
+        v = Av / lam
+        w = lam * u - Au
         nw = float(np.sqrt(np.sum(w * w)))
         if nw == 0.0:
             break
-        v = w / nw
-    return min(float(np.min(np.diag(A))), float(v @ (A @ v)))
+        u = w / nw
+    return lam, q
+
+
+def spectrum_floor_estimate(A, power_iters=16):
+    """Estimate of the smallest eigenvalue of a symmetric A that is never
+    below it: the smaller of the smallest diagonal entry and power_pair's
+    Rayleigh quotient (both are Rayleigh quotients of A)."""
+    A = np.asarray(A, dtype=np.float64)
+    return min(float(np.min(np.diag(A))), power_pair(A, power_iters)[1])
 
 
 def newton_map(m, p, mu=1.0):
@@ -340,7 +360,7 @@ def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
         # (b_0 = lam / s = 2, or (p + 1) / 2 when the fallback norm was used)
         lam = _power_lambda(A)
         b0 = 2.0 if lam > 0.0 else (p + 1) / 2.0
-        a = min(newton_map(spectrum_floor_estimate(A, lam) / s, p), newton_map(b0, p))
+        a = min(newton_map(spectrum_floor_estimate(A) / s, p), newton_map(b0, p))
     mu = 1.0
     r_prev = math.inf
     for k in range(max_iters):

@@ -632,10 +632,24 @@ def test_spectrum_floor_estimate_bounds():
     for seed in range(4):
         A = _rotated(64, 10.0 ** (seed + 1), seed)
         lam = np.linalg.eigvalsh(A)
-        e = spectrum_floor_estimate(A, lam[-1])
+        e = spectrum_floor_estimate(A)
         assert lam[0] - 1e-12 <= e <= np.diag(A).min() + 1e-12
     D = np.diag(np.linspace(2.0, 0.5, 9))
-    assert spectrum_floor_estimate(D, 2.0) == 0.5
+    assert spectrum_floor_estimate(D) == 0.5
+
+
+def test_power_pair_top_matches_mode_2_and_bottom_converges():
+    from oracle import power_pair
+    A = _rotated(48, 1e3, 13)
+    lam, q = power_pair(A, 16)
+    assert lam == pytest.approx(2.0 * newton_scale(A, 4, 2), rel=1e-15)  # the same top iteration
+    assert q >= np.linalg.eigvalsh(A)[0]
+    # an isolated bottom eigenvalue: the bottom Rayleigh quotient reaches it
+    rng = np.random.default_rng(17)
+    Q, _ = np.linalg.qr(rng.standard_normal((48, 48)))
+    ev = np.concatenate([np.linspace(1.0, 0.2, 47), [1e-3]])
+    _, qb = power_pair((Q * ev) @ Q.T, 200)
+    assert 1e-3 <= qb <= 1e-3 * (1 + 1e-6)
 
 
 @pytest.mark.parametrize("mode", [2, 3])
