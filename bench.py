@@ -205,11 +205,11 @@ def run_tensor(args, w, torch, S, synth):
     sh.set_timing(False)
     n_div = sh.n_diverged()
     kernels = class_table(tm)
-    # dominant class by kernel time; its roofline against HBM (bytes known)
-    # or the fp32 MFMA peak
+    # dominant class by kernel time; its roofline against the fp32 MFMA peak
+    # (statistics, root products, apply products) or HBM (the others)
     dom = max(tm, key=lambda k: tm[k]["ms"])
     d = tm[dom]
-    if d["bytes"] > 0 and (d["flops"] == 0 or d["bytes"] / max(d["flops"], 1.0) > 0.05):
+    if dom not in ("stats", "newton_gemm", "apply"):
         ach = d["bytes"] / (d["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4)}

@@ -210,7 +210,15 @@ struct TensorGeom {
   int32_t order;
   int32_t b[kMaxOrder];  // packed extent of every dimension
   int32_t E;             // elements of a packed block
+  // division by b[d] as a multiply-high: q = umulhi64(x, magic[d]) with
+  // magic = ceil(2^64 / b) (exact for 32-bit x); 0 when b = 1
+  uint64_t magic[kMaxOrder];
 };
+
+// ceil(2^64 / d) for d >= 2; 0 for d = 1 (division by 1 is skipped).
+inline uint64_t division_magic(uint32_t d) {
+  return d <= 1 ? 0 : ~(uint64_t)0 / d + 1;
+}
 
 // Gp[blk][e] (+ Mom = momentum Mom + Gp) from the tensors.
 hipError_t launch_tensor_pack(const TBlockMeta* blocks, const TensorMeta* tensors, TensorGeom g,

@@ -55,7 +55,16 @@ struct Plan {
   bool momentum = false;
 };
 
-enum { kPack = 0, kStats = 1, kNorms = 2, kNewtonGemm = 3, kNewtonAux = 4, kApply = 5 };
+enum {
+  kPack = 0,
+  kStats = 1,
+  kNorms = 2,
+  kNewtonGemm = 3,
+  kNewtonAux = 4,
+  kApply = 5,
+  kStatsAux = 6,
+  kApplyAux = 7
+};
 
 struct TimedLaunch {
   int cls;

@@ -27,6 +27,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 template <int K>
 struct BlockGeo {
   int b[K], ext[K];
+  uint64_t magic[K];
   int64_t base;        // element offset of the block's origin
   int64_t stride[K];
   __device__ __forceinline__ void load(const TensorGeom& g, const TBlockMeta& bm,
@@ -35,13 +36,16 @@ struct BlockGeo {
 #pragma unroll
     for (int d = 0; d < K; ++d) {
       b[d] = g.b[d];
+      magic[d] = g.magic[d];
       ext[d] = bm.extent[d];
       stride[d] = tm.stride[d];
       base += (int64_t)bm.origin[d] * tm.stride[d];
     }
   }
   // Offset of packed element e from the tensor's start, and whether it lies
-  // inside the block's real extent.
+  // inside the block's real extent. The index divisions are multiply-highs
+  // with the host's magic numbers (a runtime integer division would dominate
+  // this memory-bound kernel).
   __device__ __forceinline__ bool offset(int e, int64_t& off) const {
     off = base;
     bool in = true;
@@ -49,7 +53,7 @@ struct BlockGeo {
     for (int d = K - 1; d >= 0; --d) {
       int i = e;
       if (d > 0) {
-        const int q = e / b[d];
+        const int q = magic[d] == 0 ? e : (int)__umul64hi((uint64_t)(uint32_t)e, magic[d]);
         i = e - q * b[d];
         e = q;
       }

@@ -52,7 +52,9 @@ struct TensorState {
   int64_t foff[shp::kMaxOrder] = {0, 0, 0, 0};  // element offset of dimension i's factors
   int64_t rot_stride = 0;                 // elements per block of the transpose buffer
   double real_cube = 0.0;                 // sum of n^2 (n + 1) over the large factors (real n)
-  double stat_flops = 0.0, apply_flops = 0.0, real_elems = 0.0;
+  double real_elems = 0.0;
+  // algorithmic flops per dimension on real extents: its statistic and its mode product
+  double stat_flops[shp::kMaxOrder] = {0, 0, 0, 0}, apply_flops[shp::kMaxOrder] = {0, 0, 0, 0};
   int64_t off_blocks, off_meta, off_umeta, off_nreal, off_status, off_final, off_scale, off_rprev,
       off_cfac, off_lo, off_coef, off_active, off_flops, off_cheb, off_resid, off_partial, off_gp,
       off_mom, off_ap0,
@@ -175,6 +177,7 @@ int make_tensor_plan(const shampoo_config_t* cfg, int32_t order, const int32_t* 
     if (ts.is_big[i]) {
       ts.stat_tile[i] = occupancy_tile(ts.b[i], ts.B);
       ts.Kp[i] = (K + 15) / 16 * 16;
+
       ts.rotate[i] = !(after == 1 && K == ts.Kp[i]);
       if (ts.rotate[i]) ts.rot_stride = std::max<int64_t>(ts.rot_stride, ts.Kp[i] * ts.b[i]);
       ts.apply_tile[i] = K % 32 == 0 ? pick_tile((int)std::min<int64_t>(K, 1 << 30), ts.b[i]) : 0;
@@ -183,15 +186,16 @@ int make_tensor_plan(const shampoo_config_t* cfg, int32_t order, const int32_t* 
     }
   }
   // algorithmic counts on real extents
-  ts.real_cube = ts.stat_flops = ts.apply_flops = ts.real_elems = 0.0;
+  ts.real_cube = ts.real_elems = 0.0;
+  for (int i = 0; i < shp::kMaxOrder; ++i) ts.stat_flops[i] = ts.apply_flops[i] = 0.0;
   for (const auto& m : ts.blocks) {
     double vol = 1.0;
     for (int i = 0; i < order; ++i) vol *= m.extent[i];
     ts.real_elems += vol;
     for (int i = 0; i < order; ++i) {
       const double e = m.extent[i];
-      ts.stat_flops += e * (e + 1.0) * (vol / e);
-      ts.apply_flops += 2.0 * e * vol;
+      ts.stat_flops[i] += e * (e + 1.0) * (vol / e);
+      ts.apply_flops[i] += 2.0 * e * vol;
       if (ts.is_big[i]) ts.real_cube += e * e * (e + 1.0);
     }
   }
@@ -222,6 +226,7 @@ int make_tensor_plan(const shampoo_config_t* cfg, int32_t order, const int32_t* 
   ts.off_mom = ts.momentum ? c.take(be) : -1;
   ts.off_ap0 = c.take(ts.B * std::max<int64_t>(E, ts.rot_stride) * 4);
   ts.off_ap1 = c.take(be);
+
   ts.off_stats = c.take(ts.fall * 4);
   ts.off_xroot = c.take(ts.fall * 4);
   const bool scratch = ts.nbig > 0;
@@ -238,7 +243,10 @@ const TensorState& T(const shampoo_ctx* h) { return *h->tensor; }
 shp::TensorGeom geom(const TensorState& ts) {
   shp::TensorGeom g{};
   g.order = ts.k;
-  for (int i = 0; i < shp::kMaxOrder; ++i) g.b[i] = i < ts.k ? ts.b[i] : 1;
+  for (int i = 0; i < shp::kMaxOrder; ++i) {
+    g.b[i] = i < ts.k ? ts.b[i] : 1;
+    g.magic[i] = shp::division_magic((uint32_t)g.b[i]);
+  }
   g.E = ts.E;
   return g;
 }
@@ -291,7 +299,6 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
   float* rot = fptr(h, ts.off_ap0);
   float* stats = fptr(h, ts.off_stats);
   int64_t before = 1;
-  bool first = true;
   for (int i = 0; i < ts.k; ++i) {
     const int n = ts.b[i];
     const int64_t K = ts.E / n;
@@ -299,8 +306,7 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
     before *= n;
     const int64_t C = ts.E / before;
     float* H = stats + ts.foff[i];
-    const double fl = first ? ts.stat_flops : 0.0;
-    first = false;
+    const double fl = ts.stat_flops[i];
     int rc;
     if (ts.is_big[i]) {
       const float* op = gp;
@@ -308,7 +314,7 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
       if (ts.rotate[i]) {
         // [b_0..b_i][b_(i+1)..] -> [b_(i+1)..][b_0..b_i]: rows of n along the
         // unfolding's column index, zero rows up to Kp
-        rc = timed(h, kStats, 0.0, 8.0 * ts.B * ts.E, s, [&] {
+        rc = timed(h, kStatsAux, 0.0, 8.0 * ts.B * ts.E, s, [&] {
           return shp::launch_transpose(gp, ts.E, rot, ts.Kp[i] * n, (int32_t)(A * n), (int32_t)C,
                                        (int32_t)ts.B, s);
         });
@@ -334,7 +340,7 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
       rc = timed(h, kStats, fl, 0.0, s,
                  [&] { return shp::launch_gemm_sym(g, ts.stat_tile[i], false, s); });
     } else {
-      rc = timed(h, kStats, fl, 4.0 * ts.B * ts.E, s, [&] {
+      rc = timed(h, kStatsAux, fl, 4.0 * ts.B * ts.E, s, [&] {
         return shp::launch_small_gram(gp, ts.E, (int32_t)A, n, (int32_t)C, (int32_t)ts.B,
                                       fptr(h, ts.off_partial), ts.gram_chunks, H,
                                       (float)h->cfg.beta2, h->stat_scale, s);
@@ -397,12 +403,12 @@ int do_tensor_apply(shampoo_ctx* h, hipStream_t s, float* out) {
     const int64_t R = ts.E / n;
     float* dst = (i == ts.k - 1 && out) ? out : ap[i & 1];
     const float* X = roots + ts.foff[i];
-    const double fl = i == 0 ? ts.apply_flops : 0.0;
+    const double fl = ts.apply_flops[i];
     const double esz = h->cfg.param_dtype == SHAMPOO_BF16 ? 2.0 : 4.0;
     int rc;
     if (i == ts.k - 1 && !out && !ts.is_big[i]) {
       // last product of the chain with the update in its epilogue
-      rc = timed(h, kApply, fl, 4.0 * ts.B * ts.E + 2.0 * esz * ts.real_elems, s, [&] {
+      rc = timed(h, kApplyAux, fl, 4.0 * ts.B * ts.E + 2.0 * esz * ts.real_elems, s, [&] {
         return shp::launch_mode_product_update(
             cur, ts.E, X, (int64_t)n * n, h->at<shp::TBlockMeta>(ts.off_blocks),
             h->at<shp::TensorMeta>(ts.off_meta), geom(ts), (int32_t)R, (int32_t)ts.B,
@@ -430,7 +436,7 @@ int do_tensor_apply(shampoo_ctx* h, hipStream_t s, float* out) {
       rc = timed(h, kApply, fl, 0.0, s,
                  [&] { return shp::launch_gemm_full(g, ts.apply_tile[i], s); });
     } else {
-      rc = timed(h, kApply, fl, 8.0 * ts.B * ts.E, s, [&] {
+      rc = timed(h, kApplyAux, fl, 8.0 * ts.B * ts.E, s, [&] {
         return shp::launch_mode_product(cur, ts.E, X, (int64_t)n * n, dst, ts.E, n, (int32_t)R,
                                         (int32_t)ts.B, s);
       });
@@ -440,7 +446,7 @@ int do_tensor_apply(shampoo_ctx* h, hipStream_t s, float* out) {
   }
   if (out) return SHAMPOO_OK;
   const double esz = h->cfg.param_dtype == SHAMPOO_BF16 ? 2.0 : 4.0;
-  return timed(h, kApply, 0.0, 4.0 * ts.B * ts.E + 2.0 * esz * ts.real_elems, s, [&] {
+  return timed(h, kApplyAux, 0.0, 4.0 * ts.B * ts.E + 2.0 * esz * ts.real_elems, s, [&] {
     return shp::launch_tensor_scatter(h->at<shp::TBlockMeta>(ts.off_blocks),
                                       h->at<shp::TensorMeta>(ts.off_meta), geom(ts), (int32_t)ts.B,
                                       cur, (float)h->cfg.lr, h->cfg.param_dtype == SHAMPOO_BF16, 1,

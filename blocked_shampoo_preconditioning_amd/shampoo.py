@@ -26,7 +26,8 @@ SHAMPOO_F32 = 0
 SHAMPOO_BF16 = 1
 SHAMPOO_FORCE_REFRESH = 1
 SHAMPOO_NO_AUTO_REFRESH = 2
-TIMING_CLASSES = ("pack", "stats", "norms", "newton_gemm", "newton_aux", "apply")
+TIMING_CLASSES = ("pack", "stats", "norms", "newton_gemm", "newton_aux", "apply", "stats_aux",
+                  "apply_aux")
 ROOT_METHODS = {"newton": 0, "newton_db": 1, "chebyshev": 2}
 
 
@@ -52,8 +53,8 @@ class Layout(ctypes.Structure):
 
 
 class Timing(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 6), ("flops", ctypes.c_double * 6),
-                ("bytes", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6)]
+    _fields_ = [("ms", ctypes.c_double * 8), ("flops", ctypes.c_double * 8),
+                ("bytes", ctypes.c_double * 8), ("launches", ctypes.c_int64 * 8)]
 
 
 MAX_ORDER = 4

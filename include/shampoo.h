@@ -156,10 +156,14 @@ typedef struct {
 
 /* Accumulated kernel time per class while timing is enabled (milliseconds,
  * measured with HIP events on the stream the kernels run on) and the
- * algorithmic flop count of the launches timed. Classes: 0 pack, 1
- * statistics, 2 norms, 3 Newton GEMMs, 4 Newton bookkeeping (init, checks,
- * final copy), 5 apply (two-sided product and parameter update). */
-#define SHAMPOO_TIMING_CLASSES 6
+ * algorithmic flop and byte counts of the launches timed. Classes: 0 pack,
+ * 1 statistics (MFMA), 2 norms, 3 root products (MFMA), 4 root bookkeeping
+ * (init, checks, final copy; small-side roots of tensors), 5 apply (MFMA
+ * products and the fused parameter update), 6 memory-bound statistics
+ * kernels of tensor handles (transposed unfoldings, small-side reductions),
+ * 7 memory-bound apply kernels of tensor handles (FMA mode products, update
+ * scatter). */
+#define SHAMPOO_TIMING_CLASSES 8
 typedef struct {
   double ms[SHAMPOO_TIMING_CLASSES];
   double flops[SHAMPOO_TIMING_CLASSES];
