@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 METRIC = "Shampoo optimizer steps/sec + batched GEMM TFLOP/s vs MFMA peak, 1 GPU"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (the statistics of bf16 gradients)
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 DEFAULT_WORKLOAD = "decoder_1b_b1024_f32"
 
@@ -141,14 +142,17 @@ def cpu_baseline_tensor(w, grad_sets, budget_s=15.0, max_blocks=16, seed=0):
     }
 
 
-def class_table(tm):
+def class_table(tm, bf16_stats=False):
     kernels = {}
     for name, d in tm.items():
         entry = {"ms": round(d["ms"], 3), "launches": d["launches"]}
         if d["flops"] > 0 and d["ms"] > 0:
             tf = d["flops"] / (d["ms"] * 1e-3) / 1e12
             entry["tflops"] = round(tf, 2)
-            entry["frac_fp32_mfma"] = round(tf / PEAK_FP32_MFMA_TFLOPS, 4)
+            if name == "stats" and bf16_stats:  # bf16 gradients: bf16 MFMA statistics
+                entry["frac_bf16_mfma"] = round(tf / PEAK_BF16_MFMA_TFLOPS, 4)
+            else:
+                entry["frac_fp32_mfma"] = round(tf / PEAK_FP32_MFMA_TFLOPS, 4)
         if d["bytes"] > 0 and d["ms"] > 0:
             gbs = d["bytes"] / (d["ms"] * 1e-3) / 1e9
             entry["gbs"] = round(gbs, 1)
@@ -361,7 +365,7 @@ def main():
     log(f"timed {args.steps} steps: {elapsed * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms)")
 
     steps_per_s = args.steps / elapsed
-    kernels = class_table(tm)
+    kernels = class_table(tm, bf16_stats=w.dtype == "bf16")
     nw = tm["newton_gemm"]
     achieved = nw["flops"] / (nw["ms"] * 1e-3) / 1e12 if nw["ms"] > 0 else 0.0
     traffic = newton_traffic(w.name)

@@ -53,6 +53,10 @@ struct GemmProblem {
   // residual partials: resid[(f0 + i) * resid_stride + tile] = sum (C - I)^2
   float* resid;
   int32_t resid_stride;
+  // bf16 statistics (launch_gemm_sym_bf16): C = alpha X X^T + beta D with X
+  // [M][K] bf16 row-major (k contiguous), element stride sXh between members
+  const uint16_t* Xh;
+  int64_t sXh;
 };
 
 constexpr int kMaxProblems = 8;
@@ -140,14 +144,20 @@ constexpr int kBalanceSteps = 40;
 
 // ---- launchers (return hipGetLastError()) ----
 // Mom (nullable): momentum buffer [B][br][bc], updated as Mom = momentum * Mom + Gp.
+// GpT (fp32 transpose) or, for bf16 gradients, GpH / GpTH: the packed block and
+// its transpose as bf16 (the gradient's own values), for the bf16 statistics.
 hipError_t launch_pack(const BlockMeta* blocks, const MatMeta* mats, int32_t B, int32_t br, int32_t bc,
                        int32_t grad_bf16, float* Gp, float* GpT, float* Mom, float momentum,
-                       hipStream_t s);
+                       uint16_t* GpH, uint16_t* GpTH, hipStream_t s);
 hipError_t launch_unpack(const BlockMeta* blocks, const MatMeta* dst, int32_t B, int32_t br,
                          int32_t bc, const float* Gp, hipStream_t s);
 hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nelemR, int32_t nr,
                              int32_t B, float eps, hipStream_t s);
 hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, hipStream_t s);
+// Statistics from bf16 operands on the bf16 MFMA (exact products, fp32
+// accumulation): the problems' Xh / sXh, same epilogue as the symmetric
+// product. M and K multiples of the tile and of 32.
+hipError_t launch_gemm_sym_bf16(const GemmLaunch& g, int tile, hipStream_t s);
 hipError_t launch_gemm_full(const GemmLaunch& g, int tile, hipStream_t s);
 hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, hipStream_t s);
 hipError_t launch_norms(const float* A, FactorSet fs, NewtonCtl c, hipStream_t s);

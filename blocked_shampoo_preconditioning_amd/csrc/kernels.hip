@@ -44,7 +44,12 @@ struct Cfg {
   // a pitch of 32 (mod 64) banks keeps them on disjoint banks.
   static constexpr int LDP = BM + ((BM % 64) == 0 ? 32 : 0);
   static constexpr int LDQ = BN + ((BN % 64) == 0 ? 32 : 0);
-  static constexpr int LDS_FLOATS = 2 * BK * (LDP + LDQ);
+  static constexpr int LDS_FP32 = 2 * BK * (LDP + LDQ);
+  // bf16 operands: K-tiles of 32, rows of k contiguous, pitch 40 (16-byte
+  // aligned rows, 32 + 8 so consecutive rows start on different banks)
+  static constexpr int BKH = 32, LDKH = BKH + 8;
+  static constexpr int LDS_BF16 = 2 * (BM + BN) * LDKH / 2;  // in floats
+  static constexpr int LDS_FLOATS = LDS_FP32 > LDS_BF16 ? LDS_FP32 : LDS_BF16;
   static constexpr int PV = BM / 4, QV = BN / 4;           // float4 per operand row
   static constexpr int PPT = BK * PV / NT, QPT = BK * QV / NT;  // float4 per thread
   static_assert(PPT >= 1 && QPT >= 1, "tile too small for the thread count");
@@ -82,6 +87,7 @@ __device__ __forceinline__ void mainloop_w(const float* __restrict__ P, const fl
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
+  static_assert(C::LDS_FP32 <= C::LDS_FLOATS, "LDS");
 
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -162,6 +168,109 @@ __device__ __forceinline__ void mainloop(const float* __restrict__ P, const floa
   mainloop_w<C, MASK>(P, Q, M, N, K, m0, n0, wave % C::WM, wave / C::WM, acc, lds);
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// acc[fm][fn] = sum over K of X[m0 + ...][k] * X[n0 + ...][k] with X [rows][K]
+// bf16 (k contiguous): v_mfma_f32_32x32x16_bf16, lane l supplying
+// A[m = l % 32][k = 8 (l / 32) + 0..7] and B[k = 8 (l / 32) + 0..7][n = l % 32],
+// each a 16-byte read of one LDS row. Double-buffered like mainloop_w.
+template <class C, int MASK = -1>
+__device__ __forceinline__ void mainloop_bf16(const uint16_t* __restrict__ X, int K, int m0, int n0,
+                                              int wm, int wn, floatx16 (&acc)[C::FM][C::FN],
+                                              float* lds) {
+  constexpr int LD = C::LDKH;
+  uint16_t* sA = reinterpret_cast<uint16_t*>(lds);  // [2][BM][LD]
+  uint16_t* sB = sA + 2 * C::BM * LD;                // [2][BN][LD]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // 16-byte chunks of a K-tile: CPR per row, rows x CPR per operand
+  constexpr int CPR = C::BKH / 8;
+  constexpr int CA = C::BM * CPR, CB = C::BN * CPR;
+  static_assert(CA % C::NT == 0 && CB % C::NT == 0, "uneven operand load");
+  constexpr int PA = CA / C::NT, PB = CB / C::NT;
+  u32x4 ra[PA], rb[PB];
+  const int nk = K / C::BKH;
+#pragma unroll
+  for (int i = 0; i < PA; ++i) {
+    const int c = tid + i * C::NT;
+    ra[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(m0 + (c / CPR)) * K + ((c % CPR) * 8));
+  }
+#pragma unroll
+  for (int i = 0; i < PB; ++i) {
+    const int c = tid + i * C::NT;
+    rb[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(n0 + (c / CPR)) * K + ((c % CPR) * 8));
+  }
+#pragma unroll
+  for (int i = 0; i < PA; ++i) {
+    const int c = tid + i * C::NT;
+    *reinterpret_cast<u32x4*>(sA + (c / CPR) * LD + ((c % CPR) * 8)) = ra[i];
+  }
+#pragma unroll
+  for (int i = 0; i < PB; ++i) {
+    const int c = tid + i * C::NT;
+    *reinterpret_cast<u32x4*>(sB + (c / CPR) * LD + ((c % CPR) * 8)) = rb[i];
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int k0 = (kt + 1) * C::BKH;
+#pragma unroll
+      for (int i = 0; i < PA; ++i) {
+        const int c = tid + i * C::NT;
+        ra[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(m0 + (c / CPR)) * K + k0 +
+                                                   ((c % CPR) * 8));
+      }
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        const int c = tid + i * C::NT;
+        rb[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(n0 + (c / CPR)) * K + k0 +
+                                                   ((c % CPR) * 8));
+      }
+    }
+    const uint16_t* a0 = sA + buf * C::BM * LD + (wm * 32 * C::FM + l32) * LD + half * 8;
+    const uint16_t* b0 = sB + buf * C::BN * LD + (wn * 32 * C::FN + l32) * LD + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::BKH; ks += 16) {
+      bf16x8 a[C::FM], b[C::FN];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) a[i] = *reinterpret_cast<const bf16x8*>(a0 + i * 32 * LD + ks);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) b[j] = *reinterpret_cast<const bf16x8*>(b0 + j * 32 * LD + ks);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          if (MASK & (1 << (i * C::FN + j)))
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      uint16_t* dA = sA + (buf ^ 1) * C::BM * LD;
+      uint16_t* dB = sB + (buf ^ 1) * C::BN * LD;
+#pragma unroll
+      for (int i = 0; i < PA; ++i) {
+        const int c = tid + i * C::NT;
+        *reinterpret_cast<u32x4*>(dA + (c / CPR) * LD + ((c % CPR) * 8)) = ra[i];
+      }
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        const int c = tid + i * C::NT;
+        *reinterpret_cast<u32x4*>(dB + (c / CPR) * LD + ((c % CPR) * 8)) = rb[i];
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int FM, int FN>
 constexpr int upper_mask() {
   int m = 0;
@@ -234,6 +343,24 @@ __device__ __forceinline__ void mainloop_sym(const float* __restrict__ P,
     mainloop_w<C, 0>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
 }
 
+template <class C>
+__device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X, int K, int m0,
+                                                  int n0, floatx16 (&acc)[C::FM][C::FN],
+                                                  float* lds, const SymWave<C>& sw) {
+  constexpr int kUpper = upper_mask<C::FM, C::FN>();
+  constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
+  if (sw.mask == -1)
+    mainloop_bf16<C>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else if (sw.mask == kUpper)
+    mainloop_bf16<C, kUpper>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else if (C::FM >= 2 && sw.mask == kTop)
+    mainloop_bf16<C, kTop>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else if (C::FM >= 2 && sw.mask == kBottom)
+    mainloop_bf16<C, kBottom>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else
+    mainloop_bf16<C, 0>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+}
+
 // Row / column of accumulator register r of fragment (i, j) of the wave's
 // block (wm, wn).
 template <class C>
@@ -260,7 +387,7 @@ __device__ __forceinline__ int frag_col(int n0, int j) {
 // is written to its place and mirrored, so the stored result is exactly
 // symmetric. Used by the statistics (EMA epilogue) and the Newton chain.
 // ---------------------------------------------------------------------------
-template <class C>
+template <class C, bool BF16 = false>
 __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   __shared__ float lds[C::LDS_FLOATS];
   float* red = lds;  // residual partials reuse the operand tiles after the K loop
@@ -291,8 +418,11 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const bool diag = (ti == tj);
   const SymWave<C> sw(diag);
   floatx16 acc[C::FM][C::FN];
-  mainloop_sym<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0,
-                  acc, lds, sw);
+  if constexpr (BF16)
+    mainloop_sym_bf16<C>(pb.Xh + (size_t)f * pb.sXh, pb.K, m0, n0, acc, lds, sw);
+  else
+    mainloop_sym<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0,
+                    acc, lds, sw);
 
   // Epilogue: C = alpha acc + beta D + gamma I on and above the diagonal, and
   // the mirror below it. The four registers 4g..4g+3 of a lane hold four
@@ -361,6 +491,13 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
 template <class C>
 __global__ __launch_bounds__(C::NT, 4) void syrk_ema_kernel(GemmLaunch g) {
   sym_product<C>(g);
+}
+
+// Statistics from bf16 packed gradients: L <- beta2 L + g Gp Gp^T reads GpH
+// (rows of Gp), R <- beta2 R + g Gp^T Gp reads GpTH (rows of Gp^T).
+template <class C>
+__global__ __launch_bounds__(C::NT, 4) void syrk_bf16_kernel(GemmLaunch g) {
+  sym_product<C, true>(g);
 }
 
 // One product of the coupled Newton chain (T T, X T, T2 T2 or T4 M).
@@ -474,11 +611,18 @@ __device__ __forceinline__ float load1(const void* base, int64_t off, int bf16) 
   return reinterpret_cast<const float*>(base)[off];
 }
 
+__device__ __forceinline__ uint2 bf16_bits4(float4 v) {
+  // v holds bf16 values widened exactly: their bits are the upper halves
+  return make_uint2((__float_as_uint(v.x) >> 16) | (__float_as_uint(v.y) & 0xffff0000u),
+                    (__float_as_uint(v.z) >> 16) | (__float_as_uint(v.w) & 0xffff0000u));
+}
+
 __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__ blocks,
                                                    const MatMeta* __restrict__ mats, int br, int bc,
                                                    int bf16, float* __restrict__ Gp,
                                                    float* __restrict__ GpT, float* __restrict__ Mom,
-                                                   float momentum) {
+                                                   float momentum, uint16_t* __restrict__ GpH,
+                                                   uint16_t* __restrict__ GpTH) {
   __shared__ float tile[64][65];
   const int b = blockIdx.y;
   const BlockMeta bm = blocks[b];
@@ -509,6 +653,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
     if (pr < br && pc < bc) {
       const size_t o = ((size_t)b * br + pr) * bc + pc;
       *reinterpret_cast<float4*>(Gp + o) = v;
+      if (GpH != nullptr) *reinterpret_cast<uint2*>(GpH + o) = bf16_bits4(v);
       if (Mom != nullptr) {  // momentum folded in before preconditioning
         float4 m = *reinterpret_cast<const float4*>(Mom + o);
         m.x = momentum * m.x + v.x;
@@ -530,7 +675,11 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
     const int r = (tid % 16) * 4;
     if (cc0 + tc < bc && rr0 + r < br) {
       const float4 v = make_float4(tile[r][tc], tile[r + 1][tc], tile[r + 2][tc], tile[r + 3][tc]);
-      *reinterpret_cast<float4*>(GpT + ((size_t)b * bc + cc0 + tc) * br + rr0 + r) = v;
+      const size_t o = ((size_t)b * bc + cc0 + tc) * br + rr0 + r;
+      if (GpTH != nullptr)
+        *reinterpret_cast<uint2*>(GpTH + o) = bf16_bits4(v);
+      else
+        *reinterpret_cast<float4*>(GpT + o) = v;
     }
   }
 }
@@ -1090,11 +1239,11 @@ int grid_full(const GemmLaunch& g) {
 // ---------------------------------------------------------------------------
 hipError_t launch_pack(const BlockMeta* blocks, const MatMeta* mats, int32_t B, int32_t br,
                        int32_t bc, int32_t grad_bf16, float* Gp, float* GpT, float* Mom,
-                       float momentum, hipStream_t s) {
+                       float momentum, uint16_t* GpH, uint16_t* GpTH, hipStream_t s) {
   if (B == 0) return hipSuccess;
   dim3 grid(((br + 63) / 64) * ((bc + 63) / 64), B);
   hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, blocks, mats, br, bc, grad_bf16, Gp, GpT,
-                     Mom, momentum);
+                     Mom, momentum, GpH, GpTH);
   return hipGetLastError();
 }
 
@@ -1133,6 +1282,26 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, hipStream
     SHP_SYM_CASE(64, Cfg64)
     SHP_SYM_CASE(32, Cfg32)
 #undef SHP_SYM_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_sym_bf16(const GemmLaunch& g, int tile, hipStream_t s) {
+  if (g.n_problems == 0) return hipSuccess;
+  switch (tile) {
+#define SHP_SYMH_CASE(T, CFG)                                                                    \
+  case T: {                                                                                      \
+    const int gx = grid_sym<CFG>(g);                                                             \
+    if (gx)                                                                                      \
+      hipLaunchKernelGGL(syrk_bf16_kernel<CFG>, dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g);  \
+    break;                                                                                       \
+  }
+    SHP_SYMH_CASE(128, Cfg128)
+    SHP_SYMH_CASE(64, Cfg64)
+    SHP_SYMH_CASE(32, Cfg32)
+#undef SHP_SYMH_CASE
     default:
       return hipErrorInvalidValue;
   }

@@ -170,6 +170,11 @@ float* m_s(const shampoo_ctx* h, int i) {
   return h->at<float>(i == 0 ? h->plan.off_s0 : i == 1 ? h->plan.off_s1 : h->plan.off_s2);
 }
 float* m_gpT(const shampoo_ctx* h) { return m_s(h, 2); }   // packed transpose lives in Newton scratch
+// bf16 gradients: the packed block and its transpose as bf16 (statistics on the
+// bf16 MFMA), in the same scratch
+bool m_bf16_stats(const shampoo_ctx* h) { return h->cfg.grad_dtype == SHAMPOO_BF16; }
+uint16_t* m_gpH(const shampoo_ctx* h) { return reinterpret_cast<uint16_t*>(m_s(h, 2)); }
+uint16_t* m_gpTH(const shampoo_ctx* h) { return m_gpH(h) + h->plan.B * h->plan.br * h->plan.bc; }
 float* m_tmpT(const shampoo_ctx* h) { return m_s(h, 1); }  // apply intermediate likewise
 
 shp::FactorSet m_factors(const shampoo_ctx* h) {
@@ -267,9 +272,11 @@ int do_pack(shampoo_ctx* h, hipStream_t s) {
   const double esz = h->cfg.grad_dtype == SHAMPOO_BF16 ? 2.0 : 4.0;
   const double bytes = real * esz + (p.momentum ? 4.0 : 2.0) * 4.0 * (double)p.B * p.br * p.bc;
   return timed(h, kPack, 0.0, bytes, s, [&] {
+    const bool hb = m_bf16_stats(h);
     return shp::launch_pack(h->at<shp::BlockMeta>(p.off_blocks), h->at<shp::MatMeta>(p.off_mats),
                             (int32_t)p.B, p.br, p.bc, h->cfg.grad_dtype == SHAMPOO_BF16, m_gp(h),
-                            m_gpT(h), m_mom(h), (float)h->cfg.momentum, s);
+                            hb ? nullptr : m_gpT(h), m_mom(h), (float)h->cfg.momentum,
+                            hb ? m_gpH(h) : nullptr, hb ? m_gpTH(h) : nullptr, s);
   });
 }
 
@@ -307,11 +314,21 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
     g.p[i].sD = g.p[i].sC;
   }
   g.n_problems = 2;
+  const bool hb = m_bf16_stats(h);
+  if (hb) {
+    // bf16 operands, k contiguous: L from the rows of Gp, R from the rows of Gp^T
+    g.p[0].Xh = m_gpH(h);
+    g.p[0].sXh = (int64_t)p.br * p.bc;
+    g.p[1].Xh = m_gpTH(h);
+    g.p[1].sXh = (int64_t)p.br * p.bc;
+  }
   double flops = 0.0;
   for (const auto& b : h->blocks) flops += sym_flops(b.m, b.n) + sym_flops(b.n, b.m);
-  const double bytes = 4.0 * (double)p.B * (2.0 * p.br * p.bc + 2.0 * (double)p.br * p.br +
-                                            2.0 * (double)p.bc * p.bc);
-  return timed(h, kStats, flops, bytes, s, [&] { return shp::launch_gemm_sym(g, p.tile, false, s); });
+  const double bytes = (double)p.B * ((hb ? 2.0 : 4.0) * 2.0 * p.br * p.bc +
+                                      4.0 * (2.0 * (double)p.br * p.br + 2.0 * (double)p.bc * p.bc));
+  return timed(h, kStats, flops, bytes, s, [&] {
+    return hb ? shp::launch_gemm_sym_bf16(g, p.tile, s) : shp::launch_gemm_sym(g, p.tile, false, s);
+  });
 }
 
 // t_stats: the step whose statistics the roots are taken of (for the

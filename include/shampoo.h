@@ -111,7 +111,10 @@ typedef struct {
                                         iterations on ill-conditioned factors.
                                         Newton-DB treats 3 as 2               */
   int32_t param_dtype;            /* shampoo_dtype_t of the parameters           */
-  int32_t grad_dtype;             /* shampoo_dtype_t of the gradients            */
+  int32_t grad_dtype;             /* shampoo_dtype_t of the gradients; with bf16
+                                     gradients the statistics run on the bf16
+                                     MFMA (the products of bf16 values are exact
+                                     in fp32; fp32 accumulation)                */
   double momentum;                /* alpha of ordinary momentum folded in before
                                      preconditioning (podcast cue 28):
                                      m = alpha m + G, W -= lr L^(-1/4) m R^(-1/4);

@@ -477,3 +477,24 @@ def test_scaled_newton_lowrank_illconditioned():
         assert r.update_err <= UPDATE_TOL, r
     assert sh.n_diverged() == 0
     sh.close()
+
+
+# ---------------------------------------------------------------------------
+# bf16 gradients: statistics on the bf16 MFMA (exact products, fp32 sums)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,shapes,block", [
+    ("gpt_small_b256", ((300, 520), (256, 256), (130, 71), (512, 96)), (256, 256)),  # 128 tiles
+    ("gpt_small_b256", ((200, 100), (64, 192)), (64, 64)),                           # 64 tiles
+    ("single_64x32", ((64, 32), (70, 45)), (64, 32)),                                # 32 tiles
+])
+def test_bf16_statistics_every_block(name, shapes, block):
+    """Ragged matrices with bf16 gradients and parameters: every block's
+    statistics (<= 1e-5 against the oracle's fp64 sums of the same bf16
+    values) and update at every step."""
+    w = workload(name, shapes=shapes, block_rows=block[0], block_cols=block[1], dtype="bf16",
+                 root_every=2, steps=5, seed=61)
+    recs, sh, orc, params, W = run_parity(w, 5)
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    sh.close()
