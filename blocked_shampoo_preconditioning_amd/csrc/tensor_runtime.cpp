@@ -301,7 +301,6 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
   int64_t before = 1;
   for (int i = 0; i < ts.k; ++i) {
     const int n = ts.b[i];
-    const int64_t K = ts.E / n;
     const int64_t A = before;
     before *= n;
     const int64_t C = ts.E / before;
@@ -336,7 +335,6 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
       q.alpha = h->stat_scale;
       q.beta = (float)h->cfg.beta2;
       g.n_problems = 1;
-      (void)K;
       rc = timed(h, kStats, fl, 0.0, s,
                  [&] { return shp::launch_gemm_sym(g, ts.stat_tile[i], false, s); });
     } else {

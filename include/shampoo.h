@@ -18,7 +18,11 @@
  * p-th root, p = 4 (Guo and Higham, SIAM J. Matrix Anal. Appl. 28(3), 2006):
  * M = A / s, X = s^(-1/4) I, then repeatedly T = (5 I - M) / 4, X <- X T,
  * M <- T^4 M, until ||M - I||_F / sqrt(n) <= newton_tol, the residual stops
- * decreasing, or newton_max_iters iterations have run.
+ * decreasing, or newton_max_iters iterations have run. By default (scale
+ * mode 3) the iteration also scales M every step to lift its small
+ * eigenvalues faster, and an iteration whose next residual is bounded below
+ * newton_tol forms only X. Newton-DB and Chebyshev roots are selectable
+ * (root_method).
  *
  * Conventions of every entry point:
  *  - Return value: SHAMPOO_OK (0) or one of the SHAMPOO_ERR_* codes below.
@@ -149,7 +153,9 @@ typedef struct {
   int64_t stats;          /* fp32 [B][br][br] then [B][bc][bc]                  */
   int64_t roots;          /* fp32, same layout as stats                         */
   int64_t newton_status;  /* int32 [2B]: per factor, 0 none 1 converged 2 stalled
-                             3 diverged 4 capped (left factors first)            */
+                             3 diverged 4 capped (left factors first); 5 only
+                             while a refresh is in flight (converges after one
+                             more X-only iteration)                               */
   int64_t newton_iters;   /* int32 [2B]: iterations behind the kept root         */
   int64_t newton_scale;   /* fp32 [2B]: the scale s of the last refresh           */
   int64_t newton_residual; /* fp32 [2B]: ||M - I||_F / sqrt(n) of the kept iterate  */
