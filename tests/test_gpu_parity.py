@@ -498,3 +498,17 @@ def test_bf16_statistics_every_block(name, shapes, block):
         assert r.stats_err <= STATS_TOL, r
         assert r.update_err <= UPDATE_TOL, r
     sh.close()
+
+
+def test_largest_block_4096():
+    """The largest block side (4096): one full block and a ragged one, one
+    refresh, statistics and the update against the eigh oracle."""
+    w = workload("gpt_small_b256", shapes=((4096, 4096), (300, 4100)), block_rows=4096,
+                 block_cols=4096, root_every=1, steps=1, grad_std=1e-2, seed=23)
+    recs, sh, orc, params, W = run_parity(w, 1)
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    st, _, _ = sh.newton_info()
+    assert set(st.cpu().tolist()) <= {1, 2}
+    sh.close()

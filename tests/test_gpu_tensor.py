@@ -204,3 +204,32 @@ def test_tensor_workloads_sampled(name):
     assert s <= STATS_TOL and u <= UPDATE_TOL and wp <= UPDATE_TOL, (s, u, wp)
     assert sh.n_diverged() == 0
     sh.close()
+
+
+def test_tensor_only_small_dimensions():
+    """Every dimension blocked at <= 8: no MFMA factor at all (reductions,
+    fp64 Jacobi roots, FMA mode products), ragged tails."""
+    w = tw(name="small_only", shapes=((5, 3, 7), (8, 2, 4)), block_dims=(4, 3, 4), root_every=2,
+           steps=3)
+    s, u, wp, sh, _ = run_tensor_parity(w, 3)
+    assert s <= STATS_TOL and u <= UPDATE_TOL and wp <= UPDATE_TOL, (s, u, wp)
+    sh.close()
+
+
+def test_tensor_empty_and_zero_tensors():
+    """A handle with no tensors steps as a no-op; a zero-extent tensor among
+    others is skipped (its pointer may be NULL)."""
+    sh = S.TensorShampoo([], (32, 3))
+    sh.step([], [])
+    sh.close()
+    shapes = [(40, 3), (0, 3), (33, 2)]
+    sh = S.TensorShampoo(shapes, (32, 3), root_every=1)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    params = [torch.zeros(s, device="cuda") for s in shapes]
+    grads = [torch.randn(s, generator=gen, device="cuda") for s in shapes]
+    S.shampoo_step(sh.handle, [params[0].data_ptr(), 0, params[2].data_ptr()],
+                   [grads[0].data_ptr(), 0, grads[2].data_ptr()], 0, sh._stream())
+    torch.cuda.synchronize()
+    assert torch.isfinite(params[0]).all() and params[0].abs().sum() > 0
+    assert torch.isfinite(params[2]).all() and params[2].abs().sum() > 0
+    sh.close()
