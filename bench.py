@@ -14,8 +14,13 @@ tensors resident in HBM before the timed region (by default one distinct
 set per step, as the workload's distribution prescribes). Prints one JSON line with steps/s, blocks/s, per-kernel-class times
 and TFLOP/s measured with HIP events on the stream the kernels run on, the
 roofline fraction of the dominant kernel (the Newton products) against the
-fp32 MFMA peak, and the fp64 oracle timed on the host cores on a bounded
-sample of blocks.
+peak of the matrix-core path it runs on, and the fp64 oracle timed on the
+host cores on a bounded sample of blocks.
+
+Peaks: fp32 products on the fp32 MFMA take its 157.3 TFLOP/s; fp32 products
+split into three bf16 terms (the default) run six bf16 MFMA products per fp32
+product, so their ceiling in fp32 FLOP/s is the 2.5 PFLOP/s bf16 peak / 6 =
+416.7 TFLOP/s; statistics of bf16 gradients take the bf16 peak itself.
 """
 from __future__ import annotations
 
@@ -32,7 +37,10 @@ if ROOT not in sys.path:
 METRIC = "Shampoo optimizer steps/sec + batched GEMM TFLOP/s vs MFMA peak, 1 GPU"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (the statistics of bf16 gradients)
+PEAK_SPLIT_TFLOPS = PEAK_BF16_MFMA_TFLOPS / 6.0  # fp32 products as six bf16 products
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+PATH_PEAKS = {"f32": PEAK_FP32_MFMA_TFLOPS, "bf16": PEAK_BF16_MFMA_TFLOPS,
+              "split": PEAK_SPLIT_TFLOPS}
 DEFAULT_WORKLOAD = "decoder_1b_b1024_f32"
 
 
@@ -142,17 +150,18 @@ def cpu_baseline_tensor(w, grad_sets, budget_s=15.0, max_blocks=16, seed=0):
     }
 
 
-def class_table(tm, bf16_stats=False):
+def class_table(tm, paths):
+    """Per timing class: time, launches, TFLOP/s and the fraction of the
+    peak of its matrix-core path (paths: class -> "f32" | "bf16" | "split")."""
     kernels = {}
     for name, d in tm.items():
         entry = {"ms": round(d["ms"], 3), "launches": d["launches"]}
         if d["flops"] > 0 and d["ms"] > 0:
             tf = d["flops"] / (d["ms"] * 1e-3) / 1e12
             entry["tflops"] = round(tf, 2)
-            if name == "stats" and bf16_stats:  # bf16 gradients: bf16 MFMA statistics
-                entry["frac_bf16_mfma"] = round(tf / PEAK_BF16_MFMA_TFLOPS, 4)
-            else:
-                entry["frac_fp32_mfma"] = round(tf / PEAK_FP32_MFMA_TFLOPS, 4)
+            path = paths.get(name, "f32")
+            entry["mfma_path"] = path
+            entry["frac_mfma"] = round(tf / PATH_PEAKS[path], 4)
         if d["bytes"] > 0 and d["ms"] > 0:
             gbs = d["bytes"] / (d["ms"] * 1e-3) / 1e9
             entry["gbs"] = round(gbs, 1)
@@ -170,6 +179,8 @@ def run_tensor(args, w, torch, S, synth):
         w = dataclasses.replace(w, root_method=args.root_method)
     if args.scale_mode is not None:
         w = dataclasses.replace(w, newton_scale_mode=args.scale_mode)
+    if args.fp32_gemm is not None:
+        w = dataclasses.replace(w, fp32_gemm=args.fp32_gemm)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"tensor workload {w.name}: {len(w.shapes)} tensors, blocks {w.block_dims}")
@@ -187,7 +198,7 @@ def run_tensor(args, w, torch, S, synth):
                          root_every=w.root_every, newton_max_iters=w.newton_max_iters,
                          newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode,
                          dtype=w.dtype, momentum=w.momentum, root_method=w.root_method,
-                         cheb_degree=w.cheb_degree)
+                         cheb_degree=w.cheb_degree, fp32_gemm=w.fp32_gemm)
     B = sh.n_blocks
     log(f"{B} blocks of {int(sh.info.block_elems)} elements, workspace "
         f"{sh.workspace.numel() / 2**30:.2f} GiB")
@@ -208,9 +219,12 @@ def run_tensor(args, w, torch, S, synth):
     tm = sh.timing()
     sh.set_timing(False)
     n_div = sh.n_diverged()
-    kernels = class_table(tm)
-    # dominant class by kernel time; its roofline against the fp32 MFMA peak
-    # (statistics, root products, apply products) or HBM (the others)
+    # the tensor statistics and mode products take the fp32 MFMA; the root
+    # products the configured path
+    paths = {"stats": "f32", "apply": "f32", "newton_gemm": w.fp32_gemm}
+    kernels = class_table(tm, paths)
+    # dominant class by kernel time; its roofline against its matrix-core
+    # path (statistics, root products, apply products) or HBM (the others)
     dom = max(tm, key=lambda k: tm[k]["ms"])
     d = tm[dom]
     if dom not in ("stats", "newton_gemm", "apply"):
@@ -219,8 +233,9 @@ def run_tensor(args, w, torch, S, synth):
                 "frac": round(ach / PEAK_HBM_GBS, 4)}
     else:
         ach = d["flops"] / (d["ms"] * 1e-3) / 1e12 if d["ms"] > 0 else 0.0
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4)}
+        peak = PATH_PEAKS[paths[dom]]
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
     roof.update({"traffic": None, "kernel": f"class {dom}", "launches": d["launches"],
                  "avg_launch_ms": d["ms"] / max(1, d["launches"])})
     cpu = None if args.no_cpu_baseline else cpu_baseline_tensor(w, grad_sets)
@@ -234,7 +249,8 @@ def run_tensor(args, w, torch, S, synth):
         "data": "synthetic (seeded gradients with conv-filter shapes)",
         "config": {"workload": w.name, "tensors": len(w.shapes), "blocks": B,
                    "block": list(w.block_dims), "root_every": w.root_every,
-                   "root_method": w.root_method, "momentum": w.momentum, "grad_sets": n_sets},
+                   "root_method": w.root_method, "momentum": w.momentum,
+                   "fp32_gemm": w.fp32_gemm, "grad_sets": n_sets},
         "blocks_per_s": round(steps_per_s * B, 1),
         "kernels": kernels, "n_diverged": n_div, "roofline": roof, "cpu_baseline": cpu,
     }
@@ -242,12 +258,14 @@ def run_tensor(args, w, torch, S, synth):
     print(json.dumps(out), flush=True)
 
 
-def newton_traffic(workload):
+def newton_traffic(workload, gemm):
     """HBM bytes per Newton-product launch from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source (its
-    SHA-256 is recorded with the counters); None otherwise."""
+    counter summary of this workload and product path, if it was taken on the
+    current kernel source (its SHA-256 is recorded with the counters); None
+    otherwise."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    tag = "" if gemm == "split" else "_fp32mfma"
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}{tag}.json")
     src = os.path.join(ROOT, "blocked_shampoo_preconditioning_amd", "csrc", "kernels.hip")
     try:
         rec = json.load(open(path))
@@ -276,6 +294,9 @@ def main():
                     help="Newton scale mode (default: the workload's)")
     ap.add_argument("--cheb-degree", type=int, default=None,
                     help="Chebyshev degree (default: the workload's, 128)")
+    ap.add_argument("--fp32-gemm", default=None, choices=("split", "f32"),
+                    help="fp32 products: split into three bf16 terms on the bf16 MFMA "
+                         "(default) or the fp32 MFMA")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one plain 1 GiB device copy (a known-size kernel that "
                          "calibrates the HBM traffic counters)")
@@ -308,6 +329,8 @@ def main():
         w = dataclasses.replace(w, cheb_degree=args.cheb_degree)
     if args.scale_mode is not None:
         w = dataclasses.replace(w, newton_scale_mode=args.scale_mode)
+    if args.fp32_gemm is not None:
+        w = dataclasses.replace(w, fp32_gemm=args.fp32_gemm)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {w.name}: {len(w.shapes)} matrices, blocks {w.block_rows}x{w.block_cols}")
@@ -324,7 +347,8 @@ def main():
     sh = S.Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
                    root_every=w.root_every, newton_max_iters=w.newton_max_iters,
                    newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype,
-                   momentum=w.momentum, root_method=w.root_method, cheb_degree=w.cheb_degree)
+                   momentum=w.momentum, root_method=w.root_method, cheb_degree=w.cheb_degree,
+                   fp32_gemm=w.fp32_gemm)
     B = sh.n_blocks
     log(f"{B} blocks, workspace {sh.workspace.numel() / 2**30:.1f} GiB")
     for t in range(args.warmup):
@@ -365,14 +389,21 @@ def main():
     log(f"timed {args.steps} steps: {elapsed * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms)")
 
     steps_per_s = args.steps / elapsed
-    kernels = class_table(tm, bf16_stats=w.dtype == "bf16")
+    # statistics of bf16 gradients take the bf16 MFMA; the other products
+    # the configured fp32 path
+    paths = {"stats": "bf16" if w.dtype == "bf16" else w.fp32_gemm,
+             "newton_gemm": w.fp32_gemm, "apply": w.fp32_gemm}
+    kernels = class_table(tm, paths)
     nw = tm["newton_gemm"]
     achieved = nw["flops"] / (nw["ms"] * 1e-3) / 1e12 if nw["ms"] > 0 else 0.0
-    traffic = newton_traffic(w.name)
+    traffic = newton_traffic(w.name, w.fp32_gemm)
+    peak = PATH_PEAKS[w.fp32_gemm]
+    how = ("fp32 operands split into three bf16 terms, six bf16 MFMA 32x32x16 products"
+           if w.fp32_gemm == "split" else "fp32 MFMA 32x32x2")
     roofline = {
-        "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": traffic,
-        "kernel": "newton_sym_kernel (fp32 MFMA 32x32x2, 128x128 tiles, symmetric outputs; "
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+        "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+        "kernel": f"newton_sym_kernel ({how}, 128x128 tiles, symmetric outputs; "
                   f"{w.root_method} root products)",
         "launches": nw["launches"],
         "flops_per_launch": nw["flops"] / max(1, nw["launches"]),
@@ -392,7 +423,7 @@ def main():
                    "block": [w.block_rows, w.block_cols], "root_every": w.root_every,
                    "newton_max_iters": w.newton_max_iters, "newton_tol": w.newton_tol,
                    "newton_scale_mode": w.newton_scale_mode, "momentum": w.momentum,
-                   "root_method": w.root_method,
+                   "root_method": w.root_method, "fp32_gemm": w.fp32_gemm,
                    "cheb_degree": w.cheb_degree if w.root_method == "chebyshev" else None,
                    "grad_sets": n_sets},
         "blocks_per_s": round(steps_per_s * B, 1),

@@ -57,7 +57,19 @@ struct GemmProblem {
   // [M][K] bf16 row-major (k contiguous), element stride sXh between members
   const uint16_t* Xh;
   int64_t sXh;
+  // split path (launch_gemm_full only): Q holds B^T [K][N] (n contiguous)
+  // instead of B [N][K]
+  int32_t q_cols;
 };
+
+// How the fp32 products run. kGemmF32: C = P^T Q on the fp32 MFMA, P [K][M]
+// and Q [K][N]. kGemmSplit: C = A B^T on the bf16 MFMA, each fp32 operand
+// split into three bf16 terms (six products, fp32 accuracy); P holds A [M][K]
+// and Q holds B [N][K], both with k contiguous and row stride K. For the
+// symmetric products (statistics, root iterations) the two readings coincide
+// when the operands are symmetric; the statistics pass the transposed
+// operands on the split path.
+enum GemmMode : int { kGemmF32 = 0, kGemmSplit = 1 };
 
 constexpr int kMaxProblems = 8;
 
@@ -153,13 +165,14 @@ hipError_t launch_unpack(const BlockMeta* blocks, const MatMeta* dst, int32_t B,
                          int32_t bc, const float* Gp, hipStream_t s);
 hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nelemR, int32_t nr,
                              int32_t B, float eps, hipStream_t s);
-hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, hipStream_t s);
+hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode, hipStream_t s);
 // Statistics from bf16 operands on the bf16 MFMA (exact products, fp32
 // accumulation): the problems' Xh / sXh, same epilogue as the symmetric
 // product. M and K multiples of the tile and of 32.
 hipError_t launch_gemm_sym_bf16(const GemmLaunch& g, int tile, hipStream_t s);
-hipError_t launch_gemm_full(const GemmLaunch& g, int tile, hipStream_t s);
-hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, hipStream_t s);
+hipError_t launch_gemm_full(const GemmLaunch& g, int tile, int mode, hipStream_t s);
+hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, int mode,
+                              hipStream_t s);
 hipError_t launch_norms(const float* A, FactorSet fs, NewtonCtl c, hipStream_t s);
 hipError_t launch_newton_init(const float* A, float* M0, float* X1, FactorSet fs, NewtonCtl c,
                               hipStream_t s);

@@ -50,6 +50,11 @@ struct Cfg {
   static constexpr int BKH = 32, LDKH = BKH + 8;
   static constexpr int LDS_BF16 = 2 * (BM + BN) * LDKH / 2;  // in floats
   static constexpr int LDS_FLOATS = LDS_FP32 > LDS_BF16 ? LDS_FP32 : LDS_BF16;
+  // split products: K-tiles of 16, each operand row as three bf16 planes,
+  // rows of 16 values padded to 24 (48 bytes: 16-byte aligned rows whose
+  // 16-byte reads from eight consecutive rows fall on distinct banks)
+  static constexpr int LDX = 24;
+  static constexpr int LDS_SPLIT = 2 * 3 * (BM + BN) * LDX / 2;  // in floats
   static constexpr int PV = BM / 4, QV = BN / 4;           // float4 per operand row
   static constexpr int PPT = BK * PV / NT, QPT = BK * QV / NT;  // float4 per thread
   static_assert(PPT >= 1 && QPT >= 1, "tile too small for the thread count");
@@ -271,6 +276,160 @@ __device__ __forceinline__ void mainloop_bf16(const uint16_t* __restrict__ X, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split products: fp32 operands, bf16 matrix cores.
+// x = h + m + l exactly, each term a bf16 value: h keeps the top 16 bits of
+// x (sign, exponent, 7 fraction bits), m the top 16 bits of r = x - h, and
+// l = r - m, which has at most 8 significant bits left (for |x| >= 2^-103;
+// below that the last bits of l can be lost). Then
+//   x y = hh + (hm + mh) + (hl + mm + lh) + O(2^-24 |x y|):
+// six bf16 products, each exact in fp32, accumulated in fp32 by the MFMA,
+// cost 6 / 16 of the fp32 MFMA time at the same accuracy as fp32 products.
+// Non-finite inputs give NaN. Two values per call, packed as bf16 pairs
+// (first value in the low half).
+// ---------------------------------------------------------------------------
+struct Split3 {
+  uint32_t h, m, l;
+};
+
+__device__ __forceinline__ Split3 split3(float x0, float x1) {
+  const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+  const float r0 = x0 - __uint_as_float(u0 & 0xffff0000u);
+  const float r1 = x1 - __uint_as_float(u1 & 0xffff0000u);
+  const uint32_t v0 = __float_as_uint(r0), v1 = __float_as_uint(r1);
+  const float t0 = r0 - __uint_as_float(v0 & 0xffff0000u);
+  const float t1 = r1 - __uint_as_float(v1 & 0xffff0000u);
+  Split3 o;
+  // v_perm_b32: bytes 2, 3 of the second source, then bytes 2, 3 of the first
+  o.h = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+  o.m = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
+  o.l = __builtin_amdgcn_perm(__float_as_uint(t1), __float_as_uint(t0), 0x07060302u);
+  return o;
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Three planes of 4 consecutive k of one row.
+__device__ __forceinline__ void store_split4(uint16_t* d, int plane, const f32x4& v) {
+  const Split3 a = split3(v[0], v[1]), b = split3(v[2], v[3]);
+  *reinterpret_cast<u32x2*>(d) = (u32x2){a.h, b.h};
+  *reinterpret_cast<u32x2*>(d + plane) = (u32x2){a.m, b.m};
+  *reinterpret_cast<u32x2*>(d + 2 * plane) = (u32x2){a.l, b.l};
+}
+
+// acc[fm][fn] = sum over K of A[m0 + ...][k] * B[n0 + ...][k]: A is [M][K]
+// with row stride lda (k contiguous); B likewise [N][K] with row stride ldb,
+// or with QCOLS its transpose [K][N] (row stride ldb, n contiguous). One
+// K-tile of 16: every thread loads its share of both operands as fp32,
+// splits it and stores the three bf16 planes ([plane][row][k], rows of
+// LDX); each wave reads, per fragment, 8 consecutive k of one row from every
+// plane (lane l: row l % 32, k 8 (l / 32) + 0..7, the 32x32x16 bf16 MFMA's
+// operand layout for both A and B) and runs the six products. The next
+// K-tile's global loads are in flight during the MFMAs and are split into
+// the other LDS buffer after them, as in mainloop_w.
+template <class C, bool QCOLS, int MASK = -1>
+__device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda,
+                                            const float* __restrict__ B, int ldb, int K, int m0,
+                                            int n0, int wm, int wn,
+                                            floatx16 (&acc)[C::FM][C::FN], float* lds) {
+  constexpr int LD = C::LDX;
+  constexpr int PA = C::BM * LD, PB = C::BN * LD;  // one plane, in bf16
+  uint16_t* sA = reinterpret_cast<uint16_t*>(lds);  // [2][3][BM][LD]
+  uint16_t* sB = sA + 2 * 3 * PA;                    // [2][3][BN][LD]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // rows: 4-value chunks, 4 per row; columns: one row of B^T per thread,
+  // KC consecutive k of it
+  constexpr int NA = C::BM * 4 / C::NT, NB = C::BN * 4 / C::NT;
+  constexpr int KC = 16 * C::BN / C::NT;
+  static_assert(NA >= 1 && NB >= 1 && (C::BM * 4) % C::NT == 0 && (C::BN * 4) % C::NT == 0,
+                "uneven operand load");
+  static_assert(!QCOLS || (C::NT % C::BN == 0 && (KC == 4 || KC == 8)), "column load shape");
+  const int bc_row = tid % C::BN, bc_k = (tid / C::BN) * KC;
+  f32x4 ra[NA];
+  f32x4 rb[QCOLS ? 1 : NB];
+  float rc[QCOLS ? KC : 1];
+  const int nk = K / 16;
+  for (int kt = -1; kt < nk; ++kt) {
+    // kt = -1 only stages K-tile 0
+    const int buf = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int k0 = (kt + 1) * 16;
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int c = tid + i * C::NT;
+        ra[i] = *reinterpret_cast<const f32x4*>(A + (size_t)(m0 + c / 4) * lda + k0 + (c % 4) * 4);
+      }
+      if constexpr (QCOLS) {
+#pragma unroll
+        for (int q = 0; q < KC; ++q) rc[q] = B[(size_t)(k0 + bc_k + q) * ldb + n0 + bc_row];
+      } else {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int c = tid + i * C::NT;
+          rb[i] = *reinterpret_cast<const f32x4*>(B + (size_t)(n0 + c / 4) * ldb + k0 + (c % 4) * 4);
+        }
+      }
+    }
+    if (kt >= 0) {
+      const uint16_t* a0 = sA + buf * 3 * PA + (wm * 32 * C::FM + l32) * LD + half * 8;
+      const uint16_t* b0 = sB + buf * 3 * PB + (wn * 32 * C::FN + l32) * LD + half * 8;
+      bf16x8 a[3][C::FM], b[3][C::FN];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+          a[p][i] = *reinterpret_cast<const bf16x8*>(a0 + p * PA + i * 32 * LD);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          b[p][j] = *reinterpret_cast<const bf16x8*>(b0 + p * PB + j * 32 * LD);
+      }
+      // (plane of A, plane of B), smallest terms first; consecutive MFMAs
+      // go to different accumulators
+      constexpr int PP[6][2] = {{2, 0}, {1, 1}, {0, 2}, {1, 0}, {0, 1}, {0, 0}};
+#pragma unroll
+      for (int q = 0; q < 6; ++q)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            if (MASK & (1 << (i * C::FN + j)))
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PP[q][0]][i], b[PP[q][1]][j],
+                                                                  acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      uint16_t* dA = sA + (buf ^ 1) * 3 * PA;
+      uint16_t* dB = sB + (buf ^ 1) * 3 * PB;
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int c = tid + i * C::NT;
+        store_split4(dA + (c / 4) * LD + (c % 4) * 4, PA, ra[i]);
+      }
+      if constexpr (QCOLS) {
+        uint16_t* d = dB + bc_row * LD + bc_k;
+#pragma unroll
+        for (int q = 0; q < KC; q += 4)
+          store_split4(d + q, PB, (f32x4){rc[q], rc[q + 1], rc[q + 2], rc[q + 3]});
+      } else {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int c = tid + i * C::NT;
+          store_split4(dB + (c / 4) * LD + (c % 4) * 4, PB, rb[i]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int FM, int FN>
 constexpr int upper_mask() {
   int m = 0;
@@ -361,6 +520,25 @@ __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X
     mainloop_bf16<C, 0>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
 }
 
+template <class C>
+__device__ __forceinline__ void mainloop_sym_x6(const float* __restrict__ A,
+                                                const float* __restrict__ B, int K, int m0,
+                                                int n0, floatx16 (&acc)[C::FM][C::FN],
+                                                float* lds, const SymWave<C>& sw) {
+  constexpr int kUpper = upper_mask<C::FM, C::FN>();
+  constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
+  if (sw.mask == -1)
+    mainloop_x6<C, false>(A, K, B, K, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else if (sw.mask == kUpper)
+    mainloop_x6<C, false, kUpper>(A, K, B, K, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else if (C::FM >= 2 && sw.mask == kTop)
+    mainloop_x6<C, false, kTop>(A, K, B, K, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else if (C::FM >= 2 && sw.mask == kBottom)
+    mainloop_x6<C, false, kBottom>(A, K, B, K, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  else
+    mainloop_x6<C, false, 0>(A, K, B, K, K, m0, n0, sw.wm, sw.wn, acc, lds);
+}
+
 // Row / column of accumulator register r of fragment (i, j) of the wave's
 // block (wm, wn).
 template <class C>
@@ -387,9 +565,18 @@ __device__ __forceinline__ int frag_col(int n0, int j) {
 // is written to its place and mirrored, so the stored result is exactly
 // symmetric. Used by the statistics (EMA epilogue) and the Newton chain.
 // ---------------------------------------------------------------------------
-template <class C, bool BF16 = false>
+// Operand paths of the products: fp32 MFMA, bf16 operands (bf16
+// statistics), fp32 operands split into bf16 terms.
+enum : int { kPathF32 = 0, kPathBF16 = 1, kPathSplit = 2 };
+
+template <class C, int PATH>
+constexpr int lds_floats() {
+  return PATH == kPathSplit ? C::LDS_SPLIT : C::LDS_FLOATS;
+}
+
+template <class C, int PATH = kPathF32>
 __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
-  __shared__ float lds[C::LDS_FLOATS];
+  __shared__ float lds[lds_floats<C, PATH>()];
   float* red = lds;  // residual partials reuse the operand tiles after the K loop
   const GemmProblem& pb = g.p[blockIdx.y];
   const int T = pb.M / C::BM;
@@ -418,8 +605,11 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const bool diag = (ti == tj);
   const SymWave<C> sw(diag);
   floatx16 acc[C::FM][C::FN];
-  if constexpr (BF16)
+  if constexpr (PATH == kPathBF16)
     mainloop_sym_bf16<C>(pb.Xh + (size_t)f * pb.sXh, pb.K, m0, n0, acc, lds, sw);
+  else if constexpr (PATH == kPathSplit)
+    mainloop_sym_x6<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.K, m0, n0, acc, lds,
+                       sw);
   else
     mainloop_sym<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0,
                     acc, lds, sw);
@@ -487,29 +677,49 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   }
 }
 
-// Statistics: L <- beta2 L + g GpT^T GpT, R <- beta2 R + g Gp^T Gp.
-template <class C>
-__global__ __launch_bounds__(C::NT, 4) void syrk_ema_kernel(GemmLaunch g) {
-  sym_product<C>(g);
+// Statistics: L <- beta2 L + g Gp Gp^T, R <- beta2 R + g Gp^T Gp (fp32 path:
+// P = Q = GpT for L, Gp for R; split path: the row operands, Gp for L and
+// GpT for R).
+template <class C, int PATH>
+__global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void syrk_ema_kernel(GemmLaunch g) {
+  sym_product<C, PATH>(g);
 }
 
 // Statistics from bf16 packed gradients: L <- beta2 L + g Gp Gp^T reads GpH
 // (rows of Gp), R <- beta2 R + g Gp^T Gp reads GpTH (rows of Gp^T).
 template <class C>
 __global__ __launch_bounds__(C::NT, 4) void syrk_bf16_kernel(GemmLaunch g) {
-  sym_product<C, true>(g);
+  sym_product<C, kPathBF16>(g);
 }
 
-// One product of the coupled Newton chain (T T, X T, T2 T2 or T4 M).
-template <class C>
-__global__ __launch_bounds__(C::NT, 4) void newton_sym_kernel(GemmLaunch g) {
-  sym_product<C>(g);
+// One product of the coupled Newton chain (T T, X T, T2 T2 or T4 M); every
+// operand is symmetric, so P and Q serve as row operands as they are.
+template <class C, int PATH>
+__global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void newton_sym_kernel(GemmLaunch g) {
+  sym_product<C, PATH>(g);
+}
+
+// The product's main loop on either path: fp32 (C = P^T Q, P [K][M] and
+// Q [K][N]) or split (C = A B^T with A = P [M][K] and B = Q [N][K], or with
+// QCOLS Q = B^T [K][N]).
+template <class C, int PATH, bool QCOLS>
+__device__ __forceinline__ void full_mainloop(const GemmProblem& pb, int f, int m0, int n0,
+                                              floatx16 (&acc)[C::FM][C::FN], float* lds) {
+  const float* P = pb.P + (size_t)f * pb.sP;
+  const float* Q = pb.Q + (size_t)f * pb.sQ;
+  if constexpr (PATH == kPathSplit) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    mainloop_x6<C, QCOLS>(P, pb.K, Q, QCOLS ? pb.N : pb.K, pb.K, m0, n0, wave % C::WM,
+                          wave / C::WM, acc, lds);
+  } else {
+    mainloop<C>(P, Q, pb.M, pb.N, pb.K, m0, n0, acc, lds);
+  }
 }
 
 // Plain product, every tile, C = acc (first apply product).
-template <class C>
+template <class C, int PATH, bool QCOLS>
 __global__ __launch_bounds__(C::NT) void apply_left_kernel(GemmLaunch g) {
-  __shared__ float lds[C::LDS_FLOATS];
+  __shared__ float lds[lds_floats<C, PATH>()];
   const GemmProblem& pb = g.p[blockIdx.y];
   const int TM = pb.M / C::BM, TN = pb.N / C::BN;
   const int ntile = TM * TN;
@@ -519,8 +729,7 @@ __global__ __launch_bounds__(C::NT) void apply_left_kernel(GemmLaunch g) {
   const int tile = logical - f * ntile;
   const int m0 = (tile / TN) * C::BM, n0 = (tile % TN) * C::BN;
   floatx16 acc[C::FM][C::FN];
-  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, acc,
-              lds);
+  full_mainloop<C, PATH, QCOLS>(pb, f, m0, n0, acc, lds);
   float* Cb = pb.C + (size_t)f * pb.sC;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -544,9 +753,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 
 // Second apply product with the parameter update in the epilogue:
 // W[r0 + row][c0 + col] -= lr * U[row][col] on the block's real extent.
-template <class C>
-__global__ __launch_bounds__(C::NT, 4) void apply_update_kernel(GemmLaunch g, UpdateArgs u) {
-  __shared__ float lds[C::LDS_FLOATS];
+template <class C, int PATH>
+__global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void apply_update_kernel(GemmLaunch g, UpdateArgs u) {
+  __shared__ float lds[lds_floats<C, PATH>()];
   const GemmProblem& pb = g.p[0];
   const int TM = pb.M / C::BM, TN = pb.N / C::BN;
   const int ntile = TM * TN;
@@ -556,8 +765,7 @@ __global__ __launch_bounds__(C::NT, 4) void apply_update_kernel(GemmLaunch g, Up
   const int tile = logical - f * ntile;
   const int m0 = (tile / TN) * C::BM, n0 = (tile % TN) * C::BN;
   floatx16 acc[C::FM][C::FN];
-  mainloop<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0, acc,
-              lds);
+  full_mainloop<C, PATH, false>(pb, f, m0, n0, acc, lds);
   if (u.out_packed != nullptr) {
     float* Ub = u.out_packed + (size_t)f * pb.M * pb.N;
 #pragma unroll
@@ -1265,23 +1473,31 @@ hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nele
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, hipStream_t s) {
+hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode, hipStream_t s) {
   if (g.n_problems == 0) return hipSuccess;
+  if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
   switch (tile) {
+#define SHP_SYM_LAUNCH(CFG, PATH)                                                              \
+  if (newton)                                                                                  \
+    hipLaunchKernelGGL((newton_sym_kernel<CFG, PATH>), dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g); \
+  else                                                                                         \
+    hipLaunchKernelGGL((syrk_ema_kernel<CFG, PATH>), dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g);
 #define SHP_SYM_CASE(T, CFG)                                                                   \
   case T: {                                                                                    \
     const int gx = grid_sym<CFG>(g);                                                           \
     if (!gx) break;                                                                            \
-    if (newton)                                                                                \
-      hipLaunchKernelGGL(newton_sym_kernel<CFG>, dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g); \
-    else                                                                                       \
-      hipLaunchKernelGGL(syrk_ema_kernel<CFG>, dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g);   \
+    if (mode == kGemmSplit) {                                                                  \
+      SHP_SYM_LAUNCH(CFG, kPathSplit)                                                          \
+    } else {                                                                                   \
+      SHP_SYM_LAUNCH(CFG, kPathF32)                                                            \
+    }                                                                                          \
     break;                                                                                     \
   }
     SHP_SYM_CASE(128, Cfg128)
     SHP_SYM_CASE(64, Cfg64)
     SHP_SYM_CASE(32, Cfg32)
 #undef SHP_SYM_CASE
+#undef SHP_SYM_LAUNCH
     default:
       return hipErrorInvalidValue;
   }
@@ -1308,50 +1524,55 @@ hipError_t launch_gemm_sym_bf16(const GemmLaunch& g, int tile, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_full(const GemmLaunch& g, int tile, hipStream_t s) {
+namespace {
+template <class CFG>
+void launch_full_cfg(const GemmLaunch& g, int mode, bool qcols, hipStream_t s) {
+  const int gx = grid_full<CFG>(g);
+  if (!gx) return;
+  const dim3 grid(gx, g.n_problems), block(CFG::NT);
+  if (mode == kGemmSplit && qcols)
+    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, true>), grid, block, 0, s, g);
+  else if (mode == kGemmSplit)
+    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, false>), grid, block, 0, s, g);
+  else
+    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathF32, false>), grid, block, 0, s, g);
+}
+template <class CFG>
+void launch_update_cfg(const GemmLaunch& g, const UpdateArgs& u, int mode, hipStream_t s) {
+  const int gx = grid_full<CFG>(g);
+  if (!gx) return;
+  if (mode == kGemmSplit)
+    hipLaunchKernelGGL((apply_update_kernel<CFG, kPathSplit>), dim3(gx), dim3(CFG::NT), 0, s, g, u);
+  else
+    hipLaunchKernelGGL((apply_update_kernel<CFG, kPathF32>), dim3(gx), dim3(CFG::NT), 0, s, g, u);
+}
+}  // namespace
+
+hipError_t launch_gemm_full(const GemmLaunch& g, int tile, int mode, hipStream_t s) {
   if (g.n_problems == 0) return hipSuccess;
+  if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
+  const bool qcols = g.p[0].q_cols != 0;
+  for (int i = 1; i < g.n_problems; ++i)
+    if ((g.p[i].q_cols != 0) != qcols) return hipErrorInvalidValue;
+  if (qcols && mode != kGemmSplit) return hipErrorInvalidValue;
   switch (tile) {
-    case 128: {
-      const int gx = grid_full<Cfg128>(g);
-      if (gx) hipLaunchKernelGGL(apply_left_kernel<Cfg128>, dim3(gx, g.n_problems), dim3(Cfg128::NT), 0, s, g);
-      break;
-    }
-    case 64: {
-      const int gx = grid_full<Cfg64>(g);
-      if (gx) hipLaunchKernelGGL(apply_left_kernel<Cfg64>, dim3(gx, g.n_problems), dim3(Cfg64::NT), 0, s, g);
-      break;
-    }
-    case 32: {
-      const int gx = grid_full<Cfg32>(g);
-      if (gx) hipLaunchKernelGGL(apply_left_kernel<Cfg32>, dim3(gx, g.n_problems), dim3(Cfg32::NT), 0, s, g);
-      break;
-    }
-    default:
-      return hipErrorInvalidValue;
+    case 128: launch_full_cfg<Cfg128>(g, mode, qcols, s); break;
+    case 64: launch_full_cfg<Cfg64>(g, mode, qcols, s); break;
+    case 32: launch_full_cfg<Cfg32>(g, mode, qcols, s); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, hipStream_t s) {
-  if (g.n_problems != 1) return hipErrorInvalidValue;
+hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, int mode,
+                              hipStream_t s) {
+  if (g.n_problems != 1 || g.p[0].q_cols != 0) return hipErrorInvalidValue;
+  if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
   switch (tile) {
-    case 128: {
-      const int gx = grid_full<Cfg128>(g);
-      if (gx) hipLaunchKernelGGL(apply_update_kernel<Cfg128>, dim3(gx), dim3(Cfg128::NT), 0, s, g, u);
-      break;
-    }
-    case 64: {
-      const int gx = grid_full<Cfg64>(g);
-      if (gx) hipLaunchKernelGGL(apply_update_kernel<Cfg64>, dim3(gx), dim3(Cfg64::NT), 0, s, g, u);
-      break;
-    }
-    case 32: {
-      const int gx = grid_full<Cfg32>(g);
-      if (gx) hipLaunchKernelGGL(apply_update_kernel<Cfg32>, dim3(gx), dim3(Cfg32::NT), 0, s, g, u);
-      break;
-    }
-    default:
-      return hipErrorInvalidValue;
+    case 128: launch_update_cfg<Cfg128>(g, u, mode, s); break;
+    case 64: launch_update_cfg<Cfg64>(g, u, mode, s); break;
+    case 32: launch_update_cfg<Cfg32>(g, u, mode, s); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

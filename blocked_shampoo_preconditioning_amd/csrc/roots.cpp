@@ -83,7 +83,7 @@ void factor_problems(const RootJob& j, SymLaunches& L, const float* P, const flo
 int launch_all(shampoo_ctx* h, const SymLaunches& L, double flops, hipStream_t s) {
   for (int i = 0; i < L.n; ++i) {
     const int rc = timed(h, kNewtonGemm, i == 0 ? flops : 0.0, 0.0, s,
-                         [&] { return shp::launch_gemm_sym(L.g[i], L.tile[i], true, s); });
+                         [&] { return shp::launch_gemm_sym(L.g[i], L.tile[i], true, h->cfg.fp32_gemm, s); });
     if (rc) return rc;
   }
   return SHAMPOO_OK;

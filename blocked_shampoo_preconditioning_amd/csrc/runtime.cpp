@@ -71,6 +71,8 @@ int validate_config(const shampoo_config_t* c, bool tensor) {
                 "root_method must be 0 (coupled Newton), 1 (Newton-DB) or 2 (Chebyshev)");
   if (c->root_method == shp::kChebyshev && (c->cheb_degree < 2 || c->cheb_degree > 1024))
     return fail(SHAMPOO_ERR_INVALID_ARG, "cheb_degree must be in 2..1024");
+  if (c->fp32_gemm != SHAMPOO_GEMM_F32 && c->fp32_gemm != SHAMPOO_GEMM_SPLIT_BF16)
+    return fail(SHAMPOO_ERR_INVALID_ARG, "fp32_gemm must be 0 (fp32 MFMA) or 1 (split bf16)");
   if (!std::isfinite(c->momentum) || c->momentum < 0.0 || c->momentum >= 1.0)
     return fail(SHAMPOO_ERR_INVALID_ARG, "momentum must be in [0, 1)");
   if ((c->param_dtype != SHAMPOO_F32 && c->param_dtype != SHAMPOO_BF16) ||
@@ -303,10 +305,14 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
   const Plan& p = h->plan;
   if (p.B == 0) return SHAMPOO_OK;
   shp::GemmLaunch g{};
-  // L = beta2 L + g Gp Gp^T: C[m][n] = sum_k GpT[k][m] GpT[k][n]
-  g.p[0] = sym_problem(m_gpT(h), m_gpT(h), m_lr(h), (int64_t)p.bc * p.br, p.br, p.bc, (int)p.B);
-  // R = beta2 R + g Gp^T Gp: C[m][n] = sum_k Gp[k][m] Gp[k][n]
-  g.p[1] = sym_problem(m_gp(h), m_gp(h), m_lr(h) + p.fl, (int64_t)p.br * p.bc, p.bc, p.br, (int)p.B);
+  // fp32 MFMA: C = P^T Q, so L = beta2 L + g Gp Gp^T reads P = Q = GpT and
+  // R = beta2 R + g Gp^T Gp reads P = Q = Gp. Split path: C = A A^T with the
+  // row operand A = Gp for L and A = GpT for R.
+  const bool split = h->cfg.fp32_gemm == SHAMPOO_GEMM_SPLIT_BF16;
+  float* opL = split ? m_gp(h) : m_gpT(h);
+  float* opR = split ? m_gpT(h) : m_gp(h);
+  g.p[0] = sym_problem(opL, opL, m_lr(h), (int64_t)p.bc * p.br, p.br, p.bc, (int)p.B);
+  g.p[1] = sym_problem(opR, opR, m_lr(h) + p.fl, (int64_t)p.br * p.bc, p.bc, p.br, (int)p.B);
   for (int i = 0; i < 2; ++i) {
     g.p[i].alpha = h->stat_scale;
     g.p[i].beta = (float)h->cfg.beta2;
@@ -327,7 +333,8 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
   const double bytes = (double)p.B * ((hb ? 2.0 : 4.0) * 2.0 * p.br * p.bc +
                                       4.0 * (2.0 * (double)p.br * p.br + 2.0 * (double)p.bc * p.bc));
   return timed(h, kStats, flops, bytes, s, [&] {
-    return hb ? shp::launch_gemm_sym_bf16(g, p.tile, s) : shp::launch_gemm_sym(g, p.tile, false, s);
+    return hb ? shp::launch_gemm_sym_bf16(g, p.tile, s)
+              : shp::launch_gemm_sym(g, p.tile, false, h->cfg.fp32_gemm, s);
   });
 }
 
@@ -359,24 +366,40 @@ int do_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
 int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   const Plan& p = h->plan;
   if (p.B == 0) return SHAMPOO_OK;
-  // TmpT[m][n] = sum_k Gp[k][m] X_L[k][n]   (= (X_L Gp)^T, bc x br); with
-  // momentum the preconditioned matrix is the momentum buffer
+  // the preconditioned matrix: the packed gradient, or the momentum buffer
+  const float* G = p.momentum ? m_mom(h) : m_gp(h);
+  const bool split = h->cfg.fp32_gemm == SHAMPOO_GEMM_SPLIT_BF16;
   shp::GemmLaunch g1{};
   shp::GemmProblem a{};
-  a.P = p.momentum ? m_mom(h) : m_gp(h);
-  a.sP = (int64_t)p.br * p.bc;
-  a.Q = m_xroot(h);
-  a.sQ = (int64_t)p.br * p.br;
+  if (split) {
+    // Tmp[m][n] = sum_k X_L[m][k] G[k][n] (= X_L G, br x bc): A = X_L (rows,
+    // symmetric), B = G^T read by columns from G (the packed transpose shares
+    // memory with the root iterations, which overwrite it on refresh steps)
+    a.P = m_xroot(h);
+    a.sP = (int64_t)p.br * p.br;
+    a.Q = G;
+    a.sQ = (int64_t)p.br * p.bc;
+    a.q_cols = 1;
+    a.M = p.br;
+    a.N = p.bc;
+  } else {
+    // TmpT[m][n] = sum_k G[k][m] X_L[k][n]   (= (X_L G)^T, bc x br)
+    a.P = G;
+    a.sP = (int64_t)p.br * p.bc;
+    a.Q = m_xroot(h);
+    a.sQ = (int64_t)p.br * p.br;
+    a.M = p.bc;
+    a.N = p.br;
+  }
   a.C = m_tmpT(h);
   a.sC = (int64_t)p.bc * p.br;
-  a.M = p.bc;
-  a.N = p.br;
   a.K = p.br;
   a.batch = (int)p.B;
   a.alpha = 1.f;
   g1.p[0] = a;
   g1.n_problems = 1;
-  // U[m][n] = sum_k TmpT[k][m] X_R[k][n]   (= X_L Gp X_R, br x bc)
+  // U = X_L G X_R (br x bc). fp32 MFMA: U[m][n] = sum_k TmpT[k][m] X_R[k][n];
+  // split: U[m][n] = sum_k Tmp[m][k] X_R[n][k] (X_R symmetric)
   shp::GemmLaunch g2{};
   shp::GemmProblem b{};
   b.P = m_tmpT(h);
@@ -402,9 +425,11 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
     f1 += 2.0 * bl.m * bl.m * (double)bl.n;
     f2 += 2.0 * bl.m * (double)bl.n * bl.n;
   }
-  int rc = timed(h, kApply, f1, 0.0, s, [&] { return shp::launch_gemm_full(g1, p.tile, s); });
+  const int mode = h->cfg.fp32_gemm;
+  int rc = timed(h, kApply, f1, 0.0, s, [&] { return shp::launch_gemm_full(g1, p.tile, mode, s); });
   if (rc) return rc;
-  return timed(h, kApply, f2, 0.0, s, [&] { return shp::launch_gemm_update(g2, u, p.tile, s); });
+  return timed(h, kApply, f2, 0.0, s,
+               [&] { return shp::launch_gemm_update(g2, u, p.tile, mode, s); });
 }
 
 }  // namespace
@@ -434,6 +459,7 @@ int shampoo_config_default(shampoo_config_t* cfg) {
   cfg->momentum = 0.0;
   cfg->root_method = shp::kCoupledNewton;
   cfg->cheb_degree = 128;
+  cfg->fp32_gemm = SHAMPOO_GEMM_SPLIT_BF16;
   return SHAMPOO_OK;
 }
 

@@ -336,7 +336,7 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
       q.beta = (float)h->cfg.beta2;
       g.n_problems = 1;
       rc = timed(h, kStats, fl, 0.0, s,
-                 [&] { return shp::launch_gemm_sym(g, ts.stat_tile[i], false, s); });
+                 [&] { return shp::launch_gemm_sym(g, ts.stat_tile[i], false, shp::kGemmF32, s); });
     } else {
       rc = timed(h, kStatsAux, fl, 4.0 * ts.B * ts.E, s, [&] {
         return shp::launch_small_gram(gp, ts.E, (int32_t)A, n, (int32_t)C, (int32_t)ts.B,
@@ -432,7 +432,7 @@ int do_tensor_apply(shampoo_ctx* h, hipStream_t s, float* out) {
       q.alpha = 1.f;
       g.n_problems = 1;
       rc = timed(h, kApply, fl, 0.0, s,
-                 [&] { return shp::launch_gemm_full(g, ts.apply_tile[i], s); });
+                 [&] { return shp::launch_gemm_full(g, ts.apply_tile[i], shp::kGemmF32, s); });
     } else {
       rc = timed(h, kApplyAux, fl, 8.0 * ts.B * ts.E, s, [&] {
         return shp::launch_mode_product(cur, ts.E, X, (int64_t)n * n, dst, ts.E, n, (int32_t)R,

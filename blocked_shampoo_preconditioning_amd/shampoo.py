@@ -29,6 +29,8 @@ SHAMPOO_NO_AUTO_REFRESH = 2
 TIMING_CLASSES = ("pack", "stats", "norms", "newton_gemm", "newton_aux", "apply", "stats_aux",
                   "apply_aux")
 ROOT_METHODS = {"newton": 0, "newton_db": 1, "chebyshev": 2}
+# shampoo_fp32_gemm_t: fp32 MFMA, or fp32 operands split into three bf16 terms
+GEMM_MODES = {"f32": 0, "split": 1}
 
 
 class MatrixDesc(ctypes.Structure):
@@ -43,7 +45,7 @@ class Config(ctypes.Structure):
                 ("newton_tol", ctypes.c_double), ("newton_scale_mode", ctypes.c_int32),
                 ("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
                 ("momentum", ctypes.c_double), ("root_method", ctypes.c_int32),
-                ("cheb_degree", ctypes.c_int32)]
+                ("cheb_degree", ctypes.c_int32), ("fp32_gemm", ctypes.c_int32)]
 
 
 class Layout(ctypes.Structure):
@@ -306,7 +308,7 @@ class Shampoo:
     def __init__(self, shapes, block_rows=1024, block_cols=1024, beta2=0.999, eps=1e-6, lr=1e-3,
                  root_every=10, stat_scale=None, newton_max_iters=25, newton_tol=1e-6,
                  newton_scale_mode=3, dtype="f32", device="cuda", lds=None, momentum=0.0,
-                 root_method="newton", cheb_degree=128):
+                 root_method="newton", cheb_degree=128, fp32_gemm="split"):
         import torch
         self.torch = torch
         self.shapes = [tuple(int(v) for v in s) for s in shapes]
@@ -321,6 +323,7 @@ class Shampoo:
         cfg.momentum = momentum
         cfg.root_method = ROOT_METHODS[root_method]
         cfg.cheb_degree = cheb_degree
+        cfg.fp32_gemm = GEMM_MODES[fp32_gemm]
         dt = {"f32": SHAMPOO_F32, "bf16": SHAMPOO_BF16}[dtype]
         cfg.param_dtype = cfg.grad_dtype = dt
         self.cfg = cfg
@@ -430,7 +433,7 @@ class TensorShampoo(Shampoo):
     def __init__(self, shapes, block_dims, beta2=0.999, eps=1e-6, lr=1e-3, root_every=10,
                  stat_scale=None, newton_max_iters=25, newton_tol=1e-6, newton_scale_mode=3,
                  dtype="f32", device="cuda", strides=None, momentum=0.0, root_method="newton",
-                 cheb_degree=128):
+                 cheb_degree=128, fp32_gemm="split"):
         import torch
         self.torch = torch
         self.shapes = [tuple(int(v) for v in s) for s in shapes]
@@ -444,6 +447,7 @@ class TensorShampoo(Shampoo):
         cfg.momentum = momentum
         cfg.root_method = ROOT_METHODS[root_method]
         cfg.cheb_degree = cheb_degree
+        cfg.fp32_gemm = GEMM_MODES[fp32_gemm]
         dt = {"f32": SHAMPOO_F32, "bf16": SHAMPOO_BF16}[dtype]
         cfg.param_dtype = cfg.grad_dtype = dt
         self.cfg = cfg

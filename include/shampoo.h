@@ -63,6 +63,19 @@ enum {
 /* Storage types of gradients and parameters. Statistics and roots are fp32. */
 typedef enum { SHAMPOO_F32 = 0, SHAMPOO_BF16 = 1 } shampoo_dtype_t;
 
+/* How the fp32 matrix products (statistics of fp32 gradients, root
+ * iterations, preconditioning) run on the matrix cores. */
+typedef enum {
+  SHAMPOO_GEMM_F32 = 0,        /* fp32 MFMA (32x32x2)                           */
+  SHAMPOO_GEMM_SPLIT_BF16 = 1  /* each fp32 operand split exactly into three
+                                  bf16 terms x = h + m + l; the six products
+                                  hh, hm, mh, hl, mm, lh on the bf16 MFMA
+                                  (32x32x16), each exact in fp32, accumulated
+                                  in fp32: the dropped terms are below 2^-24
+                                  of |x y|, so the result has fp32 accuracy,
+                                  at 6/16 of the fp32 MFMA time (default)    */
+} shampoo_fp32_gemm_t;
+
 /* Flags of shampoo_step. */
 enum {
   SHAMPOO_FORCE_REFRESH = 1u,   /* recompute roots this step whatever the schedule */
@@ -139,6 +152,11 @@ typedef struct {
                                         Clenshaw recurrence: cheb_degree - 1
                                         products, no iteration, no early exit    */
   int32_t cheb_degree;            /* 2..1024, default 128                        */
+  int32_t fp32_gemm;              /* shampoo_fp32_gemm_t; default
+                                     SHAMPOO_GEMM_SPLIT_BF16. Statistics of bf16
+                                     gradients always take the bf16 MFMA
+                                     directly; the tensor handles' statistics
+                                     and mode products stay on the fp32 MFMA  */
 } shampoo_config_t;
 
 /* Byte offsets of the state inside the caller's workspace (for inspection

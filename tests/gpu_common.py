@@ -38,7 +38,8 @@ def make_shampoo(w):
     return Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
                    root_every=w.root_every, newton_max_iters=w.newton_max_iters,
                    newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype,
-                   momentum=w.momentum, root_method=w.root_method, cheb_degree=w.cheb_degree)
+                   momentum=w.momentum, root_method=w.root_method, cheb_degree=w.cheb_degree,
+                   fp32_gemm=w.fp32_gemm)
 
 
 def sample_blocks(w, k, seed=0):

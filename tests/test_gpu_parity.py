@@ -512,3 +512,25 @@ def test_largest_block_4096():
     st, _, _ = sh.newton_info()
     assert set(st.cpu().tolist()) <= {1, 2}
     sh.close()
+
+
+@pytest.mark.parametrize("gemm", ["f32", "split"])
+@pytest.mark.parametrize("block,shapes", [
+    ((256, 256), ((300, 520), (256, 256), (130, 71))),   # 128-tiles, ragged tails
+    ((128, 64), ((200, 130), (64, 100))),                # 64-tiles
+    ((64, 32), ((70, 45), (32, 32))),                    # 32-tiles
+])
+def test_fp32_gemm_paths_every_block(gemm, block, shapes):
+    """Both product paths (fp32 MFMA; fp32 operands split into three bf16
+    terms) on every tile size, with and without momentum (the split apply
+    reads the preconditioned matrix by columns): every block at every step."""
+    for momentum in (0.0, 0.9):
+        w = workload("gpt_small_b256", shapes=shapes, block_rows=block[0], block_cols=block[1],
+                     root_every=2, steps=4, seed=31, fp32_gemm=gemm, momentum=momentum)
+        log(f"gemm path {gemm} block {block} momentum {momentum}")
+        recs, sh, orc, params, W = run_parity(w, 4)
+        for r in recs:
+            assert r.stats_err <= STATS_TOL, r
+            assert r.update_err <= UPDATE_TOL, r
+        assert sh.n_diverged() == 0
+        sh.close()

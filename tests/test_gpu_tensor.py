@@ -52,7 +52,7 @@ def make(w, **over):
     kw = dict(beta2=w.beta2, eps=w.eps, lr=w.lr, root_every=w.root_every,
               newton_max_iters=w.newton_max_iters, newton_tol=w.newton_tol,
               newton_scale_mode=w.newton_scale_mode, dtype=w.dtype, momentum=w.momentum,
-              root_method=w.root_method, cheb_degree=w.cheb_degree)
+              root_method=w.root_method, cheb_degree=w.cheb_degree, fp32_gemm=w.fp32_gemm)
     kw.update(over)
     return S.TensorShampoo(w.shapes, w.block_dims, **kw)
 
@@ -232,4 +232,16 @@ def test_tensor_empty_and_zero_tensors():
     torch.cuda.synchronize()
     assert torch.isfinite(params[0]).all() and params[0].abs().sum() > 0
     assert torch.isfinite(params[2]).all() and params[2].abs().sum() > 0
+    sh.close()
+
+
+@pytest.mark.parametrize("gemm", ["f32", "split"])
+def test_tensor_fp32_gemm_paths(gemm):
+    """The root iterations on either product path (the tensor statistics and
+    mode products take the fp32 MFMA on both)."""
+    w = dataclasses.replace(CASES["conv4_64x32"], fp32_gemm=gemm)
+    log(f"tensor gemm path {gemm}")
+    s, u, wp, sh, _ = run_tensor_parity(w, 3)
+    assert s <= STATS_TOL and u <= UPDATE_TOL and wp <= UPDATE_TOL, (s, u, wp)
+    assert sh.n_diverged() == 0
     sh.close()
