@@ -64,6 +64,9 @@ struct Cfg {
 using Cfg128 = Cfg<2, 2, 2, 2>;  // 128 x 128, 256 threads
 using Cfg64 = Cfg<2, 2, 1, 1>;   //  64 x  64, 256 threads
 using Cfg32 = Cfg<1, 1, 1, 1>;   //  32 x  32,  64 threads
+// 256 x 256, 512 threads (8 waves of 128 x 64): split-path full products
+// only; its LDS (147 KiB) allows one workgroup per CU
+using Cfg256 = Cfg<2, 4, 4, 2>;
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on
 // XCD w % 8). xcd_remap gives every XCD a contiguous range of logical tiles so
@@ -1534,7 +1537,7 @@ void launch_full_cfg(const GemmLaunch& g, int mode, bool qcols, hipStream_t s) {
     hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, true>), grid, block, 0, s, g);
   else if (mode == kGemmSplit)
     hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, false>), grid, block, 0, s, g);
-  else
+  else if constexpr (CFG::BM <= 128)
     hipLaunchKernelGGL((apply_left_kernel<CFG, kPathF32, false>), grid, block, 0, s, g);
 }
 template <class CFG>
@@ -1543,7 +1546,7 @@ void launch_update_cfg(const GemmLaunch& g, const UpdateArgs& u, int mode, hipSt
   if (!gx) return;
   if (mode == kGemmSplit)
     hipLaunchKernelGGL((apply_update_kernel<CFG, kPathSplit>), dim3(gx), dim3(CFG::NT), 0, s, g, u);
-  else
+  else if constexpr (CFG::BM <= 128)
     hipLaunchKernelGGL((apply_update_kernel<CFG, kPathF32>), dim3(gx), dim3(CFG::NT), 0, s, g, u);
 }
 }  // namespace
@@ -1555,7 +1558,9 @@ hipError_t launch_gemm_full(const GemmLaunch& g, int tile, int mode, hipStream_t
   for (int i = 1; i < g.n_problems; ++i)
     if ((g.p[i].q_cols != 0) != qcols) return hipErrorInvalidValue;
   if (qcols && mode != kGemmSplit) return hipErrorInvalidValue;
+  if (tile == 256 && mode != kGemmSplit) return hipErrorInvalidValue;
   switch (tile) {
+    case 256: launch_full_cfg<Cfg256>(g, mode, qcols, s); break;
     case 128: launch_full_cfg<Cfg128>(g, mode, qcols, s); break;
     case 64: launch_full_cfg<Cfg64>(g, mode, qcols, s); break;
     case 32: launch_full_cfg<Cfg32>(g, mode, qcols, s); break;
@@ -1568,7 +1573,9 @@ hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile
                               hipStream_t s) {
   if (g.n_problems != 1 || g.p[0].q_cols != 0) return hipErrorInvalidValue;
   if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
+  if (tile == 256 && mode != kGemmSplit) return hipErrorInvalidValue;
   switch (tile) {
+    case 256: launch_update_cfg<Cfg256>(g, u, mode, s); break;
     case 128: launch_update_cfg<Cfg128>(g, u, mode, s); break;
     case 64: launch_update_cfg<Cfg64>(g, u, mode, s); break;
     case 32: launch_update_cfg<Cfg32>(g, u, mode, s); break;

@@ -426,10 +426,13 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
     f2 += 2.0 * bl.m * (double)bl.n * bl.n;
   }
   const int mode = h->cfg.fp32_gemm;
-  int rc = timed(h, kApply, f1, 0.0, s, [&] { return shp::launch_gemm_full(g1, p.tile, mode, s); });
+  // split path: 256 x 256 tiles when both block sides allow them (half the
+  // operand traffic of 128 x 128 tiles per flop)
+  const int tile = split && p.br % 256 == 0 && p.bc % 256 == 0 ? 256 : p.tile;
+  int rc = timed(h, kApply, f1, 0.0, s, [&] { return shp::launch_gemm_full(g1, tile, mode, s); });
   if (rc) return rc;
   return timed(h, kApply, f2, 0.0, s,
-               [&] { return shp::launch_gemm_update(g2, u, p.tile, mode, s); });
+               [&] { return shp::launch_gemm_update(g2, u, tile, mode, s); });
 }
 
 }  // namespace

@@ -517,13 +517,15 @@ def test_largest_block_4096():
 @pytest.mark.parametrize("gemm", ["f32", "split"])
 @pytest.mark.parametrize("block,shapes", [
     ((256, 256), ((300, 520), (256, 256), (130, 71))),   # 128-tiles, ragged tails
+    ((512, 256), ((600, 300), (512, 256))),              # split apply on 256-tiles, 2 x 1
     ((128, 64), ((200, 130), (64, 100))),                # 64-tiles
     ((64, 32), ((70, 45), (32, 32))),                    # 32-tiles
 ])
 def test_fp32_gemm_paths_every_block(gemm, block, shapes):
     """Both product paths (fp32 MFMA; fp32 operands split into three bf16
-    terms) on every tile size, with and without momentum (the split apply
-    reads the preconditioned matrix by columns): every block at every step."""
+    terms) on every tile size (the split apply takes 256-tiles when both
+    block sides allow), with and without momentum (the split apply reads the
+    preconditioned matrix by columns): every block at every step."""
     for momentum in (0.0, 0.9):
         w = workload("gpt_small_b256", shapes=shapes, block_rows=block[0], block_cols=block[1],
                      root_every=2, steps=4, seed=31, fp32_gemm=gemm, momentum=momentum)
