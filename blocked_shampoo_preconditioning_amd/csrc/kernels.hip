@@ -640,16 +640,31 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
     for (int j = 0; j < C::FN; ++j) {
       if (!((sw.mask >> (i * C::FN + j)) & 1)) continue;  // wave-uniform
       const int col = frag_col_w<C>(n0, sw.wn, j);
+      // The affine terms of HOIST registers are loaded before their stores:
+      // the stores may alias them as far as the compiler knows (the
+      // statistics update in place), which would otherwise hold every load
+      // behind the store before it. No store below targets an element another
+      // lane reads here. The split path has the registers for all 16.
+      constexpr int HOIST = PATH == kPathSplit ? 16 : 4;
+      float dv[HOIST], d2v[HOIST];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
+        if ((4 * g4) % HOIST == 0) {
+#pragma unroll
+          for (int r = 0; r < HOIST; ++r) {
+            const size_t o = (size_t)frag_row_w<C>(m0, sw.wm, i, 4 * g4 + r) * N + col;
+            dv[r] = Db != nullptr ? Db[o] : 0.f;
+            d2v[r] = D2b != nullptr ? D2b[o] : 0.f;
+          }
+        }
         const int row0 = frag_row_w<C>(m0, sw.wm, i, 4 * g4);
         f32x4 v;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = row0 + q;
           float x = e_alpha * acc[i][j][4 * g4 + q];
-          if (Db != nullptr) x += e_beta * Db[(size_t)row * N + col];
-          if (D2b != nullptr) x += e_beta2 * D2b[(size_t)row * N + col];
+          x += e_beta * dv[(4 * g4 + q) % HOIST];
+          x += e_beta2 * d2v[(4 * g4 + q) % HOIST];
           if (row == col) x += e_gamma;
           v[q] = x;
           if (!diag || row <= col) {
@@ -784,23 +799,49 @@ __global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void apply_updat
   const BlockMeta bm = u.blocks[f];
   const MatMeta mm = u.mats[bm.mat];
   const float lr = u.lr;
+  // Per fragment: the parameters are loaded first, then updated and stored
+  // (loads interleaved with stores to the same array would each wait for the
+  // store before them).
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const int col = frag_col<C>(n0, j);
       if (col >= bm.n) continue;
+      const size_t base = (size_t)bm.r0 * mm.ld + bm.c0 + col;
+      constexpr int HOIST = PATH == kPathSplit ? 16 : 4;  // registers per batch
+      if (u.param_bf16) {
+        uint16_t* w = reinterpret_cast<uint16_t*>(mm.param) + base;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = frag_row<C>(m0, i, r);
-        if (row >= bm.m) continue;
-        const size_t off = (size_t)(bm.r0 + row) * mm.ld + bm.c0 + col;
-        if (u.param_bf16) {
-          uint16_t* w = reinterpret_cast<uint16_t*>(mm.param) + off;
-          *w = f32_to_bf16(bf16_to_f32(*w) - lr * acc[i][j][r]);
-        } else {
-          float* w = reinterpret_cast<float*>(mm.param) + off;
-          *w = *w - lr * acc[i][j][r];
+        for (int r0 = 0; r0 < 16; r0 += HOIST) {
+          uint16_t wv[HOIST];
+#pragma unroll
+          for (int r = 0; r < HOIST; ++r) {
+            const int row = frag_row<C>(m0, i, r0 + r);
+            wv[r] = row < bm.m ? w[(size_t)row * mm.ld] : (uint16_t)0;
+          }
+#pragma unroll
+          for (int r = 0; r < HOIST; ++r) {
+            const int row = frag_row<C>(m0, i, r0 + r);
+            if (row < bm.m)
+              w[(size_t)row * mm.ld] = f32_to_bf16(bf16_to_f32(wv[r]) - lr * acc[i][j][r0 + r]);
+          }
+        }
+      } else {
+        float* w = reinterpret_cast<float*>(mm.param) + base;
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += HOIST) {
+          float wv[HOIST];
+#pragma unroll
+          for (int r = 0; r < HOIST; ++r) {
+            const int row = frag_row<C>(m0, i, r0 + r);
+            wv[r] = row < bm.m ? w[(size_t)row * mm.ld] : 0.f;
+          }
+#pragma unroll
+          for (int r = 0; r < HOIST; ++r) {
+            const int row = frag_row<C>(m0, i, r0 + r);
+            if (row < bm.m) w[(size_t)row * mm.ld] = wv[r] - lr * acc[i][j][r0 + r];
+          }
         }
       }
     }
