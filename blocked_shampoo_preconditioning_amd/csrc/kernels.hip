@@ -312,6 +312,16 @@ __device__ __forceinline__ Split3 split3(float x0, float x1) {
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// Row of 4-value chunk c of a split operand tile (its chunk within the row is
+// c % 4). The 16 lanes of one 128-byte LDS write group take rows {0, 2, 4, 6}
+// (odd groups {1, 3, 5, 7}) of an 8-row band: at the 48-byte row pitch their
+// 32-byte segments start 24 banks apart (mod 32), so the group covers all 32
+// banks once. Consecutive rows would put rows 0 and 3 on the same banks.
+__device__ __forceinline__ int split_row(int c) {
+  const int g = c >> 4, w = c & 15;
+  return (g >> 1) * 8 + ((w >> 2) << 1) + (g & 1);
+}
+
 // Three planes of 4 consecutive k of one row.
 __device__ __forceinline__ void store_split4(uint16_t* d, int plane, const f32x4& v) {
   const Split3 a = split3(v[0], v[1]), b = split3(v[2], v[3]);
@@ -352,6 +362,7 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
   // KC consecutive k of it
   constexpr int NA = C::BM * 4 / C::NT, NB = C::BN * 4 / C::NT;
   constexpr int KC = 16 * C::BN / C::NT;
+  static_assert(C::BM % 8 == 0 && C::BN % 8 == 0, "split_row maps 8-row bands");
   static_assert(NA >= 1 && NB >= 1 && (C::BM * 4) % C::NT == 0 && (C::BN * 4) % C::NT == 0,
                 "uneven operand load");
   static_assert(!QCOLS || (C::NT % C::BN == 0 && (KC == 4 || KC == 8)), "column load shape");
@@ -369,7 +380,7 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         const int c = tid + i * C::NT;
-        ra[i] = *reinterpret_cast<const f32x4*>(A + (size_t)(m0 + c / 4) * lda + k0 + (c % 4) * 4);
+        ra[i] = *reinterpret_cast<const f32x4*>(A + (size_t)(m0 + split_row(c)) * lda + k0 + (c % 4) * 4);
       }
       if constexpr (QCOLS) {
 #pragma unroll
@@ -378,7 +389,7 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int c = tid + i * C::NT;
-          rb[i] = *reinterpret_cast<const f32x4*>(B + (size_t)(n0 + c / 4) * ldb + k0 + (c % 4) * 4);
+          rb[i] = *reinterpret_cast<const f32x4*>(B + (size_t)(n0 + split_row(c)) * ldb + k0 + (c % 4) * 4);
         }
       }
     }
@@ -414,18 +425,26 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         const int c = tid + i * C::NT;
-        store_split4(dA + (c / 4) * LD + (c % 4) * 4, PA, ra[i]);
+        store_split4(dA + split_row(c) * LD + (c % 4) * 4, PA, ra[i]);
       }
       if constexpr (QCOLS) {
         uint16_t* d = dB + bc_row * LD + bc_k;
-#pragma unroll
-        for (int q = 0; q < KC; q += 4)
-          store_split4(d + q, PB, (f32x4){rc[q], rc[q + 1], rc[q + 2], rc[q + 3]});
+        if constexpr (KC == 8) {
+          // 16-byte writes: eight consecutive rows per 128-byte group, 12
+          // banks apart, cover all 32 banks once
+          const Split3 s0 = split3(rc[0], rc[1]), s1 = split3(rc[2], rc[3]);
+          const Split3 s2 = split3(rc[4], rc[5]), s3 = split3(rc[6], rc[7]);
+          *reinterpret_cast<u32x4*>(d) = (u32x4){s0.h, s1.h, s2.h, s3.h};
+          *reinterpret_cast<u32x4*>(d + PB) = (u32x4){s0.m, s1.m, s2.m, s3.m};
+          *reinterpret_cast<u32x4*>(d + 2 * PB) = (u32x4){s0.l, s1.l, s2.l, s3.l};
+        } else {
+          store_split4(d, PB, (f32x4){rc[0], rc[1], rc[2], rc[3]});
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int c = tid + i * C::NT;
-          store_split4(dB + (c / 4) * LD + (c % 4) * 4, PB, rb[i]);
+          store_split4(dB + split_row(c) * LD + (c % 4) * 4, PB, rb[i]);
         }
       }
     }

@@ -536,3 +536,38 @@ def test_fp32_gemm_paths_every_block(gemm, block, shapes):
             assert r.update_err <= UPDATE_TOL, r
         assert sh.n_diverged() == 0
         sh.close()
+
+
+def test_split_products_have_fp32_accuracy():
+    """One step with roots on both product paths, same gradients (rows scaled
+    over two decades, so the statistics span four): the statistics against
+    the fp64 oracle, and the preconditioned update against X_L G X_R formed
+    in fp64 from the GPU's own roots, so only the products' rounding is
+    measured. The split path (three bf16 terms per operand, six products)
+    must be as accurate as the fp32 MFMA, within a factor 2. (The update's
+    two products lose a few ulps to the roots' conditioning on either path:
+    about 3e-6 here, against 3e-7 for the statistics.)"""
+    errs = {}
+    for gemm in ("f32", "split"):
+        w = workload("gpt_small_b256", shapes=((512, 384), (300, 256)), block_rows=256,
+                     block_cols=256, root_every=1, steps=1, seed=41, eps=1e-10, grad_std=1.0,
+                     fp32_gemm=gemm)
+        table = block_table(w.shapes, w.block_rows, w.block_cols)
+        recs, sh, orc, params, W = run_parity(w, 1)
+        grads = synth.GradientSource(w, device="cuda").grads(1)
+        U_out = torch.empty(sh.n_blocks * 256 * 256, dtype=torch.float32, device="cuda")
+        sh.precondition(U_out)
+        torch.cuda.synchronize()
+        Ug = U_out.view(sh.n_blocks, 256, 256).cpu().numpy().astype(np.float64)
+        XL, XR = [x.cpu().numpy().astype(np.float64) for x in sh.roots()]
+        ue = 0.0
+        for b in table:
+            G = block_of(grads[b.mat], b)
+            ref = XL[b.id, :b.m, :b.m] @ G @ XR[b.id, :b.n, :b.n]
+            ue = max(ue, rel(Ug[b.id, :b.m, :b.n], ref))
+        errs[gemm] = (recs[0].stats_err, ue)
+        log(f"  {gemm}: statistics {recs[0].stats_err:.2e} products of the update {ue:.2e}")
+        sh.close()
+    (s32, u32), (ssp, usp) = errs["f32"], errs["split"]
+    assert ssp <= 1e-6 and usp <= 2e-5, errs
+    assert ssp <= 2 * s32 + 1e-7 and usp <= 2 * u32 + 1e-7, errs
