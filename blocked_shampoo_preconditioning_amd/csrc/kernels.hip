@@ -330,124 +330,155 @@ __device__ __forceinline__ void store_split4(uint16_t* d, int plane, const f32x4
   *reinterpret_cast<u32x2*>(d + 2 * plane) = (u32x2){a.l, b.l};
 }
 
+// One thread's share of a split operand K-tile (16 wide) in registers: 4-value
+// chunks of A and B rows, or for QCOLS KC consecutive k of one column of B.
+template <class C, bool QCOLS>
+struct SplitStage {
+  static constexpr int NA = C::BM * 4 / C::NT, NB = C::BN * 4 / C::NT;
+  static constexpr int KC = 16 * C::BN / C::NT;
+  f32x4 ra[NA];
+  f32x4 rb[QCOLS ? 1 : NB];
+  float rc[QCOLS ? KC : 1];
+};
+
+template <class C, bool QCOLS>
+__device__ __forceinline__ void split_load(SplitStage<C, QCOLS>& st, const float* __restrict__ A,
+                                           int lda, const float* __restrict__ B, int ldb, int m0,
+                                           int n0, int k0) {
+  using S = SplitStage<C, QCOLS>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < S::NA; ++i) {
+    const int c = tid + i * C::NT;
+    st.ra[i] = *reinterpret_cast<const f32x4*>(A + (size_t)(m0 + split_row(c)) * lda + k0 + (c % 4) * 4);
+  }
+  if constexpr (QCOLS) {
+    const int row = tid % C::BN, kq = (tid / C::BN) * S::KC;
+#pragma unroll
+    for (int q = 0; q < S::KC; ++q) st.rc[q] = B[(size_t)(k0 + kq + q) * ldb + n0 + row];
+  } else {
+#pragma unroll
+    for (int i = 0; i < S::NB; ++i) {
+      const int c = tid + i * C::NT;
+      st.rb[i] = *reinterpret_cast<const f32x4*>(B + (size_t)(n0 + split_row(c)) * ldb + k0 + (c % 4) * 4);
+    }
+  }
+}
+
+// Splits a stage into the three planes of one LDS buffer ([plane][row][k],
+// rows of LDX, A then B).
+template <class C, bool QCOLS>
+__device__ __forceinline__ void split_store(const SplitStage<C, QCOLS>& st, uint16_t* dA,
+                                            uint16_t* dB) {
+  using S = SplitStage<C, QCOLS>;
+  constexpr int LD = C::LDX, PA = C::BM * LD, PB = C::BN * LD;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < S::NA; ++i) {
+    const int c = tid + i * C::NT;
+    store_split4(dA + split_row(c) * LD + (c % 4) * 4, PA, st.ra[i]);
+  }
+  if constexpr (QCOLS) {
+    uint16_t* d = dB + (tid % C::BN) * LD + (tid / C::BN) * S::KC;
+    if constexpr (S::KC == 8) {
+      // 16-byte writes: eight consecutive rows per 128-byte group, 12 banks
+      // apart, cover all 32 banks once
+      const Split3 s0 = split3(st.rc[0], st.rc[1]), s1 = split3(st.rc[2], st.rc[3]);
+      const Split3 s2 = split3(st.rc[4], st.rc[5]), s3 = split3(st.rc[6], st.rc[7]);
+      *reinterpret_cast<u32x4*>(d) = (u32x4){s0.h, s1.h, s2.h, s3.h};
+      *reinterpret_cast<u32x4*>(d + PB) = (u32x4){s0.m, s1.m, s2.m, s3.m};
+      *reinterpret_cast<u32x4*>(d + 2 * PB) = (u32x4){s0.l, s1.l, s2.l, s3.l};
+    } else {
+      store_split4(d, PB, (f32x4){st.rc[0], st.rc[1], st.rc[2], st.rc[3]});
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < S::NB; ++i) {
+      const int c = tid + i * C::NT;
+      store_split4(dB + split_row(c) * LD + (c % 4) * 4, PB, st.rb[i]);
+    }
+  }
+}
+
+// The six products of one K-tile from one LDS buffer: per fragment the wave
+// reads 8 consecutive k of one row from every plane (lane l: row l % 32,
+// k 8 (l / 32) + 0..7, the 32x32x16 bf16 MFMA's operand layout for both A and
+// B), then runs the products product-major (smallest terms first), so
+// consecutive MFMAs go to different accumulators.
+template <class C, int MASK>
+__device__ __forceinline__ void split_mma(floatx16 (&acc)[C::FM][C::FN], const uint16_t* sA,
+                                          const uint16_t* sB, int wm, int wn) {
+  constexpr int LD = C::LDX, PA = C::BM * LD, PB = C::BN * LD;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const uint16_t* a0 = sA + (wm * 32 * C::FM + l32) * LD + half * 8;
+  const uint16_t* b0 = sB + (wn * 32 * C::FN + l32) * LD + half * 8;
+  bf16x8 a[3][C::FM], b[3][C::FN];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) a[p][i] = *reinterpret_cast<const bf16x8*>(a0 + p * PA + i * 32 * LD);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) b[p][j] = *reinterpret_cast<const bf16x8*>(b0 + p * PB + j * 32 * LD);
+  }
+  constexpr int PP[6][2] = {{2, 0}, {1, 1}, {0, 2}, {1, 0}, {0, 1}, {0, 0}};
+#pragma unroll
+  for (int q = 0; q < 6; ++q)
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        if (MASK & (1 << (i * C::FN + j)))
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PP[q][0]][i], b[PP[q][1]][j],
+                                                              acc[i][j], 0, 0, 0);
+}
+
 // acc[fm][fn] = sum over K of A[m0 + ...][k] * B[n0 + ...][k]: A is [M][K]
 // with row stride lda (k contiguous); B likewise [N][K] with row stride ldb,
-// or with QCOLS its transpose [K][N] (row stride ldb, n contiguous). One
-// K-tile of 16: every thread loads its share of both operands as fp32,
-// splits it and stores the three bf16 planes ([plane][row][k], rows of
-// LDX); each wave reads, per fragment, 8 consecutive k of one row from every
-// plane (lane l: row l % 32, k 8 (l / 32) + 0..7, the 32x32x16 bf16 MFMA's
-// operand layout for both A and B) and runs the six products. The next
-// K-tile's global loads are in flight during the MFMAs and are split into
-// the other LDS buffer after them, as in mainloop_w.
+// or with QCOLS its transpose [K][N] (row stride ldb, n contiguous). K is a
+// multiple of 32. Two LDS buffers of split planes and two register stages:
+// while the MFMAs run on K-tile kt, the stage of tile kt + 1 (loaded one
+// phase earlier) is split into the other buffer and tile kt + 2 is loaded
+// into the freed stage, so every load has a full phase to land.
 template <class C, bool QCOLS, int MASK = -1>
 __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda,
                                             const float* __restrict__ B, int ldb, int K, int m0,
                                             int n0, int wm, int wn,
                                             floatx16 (&acc)[C::FM][C::FN], float* lds) {
-  constexpr int LD = C::LDX;
-  constexpr int PA = C::BM * LD, PB = C::BN * LD;  // one plane, in bf16
-  uint16_t* sA = reinterpret_cast<uint16_t*>(lds);  // [2][3][BM][LD]
-  uint16_t* sB = sA + 2 * 3 * PA;                    // [2][3][BN][LD]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int half = lane >> 5, l32 = lane & 31;
+  using S = SplitStage<C, QCOLS>;
+  constexpr int PA = C::BM * C::LDX, PB = C::BN * C::LDX;  // one plane, in bf16
+  static_assert(C::BM % 8 == 0 && C::BN % 8 == 0, "split_row maps 8-row bands");
+  static_assert(S::NA >= 1 && S::NB >= 1 && (C::BM * 4) % C::NT == 0 && (C::BN * 4) % C::NT == 0,
+                "uneven operand load");
+  static_assert(!QCOLS || (C::NT % C::BN == 0 && (S::KC == 4 || S::KC == 8)), "column load shape");
+  uint16_t* sA0 = reinterpret_cast<uint16_t*>(lds);  // [2][3][BM][LDX]
+  uint16_t* sA1 = sA0 + 3 * PA;
+  uint16_t* sB0 = sA0 + 2 * 3 * PA;                   // [2][3][BN][LDX]
+  uint16_t* sB1 = sB0 + 3 * PB;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // rows: 4-value chunks, 4 per row; columns: one row of B^T per thread,
-  // KC consecutive k of it
-  constexpr int NA = C::BM * 4 / C::NT, NB = C::BN * 4 / C::NT;
-  constexpr int KC = 16 * C::BN / C::NT;
-  static_assert(C::BM % 8 == 0 && C::BN % 8 == 0, "split_row maps 8-row bands");
-  static_assert(NA >= 1 && NB >= 1 && (C::BM * 4) % C::NT == 0 && (C::BN * 4) % C::NT == 0,
-                "uneven operand load");
-  static_assert(!QCOLS || (C::NT % C::BN == 0 && (KC == 4 || KC == 8)), "column load shape");
-  const int bc_row = tid % C::BN, bc_k = (tid / C::BN) * KC;
-  f32x4 ra[NA];
-  f32x4 rb[QCOLS ? 1 : NB];
-  float rc[QCOLS ? KC : 1];
-  const int nk = K / 16;
-  for (int kt = -1; kt < nk; ++kt) {
-    // kt = -1 only stages K-tile 0
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = (kt + 1) * 16;
-#pragma unroll
-      for (int i = 0; i < NA; ++i) {
-        const int c = tid + i * C::NT;
-        ra[i] = *reinterpret_cast<const f32x4*>(A + (size_t)(m0 + split_row(c)) * lda + k0 + (c % 4) * 4);
-      }
-      if constexpr (QCOLS) {
-#pragma unroll
-        for (int q = 0; q < KC; ++q) rc[q] = B[(size_t)(k0 + bc_k + q) * ldb + n0 + bc_row];
-      } else {
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          const int c = tid + i * C::NT;
-          rb[i] = *reinterpret_cast<const f32x4*>(B + (size_t)(n0 + split_row(c)) * ldb + k0 + (c % 4) * 4);
-        }
-      }
-    }
-    if (kt >= 0) {
-      const uint16_t* a0 = sA + buf * 3 * PA + (wm * 32 * C::FM + l32) * LD + half * 8;
-      const uint16_t* b0 = sB + buf * 3 * PB + (wn * 32 * C::FN + l32) * LD + half * 8;
-      bf16x8 a[3][C::FM], b[3][C::FN];
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-          a[p][i] = *reinterpret_cast<const bf16x8*>(a0 + p * PA + i * 32 * LD);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          b[p][j] = *reinterpret_cast<const bf16x8*>(b0 + p * PB + j * 32 * LD);
-      }
-      // (plane of A, plane of B), smallest terms first; consecutive MFMAs
-      // go to different accumulators
-      constexpr int PP[6][2] = {{2, 0}, {1, 1}, {0, 2}, {1, 0}, {0, 1}, {0, 0}};
-#pragma unroll
-      for (int q = 0; q < 6; ++q)
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j)
-            if (MASK & (1 << (i * C::FN + j)))
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PP[q][0]][i], b[PP[q][1]][j],
-                                                                  acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      uint16_t* dA = sA + (buf ^ 1) * 3 * PA;
-      uint16_t* dB = sB + (buf ^ 1) * 3 * PB;
-#pragma unroll
-      for (int i = 0; i < NA; ++i) {
-        const int c = tid + i * C::NT;
-        store_split4(dA + split_row(c) * LD + (c % 4) * 4, PA, ra[i]);
-      }
-      if constexpr (QCOLS) {
-        uint16_t* d = dB + bc_row * LD + bc_k;
-        if constexpr (KC == 8) {
-          // 16-byte writes: eight consecutive rows per 128-byte group, 12
-          // banks apart, cover all 32 banks once
-          const Split3 s0 = split3(rc[0], rc[1]), s1 = split3(rc[2], rc[3]);
-          const Split3 s2 = split3(rc[4], rc[5]), s3 = split3(rc[6], rc[7]);
-          *reinterpret_cast<u32x4*>(d) = (u32x4){s0.h, s1.h, s2.h, s3.h};
-          *reinterpret_cast<u32x4*>(d + PB) = (u32x4){s0.m, s1.m, s2.m, s3.m};
-          *reinterpret_cast<u32x4*>(d + 2 * PB) = (u32x4){s0.l, s1.l, s2.l, s3.l};
-        } else {
-          store_split4(d, PB, (f32x4){rc[0], rc[1], rc[2], rc[3]});
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          const int c = tid + i * C::NT;
-          store_split4(dB + split_row(c) * LD + (c % 4) * 4, PB, rb[i]);
-        }
-      }
-    }
+  const int nk = K / 16;  // even
+  S s0, s1;
+  split_load<C, QCOLS>(s0, A, lda, B, ldb, m0, n0, 0);
+  split_load<C, QCOLS>(s1, A, lda, B, ldb, m0, n0, 16);
+  split_store<C, QCOLS>(s0, sA0, sB0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    // tile kt from buffer 0; tile kt + 1 (s1) into buffer 1; tile kt + 2
+    // into s0 (the last pair repeats tile nk - 1, in bounds and unused)
+    split_load<C, QCOLS>(s0, A, lda, B, ldb, m0, n0, min(kt + 2, nk - 1) * 16);
+    split_mma<C, MASK>(acc, sA0, sB0, wm, wn);
+    split_store<C, QCOLS>(s1, sA1, sB1);
+    __syncthreads();
+    // tile kt + 1 from buffer 1; tile kt + 2 (s0) into buffer 0; tile kt + 3
+    // into s1
+    split_load<C, QCOLS>(s1, A, lda, B, ldb, m0, n0, min(kt + 3, nk - 1) * 16);
+    split_mma<C, MASK>(acc, sA1, sB1, wm, wn);
+    if (kt + 2 < nk) split_store<C, QCOLS>(s0, sA0, sB0);
     __syncthreads();
   }
 }
@@ -1536,9 +1567,17 @@ hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nele
   return hipGetLastError();
 }
 
+// The split main loop runs K-tiles of 16 in pairs.
+bool split_k_ok(const GemmLaunch& g) {
+  for (int i = 0; i < g.n_problems; ++i)
+    if (g.p[i].K % 32 != 0) return false;
+  return true;
+}
+
 hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode, hipStream_t s) {
   if (g.n_problems == 0) return hipSuccess;
   if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
+  if (mode == kGemmSplit && !split_k_ok(g)) return hipErrorInvalidValue;
   switch (tile) {
 #define SHP_SYM_LAUNCH(CFG, PATH)                                                              \
   if (newton)                                                                                  \
@@ -1618,6 +1657,7 @@ hipError_t launch_gemm_full(const GemmLaunch& g, int tile, int mode, hipStream_t
   for (int i = 1; i < g.n_problems; ++i)
     if ((g.p[i].q_cols != 0) != qcols) return hipErrorInvalidValue;
   if (qcols && mode != kGemmSplit) return hipErrorInvalidValue;
+  if (mode == kGemmSplit && !split_k_ok(g)) return hipErrorInvalidValue;
   if (tile == 256 && mode != kGemmSplit) return hipErrorInvalidValue;
   switch (tile) {
     case 256: launch_full_cfg<Cfg256>(g, mode, qcols, s); break;
@@ -1633,6 +1673,7 @@ hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile
                               hipStream_t s) {
   if (g.n_problems != 1 || g.p[0].q_cols != 0) return hipErrorInvalidValue;
   if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
+  if (mode == kGemmSplit && !split_k_ok(g)) return hipErrorInvalidValue;
   if (tile == 256 && mode != kGemmSplit) return hipErrorInvalidValue;
   switch (tile) {
     case 256: launch_update_cfg<Cfg256>(g, u, mode, s); break;
