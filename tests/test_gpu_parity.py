@@ -571,3 +571,28 @@ def test_split_products_have_fp32_accuracy():
     (s32, u32), (ssp, usp) = errs["f32"], errs["split"]
     assert ssp <= 1e-6 and usp <= 2e-5, errs
     assert ssp <= 2 * s32 + 1e-7 and usp <= 2 * u32 + 1e-7, errs
+
+
+@pytest.mark.parametrize("gemm", ["f32", "split"])
+def test_statistics_scale_exactly_with_powers_of_two(gemm):
+    """Gradients scaled by 2^k give statistics scaled by exactly 4^k, bit for
+    bit: every bf16 term of the split scales exactly, as does every fp32
+    product and sum (eps = 1e-30 vanishes in the rounding of the diagonal).
+    A wrong exponent, sign or remainder bit in the split breaks the
+    equality. Full 256-blocks (a padded tail keeps eps on its diagonal, which
+    does not scale), 128-tiles, three steps; roots at the first step only."""
+    shapes = ((512, 256), (256, 512))
+    stats = {}
+    for k in (0, 20, -20):
+        sh = S.Shampoo(shapes, 256, 256, eps=1e-30, root_every=1000, fp32_gemm=gemm)
+        gen = torch.Generator(device="cuda").manual_seed(3)
+        params = [torch.zeros(s, device="cuda") for s in shapes]
+        for t in range(3):
+            grads = [torch.randn(s, generator=gen, device="cuda") * 1e-2 * 2.0 ** k for s in shapes]
+            sh.step(params, grads)
+        torch.cuda.synchronize()
+        stats[k] = [x.clone() for x in sh.stats()]
+        sh.close()
+    for k in (20, -20):
+        for a, b in zip(stats[k], stats[0]):
+            assert torch.equal(a, b * 4.0 ** k), (gemm, k, float((a - b * 4.0 ** k).abs().max()))
