@@ -408,6 +408,8 @@ def main():
         "launches": nw["launches"],
         "flops_per_launch": nw["flops"] / max(1, nw["launches"]),
         "avg_launch_ms": nw["ms"] / max(1, nw["launches"]),
+        # the same fp32 flops against the fp32 MFMA, for comparison with the other path
+        "frac_of_fp32_mfma_peak": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
     }
     cpu = None
     if not args.no_cpu_baseline:
