@@ -219,9 +219,9 @@ def run_tensor(args, w, torch, S, synth):
     tm = sh.timing()
     sh.set_timing(False)
     n_div = sh.n_diverged()
-    # the tensor statistics and mode products take the fp32 MFMA; the root
-    # products the configured path
-    paths = {"stats": "f32", "apply": "f32", "newton_gemm": w.fp32_gemm}
+    # statistics (of dimensions whose unfolding pads to a multiple of 32),
+    # MFMA mode products and roots all take the configured path
+    paths = {"stats": w.fp32_gemm, "apply": w.fp32_gemm, "newton_gemm": w.fp32_gemm}
     kernels = class_table(tm, paths)
     # dominant class by kernel time; its roofline against its matrix-core
     # path (statistics, root products, apply products) or HBM (the others)

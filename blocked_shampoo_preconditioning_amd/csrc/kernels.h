@@ -57,8 +57,10 @@ struct GemmProblem {
   // [M][K] bf16 row-major (k contiguous), element stride sXh between members
   const uint16_t* Xh;
   int64_t sXh;
-  // split path (launch_gemm_full only): Q holds B^T [K][N] (n contiguous)
-  // instead of B [N][K]
+  // split path: P holds A^T [K][M] (m contiguous, row stride M) instead of
+  // A [M][K], Q holds B^T [K][N] instead of B [N][K]. Full products take at
+  // most one of the two; symmetric products (statistics) both or neither.
+  int32_t p_cols;
   int32_t q_cols;
 };
 
@@ -156,8 +158,9 @@ constexpr int kBalanceSteps = 40;
 
 // ---- launchers (return hipGetLastError()) ----
 // Mom (nullable): momentum buffer [B][br][bc], updated as Mom = momentum * Mom + Gp.
-// GpT (fp32 transpose) or, for bf16 gradients, GpH / GpTH: the packed block and
-// its transpose as bf16 (the gradient's own values), for the bf16 statistics.
+// GpT (fp32 transpose; nullable, then not written) or, for bf16 gradients,
+// GpH / GpTH: the packed block and its transpose as bf16 (the gradient's own
+// values), for the bf16 statistics.
 hipError_t launch_pack(const BlockMeta* blocks, const MatMeta* mats, int32_t B, int32_t br, int32_t bc,
                        int32_t grad_bf16, float* Gp, float* GpT, float* Mom, float momentum,
                        uint16_t* GpH, uint16_t* GpTH, hipStream_t s);

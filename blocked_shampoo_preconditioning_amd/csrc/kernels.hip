@@ -330,72 +330,65 @@ __device__ __forceinline__ void store_split4(uint16_t* d, int plane, const f32x4
   *reinterpret_cast<u32x2*>(d + 2 * plane) = (u32x2){a.l, b.l};
 }
 
-// One thread's share of a split operand K-tile (16 wide) in registers: 4-value
-// chunks of A and B rows, or for QCOLS KC consecutive k of one column of B.
-template <class C, bool QCOLS>
-struct SplitStage {
-  static constexpr int NA = C::BM * 4 / C::NT, NB = C::BN * 4 / C::NT;
-  static constexpr int KC = 16 * C::BN / C::NT;
-  f32x4 ra[NA];
-  f32x4 rb[QCOLS ? 1 : NB];
-  float rc[QCOLS ? KC : 1];
+// One thread's share of one operand of a split K-tile (16 wide) in
+// registers. Rows mode (the operand stored [ROWS][K], k contiguous): NR
+// 4-value chunks, row split_row(c) and chunk c % 4 for c = tid + i NT.
+// Columns mode (stored [K][ROWS], rows contiguous): KC consecutive k of row
+// tid % ROWS, one value per load, consecutive lanes on consecutive rows.
+template <class C, int ROWS, bool COLS>
+struct SplitOperand {
+  static constexpr int NR = ROWS * 4 / C::NT;
+  static constexpr int KC = 16 * ROWS / C::NT;
+  static_assert(COLS ? (C::NT % ROWS == 0 && (KC == 4 || KC == 8))
+                     : (ROWS % 8 == 0 && NR >= 1 && (ROWS * 4) % C::NT == 0),
+                "operand tile does not fit the thread count");
+  f32x4 r[COLS ? 1 : NR];
+  float c[COLS ? KC : 1];
 };
 
-template <class C, bool QCOLS>
-__device__ __forceinline__ void split_load(SplitStage<C, QCOLS>& st, const float* __restrict__ A,
-                                           int lda, const float* __restrict__ B, int ldb, int m0,
-                                           int n0, int k0) {
-  using S = SplitStage<C, QCOLS>;
+template <class C, int ROWS, bool COLS>
+__device__ __forceinline__ void split_load(SplitOperand<C, ROWS, COLS>& o,
+                                           const float* __restrict__ X, int ld, int r0, int k0) {
+  using O = SplitOperand<C, ROWS, COLS>;
   const int tid = threadIdx.x;
+  if constexpr (COLS) {
+    const int row = tid % ROWS, kq = (tid / ROWS) * O::KC;
 #pragma unroll
-  for (int i = 0; i < S::NA; ++i) {
-    const int c = tid + i * C::NT;
-    st.ra[i] = *reinterpret_cast<const f32x4*>(A + (size_t)(m0 + split_row(c)) * lda + k0 + (c % 4) * 4);
-  }
-  if constexpr (QCOLS) {
-    const int row = tid % C::BN, kq = (tid / C::BN) * S::KC;
-#pragma unroll
-    for (int q = 0; q < S::KC; ++q) st.rc[q] = B[(size_t)(k0 + kq + q) * ldb + n0 + row];
+    for (int q = 0; q < O::KC; ++q) o.c[q] = X[(size_t)(k0 + kq + q) * ld + r0 + row];
   } else {
 #pragma unroll
-    for (int i = 0; i < S::NB; ++i) {
+    for (int i = 0; i < O::NR; ++i) {
       const int c = tid + i * C::NT;
-      st.rb[i] = *reinterpret_cast<const f32x4*>(B + (size_t)(n0 + split_row(c)) * ldb + k0 + (c % 4) * 4);
+      o.r[i] = *reinterpret_cast<const f32x4*>(X + (size_t)(r0 + split_row(c)) * ld + k0 + (c % 4) * 4);
     }
   }
 }
 
-// Splits a stage into the three planes of one LDS buffer ([plane][row][k],
-// rows of LDX, A then B).
-template <class C, bool QCOLS>
-__device__ __forceinline__ void split_store(const SplitStage<C, QCOLS>& st, uint16_t* dA,
-                                            uint16_t* dB) {
-  using S = SplitStage<C, QCOLS>;
-  constexpr int LD = C::LDX, PA = C::BM * LD, PB = C::BN * LD;
+// Splits one operand's share into the three planes at d ([plane][row][k],
+// rows of LDX).
+template <class C, int ROWS, bool COLS>
+__device__ __forceinline__ void split_store(const SplitOperand<C, ROWS, COLS>& o, uint16_t* d) {
+  using O = SplitOperand<C, ROWS, COLS>;
+  constexpr int LD = C::LDX, P = ROWS * LD;
   const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < S::NA; ++i) {
-    const int c = tid + i * C::NT;
-    store_split4(dA + split_row(c) * LD + (c % 4) * 4, PA, st.ra[i]);
-  }
-  if constexpr (QCOLS) {
-    uint16_t* d = dB + (tid % C::BN) * LD + (tid / C::BN) * S::KC;
-    if constexpr (S::KC == 8) {
+  if constexpr (COLS) {
+    uint16_t* dr = d + (tid % ROWS) * LD + (tid / ROWS) * O::KC;
+    if constexpr (O::KC == 8) {
       // 16-byte writes: eight consecutive rows per 128-byte group, 12 banks
       // apart, cover all 32 banks once
-      const Split3 s0 = split3(st.rc[0], st.rc[1]), s1 = split3(st.rc[2], st.rc[3]);
-      const Split3 s2 = split3(st.rc[4], st.rc[5]), s3 = split3(st.rc[6], st.rc[7]);
-      *reinterpret_cast<u32x4*>(d) = (u32x4){s0.h, s1.h, s2.h, s3.h};
-      *reinterpret_cast<u32x4*>(d + PB) = (u32x4){s0.m, s1.m, s2.m, s3.m};
-      *reinterpret_cast<u32x4*>(d + 2 * PB) = (u32x4){s0.l, s1.l, s2.l, s3.l};
+      const Split3 s0 = split3(o.c[0], o.c[1]), s1 = split3(o.c[2], o.c[3]);
+      const Split3 s2 = split3(o.c[4], o.c[5]), s3 = split3(o.c[6], o.c[7]);
+      *reinterpret_cast<u32x4*>(dr) = (u32x4){s0.h, s1.h, s2.h, s3.h};
+      *reinterpret_cast<u32x4*>(dr + P) = (u32x4){s0.m, s1.m, s2.m, s3.m};
+      *reinterpret_cast<u32x4*>(dr + 2 * P) = (u32x4){s0.l, s1.l, s2.l, s3.l};
     } else {
-      store_split4(d, PB, (f32x4){st.rc[0], st.rc[1], st.rc[2], st.rc[3]});
+      store_split4(dr, P, (f32x4){o.c[0], o.c[1], o.c[2], o.c[3]});
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < S::NB; ++i) {
+    for (int i = 0; i < O::NR; ++i) {
       const int c = tid + i * C::NT;
-      store_split4(dB + split_row(c) * LD + (c % 4) * 4, PB, st.rb[i]);
+      store_split4(d + split_row(c) * LD + (c % 4) * 4, P, o.r[i]);
     }
   }
 }
@@ -434,23 +427,18 @@ __device__ __forceinline__ void split_mma(floatx16 (&acc)[C::FM][C::FN], const u
 }
 
 // acc[fm][fn] = sum over K of A[m0 + ...][k] * B[n0 + ...][k]: A is [M][K]
-// with row stride lda (k contiguous); B likewise [N][K] with row stride ldb,
-// or with QCOLS its transpose [K][N] (row stride ldb, n contiguous). K is a
+// with row stride lda (k contiguous), or with PCOLS its transpose [K][M] (row
+// stride lda, m contiguous); B likewise [N][K] or, with QCOLS, [K][N]. K is a
 // multiple of 32. Two LDS buffers of split planes and two register stages:
 // while the MFMAs run on K-tile kt, the stage of tile kt + 1 (loaded one
 // phase earlier) is split into the other buffer and tile kt + 2 is loaded
 // into the freed stage, so every load has a full phase to land.
-template <class C, bool QCOLS, int MASK = -1>
+template <class C, bool PCOLS, bool QCOLS, int MASK = -1>
 __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda,
                                             const float* __restrict__ B, int ldb, int K, int m0,
                                             int n0, int wm, int wn,
                                             floatx16 (&acc)[C::FM][C::FN], float* lds) {
-  using S = SplitStage<C, QCOLS>;
   constexpr int PA = C::BM * C::LDX, PB = C::BN * C::LDX;  // one plane, in bf16
-  static_assert(C::BM % 8 == 0 && C::BN % 8 == 0, "split_row maps 8-row bands");
-  static_assert(S::NA >= 1 && S::NB >= 1 && (C::BM * 4) % C::NT == 0 && (C::BN * 4) % C::NT == 0,
-                "uneven operand load");
-  static_assert(!QCOLS || (C::NT % C::BN == 0 && (S::KC == 4 || S::KC == 8)), "column load shape");
   uint16_t* sA0 = reinterpret_cast<uint16_t*>(lds);  // [2][3][BM][LDX]
   uint16_t* sA1 = sA0 + 3 * PA;
   uint16_t* sB0 = sA0 + 2 * 3 * PA;                   // [2][3][BN][LDX]
@@ -462,23 +450,34 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = K / 16;  // even
-  S s0, s1;
-  split_load<C, QCOLS>(s0, A, lda, B, ldb, m0, n0, 0);
-  split_load<C, QCOLS>(s1, A, lda, B, ldb, m0, n0, 16);
-  split_store<C, QCOLS>(s0, sA0, sB0);
+  SplitOperand<C, C::BM, PCOLS> a0, a1;
+  SplitOperand<C, C::BN, QCOLS> b0, b1;
+  split_load<C, C::BM, PCOLS>(a0, A, lda, m0, 0);
+  split_load<C, C::BN, QCOLS>(b0, B, ldb, n0, 0);
+  split_load<C, C::BM, PCOLS>(a1, A, lda, m0, 16);
+  split_load<C, C::BN, QCOLS>(b1, B, ldb, n0, 16);
+  split_store<C, C::BM, PCOLS>(a0, sA0);
+  split_store<C, C::BN, QCOLS>(b0, sB0);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
-    // tile kt from buffer 0; tile kt + 1 (s1) into buffer 1; tile kt + 2
-    // into s0 (the last pair repeats tile nk - 1, in bounds and unused)
-    split_load<C, QCOLS>(s0, A, lda, B, ldb, m0, n0, min(kt + 2, nk - 1) * 16);
+    // tile kt from buffer 0; tile kt + 1 (stage 1) into buffer 1; tile kt + 2
+    // into stage 0 (the last pair repeats tile nk - 1, in bounds and unused)
+    const int k2 = min(kt + 2, nk - 1) * 16, k3 = min(kt + 3, nk - 1) * 16;
+    split_load<C, C::BM, PCOLS>(a0, A, lda, m0, k2);
+    split_load<C, C::BN, QCOLS>(b0, B, ldb, n0, k2);
     split_mma<C, MASK>(acc, sA0, sB0, wm, wn);
-    split_store<C, QCOLS>(s1, sA1, sB1);
+    split_store<C, C::BM, PCOLS>(a1, sA1);
+    split_store<C, C::BN, QCOLS>(b1, sB1);
     __syncthreads();
-    // tile kt + 1 from buffer 1; tile kt + 2 (s0) into buffer 0; tile kt + 3
-    // into s1
-    split_load<C, QCOLS>(s1, A, lda, B, ldb, m0, n0, min(kt + 3, nk - 1) * 16);
+    // tile kt + 1 from buffer 1; tile kt + 2 (stage 0) into buffer 0; tile
+    // kt + 3 into stage 1
+    split_load<C, C::BM, PCOLS>(a1, A, lda, m0, k3);
+    split_load<C, C::BN, QCOLS>(b1, B, ldb, n0, k3);
     split_mma<C, MASK>(acc, sA1, sB1, wm, wn);
-    if (kt + 2 < nk) split_store<C, QCOLS>(s0, sA0, sB0);
+    if (kt + 2 < nk) {
+      split_store<C, C::BM, PCOLS>(a0, sA0);
+      split_store<C, C::BN, QCOLS>(b0, sB0);
+    }
     __syncthreads();
   }
 }
@@ -573,23 +572,27 @@ __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X
     mainloop_bf16<C, 0>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
 }
 
-template <class C>
+// COLS: both operands stored [K][M] (m contiguous, row stride M), as the
+// statistics of a matrix's columns read the packed block; otherwise rows
+// with k contiguous (row stride K).
+template <class C, bool COLS>
 __device__ __forceinline__ void mainloop_sym_x6(const float* __restrict__ A,
-                                                const float* __restrict__ B, int K, int m0,
+                                                const float* __restrict__ B, int M, int K, int m0,
                                                 int n0, floatx16 (&acc)[C::FM][C::FN],
                                                 float* lds, const SymWave<C>& sw) {
   constexpr int kUpper = upper_mask<C::FM, C::FN>();
   constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
+  const int ld = COLS ? M : K;
   if (sw.mask == -1)
-    mainloop_x6<C, false>(A, K, B, K, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    mainloop_x6<C, COLS, COLS>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds);
   else if (sw.mask == kUpper)
-    mainloop_x6<C, false, kUpper>(A, K, B, K, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    mainloop_x6<C, COLS, COLS, kUpper>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds);
   else if (C::FM >= 2 && sw.mask == kTop)
-    mainloop_x6<C, false, kTop>(A, K, B, K, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    mainloop_x6<C, COLS, COLS, kTop>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds);
   else if (C::FM >= 2 && sw.mask == kBottom)
-    mainloop_x6<C, false, kBottom>(A, K, B, K, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    mainloop_x6<C, COLS, COLS, kBottom>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds);
   else
-    mainloop_x6<C, false, 0>(A, K, B, K, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    mainloop_x6<C, COLS, COLS, 0>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds);
 }
 
 // Row / column of accumulator register r of fragment (i, j) of the wave's
@@ -620,11 +623,11 @@ __device__ __forceinline__ int frag_col(int n0, int j) {
 // ---------------------------------------------------------------------------
 // Operand paths of the products: fp32 MFMA, bf16 operands (bf16
 // statistics), fp32 operands split into bf16 terms.
-enum : int { kPathF32 = 0, kPathBF16 = 1, kPathSplit = 2 };
+enum : int { kPathF32 = 0, kPathBF16 = 1, kPathSplit = 2, kPathSplitCols = 3 };
 
 template <class C, int PATH>
 constexpr int lds_floats() {
-  return PATH == kPathSplit ? C::LDS_SPLIT : C::LDS_FLOATS;
+  return PATH == kPathSplit || PATH == kPathSplitCols ? C::LDS_SPLIT : C::LDS_FLOATS;
 }
 
 template <class C, int PATH = kPathF32>
@@ -660,9 +663,10 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   floatx16 acc[C::FM][C::FN];
   if constexpr (PATH == kPathBF16)
     mainloop_sym_bf16<C>(pb.Xh + (size_t)f * pb.sXh, pb.K, m0, n0, acc, lds, sw);
-  else if constexpr (PATH == kPathSplit)
-    mainloop_sym_x6<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.K, m0, n0, acc, lds,
-                       sw);
+  else if constexpr (PATH == kPathSplit || PATH == kPathSplitCols)
+    // operands by rows, or (statistics of a matrix's columns) by columns
+    mainloop_sym_x6<C, PATH == kPathSplitCols>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ,
+                                               pb.M, pb.K, m0, n0, acc, lds, sw);
   else
     mainloop_sym<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0,
                     acc, lds, sw);
@@ -749,7 +753,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
 // P = Q = GpT for L, Gp for R; split path: the row operands, Gp for L and
 // GpT for R).
 template <class C, int PATH>
-__global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void syrk_ema_kernel(GemmLaunch g) {
+__global__ __launch_bounds__(C::NT, PATH == kPathSplit || PATH == kPathSplitCols ? 2 : 4) void syrk_ema_kernel(GemmLaunch g) {
   sym_product<C, PATH>(g);
 }
 
@@ -768,24 +772,24 @@ __global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void newton_sym_
 }
 
 // The product's main loop on either path: fp32 (C = P^T Q, P [K][M] and
-// Q [K][N]) or split (C = A B^T with A = P [M][K] and B = Q [N][K], or with
-// QCOLS Q = B^T [K][N]).
-template <class C, int PATH, bool QCOLS>
+// Q [K][N]) or split (C = A B^T with A = P [M][K], or with PCOLS P = A^T
+// [K][M]; B = Q [N][K], or with QCOLS Q = B^T [K][N]).
+template <class C, int PATH, bool PCOLS, bool QCOLS>
 __device__ __forceinline__ void full_mainloop(const GemmProblem& pb, int f, int m0, int n0,
                                               floatx16 (&acc)[C::FM][C::FN], float* lds) {
   const float* P = pb.P + (size_t)f * pb.sP;
   const float* Q = pb.Q + (size_t)f * pb.sQ;
   if constexpr (PATH == kPathSplit) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    mainloop_x6<C, QCOLS>(P, pb.K, Q, QCOLS ? pb.N : pb.K, pb.K, m0, n0, wave % C::WM,
-                          wave / C::WM, acc, lds);
+    mainloop_x6<C, PCOLS, QCOLS>(P, PCOLS ? pb.M : pb.K, Q, QCOLS ? pb.N : pb.K, pb.K, m0, n0,
+                                 wave % C::WM, wave / C::WM, acc, lds);
   } else {
     mainloop<C>(P, Q, pb.M, pb.N, pb.K, m0, n0, acc, lds);
   }
 }
 
 // Plain product, every tile, C = acc (first apply product).
-template <class C, int PATH, bool QCOLS>
+template <class C, int PATH, bool PCOLS, bool QCOLS>
 __global__ __launch_bounds__(C::NT) void apply_left_kernel(GemmLaunch g) {
   __shared__ float lds[lds_floats<C, PATH>()];
   const GemmProblem& pb = g.p[blockIdx.y];
@@ -797,7 +801,7 @@ __global__ __launch_bounds__(C::NT) void apply_left_kernel(GemmLaunch g) {
   const int tile = logical - f * ntile;
   const int m0 = (tile / TN) * C::BM, n0 = (tile % TN) * C::BN;
   floatx16 acc[C::FM][C::FN];
-  full_mainloop<C, PATH, QCOLS>(pb, f, m0, n0, acc, lds);
+  full_mainloop<C, PATH, PCOLS, QCOLS>(pb, f, m0, n0, acc, lds);
   float* Cb = pb.C + (size_t)f * pb.sC;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -833,7 +837,7 @@ __global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void apply_updat
   const int tile = logical - f * ntile;
   const int m0 = (tile / TN) * C::BM, n0 = (tile % TN) * C::BN;
   floatx16 acc[C::FM][C::FN];
-  full_mainloop<C, PATH, false>(pb, f, m0, n0, acc, lds);
+  full_mainloop<C, PATH, false, false>(pb, f, m0, n0, acc, lds);
   if (u.out_packed != nullptr) {
     float* Ub = u.out_packed + (size_t)f * pb.M * pb.N;
 #pragma unroll
@@ -970,6 +974,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
     tile[row][c + 2] = v.z;
     tile[row][c + 3] = v.w;
   }
+  // no transpose wanted (the split products read the packed block by rows
+  // and by columns): done (uniform over the workgroup)
+  if (GpT == nullptr && GpTH == nullptr) return;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1578,6 +1585,26 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
   if (g.n_problems == 0) return hipSuccess;
   if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
   if (mode == kGemmSplit && !split_k_ok(g)) return hipErrorInvalidValue;
+  int ncols = 0;
+  for (int i = 0; i < g.n_problems; ++i) {
+    // symmetric problems read both operands the same way; columns on the
+    // split path, for the statistics only
+    if ((g.p[i].p_cols != 0) != (g.p[i].q_cols != 0)) return hipErrorInvalidValue;
+    if (g.p[i].p_cols != 0 && (mode != kGemmSplit || newton)) return hipErrorInvalidValue;
+    ncols += g.p[i].p_cols != 0;
+  }
+  if (ncols != 0 && ncols != g.n_problems) {
+    // rows and columns in one call: one launch each (each kernel keeps the
+    // registers of its own operand path)
+    GemmLaunch r{}, c{};
+    for (int i = 0; i < g.n_problems; ++i) {
+      GemmLaunch& d = g.p[i].p_cols ? c : r;
+      d.p[d.n_problems++] = g.p[i];
+    }
+    const hipError_t e = launch_gemm_sym(r, tile, newton, mode, s);
+    return e != hipSuccess ? e : launch_gemm_sym(c, tile, newton, mode, s);
+  }
+  const bool cols = ncols != 0;
   switch (tile) {
 #define SHP_SYM_LAUNCH(CFG, PATH)                                                              \
   if (newton)                                                                                  \
@@ -1588,7 +1615,10 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
   case T: {                                                                                    \
     const int gx = grid_sym<CFG>(g);                                                           \
     if (!gx) break;                                                                            \
-    if (mode == kGemmSplit) {                                                                  \
+    if (cols) {                                                                                \
+      hipLaunchKernelGGL((syrk_ema_kernel<CFG, kPathSplitCols>), dim3(gx, g.n_problems),      \
+                         dim3(CFG::NT), 0, s, g);                                              \
+    } else if (mode == kGemmSplit) {                                                           \
       SHP_SYM_LAUNCH(CFG, kPathSplit)                                                          \
     } else {                                                                                   \
       SHP_SYM_LAUNCH(CFG, kPathF32)                                                            \
@@ -1628,16 +1658,18 @@ hipError_t launch_gemm_sym_bf16(const GemmLaunch& g, int tile, hipStream_t s) {
 
 namespace {
 template <class CFG>
-void launch_full_cfg(const GemmLaunch& g, int mode, bool qcols, hipStream_t s) {
+void launch_full_cfg(const GemmLaunch& g, int mode, bool pcols, bool qcols, hipStream_t s) {
   const int gx = grid_full<CFG>(g);
   if (!gx) return;
   const dim3 grid(gx, g.n_problems), block(CFG::NT);
   if (mode == kGemmSplit && qcols)
-    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, true>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, false, true>), grid, block, 0, s, g);
+  else if (mode == kGemmSplit && pcols)
+    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, true, false>), grid, block, 0, s, g);
   else if (mode == kGemmSplit)
-    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, false, false>), grid, block, 0, s, g);
   else if constexpr (CFG::BM <= 128)
-    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathF32, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathF32, false, false>), grid, block, 0, s, g);
 }
 template <class CFG>
 void launch_update_cfg(const GemmLaunch& g, const UpdateArgs& u, int mode, hipStream_t s) {
@@ -1653,17 +1685,18 @@ void launch_update_cfg(const GemmLaunch& g, const UpdateArgs& u, int mode, hipSt
 hipError_t launch_gemm_full(const GemmLaunch& g, int tile, int mode, hipStream_t s) {
   if (g.n_problems == 0) return hipSuccess;
   if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
-  const bool qcols = g.p[0].q_cols != 0;
+  const bool pcols = g.p[0].p_cols != 0, qcols = g.p[0].q_cols != 0;
   for (int i = 1; i < g.n_problems; ++i)
-    if ((g.p[i].q_cols != 0) != qcols) return hipErrorInvalidValue;
-  if (qcols && mode != kGemmSplit) return hipErrorInvalidValue;
+    if ((g.p[i].p_cols != 0) != pcols || (g.p[i].q_cols != 0) != qcols) return hipErrorInvalidValue;
+  if ((pcols || qcols) && mode != kGemmSplit) return hipErrorInvalidValue;
+  if (pcols && qcols) return hipErrorInvalidValue;  // no kernel reads both by columns
   if (mode == kGemmSplit && !split_k_ok(g)) return hipErrorInvalidValue;
   if (tile == 256 && mode != kGemmSplit) return hipErrorInvalidValue;
   switch (tile) {
-    case 256: launch_full_cfg<Cfg256>(g, mode, qcols, s); break;
-    case 128: launch_full_cfg<Cfg128>(g, mode, qcols, s); break;
-    case 64: launch_full_cfg<Cfg64>(g, mode, qcols, s); break;
-    case 32: launch_full_cfg<Cfg32>(g, mode, qcols, s); break;
+    case 256: launch_full_cfg<Cfg256>(g, mode, pcols, qcols, s); break;
+    case 128: launch_full_cfg<Cfg128>(g, mode, pcols, qcols, s); break;
+    case 64: launch_full_cfg<Cfg64>(g, mode, pcols, qcols, s); break;
+    case 32: launch_full_cfg<Cfg32>(g, mode, pcols, qcols, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1671,7 +1704,7 @@ hipError_t launch_gemm_full(const GemmLaunch& g, int tile, int mode, hipStream_t
 
 hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, int mode,
                               hipStream_t s) {
-  if (g.n_problems != 1 || g.p[0].q_cols != 0) return hipErrorInvalidValue;
+  if (g.n_problems != 1 || g.p[0].p_cols != 0 || g.p[0].q_cols != 0) return hipErrorInvalidValue;
   if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
   if (mode == kGemmSplit && !split_k_ok(g)) return hipErrorInvalidValue;
   if (tile == 256 && mode != kGemmSplit) return hipErrorInvalidValue;

@@ -272,12 +272,17 @@ int do_pack(shampoo_ctx* h, hipStream_t s) {
   double real = 0.0;
   for (const auto& b : h->blocks) real += (double)b.m * b.n;
   const double esz = h->cfg.grad_dtype == SHAMPOO_BF16 ? 2.0 : 4.0;
-  const double bytes = real * esz + (p.momentum ? 4.0 : 2.0) * 4.0 * (double)p.B * p.br * p.bc;
+  const bool hb = m_bf16_stats(h);
+  // the fp32 transpose feeds the fp32-MFMA statistics only (the split path
+  // reads the packed block by rows and by columns)
+  const bool want_t = !hb && h->cfg.fp32_gemm == SHAMPOO_GEMM_F32;
+  const double fp32_copies = 1.0 + (want_t ? 1.0 : 0.0) + (p.momentum ? 2.0 : 0.0);
+  const double bytes = real * esz + fp32_copies * 4.0 * (double)p.B * p.br * p.bc +
+                       (hb ? 2.0 * 2.0 * (double)p.B * p.br * p.bc : 0.0);
   return timed(h, kPack, 0.0, bytes, s, [&] {
-    const bool hb = m_bf16_stats(h);
     return shp::launch_pack(h->at<shp::BlockMeta>(p.off_blocks), h->at<shp::MatMeta>(p.off_mats),
                             (int32_t)p.B, p.br, p.bc, h->cfg.grad_dtype == SHAMPOO_BF16, m_gp(h),
-                            hb ? nullptr : m_gpT(h), m_mom(h), (float)h->cfg.momentum,
+                            want_t ? m_gpT(h) : nullptr, m_mom(h), (float)h->cfg.momentum,
                             hb ? m_gpH(h) : nullptr, hb ? m_gpTH(h) : nullptr, s);
   });
 }
@@ -306,13 +311,13 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
   if (p.B == 0) return SHAMPOO_OK;
   shp::GemmLaunch g{};
   // fp32 MFMA: C = P^T Q, so L = beta2 L + g Gp Gp^T reads P = Q = GpT and
-  // R = beta2 R + g Gp^T Gp reads P = Q = Gp. Split path: C = A A^T with the
-  // row operand A = Gp for L and A = GpT for R.
+  // R = beta2 R + g Gp^T Gp reads P = Q = Gp. Split path: C = A A^T with
+  // A = Gp read by rows for L and by columns for R (Gp stored [K = br][M = bc]).
   const bool split = h->cfg.fp32_gemm == SHAMPOO_GEMM_SPLIT_BF16;
   float* opL = split ? m_gp(h) : m_gpT(h);
-  float* opR = split ? m_gpT(h) : m_gp(h);
   g.p[0] = sym_problem(opL, opL, m_lr(h), (int64_t)p.bc * p.br, p.br, p.bc, (int)p.B);
-  g.p[1] = sym_problem(opR, opR, m_lr(h) + p.fl, (int64_t)p.br * p.bc, p.bc, p.br, (int)p.B);
+  g.p[1] = sym_problem(m_gp(h), m_gp(h), m_lr(h) + p.fl, (int64_t)p.br * p.bc, p.bc, p.br, (int)p.B);
+  g.p[1].p_cols = g.p[1].q_cols = split ? 1 : 0;
   for (int i = 0; i < 2; ++i) {
     g.p[i].alpha = h->stat_scale;
     g.p[i].beta = (float)h->cfg.beta2;

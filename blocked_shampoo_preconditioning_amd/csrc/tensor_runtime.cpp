@@ -292,6 +292,8 @@ int do_tensor_pack(shampoo_ctx* h, hipStream_t s) {
   });
 }
 
+bool split_gemm(const shampoo_ctx* h) { return h->cfg.fp32_gemm == SHAMPOO_GEMM_SPLIT_BF16; }
+
 int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
   const TensorState& ts = T(h);
   if (ts.B == 0) return SHAMPOO_OK;
@@ -335,8 +337,13 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
       q.alpha = h->stat_scale;
       q.beta = (float)h->cfg.beta2;
       g.n_problems = 1;
+      // split path: the k-major operand [Kp][n] read by columns; its K-tiles
+      // run in pairs, so an unfolding padded to an odd multiple of 16 stays on
+      // the fp32 MFMA
+      const int mode = split_gemm(h) && ts.Kp[i] % 32 == 0 ? shp::kGemmSplit : shp::kGemmF32;
+      q.p_cols = q.q_cols = mode == shp::kGemmSplit ? 1 : 0;
       rc = timed(h, kStats, fl, 0.0, s,
-                 [&] { return shp::launch_gemm_sym(g, ts.stat_tile[i], false, shp::kGemmF32, s); });
+                 [&] { return shp::launch_gemm_sym(g, ts.stat_tile[i], false, mode, s); });
     } else {
       rc = timed(h, kStatsAux, fl, 4.0 * ts.B * ts.E, s, [&] {
         return shp::launch_small_gram(gp, ts.E, (int32_t)A, n, (int32_t)C, (int32_t)ts.B,
@@ -416,7 +423,8 @@ int do_tensor_apply(shampoo_ctx* h, hipStream_t s, float* out) {
     }
     if (ts.is_big[i] && ts.apply_tile[i] > 0) {
       // C[r][j] = sum_l cur[l][r] X[l][j]: the product along dimension i (X is
-      // symmetric), which leaves dimension i last
+      // symmetric), which leaves dimension i last. On the split path cur is
+      // the A operand read by columns (stored [K = n][M = R]).
       shp::GemmLaunch g{};
       shp::GemmProblem& q = g.p[0];
       q.P = cur;
@@ -431,8 +439,10 @@ int do_tensor_apply(shampoo_ctx* h, hipStream_t s, float* out) {
       q.batch = (int32_t)ts.B;
       q.alpha = 1.f;
       g.n_problems = 1;
+      const int mode = split_gemm(h) ? shp::kGemmSplit : shp::kGemmF32;
+      q.p_cols = mode == shp::kGemmSplit ? 1 : 0;
       rc = timed(h, kApply, fl, 0.0, s,
-                 [&] { return shp::launch_gemm_full(g, ts.apply_tile[i], shp::kGemmF32, s); });
+                 [&] { return shp::launch_gemm_full(g, ts.apply_tile[i], mode, s); });
     } else {
       rc = timed(h, kApplyAux, fl, 8.0 * ts.B * ts.E, s, [&] {
         return shp::launch_mode_product(cur, ts.E, X, (int64_t)n * n, dst, ts.E, n, (int32_t)R,

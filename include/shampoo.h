@@ -155,8 +155,9 @@ typedef struct {
   int32_t fp32_gemm;              /* shampoo_fp32_gemm_t; default
                                      SHAMPOO_GEMM_SPLIT_BF16. Statistics of bf16
                                      gradients always take the bf16 MFMA
-                                     directly; the tensor handles' statistics
-                                     and mode products stay on the fp32 MFMA  */
+                                     directly; a tensor dimension whose
+                                     unfolding pads to an odd multiple of 16
+                                     keeps its statistics on the fp32 MFMA   */
 } shampoo_config_t;
 
 /* Byte offsets of the state inside the caller's workspace (for inspection
