@@ -62,6 +62,12 @@ struct GemmProblem {
   // most one of the two; symmetric products (statistics) both or neither.
   int32_t p_cols;
   int32_t q_cols;
+  // symmetric products only: two more affine terms of the epilogue, laid out
+  // like D (element stride sE between members), weights coef[4] and coef[5]
+  // (per-factor coefficients required)
+  const float* E1;
+  const float* E2;
+  int64_t sE;
 };
 
 // How the fp32 products run. kGemmF32: C = P^T Q on the fp32 MFMA, P [K][M]
@@ -125,10 +131,22 @@ constexpr int kStatusFinalX = 5;
 // Residual level below which fp32 rounding, not the iteration, decides.
 constexpr float kRoundingFloor = 2.f * 1.1920929e-7f;
 
+// Chebyshev roots by baby steps and giant steps: p(y) = sum_j c_j T_j(y) =
+// sum_k B_k(y) T_k(z) with z = T_3(y) (T_(3k) = T_k o T_3) and B_k in the span
+// of T_0, T_1, T_2. Per factor, records of kChebRec floats: 0 forms T_2, 1
+// forms z, 2 + k the giant step k (k = 0 .. cheb_giant(degree)); each record
+// holds alpha, beta, beta2, gamma and the weights of Ahat and T_2.
+constexpr int kChebBaby = 3;
+constexpr int kChebRec = 8;
+__host__ __device__ inline int cheb_giant(int degree) {
+  return degree < kChebBaby ? 0 : (degree - (kChebBaby - 1) + kChebBaby - 1) / kChebBaby;
+}
+__host__ __device__ inline int cheb_floats(int degree) { return (cheb_giant(degree) + 3) * kChebRec; }
+
 struct NewtonCtl {
   int32_t solver;       // RootSolver
   float floor;          // lower bound of every statistic's spectrum: beta2^t eps
-  float* cheb;          // Chebyshev coefficient quadruples [factor][degree + 1][4]
+  float* cheb;          // Chebyshev records [factor][cheb_floats(degree)]
   int32_t degree;
   int32_t* status;
   int32_t* final_iter;
@@ -190,11 +208,13 @@ hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, int32_t 
 hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, NewtonCtl c,
                                int32_t scale, hipStream_t s);
 // Chebyshev: per factor, the interval [r, 1] (r = floor / s), the interpolant's
-// coefficients and the Clenshaw epilogue quadruples; status = capped.
+// coefficients c_j at degree + 1 Chebyshev points, their giant-step form and
+// the epilogue records (kChebRec); status = capped (a fixed-degree result).
 hipError_t launch_cheb_setup(FactorSet fs, NewtonCtl c, hipStream_t s);
-// B_d = c_d I and B_(d-1) = c_(d-1) I + 2 c_d T(Ahat), T = (2 Ahat - (1 + r) I) / (1 - r).
-hipError_t launch_cheb_init(const float* Ahat, float* Bd, float* Bd1, FactorSet fs, NewtonCtl c,
-                            hipStream_t s);
+// out = gamma I + t_A Ahat + t_2 T2 with the weights of record `rec` of each
+// factor (the giant sum's leading term B_m).
+hipError_t launch_cheb_combine(const float* Ahat, const float* T2, float* out, FactorSet fs,
+                               NewtonCtl c, int32_t rec, hipStream_t s);
 // Between the two Denman-Beavers stages: Y1 (kept pair of stage 1, in Ybuf0 or
 // Ybuf1 by parity) becomes stage 2's Y0 in Ybuf0, Z0 = I goes to Z0buf.
 hipError_t launch_db_stage2_init(float* Ybuf0, const float* Ybuf1, float* Z0buf, FactorSet fs,

@@ -630,7 +630,9 @@ constexpr int lds_floats() {
   return PATH == kPathSplit || PATH == kPathSplitCols ? C::LDS_SPLIT : C::LDS_FLOATS;
 }
 
-template <class C, int PATH = kPathF32>
+// TERMS: the epilogue also adds coef[4] E1 + coef[5] E2 (the Chebyshev giant
+// steps); a separate instantiation, so the other products keep their registers.
+template <class C, int PATH = kPathF32, bool TERMS = false>
 __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   __shared__ float lds[lds_floats<C, PATH>()];
   float* red = lds;  // residual partials reuse the operand tiles after the K loop
@@ -679,13 +681,20 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const float* Db = pb.D != nullptr ? pb.D + (size_t)f * pb.sD : nullptr;
   const float* D2b = pb.D2 != nullptr ? pb.D2 + (size_t)f * pb.sD2 : nullptr;
   float e_alpha = pb.alpha, e_beta = pb.beta, e_beta2 = pb.beta2, e_gamma = pb.gamma;
+  float e_t1 = 0.f, e_t2 = 0.f;
   if (pb.coef != nullptr) {
     const float* cf = pb.coef + (size_t)(pb.f0 + f) * pb.coef_stride;
     e_alpha = cf[0];
     e_beta = cf[1];
     e_beta2 = cf[2];
     e_gamma = cf[3];
+    if constexpr (TERMS) {
+      e_t1 = cf[4];
+      e_t2 = cf[5];
+    }
   }
+  const float* E1b = TERMS && pb.E1 != nullptr ? pb.E1 + (size_t)f * pb.sE : nullptr;
+  const float* E2b = TERMS && pb.E2 != nullptr ? pb.E2 + (size_t)f * pb.sE : nullptr;
   const int N = pb.N;
   float rs = 0.f;
 #pragma unroll
@@ -700,7 +709,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
       // behind the store before it. No store below targets an element another
       // lane reads here. The split path has the registers for all 16.
       constexpr int HOIST = PATH == kPathSplit ? 16 : 4;
-      float dv[HOIST], d2v[HOIST];
+      float dv[HOIST], d2v[HOIST], ev[TERMS ? HOIST : 1];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         if ((4 * g4) % HOIST == 0) {
@@ -709,6 +718,8 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
             const size_t o = (size_t)frag_row_w<C>(m0, sw.wm, i, 4 * g4 + r) * N + col;
             dv[r] = Db != nullptr ? Db[o] : 0.f;
             d2v[r] = D2b != nullptr ? D2b[o] : 0.f;
+            if constexpr (TERMS)
+              ev[r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) + (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
           }
         }
         const int row0 = frag_row_w<C>(m0, sw.wm, i, 4 * g4);
@@ -719,6 +730,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
           float x = e_alpha * acc[i][j][4 * g4 + q];
           x += e_beta * dv[(4 * g4 + q) % HOIST];
           x += e_beta2 * d2v[(4 * g4 + q) % HOIST];
+          if constexpr (TERMS) x += ev[(4 * g4 + q) % HOIST];
           if (row == col) x += e_gamma;
           v[q] = x;
           if (!diag || row <= col) {
@@ -786,6 +798,13 @@ __device__ __forceinline__ void full_mainloop(const GemmProblem& pb, int f, int 
   } else {
     mainloop<C>(P, Q, pb.M, pb.N, pb.K, m0, n0, acc, lds);
   }
+}
+
+// A giant step of the Chebyshev sum: a symmetric product whose epilogue has
+// the two extra terms (Ahat and T_2 with per-factor weights).
+template <class C, int PATH>
+__global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void cheb_sym_kernel(GemmLaunch g) {
+  sym_product<C, PATH, true>(g);
 }
 
 // Plain product, every tile, C = acc (first apply product).
@@ -1471,9 +1490,11 @@ __global__ __launch_bounds__(256) void db_stage2_reset_kernel(FactorSet fs, Newt
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void cheb_setup_kernel(FactorSet fs, NewtonCtl c) {
   __shared__ double fx[1025];
+  __shared__ double cp[1025 + kChebBaby];
   const int f = blockIdx.x;
   const int d = c.degree, N = d + 1;
-  float* q = c.cheb + (size_t)f * N * 4;
+  const int m = cheb_giant(d);
+  float* q = c.cheb + (size_t)f * cheb_floats(d);
   const double s = c.scale[f];
   const bool ok = c.status[f] == 0 && s > 0.0;
   const double r = ok ? fmin((double)c.floor / s, 0.999) : 0.5;
@@ -1483,44 +1504,76 @@ __global__ __launch_bounds__(256) void cheb_setup_kernel(FactorSet fs, NewtonCtl
     const double x = ((1.0 - r) * cos(th) + 1.0 + r) * 0.5;
     fx[j] = pow(x, -1.0 / c.p);
   }
+  for (int k = threadIdx.x; k < m * kChebBaby + kChebBaby; k += blockDim.x) cp[k] = 0.0;
   __syncthreads();
-  const float a = (float)(4.0 / (1.0 - r)), b = (float)(-2.0 * (1.0 + r) / (1.0 - r));
+  // c_j of the interpolant at the Chebyshev points, c_0 halved so that
+  // p(y) = sum_j cp[j] T_j(y), y = (2 x - (1 + r)) / (1 - r)
   for (int k = threadIdx.x; k < N; k += blockDim.x) {
     double ck = 0.0;
     for (int j = 0; j < N; ++j) ck += fx[j] * cos(k * pi * (j + 0.5) / N);
-    ck *= 2.0 / N;
-    // slot k: the epilogue of the product forming B_k (k = 1 .. d-2) or p (k = 0)
-    q[k * 4 + 0] = k == 0 ? 0.5f * a : a;
-    q[k * 4 + 1] = k == 0 ? 0.5f * b : b;
-    q[k * 4 + 2] = -1.f;
-    q[k * 4 + 3] = (float)(k == 0 ? 0.5 * ck : ck);
+    cp[k] = ck * (k == 0 ? 1.0 : 2.0) / N;
   }
-  if (threadIdx.x == 0) {
-    c.status[f] = ok ? 4 : 3;
-    c.final_iter[f] = 0;
-    c.rprev[f] = 0.f;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  // y = (a/2) Ahat + (b/2) I with a = 4 / (1 - r), b = -2 (1 + r) / (1 - r)
+  const double a = 4.0 / (1.0 - r), b = -2.0 * (1.0 + r) / (1.0 - r);
+  for (int e = 0; e < cheb_floats(d); ++e) q[e] = 0.f;
+  // T_2 = 2 y^2 - I = (a^2 / 2) Ahat Ahat + a b Ahat + (b^2 / 2 - 1) I
+  q[0] = (float)(0.5 * a * a);
+  q[1] = (float)(a * b);
+  q[3] = (float)(0.5 * b * b - 1.0);
+  // z = T_3 = 2 y T_2 - T_1 = a Ahat T_2 + b T_2 - (a/2) Ahat - (b/2) I
+  q[kChebRec + 0] = (float)a;
+  q[kChebRec + 1] = (float)b;
+  q[kChebRec + 2] = (float)(-0.5 * a);
+  q[kChebRec + 3] = (float)(-0.5 * b);
+  // Giant-step form, from the top: T_(3k) T_r = (T_(3k+r) + T_(3k-r)) / 2 for
+  // k, r >= 1, so the weight of T_(3k) T_r is 2 cp[3k + r], which also puts
+  // cp[3k + r] on T_(3k - r) (one block lower); T_(3k) T_0 = T_(3k).
+  // B_k = w0 I + w1 T_1 + w2 T_2 = (w0 + w1 b/2) I + (w1 a/2) Ahat + w2 T_2.
+  for (int k = m; k >= 0; --k) {
+    double w[kChebBaby];
+    for (int rr = kChebBaby - 1; rr >= 1; --rr) {
+      const int j = k * kChebBaby + rr;
+      if (k > 0) {
+        w[rr] = 2.0 * cp[j];
+        cp[k * kChebBaby - rr] -= cp[j];
+      } else {
+        w[rr] = cp[j];
+      }
+    }
+    w[0] = cp[k * kChebBaby];
+    float* rec = q + (2 + k) * kChebRec;
+    // the step k < m: beta_k = B_k + 2 z beta_(k+1) - beta_(k+2); k = 0 takes
+    // z beta_1 once; beta_(m+1) = 0 (no beta2 term at k = m - 1)
+    rec[0] = k == 0 ? 1.f : 2.f;
+    rec[1] = 0.f;
+    rec[2] = k + 2 <= m ? -1.f : 0.f;
+    rec[3] = (float)(w[0] + 0.5 * b * w[1]);
+    rec[4] = (float)(0.5 * a * w[1]);
+    rec[5] = (float)w[2];
   }
+  c.status[f] = ok ? 4 : 3;
+  c.final_iter[f] = 0;
+  c.rprev[f] = 0.f;
 }
 
-// B_d = c_d I; B_(d-1) = c_(d-1) I + c_d (a Ahat + b I) with a, b from slot 1.
-__global__ __launch_bounds__(256) void cheb_init_kernel(const float* __restrict__ Ahat,
-                                                        float* __restrict__ Bd,
-                                                        float* __restrict__ Bd1, FactorSet fs,
-                                                        NewtonCtl c) {
+// out = gamma I + t_A Ahat + t_2 T2 with the weights of record `rec`.
+__global__ __launch_bounds__(256) void cheb_combine_kernel(const float* __restrict__ Ahat,
+                                                           const float* __restrict__ T2,
+                                                           float* __restrict__ out, FactorSet fs,
+                                                           NewtonCtl c, int rec) {
   const int f = blockIdx.y;
   int n;
   const float* af = factor_ptr(Ahat, fs, f, n);
   const int64_t base = af - Ahat;
-  const int d = c.degree;
-  const float* q = c.cheb + (size_t)f * (d + 1) * 4;
-  const float cd = q[d * 4 + 3], cd1 = q[(d - 1) * 4 + 3];
-  const float a = q[1 * 4 + 0], b = q[1 * 4 + 1];
+  const float* q = c.cheb + (size_t)f * cheb_floats(c.degree) + rec * kChebRec;
+  const float g = q[3], ta = q[4], t2 = q[5];
   const int64_t nn = (int64_t)n * n;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
        e += (int64_t)gridDim.x * blockDim.x) {
-    const float id = (e / n == e % n) ? 1.f : 0.f;
-    Bd[base + e] = cd * id;
-    Bd1[base + e] = cd * a * af[e] + (cd1 + cd * b) * id;
+    const float id = (e / n == e % n) ? g : 0.f;
+    out[base + e] = id + ta * af[e] + t2 * T2[base + e];
   }
 }
 
@@ -1605,9 +1658,18 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
     return e != hipSuccess ? e : launch_gemm_sym(c, tile, newton, mode, s);
   }
   const bool cols = ncols != 0;
+  int nterms = 0;
+  for (int i = 0; i < g.n_problems; ++i) {
+    const bool t = g.p[i].E1 != nullptr || g.p[i].E2 != nullptr;
+    if (t && (g.p[i].coef == nullptr || g.p[i].coef_stride < 6 || cols)) return hipErrorInvalidValue;
+    nterms += t;
+  }
+  if (nterms != 0 && nterms != g.n_problems) return hipErrorInvalidValue;
   switch (tile) {
 #define SHP_SYM_LAUNCH(CFG, PATH)                                                              \
-  if (newton)                                                                                  \
+  if (nterms)                                                                                  \
+    hipLaunchKernelGGL((cheb_sym_kernel<CFG, PATH>), dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g); \
+  else if (newton)                                                                             \
     hipLaunchKernelGGL((newton_sym_kernel<CFG, PATH>), dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g); \
   else                                                                                         \
     hipLaunchKernelGGL((syrk_ema_kernel<CFG, PATH>), dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g);
@@ -1759,13 +1821,14 @@ hipError_t launch_cheb_setup(FactorSet fs, NewtonCtl c, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_cheb_init(const float* Ahat, float* Bd, float* Bd1, FactorSet fs, NewtonCtl c,
-                            hipStream_t s) {
+hipError_t launch_cheb_combine(const float* Ahat, const float* T2, float* out, FactorSet fs,
+                               NewtonCtl c, int32_t rec, hipStream_t s) {
   if (fs.B == 0) return hipSuccess;
+  if (rec < 0 || rec >= cheb_floats(c.degree) / kChebRec) return hipErrorInvalidValue;
   const int nmax = fs.max_side();
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
-  hipLaunchKernelGGL(cheb_init_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, Ahat, Bd, Bd1, fs,
-                     c);
+  hipLaunchKernelGGL(cheb_combine_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, Ahat, T2, out,
+                     fs, c, rec);
   return hipGetLastError();
 }
 

@@ -200,43 +200,69 @@ int newton_db(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
                [&] { return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 1, s); });
 }
 
-// Chebyshev: X = s^(-1/p) q(Ahat), Ahat = A / s, by the Clenshaw recurrence
-// B_k = a Ahat B_(k+1) + b B_(k+1) - B_(k+2) + c_k I (per-factor epilogue
-// coefficients); B_k lives in s[(d - k) % 3], the last product (k = 0) forms
-// q into xroot.
+// Chebyshev: X = s^(-1/p) p(Ahat), Ahat = A / s, p = sum_j c_j T_j(y) with
+// y = (2 Ahat - (1 + r) I) / (1 - r), evaluated by baby steps and giant steps:
+// T_2 and z = T_3 (two products), then the Clenshaw recurrence in z over
+// p = sum_k B_k T_k(z), B_k = w0 I + w1 T_1 + w2 T_2 (T_(3k) = T_k o T_3): one
+// product per giant step with B_k added in its epilogue, cheb_giant(d) of
+// them, 2 + ceil((d - 2) / 3) products in all instead of d - 1. Buffers: T_2
+// in s[0], z in s[1], beta_k in xroot / s[2] / s[3] by k % 3.
 int chebyshev(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
   const shp::FactorSet& fs = j.fs;
   shp::NewtonCtl c = j.c;
   c.floor = (float)(std::pow(h->cfg.beta2, (double)j.t_stats) * h->cfg.eps);
   const int d = c.degree;
+  const int m = shp::cheb_giant(d);
+  const int rec_floats = shp::cheb_floats(d);
+  if (j.s[3] == nullptr) return fail(SHAMPOO_ERR_INVALID_ARG, "Chebyshev roots need a fourth scratch buffer");
   int rc = timed(h, kNorms, 0.0, norm_bytes(j), s, [&] { return shp::launch_norms(j.A, fs, c, s); });
   if (rc) return rc;
-  // Ahat in xalt (identity on tail padding); the coefficients (which mark
-  // every factor as a fixed-degree result); B_d, B_(d-1) in s[0], s[1]
+  // Ahat in xalt (identity on tail padding); the records (which mark every
+  // factor as a fixed-degree result)
   rc = timed(h, kNewtonAux, 0.0, 0.0, s,
              [&] { return shp::launch_newton_init(j.A, j.xalt, nullptr, fs, c, s); });
   if (rc) return rc;
   rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] { return shp::launch_cheb_setup(fs, c, s); });
   if (rc) return rc;
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_cheb_init(j.xalt, j.s[0], j.s[1], fs, c, s); });
-  if (rc) return rc;
-  for (int k = d - 2; k >= 0; --k) {
-    float* Bk1 = j.s[(d - k - 1) % 3];
-    float* Bk2 = j.s[(d - k - 2) % 3];
-    float* Bk = k == 0 ? j.xroot : j.s[(d - k) % 3];
+  float* Ahat = j.xalt;
+  float* T2 = j.s[0];
+  float* Z = j.s[1];
+  float* ring[3] = {j.xroot, j.s[2], j.s[3]};  // beta_k in ring[k % 3]; p = beta_0 in xroot
+  // one symmetric product per factor group, C = P Q with the epilogue of
+  // record `rec`: beta D + beta2 D2 (+ the Ahat and T_2 terms when `terms`)
+  auto step = [&](const float* P, const float* Q, float* C, const float* D, const float* D2,
+                  int rec, bool terms) {
     SymLaunches L;
-    factor_problems(j, L, j.xalt, Bk1, Bk, Bk1, 1.f, 0.f, 0.f, false);
+    factor_problems(j, L, P, Q, C, D, 1.f, 0.f, 0.f, false);
     for (int li = 0; li < L.n; ++li)
       for (int i = 0; i < L.g[li].n_problems; ++i) {
         shp::GemmProblem& q = L.g[li].p[i];
-        q.D2 = Bk2 + (q.D - Bk1);
-        q.sD2 = q.sD;
-        q.status = nullptr;  // every factor runs the whole recurrence
-        q.coef = c.cheb + (size_t)k * 4;
-        q.coef_stride = (d + 1) * 4;
+        const int64_t off = q.C - C;
+        q.D2 = D2 != nullptr ? D2 + off : nullptr;
+        q.sD2 = q.sC;
+        if (terms) {
+          q.E1 = Ahat + off;
+          q.E2 = T2 + off;
+          q.sE = q.sC;
+        }
+        q.status = nullptr;  // every factor runs the whole sum
+        q.coef = c.cheb + (size_t)rec * shp::kChebRec;
+        q.coef_stride = rec_floats;
       }
-    if ((rc = launch_all(h, L, j.real_cube, s))) return rc;
+    return launch_all(h, L, j.real_cube, s);
+  };
+  // baby steps: T_2 = (a^2/2) Ahat Ahat + a b Ahat + ..., z = a Ahat T_2 + b T_2 - (a/2) Ahat + ...
+  if ((rc = step(Ahat, Ahat, T2, Ahat, nullptr, 0, false))) return rc;
+  if (m > 0 && (rc = step(Ahat, T2, Z, T2, Ahat, 1, false))) return rc;
+  // giant steps: beta_m = B_m, then beta_k = B_k + 2 z beta_(k+1) - beta_(k+2)
+  // down to p = B_0 + z beta_1 - beta_2
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
+    return shp::launch_cheb_combine(Ahat, T2, ring[m % 3], fs, c, 2 + m, s);
+  });
+  if (rc) return rc;
+  for (int k = m - 1; k >= 0; --k) {
+    const float* D2 = k + 2 <= m ? ring[(k + 2) % 3] : nullptr;
+    if ((rc = step(Z, ring[(k + 1) % 3], ring[k % 3], nullptr, D2, 2 + k, true))) return rc;
   }
   return timed(h, kNewtonAux, 0.0, 0.0, s,
                [&] { return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 2, s); });

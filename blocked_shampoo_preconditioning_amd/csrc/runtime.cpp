@@ -128,7 +128,7 @@ Plan make_plan(const shampoo_config_t* c, const shampoo_matrix_desc_t* m, int32_
   p.off_active = take((int64_t)(p.max_iters + 1) * shp::kMaxGroups * 4);
   p.off_flops = take(8);
   p.off_cheb = c->root_method == shp::kChebyshev
-                   ? take(2 * p.B * (int64_t)(c->cheb_degree + 1) * 4 * 4)
+                   ? take(2 * p.B * (int64_t)shp::cheb_floats(c->cheb_degree) * 4)
                    : -1;
   p.off_resid = take(2 * p.B * p.resid_stride * 4);
   p.off_gp = take(p.B * p.br * p.bc * 4);
@@ -140,6 +140,7 @@ Plan make_plan(const shampoo_config_t* c, const shampoo_matrix_desc_t* m, int32_
   p.off_s0 = take(fbytes);
   p.off_s1 = take(fbytes);
   p.off_s2 = take(fbytes);
+  p.off_s3 = c->root_method == shp::kChebyshev ? take(fbytes) : -1;  // the giant steps' third buffer
   p.total = o;
   return p;
 }
@@ -358,6 +359,7 @@ int do_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
   j.xroot = m_xroot(h);
   j.xalt = m_xalt(h);
   for (int i = 0; i < 3; ++i) j.s[i] = m_s(h, i);
+  j.s[3] = p.off_s3 >= 0 ? h->at<float>(p.off_s3) : nullptr;
   j.tile[0] = j.tile[1] = p.tile;
   for (const auto& b : h->blocks)
     j.real_cube += (double)b.m * b.m * (b.m + 1.0) + (double)b.n * b.n * (b.n + 1.0);

@@ -51,7 +51,7 @@ struct Plan {
   int64_t fl = 0, fr = 0;  // elements of all left / right factors
   int64_t off_blocks, off_mats, off_umats, off_nreal, off_status, off_final, off_scale, off_rprev,
       off_cfac, off_lo, off_coef, off_active, off_flops, off_resid, off_gp, off_mom, off_lr,
-      off_xroot, off_xalt, off_s0, off_s1, off_s2, off_cheb, total;
+      off_xroot, off_xalt, off_s0, off_s1, off_s2, off_s3, off_cheb, total;
   bool momentum = false;
 };
 

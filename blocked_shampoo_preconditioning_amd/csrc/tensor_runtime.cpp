@@ -217,7 +217,7 @@ int make_tensor_plan(const shampoo_config_t* cfg, int32_t order, const int32_t* 
   ts.off_active = c.take((int64_t)(cfg->newton_max_iters + 1) * shp::kMaxGroups * 4);
   ts.off_flops = c.take(8);
   ts.off_cheb = cfg->root_method == shp::kChebyshev && ts.nbig
-                    ? c.take((int64_t)ts.nbig * ts.B * (cfg->cheb_degree + 1) * 4 * 4)
+                    ? c.take((int64_t)ts.nbig * ts.B * shp::cheb_floats(cfg->cheb_degree) * 4)
                     : -1;
   ts.off_resid = c.take((int64_t)ts.nbig * ts.B * ts.resid_stride * 4);
   ts.off_partial = ts.nsmall ? c.take(ts.B * ts.gram_chunks * 36 * 4) : -1;
@@ -232,7 +232,10 @@ int make_tensor_plan(const shampoo_config_t* cfg, int32_t order, const int32_t* 
   const bool scratch = ts.nbig > 0;
   ts.off_xalt = scratch ? c.take(ts.fbig * 4) : -1;
   for (int i = 0; i < 4; ++i)
-    ts.off_s[i] = scratch && (i < 3 || ts.p > 4) ? c.take(ts.fbig * 4) : -1;
+    // the fourth: the coupled Newton at p > 4, and the Chebyshev giant steps
+    ts.off_s[i] = scratch && (i < 3 || ts.p > 4 || cfg->root_method == shp::kChebyshev)
+                      ? c.take(ts.fbig * 4)
+                      : -1;
   ts.total = c.o;
   return SHAMPOO_OK;
 }
@@ -477,7 +480,7 @@ int tensor_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
     j.A = fptr(h, ts.off_stats);
     j.xroot = fptr(h, ts.off_xroot);
     j.xalt = fptr(h, ts.off_xalt);
-    for (int i = 0; i < 4; ++i) j.s[i] = fptr(h, ts.off_s[i]);
+    for (int i = 0; i < 4; ++i) j.s[i] = ts.off_s[i] >= 0 ? fptr(h, ts.off_s[i]) : nullptr;
     for (int g = 0; g < ts.nbig; ++g) j.tile[g] = ts.stat_tile[ts.big[g]];
     j.real_cube = ts.real_cube;
     j.t_stats = t_stats;

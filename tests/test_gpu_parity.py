@@ -392,7 +392,7 @@ def test_newton_db_decoder_1b_sampled():
 
 
 # ---------------------------------------------------------------------------
-# Chebyshev roots (degree-d interpolant of x^(-1/4), Clenshaw recurrence)
+# Chebyshev roots (degree-d interpolant of x^(-1/4), baby and giant steps)
 # ---------------------------------------------------------------------------
 def test_chebyshev_same_algorithm_small_ragged():
     """Degree 24 on a ragged set: the GPU evaluates the same interpolant as the
@@ -403,6 +403,23 @@ def test_chebyshev_same_algorithm_small_ragged():
     for r in recs:
         assert r.stats_err <= STATS_TOL, r
         assert r.update_err <= 1e-4, r
+    assert set(sh.newton_info()[0].cpu().tolist()) == {4}
+    sh.close()
+
+
+@pytest.mark.parametrize("degree", [2, 3, 5, 8, 9])
+def test_chebyshev_low_degrees_same_algorithm(degree):
+    """The giant-step form at its edges: degree 2 has no giant product (the sum
+    is B_0 itself), 3 and 5 one, 8 two (the first with no beta2 term), 9
+    three. The GPU evaluates the same interpolant as the fp64 oracle; at
+    these degrees the interpolant is far from x^(-1/4), so the bar is the
+    fp32 rounding of the same polynomial, relative to the update."""
+    w = workload("gpt_small_b256", shapes=((300, 520), (130, 71)), root_every=2,
+                 root_method="chebyshev", cheb_degree=degree, seed=97)
+    recs, sh, orc, params, W = run_parity(w, 3, root_method="chebyshev")
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= 1e-4, (degree, r)
     assert set(sh.newton_info()[0].cpu().tolist()) == {4}
     sh.close()
 

@@ -184,9 +184,12 @@ def test_tensor_scaled_newton():
         sh.close()
 
 
-def test_tensor_chebyshev():
-    w = dataclasses.replace(CASES["conv4_64x32"], root_method="chebyshev")
-    log("tensor chebyshev")
+@pytest.mark.parametrize("case", ["conv4_64x32", "order2"])
+def test_tensor_chebyshev(case):
+    """Order 4 (p = 8) and order 2 (p = 4: the fourth scratch buffer exists
+    for the Chebyshev giant steps only)."""
+    w = dataclasses.replace(CASES[case], root_method="chebyshev")
+    log(f"tensor chebyshev {case}")
     s, u, wp, sh, _ = run_tensor_parity(w, 3)
     assert s <= STATS_TOL and u <= UPDATE_TOL and wp <= UPDATE_TOL, (s, u, wp)
     sh.close()
