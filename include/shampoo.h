@@ -149,8 +149,12 @@ typedef struct {
                                         on [beta2^t eps / s, 1] at the Chebyshev
                                         points, s an upper bound of the spectrum
                                         (min(lam/0.55, ||A||_F, ||A||_inf)),
-                                        Clenshaw recurrence: cheb_degree - 1
-                                        products, no iteration, no early exit    */
+                                        evaluated by baby steps (T_2, T_3) and
+                                        giant steps in T_3 (T_3k = T_k o T_3):
+                                        2 + ceil((cheb_degree - 2) / 3)
+                                        products, no iteration, no early exit;
+                                        one more scratch buffer of the roots'
+                                        size in the workspace                  */
   int32_t cheb_degree;            /* 2..1024, default 128                        */
   int32_t fp32_gemm;              /* shampoo_fp32_gemm_t; default
                                      SHAMPOO_GEMM_SPLIT_BF16. Statistics of bf16
