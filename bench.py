@@ -18,9 +18,11 @@ peak of the matrix-core path it runs on, and the fp64 oracle timed on the
 host cores on a bounded sample of blocks.
 
 Peaks: fp32 products on the fp32 MFMA take its 157.3 TFLOP/s; fp32 products
-split into three bf16 terms (the default) run six bf16 MFMA products per fp32
-product, so their ceiling in fp32 FLOP/s is the 2.5 PFLOP/s bf16 peak / 6 =
-416.7 TFLOP/s; statistics of bf16 gradients take the bf16 peak itself.
+split into three bf16 terms run six bf16 MFMA products per fp32 product, so
+their ceiling in fp32 FLOP/s is the 2.5 PFLOP/s bf16 peak / 6 = 416.7
+TFLOP/s; split into two fp16 terms they run three fp16 MFMA products, a
+ceiling of 2.5 PFLOP/s / 3 = 833.3 TFLOP/s; statistics of bf16 gradients take
+the bf16 peak itself.
 """
 from __future__ import annotations
 
@@ -38,9 +40,15 @@ METRIC = "Shampoo optimizer steps/sec + batched GEMM TFLOP/s vs MFMA peak, 1 GPU
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (the statistics of bf16 gradients)
 PEAK_SPLIT_TFLOPS = PEAK_BF16_MFMA_TFLOPS / 6.0  # fp32 products as six bf16 products
+PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
+PEAK_SPLIT16_TFLOPS = PEAK_F16_MFMA_TFLOPS / 3.0  # fp32 products as three fp16 products
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 PATH_PEAKS = {"f32": PEAK_FP32_MFMA_TFLOPS, "bf16": PEAK_BF16_MFMA_TFLOPS,
-              "split": PEAK_SPLIT_TFLOPS}
+              "split": PEAK_SPLIT_TFLOPS, "split16": PEAK_SPLIT16_TFLOPS}
+GEMM_HOW = {"split16": "fp32 operands scaled and split into two fp16 terms, three fp16 MFMA "
+                       "32x32x16 products",
+            "split": "fp32 operands split into three bf16 terms, six bf16 MFMA 32x32x16 products",
+            "f32": "fp32 MFMA 32x32x2"}
 DEFAULT_WORKLOAD = "decoder_1b_b1024_f32"
 
 
@@ -220,8 +228,10 @@ def run_tensor(args, w, torch, S, synth):
     sh.set_timing(False)
     n_div = sh.n_diverged()
     # statistics (of dimensions whose unfolding pads to a multiple of 32),
-    # MFMA mode products and roots all take the configured path
-    paths = {"stats": w.fp32_gemm, "apply": w.fp32_gemm, "newton_gemm": w.fp32_gemm}
+    # MFMA mode products and roots all take the configured path (tensor
+    # handles run the bf16 split under either split setting)
+    tp = "f32" if w.fp32_gemm == "f32" else "split"
+    paths = {"stats": tp, "apply": tp, "newton_gemm": tp}
     kernels = class_table(tm, paths)
     # dominant class by kernel time; its roofline against its matrix-core
     # path (statistics, root products, apply products) or HBM (the others)
@@ -264,7 +274,7 @@ def newton_traffic(workload, gemm):
     current kernel source (its SHA-256 is recorded with the counters); None
     otherwise."""
     import hashlib
-    tag = "" if gemm == "split" else "_fp32mfma"
+    tag = "" if gemm == "split16" else "_" + gemm
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}{tag}.json")
     src = os.path.join(ROOT, "blocked_shampoo_preconditioning_amd", "csrc", "kernels.hip")
     try:
@@ -294,9 +304,10 @@ def main():
                     help="Newton scale mode (default: the workload's)")
     ap.add_argument("--cheb-degree", type=int, default=None,
                     help="Chebyshev degree (default: the workload's, 128)")
-    ap.add_argument("--fp32-gemm", default=None, choices=("split", "f32"),
-                    help="fp32 products: split into three bf16 terms on the bf16 MFMA "
-                         "(default) or the fp32 MFMA")
+    ap.add_argument("--fp32-gemm", default=None, choices=("split16", "split", "f32"),
+                    help="fp32 products: scaled and split into two fp16 terms on the fp16 MFMA "
+                         "(default), split into three bf16 terms on the bf16 MFMA, or the "
+                         "fp32 MFMA")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one plain 1 GiB device copy (a known-size kernel that "
                          "calibrates the HBM traffic counters)")
@@ -398,8 +409,7 @@ def main():
     achieved = nw["flops"] / (nw["ms"] * 1e-3) / 1e12 if nw["ms"] > 0 else 0.0
     traffic = newton_traffic(w.name, w.fp32_gemm)
     peak = PATH_PEAKS[w.fp32_gemm]
-    how = ("fp32 operands split into three bf16 terms, six bf16 MFMA 32x32x16 products"
-           if w.fp32_gemm == "split" else "fp32 MFMA 32x32x2")
+    how = GEMM_HOW[w.fp32_gemm]
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,

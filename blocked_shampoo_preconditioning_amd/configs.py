@@ -43,7 +43,7 @@ class Workload:
     momentum: float = 0.0         # ordinary momentum folded in before preconditioning
     root_method: str = "newton"   # newton (coupled) | newton_db (Denman-Beavers) | chebyshev
     cheb_degree: int = 128        # degree of the Chebyshev interpolant (chebyshev only)
-    fp32_gemm: str = "split"      # fp32 products: split (three bf16 terms) | f32 (fp32 MFMA)
+    fp32_gemm: str = "split16"    # fp32 products: split16 (two scaled fp16 terms) | split (three bf16 terms) | f32 (fp32 MFMA)
     init_std: float = 0.02
     seed: int = 0
     notes: str = field(default="", compare=False)

@@ -68,6 +68,33 @@ struct GemmProblem {
   const float* E1;
   const float* E2;
   int64_t sE;
+  // fp16 split path (kGemmSplitF16): the binary exponent of the largest
+  // |value| of each operand and of the result per batch member, as versioned
+  // words (max_word): member i scales P by mP[i] and Q by mQ[i] and, when mC
+  // is set, raises mC[i] with version ver over the values it stores
+  const uint64_t* mP;
+  const uint64_t* mQ;
+  uint64_t* mC;
+  uint64_t ver;
+};
+
+// Versioned maximum of a buffer's values: (version << 8) | biased exponent
+// of the largest |value| written with that version (255 for infinity or
+// NaN). Writers raise it by 64-bit atomic max, so the word describes the
+// latest write (a later version wins whatever its exponent) and no word is
+// ever cleared. Versions are below 2^56 and grow with every launch that
+// writes such words (the host numbers them by step and launch).
+__host__ __device__ inline uint64_t max_word(uint64_t ver, uint32_t exp_bits) {
+  return (ver << 8) | (exp_bits & 0xffu);
+}
+
+// Output maxima of the per-factor elementwise root kernels (init, final
+// copy, Denman-Beavers restart, Chebyshev combination): a and b are indexed
+// by factor and may be NULL.
+struct MaxOut {
+  uint64_t* a;
+  uint64_t* b;
+  uint64_t ver;
 };
 
 // How the fp32 products run. kGemmF32: C = P^T Q on the fp32 MFMA, P [K][M]
@@ -76,8 +103,11 @@ struct GemmProblem {
 // and Q holds B [N][K], both with k contiguous and row stride K. For the
 // symmetric products (statistics, root iterations) the two readings coincide
 // when the operands are symmetric; the statistics pass the transposed
-// operands on the split path.
-enum GemmMode : int { kGemmF32 = 0, kGemmSplit = 1 };
+// operands on the split path. kGemmSplitF16: as kGemmSplit, but each operand,
+// scaled by a power of two from its recorded maximum, is split into two fp16
+// terms and three fp16 MFMA products are summed; every problem needs mP and
+// mQ.
+enum GemmMode : int { kGemmF32 = 0, kGemmSplit = 1, kGemmSplitF16 = 2 };
 
 constexpr int kMaxProblems = 8;
 
@@ -178,10 +208,10 @@ constexpr int kBalanceSteps = 40;
 // Mom (nullable): momentum buffer [B][br][bc], updated as Mom = momentum * Mom + Gp.
 // GpT (fp32 transpose; nullable, then not written) or, for bf16 gradients,
 // GpH / GpTH: the packed block and its transpose as bf16 (the gradient's own
-// values), for the bf16 statistics.
+// values), for the bf16 statistics. mo: maxima of Gp (a) and Mom (b) per block.
 hipError_t launch_pack(const BlockMeta* blocks, const MatMeta* mats, int32_t B, int32_t br, int32_t bc,
                        int32_t grad_bf16, float* Gp, float* GpT, float* Mom, float momentum,
-                       uint16_t* GpH, uint16_t* GpTH, hipStream_t s);
+                       uint16_t* GpH, uint16_t* GpTH, hipStream_t s, MaxOut mo = MaxOut{});
 hipError_t launch_unpack(const BlockMeta* blocks, const MatMeta* dst, int32_t B, int32_t br,
                          int32_t bc, const float* Gp, hipStream_t s);
 hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nelemR, int32_t nr,
@@ -195,8 +225,9 @@ hipError_t launch_gemm_full(const GemmLaunch& g, int tile, int mode, hipStream_t
 hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, int mode,
                               hipStream_t s);
 hipError_t launch_norms(const float* A, FactorSet fs, NewtonCtl c, hipStream_t s);
+// mo: maxima of M0 (a) and X1 (b) per factor.
 hipError_t launch_newton_init(const float* A, float* M0, float* X1, FactorSet fs, NewtonCtl c,
-                              hipStream_t s);
+                              hipStream_t s, MaxOut mo = MaxOut{});
 // shift: the residual just computed belongs to iterate iter + shift (1 for
 // coupled Newton, whose products first make the next iterate; 0 for the
 // Denman-Beavers pair, whose residual product comes first). prod_before /
@@ -205,8 +236,9 @@ hipError_t launch_newton_init(const float* A, float* M0, float* X1, FactorSet fs
 hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, int32_t shift,
                                int32_t prod_before, int32_t prod_after, hipStream_t s);
 // scale: multiply the kept iterate by s^(-1/p) (Denman-Beavers result).
+// mo.a: maxima of Xroot per factor (raised where this kernel writes).
 hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, NewtonCtl c,
-                               int32_t scale, hipStream_t s);
+                               int32_t scale, hipStream_t s, MaxOut mo = MaxOut{});
 // Chebyshev: per factor, the interval [r, 1] (r = floor / s), the interpolant's
 // coefficients c_j at degree + 1 Chebyshev points, their giant-step form and
 // the epilogue records (kChebRec); status = capped (a fixed-degree result).
@@ -214,11 +246,12 @@ hipError_t launch_cheb_setup(FactorSet fs, NewtonCtl c, hipStream_t s);
 // out = gamma I + t_A Ahat + t_2 T2 with the weights of record `rec` of each
 // factor (the giant sum's leading term B_m).
 hipError_t launch_cheb_combine(const float* Ahat, const float* T2, float* out, FactorSet fs,
-                               NewtonCtl c, int32_t rec, hipStream_t s);
+                               NewtonCtl c, int32_t rec, hipStream_t s, MaxOut mo = MaxOut{});
 // Between the two Denman-Beavers stages: Y1 (kept pair of stage 1, in Ybuf0 or
 // Ybuf1 by parity) becomes stage 2's Y0 in Ybuf0, Z0 = I goes to Z0buf.
+// mo: maxima of Ybuf0 (a) and Z0buf (b) per factor.
 hipError_t launch_db_stage2_init(float* Ybuf0, const float* Ybuf1, float* Z0buf, FactorSet fs,
-                                 NewtonCtl c, hipStream_t s);
+                                 NewtonCtl c, hipStream_t s, MaxOut mo = MaxOut{});
 
 // Tiles written by a symmetric product of side n with square tile t.
 inline int32_t sym_tiles(int32_t n, int32_t t) {

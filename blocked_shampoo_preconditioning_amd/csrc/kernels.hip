@@ -55,6 +55,7 @@ struct Cfg {
   // 16-byte reads from eight consecutive rows fall on distinct banks)
   static constexpr int LDX = 24;
   static constexpr int LDS_SPLIT = 2 * 3 * (BM + BN) * LDX / 2;  // in floats
+  static constexpr int LDS_SPLITH = 2 * 2 * (BM + BN) * LDX / 2;  // two fp16 planes
   static constexpr int PV = BM / 4, QV = BN / 4;           // float4 per operand row
   static constexpr int PPT = BK * PV / NT, QPT = BK * QV / NT;  // float4 per thread
   static_assert(PPT >= 1 && QPT >= 1, "tile too small for the thread count");
@@ -312,6 +313,57 @@ __device__ __forceinline__ Split3 split3(float x0, float x1) {
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// ---------------------------------------------------------------------------
+// fp16 split products: each operand of a product is first scaled by a power
+// of two, 2^e, that brings its largest |value| into [2^14, 2^15) (exact; the
+// result is scaled back by 2^-(e_A + e_B), also exact). Then x = h + l + d
+// with h = fp16(x) and l = fp16(x - h), both rounded to nearest (x - h is
+// exact in fp32): |d| <= 2^-22 |x| while l is normal, and |d| <= 2^-25 below
+// that, which is 2^-39 of the operand's largest value. Three fp16 products
+//   x y = hh + hl + lh + O(2^-21 |x y|)
+// each exact in fp32, accumulated in fp32 by the MFMA: fp32-level accuracy
+// with half the products and two thirds of the planes of the bf16 split.
+// Non-finite inputs give NaN or infinity as before.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+struct Split2 {
+  uint32_t h, l;
+};
+
+__device__ __forceinline__ Split2 split2h(float x0, float x1, int e) {
+  x0 = ldexpf(x0, e);
+  x1 = ldexpf(x1, e);
+  const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+  const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+  Split2 o;
+  o.h = __builtin_bit_cast(uint32_t, (f16x2){h0, h1});
+  o.l = __builtin_bit_cast(uint32_t, (f16x2){l0, l1});
+  return o;
+}
+
+// Scale exponent of an operand from its versioned maximum word: 2^e brings
+// the largest |value| into [2^14, 2^15) (a zero or subnormal maximum is
+// treated as 2^-126; an infinite or NaN maximum takes 0, so those values
+// propagate as they are).
+__device__ __forceinline__ int f16_exp(uint64_t w) {
+  const int e = (int)(w & 0xffu);
+  return e == 0xff ? 0 : 141 - (e > 0 ? e : 1);
+}
+
+// Raises the versioned maximum word *slot over this wave's values (m: this
+// lane's largest |value|, non-negative); one 64-bit atomic per wave. Every
+// lane of the wave must call it. fmaxf drops NaN, which the products
+// propagate anyway.
+__device__ __forceinline__ void raise_max(uint64_t* slot, float m, uint64_t ver) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0)
+    atomicMax(reinterpret_cast<unsigned long long*>(slot),
+              (unsigned long long)max_word(ver, __float_as_uint(m) >> 23));
+}
+
 // Row of 4-value chunk c of a split operand tile (its chunk within the row is
 // c % 4). The 16 lanes of one 128-byte LDS write group take rows {0, 2, 4, 6}
 // (odd groups {1, 3, 5, 7}) of an 8-row band: at the 48-byte row pitch their
@@ -328,6 +380,13 @@ __device__ __forceinline__ void store_split4(uint16_t* d, int plane, const f32x4
   *reinterpret_cast<u32x2*>(d) = (u32x2){a.h, b.h};
   *reinterpret_cast<u32x2*>(d + plane) = (u32x2){a.m, b.m};
   *reinterpret_cast<u32x2*>(d + 2 * plane) = (u32x2){a.l, b.l};
+}
+
+// The two fp16 planes of 4 consecutive k of one row, scaled by 2^e.
+__device__ __forceinline__ void store_split4h(uint16_t* d, int plane, const f32x4& v, int e) {
+  const Split2 a = split2h(v[0], v[1], e), b = split2h(v[2], v[3], e);
+  *reinterpret_cast<u32x2*>(d) = (u32x2){a.h, b.h};
+  *reinterpret_cast<u32x2*>(d + plane) = (u32x2){a.l, b.l};
 }
 
 // One thread's share of one operand of a split K-tile (16 wide) in
@@ -364,14 +423,32 @@ __device__ __forceinline__ void split_load(SplitOperand<C, ROWS, COLS>& o,
   }
 }
 
-// Splits one operand's share into the three planes at d ([plane][row][k],
-// rows of LDX).
-template <class C, int ROWS, bool COLS>
-__device__ __forceinline__ void split_store(const SplitOperand<C, ROWS, COLS>& o, uint16_t* d) {
+// Splits one operand's share into the planes at d ([plane][row][k], rows of
+// LDX): three bf16 planes, or with F16 two fp16 planes of the values scaled
+// by 2^e.
+template <class C, int ROWS, bool COLS, bool F16 = false>
+__device__ __forceinline__ void split_store(const SplitOperand<C, ROWS, COLS>& o, uint16_t* d,
+                                            int e = 0) {
   using O = SplitOperand<C, ROWS, COLS>;
   constexpr int LD = C::LDX, P = ROWS * LD;
   const int tid = threadIdx.x;
-  if constexpr (COLS) {
+  if constexpr (F16 && COLS) {
+    uint16_t* dr = d + (tid % ROWS) * LD + (tid / ROWS) * O::KC;
+    if constexpr (O::KC == 8) {
+      const Split2 s0 = split2h(o.c[0], o.c[1], e), s1 = split2h(o.c[2], o.c[3], e);
+      const Split2 s2 = split2h(o.c[4], o.c[5], e), s3 = split2h(o.c[6], o.c[7], e);
+      *reinterpret_cast<u32x4*>(dr) = (u32x4){s0.h, s1.h, s2.h, s3.h};
+      *reinterpret_cast<u32x4*>(dr + P) = (u32x4){s0.l, s1.l, s2.l, s3.l};
+    } else {
+      store_split4h(dr, P, (f32x4){o.c[0], o.c[1], o.c[2], o.c[3]}, e);
+    }
+  } else if constexpr (F16) {
+#pragma unroll
+    for (int i = 0; i < O::NR; ++i) {
+      const int c = tid + i * C::NT;
+      store_split4h(d + split_row(c) * LD + (c % 4) * 4, P, o.r[i], e);
+    }
+  } else if constexpr (COLS) {
     uint16_t* dr = d + (tid % ROWS) * LD + (tid / ROWS) * O::KC;
     if constexpr (O::KC == 8) {
       // 16-byte writes: eight consecutive rows per 128-byte group, 12 banks
@@ -398,7 +475,7 @@ __device__ __forceinline__ void split_store(const SplitOperand<C, ROWS, COLS>& o
 // k 8 (l / 32) + 0..7, the 32x32x16 bf16 MFMA's operand layout for both A and
 // B), then runs the products product-major (smallest terms first), so
 // consecutive MFMAs go to different accumulators.
-template <class C, int MASK>
+template <class C, int MASK, bool F16 = false>
 __device__ __forceinline__ void split_mma(floatx16 (&acc)[C::FM][C::FN], const uint16_t* sA,
                                           const uint16_t* sB, int wm, int wn) {
   constexpr int LD = C::LDX, PA = C::BM * LD, PB = C::BN * LD;
@@ -406,6 +483,28 @@ __device__ __forceinline__ void split_mma(floatx16 (&acc)[C::FM][C::FN], const u
   const int half = lane >> 5, l32 = lane & 31;
   const uint16_t* a0 = sA + (wm * 32 * C::FM + l32) * LD + half * 8;
   const uint16_t* b0 = sB + (wn * 32 * C::FN + l32) * LD + half * 8;
+  if constexpr (F16) {
+    // the fp16 terms: lh, hl, hh (same operand layout as the bf16 MFMA)
+    f16x8 a[2][C::FM], b[2][C::FN];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) a[p][i] = *reinterpret_cast<const f16x8*>(a0 + p * PA + i * 32 * LD);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) b[p][j] = *reinterpret_cast<const f16x8*>(b0 + p * PB + j * 32 * LD);
+    }
+    constexpr int PP[3][2] = {{1, 0}, {0, 1}, {0, 0}};
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          if (MASK & (1 << (i * C::FN + j)))
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[PP[q][0]][i], b[PP[q][1]][j],
+                                                               acc[i][j], 0, 0, 0);
+    return;
+  }
   bf16x8 a[3][C::FM], b[3][C::FN];
 #pragma unroll
   for (int p = 0; p < 3; ++p) {
@@ -432,17 +531,21 @@ __device__ __forceinline__ void split_mma(floatx16 (&acc)[C::FM][C::FN], const u
 // multiple of 32. Two LDS buffers of split planes and two register stages:
 // while the MFMAs run on K-tile kt, the stage of tile kt + 1 (loaded one
 // phase earlier) is split into the other buffer and tile kt + 2 is loaded
-// into the freed stage, so every load has a full phase to land.
-template <class C, bool PCOLS, bool QCOLS, int MASK = -1>
+// into the freed stage, so every load has a full phase to land. F16: two
+// fp16 planes of A 2^ea and B 2^eb and three products instead (the caller
+// scales the sums back by 2^-(ea + eb)).
+template <class C, bool PCOLS, bool QCOLS, int MASK = -1, bool F16 = false>
 __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda,
                                             const float* __restrict__ B, int ldb, int K, int m0,
                                             int n0, int wm, int wn,
-                                            floatx16 (&acc)[C::FM][C::FN], float* lds) {
-  constexpr int PA = C::BM * C::LDX, PB = C::BN * C::LDX;  // one plane, in bf16
-  uint16_t* sA0 = reinterpret_cast<uint16_t*>(lds);  // [2][3][BM][LDX]
-  uint16_t* sA1 = sA0 + 3 * PA;
-  uint16_t* sB0 = sA0 + 2 * 3 * PA;                   // [2][3][BN][LDX]
-  uint16_t* sB1 = sB0 + 3 * PB;
+                                            floatx16 (&acc)[C::FM][C::FN], float* lds,
+                                            int ea = 0, int eb = 0) {
+  constexpr int NPL = F16 ? 2 : 3;                          // planes per operand
+  constexpr int PA = C::BM * C::LDX, PB = C::BN * C::LDX;  // one plane, in 16-bit words
+  uint16_t* sA0 = reinterpret_cast<uint16_t*>(lds);  // [2][NPL][BM][LDX]
+  uint16_t* sA1 = sA0 + NPL * PA;
+  uint16_t* sB0 = sA0 + 2 * NPL * PA;                 // [2][NPL][BN][LDX]
+  uint16_t* sB1 = sB0 + NPL * PB;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -456,8 +559,8 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
   split_load<C, C::BN, QCOLS>(b0, B, ldb, n0, 0);
   split_load<C, C::BM, PCOLS>(a1, A, lda, m0, 16);
   split_load<C, C::BN, QCOLS>(b1, B, ldb, n0, 16);
-  split_store<C, C::BM, PCOLS>(a0, sA0);
-  split_store<C, C::BN, QCOLS>(b0, sB0);
+  split_store<C, C::BM, PCOLS, F16>(a0, sA0, ea);
+  split_store<C, C::BN, QCOLS, F16>(b0, sB0, eb);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
     // tile kt from buffer 0; tile kt + 1 (stage 1) into buffer 1; tile kt + 2
@@ -465,21 +568,33 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
     const int k2 = min(kt + 2, nk - 1) * 16, k3 = min(kt + 3, nk - 1) * 16;
     split_load<C, C::BM, PCOLS>(a0, A, lda, m0, k2);
     split_load<C, C::BN, QCOLS>(b0, B, ldb, n0, k2);
-    split_mma<C, MASK>(acc, sA0, sB0, wm, wn);
-    split_store<C, C::BM, PCOLS>(a1, sA1);
-    split_store<C, C::BN, QCOLS>(b1, sB1);
+    split_mma<C, MASK, F16>(acc, sA0, sB0, wm, wn);
+    split_store<C, C::BM, PCOLS, F16>(a1, sA1, ea);
+    split_store<C, C::BN, QCOLS, F16>(b1, sB1, eb);
     __syncthreads();
     // tile kt + 1 from buffer 1; tile kt + 2 (stage 0) into buffer 0; tile
     // kt + 3 into stage 1
     split_load<C, C::BM, PCOLS>(a1, A, lda, m0, k3);
     split_load<C, C::BN, QCOLS>(b1, B, ldb, n0, k3);
-    split_mma<C, MASK>(acc, sA1, sB1, wm, wn);
+    split_mma<C, MASK, F16>(acc, sA1, sB1, wm, wn);
     if (kt + 2 < nk) {
-      split_store<C, C::BM, PCOLS>(a0, sA0);
-      split_store<C, C::BN, QCOLS>(b0, sB0);
+      split_store<C, C::BM, PCOLS, F16>(a0, sA0, ea);
+      split_store<C, C::BN, QCOLS, F16>(b0, sB0, eb);
     }
     __syncthreads();
   }
+}
+
+// Undoes the operand scaling of the fp16 split on the sums (exact unless the
+// result leaves the fp32 range).
+template <class C>
+__device__ __forceinline__ void unscale_acc(floatx16 (&acc)[C::FM][C::FN], int e) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = ldexpf(acc[i][j][r], e);
 }
 
 template <int FM, int FN>
@@ -575,24 +690,25 @@ __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X
 // COLS: both operands stored [K][M] (m contiguous, row stride M), as the
 // statistics of a matrix's columns read the packed block; otherwise rows
 // with k contiguous (row stride K).
-template <class C, bool COLS>
+template <class C, bool COLS, bool F16 = false>
 __device__ __forceinline__ void mainloop_sym_x6(const float* __restrict__ A,
                                                 const float* __restrict__ B, int M, int K, int m0,
                                                 int n0, floatx16 (&acc)[C::FM][C::FN],
-                                                float* lds, const SymWave<C>& sw) {
+                                                float* lds, const SymWave<C>& sw, int ea = 0,
+                                                int eb = 0) {
   constexpr int kUpper = upper_mask<C::FM, C::FN>();
   constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
   const int ld = COLS ? M : K;
   if (sw.mask == -1)
-    mainloop_x6<C, COLS, COLS>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    mainloop_x6<C, COLS, COLS, -1, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
   else if (sw.mask == kUpper)
-    mainloop_x6<C, COLS, COLS, kUpper>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    mainloop_x6<C, COLS, COLS, kUpper, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
   else if (C::FM >= 2 && sw.mask == kTop)
-    mainloop_x6<C, COLS, COLS, kTop>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    mainloop_x6<C, COLS, COLS, kTop, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
   else if (C::FM >= 2 && sw.mask == kBottom)
-    mainloop_x6<C, COLS, COLS, kBottom>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    mainloop_x6<C, COLS, COLS, kBottom, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
   else
-    mainloop_x6<C, COLS, COLS, 0>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    mainloop_x6<C, COLS, COLS, 0, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
 }
 
 // Row / column of accumulator register r of fragment (i, j) of the wave's
@@ -622,12 +738,23 @@ __device__ __forceinline__ int frag_col(int n0, int j) {
 // symmetric. Used by the statistics (EMA epilogue) and the Newton chain.
 // ---------------------------------------------------------------------------
 // Operand paths of the products: fp32 MFMA, bf16 operands (bf16
-// statistics), fp32 operands split into bf16 terms.
-enum : int { kPathF32 = 0, kPathBF16 = 1, kPathSplit = 2, kPathSplitCols = 3 };
+// statistics), fp32 operands split into three bf16 terms or (scaled) into two
+// fp16 terms, each with operands read by rows or by columns.
+enum : int {
+  kPathF32 = 0,
+  kPathBF16 = 1,
+  kPathSplit = 2,
+  kPathSplitCols = 3,
+  kPathSplitH = 4,
+  kPathSplitHCols = 5
+};
+constexpr bool path_split(int p) { return p >= kPathSplit; }
+constexpr bool path_f16(int p) { return p == kPathSplitH || p == kPathSplitHCols; }
+constexpr bool path_cols(int p) { return p == kPathSplitCols || p == kPathSplitHCols; }
 
 template <class C, int PATH>
 constexpr int lds_floats() {
-  return PATH == kPathSplit || PATH == kPathSplitCols ? C::LDS_SPLIT : C::LDS_FLOATS;
+  return path_f16(PATH) ? C::LDS_SPLITH : path_split(PATH) ? C::LDS_SPLIT : C::LDS_FLOATS;
 }
 
 // TERMS: the epilogue also adds coef[4] E1 + coef[5] E2 (the Chebyshev giant
@@ -663,13 +790,18 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const bool diag = (ti == tj);
   const SymWave<C> sw(diag);
   floatx16 acc[C::FM][C::FN];
-  if constexpr (PATH == kPathBF16)
+  if constexpr (PATH == kPathBF16) {
     mainloop_sym_bf16<C>(pb.Xh + (size_t)f * pb.sXh, pb.K, m0, n0, acc, lds, sw);
-  else if constexpr (PATH == kPathSplit || PATH == kPathSplitCols)
+  } else if constexpr (path_f16(PATH)) {
+    const int ea = f16_exp(pb.mP[f]), eb = f16_exp(pb.mQ[f]);
+    mainloop_sym_x6<C, path_cols(PATH), true>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ,
+                                              pb.M, pb.K, m0, n0, acc, lds, sw, ea, eb);
+    unscale_acc<C>(acc, -(ea + eb));
+  } else if constexpr (path_split(PATH)) {
     // operands by rows, or (statistics of a matrix's columns) by columns
-    mainloop_sym_x6<C, PATH == kPathSplitCols>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ,
-                                               pb.M, pb.K, m0, n0, acc, lds, sw);
-  else
+    mainloop_sym_x6<C, path_cols(PATH)>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ,
+                                        pb.M, pb.K, m0, n0, acc, lds, sw);
+  } else
     mainloop_sym<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0,
                     acc, lds, sw);
 
@@ -697,6 +829,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const float* E2b = TERMS && pb.E2 != nullptr ? pb.E2 + (size_t)f * pb.sE : nullptr;
   const int N = pb.N;
   float rs = 0.f;
+  float mx = 0.f;  // largest |value| stored (fp16 split: the result's maximum)
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -708,7 +841,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
       // statistics update in place), which would otherwise hold every load
       // behind the store before it. No store below targets an element another
       // lane reads here. The split path has the registers for all 16.
-      constexpr int HOIST = PATH == kPathSplit ? 16 : 4;
+      constexpr int HOIST = PATH == kPathSplit || PATH == kPathSplitH ? 16 : 4;
       float dv[HOIST], d2v[HOIST], ev[TERMS ? HOIST : 1];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -737,6 +870,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
             Cb[(size_t)row * N + col] = x;
             const float d = x - (row == col ? 1.f : 0.f);
             rs += (row == col ? 1.f : 2.f) * d * d;
+            if constexpr (path_f16(PATH)) mx = fmaxf(mx, fabsf(x));
           }
         }
         if (!diag || row0 + 3 < col) {
@@ -748,6 +882,8 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
         }
       }
     }
+  if constexpr (path_f16(PATH))
+    if (pb.mC != nullptr) raise_max(pb.mC + f, mx, pb.ver);
   if (pb.resid != nullptr) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) rs += __shfl_xor(rs, o);
@@ -765,7 +901,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
 // P = Q = GpT for L, Gp for R; split path: the row operands, Gp for L and
 // GpT for R).
 template <class C, int PATH>
-__global__ __launch_bounds__(C::NT, PATH == kPathSplit || PATH == kPathSplitCols ? 2 : 4) void syrk_ema_kernel(GemmLaunch g) {
+__global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void syrk_ema_kernel(GemmLaunch g) {
   sym_product<C, PATH>(g);
 }
 
@@ -779,7 +915,7 @@ __global__ __launch_bounds__(C::NT, 4) void syrk_bf16_kernel(GemmLaunch g) {
 // One product of the coupled Newton chain (T T, X T, T2 T2 or T4 M); every
 // operand is symmetric, so P and Q serve as row operands as they are.
 template <class C, int PATH>
-__global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void newton_sym_kernel(GemmLaunch g) {
+__global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void newton_sym_kernel(GemmLaunch g) {
   sym_product<C, PATH>(g);
 }
 
@@ -791,7 +927,13 @@ __device__ __forceinline__ void full_mainloop(const GemmProblem& pb, int f, int 
                                               floatx16 (&acc)[C::FM][C::FN], float* lds) {
   const float* P = pb.P + (size_t)f * pb.sP;
   const float* Q = pb.Q + (size_t)f * pb.sQ;
-  if constexpr (PATH == kPathSplit) {
+  if constexpr (PATH == kPathSplitH) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ea = f16_exp(pb.mP[f]), eb = f16_exp(pb.mQ[f]);
+    mainloop_x6<C, PCOLS, QCOLS, -1, true>(P, PCOLS ? pb.M : pb.K, Q, QCOLS ? pb.N : pb.K, pb.K,
+                                           m0, n0, wave % C::WM, wave / C::WM, acc, lds, ea, eb);
+    unscale_acc<C>(acc, -(ea + eb));
+  } else if constexpr (PATH == kPathSplit) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     mainloop_x6<C, PCOLS, QCOLS>(P, PCOLS ? pb.M : pb.K, Q, QCOLS ? pb.N : pb.K, pb.K, m0, n0,
                                  wave % C::WM, wave / C::WM, acc, lds);
@@ -803,7 +945,7 @@ __device__ __forceinline__ void full_mainloop(const GemmProblem& pb, int f, int 
 // A giant step of the Chebyshev sum: a symmetric product whose epilogue has
 // the two extra terms (Ahat and T_2 with per-factor weights).
 template <class C, int PATH>
-__global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void cheb_sym_kernel(GemmLaunch g) {
+__global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void cheb_sym_kernel(GemmLaunch g) {
   sym_product<C, PATH, true>(g);
 }
 
@@ -822,14 +964,20 @@ __global__ __launch_bounds__(C::NT) void apply_left_kernel(GemmLaunch g) {
   floatx16 acc[C::FM][C::FN];
   full_mainloop<C, PATH, PCOLS, QCOLS>(pb, f, m0, n0, acc, lds);
   float* Cb = pb.C + (size_t)f * pb.sC;
+  float mx = 0.f;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
       const int col = frag_col<C>(n0, j);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Cb[(size_t)frag_row<C>(m0, i, r) * pb.N + col] = acc[i][j][r];
+      for (int r = 0; r < 16; ++r) {
+        Cb[(size_t)frag_row<C>(m0, i, r) * pb.N + col] = acc[i][j][r];
+        if constexpr (path_f16(PATH)) mx = fmaxf(mx, fabsf(acc[i][j][r]));
+      }
     }
+  if constexpr (path_f16(PATH))
+    if (pb.mC != nullptr) raise_max(pb.mC + f, mx, pb.ver);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -845,7 +993,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 // Second apply product with the parameter update in the epilogue:
 // W[r0 + row][c0 + col] -= lr * U[row][col] on the block's real extent.
 template <class C, int PATH>
-__global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void apply_update_kernel(GemmLaunch g, UpdateArgs u) {
+__global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void apply_update_kernel(GemmLaunch g, UpdateArgs u) {
   __shared__ float lds[lds_floats<C, PATH>()];
   const GemmProblem& pb = g.p[0];
   const int TM = pb.M / C::BM, TN = pb.N / C::BN;
@@ -882,7 +1030,7 @@ __global__ __launch_bounds__(C::NT, PATH == kPathSplit ? 2 : 4) void apply_updat
       const int col = frag_col<C>(n0, j);
       if (col >= bm.n) continue;
       const size_t base = (size_t)bm.r0 * mm.ld + bm.c0 + col;
-      constexpr int HOIST = PATH == kPathSplit ? 16 : 4;  // registers per batch
+      constexpr int HOIST = path_split(PATH) ? 16 : 4;  // registers per batch
       if (u.param_bf16) {
         uint16_t* w = reinterpret_cast<uint16_t*>(mm.param) + base;
 #pragma unroll
@@ -947,8 +1095,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
                                                    int bf16, float* __restrict__ Gp,
                                                    float* __restrict__ GpT, float* __restrict__ Mom,
                                                    float momentum, uint16_t* __restrict__ GpH,
-                                                   uint16_t* __restrict__ GpTH) {
+                                                   uint16_t* __restrict__ GpTH, MaxOut mo) {
   __shared__ float tile[64][65];
+  float mg = 0.f, mmom = 0.f;  // largest |value| written to Gp and Mom
   const int b = blockIdx.y;
   const BlockMeta bm = blocks[b];
   const MatMeta mm = mats[bm.mat];
@@ -978,6 +1127,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
     if (pr < br && pc < bc) {
       const size_t o = ((size_t)b * br + pr) * bc + pc;
       *reinterpret_cast<float4*>(Gp + o) = v;
+      mg = fmaxf(mg, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
       if (GpH != nullptr) *reinterpret_cast<uint2*>(GpH + o) = bf16_bits4(v);
       if (Mom != nullptr) {  // momentum folded in before preconditioning
         float4 m = *reinterpret_cast<const float4*>(Mom + o);
@@ -986,6 +1136,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
         m.z = momentum * m.z + v.z;
         m.w = momentum * m.w + v.w;
         *reinterpret_cast<float4*>(Mom + o) = m;
+        mmom = fmaxf(mmom, fmaxf(fmaxf(fabsf(m.x), fabsf(m.y)), fmaxf(fabsf(m.z), fabsf(m.w))));
       }
     }
     tile[row][c] = v.x;
@@ -993,6 +1144,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
     tile[row][c + 2] = v.z;
     tile[row][c + 3] = v.w;
   }
+  if (mo.a != nullptr) raise_max(mo.a + b, mg, mo.ver);
+  if (mo.b != nullptr) raise_max(mo.b + b, mmom, mo.ver);
   // no transpose wanted (the split products read the packed block by rows
   // and by columns): done (uniform over the workgroup)
   if (GpT == nullptr && GpTH == nullptr) return;
@@ -1296,9 +1449,10 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
 __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restrict__ A,
                                                           float* __restrict__ M0,
                                                           float* __restrict__ X1, FactorSet fs,
-                                                          NewtonCtl c) {
+                                                          NewtonCtl c, MaxOut mo) {
   const int f = blockIdx.y;
   if (c.status[f] != 0) return;
+  float mm = 0.f, mx = 0.f;
   int n;
   const float* Af = factor_ptr(A, fs, f, n);
   const int64_t base = Af - A;
@@ -1312,9 +1466,15 @@ __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restric
     const float id = (r == col) ? 1.f : 0.f;
     const float m = (r < nr && col < nr) ? Af[e] / s : id;
     M0[base + e] = m;
-    if (c.solver != kChebyshev)
-      X1[base + e] = c.solver == kNewtonDB ? id : cf * (ip1 * id - ip * m);
+    mm = fmaxf(mm, fabsf(m));
+    if (c.solver != kChebyshev) {
+      const float x = c.solver == kNewtonDB ? id : cf * (ip1 * id - ip * m);
+      X1[base + e] = x;
+      mx = fmaxf(mx, fabsf(x));
+    }
   }
+  if (mo.a != nullptr) raise_max(mo.a + f, mm, mo.ver);
+  if (mo.b != nullptr) raise_max(mo.b + f, mx, mo.ver);
 }
 
 // After iteration `iter` (which produced M_{iter+1} and X_{iter+1}): residual
@@ -1429,7 +1589,8 @@ __global__ __launch_bounds__(1024) void newton_check_kernel(FactorSet fs, Newton
 // is stored in Xroot by the stage-2 init.
 __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ Xroot,
                                                            const float* __restrict__ Xalt,
-                                                           FactorSet fs, NewtonCtl c, int scale) {
+                                                           FactorSet fs, NewtonCtl c, int scale,
+                                                           MaxOut mo) {
   const int f = blockIdx.y;
   const int k = c.final_iter[f];
   if (!scale && k > 0 && (k & 1) == 0) return;
@@ -1440,15 +1601,20 @@ __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ X
   const int64_t base = xf - Xroot;
   const float cf = c.cfac[f];
   const int64_t nn = (int64_t)n * n;
+  float mx = 0.f;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
        e += (int64_t)gridDim.x * blockDim.x) {
+    float x;
     if (dead)
-      Xroot[base + e] = 0.f;
+      x = 0.f;
     else if (scale)
-      Xroot[base + e] = cf * (odd ? Xalt[base + e] : Xroot[base + e]);
+      x = cf * (odd ? Xalt[base + e] : Xroot[base + e]);
     else
-      Xroot[base + e] = (k == 0) ? ((e / n == e % n) ? cf : 0.f) : Xalt[base + e];
+      x = (k == 0) ? ((e / n == e % n) ? cf : 0.f) : Xalt[base + e];
+    Xroot[base + e] = x;
+    mx = fmaxf(mx, fabsf(x));
   }
+  if (mo.a != nullptr) raise_max(mo.a + f, mx, mo.ver);
 }
 
 // Stage 1's kept Y (index final_iter, Ybuf0 for even, Ybuf1 for odd) becomes
@@ -1457,19 +1623,28 @@ __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ X
 __global__ __launch_bounds__(256) void db_stage2_init_kernel(float* __restrict__ Ybuf0,
                                                              const float* __restrict__ Ybuf1,
                                                              float* __restrict__ Z0buf,
-                                                             FactorSet fs, NewtonCtl c) {
+                                                             FactorSet fs, NewtonCtl c, MaxOut mo) {
   const int f = blockIdx.y;
   const int k = c.final_iter[f];
   const bool dead = c.status[f] == 3;
+  const bool copy = !dead && (k & 1);
+  float my = 0.f;
   int n;
   const float* yf = factor_ptr(Ybuf0, fs, f, n);
   const int64_t base = yf - Ybuf0;
   const int64_t nn = (int64_t)n * n;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
        e += (int64_t)gridDim.x * blockDim.x) {
-    if (!dead && (k & 1)) Ybuf0[base + e] = Ybuf1[base + e];
+    if (copy) {
+      const float y = Ybuf1[base + e];
+      Ybuf0[base + e] = y;
+      my = fmaxf(my, fabsf(y));
+    }
     Z0buf[base + e] = (e / n == e % n) ? 1.f : 0.f;
   }
+  // Ybuf0 keeps its word where it was not rewritten; Z0 = I has maximum 1
+  if (copy && mo.a != nullptr) raise_max(mo.a + f, my, mo.ver);
+  if (mo.b != nullptr) raise_max(mo.b + f, 1.f, mo.ver);
 }
 
 // After the copy above has read every factor's final_iter: stage 2 starts.
@@ -1562,7 +1737,7 @@ __global__ __launch_bounds__(256) void cheb_setup_kernel(FactorSet fs, NewtonCtl
 __global__ __launch_bounds__(256) void cheb_combine_kernel(const float* __restrict__ Ahat,
                                                            const float* __restrict__ T2,
                                                            float* __restrict__ out, FactorSet fs,
-                                                           NewtonCtl c, int rec) {
+                                                           NewtonCtl c, int rec, MaxOut mo) {
   const int f = blockIdx.y;
   int n;
   const float* af = factor_ptr(Ahat, fs, f, n);
@@ -1570,11 +1745,15 @@ __global__ __launch_bounds__(256) void cheb_combine_kernel(const float* __restri
   const float* q = c.cheb + (size_t)f * cheb_floats(c.degree) + rec * kChebRec;
   const float g = q[3], ta = q[4], t2 = q[5];
   const int64_t nn = (int64_t)n * n;
+  float mx = 0.f;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
        e += (int64_t)gridDim.x * blockDim.x) {
     const float id = (e / n == e % n) ? g : 0.f;
-    out[base + e] = id + ta * af[e] + t2 * T2[base + e];
+    const float x = id + ta * af[e] + t2 * T2[base + e];
+    out[base + e] = x;
+    mx = fmaxf(mx, fabsf(x));
   }
+  if (mo.a != nullptr) raise_max(mo.a + f, mx, mo.ver);
 }
 
 template <class C>
@@ -1601,11 +1780,11 @@ int grid_full(const GemmLaunch& g) {
 // ---------------------------------------------------------------------------
 hipError_t launch_pack(const BlockMeta* blocks, const MatMeta* mats, int32_t B, int32_t br,
                        int32_t bc, int32_t grad_bf16, float* Gp, float* GpT, float* Mom,
-                       float momentum, uint16_t* GpH, uint16_t* GpTH, hipStream_t s) {
+                       float momentum, uint16_t* GpH, uint16_t* GpTH, hipStream_t s, MaxOut mo) {
   if (B == 0) return hipSuccess;
   dim3 grid(((br + 63) / 64) * ((bc + 63) / 64), B);
   hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, s, blocks, mats, br, bc, grad_bf16, Gp, GpT,
-                     Mom, momentum, GpH, GpTH);
+                     Mom, momentum, GpH, GpTH, mo);
   return hipGetLastError();
 }
 
@@ -1628,22 +1807,27 @@ hipError_t launch_init_state(float* LR, int64_t nelemL, int32_t nl, int64_t nele
 }
 
 // The split main loop runs K-tiles of 16 in pairs.
-bool split_k_ok(const GemmLaunch& g) {
-  for (int i = 0; i < g.n_problems; ++i)
+// Split modes: K a multiple of 32 (the main loop takes K-tiles in pairs);
+// the fp16 split also needs every operand's maximum words.
+bool split_ok(const GemmLaunch& g, int mode) {
+  if (mode == kGemmF32) return true;
+  for (int i = 0; i < g.n_problems; ++i) {
     if (g.p[i].K % 32 != 0) return false;
+    if (mode == kGemmSplitF16 && (g.p[i].mP == nullptr || g.p[i].mQ == nullptr)) return false;
+  }
   return true;
 }
+bool mode_ok(int mode) { return mode == kGemmF32 || mode == kGemmSplit || mode == kGemmSplitF16; }
 
 hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode, hipStream_t s) {
   if (g.n_problems == 0) return hipSuccess;
-  if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
-  if (mode == kGemmSplit && !split_k_ok(g)) return hipErrorInvalidValue;
+  if (!mode_ok(mode) || !split_ok(g, mode)) return hipErrorInvalidValue;
   int ncols = 0;
   for (int i = 0; i < g.n_problems; ++i) {
     // symmetric problems read both operands the same way; columns on the
     // split path, for the statistics only
     if ((g.p[i].p_cols != 0) != (g.p[i].q_cols != 0)) return hipErrorInvalidValue;
-    if (g.p[i].p_cols != 0 && (mode != kGemmSplit || newton)) return hipErrorInvalidValue;
+    if (g.p[i].p_cols != 0 && (mode == kGemmF32 || newton)) return hipErrorInvalidValue;
     ncols += g.p[i].p_cols != 0;
   }
   if (ncols != 0 && ncols != g.n_problems) {
@@ -1677,9 +1861,14 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
   case T: {                                                                                    \
     const int gx = grid_sym<CFG>(g);                                                           \
     if (!gx) break;                                                                            \
-    if (cols) {                                                                                \
+    if (cols && mode == kGemmSplitF16) {                                                       \
+      hipLaunchKernelGGL((syrk_ema_kernel<CFG, kPathSplitHCols>), dim3(gx, g.n_problems),     \
+                         dim3(CFG::NT), 0, s, g);                                              \
+    } else if (cols) {                                                                         \
       hipLaunchKernelGGL((syrk_ema_kernel<CFG, kPathSplitCols>), dim3(gx, g.n_problems),      \
                          dim3(CFG::NT), 0, s, g);                                              \
+    } else if (mode == kGemmSplitF16) {                                                        \
+      SHP_SYM_LAUNCH(CFG, kPathSplitH)                                                         \
     } else if (mode == kGemmSplit) {                                                           \
       SHP_SYM_LAUNCH(CFG, kPathSplit)                                                          \
     } else {                                                                                   \
@@ -1724,7 +1913,13 @@ void launch_full_cfg(const GemmLaunch& g, int mode, bool pcols, bool qcols, hipS
   const int gx = grid_full<CFG>(g);
   if (!gx) return;
   const dim3 grid(gx, g.n_problems), block(CFG::NT);
-  if (mode == kGemmSplit && qcols)
+  if (mode == kGemmSplitF16 && qcols)
+    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplitH, false, true>), grid, block, 0, s, g);
+  else if (mode == kGemmSplitF16 && pcols)
+    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplitH, true, false>), grid, block, 0, s, g);
+  else if (mode == kGemmSplitF16)
+    hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplitH, false, false>), grid, block, 0, s, g);
+  else if (mode == kGemmSplit && qcols)
     hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, false, true>), grid, block, 0, s, g);
   else if (mode == kGemmSplit && pcols)
     hipLaunchKernelGGL((apply_left_kernel<CFG, kPathSplit, true, false>), grid, block, 0, s, g);
@@ -1737,7 +1932,9 @@ template <class CFG>
 void launch_update_cfg(const GemmLaunch& g, const UpdateArgs& u, int mode, hipStream_t s) {
   const int gx = grid_full<CFG>(g);
   if (!gx) return;
-  if (mode == kGemmSplit)
+  if (mode == kGemmSplitF16)
+    hipLaunchKernelGGL((apply_update_kernel<CFG, kPathSplitH>), dim3(gx), dim3(CFG::NT), 0, s, g, u);
+  else if (mode == kGemmSplit)
     hipLaunchKernelGGL((apply_update_kernel<CFG, kPathSplit>), dim3(gx), dim3(CFG::NT), 0, s, g, u);
   else if constexpr (CFG::BM <= 128)
     hipLaunchKernelGGL((apply_update_kernel<CFG, kPathF32>), dim3(gx), dim3(CFG::NT), 0, s, g, u);
@@ -1746,14 +1943,13 @@ void launch_update_cfg(const GemmLaunch& g, const UpdateArgs& u, int mode, hipSt
 
 hipError_t launch_gemm_full(const GemmLaunch& g, int tile, int mode, hipStream_t s) {
   if (g.n_problems == 0) return hipSuccess;
-  if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
+  if (!mode_ok(mode) || !split_ok(g, mode)) return hipErrorInvalidValue;
   const bool pcols = g.p[0].p_cols != 0, qcols = g.p[0].q_cols != 0;
   for (int i = 1; i < g.n_problems; ++i)
     if ((g.p[i].p_cols != 0) != pcols || (g.p[i].q_cols != 0) != qcols) return hipErrorInvalidValue;
-  if ((pcols || qcols) && mode != kGemmSplit) return hipErrorInvalidValue;
+  if ((pcols || qcols) && mode == kGemmF32) return hipErrorInvalidValue;
   if (pcols && qcols) return hipErrorInvalidValue;  // no kernel reads both by columns
-  if (mode == kGemmSplit && !split_k_ok(g)) return hipErrorInvalidValue;
-  if (tile == 256 && mode != kGemmSplit) return hipErrorInvalidValue;
+  if (tile == 256 && mode == kGemmF32) return hipErrorInvalidValue;
   switch (tile) {
     case 256: launch_full_cfg<Cfg256>(g, mode, pcols, qcols, s); break;
     case 128: launch_full_cfg<Cfg128>(g, mode, pcols, qcols, s); break;
@@ -1767,9 +1963,8 @@ hipError_t launch_gemm_full(const GemmLaunch& g, int tile, int mode, hipStream_t
 hipError_t launch_gemm_update(const GemmLaunch& g, const UpdateArgs& u, int tile, int mode,
                               hipStream_t s) {
   if (g.n_problems != 1 || g.p[0].p_cols != 0 || g.p[0].q_cols != 0) return hipErrorInvalidValue;
-  if (mode != kGemmF32 && mode != kGemmSplit) return hipErrorInvalidValue;
-  if (mode == kGemmSplit && !split_k_ok(g)) return hipErrorInvalidValue;
-  if (tile == 256 && mode != kGemmSplit) return hipErrorInvalidValue;
+  if (!mode_ok(mode) || !split_ok(g, mode)) return hipErrorInvalidValue;
+  if (tile == 256 && mode == kGemmF32) return hipErrorInvalidValue;
   switch (tile) {
     case 256: launch_update_cfg<Cfg256>(g, u, mode, s); break;
     case 128: launch_update_cfg<Cfg128>(g, u, mode, s); break;
@@ -1789,11 +1984,12 @@ hipError_t launch_norms(const float* A, FactorSet fs, NewtonCtl c, hipStream_t s
 }
 
 hipError_t launch_newton_init(const float* A, float* M0, float* X1, FactorSet fs, NewtonCtl c,
-                              hipStream_t s) {
+                              hipStream_t s, MaxOut mo) {
   if (fs.B == 0) return hipSuccess;
   const int nmax = fs.max_side();
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
-  hipLaunchKernelGGL(newton_init_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, A, M0, X1, fs, c);
+  hipLaunchKernelGGL(newton_init_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, A, M0, X1, fs, c,
+                     mo);
   return hipGetLastError();
 }
 
@@ -1806,12 +2002,12 @@ hipError_t launch_newton_check(FactorSet fs, NewtonCtl c, int32_t iter, int32_t 
 }
 
 hipError_t launch_newton_final(float* Xroot, const float* Xalt, FactorSet fs, NewtonCtl c,
-                               int32_t scale, hipStream_t s) {
+                               int32_t scale, hipStream_t s, MaxOut mo) {
   if (fs.B == 0) return hipSuccess;
   const int nmax = fs.max_side();
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
   hipLaunchKernelGGL(newton_final_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, Xroot, Xalt, fs,
-                     c, scale);
+                     c, scale, mo);
   return hipGetLastError();
 }
 
@@ -1822,23 +2018,23 @@ hipError_t launch_cheb_setup(FactorSet fs, NewtonCtl c, hipStream_t s) {
 }
 
 hipError_t launch_cheb_combine(const float* Ahat, const float* T2, float* out, FactorSet fs,
-                               NewtonCtl c, int32_t rec, hipStream_t s) {
+                               NewtonCtl c, int32_t rec, hipStream_t s, MaxOut mo) {
   if (fs.B == 0) return hipSuccess;
   if (rec < 0 || rec >= cheb_floats(c.degree) / kChebRec) return hipErrorInvalidValue;
   const int nmax = fs.max_side();
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
   hipLaunchKernelGGL(cheb_combine_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, Ahat, T2, out,
-                     fs, c, rec);
+                     fs, c, rec, mo);
   return hipGetLastError();
 }
 
 hipError_t launch_db_stage2_init(float* Ybuf0, const float* Ybuf1, float* Z0buf, FactorSet fs,
-                                 NewtonCtl c, hipStream_t s) {
+                                 NewtonCtl c, hipStream_t s, MaxOut mo) {
   if (fs.B == 0) return hipSuccess;
   const int nmax = fs.max_side();
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
   hipLaunchKernelGGL(db_stage2_init_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, Ybuf0, Ybuf1,
-                     Z0buf, fs, c);
+                     Z0buf, fs, c, mo);
   hipLaunchKernelGGL(db_stage2_reset_kernel, dim3((fs.count() + 255) / 256), dim3(256), 0, s, fs, c);
   return hipGetLastError();
 }

@@ -34,6 +34,23 @@ shp::GemmProblem sym_problem(const float* P, const float* Q, float* C, int64_t s
   return g;
 }
 
+// Maximum words of one of the job's buffers (fp16 split products), or NULL.
+uint64_t* slot_of(const RootJob& j, const float* buf) {
+  if (buf == nullptr) return nullptr;
+  const float* bufs[6] = {j.xroot, j.xalt, j.s[0], j.s[1], j.s[2], j.s[3]};
+  for (int i = 0; i < 6; ++i)
+    if (bufs[i] == buf) return j.mx[i];
+  return nullptr;
+}
+
+shp::MaxOut max_out(shampoo_ctx* h, const RootJob& j, const float* a, const float* b) {
+  shp::MaxOut mo{};
+  mo.a = slot_of(j, a);
+  mo.b = slot_of(j, b);
+  if (mo.a != nullptr || mo.b != nullptr) mo.ver = h->next_ver();
+  return mo;
+}
+
 // C = alpha P Q + beta D + gamma I over every factor; groups of one side and
 // tile stored back to back share a problem. coef_slot >= 0: the epilogue
 // coefficients come per factor from that slot of the scale-mode-3 records.
@@ -68,6 +85,13 @@ void factor_problems(const RootJob& j, SymLaunches& L, const float* P, const flo
       q.resid = j.c.resid;
       q.resid_stride = j.c.resid_stride;
     }
+    // operand and result maxima of the fp16 split (member i is factor f0 + i)
+    uint64_t* mp = slot_of(j, P);
+    uint64_t* mq = slot_of(j, Q);
+    uint64_t* mc = slot_of(j, C);
+    q.mP = mp != nullptr ? mp + q.f0 : nullptr;
+    q.mQ = mq != nullptr ? mq + q.f0 : nullptr;
+    q.mC = mc != nullptr ? mc + q.f0 : nullptr;
     int li = 0;
     while (li < L.n && L.tile[li] != j.tile[g]) ++li;
     if (li == L.n) {
@@ -80,10 +104,14 @@ void factor_problems(const RootJob& j, SymLaunches& L, const float* P, const flo
   }
 }
 
-int launch_all(shampoo_ctx* h, const SymLaunches& L, double flops, hipStream_t s) {
+int launch_all(shampoo_ctx* h, const RootJob& j, const SymLaunches& L, double flops,
+               hipStream_t s) {
   for (int i = 0; i < L.n; ++i) {
+    shp::GemmLaunch g = L.g[i];
+    const uint64_t ver = h->next_ver();
+    for (int k = 0; k < g.n_problems; ++k) g.p[k].ver = ver;
     const int rc = timed(h, kNewtonGemm, i == 0 ? flops : 0.0, 0.0, s,
-                         [&] { return shp::launch_gemm_sym(L.g[i], L.tile[i], true, h->cfg.fp32_gemm, s); });
+                         [&] { return shp::launch_gemm_sym(g, L.tile[i], true, j.gemm_mode, s); });
     if (rc) return rc;
   }
   return SHAMPOO_OK;
@@ -108,8 +136,9 @@ int newton(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
   const shp::NewtonCtl& c = j.c;
   int rc = timed(h, kNorms, 0.0, norm_bytes(j), s, [&] { return shp::launch_norms(j.A, fs, c, s); });
   if (rc) return rc;
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_newton_init(j.A, j.s[0], j.xalt, fs, c, s); });
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
+    return shp::launch_newton_init(j.A, j.s[0], j.xalt, fs, c, s, max_out(h, j, j.s[0], j.xalt));
+  });
   if (rc) return rc;
   const double p = c.p;
   const float a2 = (float)(1.0 / (p * p)), b2 = (float)(-2.0 * (p + 1.0) / (p * p)),
@@ -141,18 +170,19 @@ int newton(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
     }
     factor_problems(j, l4, Tp, M, T2, nullptr, 1.f, 0.f, 0.f, true,
                     sc ? shp::kCoefM : -1);  // M <- T^p (mu M)
-    if ((rc = launch_all(h, l1, 0.0, s))) return rc;
-    if ((rc = launch_all(h, l2, 0.0, s))) return rc;
-    if ((rc = launch_all(h, l3, 0.0, s))) return rc;
-    if ((rc = launch_all(h, l4, 0.0, s))) return rc;
+    if ((rc = launch_all(h, j, l1, 0.0, s))) return rc;
+    if ((rc = launch_all(h, j, l2, 0.0, s))) return rc;
+    if ((rc = launch_all(h, j, l3, 0.0, s))) return rc;
+    if ((rc = launch_all(h, j, l4, 0.0, s))) return rc;
     const int before = k == 0 ? per_iter - 1 : per_iter;
     rc = timed(h, kNewtonAux, 0.0, 0.0, s,
                [&] { return shp::launch_newton_check(fs, c, k, 1, before, 0, s); });
     if (rc) return rc;
     std::swap(iM, iT);
   }
-  return timed(h, kNewtonAux, 0.0, 0.0, s,
-               [&] { return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 0, s); });
+  return timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
+    return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 0, s, max_out(h, j, j.xroot, nullptr));
+  });
 }
 
 // Newton-DB: two Denman-Beavers square-root stages in inverse-free form on
@@ -166,8 +196,9 @@ int newton_db(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
   const shp::NewtonCtl& c = j.c;
   int rc = timed(h, kNorms, 0.0, norm_bytes(j), s, [&] { return shp::launch_norms(j.A, fs, c, s); });
   if (rc) return rc;
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_newton_init(j.A, j.s[0], j.xroot, fs, c, s); });
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
+    return shp::launch_newton_init(j.A, j.s[0], j.xroot, fs, c, s, max_out(h, j, j.s[0], j.xroot));
+  });
   if (rc) return rc;
   const int kmax = c.max_iters;
   for (int stage = 0; stage < 2; ++stage) {
@@ -178,7 +209,7 @@ int newton_db(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
       float* Zn = ((k + 1) & 1) ? j.xalt : j.xroot;
       SymLaunches l1;
       factor_problems(j, l1, Z, Y, j.s[2], nullptr, 1.f, 0.f, 0.f, true);  // M = Z Y
-      if ((rc = launch_all(h, l1, 0.0, s))) return rc;
+      if ((rc = launch_all(h, j, l1, 0.0, s))) return rc;
       const int after = k < kmax ? 2 : 0;
       rc = timed(h, kNewtonAux, 0.0, 0.0, s,
                  [&] { return shp::launch_newton_check(fs, c, k, 0, 1, after, s); });
@@ -187,17 +218,19 @@ int newton_db(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
       SymLaunches l2;
       factor_problems(j, l2, Y, j.s[2], Yn, Y, -0.5f, 1.5f, 0.f, false);  // Y (3I - M) / 2
       factor_problems(j, l2, j.s[2], Z, Zn, Z, -0.5f, 1.5f, 0.f, false);  // (3I - M) Z / 2
-      if ((rc = launch_all(h, l2, 0.0, s))) return rc;
+      if ((rc = launch_all(h, j, l2, 0.0, s))) return rc;
     }
     if (stage == 0) {
       rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
-        return shp::launch_db_stage2_init(j.s[0], j.s[1], j.xroot, fs, c, s);
+        return shp::launch_db_stage2_init(j.s[0], j.s[1], j.xroot, fs, c, s,
+                                          max_out(h, j, j.s[0], j.xroot));
       });
       if (rc) return rc;
     }
   }
-  return timed(h, kNewtonAux, 0.0, 0.0, s,
-               [&] { return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 1, s); });
+  return timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
+    return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 1, s, max_out(h, j, j.xroot, nullptr));
+  });
 }
 
 // Chebyshev: X = s^(-1/p) p(Ahat), Ahat = A / s, p = sum_j c_j T_j(y) with
@@ -219,8 +252,9 @@ int chebyshev(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
   if (rc) return rc;
   // Ahat in xalt (identity on tail padding); the records (which mark every
   // factor as a fixed-degree result)
-  rc = timed(h, kNewtonAux, 0.0, 0.0, s,
-             [&] { return shp::launch_newton_init(j.A, j.xalt, nullptr, fs, c, s); });
+  rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
+    return shp::launch_newton_init(j.A, j.xalt, nullptr, fs, c, s, max_out(h, j, j.xalt, nullptr));
+  });
   if (rc) return rc;
   rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] { return shp::launch_cheb_setup(fs, c, s); });
   if (rc) return rc;
@@ -249,7 +283,7 @@ int chebyshev(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
         q.coef = c.cheb + (size_t)rec * shp::kChebRec;
         q.coef_stride = rec_floats;
       }
-    return launch_all(h, L, j.real_cube, s);
+    return launch_all(h, j, L, j.real_cube, s);
   };
   // baby steps: T_2 = (a^2/2) Ahat Ahat + a b Ahat + ..., z = a Ahat T_2 + b T_2 - (a/2) Ahat + ...
   if ((rc = step(Ahat, Ahat, T2, Ahat, nullptr, 0, false))) return rc;
@@ -257,15 +291,17 @@ int chebyshev(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
   // giant steps: beta_m = B_m, then beta_k = B_k + 2 z beta_(k+1) - beta_(k+2)
   // down to p = B_0 + z beta_1 - beta_2
   rc = timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
-    return shp::launch_cheb_combine(Ahat, T2, ring[m % 3], fs, c, 2 + m, s);
+    return shp::launch_cheb_combine(Ahat, T2, ring[m % 3], fs, c, 2 + m, s,
+                                    max_out(h, j, ring[m % 3], nullptr));
   });
   if (rc) return rc;
   for (int k = m - 1; k >= 0; --k) {
     const float* D2 = k + 2 <= m ? ring[(k + 2) % 3] : nullptr;
     if ((rc = step(Z, ring[(k + 1) % 3], ring[k % 3], nullptr, D2, 2 + k, true))) return rc;
   }
-  return timed(h, kNewtonAux, 0.0, 0.0, s,
-               [&] { return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 2, s); });
+  return timed(h, kNewtonAux, 0.0, 0.0, s, [&] {
+    return shp::launch_newton_final(j.xroot, j.xalt, fs, c, 2, s, max_out(h, j, j.xroot, nullptr));
+  });
 }
 
 }  // namespace

@@ -71,8 +71,10 @@ int validate_config(const shampoo_config_t* c, bool tensor) {
                 "root_method must be 0 (coupled Newton), 1 (Newton-DB) or 2 (Chebyshev)");
   if (c->root_method == shp::kChebyshev && (c->cheb_degree < 2 || c->cheb_degree > 1024))
     return fail(SHAMPOO_ERR_INVALID_ARG, "cheb_degree must be in 2..1024");
-  if (c->fp32_gemm != SHAMPOO_GEMM_F32 && c->fp32_gemm != SHAMPOO_GEMM_SPLIT_BF16)
-    return fail(SHAMPOO_ERR_INVALID_ARG, "fp32_gemm must be 0 (fp32 MFMA) or 1 (split bf16)");
+  if (c->fp32_gemm != SHAMPOO_GEMM_F32 && c->fp32_gemm != SHAMPOO_GEMM_SPLIT_BF16 &&
+      c->fp32_gemm != SHAMPOO_GEMM_SPLIT_F16)
+    return fail(SHAMPOO_ERR_INVALID_ARG,
+                "fp32_gemm must be 0 (fp32 MFMA), 1 (split bf16) or 2 (split fp16)");
   if (!std::isfinite(c->momentum) || c->momentum < 0.0 || c->momentum >= 1.0)
     return fail(SHAMPOO_ERR_INVALID_ARG, "momentum must be in [0, 1)");
   if ((c->param_dtype != SHAMPOO_F32 && c->param_dtype != SHAMPOO_BF16) ||
@@ -141,6 +143,7 @@ Plan make_plan(const shampoo_config_t* c, const shampoo_matrix_desc_t* m, int32_
   p.off_s1 = take(fbytes);
   p.off_s2 = take(fbytes);
   p.off_s3 = c->root_method == shp::kChebyshev ? take(fbytes) : -1;  // the giant steps' third buffer
+  p.off_mx = c->fp32_gemm == SHAMPOO_GEMM_SPLIT_F16 ? take((6 * 2 * p.B + 3 * p.B) * 8) : -1;
   p.total = o;
   return p;
 }
@@ -179,6 +182,15 @@ bool m_bf16_stats(const shampoo_ctx* h) { return h->cfg.grad_dtype == SHAMPOO_BF
 uint16_t* m_gpH(const shampoo_ctx* h) { return reinterpret_cast<uint16_t*>(m_s(h, 2)); }
 uint16_t* m_gpTH(const shampoo_ctx* h) { return m_gpH(h) + h->plan.B * h->plan.br * h->plan.bc; }
 float* m_tmpT(const shampoo_ctx* h) { return m_s(h, 1); }  // apply intermediate likewise
+// fp16 split products: maximum words per factor of xroot, xalt, s0, s1, s2,
+// s3 (i = 0..5), then per block of Gp, the momentum buffer and the apply
+// intermediate (i = 6, 7, 8); NULL on the other paths
+bool m_f16(const shampoo_ctx* h) { return h->cfg.fp32_gemm == SHAMPOO_GEMM_SPLIT_F16; }
+uint64_t* m_mx(const shampoo_ctx* h, int i) {
+  if (h->plan.off_mx < 0) return nullptr;
+  const int64_t B = h->plan.B;
+  return h->at<uint64_t>(h->plan.off_mx) + (i < 6 ? i * 2 * B : 12 * B + (i - 6) * B);
+}
 
 shp::FactorSet m_factors(const shampoo_ctx* h) {
   const Plan& plan = h->plan;
@@ -280,11 +292,17 @@ int do_pack(shampoo_ctx* h, hipStream_t s) {
   const double fp32_copies = 1.0 + (want_t ? 1.0 : 0.0) + (p.momentum ? 2.0 : 0.0);
   const double bytes = real * esz + fp32_copies * 4.0 * (double)p.B * p.br * p.bc +
                        (hb ? 2.0 * 2.0 * (double)p.B * p.br * p.bc : 0.0);
+  shp::MaxOut mo{};
+  if (m_f16(h)) {
+    mo.a = m_mx(h, 6);
+    mo.b = p.momentum ? m_mx(h, 7) : nullptr;
+    mo.ver = h->next_ver();
+  }
   return timed(h, kPack, 0.0, bytes, s, [&] {
     return shp::launch_pack(h->at<shp::BlockMeta>(p.off_blocks), h->at<shp::MatMeta>(p.off_mats),
                             (int32_t)p.B, p.br, p.bc, h->cfg.grad_dtype == SHAMPOO_BF16, m_gp(h),
                             want_t ? m_gpT(h) : nullptr, m_mom(h), (float)h->cfg.momentum,
-                            hb ? m_gpH(h) : nullptr, hb ? m_gpTH(h) : nullptr, s);
+                            hb ? m_gpH(h) : nullptr, hb ? m_gpTH(h) : nullptr, s, mo);
   });
 }
 
@@ -314,7 +332,7 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
   // fp32 MFMA: C = P^T Q, so L = beta2 L + g Gp Gp^T reads P = Q = GpT and
   // R = beta2 R + g Gp^T Gp reads P = Q = Gp. Split path: C = A A^T with
   // A = Gp read by rows for L and by columns for R (Gp stored [K = br][M = bc]).
-  const bool split = h->cfg.fp32_gemm == SHAMPOO_GEMM_SPLIT_BF16;
+  const bool split = h->cfg.fp32_gemm != SHAMPOO_GEMM_F32;
   float* opL = split ? m_gp(h) : m_gpT(h);
   g.p[0] = sym_problem(opL, opL, m_lr(h), (int64_t)p.bc * p.br, p.br, p.bc, (int)p.B);
   g.p[1] = sym_problem(m_gp(h), m_gp(h), m_lr(h) + p.fl, (int64_t)p.br * p.bc, p.bc, p.br, (int)p.B);
@@ -324,6 +342,7 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
     g.p[i].beta = (float)h->cfg.beta2;
     g.p[i].D = g.p[i].C;  // EMA: reads the old statistic in place
     g.p[i].sD = g.p[i].sC;
+    g.p[i].mP = g.p[i].mQ = m_mx(h, 6);  // fp16 split: the packed blocks' maxima
   }
   g.n_problems = 2;
   const bool hb = m_bf16_stats(h);
@@ -361,6 +380,8 @@ int do_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
   for (int i = 0; i < 3; ++i) j.s[i] = m_s(h, i);
   j.s[3] = p.off_s3 >= 0 ? h->at<float>(p.off_s3) : nullptr;
   j.tile[0] = j.tile[1] = p.tile;
+  j.gemm_mode = h->cfg.fp32_gemm;
+  for (int i = 0; i < 6; ++i) j.mx[i] = m_mx(h, i);
   for (const auto& b : h->blocks)
     j.real_cube += (double)b.m * b.m * (b.m + 1.0) + (double)b.n * b.n * (b.n + 1.0);
   j.t_stats = t_stats;
@@ -375,7 +396,7 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   if (p.B == 0) return SHAMPOO_OK;
   // the preconditioned matrix: the packed gradient, or the momentum buffer
   const float* G = p.momentum ? m_mom(h) : m_gp(h);
-  const bool split = h->cfg.fp32_gemm == SHAMPOO_GEMM_SPLIT_BF16;
+  const bool split = h->cfg.fp32_gemm != SHAMPOO_GEMM_F32;
   shp::GemmLaunch g1{};
   shp::GemmProblem a{};
   if (split) {
@@ -403,6 +424,12 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   a.K = p.br;
   a.batch = (int)p.B;
   a.alpha = 1.f;
+  if (m_f16(h)) {  // maxima: left roots, the preconditioned blocks; raises Tmp's
+    a.mP = m_mx(h, 0);
+    a.mQ = m_mx(h, p.momentum ? 7 : 6);
+    a.mC = m_mx(h, 8);
+    a.ver = h->next_ver();
+  }
   g1.p[0] = a;
   g1.n_problems = 1;
   // U = X_L G X_R (br x bc). fp32 MFMA: U[m][n] = sum_k TmpT[k][m] X_R[k][n];
@@ -419,6 +446,10 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   b.K = p.bc;
   b.batch = (int)p.B;
   b.alpha = 1.f;
+  if (m_f16(h)) {  // maxima: Tmp, right roots
+    b.mP = m_mx(h, 8);
+    b.mQ = m_mx(h, 0) + p.B;
+  }
   g2.p[0] = b;
   g2.n_problems = 1;
   shp::UpdateArgs u{};
@@ -469,7 +500,7 @@ int shampoo_config_default(shampoo_config_t* cfg) {
   cfg->momentum = 0.0;
   cfg->root_method = shp::kCoupledNewton;
   cfg->cheb_degree = 128;
-  cfg->fp32_gemm = SHAMPOO_GEMM_SPLIT_BF16;
+  cfg->fp32_gemm = SHAMPOO_GEMM_SPLIT_F16;
   return SHAMPOO_OK;
 }
 
@@ -550,6 +581,8 @@ int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats,
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(plan.off_flops), 0, 8, s);
     if (e == hipSuccess && plan.momentum)
       e = hipMemsetAsync(h->at<void>(plan.off_mom), 0, plan.B * plan.br * plan.bc * 4, s);
+    if (e == hipSuccess && plan.off_mx >= 0)  // no maximum word written yet
+      e = hipMemsetAsync(h->at<void>(plan.off_mx), 0, (6 * 2 * plan.B + 3 * plan.B) * 8, s);
     if (e == hipSuccess)
       e = shp::launch_init_state(m_lr(h), plan.fl, plan.br, plan.fr, plan.bc, (int32_t)plan.B,
                                  (float)cfg->eps, s);
@@ -624,6 +657,7 @@ int shampoo_state_layout(shampoo_t h, shampoo_layout_t* out) {
   out->newton_residual = h->plan.off_rprev;
   out->momentum = h->plan.off_mom;
   out->workspace_bytes = h->plan.total;
+  out->root_maxima = h->plan.off_mx;
   return SHAMPOO_OK;
 }
 
@@ -636,6 +670,13 @@ int shampoo_get_step(shampoo_t h, int64_t* t_out) {
 int shampoo_set_step(shampoo_t h, int64_t t) {
   if (!h || t < 0) return fail(SHAMPOO_ERR_INVALID_ARG, "NULL handle or negative step");
   h->t = t;
+  return SHAMPOO_OK;
+}
+
+int shampoo_restore(shampoo_t h, int64_t t) {
+  if (!h || t < 0) return fail(SHAMPOO_ERR_INVALID_ARG, "NULL handle or negative step");
+  h->t = t;
+  h->roots_valid = t > 0;
   return SHAMPOO_OK;
 }
 

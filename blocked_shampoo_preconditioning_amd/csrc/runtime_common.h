@@ -52,6 +52,11 @@ struct Plan {
   int64_t off_blocks, off_mats, off_umats, off_nreal, off_status, off_final, off_scale, off_rprev,
       off_cfac, off_lo, off_coef, off_active, off_flops, off_resid, off_gp, off_mom, off_lr,
       off_xroot, off_xalt, off_s0, off_s1, off_s2, off_s3, off_cheb, total;
+  // fp16 split products: maximum words (uint64, see shp::max_word) per
+  // factor of xroot, xalt, s0..s3 (6 x 2B, xroot's first: the roots') and
+  // per block of Gp, the momentum buffer and the apply intermediate (3 x B);
+  // -1 on the other product paths
+  int64_t off_mx = -1;
   bool momentum = false;
 };
 
@@ -93,6 +98,10 @@ struct shampoo_ctx {
   hipEvent_t meta_copied = nullptr;     // the last upload of meta_host has finished
   int64_t t = 0;
   bool roots_valid = false;
+  // versions of the maximum words: (t + 1) << 24 | launch number within the
+  // step (saturating), so they keep growing across a restore that sets t
+  int64_t ver_t = -1;
+  uint32_t ver_idx = 0;
   float stat_scale = 0.f;
   // timing
   bool timing = false;
@@ -103,6 +112,14 @@ struct shampoo_ctx {
   template <class T>
   T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
   hipEvent_t get_event();
+  uint64_t next_ver() {
+    if (ver_t != t) {
+      ver_t = t;
+      ver_idx = 0;
+    }
+    if (ver_idx < 0xffffffu) ++ver_idx;
+    return ((uint64_t)(t + 1) << 24) | ver_idx;
+  }
 };
 
 namespace shp_rt {
@@ -137,6 +154,10 @@ struct RootJob {
   float* xroot = nullptr;
   float* xalt = nullptr;
   float* s[4] = {nullptr, nullptr, nullptr, nullptr};
+  // how the products run (shp::GemmMode); kGemmSplitF16 needs the maximum
+  // words per factor of xroot, xalt, s[0..3] in mx[0..5]
+  int gemm_mode = shp::kGemmSplit;
+  uint64_t* mx[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   int tile[shp::kMaxGroups] = {32, 32, 32, 32};
   double real_cube = 0.0;  // sum over factors of n^2 (n + 1), n the real extent
   int64_t t_stats = 0;     // step whose statistics are taken (Chebyshev floor)

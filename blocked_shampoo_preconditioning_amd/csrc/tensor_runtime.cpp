@@ -295,7 +295,10 @@ int do_tensor_pack(shampoo_ctx* h, hipStream_t s) {
   });
 }
 
-bool split_gemm(const shampoo_ctx* h) { return h->cfg.fp32_gemm == SHAMPOO_GEMM_SPLIT_BF16; }
+// Tensor handles split their fp32 products into bf16 terms under either split
+// setting: the fp16 split needs every operand's recorded maximum, which the
+// mode products' intermediates do not keep.
+bool split_gemm(const shampoo_ctx* h) { return h->cfg.fp32_gemm != SHAMPOO_GEMM_F32; }
 
 int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
   const TensorState& ts = T(h);
@@ -484,6 +487,7 @@ int tensor_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
     for (int g = 0; g < ts.nbig; ++g) j.tile[g] = ts.stat_tile[ts.big[g]];
     j.real_cube = ts.real_cube;
     j.t_stats = t_stats;
+    j.gemm_mode = split_gemm(h) ? shp::kGemmSplit : shp::kGemmF32;
     const int rc = run_roots(h, j, s);
     if (rc) return rc;
   }
@@ -556,6 +560,7 @@ int tensor_layout(const shampoo_ctx* h, shampoo_layout_t* out) {
   out->newton_residual = ts.off_rprev;
   out->momentum = ts.off_mom;
   out->workspace_bytes = ts.total;
+  out->root_maxima = -1;
   return SHAMPOO_OK;
 }
 

@@ -29,8 +29,9 @@ SHAMPOO_NO_AUTO_REFRESH = 2
 TIMING_CLASSES = ("pack", "stats", "norms", "newton_gemm", "newton_aux", "apply", "stats_aux",
                   "apply_aux")
 ROOT_METHODS = {"newton": 0, "newton_db": 1, "chebyshev": 2}
-# shampoo_fp32_gemm_t: fp32 MFMA, or fp32 operands split into three bf16 terms
-GEMM_MODES = {"f32": 0, "split": 1}
+# shampoo_fp32_gemm_t: fp32 MFMA, fp32 operands split into three bf16 terms,
+# or scaled and split into two fp16 terms
+GEMM_MODES = {"f32": 0, "split": 1, "split16": 2}
 
 
 class MatrixDesc(ctypes.Structure):
@@ -51,7 +52,8 @@ class Config(ctypes.Structure):
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("n_blocks", "grad_packed", "stats", "roots",
                                               "newton_status", "newton_iters", "newton_scale",
-                                              "newton_residual", "momentum", "workspace_bytes")]
+                                              "newton_residual", "momentum", "workspace_bytes",
+                                              "root_maxima")]
 
 
 class Timing(ctypes.Structure):
@@ -96,6 +98,7 @@ _SIGNATURES = {
     "shampoo_state_layout": [_P, ctypes.POINTER(Layout)],
     "shampoo_get_step": [_P, ctypes.POINTER(ctypes.c_int64)],
     "shampoo_set_step": [_P, ctypes.c_int64],
+    "shampoo_restore": [_P, ctypes.c_int64],
     "shampoo_pack": [_P, _PP, _P],
     "shampoo_unpack": [_P, _PP, _P],
     "shampoo_precondition": [_P, _P, _P],
@@ -218,6 +221,10 @@ def shampoo_set_step(h, t):
     _check(load_library().shampoo_set_step(h, t))
 
 
+def shampoo_restore(h, t):
+    _check(load_library().shampoo_restore(h, t))
+
+
 def shampoo_pack(h, grad_ptrs, stream):
     g, _gk = _ptr_array(grad_ptrs)
     _check(load_library().shampoo_pack(h, g, ctypes.c_void_p(stream)))
@@ -308,7 +315,7 @@ class Shampoo:
     def __init__(self, shapes, block_rows=1024, block_cols=1024, beta2=0.999, eps=1e-6, lr=1e-3,
                  root_every=10, stat_scale=None, newton_max_iters=25, newton_tol=1e-6,
                  newton_scale_mode=3, dtype="f32", device="cuda", lds=None, momentum=0.0,
-                 root_method="newton", cheb_degree=128, fp32_gemm="split"):
+                 root_method="newton", cheb_degree=128, fp32_gemm="split16"):
         import torch
         self.torch = torch
         self.shapes = [tuple(int(v) for v in s) for s in shapes]
@@ -412,6 +419,12 @@ class Shampoo:
 
     def roots(self):
         return self._factors(self.layout.roots)
+
+    def root_maxima(self):
+        """Versioned exponent words of the roots (fp16 split products only)."""
+        if self.layout.root_maxima < 0:
+            return None
+        return self._view(self.layout.root_maxima, 2 * self.n_blocks, self.torch.int64)
 
     def newton_info(self):
         B = self.n_blocks

@@ -67,13 +67,31 @@ typedef enum { SHAMPOO_F32 = 0, SHAMPOO_BF16 = 1 } shampoo_dtype_t;
  * iterations, preconditioning) run on the matrix cores. */
 typedef enum {
   SHAMPOO_GEMM_F32 = 0,        /* fp32 MFMA (32x32x2)                           */
-  SHAMPOO_GEMM_SPLIT_BF16 = 1  /* each fp32 operand split exactly into three
+  SHAMPOO_GEMM_SPLIT_BF16 = 1, /* each fp32 operand split exactly into three
                                   bf16 terms x = h + m + l; the six products
                                   hh, hm, mh, hl, mm, lh on the bf16 MFMA
                                   (32x32x16), each exact in fp32, accumulated
                                   in fp32: the dropped terms are below 2^-24
                                   of |x y|, so the result has fp32 accuracy,
-                                  at 6/16 of the fp32 MFMA time (default)    */
+                                  at 6/16 of the fp32 MFMA time              */
+  SHAMPOO_GEMM_SPLIT_F16 = 2   /* each fp32 operand scaled by a power of two
+                                  (exact) that puts its largest |value| in
+                                  [2^14, 2^15), then split into two fp16
+                                  terms x = h + l + d, |d| <= 2^-22 |x| (or
+                                  2^-39 of the largest |value| for tiny x);
+                                  the three products hh, hl, lh on the fp16
+                                  MFMA (32x32x16), exact in fp32, accumulated
+                                  in fp32 and scaled back (exact): errors of
+                                  order 2^-21 |x y| per term, fp32 level, at
+                                  3/16 of the fp32 MFMA time. Every kernel
+                                  that writes a product operand records the
+                                  binary exponent of its largest |value| per
+                                  block or factor (64-bit words with a
+                                  version that grows with the step counter
+                                  and the launch); the roots' words are part
+                                  of the state (layout.root_maxima). Tensor
+                                  handles take the bf16 split instead
+                                  (default)                                  */
 } shampoo_fp32_gemm_t;
 
 /* Flags of shampoo_step. */
@@ -157,11 +175,13 @@ typedef struct {
                                         size in the workspace                  */
   int32_t cheb_degree;            /* 2..1024, default 128                        */
   int32_t fp32_gemm;              /* shampoo_fp32_gemm_t; default
-                                     SHAMPOO_GEMM_SPLIT_BF16. Statistics of bf16
+                                     SHAMPOO_GEMM_SPLIT_F16. Statistics of bf16
                                      gradients always take the bf16 MFMA
-                                     directly; a tensor dimension whose
-                                     unfolding pads to an odd multiple of 16
-                                     keeps its statistics on the fp32 MFMA   */
+                                     directly; tensor handles run the bf16
+                                     split under either split setting, and a
+                                     tensor dimension whose unfolding pads to
+                                     an odd multiple of 16 keeps its
+                                     statistics on the fp32 MFMA              */
 } shampoo_config_t;
 
 /* Byte offsets of the state inside the caller's workspace (for inspection
@@ -184,6 +204,12 @@ typedef struct {
   int64_t newton_residual; /* fp32 [2B]: ||M - I||_F / sqrt(n) of the kept iterate  */
   int64_t momentum;       /* fp32 [B][br][bc] momentum, or -1 when it is off         */
   int64_t workspace_bytes;
+  int64_t root_maxima;    /* fp32_gemm = SHAMPOO_GEMM_SPLIT_F16 only, else -1:
+                             uint64 [2B], per root (left factors first) the
+                             versioned binary exponent of its largest |value|,
+                             which the preconditioning products scale by. Part
+                             of the state: a checkpoint keeps it with the roots,
+                             and a restore writes both (shampoo_restore)       */
 } shampoo_layout_t;
 
 /* Accumulated kernel time per class while timing is enabled (milliseconds,
@@ -247,6 +273,15 @@ int shampoo_destroy(shampoo_t h);
 int shampoo_state_layout(shampoo_t h, shampoo_layout_t* out);
 int shampoo_get_step(shampoo_t h, int64_t* t_out);
 int shampoo_set_step(shampoo_t h, int64_t t);
+
+/* Checkpoint restore, after the caller has written the state regions of
+ * shampoo_state_layout (stats, roots, root_maxima when present, momentum
+ * when on, the four Newton records) from a checkpoint taken at step t of a
+ * handle with the same configuration and matrices: sets the step counter to
+ * t and, for t > 0, takes the restored roots as current, so the next step
+ * uses them unless the schedule refreshes them. The following steps then
+ * match the uninterrupted run bit for bit. */
+int shampoo_restore(shampoo_t h, int64_t t);
 
 /* Pack alone: gather the gradient blocks into grad_packed (zero-padded). */
 int shampoo_pack(shampoo_t h, const void* const* grads, void* hip_stream);

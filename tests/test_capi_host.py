@@ -32,7 +32,7 @@ def test_config_default(lib):
     assert c.lr == pytest.approx(1e-3) and c.root_every == 10 and c.stat_scale < 0
     assert c.newton_max_iters == 25 and c.newton_scale_mode == 3 and c.momentum == 0.0
     assert c.root_method == 0 and c.cheb_degree == 128
-    assert c.fp32_gemm == 1  # fp32 products as three bf16 terms on the bf16 MFMA
+    assert c.fp32_gemm == 2  # fp32 products as two scaled fp16 terms on the fp16 MFMA
     assert lib.shampoo_config_default(None) == S.SHAMPOO_ERR_INVALID_ARG
 
 
@@ -76,7 +76,7 @@ def test_workspace_size_grows_with_blocks(lib):
     ("momentum", 1.0, S.SHAMPOO_ERR_INVALID_ARG),
     ("root_method", 3, S.SHAMPOO_ERR_UNSUPPORTED),
     ("momentum", -0.1, S.SHAMPOO_ERR_INVALID_ARG),
-    ("fp32_gemm", 2, S.SHAMPOO_ERR_INVALID_ARG),
+    ("fp32_gemm", 3, S.SHAMPOO_ERR_INVALID_ARG),
     ("fp32_gemm", -1, S.SHAMPOO_ERR_INVALID_ARG),
 ])
 def test_config_validation(lib, field, value, code):
@@ -123,6 +123,7 @@ def test_null_handle_everywhere(lib):
     assert lib.shampoo_state_layout(None, None) == E
     assert lib.shampoo_get_step(None, None) == E
     assert lib.shampoo_set_step(None, 3) == E
+    assert lib.shampoo_restore(None, 3) == E
     assert lib.shampoo_pack(None, None, None) == E
     assert lib.shampoo_unpack(None, None, None) == E
     assert lib.shampoo_precondition(None, None, None) == E

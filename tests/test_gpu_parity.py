@@ -531,7 +531,7 @@ def test_largest_block_4096():
     sh.close()
 
 
-@pytest.mark.parametrize("gemm", ["f32", "split"])
+@pytest.mark.parametrize("gemm", ["f32", "split", "split16"])
 @pytest.mark.parametrize("block,shapes", [
     ((256, 256), ((300, 520), (256, 256), (130, 71))),   # 128-tiles, ragged tails
     ((512, 256), ((600, 300), (512, 256))),              # split apply on 256-tiles, 2 x 1
@@ -539,10 +539,11 @@ def test_largest_block_4096():
     ((64, 32), ((70, 45), (32, 32))),                    # 32-tiles
 ])
 def test_fp32_gemm_paths_every_block(gemm, block, shapes):
-    """Both product paths (fp32 MFMA; fp32 operands split into three bf16
-    terms) on every tile size (the split apply takes 256-tiles when both
-    block sides allow), with and without momentum (the split apply reads the
-    preconditioned matrix by columns): every block at every step."""
+    """Every product path (fp32 MFMA; fp32 operands split into three bf16
+    terms; scaled and split into two fp16 terms) on every tile size (the
+    split apply takes 256-tiles when both block sides allow), with and
+    without momentum (the split apply reads the preconditioned matrix by
+    columns): every block at every step."""
     for momentum in (0.0, 0.9):
         w = workload("gpt_small_b256", shapes=shapes, block_rows=block[0], block_cols=block[1],
                      root_every=2, steps=4, seed=31, fp32_gemm=gemm, momentum=momentum)
@@ -560,12 +561,15 @@ def test_split_products_have_fp32_accuracy():
     over two decades, so the statistics span four): the statistics against
     the fp64 oracle, and the preconditioned update against X_L G X_R formed
     in fp64 from the GPU's own roots, so only the products' rounding is
-    measured. The split path (three bf16 terms per operand, six products)
-    must be as accurate as the fp32 MFMA, within a factor 2. (The update's
-    two products lose a few ulps to the roots' conditioning on either path:
-    about 3e-6 here, against 3e-7 for the statistics.)"""
+    measured. The bf16 split (three bf16 terms per operand, six products)
+    must be as accurate as the fp32 MFMA, within a factor 2; so must the
+    fp16 split (two fp16 terms, three products), whose terms carry 22 bits
+    against the bf16 split's 24 (2^-22 per operand against fp32
+    accumulation's own rounding over the K sums). (The update's two products
+    lose a few ulps to the roots' conditioning on every path: about 3e-6
+    here, against 3e-7 for the statistics.)"""
     errs = {}
-    for gemm in ("f32", "split"):
+    for gemm in ("f32", "split", "split16"):
         w = workload("gpt_small_b256", shapes=((512, 384), (300, 256)), block_rows=256,
                      block_cols=256, root_every=1, steps=1, seed=41, eps=1e-10, grad_std=1.0,
                      fp32_gemm=gemm)
@@ -585,17 +589,22 @@ def test_split_products_have_fp32_accuracy():
         errs[gemm] = (recs[0].stats_err, ue)
         log(f"  {gemm}: statistics {recs[0].stats_err:.2e} products of the update {ue:.2e}")
         sh.close()
-    (s32, u32), (ssp, usp) = errs["f32"], errs["split"]
-    assert ssp <= 1e-6 and usp <= 2e-5, errs
-    assert ssp <= 2 * s32 + 1e-7 and usp <= 2 * u32 + 1e-7, errs
+    s32, u32 = errs["f32"]
+    for gemm in ("split", "split16"):
+        ssp, usp = errs[gemm]
+        assert ssp <= 1e-6 and usp <= 2e-5, errs
+        assert ssp <= 2 * s32 + 1e-7 and usp <= 2 * u32 + 1e-7, errs
 
 
-@pytest.mark.parametrize("gemm", ["f32", "split"])
+@pytest.mark.parametrize("gemm", ["f32", "split", "split16"])
 def test_statistics_scale_exactly_with_powers_of_two(gemm):
     """Gradients scaled by 2^k give statistics scaled by exactly 4^k, bit for
     bit: every bf16 term of the split scales exactly, as does every fp32
-    product and sum (eps = 1e-30 vanishes in the rounding of the diagonal).
-    A wrong exponent, sign or remainder bit in the split breaks the
+    product and sum (eps = 1e-30 vanishes in the rounding of the diagonal);
+    the fp16 split scales each operand by a power of two from its recorded
+    maximum, so its fp16 terms are the same bits at every k (at k = -20 the
+    gradients, about 1e-8, are below fp16's normal range without that
+    scaling). A wrong exponent, sign or remainder bit in the split breaks the
     equality. Full 256-blocks (a padded tail keeps eps on its diagonal, which
     does not scale), 128-tiles, three steps; roots at the first step only."""
     shapes = ((512, 256), (256, 512))
@@ -613,3 +622,50 @@ def test_statistics_scale_exactly_with_powers_of_two(gemm):
     for k in (20, -20):
         for a, b in zip(stats[k], stats[0]):
             assert torch.equal(a, b * 4.0 ** k), (gemm, k, float((a - b * 4.0 ** k).abs().max()))
+
+
+@pytest.mark.parametrize("gemm", ["split", "split16"])
+def test_restore_from_documented_state_matches_uninterrupted(gemm):
+    """Checkpoint and restore through the documented state (statistics,
+    roots, root maxima on the fp16 split, momentum, the Newton records) and
+    shampoo_restore into a fresh handle, between two refreshes: the following
+    steps, a refresh among them, give bit-identical parameters to an
+    uninterrupted run. On the fp16
+    split the restored root maxima scale the first products after the
+    restore, and the next refresh's words must win over the restored ones."""
+    shapes = ((300, 520), (256, 256))
+    kw = dict(root_every=3, momentum=0.9, fp32_gemm=gemm)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    grads = [[torch.randn(s, generator=gen, device="cuda") * 1e-3 for s in shapes] for _ in range(7)]
+    ref = S.Shampoo(shapes, 256, 256, **kw)
+    p_ref = [torch.zeros(s, device="cuda") for s in shapes]
+    for t in range(7):
+        ref.step(p_ref, grads[t])
+    a = S.Shampoo(shapes, 256, 256, **kw)
+    p = [torch.zeros(s, device="cuda") for s in shapes]
+    for t in range(4):
+        a.step(p, grads[t])
+    torch.cuda.synchronize()
+
+    def regions(sh):
+        out = list(sh.stats()) + list(sh.roots()) + [sh.momentum_buffer(), sh.newton_residual()]
+        out += list(sh.newton_info())
+        if sh.root_maxima() is not None:
+            out.append(sh.root_maxima())
+        return out
+
+    saved = [x.clone() for x in regions(a)]
+    t_saved = a.t
+    a.close()
+    b = S.Shampoo(shapes, 256, 256, **kw)
+    for dst, src in zip(regions(b), saved):
+        dst.copy_(src)
+    S.shampoo_restore(b.handle, t_saved)
+    for t in range(4, 7):
+        b.step(p, grads[t])
+    torch.cuda.synchronize()
+    for x, y in zip(p, p_ref):
+        assert torch.equal(x, y), float((x - y).abs().max())
+    assert b.n_diverged() == 0
+    b.close()
+    ref.close()
