@@ -1144,8 +1144,28 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
     tile[row][c + 2] = v.z;
     tile[row][c + 3] = v.w;
   }
-  if (mo.a != nullptr) raise_max(mo.a + b, mg, mo.ver);
-  if (mo.b != nullptr) raise_max(mo.b + b, mmom, mo.ver);
+  if (mo.a != nullptr || mo.b != nullptr) {
+    // one atomic per workgroup and word (a block's 64 x 64 tiles are many
+    // workgroups raising the same word)
+    __shared__ float red[2][4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      mg = fmaxf(mg, __shfl_xor(mg, o));
+      mmom = fmaxf(mmom, __shfl_xor(mmom, o));
+    }
+    if ((tid & 63) == 0) {
+      red[0][tid >> 6] = mg;
+      red[1][tid >> 6] = mmom;
+    }
+    __syncthreads();
+    if (tid < 2) {
+      uint64_t* slot = tid == 0 ? mo.a : mo.b;
+      const float m = fmaxf(fmaxf(red[tid][0], red[tid][1]), fmaxf(red[tid][2], red[tid][3]));
+      if (slot != nullptr)
+        atomicMax(reinterpret_cast<unsigned long long*>(slot + b),
+                  (unsigned long long)max_word(mo.ver, __float_as_uint(m) >> 23));
+    }
+  }
   // no transpose wanted (the split products read the packed block by rows
   // and by columns): done (uniform over the workgroup)
   if (GpT == nullptr && GpTH == nullptr) return;
