@@ -82,8 +82,8 @@ struct GemmProblem {
 // of the largest |value| written with that version (255 for infinity or
 // NaN). Writers raise it by 64-bit atomic max, so the word describes the
 // latest write (a later version wins whatever its exponent) and no word is
-// ever cleared. Versions are below 2^56 and grow with every launch that
-// writes such words (the host numbers them by step and launch).
+// ever cleared. Versions are below 2^56 and grow by one with every launch
+// that writes such words (a per-handle count).
 __host__ __device__ inline uint64_t max_word(uint64_t ver, uint32_t exp_bits) {
   return (ver << 8) | (exp_bits & 0xffu);
 }
@@ -252,6 +252,9 @@ hipError_t launch_cheb_combine(const float* Ahat, const float* T2, float* out, F
 // mo: maxima of Ybuf0 (a) and Z0buf (b) per factor.
 hipError_t launch_db_stage2_init(float* Ybuf0, const float* Ybuf1, float* Z0buf, FactorSet fs,
                                  NewtonCtl c, hipStream_t s, MaxOut mo = MaxOut{});
+// Maximum words w[0 .. n) keep their exponents and take version ver (after a
+// restore wrote words of another handle's versions).
+hipError_t launch_rebase_words(uint64_t* w, int64_t n, uint64_t ver, hipStream_t s);
 
 // Tiles written by a symmetric product of side n with square tile t.
 inline int32_t sym_tiles(int32_t n, int32_t t) {

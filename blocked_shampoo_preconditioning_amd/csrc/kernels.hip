@@ -1667,6 +1667,13 @@ __global__ __launch_bounds__(256) void db_stage2_init_kernel(float* __restrict__
   if (mo.b != nullptr) raise_max(mo.b + f, 1.f, mo.ver);
 }
 
+__global__ __launch_bounds__(256) void rebase_words_kernel(uint64_t* __restrict__ w, int64_t n,
+                                                           uint64_t ver) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    w[i] = max_word(ver, (uint32_t)(w[i] & 0xffu));
+}
+
 // After the copy above has read every factor's final_iter: stage 2 starts.
 __global__ __launch_bounds__(256) void db_stage2_reset_kernel(FactorSet fs, NewtonCtl c) {
   const int f = blockIdx.x * blockDim.x + threadIdx.x;
@@ -2045,6 +2052,13 @@ hipError_t launch_cheb_combine(const float* Ahat, const float* T2, float* out, F
   const int chunks = std::max(1, std::min(64, (int)(((int64_t)nmax * nmax + 4095) / 4096)));
   hipLaunchKernelGGL(cheb_combine_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, Ahat, T2, out,
                      fs, c, rec, mo);
+  return hipGetLastError();
+}
+
+hipError_t launch_rebase_words(uint64_t* w, int64_t n, uint64_t ver, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(rebase_words_kernel, dim3(blocks), dim3(256), 0, s, w, n, ver);
   return hipGetLastError();
 }
 

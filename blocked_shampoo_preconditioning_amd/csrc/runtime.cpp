@@ -673,8 +673,17 @@ int shampoo_set_step(shampoo_t h, int64_t t) {
   return SHAMPOO_OK;
 }
 
-int shampoo_restore(shampoo_t h, int64_t t) {
+int shampoo_restore(shampoo_t h, int64_t t, void* hip_stream) {
   if (!h || t < 0) return fail(SHAMPOO_ERR_INVALID_ARG, "NULL handle or negative step");
+  if (!h->tensor && h->plan.off_mx >= 0) {
+    // words written by another handle carry its versions: take them as this
+    // handle's current ones, so every later write wins over them
+    const uint64_t ver = h->next_ver();
+    const int64_t n = 6 * 2 * h->plan.B + 3 * h->plan.B;
+    const hipError_t e =
+        shp::launch_rebase_words(h->at<uint64_t>(h->plan.off_mx), n, ver, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "rebase of the maximum words");
+  }
   h->t = t;
   h->roots_valid = t > 0;
   return SHAMPOO_OK;

@@ -98,10 +98,9 @@ struct shampoo_ctx {
   hipEvent_t meta_copied = nullptr;     // the last upload of meta_host has finished
   int64_t t = 0;
   bool roots_valid = false;
-  // versions of the maximum words: (t + 1) << 24 | launch number within the
-  // step (saturating), so they keep growing across a restore that sets t
-  int64_t ver_t = -1;
-  uint32_t ver_idx = 0;
+  // version of the last launch that wrote maximum words; grows by one per
+  // such launch (shampoo_restore rebases restored words onto it)
+  uint64_t ver_count = 0;
   float stat_scale = 0.f;
   // timing
   bool timing = false;
@@ -112,14 +111,7 @@ struct shampoo_ctx {
   template <class T>
   T* at(int64_t off) const { return reinterpret_cast<T*>(ws + off); }
   hipEvent_t get_event();
-  uint64_t next_ver() {
-    if (ver_t != t) {
-      ver_t = t;
-      ver_idx = 0;
-    }
-    if (ver_idx < 0xffffffu) ++ver_idx;
-    return ((uint64_t)(t + 1) << 24) | ver_idx;
-  }
+  uint64_t next_ver() { return ++ver_count; }
 };
 
 namespace shp_rt {

@@ -98,7 +98,7 @@ _SIGNATURES = {
     "shampoo_state_layout": [_P, ctypes.POINTER(Layout)],
     "shampoo_get_step": [_P, ctypes.POINTER(ctypes.c_int64)],
     "shampoo_set_step": [_P, ctypes.c_int64],
-    "shampoo_restore": [_P, ctypes.c_int64],
+    "shampoo_restore": [_P, ctypes.c_int64, ctypes.c_void_p],
     "shampoo_pack": [_P, _PP, _P],
     "shampoo_unpack": [_P, _PP, _P],
     "shampoo_precondition": [_P, _P, _P],
@@ -221,8 +221,8 @@ def shampoo_set_step(h, t):
     _check(load_library().shampoo_set_step(h, t))
 
 
-def shampoo_restore(h, t):
-    _check(load_library().shampoo_restore(h, t))
+def shampoo_restore(h, t, stream=None):
+    _check(load_library().shampoo_restore(h, t, stream))
 
 
 def shampoo_pack(h, grad_ptrs, stream):

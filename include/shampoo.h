@@ -87,9 +87,9 @@ typedef enum {
                                   that writes a product operand records the
                                   binary exponent of its largest |value| per
                                   block or factor (64-bit words with a
-                                  version that grows with the step counter
-                                  and the launch); the roots' words are part
-                                  of the state (layout.root_maxima). Tensor
+                                  version that grows with every launch that
+                                  writes them); the roots' words are part of
+                                  the state (layout.root_maxima). Tensor
                                   handles take the bf16 split instead
                                   (default)                                  */
 } shampoo_fp32_gemm_t;
@@ -279,9 +279,12 @@ int shampoo_set_step(shampoo_t h, int64_t t);
  * when on, the four Newton records) from a checkpoint taken at step t of a
  * handle with the same configuration and matrices: sets the step counter to
  * t and, for t > 0, takes the restored roots as current, so the next step
- * uses them unless the schedule refreshes them. The following steps then
- * match the uninterrupted run bit for bit. */
-int shampoo_restore(shampoo_t h, int64_t t);
+ * uses them unless the schedule refreshes them. With root_maxima present it
+ * enqueues on hip_stream (after the caller's copies) one small kernel that
+ * gives every maximum word this handle's current version, keeping its
+ * exponent. The following steps then match the uninterrupted run bit for
+ * bit. */
+int shampoo_restore(shampoo_t h, int64_t t, void* hip_stream);
 
 /* Pack alone: gather the gradient blocks into grad_packed (zero-padded). */
 int shampoo_pack(shampoo_t h, const void* const* grads, void* hip_stream);

@@ -123,7 +123,7 @@ def test_null_handle_everywhere(lib):
     assert lib.shampoo_state_layout(None, None) == E
     assert lib.shampoo_get_step(None, None) == E
     assert lib.shampoo_set_step(None, 3) == E
-    assert lib.shampoo_restore(None, 3) == E
+    assert lib.shampoo_restore(None, 3, None) == E
     assert lib.shampoo_pack(None, None, None) == E
     assert lib.shampoo_unpack(None, None, None) == E
     assert lib.shampoo_precondition(None, None, None) == E

@@ -628,7 +628,7 @@ def test_statistics_scale_exactly_with_powers_of_two(gemm):
 def test_restore_from_documented_state_matches_uninterrupted(gemm):
     """Checkpoint and restore through the documented state (statistics,
     roots, root maxima on the fp16 split, momentum, the Newton records) and
-    shampoo_restore into a fresh handle, between two refreshes: the following
+    shampoo_restore into another handle, between two refreshes: the following
     steps, a refresh among them, give bit-identical parameters to an
     uninterrupted run. On the fp16
     split the restored root maxima scale the first products after the
@@ -657,10 +657,15 @@ def test_restore_from_documented_state_matches_uninterrupted(gemm):
     saved = [x.clone() for x in regions(a)]
     t_saved = a.t
     a.close()
+    # the handle restored into has a history of its own (other gradients, a
+    # thousand times larger, and a refresh), which the restore must override
     b = S.Shampoo(shapes, 256, 256, **kw)
+    q = [torch.zeros(s, device="cuda") for s in shapes]
+    for t in range(2):
+        b.step(q, [g * 1e3 for g in grads[6 - t]])
     for dst, src in zip(regions(b), saved):
         dst.copy_(src)
-    S.shampoo_restore(b.handle, t_saved)
+    S.shampoo_restore(b.handle, t_saved, torch.cuda.current_stream().cuda_stream)
     for t in range(4, 7):
         b.step(p, grads[t])
     torch.cuda.synchronize()
