@@ -327,6 +327,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct Split2 {
   uint32_t h, l;
@@ -335,10 +336,11 @@ struct Split2 {
 __device__ __forceinline__ Split2 split2h(float x0, float x1, int e) {
   x0 = ldexpf(x0, e);
   x1 = ldexpf(x1, e);
-  const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-  const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+  // one packed conversion for both high terms (v_cvt_pk_f16_f32)
+  const f16x2 h = __builtin_convertvector((f32x2){x0, x1}, f16x2);
+  const _Float16 l0 = (_Float16)(x0 - (float)h[0]), l1 = (_Float16)(x1 - (float)h[1]);
   Split2 o;
-  o.h = __builtin_bit_cast(uint32_t, (f16x2){h0, h1});
+  o.h = __builtin_bit_cast(uint32_t, h);
   o.l = __builtin_bit_cast(uint32_t, (f16x2){l0, l1});
   return o;
 }

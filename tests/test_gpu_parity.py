@@ -674,3 +674,22 @@ def test_restore_from_documented_state_matches_uninterrupted(gemm):
     assert b.n_diverged() == 0
     b.close()
     ref.close()
+
+
+@pytest.mark.parametrize("scale", [1e-15, 1e12])
+def test_split16_extreme_gradient_magnitudes(scale):
+    """Gradients of about 1e-15 and 1e12, eps scaled with their square (the
+    workload's own ratio, eps = 1e-2 grad_std^2, so the statistics keep their
+    conditioning): the fp16 split scales every operand by its recorded
+    maximum (exponents near +64 and -26 here), where unscaled fp16 would
+    flush the first to zero and overflow the second. Every block at every
+    step against the oracle, roots every other step."""
+    w = workload("gpt_small_b256", shapes=((300, 520), (256, 256)), block_rows=256, block_cols=256,
+                 root_every=2, steps=4, seed=53, grad_std=scale, eps=1e-2 * scale * scale,
+                 fp32_gemm="split16")
+    recs, sh, orc, params, W = run_parity(w, 4)
+    for r in recs:
+        assert r.stats_err <= STATS_TOL, r
+        assert r.update_err <= UPDATE_TOL, r
+    assert sh.n_diverged() == 0
+    sh.close()
