@@ -1263,6 +1263,102 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+// y = A x and, with TWO, yu = A xu for a symmetric factor A (row stride n,
+// real extent nr; x, xu, y, yu in LDS). Wave w owns the 256-column chunks
+// w, w + 4, ... (four consecutive columns a lane) and runs down every row, so
+// y_j = sum_r A_rj x_r, which is (A x)_j since A is symmetric, needs no sum
+// across lanes or waves: one 16-byte load and four FMAs per row and vector.
+// Four partial sums per column (rows r mod 4) keep the fp32 chains short.
+template <bool TWO>
+__device__ __forceinline__ void sym_matvec(const float* __restrict__ Af, int n, int nr,
+                                           const float* x, const float* xu, float* y, float* yu) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int c0 = wave * 256; c0 < nr; c0 += 1024) {
+    const int j = c0 + lane * 4;
+    float4 s[4], t[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      t[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (j + 3 < nr) {
+      const float* col = Af + j;
+      const int r4 = nr & ~3;
+      for (int r = 0; r < r4; r += 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 a = *reinterpret_cast<const float4*>(col + (int64_t)(r + q) * n);
+          const float xr = x[r + q];
+          s[q].x += a.x * xr;
+          s[q].y += a.y * xr;
+          s[q].z += a.z * xr;
+          s[q].w += a.w * xr;
+          if constexpr (TWO) {
+            const float ur = xu[r + q];
+            t[q].x += a.x * ur;
+            t[q].y += a.y * ur;
+            t[q].z += a.z * ur;
+            t[q].w += a.w * ur;
+          }
+        }
+      }
+      for (int r = r4; r < nr; ++r) {
+        const float4 a = *reinterpret_cast<const float4*>(col + (int64_t)r * n);
+        const float xr = x[r];
+        s[0].x += a.x * xr;
+        s[0].y += a.y * xr;
+        s[0].z += a.z * xr;
+        s[0].w += a.w * xr;
+        if constexpr (TWO) {
+          const float ur = xu[r];
+          t[0].x += a.x * ur;
+          t[0].y += a.y * ur;
+          t[0].z += a.z * ur;
+          t[0].w += a.w * ur;
+        }
+      }
+    } else if (j < nr) {
+      // the ragged end of the last chunk: the columns below nr one by one
+      for (int r = 0; r < nr; ++r) {
+        const float* a = Af + (int64_t)r * n + j;
+        const float xr = x[r], ur = TWO ? xu[r] : 0.f;
+        s[0].x += a[0] * xr;
+        if (j + 1 < nr) s[0].y += a[1] * xr;
+        if (j + 2 < nr) s[0].z += a[2] * xr;
+        if constexpr (TWO) {
+          t[0].x += a[0] * ur;
+          if (j + 1 < nr) t[0].y += a[1] * ur;
+          if (j + 2 < nr) t[0].z += a[2] * ur;
+        }
+      }
+    }
+    if (j < nr) {
+      const float4 sv = make_float4((s[0].x + s[1].x) + (s[2].x + s[3].x),
+                                    (s[0].y + s[1].y) + (s[2].y + s[3].y),
+                                    (s[0].z + s[1].z) + (s[2].z + s[3].z),
+                                    (s[0].w + s[1].w) + (s[2].w + s[3].w));
+      const float4 tv = make_float4((t[0].x + t[1].x) + (t[2].x + t[3].x),
+                                    (t[0].y + t[1].y) + (t[2].y + t[3].y),
+                                    (t[0].z + t[1].z) + (t[2].z + t[3].z),
+                                    (t[0].w + t[1].w) + (t[2].w + t[3].w));
+      y[j] = sv.x;
+      if (TWO) yu[j] = tv.x;
+      if (j + 1 < nr) {
+        y[j + 1] = sv.y;
+        if (TWO) yu[j + 1] = tv.y;
+      }
+      if (j + 2 < nr) {
+        y[j + 2] = sv.z;
+        if (TWO) yu[j + 2] = tv.z;
+      }
+      if (j + 3 < nr) {
+        y[j + 3] = sv.w;
+        if (TWO) yu[j + 3] = tv.w;
+      }
+    }
+  }
+}
+
 // Scalar map of one coupled Newton iteration on an eigenvalue m of M scaled
 // by mu: f(mu m) = mu m ((p + 1 - mu m) / p)^p.
 __device__ __forceinline__ double newton_map(double m, int p, double mu) {
@@ -1326,42 +1422,58 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   const float* Af = factor_ptr(A, fs, f, n);
   const int nr = fs.nreal[f];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n4 = nr & ~3;
   const bool db = c.solver == kNewtonDB;
   const bool cheb = c.solver == kChebyshev;
   const bool power = c.scale_mode >= 2 || cheb;
   const bool scaled = c.scale_mode == 3 && c.solver == kCoupledNewton;
   const float inv0 = (float)(1.0 / sqrt((double)nr));
-  // pass 1: squares, absolute row sums, w = A 1 (row sums), the smallest
-  // diagonal entry and (mode 3) wu = A u_0 with u_0 = (1, -1, 1, ...) / sqrt(n)
+  // pass 1, by columns as in sym_matvec: squares, absolute column sums (the
+  // absolute row sums: A is symmetric), w = A 1 (the column sums) and, in
+  // mode 3, wu = A u_0 with u_0 = (1, -1, 1, ...) / sqrt(n); then the smallest
+  // diagonal entry
   double sq = 0.0, rowmax = 0.0, dmin = INFINITY;
-  for (int r = wave; r < nr; r += 4) {
-    const float* row = Af + (int64_t)r * n;
-    dmin = fmin(dmin, (double)row[r]);
-    double as = 0.0, rs = 0.0, alt = 0.0;
-    for (int j = lane * 4; j < n4; j += 256) {
-      const float4 x = *reinterpret_cast<const float4*>(row + j);
-      as += fabs((double)x.x) + fabs((double)x.y) + fabs((double)x.z) + fabs((double)x.w);
-      rs += (double)x.x + (double)x.y + (double)x.z + (double)x.w;
-      alt += (double)x.x - (double)x.y + (double)x.z - (double)x.w;
-      sq += (double)x.x * x.x + (double)x.y * x.y + (double)x.z * x.z + (double)x.w * x.w;
-    }
-    for (int j = n4 + lane; j < nr; j += 64) {
-      const double x = row[j];
-      as += fabs(x);
-      rs += x;
-      alt += (j & 1) ? -x : x;
-      sq += x * x;
+  for (int c0 = wave * 256; c0 < nr; c0 += 1024) {
+    const int j = c0 + lane * 4;
+    if (j >= nr) continue;
+    double as[4] = {0.0, 0.0, 0.0, 0.0}, rs[4] = {0.0, 0.0, 0.0, 0.0}, alt[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int r = 0; r < nr; ++r) {
+      const float* a = Af + (int64_t)r * n + j;
+      float xs[4];
+      if (j + 3 < nr) {
+        const float4 x4 = *reinterpret_cast<const float4*>(a);
+        xs[0] = x4.x;
+        xs[1] = x4.y;
+        xs[2] = x4.z;
+        xs[3] = x4.w;
+      } else {
+        xs[0] = a[0];
+        xs[1] = j + 1 < nr ? a[1] : 0.f;
+        xs[2] = j + 2 < nr ? a[2] : 0.f;
+        xs[3] = 0.f;
+      }
+      const double sgn = (r & 1) ? -1.0 : 1.0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const double x = xs[k];
+        as[k] += fabs(x);
+        rs[k] += x;
+        alt[k] += sgn * x;
+        sq += x * x;
+      }
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      as += __shfl_xor(as, o);
-      rs += __shfl_xor(rs, o);
-      alt += __shfl_xor(alt, o);
+    for (int k = 0; k < 4; ++k) {
+      if (j + k >= nr) break;
+      rowmax = fmax(rowmax, as[k]);
+      if (power) w[j + k] = (float)rs[k];
+      if (scaled) wu[j + k] = (float)(alt[k] * inv0);
     }
-    rowmax = fmax(rowmax, as);
-    if (lane == 0 && power) w[r] = (float)rs;
-    if (lane == 0 && scaled) wu[r] = (float)(alt * inv0);
+  }
+  for (int r = threadIdx.x; r < nr; r += 256) dmin = fmin(dmin, (double)Af[(int64_t)r * n + r]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    rowmax = fmax(rowmax, __shfl_xor(rowmax, o));
+    dmin = fmin(dmin, __shfl_xor(dmin, o));
   }
   if (scaled)
     for (int r = threadIdx.x; r < nr; r += 256) u[r] = (r & 1) ? -inv0 : inv0;
@@ -1382,32 +1494,10 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
     // both): q_j = u_j^T A u_j, u_(j+1) = normalised lam_j u_j - A u_j.
     for (int it = 0; it < kPowerIters; ++it) {
       if (it > 0) {
-        for (int r = wave; r < nr; r += 4) {
-          const float* row = Af + (int64_t)r * n;
-          float d = 0.f, du = 0.f;
-          for (int j = lane * 4; j < n4; j += 256) {
-            const float4 x = *reinterpret_cast<const float4*>(row + j);
-            const float4 y = *reinterpret_cast<const float4*>(v + j);
-            d += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
-            if (scaled) {
-              const float4 z = *reinterpret_cast<const float4*>(u + j);
-              du += x.x * z.x + x.y * z.y + x.z * z.z + x.w * z.w;
-            }
-          }
-          for (int j = n4 + lane; j < nr; j += 64) {
-            d += row[j] * v[j];
-            if (scaled) du += row[j] * u[j];
-          }
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) {
-            d += __shfl_xor(d, o);
-            du += __shfl_xor(du, o);
-          }
-          if (lane == 0) {
-            w[r] = d;
-            if (scaled) wu[r] = du;
-          }
-        }
+        if (scaled)
+          sym_matvec<true>(Af, n, nr, v, u, w, wu);
+        else
+          sym_matvec<false>(Af, n, nr, v, nullptr, w, nullptr);
       }
       __syncthreads();
       double nn = 0.0;
