@@ -117,10 +117,14 @@ int launch_all(shampoo_ctx* h, const RootJob& j, const SymLaunches& L, double fl
   return SHAMPOO_OK;
 }
 
+// Bytes the norm pass reads: every factor (at its padded side) once, and again
+// for each power-iteration step after the first (scale modes 2 and 3, Chebyshev).
 double norm_bytes(const RootJob& j) {
+  const bool power = j.c.scale_mode >= 2 || j.c.solver == shp::kChebyshev;
+  const double passes = power ? shp::kPowerIters : 1.0;
   double b = 0.0;
   for (int g = 0; g < j.fs.n_groups; ++g) b += 4.0 * j.fs.B * (double)j.fs.side[g] * j.fs.side[g];
-  return b;
+  return b * passes;
 }
 
 // Coupled Newton for A^(-1/p), p in {4, 6, 8} (scale mode 3: M scaled by a
