@@ -1571,18 +1571,24 @@ __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restric
   const int nr = fs.nreal[f];
   const float s = c.scale[f], cf = c.cfac[f];
   const float ip = 1.f / (float)c.p, ip1 = (float)(c.p + 1) / (float)c.p;
-  const int64_t nn = (int64_t)n * n;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int r = (int)(e / n), col = (int)(e % n);
-    const float id = (r == col) ? 1.f : 0.f;
-    const float m = (r < nr && col < nr) ? Af[e] / s : id;
-    M0[base + e] = m;
-    mm = fmaxf(mm, fabsf(m));
+  // four consecutive elements of one row per step (sides are multiples of 32)
+  const int nn4 = n * n / 4;
+  for (int e4 = blockIdx.x * blockDim.x + threadIdx.x; e4 < nn4; e4 += gridDim.x * blockDim.x) {
+    const int e = 4 * e4, r = e / n, col = e - r * n;
+    const float4 a = *reinterpret_cast<const float4*>(Af + e);
+    const float av[4] = {a.x, a.y, a.z, a.w};
+    float m[4], x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float id = (r == col + k) ? 1.f : 0.f;
+      m[k] = (r < nr && col + k < nr) ? av[k] / s : id;
+      mm = fmaxf(mm, fabsf(m[k]));
+      x[k] = c.solver == kNewtonDB ? id : cf * (ip1 * id - ip * m[k]);
+    }
+    *reinterpret_cast<float4*>(M0 + base + e) = make_float4(m[0], m[1], m[2], m[3]);
     if (c.solver != kChebyshev) {
-      const float x = c.solver == kNewtonDB ? id : cf * (ip1 * id - ip * m);
-      X1[base + e] = x;
-      mx = fmaxf(mx, fabsf(x));
+      *reinterpret_cast<float4*>(X1 + base + e) = make_float4(x[0], x[1], x[2], x[3]);
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
     }
   }
   if (mo.a != nullptr) raise_max(mo.a + f, mm, mo.ver);
@@ -1712,19 +1718,28 @@ __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ X
   const float* xf = factor_ptr(Xroot, fs, f, n);
   const int64_t base = xf - Xroot;
   const float cf = c.cfac[f];
-  const int64_t nn = (int64_t)n * n;
+  // four consecutive elements of one row per step (sides are multiples of 32)
+  const int nn4 = n * n / 4;
   float mx = 0.f;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < nn;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    float x;
-    if (dead)
-      x = 0.f;
-    else if (scale)
-      x = cf * (odd ? Xalt[base + e] : Xroot[base + e]);
-    else
-      x = (k == 0) ? ((e / n == e % n) ? cf : 0.f) : Xalt[base + e];
-    Xroot[base + e] = x;
-    mx = fmaxf(mx, fabsf(x));
+  for (int e4 = blockIdx.x * blockDim.x + threadIdx.x; e4 < nn4; e4 += gridDim.x * blockDim.x) {
+    const int e = 4 * e4, r = e / n, col = e - r * n;
+    float4 x;
+    if (dead) {
+      x = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else if (scale || k > 0) {
+      x = *reinterpret_cast<const float4*>((scale && !odd ? Xroot : Xalt) + base + e);
+      if (scale) {
+        x.x *= cf;
+        x.y *= cf;
+        x.z *= cf;
+        x.w *= cf;
+      }
+    } else {  // X_0 = s^(-1/p) I
+      x = make_float4(r == col ? cf : 0.f, r == col + 1 ? cf : 0.f, r == col + 2 ? cf : 0.f,
+                      r == col + 3 ? cf : 0.f);
+    }
+    *reinterpret_cast<float4*>(Xroot + base + e) = x;
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
   }
   if (mo.a != nullptr) raise_max(mo.a + f, mx, mo.ver);
 }
