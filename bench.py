@@ -160,7 +160,7 @@ def cpu_baseline_tensor(w, grad_sets, budget_s=15.0, max_blocks=16, seed=0):
 
 def class_table(tm, paths):
     """Per timing class: time, launches, TFLOP/s and the fraction of the
-    peak of its matrix-core path (paths: class -> "f32" | "bf16" | "split")."""
+    peak of its matrix-core path (paths: class -> "f32" | "bf16" | "split" | "split16")."""
     kernels = {}
     for name, d in tm.items():
         entry = {"ms": round(d["ms"], 3), "launches": d["launches"]}

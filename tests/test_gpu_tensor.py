@@ -238,10 +238,11 @@ def test_tensor_empty_and_zero_tensors():
     sh.close()
 
 
-@pytest.mark.parametrize("gemm", ["f32", "split"])
+@pytest.mark.parametrize("gemm", ["f32", "split", "split16"])
 def test_tensor_fp32_gemm_paths(gemm):
-    """The root iterations on either product path (the tensor statistics and
-    mode products take the fp32 MFMA on both)."""
+    """Every MFMA product of a tensor handle (statistics of dimensions whose
+    unfolding pads to a multiple of 32, roots, mode products) on each product
+    setting; tensor handles run the bf16 split for either split setting."""
     w = dataclasses.replace(CASES["conv4_64x32"], fp32_gemm=gemm)
     log(f"tensor gemm path {gemm}")
     s, u, wp, sh, _ = run_tensor_parity(w, 3)
