@@ -228,10 +228,8 @@ def run_tensor(args, w, torch, S, synth):
     sh.set_timing(False)
     n_div = sh.n_diverged()
     # statistics (of dimensions whose unfolding pads to a multiple of 32),
-    # MFMA mode products and roots all take the configured path (tensor
-    # handles run the bf16 split under either split setting)
-    tp = "f32" if w.fp32_gemm == "f32" else "split"
-    paths = {"stats": tp, "apply": tp, "newton_gemm": tp}
+    # MFMA mode products and roots all take the configured path
+    paths = {"stats": w.fp32_gemm, "apply": w.fp32_gemm, "newton_gemm": w.fp32_gemm}
     kernels = class_table(tm, paths)
     # dominant class by kernel time; its roofline against its matrix-core
     # path (statistics, root products, apply products) or HBM (the others)

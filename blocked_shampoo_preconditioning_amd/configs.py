@@ -118,7 +118,7 @@ class TensorWorkload:
     momentum: float = 0.0
     root_method: str = "newton"
     cheb_degree: int = 128
-    fp32_gemm: str = "split"
+    fp32_gemm: str = "split16"
     init_std: float = 0.02
     seed: int = 0
     notes: str = field(default="", compare=False)

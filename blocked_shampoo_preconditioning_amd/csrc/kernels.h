@@ -97,6 +97,48 @@ struct MaxOut {
   uint64_t ver;
 };
 
+// Raises the versioned maximum word *slot over this wave's values (m: this
+// lane's largest |value|, non-negative); one 64-bit atomic per wave. Every
+// lane of the wave must call it. fmaxf drops NaN, which the products
+// propagate anyway.
+__device__ __forceinline__ void raise_max(uint64_t* slot, float m, uint64_t ver) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0)
+    atomicMax(reinterpret_cast<unsigned long long*>(slot),
+              (unsigned long long)max_word(ver, __float_as_uint(m) >> 23));
+}
+
+// As raise_max for up to two words (a or b may be NULL), one atomic per word
+// and workgroup of NT threads: for kernels whose many workgroups raise the
+// same word (many atomics on one address serialise). Every thread of the
+// workgroup must call it.
+template <int NT>
+__device__ __forceinline__ void raise_max2_wg(uint64_t* a, float ma, uint64_t* b, float mb,
+                                              uint64_t ver) {
+  __shared__ float red[2][NT / 64];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ma = fmaxf(ma, __shfl_xor(ma, o));
+    mb = fmaxf(mb, __shfl_xor(mb, o));
+  }
+  __syncthreads();  // the workgroup's LDS may still be read by earlier code
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = ma;
+    red[1][threadIdx.x >> 6] = mb;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    uint64_t* slot = threadIdx.x == 0 ? a : b;
+    if (slot != nullptr) {
+      float m = red[threadIdx.x][0];
+      for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[threadIdx.x][w]);
+      atomicMax(reinterpret_cast<unsigned long long*>(slot),
+                (unsigned long long)max_word(ver, __float_as_uint(m) >> 23));
+    }
+  }
+}
+
 // How the fp32 products run. kGemmF32: C = P^T Q on the fp32 MFMA, P [K][M]
 // and Q [K][N]. kGemmSplit: C = A B^T on the bf16 MFMA, each fp32 operand
 // split into three bf16 terms (six products, fp32 accuracy); P holds A [M][K]
@@ -302,10 +344,11 @@ inline uint64_t division_magic(uint32_t d) {
   return d <= 1 ? 0 : ~(uint64_t)0 / d + 1;
 }
 
-// Gp[blk][e] (+ Mom = momentum Mom + Gp) from the tensors.
+// Gp[blk][e] (+ Mom = momentum Mom + Gp) from the tensors; mo: maxima of
+// Gp (a) and Mom (b) per block.
 hipError_t launch_tensor_pack(const TBlockMeta* blocks, const TensorMeta* tensors, TensorGeom g,
                               int32_t B, int32_t grad_bf16, float* Gp, float* Mom, float momentum,
-                              hipStream_t s);
+                              hipStream_t s, MaxOut mo = MaxOut{});
 // mode 0: dst[...] = Src (unpack into the param pointers of `tensors`);
 // mode 1: param -= lr * Src (update; bf16 parameters rounded to nearest even).
 hipError_t launch_tensor_scatter(const TBlockMeta* blocks, const TensorMeta* tensors, TensorGeom g,
@@ -324,9 +367,10 @@ hipError_t launch_small_gram(const float* In, int64_t in_stride, int32_t A, int3
 // Out[blk][r][j] = sum_l X[blk][j][l] In[blk][l][r]: the product along the
 // leading dimension (extent n), which moves that dimension last. FMA kernel
 // for small n or a row count R that the MFMA tiles do not divide.
+// mo.a: maxima of Out per block.
 hipError_t launch_mode_product(const float* In, int64_t in_stride, const float* X, int64_t x_stride,
                                float* Out, int64_t out_stride, int32_t n, int32_t R, int32_t B,
-                               hipStream_t s);
+                               hipStream_t s, MaxOut mo = MaxOut{});
 // The last product (leading dimension k-1, extent <= 8) with the update
 // W -= lr * U written straight into the parameters (no packed U).
 hipError_t launch_mode_product_update(const float* In, int64_t in_stride, const float* X,

@@ -354,17 +354,6 @@ __device__ __forceinline__ int f16_exp(uint64_t w) {
   return e == 0xff ? 0 : 141 - (e > 0 ? e : 1);
 }
 
-// Raises the versioned maximum word *slot over this wave's values (m: this
-// lane's largest |value|, non-negative); one 64-bit atomic per wave. Every
-// lane of the wave must call it. fmaxf drops NaN, which the products
-// propagate anyway.
-__device__ __forceinline__ void raise_max(uint64_t* slot, float m, uint64_t ver) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0)
-    atomicMax(reinterpret_cast<unsigned long long*>(slot),
-              (unsigned long long)max_word(ver, __float_as_uint(m) >> 23));
-}
 
 // Row of 4-value chunk c of a split operand tile (its chunk within the row is
 // c % 4). The 16 lanes of one 128-byte LDS write group take rows {0, 2, 4, 6}
@@ -1146,28 +1135,11 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
     tile[row][c + 2] = v.z;
     tile[row][c + 3] = v.w;
   }
-  if (mo.a != nullptr || mo.b != nullptr) {
-    // one atomic per workgroup and word (a block's 64 x 64 tiles are many
-    // workgroups raising the same word)
-    __shared__ float red[2][4];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      mg = fmaxf(mg, __shfl_xor(mg, o));
-      mmom = fmaxf(mmom, __shfl_xor(mmom, o));
-    }
-    if ((tid & 63) == 0) {
-      red[0][tid >> 6] = mg;
-      red[1][tid >> 6] = mmom;
-    }
-    __syncthreads();
-    if (tid < 2) {
-      uint64_t* slot = tid == 0 ? mo.a : mo.b;
-      const float m = fmaxf(fmaxf(red[tid][0], red[tid][1]), fmaxf(red[tid][2], red[tid][3]));
-      if (slot != nullptr)
-        atomicMax(reinterpret_cast<unsigned long long*>(slot + b),
-                  (unsigned long long)max_word(mo.ver, __float_as_uint(m) >> 23));
-    }
-  }
+  // one atomic per workgroup and word (a block's 64 x 64 tiles are many
+  // workgroups raising the same word)
+  if (mo.a != nullptr || mo.b != nullptr)
+    raise_max2_wg<256>(mo.a != nullptr ? mo.a + b : nullptr, mg,
+                       mo.b != nullptr ? mo.b + b : nullptr, mmom, mo.ver);
   // no transpose wanted (the split products read the packed block by rows
   // and by columns): done (uniform over the workgroup)
   if (GpT == nullptr && GpTH == nullptr) return;
@@ -1591,8 +1563,9 @@ __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restric
       mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
     }
   }
-  if (mo.a != nullptr) raise_max(mo.a + f, mm, mo.ver);
-  if (mo.b != nullptr) raise_max(mo.b + f, mx, mo.ver);
+  if (mo.a != nullptr || mo.b != nullptr)
+    raise_max2_wg<256>(mo.a != nullptr ? mo.a + f : nullptr, mm,
+                       mo.b != nullptr ? mo.b + f : nullptr, mx, mo.ver);
 }
 
 // After iteration `iter` (which produced M_{iter+1} and X_{iter+1}): residual

@@ -675,7 +675,10 @@ int shampoo_set_step(shampoo_t h, int64_t t) {
 
 int shampoo_restore(shampoo_t h, int64_t t, void* hip_stream) {
   if (!h || t < 0) return fail(SHAMPOO_ERR_INVALID_ARG, "NULL handle or negative step");
-  if (!h->tensor && h->plan.off_mx >= 0) {
+  if (h->tensor) {
+    const int rc = tensor_rebase_words(h, static_cast<hipStream_t>(hip_stream));
+    if (rc) return rc;
+  } else if (h->plan.off_mx >= 0) {
     // words written by another handle carry its versions: take them as this
     // handle's current ones, so every later write wins over them
     const uint64_t ver = h->next_ver();

@@ -170,5 +170,7 @@ int tensor_unpack(shampoo_ctx* h, void* const* dst, hipStream_t s);
 int tensor_precondition(shampoo_ctx* h, float* out, hipStream_t s);
 int tensor_layout(const shampoo_ctx* h, shampoo_layout_t* out);
 int tensor_status_count(const shampoo_ctx* h, int64_t* off, int64_t* count);
+// shampoo_restore on a tensor handle: every maximum word takes the current version.
+int tensor_rebase_words(shampoo_ctx* h, hipStream_t s);
 
 }  // namespace shp_rt

@@ -69,8 +69,10 @@ __global__ __launch_bounds__(256) void tensor_pack_kernel(const TBlockMeta* __re
                                                           const TensorMeta* __restrict__ tensors,
                                                           TensorGeom g, int bf16,
                                                           float* __restrict__ Gp,
-                                                          float* __restrict__ Mom, float momentum) {
+                                                          float* __restrict__ Mom, float momentum,
+                                                          MaxOut mo) {
   const int b = blockIdx.y;
+  float mg = 0.f, mm = 0.f;  // largest |value| written to Gp and Mom
   const TBlockMeta bm = blocks[b];
   BlockGeo<K> geo;
   geo.load(g, bm, tensors[bm.tensor]);
@@ -83,8 +85,16 @@ __global__ __launch_bounds__(256) void tensor_pack_kernel(const TBlockMeta* __re
                : reinterpret_cast<const float*>(grad)[off];
     const size_t o = (size_t)b * g.E + e;
     Gp[o] = v;
-    if (Mom != nullptr) Mom[o] = momentum * Mom[o] + v;
+    mg = fmaxf(mg, fabsf(v));
+    if (Mom != nullptr) {
+      const float m = momentum * Mom[o] + v;
+      Mom[o] = m;
+      mm = fmaxf(mm, fabsf(m));
+    }
   }
+  if (mo.a != nullptr || mo.b != nullptr)
+    raise_max2_wg<256>(mo.a != nullptr ? mo.a + b : nullptr, mg,
+                       mo.b != nullptr ? mo.b + b : nullptr, mm, mo.ver);
 }
 
 template <int K>
@@ -221,7 +231,8 @@ __global__ __launch_bounds__(256) void mode_product_kernel(const float* __restri
                                                            int64_t in_stride,
                                                            const float* __restrict__ X,
                                                            int64_t x_stride, float* __restrict__ Out,
-                                                           int64_t out_stride, int n, int R) {
+                                                           int64_t out_stride, int n, int R,
+                                                           MaxOut mo) {
   __shared__ float stage[256 * J];
   const int b = blockIdx.z;
   const float* in = In + (size_t)b * in_stride;
@@ -240,6 +251,13 @@ __global__ __launch_bounds__(256) void mode_product_kernel(const float* __restri
       for (int jj = 0; jj < J; ++jj)
         if (j0 + jj < n) acc[jj] += x[(j0 + jj) * n + l] * v;
     }
+  }
+  if (mo.a != nullptr) {  // the output's maximum (uniform branch)
+    float mx = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < J; ++jj)
+      if (r < R && j0 + jj < n) mx = fmaxf(mx, fabsf(acc[jj]));
+    raise_max2_wg<256>(mo.a + b, mx, nullptr, 0.f, mo.ver);
   }
   if (gridDim.y == 1 && n == J) {
 #pragma unroll
@@ -385,22 +403,24 @@ __global__ __launch_bounds__(kJacobiThreads) void small_root_kernel(
 
 hipError_t launch_tensor_pack(const TBlockMeta* blocks, const TensorMeta* tensors, TensorGeom g,
                               int32_t B, int32_t grad_bf16, float* Gp, float* Mom, float momentum,
-                              hipStream_t s) {
+                              hipStream_t s, MaxOut mo) {
   if (B == 0 || g.E == 0) return hipSuccess;
-  const int chunks = std::max(1, std::min(1024, (g.E + 1023) / 1024));
+  // with maxima, 16 elements a thread (fewer workgroups raising each word)
+  const int per = mo.a != nullptr || mo.b != nullptr ? 4096 : 1024;
+  const int chunks = std::max(1, std::min(1024, (g.E + per - 1) / per));
   const dim3 grid(chunks, B);
   switch (g.order) {
     case 2:
       hipLaunchKernelGGL(tensor_pack_kernel<2>, grid, dim3(256), 0, s, blocks, tensors, g,
-                         grad_bf16, Gp, Mom, momentum);
+                         grad_bf16, Gp, Mom, momentum, mo);
       break;
     case 3:
       hipLaunchKernelGGL(tensor_pack_kernel<3>, grid, dim3(256), 0, s, blocks, tensors, g,
-                         grad_bf16, Gp, Mom, momentum);
+                         grad_bf16, Gp, Mom, momentum, mo);
       break;
     case 4:
       hipLaunchKernelGGL(tensor_pack_kernel<4>, grid, dim3(256), 0, s, blocks, tensors, g,
-                         grad_bf16, Gp, Mom, momentum);
+                         grad_bf16, Gp, Mom, momentum, mo);
       break;
     default:
       return hipErrorInvalidValue;
@@ -471,20 +491,20 @@ hipError_t launch_small_gram(const float* In, int64_t in_stride, int32_t A, int3
 
 hipError_t launch_mode_product(const float* In, int64_t in_stride, const float* X, int64_t x_stride,
                                float* Out, int64_t out_stride, int32_t n, int32_t R, int32_t B,
-                               hipStream_t s) {
+                               hipStream_t s, MaxOut mo) {
   if (B == 0 || R == 0) return hipSuccess;
   const int gx = (R + 255) / 256;
   switch (n <= kMaxSmallSide ? n : 0) {
 #define SHP_MP(N)                                                                               \
   case N:                                                                                       \
     hipLaunchKernelGGL(mode_product_kernel<N>, dim3(gx, 1, B), dim3(256), 0, s, In, in_stride, X, \
-                       x_stride, Out, out_stride, n, R);                                        \
+                       x_stride, Out, out_stride, n, R, mo);                                    \
     break;
     SHP_MP(1) SHP_MP(2) SHP_MP(3) SHP_MP(4) SHP_MP(5) SHP_MP(6) SHP_MP(7) SHP_MP(8)
 #undef SHP_MP
     default:
       hipLaunchKernelGGL(mode_product_kernel<8>, dim3(gx, (n + 7) / 8, B), dim3(256), 0, s, In,
-                         in_stride, X, x_stride, Out, out_stride, n, R);
+                         in_stride, X, x_stride, Out, out_stride, n, R, mo);
   }
   return hipGetLastError();
 }

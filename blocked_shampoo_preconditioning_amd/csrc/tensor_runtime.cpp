@@ -59,6 +59,12 @@ struct TensorState {
       off_cfac, off_lo, off_coef, off_active, off_flops, off_cheb, off_resid, off_partial, off_gp,
       off_mom, off_ap0,
       off_ap1, off_stats, off_xroot, off_xalt, off_s[4], total;
+  // fp16 split products: maximum words (uint64, see shp::max_word) per large
+  // factor of xroot, xalt, s0..s3 (6 x nbig B, xroot's first: the roots') and
+  // per block of Gp, the momentum buffer and the two apply buffers (4 x B);
+  // -1 on the other product paths
+  int64_t off_mx = -1;
+  int64_t n_mx = 0;
 };
 
 void destroy_tensor_state(TensorState* t) {
@@ -236,6 +242,10 @@ int make_tensor_plan(const shampoo_config_t* cfg, int32_t order, const int32_t* 
     ts.off_s[i] = scratch && (i < 3 || ts.p > 4 || cfg->root_method == shp::kChebyshev)
                       ? c.take(ts.fbig * 4)
                       : -1;
+  if (cfg->fp32_gemm == SHAMPOO_GEMM_SPLIT_F16) {
+    ts.n_mx = 6 * (int64_t)ts.nbig * ts.B + 4 * ts.B;
+    ts.off_mx = c.take(ts.n_mx * 8);
+  }
   ts.total = c.o;
   return SHAMPOO_OK;
 }
@@ -255,6 +265,25 @@ shp::TensorGeom geom(const TensorState& ts) {
 }
 
 float* fptr(const shampoo_ctx* h, int64_t off) { return off < 0 ? nullptr : h->at<float>(off); }
+
+// Maximum words (fp16 split): i = 0..5 per large factor of xroot, xalt,
+// s0..s3; i = 6..9 per block of Gp, the momentum buffer, ap0, ap1. NULL on the
+// other product paths.
+uint64_t* tmx(const shampoo_ctx* h, int i) {
+  const TensorState& ts = *h->tensor;
+  if (ts.off_mx < 0) return nullptr;
+  const int64_t nfb = (int64_t)ts.nbig * ts.B;
+  return h->at<uint64_t>(ts.off_mx) + (i < 6 ? i * nfb : 6 * nfb + (i - 6) * ts.B);
+}
+
+// The words of one of the per-block buffers (Gp, momentum, apply buffers).
+uint64_t* tmx_of(const shampoo_ctx* h, const float* buf) {
+  const TensorState& ts = *h->tensor;
+  const int64_t offs[4] = {ts.off_gp, ts.off_mom, ts.off_ap0, ts.off_ap1};
+  for (int i = 0; i < 4; ++i)
+    if (offs[i] >= 0 && buf == h->at<float>(offs[i])) return tmx(h, 6 + i);
+  return nullptr;
+}
 
 int upload_tensor_meta(shampoo_ctx* h, const void* const* grads, void* const* params,
                        hipStream_t s) {
@@ -287,17 +316,20 @@ int do_tensor_pack(shampoo_ctx* h, hipStream_t s) {
   const TensorState& ts = T(h);
   const double esz = h->cfg.grad_dtype == SHAMPOO_BF16 ? 2.0 : 4.0;
   const double bytes = ts.real_elems * esz + (ts.momentum ? 3.0 : 1.0) * 4.0 * (double)ts.B * ts.E;
+  shp::MaxOut mo{};
+  if (ts.off_mx >= 0) {
+    mo.a = tmx(h, 6);
+    mo.b = ts.momentum ? tmx(h, 7) : nullptr;
+    mo.ver = h->next_ver();
+  }
   return timed(h, kPack, 0.0, bytes, s, [&] {
     return shp::launch_tensor_pack(h->at<shp::TBlockMeta>(ts.off_blocks),
                                    h->at<shp::TensorMeta>(ts.off_meta), geom(ts), (int32_t)ts.B,
                                    h->cfg.grad_dtype == SHAMPOO_BF16, fptr(h, ts.off_gp),
-                                   fptr(h, ts.off_mom), (float)h->cfg.momentum, s);
+                                   fptr(h, ts.off_mom), (float)h->cfg.momentum, s, mo);
   });
 }
 
-// Tensor handles split their fp32 products into bf16 terms under either split
-// setting: the fp16 split needs every operand's recorded maximum, which the
-// mode products' intermediates do not keep.
 bool split_gemm(const shampoo_ctx* h) { return h->cfg.fp32_gemm != SHAMPOO_GEMM_F32; }
 
 int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
@@ -343,11 +375,13 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
       q.alpha = h->stat_scale;
       q.beta = (float)h->cfg.beta2;
       g.n_problems = 1;
-      // split path: the k-major operand [Kp][n] read by columns; its K-tiles
+      // split paths: the k-major operand [Kp][n] read by columns; its K-tiles
       // run in pairs, so an unfolding padded to an odd multiple of 16 stays on
-      // the fp32 MFMA
-      const int mode = split_gemm(h) && ts.Kp[i] % 32 == 0 ? shp::kGemmSplit : shp::kGemmF32;
-      q.p_cols = q.q_cols = mode == shp::kGemmSplit ? 1 : 0;
+      // the fp32 MFMA. The transposed copy holds Gp's values (and zeros), so
+      // Gp's maxima serve it.
+      const int mode = split_gemm(h) && ts.Kp[i] % 32 == 0 ? h->cfg.fp32_gemm : shp::kGemmF32;
+      q.p_cols = q.q_cols = mode != shp::kGemmF32 ? 1 : 0;
+      q.mP = q.mQ = tmx(h, 6);
       rc = timed(h, kStats, fl, 0.0, s,
                  [&] { return shp::launch_gemm_sym(g, ts.stat_tile[i], false, mode, s); });
     } else {
@@ -413,6 +447,8 @@ int do_tensor_apply(shampoo_ctx* h, hipStream_t s, float* out) {
     const int n = ts.b[i];
     const int64_t R = ts.E / n;
     float* dst = (i == ts.k - 1 && out) ? out : ap[i & 1];
+    // the product's maxima are needed only when an MFMA mode product reads it next
+    const bool words = i + 1 < ts.k && ts.is_big[i + 1] && ts.apply_tile[i + 1] > 0;
     const float* X = roots + ts.foff[i];
     const double fl = ts.apply_flops[i];
     const double esz = h->cfg.param_dtype == SHAMPOO_BF16 ? 2.0 : 4.0;
@@ -444,15 +480,24 @@ int do_tensor_apply(shampoo_ctx* h, hipStream_t s, float* out) {
       q.K = n;
       q.batch = (int32_t)ts.B;
       q.alpha = 1.f;
+      // fp16 split: maxima of the current block, of dimension i's roots and
+      // of the product (unless it is the caller's output)
+      q.mP = tmx_of(h, cur);
+      q.mQ = tmx(h, 0) != nullptr ? tmx(h, 0) + (int64_t)ts.group[i] * ts.B : nullptr;
+      q.mC = words ? tmx_of(h, dst) : nullptr;
+      if (q.mC != nullptr) q.ver = h->next_ver();
       g.n_problems = 1;
-      const int mode = split_gemm(h) ? shp::kGemmSplit : shp::kGemmF32;
-      q.p_cols = mode == shp::kGemmSplit ? 1 : 0;
+      const int mode = split_gemm(h) ? h->cfg.fp32_gemm : shp::kGemmF32;
+      q.p_cols = mode != shp::kGemmF32 ? 1 : 0;
       rc = timed(h, kApply, fl, 0.0, s,
                  [&] { return shp::launch_gemm_full(g, ts.apply_tile[i], mode, s); });
     } else {
+      shp::MaxOut mo{};
+      mo.a = words ? tmx_of(h, dst) : nullptr;
+      if (mo.a != nullptr) mo.ver = h->next_ver();
       rc = timed(h, kApplyAux, fl, 8.0 * ts.B * ts.E, s, [&] {
         return shp::launch_mode_product(cur, ts.E, X, (int64_t)n * n, dst, ts.E, n, (int32_t)R,
-                                        (int32_t)ts.B, s);
+                                        (int32_t)ts.B, s, mo);
       });
     }
     if (rc) return rc;
@@ -487,7 +532,8 @@ int tensor_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
     for (int g = 0; g < ts.nbig; ++g) j.tile[g] = ts.stat_tile[ts.big[g]];
     j.real_cube = ts.real_cube;
     j.t_stats = t_stats;
-    j.gemm_mode = split_gemm(h) ? shp::kGemmSplit : shp::kGemmF32;
+    j.gemm_mode = h->cfg.fp32_gemm;
+    for (int i = 0; i < 6; ++i) j.mx[i] = tmx(h, i);
     const int rc = run_roots(h, j, s);
     if (rc) return rc;
   }
@@ -560,8 +606,15 @@ int tensor_layout(const shampoo_ctx* h, shampoo_layout_t* out) {
   out->newton_residual = ts.off_rprev;
   out->momentum = ts.off_mom;
   out->workspace_bytes = ts.total;
-  out->root_maxima = -1;
+  out->root_maxima = ts.off_mx;
   return SHAMPOO_OK;
+}
+
+int tensor_rebase_words(shampoo_ctx* h, hipStream_t s) {
+  const TensorState& ts = T(h);
+  if (ts.off_mx < 0) return SHAMPOO_OK;
+  const hipError_t e = shp::launch_rebase_words(h->at<uint64_t>(ts.off_mx), ts.n_mx, h->next_ver(), s);
+  return e == hipSuccess ? SHAMPOO_OK : hip_fail(e, "rebase of the maximum words");
 }
 
 int tensor_status_count(const shampoo_ctx* h, int64_t* off, int64_t* count) {
@@ -647,6 +700,8 @@ int shampoo_tensor_init(const shampoo_config_t* cfg, int32_t order, const int32_
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(ts->off_rprev), 0, nf * 4, s);
     if (e == hipSuccess && ts->momentum)
       e = hipMemsetAsync(h->at<void>(ts->off_mom), 0, ts->B * (int64_t)ts->E * 4, s);
+    if (e == hipSuccess && ts->off_mx >= 0)  // no maximum word written yet
+      e = hipMemsetAsync(h->at<void>(ts->off_mx), 0, ts->n_mx * 8, s);
     for (int i = 0; i < order && e == hipSuccess; ++i) {
       const int n = ts->b[i];
       e = shp::launch_init_state(h->at<float>(ts->off_stats) + ts->foff[i], ts->B * n * n, n, 0, 1,

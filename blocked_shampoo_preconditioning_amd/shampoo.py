@@ -446,7 +446,7 @@ class TensorShampoo(Shampoo):
     def __init__(self, shapes, block_dims, beta2=0.999, eps=1e-6, lr=1e-3, root_every=10,
                  stat_scale=None, newton_max_iters=25, newton_tol=1e-6, newton_scale_mode=3,
                  dtype="f32", device="cuda", strides=None, momentum=0.0, root_method="newton",
-                 cheb_degree=128, fp32_gemm="split"):
+                 cheb_degree=128, fp32_gemm="split16"):
         import torch
         self.torch = torch
         self.shapes = [tuple(int(v) for v in s) for s in shapes]
@@ -518,3 +518,27 @@ class TensorShampoo(Shampoo):
 
     def newton_residual(self):
         return self._per_factor(self.layout.newton_residual, self.torch.float32)
+
+    def root_maxima(self):
+        """Versioned exponent words of the large dimensions' roots (fp16 split
+        products only), nb * B of them, the dimensions in order."""
+        if self.layout.root_maxima < 0:
+            return None
+        nb = sum(1 for n in self.block_dims if n % 32 == 0 and 32 <= n <= 4096)
+        return self._view(self.layout.root_maxima, nb * self.n_blocks, self.torch.int64)
+
+    def state_regions(self):
+        """Flat views of the checkpointed state: statistics, roots, momentum,
+        the four Newton records and the root maxima (when present)."""
+        t = self.torch
+        kB = self.order * self.n_blocks
+        out = self.stats() + self.roots()
+        if self.momentum_buffer() is not None:
+            out.append(self.momentum_buffer())
+        out += [self._view(self.layout.newton_status, kB, t.int32),
+                self._view(self.layout.newton_iters, kB, t.int32),
+                self._view(self.layout.newton_scale, kB, t.float32),
+                self._view(self.layout.newton_residual, kB, t.float32)]
+        if self.root_maxima() is not None:
+            out.append(self.root_maxima())
+        return out

@@ -89,9 +89,7 @@ typedef enum {
                                   block or factor (64-bit words with a
                                   version that grows with every launch that
                                   writes them); the roots' words are part of
-                                  the state (layout.root_maxima). Tensor
-                                  handles take the bf16 split instead
-                                  (default)                                  */
+                                  the state (layout.root_maxima) (default)   */
 } shampoo_fp32_gemm_t;
 
 /* Flags of shampoo_step. */
@@ -177,11 +175,9 @@ typedef struct {
   int32_t fp32_gemm;              /* shampoo_fp32_gemm_t; default
                                      SHAMPOO_GEMM_SPLIT_F16. Statistics of bf16
                                      gradients always take the bf16 MFMA
-                                     directly; tensor handles run the bf16
-                                     split under either split setting, and a
-                                     tensor dimension whose unfolding pads to
-                                     an odd multiple of 16 keeps its
-                                     statistics on the fp32 MFMA              */
+                                     directly; a tensor dimension whose
+                                     unfolding pads to an odd multiple of 16
+                                     keeps its statistics on the fp32 MFMA    */
 } shampoo_config_t;
 
 /* Byte offsets of the state inside the caller's workspace (for inspection
@@ -205,10 +201,13 @@ typedef struct {
   int64_t momentum;       /* fp32 [B][br][bc] momentum, or -1 when it is off         */
   int64_t workspace_bytes;
   int64_t root_maxima;    /* fp32_gemm = SHAMPOO_GEMM_SPLIT_F16 only, else -1:
-                             uint64 [2B], per root (left factors first) the
-                             versioned binary exponent of its largest |value|,
-                             which the preconditioning products scale by. Part
-                             of the state: a checkpoint keeps it with the roots,
+                             uint64 per root, the versioned binary exponent of
+                             its largest |value|, which the preconditioning
+                             products scale by: [2B] for matrix handles (left
+                             factors first), [nb B] for tensor handles (the
+                             nb dimensions blocked at a multiple of 32, in order;
+                             smaller dimensions take no MFMA product). Part of
+                             the state: a checkpoint keeps it with the roots,
                              and a restore writes both (shampoo_restore)       */
 } shampoo_layout_t;
 

@@ -242,10 +242,50 @@ def test_tensor_empty_and_zero_tensors():
 def test_tensor_fp32_gemm_paths(gemm):
     """Every MFMA product of a tensor handle (statistics of dimensions whose
     unfolding pads to a multiple of 32, roots, mode products) on each product
-    setting; tensor handles run the bf16 split for either split setting."""
+    path."""
     w = dataclasses.replace(CASES["conv4_64x32"], fp32_gemm=gemm)
     log(f"tensor gemm path {gemm}")
     s, u, wp, sh, _ = run_tensor_parity(w, 3)
     assert s <= STATS_TOL and u <= UPDATE_TOL and wp <= UPDATE_TOL, (s, u, wp)
     assert sh.n_diverged() == 0
     sh.close()
+
+
+@pytest.mark.parametrize("gemm", ["split", "split16"])
+def test_tensor_restore_matches_uninterrupted(gemm):
+    """Checkpoint and restore of a tensor handle through its documented state
+    (statistics and roots of every dimension, momentum, the Newton records,
+    the large dimensions' root maxima on the fp16 split) and shampoo_restore
+    into another handle with a history of its own, between two refreshes: the
+    following steps, a refresh among them, give bit-identical parameters to an
+    uninterrupted run."""
+    w = dataclasses.replace(CASES["conv4_64x32"], fp32_gemm=gemm, momentum=0.9, root_every=3)
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    grads = [[torch.randn(s, generator=gen, device="cuda") * 0.1 for s in w.shapes] for _ in range(7)]
+    ref = make(w, root_method="newton")
+    p_ref = [torch.zeros(s, device="cuda") for s in w.shapes]
+    for t in range(7):
+        ref.step(p_ref, grads[t])
+    a = make(w, root_method="newton")
+    p = [torch.zeros(s, device="cuda") for s in w.shapes]
+    for t in range(4):
+        a.step(p, grads[t])
+    torch.cuda.synchronize()
+    saved = [x.clone() for x in a.state_regions()]
+    t_saved = a.t
+    a.close()
+    b = make(w, root_method="newton")
+    q = [torch.zeros(s, device="cuda") for s in w.shapes]
+    for t in range(2):
+        b.step(q, [g * 1e3 for g in grads[6 - t]])
+    for dst, src in zip(b.state_regions(), saved):
+        dst.copy_(src)
+    S.shampoo_restore(b.handle, t_saved, torch.cuda.current_stream().cuda_stream)
+    for t in range(4, 7):
+        b.step(p, grads[t])
+    torch.cuda.synchronize()
+    for x, y in zip(p, p_ref):
+        assert torch.equal(x, y), float((x - y).abs().max())
+    assert b.n_diverged() == 0
+    b.close()
+    ref.close()
