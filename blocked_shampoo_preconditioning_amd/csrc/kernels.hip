@@ -323,7 +323,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 //   x y = hh + hl + lh + O(2^-21 |x y|)
 // each exact in fp32, accumulated in fp32 by the MFMA: fp32-level accuracy
 // with half the products and two thirds of the planes of the bf16 split.
-// Non-finite inputs give NaN or infinity as before.
+// A non-finite input gives a non-finite high term and a NaN low term, so the
+// result is not finite either.
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
