@@ -64,6 +64,17 @@ struct BlockGeo {
   }
 };
 
+// floor(i / d) for 0 <= i < 2^22 and d >= 1, from inv = 1 / d: the float
+// quotient is within one of the integer one, which the correction fixes.
+__device__ __forceinline__ int div_small(int i, int d, float inv) {
+  int q = (int)((float)i * inv);
+  if (q * d > i)
+    --q;
+  else if ((q + 1) * d <= i)
+    ++q;
+  return q;
+}
+
 template <int K>
 __global__ __launch_bounds__(256) void tensor_pack_kernel(const TBlockMeta* __restrict__ blocks,
                                                           const TensorMeta* __restrict__ tensors,
@@ -139,13 +150,16 @@ __global__ __launch_bounds__(256) void transpose_kernel(const float* __restrict_
   const int pitch = tw | 1;  // odd pitch: column reads spread over the banks
   const float* in = In + (size_t)b * in_stride;
   float* out = Out + (size_t)b * out_stride;
+  // tile-local indices by a float reciprocal and one correction (an integer
+  // division per element would bound this memory-bound kernel)
+  const float itw = 1.f / (float)tw, ith = 1.f / (float)th;
   for (int i = threadIdx.x; i < th * tw; i += 256) {
-    const int r = i / tw, c = i - r * tw;
+    const int r = div_small(i, tw, itw), c = i - r * tw;
     tile[r * pitch + c] = in[(size_t)(r0 + r) * C + c0 + c];
   }
   __syncthreads();
   for (int i = threadIdx.x; i < th * tw; i += 256) {
-    const int c = i / th, r = i - c * th;
+    const int c = div_small(i, th, ith), r = i - c * th;
     out[(size_t)(c0 + c) * R + r0 + r] = tile[r * pitch + c];
   }
 }
