@@ -285,6 +285,39 @@ def newton_traffic(workload, gemm):
     return round(rec["kernels"]["newton_sym_kernel"]["traffic_bytes_per_launch"])
 
 
+def vendor_gemm(torch, w, reps=10):
+    """Rate of torch.bmm (the vendor GEMM library) on [B, n, n] x [B, n, n], B the workload's
+    block count and n its block side: a full product with none of the fused work (no
+    symmetry, no split, no epilogue), timed like the step. Context for the hand-written
+    products, not part of the step."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = w.block_rows
+    B = sum(((r + n - 1) // n) * ((c + w.block_cols - 1) // w.block_cols) for r, c in w.shapes)
+    out = {"vendor_gemm": "torch.bmm", "shape": [B, n, n, n]}
+    for name, dt in (("fp16", torch.float16), ("bf16", torch.bfloat16), ("fp32", torch.float32)):
+        g = torch.Generator(device=dev).manual_seed(0)
+        a = torch.randn(B, n, n, device=dev, dtype=dt, generator=g)
+        b = torch.randn(B, n, n, device=dev, dtype=dt, generator=g)
+        c = torch.empty(B, n, n, device=dev, dtype=dt)
+        for _ in range(3):
+            torch.bmm(a, b, out=c)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.bmm(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 3), "tflops": round(2.0 * B * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+        log(f"vendor {name}: {out[name]}")
+        del a, b, c
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +339,10 @@ def main():
                     help="fp32 products: scaled and split into two fp16 terms on the fp16 MFMA "
                          "(default), split into three bf16 terms on the bf16 MFMA, or the "
                          "fp32 MFMA")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="instead of the step, time the vendor library's batched GEMM "
+                         "(torch.bmm on hipBLASLt) at the workload's block shape in fp16, bf16 "
+                         "and fp32: the practical ceiling of a plain product on this chip")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one plain 1 GiB device copy (a known-size kernel that "
                          "calibrates the HBM traffic counters)")
@@ -326,6 +363,8 @@ def main():
         from blocked_shampoo_preconditioning_amd import build
         build.build()
     S.load_library()
+    if args.vendor_gemm:
+        return vendor_gemm(torch, configs.get(args.workload))
     if args.workload in configs.TENSOR_WORKLOADS:
         return run_tensor(args, configs.get_tensor(args.workload), torch, S, synth)
     w = configs.get(args.workload)
