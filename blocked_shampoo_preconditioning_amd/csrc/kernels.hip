@@ -23,6 +23,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace shp {
 namespace {
 
@@ -982,6 +984,61 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return (uint16_t)(u >> 16);
 }
 
+// The parameter update of one tile on the split paths: the parameters of a
+// batch of fragments are all loaded before any of them is updated and
+// stored. A store to the parameter array holds back every later load from it
+// (the compiler must assume they alias), so each batch costs one memory round
+// trip, where one per fragment had stalled the workgroup eight times on the
+// 256-tiles. BF16: parameters stored as bfloat16 (updated in fp32, rounded
+// to nearest even).
+template <class C, bool BF16>
+__device__ __forceinline__ void update_batched(const floatx16 (&acc)[C::FM][C::FN],
+                                               const BlockMeta& bm, const MatMeta& mm, float lr,
+                                               int m0, int n0) {
+  typedef typename std::conditional<BF16, uint16_t, float>::type P;
+  P* w = reinterpret_cast<P*>(mm.param) + (size_t)bm.r0 * mm.ld + bm.c0;
+  constexpr int NF = C::FM * C::FN;
+  constexpr int G = NF > 2 ? 2 : NF;  // fragments per batch (32 registers)
+#pragma unroll
+  for (int q0 = 0; q0 < NF; q0 += G) {
+    float wv[G][16];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
+      const int col = frag_col<C>(n0, j);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = frag_row<C>(m0, i, r);
+        float v = 0.f;
+        if (col < bm.n && row < bm.m) {
+          const P x = w[(size_t)row * mm.ld + col];
+          if constexpr (BF16)
+            v = bf16_to_f32(x);
+          else
+            v = x;
+        }
+        wv[q][r] = v;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
+      const int col = frag_col<C>(n0, j);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = frag_row<C>(m0, i, r);
+        if (col < bm.n && row < bm.m) {
+          const float v = wv[q][r] - lr * acc[i][j][r];
+          if constexpr (BF16)
+            w[(size_t)row * mm.ld + col] = f32_to_bf16(v);
+          else
+            w[(size_t)row * mm.ld + col] = v;
+        }
+      }
+    }
+  }
+}
+
 // Second apply product with the parameter update in the epilogue:
 // W[r0 + row][c0 + col] -= lr * U[row][col] on the block's real extent.
 template <class C, int PATH>
@@ -1012,9 +1069,15 @@ __global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void apply_update_
   const BlockMeta bm = u.blocks[f];
   const MatMeta mm = u.mats[bm.mat];
   const float lr = u.lr;
-  // Per fragment: the parameters are loaded first, then updated and stored
-  // (loads interleaved with stores to the same array would each wait for the
-  // store before them).
+  if constexpr (path_split(PATH)) {
+    if (u.param_bf16)
+      update_batched<C, true>(acc, bm, mm, u.lr, m0, n0);
+    else
+      update_batched<C, false>(acc, bm, mm, u.lr, m0, n0);
+    return;
+  }
+  // fp32 MFMA path (four waves per SIMD, fewer free registers): per fragment,
+  // four parameters at a time are loaded, then updated and stored.
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -1022,7 +1085,7 @@ __global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void apply_update_
       const int col = frag_col<C>(n0, j);
       if (col >= bm.n) continue;
       const size_t base = (size_t)bm.r0 * mm.ld + bm.c0 + col;
-      constexpr int HOIST = path_split(PATH) ? 16 : 4;  // registers per batch
+      constexpr int HOIST = 4;  // registers per batch
       if (u.param_bf16) {
         uint16_t* w = reinterpret_cast<uint16_t*>(mm.param) + base;
 #pragma unroll
