@@ -824,42 +824,68 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const int N = pb.N;
   float rs = 0.f;
   float mx = 0.f;  // largest |value| stored (fp16 split: the result's maximum)
+  // The affine terms are loaded before their stores: the stores may alias
+  // them as far as the compiler knows (the statistics update in place), which
+  // would otherwise hold every load behind the store before it. No store
+  // below targets an element another lane reads here. The split paths with
+  // row operands have the registers for two whole fragments per batch (one
+  // memory round trip per two fragments); the others load HOIST registers of
+  // one fragment at a time.
+  constexpr bool BATCH = PATH == kPathSplit || PATH == kPathSplitH;
+  constexpr int NF = C::FM * C::FN;
+  constexpr int GF = BATCH && NF >= 2 ? 2 : 1;  // fragments per batch
+  constexpr int HOIST = BATCH ? 16 : 4;
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+  for (int q0 = 0; q0 < NF; q0 += GF) {
+    float dv[GF][HOIST], d2v[GF][HOIST], ev[GF][TERMS ? HOIST : 1];
+    if constexpr (BATCH) {
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
+      for (int q = 0; q < GF; ++q) {
+        const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
+        if (!((sw.mask >> (i * C::FN + j)) & 1)) continue;  // wave-uniform
+        const int col = frag_col_w<C>(n0, sw.wn, j);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const size_t o = (size_t)frag_row_w<C>(m0, sw.wm, i, r) * N + col;
+          dv[q][r] = Db != nullptr ? Db[o] : 0.f;
+          d2v[q][r] = D2b != nullptr ? D2b[o] : 0.f;
+          if constexpr (TERMS)
+            ev[q][r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) + (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < GF; ++q) {
+      const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
       if (!((sw.mask >> (i * C::FN + j)) & 1)) continue;  // wave-uniform
       const int col = frag_col_w<C>(n0, sw.wn, j);
-      // The affine terms of HOIST registers are loaded before their stores:
-      // the stores may alias them as far as the compiler knows (the
-      // statistics update in place), which would otherwise hold every load
-      // behind the store before it. No store below targets an element another
-      // lane reads here. The split path has the registers for all 16.
-      constexpr int HOIST = PATH == kPathSplit || PATH == kPathSplitH ? 16 : 4;
-      float dv[HOIST], d2v[HOIST], ev[TERMS ? HOIST : 1];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        if ((4 * g4) % HOIST == 0) {
+        if constexpr (!BATCH) {
+          if ((4 * g4) % HOIST == 0) {
 #pragma unroll
-          for (int r = 0; r < HOIST; ++r) {
-            const size_t o = (size_t)frag_row_w<C>(m0, sw.wm, i, 4 * g4 + r) * N + col;
-            dv[r] = Db != nullptr ? Db[o] : 0.f;
-            d2v[r] = D2b != nullptr ? D2b[o] : 0.f;
-            if constexpr (TERMS)
-              ev[r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) + (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
+            for (int r = 0; r < HOIST; ++r) {
+              const size_t o = (size_t)frag_row_w<C>(m0, sw.wm, i, 4 * g4 + r) * N + col;
+              dv[q][r] = Db != nullptr ? Db[o] : 0.f;
+              d2v[q][r] = D2b != nullptr ? D2b[o] : 0.f;
+              if constexpr (TERMS)
+                ev[q][r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) +
+                           (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
+            }
           }
         }
         const int row0 = frag_row_w<C>(m0, sw.wm, i, 4 * g4);
         f32x4 v;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = row0 + q;
-          float x = e_alpha * acc[i][j][4 * g4 + q];
-          x += e_beta * dv[(4 * g4 + q) % HOIST];
-          x += e_beta2 * d2v[(4 * g4 + q) % HOIST];
-          if constexpr (TERMS) x += ev[(4 * g4 + q) % HOIST];
+        for (int qq = 0; qq < 4; ++qq) {
+          const int row = row0 + qq;
+          const int h = (4 * g4 + qq) % HOIST;
+          float x = e_alpha * acc[i][j][4 * g4 + qq];
+          x += e_beta * dv[q][h];
+          x += e_beta2 * d2v[q][h];
+          if constexpr (TERMS) x += ev[q][h];
           if (row == col) x += e_gamma;
-          v[q] = x;
+          v[qq] = x;
           if (!diag || row <= col) {
             Cb[(size_t)row * N + col] = x;
             const float d = x - (row == col ? 1.f : 0.f);
@@ -871,11 +897,12 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
           *reinterpret_cast<f32x4*>(Cb + (size_t)col * N + row0) = v;
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (row0 + q < col) Cb[(size_t)col * N + row0 + q] = v[q];
+          for (int qq = 0; qq < 4; ++qq)
+            if (row0 + qq < col) Cb[(size_t)col * N + row0 + qq] = v[qq];
         }
       }
     }
+  }
   if constexpr (path_f16(PATH))
     if (pb.mC != nullptr) raise_max(pb.mC + f, mx, pb.ver);
   if (pb.resid != nullptr) {
