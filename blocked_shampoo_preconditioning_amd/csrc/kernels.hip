@@ -182,104 +182,120 @@ __device__ __forceinline__ void mainloop(const float* __restrict__ P, const floa
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// acc[fm][fn] = sum over K of X[m0 + ...][k] * X[n0 + ...][k] with X [rows][K]
-// bf16 (k contiguous): v_mfma_f32_32x32x16_bf16, lane l supplying
-// A[m = l % 32][k = 8 (l / 32) + 0..7] and B[k = 8 (l / 32) + 0..7][n = l % 32],
-// each a 16-byte read of one LDS row. Double-buffered like mainloop_w.
+// One thread's share of a bf16 K-tile (BKH wide) of both operands in
+// registers: 16-byte chunks, CPR per row; chunk c = tid + i NT is row c / CPR,
+// k (c % CPR) 8.
+template <class C>
+struct Bf16Stage {
+  static constexpr int CPR = C::BKH / 8;
+  static constexpr int CA = C::BM * CPR, CB = C::BN * CPR;
+  static_assert(CA % C::NT == 0 && CB % C::NT == 0, "uneven operand load");
+  static constexpr int PA = CA / C::NT, PB = CB / C::NT;
+  u32x4 a[PA], b[PB];
+};
+
+template <class C>
+__device__ __forceinline__ void bf16_load(Bf16Stage<C>& st, const uint16_t* __restrict__ X, int K,
+                                          int m0, int n0, int kt) {
+  using S = Bf16Stage<C>;
+  const int tid = threadIdx.x, k0 = kt * C::BKH;
+#pragma unroll
+  for (int i = 0; i < S::PA; ++i) {
+    const int c = tid + i * C::NT;
+    st.a[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(m0 + c / S::CPR) * K + k0 +
+                                              (c % S::CPR) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < S::PB; ++i) {
+    const int c = tid + i * C::NT;
+    st.b[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(n0 + c / S::CPR) * K + k0 +
+                                              (c % S::CPR) * 8);
+  }
+}
+
+// Into LDS buffer buf: [BM][LDKH] of A then [BN][LDKH] of B per buffer.
+template <class C>
+__device__ __forceinline__ void bf16_store(const Bf16Stage<C>& st, uint16_t* sA, uint16_t* sB,
+                                           int buf) {
+  using S = Bf16Stage<C>;
+  constexpr int LD = C::LDKH;
+  const int tid = threadIdx.x;
+  uint16_t* dA = sA + buf * C::BM * LD;
+  uint16_t* dB = sB + buf * C::BN * LD;
+#pragma unroll
+  for (int i = 0; i < S::PA; ++i) {
+    const int c = tid + i * C::NT;
+    *reinterpret_cast<u32x4*>(dA + (c / S::CPR) * LD + (c % S::CPR) * 8) = st.a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < S::PB; ++i) {
+    const int c = tid + i * C::NT;
+    *reinterpret_cast<u32x4*>(dB + (c / S::CPR) * LD + (c % S::CPR) * 8) = st.b[i];
+  }
+}
+
+// The MFMAs of the K-tile in LDS buffer buf (v_mfma_f32_32x32x16_bf16): per
+// 16 k, lane l supplies A[m = l % 32][k = 8 (l / 32) + 0..7] and
+// B[k = 8 (l / 32) + 0..7][n = l % 32], each a 16-byte read of one LDS row.
+template <class C, int MASK>
+__device__ __forceinline__ void bf16_mma(floatx16 (&acc)[C::FM][C::FN], const uint16_t* sA,
+                                         const uint16_t* sB, int buf, int wm, int wn) {
+  constexpr int LD = C::LDKH;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const uint16_t* a0 = sA + buf * C::BM * LD + (wm * 32 * C::FM + l32) * LD + half * 8;
+  const uint16_t* b0 = sB + buf * C::BN * LD + (wn * 32 * C::FN + l32) * LD + half * 8;
+#pragma unroll
+  for (int ks = 0; ks < C::BKH; ks += 16) {
+    bf16x8 a[C::FM], b[C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) a[i] = *reinterpret_cast<const bf16x8*>(a0 + i * 32 * LD + ks);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) b[j] = *reinterpret_cast<const bf16x8*>(b0 + j * 32 * LD + ks);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        if (MASK & (1 << (i * C::FN + j)))
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// acc = X[m0 ..] X[n0 ..]^T over K for bf16 rows with k contiguous (row
+// stride K, a multiple of BKH). Two LDS buffers and two register stages:
+// while the MFMAs run on K-tile kt, tile kt + 1 (loaded one phase earlier)
+// goes to the other buffer and tile kt + 2 is loaded into the freed stage, so
+// every load has a full phase to land; an odd last tile runs alone.
 template <class C, int MASK = -1>
 __device__ __forceinline__ void mainloop_bf16(const uint16_t* __restrict__ X, int K, int m0, int n0,
                                               int wm, int wn, floatx16 (&acc)[C::FM][C::FN],
                                               float* lds) {
-  constexpr int LD = C::LDKH;
-  uint16_t* sA = reinterpret_cast<uint16_t*>(lds);  // [2][BM][LD]
-  uint16_t* sB = sA + 2 * C::BM * LD;                // [2][BN][LD]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int half = lane >> 5, l32 = lane & 31;
+  uint16_t* sA = reinterpret_cast<uint16_t*>(lds);  // [2][BM][LDKH]
+  uint16_t* sB = sA + 2 * C::BM * C::LDKH;           // [2][BN][LDKH]
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // 16-byte chunks of a K-tile: CPR per row, rows x CPR per operand
-  constexpr int CPR = C::BKH / 8;
-  constexpr int CA = C::BM * CPR, CB = C::BN * CPR;
-  static_assert(CA % C::NT == 0 && CB % C::NT == 0, "uneven operand load");
-  constexpr int PA = CA / C::NT, PB = CB / C::NT;
-  u32x4 ra[PA], rb[PB];
   const int nk = K / C::BKH;
-#pragma unroll
-  for (int i = 0; i < PA; ++i) {
-    const int c = tid + i * C::NT;
-    ra[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(m0 + (c / CPR)) * K + ((c % CPR) * 8));
-  }
-#pragma unroll
-  for (int i = 0; i < PB; ++i) {
-    const int c = tid + i * C::NT;
-    rb[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(n0 + (c / CPR)) * K + ((c % CPR) * 8));
-  }
-#pragma unroll
-  for (int i = 0; i < PA; ++i) {
-    const int c = tid + i * C::NT;
-    *reinterpret_cast<u32x4*>(sA + (c / CPR) * LD + ((c % CPR) * 8)) = ra[i];
-  }
-#pragma unroll
-  for (int i = 0; i < PB; ++i) {
-    const int c = tid + i * C::NT;
-    *reinterpret_cast<u32x4*>(sB + (c / CPR) * LD + ((c % CPR) * 8)) = rb[i];
-  }
+  Bf16Stage<C> s0, s1;
+  bf16_load<C>(s0, X, K, m0, n0, 0);
+  if (nk > 1) bf16_load<C>(s1, X, K, m0, n0, 1);
+  bf16_store<C>(s0, sA, sB, 0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = (kt + 1) * C::BKH;
-#pragma unroll
-      for (int i = 0; i < PA; ++i) {
-        const int c = tid + i * C::NT;
-        ra[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(m0 + (c / CPR)) * K + k0 +
-                                                   ((c % CPR) * 8));
-      }
-#pragma unroll
-      for (int i = 0; i < PB; ++i) {
-        const int c = tid + i * C::NT;
-        rb[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(n0 + (c / CPR)) * K + k0 +
-                                                   ((c % CPR) * 8));
-      }
-    }
-    const uint16_t* a0 = sA + buf * C::BM * LD + (wm * 32 * C::FM + l32) * LD + half * 8;
-    const uint16_t* b0 = sB + buf * C::BN * LD + (wn * 32 * C::FN + l32) * LD + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < C::BKH; ks += 16) {
-      bf16x8 a[C::FM], b[C::FN];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) a[i] = *reinterpret_cast<const bf16x8*>(a0 + i * 32 * LD + ks);
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) b[j] = *reinterpret_cast<const bf16x8*>(b0 + j * 32 * LD + ks);
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          if (MASK & (1 << (i * C::FN + j)))
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      uint16_t* dA = sA + (buf ^ 1) * C::BM * LD;
-      uint16_t* dB = sB + (buf ^ 1) * C::BN * LD;
-#pragma unroll
-      for (int i = 0; i < PA; ++i) {
-        const int c = tid + i * C::NT;
-        *reinterpret_cast<u32x4*>(dA + (c / CPR) * LD + ((c % CPR) * 8)) = ra[i];
-      }
-#pragma unroll
-      for (int i = 0; i < PB; ++i) {
-        const int c = tid + i * C::NT;
-        *reinterpret_cast<u32x4*>(dB + (c / CPR) * LD + ((c % CPR) * 8)) = rb[i];
-      }
-    }
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    if (kt + 2 < nk) bf16_load<C>(s0, X, K, m0, n0, kt + 2);
+    bf16_mma<C, MASK>(acc, sA, sB, 0, wm, wn);
+    bf16_store<C>(s1, sA, sB, 1);
+    __syncthreads();
+    if (kt + 3 < nk) bf16_load<C>(s1, X, K, m0, n0, kt + 3);
+    bf16_mma<C, MASK>(acc, sA, sB, 1, wm, wn);
+    if (kt + 2 < nk) bf16_store<C>(s0, sA, sB, 0);
     __syncthreads();
   }
+  if (kt < nk) bf16_mma<C, MASK>(acc, sA, sB, 0, wm, wn);
 }
 
 // ---------------------------------------------------------------------------
@@ -929,7 +945,7 @@ __global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void syrk_ema_kern
 // Statistics from bf16 packed gradients: L <- beta2 L + g Gp Gp^T reads GpH
 // (rows of Gp), R <- beta2 R + g Gp^T Gp reads GpTH (rows of Gp^T).
 template <class C>
-__global__ __launch_bounds__(C::NT, 4) void syrk_bf16_kernel(GemmLaunch g) {
+__global__ __launch_bounds__(C::NT, 3) void syrk_bf16_kernel(GemmLaunch g) {
   sym_product<C, kPathBF16>(g);
 }
 

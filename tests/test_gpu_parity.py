@@ -503,6 +503,8 @@ def test_scaled_newton_lowrank_illconditioned():
     ("gpt_small_b256", ((300, 520), (256, 256), (130, 71), (512, 96)), (256, 256)),  # 128 tiles
     ("gpt_small_b256", ((200, 100), (64, 192)), (64, 64)),                           # 64 tiles
     ("single_64x32", ((64, 32), (70, 45)), (64, 32)),                                # 32 tiles
+    # odd K-tile counts of the two-stage main loop: K = 160 (L, 5 tiles), 96 (R, 3)
+    ("gpt_small_b256", ((200, 330), (96, 160)), (96, 160)),
 ])
 def test_bf16_statistics_every_block(name, shapes, block):
     """Ragged matrices with bf16 gradients and parameters: every block's
