@@ -45,6 +45,8 @@ struct TensorState {
   int apply_tile[shp::kMaxOrder] = {0, 0, 0, 0};  // 0: FMA mode product
   int64_t Kp[shp::kMaxOrder] = {0, 0, 0, 0};      // padded unfolding length (large dims)
   bool rotate[shp::kMaxOrder] = {false, false, false, false};
+  // statistics read the block itself by rows (dimension 0 on the split paths)
+  bool rows[shp::kMaxOrder] = {false, false, false, false};
   int ntiles[shp::kMaxOrder] = {0, 0, 0, 0};
   int resid_stride = 1, gram_chunks = 1, p = 4;
   bool momentum = false;
@@ -187,7 +189,12 @@ int make_tensor_plan(const shampoo_config_t* cfg, int32_t order, const int32_t* 
       ts.stat_tile[i] = occupancy_tile(ts.b[i], ts.B);
       ts.Kp[i] = (K + 15) / 16 * 16;
 
-      ts.rotate[i] = !(after == 1 && K == ts.Kp[i]);
+      // The unfolding of dimension 0 is the block itself, [b_0][K] with k
+      // contiguous: the split paths read it by rows when K-tiles pair up (the
+      // fp32 MFMA path wants it k-major). The last dimension's unfolding is
+      // k-major already; the others are transposed first.
+      ts.rows[i] = i == 0 && cfg->fp32_gemm != SHAMPOO_GEMM_F32 && K % 32 == 0;
+      ts.rotate[i] = !ts.rows[i] && !(after == 1 && K == ts.Kp[i]);
       if (ts.rotate[i]) ts.rot_stride = std::max<int64_t>(ts.rot_stride, ts.Kp[i] * ts.b[i]);
       ts.apply_tile[i] = K % 32 == 0 ? pick_tile((int)std::min<int64_t>(K, 1 << 30), ts.b[i]) : 0;
       ts.ntiles[ts.group[i]] = shp::sym_tiles(ts.b[i], ts.stat_tile[i]);
@@ -378,12 +385,13 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
       q.alpha = h->stat_scale;
       q.beta = (float)h->cfg.beta2;
       g.n_problems = 1;
-      // split paths: the k-major operand [Kp][n] read by columns; its K-tiles
-      // run in pairs, so an unfolding padded to an odd multiple of 16 stays on
-      // the fp32 MFMA. The transposed copy holds Gp's values (and zeros), so
-      // Gp's maxima serve it.
+      // split paths: the k-major operand [Kp][n] read by columns, or for
+      // dimension 0 the block itself [n][K] read by rows; K-tiles run in
+      // pairs, so an unfolding padded to an odd multiple of 16 stays on the
+      // fp32 MFMA. The transposed copy holds Gp's values (and zeros), so Gp's
+      // maxima serve it.
       const int mode = split_gemm(h) && ts.Kp[i] % 32 == 0 ? h->cfg.fp32_gemm : shp::kGemmF32;
-      q.p_cols = q.q_cols = mode != shp::kGemmF32 ? 1 : 0;
+      q.p_cols = q.q_cols = mode != shp::kGemmF32 && !ts.rows[i] ? 1 : 0;
       q.mP = q.mQ = tmx(h, 6);
       rc = timed(h, kStats, fl, 0.0, s,
                  [&] { return shp::launch_gemm_sym(g, ts.stat_tile[i], false, mode, s); });
