@@ -377,6 +377,16 @@ hipError_t launch_mode_product_update(const float* In, int64_t in_stride, const 
                                       int64_t x_stride, const TBlockMeta* blocks,
                                       const TensorMeta* tensors, TensorGeom g, int32_t R, int32_t B,
                                       float lr, int32_t param_bf16, hipStream_t s);
+// The last two mode products fused with the update, for two small trailing
+// dimensions of equal side n = g.b[order - 1] <= kMaxFusedSide: In is the
+// block rotated to [n][n][R], X2 and X3 the roots of dimensions order - 2 and
+// order - 1 (n x n per block, x_stride apart).
+constexpr int kMaxFusedSide = 5;
+hipError_t launch_mode_product2_update(const float* In, int64_t in_stride, const float* X2,
+                                       const float* X3, int64_t x_stride,
+                                       const TBlockMeta* blocks, const TensorMeta* tensors,
+                                       TensorGeom g, int32_t R, int32_t B, float lr,
+                                       int32_t param_bf16, hipStream_t s);
 // Small-side roots: per factor (count factors of side n, real extent nreal[f]),
 // fp64 cyclic Jacobi of H, X = V diag(max(lam, floor)^(-1/p)) V^T on the real
 // extent, zero elsewhere. status / final_iter / resid of each factor are written

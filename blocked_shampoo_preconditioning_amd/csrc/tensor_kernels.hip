@@ -334,6 +334,80 @@ __global__ __launch_bounds__(256) void mode_product_update_kernel(
   }
 }
 
+// The last two products of the chain fused with the parameter update, for two
+// small trailing dimensions of equal side N. In is the block rotated to
+// [N][N][R] (dimensions k - 2 and k - 1 first, the others after them in
+// order); for every r, T[l3][j2] = sum_l2 X2[j2][l2] In[l2][l3][r], then
+// U[r][j2][j3] = sum_l3 X3[j3][l3] T[l3][j2] (the two mode products of the
+// chain in their order, T kept in fp32 registers where the unfused chain
+// stores it as fp32), and W -= lr U on the block's real extent. One pass over
+// the block instead of two.
+template <int N, int K>
+__global__ __launch_bounds__(256) void mode_product2_update_kernel(
+    const float* __restrict__ In, int64_t in_stride, const float* __restrict__ X2,
+    const float* __restrict__ X3, int64_t x_stride, const TBlockMeta* __restrict__ blocks,
+    const TensorMeta* __restrict__ tensors, TensorGeom g, int R, float lr, int bf16) {
+  constexpr int NN = N * N;
+  __shared__ float su[256 * NN];    // U of the workgroup's 256 r, [r][j2][j3]
+  __shared__ int64_t soff[256];     // parameter offset of (r, 0, 0), -1 outside
+  const int b = blockIdx.z;
+  const float* in = In + (size_t)b * in_stride;
+  const float* x2 = X2 + (size_t)b * x_stride;
+  const float* x3 = X3 + (size_t)b * x_stride;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const TBlockMeta bm = blocks[b];
+  BlockGeo<K> geo;
+  geo.load(g, bm, tensors[bm.tensor]);
+  int64_t off = -1;
+  const bool ok = r < R && geo.offset(r * NN, off);
+  if (ok) {
+    float t[N][N];  // [l3][j2]
+#pragma unroll
+    for (int l3 = 0; l3 < N; ++l3)
+#pragma unroll
+      for (int j2 = 0; j2 < N; ++j2) t[l3][j2] = 0.f;
+#pragma unroll
+    for (int l2 = 0; l2 < N; ++l2)
+#pragma unroll
+      for (int l3 = 0; l3 < N; ++l3) {
+        const float v = in[(size_t)(l2 * N + l3) * R + r];
+#pragma unroll
+        for (int j2 = 0; j2 < N; ++j2) t[l3][j2] += x2[j2 * N + l2] * v;
+      }
+#pragma unroll
+    for (int j2 = 0; j2 < N; ++j2)
+#pragma unroll
+      for (int j3 = 0; j3 < N; ++j3) {
+        float u = 0.f;
+#pragma unroll
+        for (int l3 = 0; l3 < N; ++l3) u += x3[j3 * N + l3] * t[l3][j2];
+        su[threadIdx.x * NN + j2 * N + j3] = u;
+      }
+  }
+  soff[threadIdx.x] = ok ? off : -1;
+  __syncthreads();
+  // The update, element e of the workgroup's 256 N N values per thread step:
+  // with the tensor's natural strides consecutive threads reach consecutive
+  // parameters.
+  const int64_t st2 = geo.stride[K - 2], st3 = geo.stride[K - 1];
+  const int ext2 = geo.ext[K - 2], ext3 = geo.ext[K - 1];
+  void* param = tensors[bm.tensor].param;
+  for (int e = threadIdx.x; e < 256 * NN; e += 256) {
+    const int rl = e / NN, jj = e - rl * NN, j2 = jj / N, j3 = jj - j2 * N;
+    const int64_t o0 = soff[rl];
+    if (o0 < 0 || j2 >= ext2 || j3 >= ext3) continue;
+    const int64_t o = o0 + j2 * st2 + j3 * st3;
+    const float u = su[e];
+    if (bf16) {
+      uint16_t* w = reinterpret_cast<uint16_t*>(param) + o;
+      *w = f32_to_bf16(bf16_to_f32(*w) - lr * u);
+    } else {
+      float* w = reinterpret_cast<float*>(param) + o;
+      *w = *w - lr * u;
+    }
+  }
+}
+
 // One thread per factor: cyclic Jacobi in fp64 on the factor's real extent,
 // matrix and eigenvectors in this thread's slice of LDS.
 constexpr int kJacobiThreads = 64;
@@ -542,6 +616,29 @@ hipError_t launch_mode_product_update(const float* In, int64_t in_stride, const 
   SHP_MPU_K(8)
 #undef SHP_MPU_K
 #undef SHP_MPU
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mode_product2_update(const float* In, int64_t in_stride, const float* X2,
+                                       const float* X3, int64_t x_stride,
+                                       const TBlockMeta* blocks, const TensorMeta* tensors,
+                                       TensorGeom g, int32_t R, int32_t B, float lr,
+                                       int32_t param_bf16, hipStream_t s) {
+  if (B == 0 || R == 0) return hipSuccess;
+  if (g.order < 2 || g.order > 4) return hipErrorInvalidValue;
+  const int n = g.b[g.order - 1];
+  if (g.b[g.order - 2] != n) return hipErrorInvalidValue;
+  const dim3 grid((R + 255) / 256, 1, B);
+#define SHP_MP2(N, K)                                                                          \
+  if (n == N && g.order == K) {                                                                \
+    hipLaunchKernelGGL((mode_product2_update_kernel<N, K>), grid, dim3(256), 0, s, In,          \
+                       in_stride, X2, X3, x_stride, blocks, tensors, g, R, lr, param_bf16);    \
+    return hipGetLastError();                                                                  \
+  }
+#define SHP_MP2_K(N) SHP_MP2(N, 2) SHP_MP2(N, 3) SHP_MP2(N, 4)
+  SHP_MP2_K(1) SHP_MP2_K(2) SHP_MP2_K(3) SHP_MP2_K(4) SHP_MP2_K(5)
+#undef SHP_MP2_K
+#undef SHP_MP2
   return hipErrorInvalidValue;
 }
 

@@ -464,6 +464,20 @@ int do_tensor_apply(shampoo_ctx* h, hipStream_t s, float* out) {
     const double fl = ts.apply_flops[i];
     const double esz = h->cfg.param_dtype == SHAMPOO_BF16 ? 2.0 : 4.0;
     int rc;
+    if (i == ts.k - 2 && !out && !ts.is_big[i] && !ts.is_big[i + 1] && ts.b[i + 1] == n &&
+        n <= shp::kMaxFusedSide) {
+      // the last two products (two small dimensions of one side) and the
+      // update in one pass
+      const int64_t R2 = R / n;
+      const double fl2 = fl + ts.apply_flops[i + 1];
+      return timed(h, kApplyAux, fl2, 4.0 * ts.B * ts.E + 2.0 * esz * ts.real_elems, s, [&] {
+        return shp::launch_mode_product2_update(
+            cur, ts.E, X, roots + ts.foff[i + 1], (int64_t)n * n,
+            h->at<shp::TBlockMeta>(ts.off_blocks), h->at<shp::TensorMeta>(ts.off_meta),
+            geom(ts), (int32_t)R2, (int32_t)ts.B, (float)h->cfg.lr,
+            h->cfg.param_dtype == SHAMPOO_BF16, s);
+      });
+    }
     if (i == ts.k - 1 && !out && !ts.is_big[i]) {
       // last product of the chain with the update in its epilogue
       rc = timed(h, kApplyAux, fl, 4.0 * ts.B * ts.E + 2.0 * esz * ts.real_elems, s, [&] {

@@ -33,9 +33,11 @@ def tw(name="case", **kw):
 
 
 CASES = {
-    # two large dimensions (transpose + SYRK, MFMA products), two small ones;
-    # the second tensor is one ragged block
-    "conv4_64x32": tw(shapes=((64, 32, 3, 3), (40, 20, 3, 3))),
+    # two large dimensions (SYRK in place and after a transpose, MFMA
+    # products), two small ones (their products fused with the update); the
+    # second tensor is one ragged block, the third ragged in the small
+    # dimensions too
+    "conv4_64x32": tw(shapes=((64, 32, 3, 3), (40, 20, 3, 3), (16, 8, 2, 3))),
     # large dimension whose unfolding length (12) needs padding and whose
     # product runs on the FMA kernel; ragged in every dimension
     "conv3_fma": tw(shapes=((96, 3, 3), (50, 7, 2)), block_dims=(32, 4, 3)),
