@@ -377,6 +377,13 @@ hipError_t launch_mode_product_update(const float* In, int64_t in_stride, const 
                                       int64_t x_stride, const TBlockMeta* blocks,
                                       const TensorMeta* tensors, TensorGeom g, int32_t R, int32_t B,
                                       float lr, int32_t param_bf16, hipStream_t s);
+// Statistics of two small trailing dimensions of one side n <= kMaxFusedSide in
+// one pass over the blocks ([A][n][n] each): chunk partials of both (pairs of
+// dimension order - 2, then of order - 1, in one row of kMaxPairs), then the
+// EMA of H2 and H3.
+hipError_t launch_small_gram2(const float* In, int64_t in_stride, int32_t A, int32_t n,
+                              int32_t B, float* partial, int32_t chunks, float* H2, float* H3,
+                              float beta2, float gamma, hipStream_t s);
 // The last two mode products fused with the update, for two small trailing
 // dimensions of equal side n = g.b[order - 1] <= kMaxFusedSide: In is the
 // block rotated to [n][n][R], X2 and X3 the roots of dimensions order - 2 and

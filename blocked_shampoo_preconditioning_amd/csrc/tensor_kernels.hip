@@ -213,6 +213,66 @@ __global__ __launch_bounds__(256) void small_gram_kernel(const float* __restrict
         red[0][q] + red[1][q] + red[2][q] + red[3][q];
 }
 
+// Both statistics of two small trailing dimensions of one side N in one pass:
+// the block is [A][N][N] (slices S_a of N x N contiguous values). Dimension
+// k - 2 sums S_a[l][c] S_a[m][c] over a and c, dimension k - 1 sums
+// S_a[c][l] S_a[c][m]; their pairs go to q < NP and NP <= q < 2 NP of the
+// chunk's partial row. Each workgroup stages its 256 slices through LDS, so
+// the block is read in whole lines.
+template <int N>
+__global__ __launch_bounds__(256) void small_gram2_kernel(const float* __restrict__ In,
+                                                          int64_t in_stride, int A,
+                                                          float* __restrict__ partial) {
+  constexpr int NN = N * N, NP = N * (N + 1) / 2;
+  static_assert(2 * NP <= kMaxPairs, "pairs of both dimensions must fit one partial row");
+  __shared__ float tile[256 * NN];
+  __shared__ float red[4][2 * NP];
+  const int b = blockIdx.y;
+  const float* in = In + (size_t)b * in_stride;
+  float acc[2 * NP];
+#pragma unroll
+  for (int q = 0; q < 2 * NP; ++q) acc[q] = 0.f;
+  for (int64_t a0 = (int64_t)blockIdx.x * 256; a0 < A; a0 += (int64_t)gridDim.x * 256) {
+    const int cnt = (int)min((int64_t)256, A - a0) * NN;
+    __syncthreads();  // the previous slices have been read
+    for (int e = threadIdx.x; e < cnt; e += 256) tile[e] = in[a0 * NN + e];
+    __syncthreads();
+    if (a0 + threadIdx.x < A) {
+      float v[N][N];
+#pragma unroll
+      for (int l = 0; l < N; ++l)
+#pragma unroll
+        for (int c = 0; c < N; ++c) v[l][c] = tile[threadIdx.x * NN + l * N + c];
+      int k = 0;
+#pragma unroll
+      for (int l = 0; l < N; ++l)
+#pragma unroll
+        for (int m = l; m < N; ++m, ++k) {
+          float x = 0.f, y = 0.f;
+#pragma unroll
+          for (int c = 0; c < N; ++c) {
+            x += v[l][c] * v[m][c];
+            y += v[c][l] * v[c][m];
+          }
+          acc[k] += x;
+          acc[NP + k] += y;
+        }
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 2 * NP; ++q) {
+    float x = acc[q];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    if (lane == 0) red[wave][q] = x;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 2 * NP; q += 256)
+    partial[((size_t)b * gridDim.x + blockIdx.x) * kMaxPairs + q] =
+        red[0][q] + red[1][q] + red[2][q] + red[3][q];
+}
+
 // H <- beta2 H + gamma * (sum of the chunk partials, in chunk order).
 __global__ __launch_bounds__(64) void small_gram_ema_kernel(const float* __restrict__ partial,
                                                             int chunks, int n, float* __restrict__ H,
@@ -574,6 +634,29 @@ hipError_t launch_small_gram(const float* In, int64_t in_stride, int32_t A, int3
   }
   hipLaunchKernelGGL(small_gram_ema_kernel, dim3(B), dim3(64), 0, s, partial, chunks, n, H, beta2,
                      gamma);
+  return hipGetLastError();
+}
+
+hipError_t launch_small_gram2(const float* In, int64_t in_stride, int32_t A, int32_t n,
+                              int32_t B, float* partial, int32_t chunks, float* H2, float* H3,
+                              float beta2, float gamma, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid(chunks, B);
+  switch (n) {
+#define SHP_GRAM2(N)                                                                            \
+  case N:                                                                                       \
+    hipLaunchKernelGGL(small_gram2_kernel<N>, grid, dim3(256), 0, s, In, in_stride, A, partial); \
+    break;
+    SHP_GRAM2(1) SHP_GRAM2(2) SHP_GRAM2(3) SHP_GRAM2(4) SHP_GRAM2(5)
+#undef SHP_GRAM2
+    default:
+      return hipErrorInvalidValue;
+  }
+  const int np = n * (n + 1) / 2;
+  hipLaunchKernelGGL(small_gram_ema_kernel, dim3(B), dim3(64), 0, s, partial, chunks, n, H2, beta2,
+                     gamma);
+  hipLaunchKernelGGL(small_gram_ema_kernel, dim3(B), dim3(64), 0, s, partial + np, chunks, n, H3,
+                     beta2, gamma);
   return hipGetLastError();
 }
 

@@ -395,6 +395,17 @@ int do_tensor_stats(shampoo_ctx* h, hipStream_t s) {
       q.mP = q.mQ = tmx(h, 6);
       rc = timed(h, kStats, fl, 0.0, s,
                  [&] { return shp::launch_gemm_sym(g, ts.stat_tile[i], false, mode, s); });
+    } else if (i == ts.k - 2 && !ts.is_big[i + 1] && ts.b[i + 1] == n &&
+               n <= shp::kMaxFusedSide) {
+      // both small trailing dimensions in one pass over the blocks
+      rc = timed(h, kStatsAux, fl + ts.stat_flops[i + 1], 4.0 * ts.B * ts.E, s, [&] {
+        return shp::launch_small_gram2(gp, ts.E, (int32_t)(ts.E / ((int64_t)n * n)), n,
+                                       (int32_t)ts.B, fptr(h, ts.off_partial), ts.gram_chunks, H,
+                                       stats + ts.foff[i + 1], (float)h->cfg.beta2,
+                                       h->stat_scale, s);
+      });
+      if (rc) return rc;
+      break;  // the last dimension's statistic is formed too
     } else {
       rc = timed(h, kStatsAux, fl, 4.0 * ts.B * ts.E, s, [&] {
         return shp::launch_small_gram(gp, ts.E, (int32_t)A, n, (int32_t)C, (int32_t)ts.B,
