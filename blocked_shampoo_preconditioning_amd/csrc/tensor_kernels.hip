@@ -62,6 +62,35 @@ struct BlockGeo {
     }
     return in;
   }
+  // Indices of packed element e (the last dimension fastest), the offset and
+  // real-extent test of an index, and the next element in packed order: a
+  // thread that takes consecutive elements decomposes only the first.
+  __device__ __forceinline__ void indices(int e, int (&idx)[K]) const {
+#pragma unroll
+    for (int d = K - 1; d > 0; --d) {
+      const int q = magic[d] == 0 ? e : (int)__umul64hi((uint64_t)(uint32_t)e, magic[d]);
+      idx[d] = e - q * b[d];
+      e = q;
+    }
+    idx[0] = e;
+  }
+  __device__ __forceinline__ bool at(const int (&idx)[K], int64_t& off) const {
+    off = base;
+    bool in = true;
+#pragma unroll
+    for (int d = 0; d < K; ++d) {
+      in = in && idx[d] < ext[d];
+      off += (int64_t)idx[d] * stride[d];
+    }
+    return in;
+  }
+  __device__ __forceinline__ void step(int (&idx)[K]) const {
+#pragma unroll
+    for (int d = K - 1; d >= 0; --d) {
+      if (++idx[d] < b[d]) return;
+      idx[d] = 0;
+    }
+  }
 };
 
 // floor(i / d) for 0 <= i < 2^22 and d >= 1, from inv = 1 / d: the float
@@ -88,19 +117,50 @@ __global__ __launch_bounds__(256) void tensor_pack_kernel(const TBlockMeta* __re
   BlockGeo<K> geo;
   geo.load(g, bm, tensors[bm.tensor]);
   const void* grad = tensors[bm.tensor].grad;
-  for (int e = blockIdx.x * 256 + threadIdx.x; e < g.E; e += gridDim.x * 256) {
-    int64_t off;
-    float v = 0.f;
-    if (geo.offset(e, off))
-      v = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(grad)[off])
-               : reinterpret_cast<const float*>(grad)[off];
-    const size_t o = (size_t)b * g.E + e;
-    Gp[o] = v;
-    mg = fmaxf(mg, fabsf(v));
-    if (Mom != nullptr) {
-      const float m = momentum * Mom[o] + v;
-      Mom[o] = m;
-      mm = fmaxf(mm, fabsf(m));
+  if ((g.E & 3) == 0) {
+    // four consecutive elements a thread: one index decomposition, 16-byte
+    // stores of the packed block (and momentum)
+    for (int e = (blockIdx.x * 256 + threadIdx.x) * 4; e < g.E; e += gridDim.x * 256 * 4) {
+      int idx[K];
+      geo.indices(e, idx);
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int64_t off;
+        v[q] = 0.f;
+        if (geo.at(idx, off))
+          v[q] = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(grad)[off])
+                      : reinterpret_cast<const float*>(grad)[off];
+        if (q < 3) geo.step(idx);
+      }
+      const size_t o = (size_t)b * g.E + e;
+      *reinterpret_cast<float4*>(Gp + o) = make_float4(v[0], v[1], v[2], v[3]);
+      mg = fmaxf(mg, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+      if (Mom != nullptr) {
+        float4 m = *reinterpret_cast<const float4*>(Mom + o);
+        m.x = momentum * m.x + v[0];
+        m.y = momentum * m.y + v[1];
+        m.z = momentum * m.z + v[2];
+        m.w = momentum * m.w + v[3];
+        *reinterpret_cast<float4*>(Mom + o) = m;
+        mm = fmaxf(mm, fmaxf(fmaxf(fabsf(m.x), fabsf(m.y)), fmaxf(fabsf(m.z), fabsf(m.w))));
+      }
+    }
+  } else {
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < g.E; e += gridDim.x * 256) {
+      int64_t off;
+      float v = 0.f;
+      if (geo.offset(e, off))
+        v = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(grad)[off])
+                 : reinterpret_cast<const float*>(grad)[off];
+      const size_t o = (size_t)b * g.E + e;
+      Gp[o] = v;
+      mg = fmaxf(mg, fabsf(v));
+      if (Mom != nullptr) {
+        const float m = momentum * Mom[o] + v;
+        Mom[o] = m;
+        mm = fmaxf(mm, fabsf(m));
+      }
     }
   }
   if (mo.a != nullptr || mo.b != nullptr)

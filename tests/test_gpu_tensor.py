@@ -107,9 +107,13 @@ def run_tensor_parity(w, steps, ids=None, root_method="eigh", sh_over=None):
     return worst_s, worst_u, wp, sh, orc
 
 
-@pytest.mark.parametrize("case", sorted(CASES))
+# blocks of an odd element count (3 x 5 x 3): the pack's one-element path
+PACK_CASES = dict(CASES, odd_block=tw(shapes=((7, 5, 3), (3, 2, 3)), block_dims=(3, 5, 3)))
+
+
+@pytest.mark.parametrize("case", sorted(PACK_CASES))
 def test_tensor_pack_unpack_bitexact(case):
-    w = CASES[case]
+    w = PACK_CASES[case]
     log(f"tensor pack {case}")
     src = synth.TensorGradientSource(w, device="cuda")
     grads = src.grads(1)
