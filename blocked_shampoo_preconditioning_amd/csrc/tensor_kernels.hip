@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void small_gram2_kernel(const float* __restric
                                                           float* __restrict__ partial) {
   constexpr int NN = N * N, NP = N * (N + 1) / 2;
   static_assert(2 * NP <= kMaxPairs, "pairs of both dimensions must fit one partial row");
-  __shared__ float tile[256 * NN];
+  __shared__ __align__(16) float tile[256 * NN];
   __shared__ float red[4][2 * NP];
   const int b = blockIdx.y;
   const float* in = In + (size_t)b * in_stride;
@@ -295,7 +295,16 @@ __global__ __launch_bounds__(256) void small_gram2_kernel(const float* __restric
   for (int64_t a0 = (int64_t)blockIdx.x * 256; a0 < A; a0 += (int64_t)gridDim.x * 256) {
     const int cnt = (int)min((int64_t)256, A - a0) * NN;
     __syncthreads();  // the previous slices have been read
-    for (int e = threadIdx.x; e < cnt; e += 256) tile[e] = in[a0 * NN + e];
+    const float* src = in + a0 * NN;
+    if ((in_stride & 3) == 0) {
+      // 16-byte loads: 256 N N floats per step keep a0 N N a multiple of 4
+      const int c4 = cnt >> 2;
+      for (int e = threadIdx.x; e < c4; e += 256)
+        reinterpret_cast<float4*>(tile)[e] = reinterpret_cast<const float4*>(src)[e];
+      for (int e = 4 * c4 + threadIdx.x; e < cnt; e += 256) tile[e] = src[e];
+    } else {
+      for (int e = threadIdx.x; e < cnt; e += 256) tile[e] = src[e];
+    }
     __syncthreads();
     if (a0 + threadIdx.x < A) {
       float v[N][N];
