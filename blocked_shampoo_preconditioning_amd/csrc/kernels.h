@@ -377,6 +377,9 @@ hipError_t launch_mode_product_update(const float* In, int64_t in_stride, const 
                                       int64_t x_stride, const TBlockMeta* blocks,
                                       const TensorMeta* tensors, TensorGeom g, int32_t R, int32_t B,
                                       float lr, int32_t param_bf16, hipStream_t s);
+// Largest side of the two-dimension fusions below (small statistics, last
+// two mode products with the update).
+constexpr int kMaxFusedSide = 5;
 // Statistics of two small trailing dimensions of one side n <= kMaxFusedSide in
 // one pass over the blocks ([A][n][n] each): chunk partials of both (pairs of
 // dimension order - 2, then of order - 1, in one row of kMaxPairs), then the
@@ -388,7 +391,6 @@ hipError_t launch_small_gram2(const float* In, int64_t in_stride, int32_t A, int
 // dimensions of equal side n = g.b[order - 1] <= kMaxFusedSide: In is the
 // block rotated to [n][n][R], X2 and X3 the roots of dimensions order - 2 and
 // order - 1 (n x n per block, x_stride apart).
-constexpr int kMaxFusedSide = 5;
 hipError_t launch_mode_product2_update(const float* In, int64_t in_stride, const float* X2,
                                        const float* X3, int64_t x_stride,
                                        const TBlockMeta* blocks, const TensorMeta* tensors,
