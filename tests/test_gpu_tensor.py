@@ -225,6 +225,25 @@ def test_tensor_only_small_dimensions():
     sh.close()
 
 
+@pytest.mark.parametrize("shapes,block_dims", [
+    (((5, 4, 4), (3, 2, 3)), (4, 4, 4)),   # order 3, last two dimensions 4 x 4, ragged
+    (((5, 5), (3, 2)), (5, 5)),            # order 2: both dimensions small and equal
+    (((40, 2, 2), (70, 1, 2)), (32, 2, 2)),  # a large dimension, then 2 x 2, ragged
+])
+def test_tensor_fused_small_pair(shapes, block_dims):
+    """The two small trailing dimensions of one side: statistics from one pass
+    and the last two mode products fused with the update (other sides and
+    orders than the conv filters' 3 x 3), with momentum on one step path."""
+    w = tw(name="small_pair", shapes=shapes, block_dims=block_dims, root_every=2, steps=3)
+    s, u, wp, sh, _ = run_tensor_parity(w, 3)
+    assert s <= STATS_TOL and u <= UPDATE_TOL and wp <= UPDATE_TOL, (s, u, wp)
+    sh.close()
+    w = dataclasses.replace(w, momentum=0.9)
+    s, u, wp, sh, _ = run_tensor_parity(w, 3)
+    assert s <= STATS_TOL and u <= UPDATE_TOL and wp <= UPDATE_TOL, (s, u, wp)
+    sh.close()
+
+
 def test_tensor_empty_and_zero_tensors():
     """A handle with no tensors steps as a no-op; a zero-extent tensor among
     others is skipped (its pointer may be NULL)."""
