@@ -342,26 +342,37 @@ __global__ __launch_bounds__(256) void small_gram2_kernel(const float* __restric
         red[0][q] + red[1][q] + red[2][q] + red[3][q];
 }
 
-// H <- beta2 H + gamma * (sum of the chunk partials, in chunk order).
+// H <- beta2 H + gamma * (sum of the chunk partials). One wave per block and
+// statistic: lanes take chunks lane, lane + 64, ... and a shuffle tree adds
+// the lanes, in fp64 and a fixed order (a serial sum per pair had been one
+// chain of dependent loads). blockIdx.y = 1 forms a second statistic H2 from
+// the pairs that follow the first's in the partial row.
 __global__ __launch_bounds__(64) void small_gram_ema_kernel(const float* __restrict__ partial,
                                                             int chunks, int n, float* __restrict__ H,
-                                                            float beta2, float gamma) {
+                                                            float* __restrict__ H2, float beta2,
+                                                            float gamma) {
   const int b = blockIdx.x;
   const int np = n * (n + 1) / 2;
-  float* h = H + (size_t)b * n * n;
-  for (int q = threadIdx.x; q < np; q += 64) {
+  const int q0 = blockIdx.y * np;
+  float* h = (blockIdx.y == 0 ? H : H2) + (size_t)b * n * n;
+  const int lane = threadIdx.x;
+  for (int q = 0; q < np; ++q) {
     double s = 0.0;
-    for (int c = 0; c < chunks; ++c) s += partial[((size_t)b * chunks + c) * kMaxPairs + q];
-    // pair q -> (l, m), l <= m
-    int l = 0, rem = q;
-    while (rem >= n - l) {
-      rem -= n - l;
-      ++l;
+    for (int c = lane; c < chunks; c += 64) s += partial[((size_t)b * chunks + c) * kMaxPairs + q0 + q];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) {
+      // pair q -> (l, m), l <= m
+      int l = 0, rem = q;
+      while (rem >= n - l) {
+        rem -= n - l;
+        ++l;
+      }
+      const int m = l + rem;
+      const float v = beta2 * h[l * n + m] + gamma * (float)s;
+      h[l * n + m] = v;
+      h[m * n + l] = v;
     }
-    const int m = l + rem;
-    const float v = beta2 * h[l * n + m] + gamma * (float)s;
-    h[l * n + m] = v;
-    h[m * n + l] = v;
   }
 }
 
@@ -701,8 +712,8 @@ hipError_t launch_small_gram(const float* In, int64_t in_stride, int32_t A, int3
     default:
       return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(small_gram_ema_kernel, dim3(B), dim3(64), 0, s, partial, chunks, n, H, beta2,
-                     gamma);
+  hipLaunchKernelGGL(small_gram_ema_kernel, dim3(B, 1), dim3(64), 0, s, partial, chunks, n, H,
+                     nullptr, beta2, gamma);
   return hipGetLastError();
 }
 
@@ -721,11 +732,8 @@ hipError_t launch_small_gram2(const float* In, int64_t in_stride, int32_t A, int
     default:
       return hipErrorInvalidValue;
   }
-  const int np = n * (n + 1) / 2;
-  hipLaunchKernelGGL(small_gram_ema_kernel, dim3(B), dim3(64), 0, s, partial, chunks, n, H2, beta2,
-                     gamma);
-  hipLaunchKernelGGL(small_gram_ema_kernel, dim3(B), dim3(64), 0, s, partial + np, chunks, n, H3,
-                     beta2, gamma);
+  hipLaunchKernelGGL(small_gram_ema_kernel, dim3(B, 2), dim3(64), 0, s, partial, chunks, n, H2,
+                     H3, beta2, gamma);
   return hipGetLastError();
 }
 
