@@ -88,6 +88,8 @@ class BlockInfo:
     bi, bj: block row / block column inside that matrix.
     r0, c0: first row / column of the block in the matrix.
     m, n:   real extent of the block (smaller than the block shape for tails).
+
+    Pinned by: test_block_counts_of_the_workloads, test_pack_matches_elementwise_enumeration.
     """
 
     id: int
@@ -105,6 +107,9 @@ def block_table(shapes, block_rows, block_cols):
 
     Matrices keep registration order; inside a matrix, blocks go in row-major
     block order; a tail block keeps its real extent.
+
+    Pinned by: test_block_counts_of_the_workloads (the workloads' block counts from their shapes),
+        test_pack_matches_elementwise_enumeration (row-major order).
     """
     table = []
     for mat, (rows, cols) in enumerate(shapes):
@@ -124,6 +129,9 @@ def pack_blocks(mats, table, block_rows, block_cols):
 
     Values are copied unchanged (same dtype as the inputs); entries outside
     a tail block's real extent are +0.0.
+
+    Pinned by: test_pack_matches_elementwise_enumeration (an independent per-element enumeration,
+        zero tails), test_tail_blocks_equal_padded_blocks.
     """
     dtype = mats[0].dtype if mats else np.float32
     out = np.zeros((len(table), block_rows, block_cols), dtype=dtype)
@@ -133,7 +141,10 @@ def pack_blocks(mats, table, block_rows, block_cols):
 
 
 def unpack_blocks(packed, table, shapes):
-    """Inverse of pack_blocks: write each block's real extent back."""
+    """Inverse of pack_blocks: write each block's real extent back.
+
+    Pinned by: test_pack_matches_elementwise_enumeration (the exact round trip).
+    """
     mats = [np.zeros(s, dtype=packed.dtype) for s in shapes]
     for b in table:
         mats[b.mat][b.r0:b.r0 + b.m, b.c0:b.c0 + b.n] = packed[b.id, :b.m, :b.n]
@@ -145,7 +156,11 @@ def unpack_blocks(packed, table, shapes):
 # EMA weight as in the SOAP record's beta_shampoo sweep)
 # ---------------------------------------------------------------------------
 def update_statistics(L, R, G, beta2, stat_scale):
-    """L <- beta2 L + stat_scale G G^T ;  R <- beta2 R + stat_scale G^T G."""
+    """L <- beta2 L + stat_scale G G^T ;  R <- beta2 R + stat_scale G^T G.
+
+    Pinned by: test_statistics_closed_sum (the non-recursive sum), test_kronecker_bruteforce_tiny,
+        test_first_step_svd_closed_form, test_two_by_two_example_all_ones.
+    """
     G = np.asarray(G, dtype=np.float64)
     L_new = beta2 * L + stat_scale * (G @ G.T)
     R_new = beta2 * R + stat_scale * (G.T @ G)
@@ -160,6 +175,9 @@ def inverse_root_eigh(A, p=4):
 
     A = Q diag(lam) Q^T  =>  A^(-1/p) = Q diag(lam^(-1/p)) Q^T.  A matrix
     that is not positive definite is an error, never silently clamped.
+
+    Pinned by: test_inverse_root_2x2_analytic, test_invariants, test_scalar_one_by_one,
+        test_diagonal_gradients_closed_form, test_kronecker_bruteforce_tiny.
     """
     A = np.asarray(A, dtype=np.float64)
     lam, Q = np.linalg.eigh(A)
@@ -171,7 +189,10 @@ def inverse_root_eigh(A, p=4):
 
 
 def _power_lambda(A, power_iters=16):
-    """||A v_k|| after power_iters products from v_0 = 1 / sqrt(n) (0 if A v = 0)."""
+    """||A v_k|| after power_iters products from v_0 = 1 / sqrt(n) (0 if A v = 0).
+
+    Pinned by: test_newton_scale_mode2_power_iteration (closed form on a diagonal matrix).
+    """
     v = np.full(A.shape[0], 1.0 / math.sqrt(A.shape[0]))
     lam = 0.0
     for _ in range(power_iters):
@@ -202,6 +223,8 @@ def newton_scale(A, p=4, mode=1, power_iters=16):
             eigenvector: the spectrum of A / s stays below 5 (the iteration's
             convergence region) unless |c_1| < 0.4^16 = 4.3e-7. If lam is 0,
             s falls back to min(||A||_F, ||A||_inf) * 2 / (p + 1).
+
+    Pinned by: test_newton_scale_bounds_spectrum, test_newton_scale_mode2_power_iteration.
     """
     A = np.asarray(A, dtype=np.float64)
     fro = math.sqrt(float(np.sum(A * A)))
@@ -248,7 +271,10 @@ def power_pair(A, power_iters=16):
     q_j = u_j^T A u_j and u_(j+1) the normalised lam_j u_j - A u_j (a power
     step on lam_j I - A, whose top eigenvector is A's bottom one). Returns
     (lam_(P-1), q_(P-1)) for P = power_iters: lam is mode 2's estimate, q a
-    Rayleigh quotient (never below the smallest eigenvalue)."""
+    Rayleigh quotient (never below the smallest eigenvalue).
+
+    Pinned by: test_power_pair_top_matches_mode_2_and_bottom_converges.
+    """
     A = np.asarray(A, dtype=np.float64)
     n = A.shape[0]
     v = np.full(n, 1.0 / math.sqrt(n))
@@ -272,13 +298,20 @@ def power_pair(A, power_iters=16):
 def spectrum_floor_estimate(A, power_iters=16):
     """Estimate of the smallest eigenvalue of a symmetric A that is never
     below it: the smaller of the smallest diagonal entry and power_pair's
-    Rayleigh quotient (both are Rayleigh quotients of A)."""
+    Rayleigh quotient (both are Rayleigh quotients of A).
+
+    Pinned by: test_spectrum_floor_estimate_bounds.
+    """
     A = np.asarray(A, dtype=np.float64)
     return min(float(np.min(np.diag(A))), power_pair(A, power_iters)[1])
 
 
 def newton_map(m, p, mu=1.0):
-    """f(mu m) = mu m ((p + 1 - mu m) / p)^p."""
+    """f(mu m) = mu m ((p + 1 - mu m) / p)^p.
+
+    Pinned by: test_newton_map_shape (maximum 1 at the fixed point, the quadratic constant (p + 1) /
+        (2 p)).
+    """
     y = mu * m
     return y * ((p + 1 - y) / p) ** p
 
@@ -286,7 +319,11 @@ def newton_map(m, p, mu=1.0):
 def newton_balance(a, p):
     """mu in [1, 0.9 (p + 1)] with f(mu a) = f(mu), by BALANCE_STEPS bisection
     steps (the lower end of the last bracket); 0.9 (p + 1) when f(mu a) < f(mu)
-    holds even there."""
+    holds even there.
+
+    Pinned by: test_newton_balance_closed_form (closed-form balance point, an independent root
+        finder, the cap).
+    """
     lo, hi = 1.0, 0.9 * (p + 1)
     if newton_map(a, p, hi) < newton_map(1.0, p, hi):
         return hi
@@ -324,7 +361,11 @@ def final_step_bound(r, n, p):
     sum e^4 <= (sum e^2)^2, so the new residual is at most C sqrt(n) r^2 (to
     leading order). When this is already below tol the last iteration needs
     only X <- X T: M would be formed only to be checked. (A reading: the stop
-    rule's tolerance is met by the bound instead of by a formed residual.)"""
+    rule's tolerance is met by the bound instead of by a formed residual.)
+
+    Pinned by: test_final_step_forms_only_x (the bound holds against the formed residual and the
+        eigh root).
+    """
     return (p + 1) / (2.0 * p) * math.sqrt(n) * r * r
 
 
@@ -345,6 +386,10 @@ def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
     rounding floor). tol <= 0 runs exactly max_iters iterations and skips
     those tests; in both modes a non-finite residual stops the iteration and
     keeps the previous X.
+
+    Pinned by: test_newton_converges_to_eigh, test_newton_orthogonal_similarity,
+        test_newton_scalar_fixed_point_and_monotone, test_newton_guard_keeps_finite_iterate,
+        test_scaled_newton_reaches_the_root, test_scaled_newton_diagonal_closed_form.
     """
     A = np.asarray(A, dtype=np.float64)
     n = A.shape[0]
@@ -409,7 +454,10 @@ def db_scale(A, mode=2, power_iters=16):
     """Scale for the Denman-Beavers stages: the iteration converges for a
     spectrum inside (0, 2), so the spectral target is 1 instead of Newton's:
     mode 0 ||A||_F, mode 1 min(||A||_F, ||A||_inf), mode 2 the power estimate
-    lam itself (norm bound when lam is 0)."""
+    lam itself (norm bound when lam is 0).
+
+    Pinned by: test_newton_db_root_matches_eigh.
+    """
     A = np.asarray(A, dtype=np.float64)
     fro = math.sqrt(float(np.sum(A * A)))
     if mode == 0:
@@ -433,7 +481,11 @@ def sqrt_pair_db(A, max_iters=25, tol=0.0, divergence_factor=1.2):
     at r_k <= tol (keep pair k), on r_k >= r_(k-1) (stalled, or diverged for a
     growth beyond divergence_factor from r_(k-1) > FLOOR_GUARD; keep pair
     k - 1), on a non-finite r_k (keep pair k - 1), or after max_iters updates.
-    tol <= 0: exactly max_iters updates (only the non-finite guard)."""
+    tol <= 0: exactly max_iters updates (only the non-finite guard).
+
+    Pinned by: test_db_pair_gives_square_root_and_inverse, test_db_scalar_map,
+        test_growth_at_the_floor_is_a_stall_not_divergence.
+    """
     A = np.asarray(A, dtype=np.float64)
     n = A.shape[0]
     eye = np.eye(n)
@@ -476,7 +528,10 @@ def inverse_root_newton_db(A, max_iters=25, tol=0.0, scale_mode=2):
     DASH page's "Newton-DB" solver, whose formula the page does not give):
     with A~ = A / s, the first stage gives Y1 ~ A~^(1/2); the second, run on
     Y1, gives Z2 ~ Y1^(-1/2) = A~^(-1/4); the root is s^(-1/4) Z2.
-    Returns (X, (info_stage1, info_stage2))."""
+    Returns (X, (info_stage1, info_stage2)).
+
+    Pinned by: test_newton_db_root_matches_eigh, test_newton_db_orthogonal_similarity.
+    """
     A = np.asarray(A, dtype=np.float64)
     s = db_scale(A, scale_mode)
     Y1, _, info1 = sqrt_pair_db(A / s, max_iters, tol)
@@ -492,7 +547,10 @@ def chebyshev_interval(A, floor, power_iters=16):
     unless v_0 is almost orthogonal to the top eigenvector; the norms bound it
     always). floor is a lower bound of the smallest eigenvalue: for a Shampoo
     statistic, beta2^t eps (the decayed eps I start plus a PSD sum). r =
-    floor / s, kept below 0.999."""
+    floor / s, kept below 0.999.
+
+    Pinned by: test_chebyshev_converges_to_eigh_and_interval_is_valid.
+    """
     A = np.asarray(A, dtype=np.float64)
     fro = math.sqrt(float(np.sum(A * A)))
     bound = min(fro, float(np.max(np.sum(np.abs(A), axis=1))))
@@ -507,7 +565,11 @@ def chebyshev_coefficients(r, degree):
     [r, 1] at the d + 1 Chebyshev points (first kind): with
     theta_j = pi (j + 1/2) / (d + 1) and x_j = ((1 - r) cos theta_j + 1 + r) / 2,
     c_k = 2 / (d + 1) sum_j x_j^(-1/4) cos(k theta_j); the interpolant is
-    c_0 / 2 + sum_{k>=1} c_k T_k(t), t = (2 x - 1 - r) / (1 - r)."""
+    c_0 / 2 + sum_{k>=1} c_k T_k(t), t = (2 x - 1 - r) / (1 - r).
+
+    Pinned by: test_chebyshev_matches_numpy_interpolant_on_scalars,
+        test_chebyshev_coefficients_reproduce_the_function_at_the_nodes.
+    """
     N = degree + 1
     theta = math.pi * (np.arange(N) + 0.5) / N
     x = ((1.0 - r) * np.cos(theta) + 1.0 + r) / 2.0
@@ -522,7 +584,11 @@ def inverse_root_chebyshev(A, floor, degree=128, power_iters=16, interval=None):
     B_k = c_k I + 2 T B_(k+1) - B_(k+2), p = c_0 / 2 I + T B_1 - B_2 with
     T = (2 A / s - (1 + r) I) / (1 - r). A reading of the DASH page's
     Chebyshev inverse-root solver (the page gives no formula). interval, if
-    given, is the (s, r) to use instead of chebyshev_interval's."""
+    given, is the (s, r) to use instead of chebyshev_interval's.
+
+    Pinned by: test_chebyshev_converges_to_eigh_and_interval_is_valid,
+        test_chebyshev_orthogonal_similarity.
+    """
     A = np.asarray(A, dtype=np.float64)
     n = A.shape[0]
     eye = np.eye(n)
@@ -542,7 +608,11 @@ def inverse_root_chebyshev(A, floor, degree=128, power_iters=16, interval=None):
 # podcast cue 20)
 # ---------------------------------------------------------------------------
 def precondition(XL, G, XR):
-    """U = L^(-1/4) G R^(-1/4), given the two roots."""
+    """U = L^(-1/4) G R^(-1/4), given the two roots.
+
+    Pinned by: test_precondition_is_left_then_right, test_kronecker_bruteforce_tiny,
+        test_first_step_svd_closed_form.
+    """
     return np.asarray(XL, np.float64) @ np.asarray(G, np.float64) @ np.asarray(XR, np.float64)
 
 
@@ -552,6 +622,8 @@ def round_to_bf16(x):
     bfloat16 keeps 8 significant bits: write x = f * 2^e with f in [0.5, 1),
     round f * 256 to an integer with ties to even, scale back. Finite normal
     range only (the parameters here are far from under- and overflow).
+
+    Pinned by: test_round_to_bf16_matches_torch (torch's bfloat16 cast, ties included).
     """
     x = np.asarray(x, dtype=np.float64)
     f, e = np.frexp(x)
@@ -559,7 +631,10 @@ def round_to_bf16(x):
 
 
 def is_refresh_step(t, root_every):
-    """Roots are recomputed at t = 1, 1 + k, 1 + 2k, ... (k = root_every)."""
+    """Roots are recomputed at t = 1, 1 + k, 1 + 2k, ... (k = root_every).
+
+    Pinned by: test_refresh_schedule.
+    """
     return root_every > 0 and (t - 1) % root_every == 0
 
 
@@ -596,6 +671,11 @@ class ShampooOracle:
     param_bf16:   parameters are stored in bfloat16 after every update.
     momentum:     alpha of the momentum folded in before preconditioning
                   (0: none).
+
+    Pinned by: test_kronecker_bruteforce_single_64x32, test_shared_singular_vectors_multistep,
+        test_stale_roots_between_refreshes, test_update_sign_and_step_size,
+        test_momentum_constant_gradient_closed_form, test_momentum_is_linear_sum_of_past_updates,
+        test_bf16_params_are_rounded_after_each_step, test_two_by_two_example_diagonal_sum_form.
     """
 
     def __init__(self, shapes, block_rows, block_cols, beta2, eps, lr, root_every,

@@ -51,7 +51,10 @@ def _sizes(b, k):
 def tensor_block_table(shapes, b):
     """Blocks of every tensor: b is one block size for every dimension or one
     per dimension; dimension i is cut into chunks of b_i (the last one ragged).
-    Row-major block order inside a tensor, tensors in registration order."""
+    Row-major block order inside a tensor, tensors in registration order.
+
+    Pinned by: test_tensor_block_table, test_tensor_block_table_per_dimension_sizes.
+    """
     table = []
     for t, shape in enumerate(shapes):
         sizes = _sizes(b, len(shape))
@@ -65,7 +68,10 @@ def tensor_block_table(shapes, b):
 
 
 def pack_tensor_blocks(tensors, table, b):
-    """[n_blocks, b_1, ..., b_k]: each block at its origin, zeros past its real extent."""
+    """[n_blocks, b_1, ..., b_k]: each block at its origin, zeros past its real extent.
+
+    Pinned by: test_pack_tensor_blocks_places_and_pads.
+    """
     k = len(table[0].extent) if table else 0
     sizes = _sizes(b, k)
     out = np.zeros((len(table),) + sizes, dtype=np.asarray(tensors[0]).dtype if tensors else float)
@@ -77,18 +83,29 @@ def pack_tensor_blocks(tensors, table, b):
 
 def mode_unfold(G, i):
     """Mode-i unfolding: rows indexed by dimension i, columns by the others
-    in their original (row-major) order."""
+    in their original (row-major) order.
+
+    Pinned by: test_unfold_and_mode_product_by_hand,
+        test_statistics_sum_over_every_other_dimension_by_hand.
+    """
     G = np.asarray(G)
     return np.moveaxis(G, i, 0).reshape(G.shape[i], -1)
 
 
 def mode_product(G, X, i):
-    """G x_i X: Y[..., j, ...] = sum_l X[j, l] G[..., l, ...] along dimension i."""
+    """G x_i X: Y[..., j, ...] = sum_l X[j, l] G[..., l, ...] along dimension i.
+
+    Pinned by: test_unfold_and_mode_product_by_hand, test_mode_order_does_not_matter.
+    """
     return np.moveaxis(np.tensordot(X, np.asarray(G, np.float64), axes=([1], [i])), 0, i)
 
 
 def precondition_tensor(G, roots, order=None):
-    """G x_1 X_1 x_2 X_2 ... x_k X_k (in the given order of dimensions)."""
+    """G x_1 X_1 x_2 X_2 ... x_k X_k (in the given order of dimensions).
+
+    Pinned by: test_kronecker_bruteforce, test_rank_one_closed_form,
+        test_mode_order_does_not_matter.
+    """
     U = np.asarray(G, np.float64)
     for i in (range(U.ndim) if order is None else order):
         U = mode_product(U, roots[i], i)
@@ -102,6 +119,9 @@ class TensorShampooOracle:
     dimension); root_method "eigh" (the definition) or "newton" (coupled
     Newton for the inverse 2k-th root, newton_iters / newton_tol /
     newton_scale_mode as for matrices). Other arguments as ShampooOracle.
+
+    Pinned by: test_order_two_is_the_matrix_method, test_kronecker_bruteforce,
+        test_newton_root_at_power_2k, test_full_tensor_step_moves_only_its_blocks.
     """
 
     def __init__(self, shapes, b, beta2, eps, lr, root_every, stat_scale=None, blocks=None,

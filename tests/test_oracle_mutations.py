@@ -11,7 +11,8 @@ import oracle.shampoo_oracle as orc
 from tests import test_oracle_pins as pins
 
 _ORIG = {name: getattr(orc, name) for name in
-         ("update_statistics", "precondition", "inverse_root_eigh", "pack_blocks", "block_table")}
+         ("update_statistics", "precondition", "inverse_root_eigh", "pack_blocks", "block_table",
+          "newton_map", "newton_balance")}
 
 
 def _stats_L_uses_GtG(L, R, G, beta2, stat_scale):
@@ -70,6 +71,26 @@ def _table_column_major(shapes, br, bc):
     return [orc.BlockInfo(i, b.mat, b.bi, b.bj, b.r0, b.c0, b.m, b.n) for i, b in enumerate(out)]
 
 
+def _map_exponent_off_by_one(m, p, mu=1.0):
+    # one power too few in the eigenvalue map of a Newton iteration
+    y = mu * m
+    return y * ((p + 1 - y) / p) ** (p - 1)
+
+
+def _balance_branch_flipped(a, p):
+    # the bisection keeps the wrong half of its bracket
+    lo, hi = 1.0, 0.9 * (p + 1)
+    if orc.newton_map(a, p, hi) < orc.newton_map(1.0, p, hi):
+        return hi
+    for _ in range(orc.BALANCE_STEPS):
+        mid = 0.5 * (lo + hi)
+        if orc.newton_map(a, p, mid) < orc.newton_map(1.0, p, mid):
+            hi = mid
+        else:
+            lo = mid
+    return lo
+
+
 PIN_TESTS = [
     ("two_by_two_all_ones", pins.test_two_by_two_example_all_ones, ()),
     ("two_by_two_sum", pins.test_two_by_two_example_diagonal_sum_form, ()),
@@ -83,6 +104,8 @@ PIN_TESTS = [
     ("stale", pins.test_stale_roots_between_refreshes, ()),
     ("pack_enum", pins.test_pack_matches_elementwise_enumeration, ()),
     ("analytic_2x2", pins.test_inverse_root_2x2_analytic, ()),
+    ("newton_map_shape", pins.test_newton_map_shape, (4,)),
+    ("newton_balance", pins.test_newton_balance_closed_form, (4,)),
 ]
 
 MUTATIONS = [
@@ -95,6 +118,8 @@ MUTATIONS = [
     ("inverse_root_eigh", _root_wrong_sign_power),
     ("pack_blocks", _pack_transposed_blocks),
     ("block_table", _table_column_major),
+    ("newton_map", _map_exponent_off_by_one),
+    ("newton_balance", _balance_branch_flipped),
 ]
 
 

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 from oracle import (ShampooOracle, block_table, inverse_root_coupled_newton, inverse_root_eigh,
+                    newton_balance, newton_map,
                     is_refresh_step, newton_scale, pack_blocks, precondition, round_to_bf16,
                     unpack_blocks, update_statistics)
 
@@ -666,3 +667,59 @@ def test_final_step_forms_only_x(mode):
         M = np.linalg.matrix_power(X, 4) @ A  # the residual of the kept X, formed here
         # (formed again here, so up to the rounding of X^4 A itself)
         assert np.linalg.norm(M - np.eye(64)) / 8.0 <= info.residuals[-1] * 1.01 + 1e-11
+
+
+# ---------------------------------------------------------------------------
+# The scalar map of one coupled Newton iteration and the balance of scale
+# mode 3, pinned by their closed forms (not by the code's own formula)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("p", [4, 6, 8])
+def test_newton_map_shape(p):
+    """f(m) = m ((p + 1 - m)/p)^p is the eigenvalue map of one iteration. Its
+    fixed point 1 is a maximum of value 1 (f'(1) = 0 only for the exponent
+    p), f is 0 at both ends of (0, p + 1) and maps the interval into (0, 1],
+    and near 1 it is quadratic: 1 - f(1 + e) = C e^2 + O(e^3) with
+    C = (p + 1) / (2 p), the constant of the final-step bound."""
+    assert newton_map(1.0, p) == 1.0
+    assert newton_map(0.0, p) == 0.0 and abs(newton_map(p + 1.0, p)) == 0.0
+    m = np.linspace(1e-6, p + 1 - 1e-6, 4001)
+    fm = np.array([newton_map(x, p) for x in m])
+    assert np.all(fm > 0.0) and np.all(fm <= 1.0)
+    assert np.all(np.diff(fm[m < 1.0]) > 0.0) and np.all(np.diff(fm[m > 1.0]) < 0.0)
+    for e in (1e-3, -1e-3):
+        assert newton_map(1.0 + e, p) < 1.0
+        C = (1.0 - newton_map(1.0 + e, p)) / (e * e)
+        assert C == pytest.approx((p + 1) / (2.0 * p), rel=5e-3)
+    # mu scales the argument: f(m; mu) = f(mu m)
+    assert newton_map(0.3, p, 2.5) == newton_map(0.75, p)
+
+
+def _balance_closed_form(a, p):
+    """f(mu a) = f(mu) reduces to a^(1/p) (p + 1 - mu a) = p + 1 - mu, so
+    mu = (p + 1)(1 - c) / (1 - c a) with c = a^(1/p); capped at 0.9 (p + 1)."""
+    c = a ** (1.0 / p)
+    return min((p + 1) * (1.0 - c) / (1.0 - c * a), 0.9 * (p + 1))
+
+
+@pytest.mark.parametrize("p", [4, 6, 8])
+def test_newton_balance_closed_form(p):
+    """The bisection lands within its final bracket of the closed-form
+    balance point, the balance holds there (f(mu a) = f(mu) up to the bracket
+    width times the map's slope), and a bottom estimate too small to balance
+    inside [1, 0.9 (p + 1)] returns the cap."""
+    from scipy.optimize import brentq
+    width = (0.9 * (p + 1) - 1.0) / 2.0 ** 40
+    for a in (1e-3, 0.01, 0.05, 0.1, 0.3, 0.5, 0.74):
+        mu = newton_balance(a, p)
+        ref = _balance_closed_form(a, p)
+        assert 1.0 <= mu <= 0.9 * (p + 1)
+        assert abs(mu - ref) <= 2.0 * width + 1e-14 * ref, (a, mu, ref)
+        if ref < 0.9 * (p + 1):
+            # an independent root finder on the defining equation
+            g = lambda x: x * a * (p + 1 - x * a) ** p - x * (p + 1 - x) ** p  # noqa: E731
+            assert abs(mu - brentq(g, 1.0, 0.9 * (p + 1), xtol=1e-15, rtol=1e-15)) <= 2.0 * width
+            # the two ends of the spectrum land together
+            assert abs(newton_map(mu * a, p) - newton_map(mu, p)) < 1e-9
+    # tiny bottom estimate: the balance point lies beyond the cap
+    assert _balance_closed_form(1e-12, p) == 0.9 * (p + 1)
+    assert newton_balance(1e-12, p) == 0.9 * (p + 1)
