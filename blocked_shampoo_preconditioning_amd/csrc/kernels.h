@@ -297,6 +297,12 @@ hipError_t launch_db_stage2_init(float* Ybuf0, const float* Ybuf1, float* Z0buf,
 // Maximum words w[0 .. n) keep their exponents and take version ver (after a
 // restore wrote words of another handle's versions).
 hipError_t launch_rebase_words(uint64_t* w, int64_t n, uint64_t ver, hipStream_t s);
+// Copies `bytes` of host memory at src to device memory at dst (8-byte
+// aligned, with room for bytes rounded up to a multiple of 8) through the
+// arguments of small kernels: they are copied when a launch is enqueued, so
+// src may be freed or reused as soon as this returns and the host never
+// waits for a copy from pageable memory.
+hipError_t launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t s);
 
 // Tiles written by a symmetric product of side n with square tile t.
 inline int32_t sym_tiles(int32_t n, int32_t t) {

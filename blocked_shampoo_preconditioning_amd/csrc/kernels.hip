@@ -22,6 +22,7 @@
 #include "kernels.h"
 
 #include <math.h>
+#include <cstring>
 
 #include <type_traits>
 
@@ -2240,6 +2241,33 @@ hipError_t launch_cheb_combine(const float* Ahat, const float* T2, float* out, F
   hipLaunchKernelGGL(cheb_combine_kernel, dim3(chunks, fs.count()), dim3(256), 0, s, Ahat, T2, out,
                      fs, c, rec, mo);
   return hipGetLastError();
+}
+
+// Host tables (block map, pointer tables) travel as kernel arguments, 2 KiB
+// per launch.
+constexpr int kUploadWords = 256;
+struct UploadChunk {
+  uint64_t w[kUploadWords];
+};
+
+__global__ __launch_bounds__(kUploadWords) void upload_kernel(uint64_t* __restrict__ dst,
+                                                              UploadChunk c, int n) {
+  const int i = threadIdx.x;
+  if (i < n) dst[i] = c.w[i];
+}
+
+hipError_t launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t s) {
+  const int64_t words = (bytes + 7) / 8;
+  for (int64_t o = 0; o < words; o += kUploadWords) {
+    UploadChunk c{};
+    const int n = (int)std::min<int64_t>(kUploadWords, words - o);
+    std::memcpy(c.w, static_cast<const char*>(src) + 8 * o, (size_t)std::min<int64_t>(8 * n, bytes - 8 * o));
+    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(kUploadWords), 0, s,
+                       static_cast<uint64_t*>(dst) + o, c, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_rebase_words(uint64_t* w, int64_t n, uint64_t ver, hipStream_t s) {

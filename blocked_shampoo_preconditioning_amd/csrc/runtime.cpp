@@ -245,16 +245,10 @@ int upload_meta(shampoo_ctx* h, const void* const* grads, void* const* params, h
   for (int i = 0; same && i < n; ++i)
     same = m[i].grad == h->meta_host[i].grad && m[i].param == h->meta_host[i].param;
   if (same) return SHAMPOO_OK;
-  // the previous upload reads meta_host: let it finish before overwriting
-  if (h->meta_copied) HIP_CHECK(hipEventSynchronize(h->meta_copied));
+  // the table travels in kernel arguments: nothing to wait for
+  HIP_CHECK(shp::launch_upload(h->at<void>(h->plan.off_mats), m.data(), n * sizeof(shp::MatMeta), s));
   h->meta_host = m;
   h->meta_valid = true;
-  if (n) {
-    HIP_CHECK(hipMemcpyAsync(h->at<void>(h->plan.off_mats), h->meta_host.data(),
-                             n * sizeof(shp::MatMeta), hipMemcpyHostToDevice, s));
-    if (!h->meta_copied) HIP_CHECK(hipEventCreateWithFlags(&h->meta_copied, hipEventDisableTiming));
-    HIP_CHECK(hipEventRecord(h->meta_copied, s));
-  }
   return SHAMPOO_OK;
 }
 
@@ -570,11 +564,10 @@ int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats,
   };
   hipError_t e = hipSuccess;
   if (plan.B) {
-    e = hipMemcpyAsync(h->at<void>(plan.off_blocks), h->blocks.data(),
-                       plan.B * sizeof(shp::BlockMeta), hipMemcpyHostToDevice, s);
+    e = shp::launch_upload(h->at<void>(plan.off_blocks), h->blocks.data(),
+                           plan.B * sizeof(shp::BlockMeta), s);
     if (e == hipSuccess)
-      e = hipMemcpyAsync(h->at<void>(plan.off_nreal), nreal.data(), nreal.size() * 4,
-                         hipMemcpyHostToDevice, s);
+      e = shp::launch_upload(h->at<void>(plan.off_nreal), nreal.data(), nreal.size() * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(plan.off_status), 0, 2 * plan.B * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(plan.off_final), 0, 2 * plan.B * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(plan.off_scale), 0, 2 * plan.B * 4, s);
@@ -586,9 +579,6 @@ int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats,
     if (e == hipSuccess)
       e = shp::launch_init_state(m_lr(h), plan.fl, plan.br, plan.fr, plan.bc, (int32_t)plan.B,
                                  (float)cfg->eps, s);
-    // the host copies above are from pageable memory; make sure they are done
-    // before the temporaries go away
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
   }
   if (e != hipSuccess) return cleanup(hip_fail(e, "shampoo_init"));
   *out = h;
@@ -639,7 +629,6 @@ int shampoo_destroy(shampoo_t h) {
     (void)hipEventDestroy(r.stop);
   }
   for (auto e : h->event_pool) (void)hipEventDestroy(e);
-  if (h->meta_copied) (void)hipEventDestroy(h->meta_copied);
   delete h;
   return SHAMPOO_OK;
 }
@@ -716,14 +705,9 @@ int shampoo_unpack(shampoo_t h, void* const* dst, void* hip_stream) {
     m[i].param = dst[i];
     m[i].ld = h->mats[i].ld;
   }
-  if (p.n_mats) {
-    HIP_CHECK(hipMemcpyAsync(h->at<void>(p.off_umats), m.data(), m.size() * sizeof(shp::MatMeta),
-                             hipMemcpyHostToDevice, s));
-  }
+  HIP_CHECK(shp::launch_upload(h->at<void>(p.off_umats), m.data(), m.size() * sizeof(shp::MatMeta), s));
   HIP_CHECK(shp::launch_unpack(h->at<shp::BlockMeta>(p.off_blocks), h->at<shp::MatMeta>(p.off_umats),
                                (int32_t)p.B, p.br, p.bc, m_gp(h), s));
-  // the descriptor copy is from pageable host memory that dies here
-  HIP_CHECK(hipStreamSynchronize(s));
   return SHAMPOO_OK;
 }
 

@@ -95,7 +95,6 @@ struct shampoo_ctx {
   std::vector<shp::BlockMeta> blocks;
   std::vector<shp::MatMeta> meta_host;  // what the device table holds
   bool meta_valid = false;
-  hipEvent_t meta_copied = nullptr;     // the last upload of meta_host has finished
   int64_t t = 0;
   bool roots_valid = false;
   // version of the last launch that wrote maximum words; grows by one per

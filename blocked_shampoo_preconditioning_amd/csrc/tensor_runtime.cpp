@@ -35,7 +35,6 @@ struct TensorState {
   std::vector<shp::TBlockMeta> blocks;
   std::vector<shp::TensorMeta> meta_host;
   bool meta_valid = false;
-  hipEvent_t meta_copied = nullptr;
   // dimensions by kind; group[i]: index of dimension i's factors in the
   // per-factor arrays (large dimensions first, in order, then the small ones)
   int nbig = 0, nsmall = 0;
@@ -71,7 +70,6 @@ struct TensorState {
 
 void destroy_tensor_state(TensorState* t) {
   if (!t) return;
-  if (t->meta_copied) (void)hipEventDestroy(t->meta_copied);
   delete t;
 }
 
@@ -309,16 +307,10 @@ int upload_tensor_meta(shampoo_ctx* h, const void* const* grads, void* const* pa
   for (int i = 0; same && i < n; ++i)
     same = m[i].grad == ts.meta_host[i].grad && m[i].param == ts.meta_host[i].param;
   if (same) return SHAMPOO_OK;
-  // the previous upload reads meta_host: let it finish before overwriting
-  if (ts.meta_copied) HIP_CHECK(hipEventSynchronize(ts.meta_copied));
+  // the table travels in kernel arguments: nothing to wait for
+  HIP_CHECK(shp::launch_upload(h->at<void>(ts.off_meta), m.data(), n * sizeof(shp::TensorMeta), s));
   ts.meta_host = m;
   ts.meta_valid = true;
-  if (n) {
-    HIP_CHECK(hipMemcpyAsync(h->at<void>(ts.off_meta), ts.meta_host.data(),
-                             n * sizeof(shp::TensorMeta), hipMemcpyHostToDevice, s));
-    if (!ts.meta_copied) HIP_CHECK(hipEventCreateWithFlags(&ts.meta_copied, hipEventDisableTiming));
-    HIP_CHECK(hipEventRecord(ts.meta_copied, s));
-  }
   return SHAMPOO_OK;
 }
 
@@ -615,14 +607,11 @@ int tensor_unpack(shampoo_ctx* h, void* const* dst, hipStream_t s) {
     m[i].param = dst[i];
     for (int dd = 0; dd < shp::kMaxOrder; ++dd) m[i].stride[dd] = dd < ts.k ? ts.descs[i].strides[dd] : 1;
   }
-  if (ts.n_tensors)
-    HIP_CHECK(hipMemcpyAsync(h->at<void>(ts.off_umeta), m.data(), m.size() * sizeof(shp::TensorMeta),
-                             hipMemcpyHostToDevice, s));
+  HIP_CHECK(shp::launch_upload(h->at<void>(ts.off_umeta), m.data(), m.size() * sizeof(shp::TensorMeta),
+                               s));
   HIP_CHECK(shp::launch_tensor_scatter(h->at<shp::TBlockMeta>(ts.off_blocks),
                                        h->at<shp::TensorMeta>(ts.off_umeta), geom(ts),
                                        (int32_t)ts.B, fptr(h, ts.off_gp), 0.f, 0, 0, s));
-  // the descriptor copy is from pageable host memory that dies here
-  HIP_CHECK(hipStreamSynchronize(s));
   return SHAMPOO_OK;
 }
 
@@ -725,11 +714,10 @@ int shampoo_tensor_init(const shampoo_config_t* cfg, int32_t order, const int32_
   hipError_t e = hipSuccess;
   const int64_t nf = (int64_t)order * ts->B;
   if (ts->B) {
-    e = hipMemcpyAsync(h->at<void>(ts->off_blocks), ts->blocks.data(),
-                       ts->B * sizeof(shp::TBlockMeta), hipMemcpyHostToDevice, s);
+    e = shp::launch_upload(h->at<void>(ts->off_blocks), ts->blocks.data(),
+                           ts->B * sizeof(shp::TBlockMeta), s);
     if (e == hipSuccess)
-      e = hipMemcpyAsync(h->at<void>(ts->off_nreal), nreal.data(), nreal.size() * 4,
-                         hipMemcpyHostToDevice, s);
+      e = shp::launch_upload(h->at<void>(ts->off_nreal), nreal.data(), nreal.size() * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(ts->off_status), 0, nf * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(ts->off_final), 0, nf * 4, s);
     if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(ts->off_scale), 0, nf * 4, s);
@@ -745,9 +733,6 @@ int shampoo_tensor_init(const shampoo_config_t* cfg, int32_t order, const int32_
     }
   }
   if (e == hipSuccess) e = hipMemsetAsync(h->at<void>(ts->off_flops), 0, 8, s);
-  // the host copies above are from pageable memory; make sure they are done
-  // before the temporaries go away
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     const int code = hip_fail(e, "shampoo_tensor_init");
     delete h;

@@ -33,8 +33,11 @@
  *    the library never allocates or frees device memory. "host" pointers are
  *    read during the call only.
  *  - hip_stream is a hipStream_t (NULL = the default stream). All device
- *    work is enqueued on it asynchronously; calls return before it runs,
- *    except the ones documented as synchronising.
+ *    work is enqueued on it asynchronously; calls return before it runs.
+ *    Only shampoo_get_status and shampoo_get_timing wait for the GPU. Host
+ *    tables (block map, pointer arrays) reach the device inside kernel
+ *    arguments, so no other call waits, also when the parameter or
+ *    gradient pointers change from one step to the next.
  *  - Matrices are row-major with a leading dimension ld (elements) >= cols.
  *  - A handle is not thread-safe; separate handles are independent.
  *  - Device faults surface as SHAMPOO_ERR_HIP at a later synchronising call.
@@ -244,8 +247,10 @@ int shampoo_workspace_size(const shampoo_config_t* cfg, const shampoo_matrix_des
 /* Create a handle. workspace: device buffer of at least workspace_size
  * bytes, 256-byte aligned, owned by the caller and kept alive and unmoved
  * until shampoo_destroy. Enqueues on hip_stream the upload of the block map
- * and the start state L = R = eps I; the step counter starts at 0 with no
- * roots. *out receives the handle. */
+ * and the start state L = R = eps I (page "Shampoo optimizer", matrix-case
+ * loop: both statistics start at eps times the identity before the first
+ * gradient); the step counter starts at 0 with no roots. *out receives the
+ * handle. Returns without waiting for the enqueued work. */
 int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats, int32_t n_mats,
                  void* workspace, size_t workspace_bytes, void* hip_stream, shampoo_t* out);
 
@@ -260,7 +265,15 @@ int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats,
 int shampoo_step(shampoo_t h, void* const* params, const void* const* grads, uint32_t flags,
                  void* hip_stream);
 
-/* Recompute the roots from the current L and R (coupled Newton). */
+/* Recompute the roots L^(-1/4) and R^(-1/4) of every block from the
+ * current L and R, as a step does on its refresh schedule (podcast
+ * "Preconditioned Optimization Without the Full Matrix Cost", cue 28: the
+ * roots are expensive and are recomputed only every few steps, reused in
+ * between). The solver is root_method: by default the norm-scaled coupled
+ * Newton iteration for the inverse 4th root (described at the top of this
+ * file), a chain of symmetric matrix products on the matrix cores; a factor
+ * whose iteration diverges gets status "diverged" and keeps finite roots
+ * (shampoo_get_status counts them). Later steps use the new roots. */
 int shampoo_refresh_roots(shampoo_t h, void* hip_stream);
 
 /* Release the handle (host memory only; the workspace stays the caller's).

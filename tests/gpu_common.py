@@ -62,6 +62,20 @@ def sample_blocks(w, k, seed=0):
     return sorted(ids)
 
 
+def spread_sample(w, k, seed=0, residues=8):
+    """sample_blocks(w, k, seed) widened so that it holds the first and the
+    last block and a block of every residue of the block id mod `residues`
+    (the symmetric products deal factor f to XCD f mod 8, and factor ids
+    are block ids for L and B + block id for R)."""
+    B = len(block_table(w.shapes, w.block_rows, w.block_cols))
+    ids = set(sample_blocks(w, k, seed)) | {0, B - 1}
+    rng = np.random.default_rng(seed + 1000)
+    for r in range(residues):
+        if not any(i % residues == r for i in ids):
+            ids.add(int(rng.choice(np.arange(r, B, residues))))
+    return sorted(ids)
+
+
 def block_of(t, b):
     """Host fp64 copy of block b (real extent) of a device matrix."""
     return t[b.r0:b.r0 + b.m, b.c0:b.c0 + b.n].float().cpu().numpy().astype(np.float64)
@@ -130,6 +144,23 @@ def run_parity(w, steps, ids=None, root_method="eigh", check_update=True, on_ste
             on_step(t, sh, orc, params, grads, U, Ugpu)
         log(f"  {w.name} t={t}: stats {se:.2e} update {ue:.2e}")
     return records, sh, orc, params, W
+
+
+def assert_params_match(w, params, W, tol=UPDATE_TOL):
+    """The fused parameter write of every tracked block: the GPU's cumulative
+    parameter change against the oracle's, relative Frobenius error <= tol
+    per block (the update bar applied to the sum of the steps)."""
+    table = block_table(w.shapes, w.block_rows, w.block_cols)
+    W0 = synth.GradientSource(w, device="cuda").init_params()
+    worst = 0.0
+    for i, Wo in W.items():
+        b = table[i]
+        w0 = block_of(W0[b.mat], b)
+        e = rel(block_of(params[b.mat], b) - w0, Wo - w0)
+        worst = max(worst, e)
+        assert e <= tol, (i, e)
+    log(f"  parameter change vs oracle, worst block: {worst:.2e}")
+    return worst
 
 
 def cond_of(A):

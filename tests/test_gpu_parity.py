@@ -10,9 +10,10 @@ import torch
 
 from blocked_shampoo_preconditioning_amd import synth
 from blocked_shampoo_preconditioning_amd import shampoo as S
-from oracle import block_table, pack_blocks, unpack_blocks
-from tests.gpu_common import (STATS_TOL, UPDATE_TOL, block_of, cond_of, log, make_shampoo, rel,
-                              run_parity, sample_blocks, workload)
+from oracle import ShampooOracle, block_table, pack_blocks, unpack_blocks
+from tests.gpu_common import (STATS_TOL, UPDATE_TOL, assert_params_match, block_of, cond_of, log,
+                              make_shampoo, rel,
+                              run_parity, sample_blocks, spread_sample, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +118,44 @@ def test_multi_tile_ragged_small():
     for r in recs:
         assert r.stats_err <= STATS_TOL, r
         assert r.update_err <= UPDATE_TOL, r
+    assert_params_match(w, params, W)  # the fused update on ragged tails
+    sh.close()
+
+
+def test_params_with_leading_dimension():
+    """Parameters and gradients stored with a leading dimension larger than
+    their width (ragged tails in both directions): the fused update writes
+    the real extent of every block, matches the oracle's parameter change,
+    and leaves the elements past the width and past the last row alone."""
+    shapes = ((300, 520), (130, 68), (96, 260))
+    lds = (532, 80, 264)
+    w = workload("gpt_small_b256", shapes=shapes, root_every=2, seed=57)
+    table = block_table(shapes, 256, 256)
+    src = synth.GradientSource(w, device="cuda")
+    W0 = src.init_params()
+    pbufs = [torch.full((r * ld + 8,), 5.0, device="cuda") for (r, c), ld in zip(shapes, lds)]
+    params = [b[:r * ld].view(r, ld)[:, :c] for b, (r, c), ld in zip(pbufs, shapes, lds)]
+    for p, p0 in zip(params, W0):
+        p.copy_(p0)
+    sh = S.Shampoo(shapes, 256, 256, beta2=w.beta2, eps=w.eps, lr=w.lr, root_every=w.root_every,
+                   newton_max_iters=w.newton_max_iters, newton_tol=w.newton_tol,
+                   newton_scale_mode=w.newton_scale_mode, lds=lds)
+    orc = ShampooOracle(shapes, 256, 256, w.beta2, w.eps, w.lr, w.root_every)
+    W = {b.id: block_of(W0[b.mat], b) for b in table}
+    for t in range(1, 5):
+        g = src.grads(t)
+        gbufs = [torch.full((r * ld + 8,), float("nan"), device="cuda") for (r, c), ld in zip(shapes, lds)]
+        grads = [b[:r * ld].view(r, ld)[:, :c] for b, (r, c), ld in zip(gbufs, shapes, lds)]
+        for gb, gs in zip(grads, g):
+            gb.copy_(gs)
+        S.shampoo_step(sh.handle, [b.data_ptr() for b in pbufs], [b.data_ptr() for b in gbufs], 0,
+                       sh._stream())
+        W, _ = orc.step_blocks({b.id: block_of(g[b.mat], b) for b in table}, W)
+    torch.cuda.synchronize()
+    assert_params_match(w, params, W)
+    for b, (r, c), ld in zip(pbufs, shapes, lds):
+        m = b[:r * ld].view(r, ld)
+        assert torch.all(m[:, c:] == 5.0) and torch.all(b[r * ld:] == 5.0)  # nothing else written
     sh.close()
 
 
@@ -132,9 +171,12 @@ def test_gpt_small_b256_sampled():
 
 def test_decoder_1b_f32_sampled():
     """The 1B-class decoder set at block 1024 (1152 blocks), 10 steps, a seeded
-    sample of blocks of every matrix shape compared at every step."""
+    sample of blocks of every matrix shape, the first and the last block and
+    a block of every residue mod 8, compared at every step."""
     w = workload("decoder_1b_b1024_f32")
-    ids = sample_blocks(w, 6, seed=2)
+    ids = spread_sample(w, 6, seed=2)
+    assert 0 in ids and 1151 in ids and {i % 8 for i in ids} == set(range(8))
+    log(f"  blocks {ids}")
     recs, sh, orc, params, W = run_parity(w, 10, ids=ids)
     for r in recs:
         assert r.stats_err <= STATS_TOL, r
@@ -331,6 +373,7 @@ def test_momentum_small_ragged_every_block():
     for b in table:
         assert rel(Mg[b.id, :b.m, :b.n].cpu().numpy(), orc.state[b.id].mom) <= 1e-6
         assert torch.count_nonzero(Mg[b.id, b.m:, :]) == 0 and torch.count_nonzero(Mg[b.id, :, b.n:]) == 0
+    assert_params_match(w, params, W)
     sh.close()
 
 
@@ -555,6 +598,7 @@ def test_fp32_gemm_paths_every_block(gemm, block, shapes):
             assert r.stats_err <= STATS_TOL, r
             assert r.update_err <= UPDATE_TOL, r
         assert sh.n_diverged() == 0
+        assert_params_match(w, params, W)  # the fused update of this product path
         sh.close()
 
 
