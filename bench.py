@@ -56,17 +56,47 @@ GEMM_HOW = {"split16": "fp32 operands scaled and split into two fp16 terms, thre
             "split": "fp32 operands split into three bf16 terms, six bf16 MFMA 32x32x16 products",
             "f32": "fp32 MFMA 32x32x2"}
 DEFAULT_WORKLOAD = "decoder_1b_b1024_f32"
+# the arithmetic the fp32 products execute, for the JSON line's dtype
+DTYPE_OF_PATH = {"split16": "f32 storage; products as fp16x2 split (3 fp16 MFMA, fp32 accumulate)",
+                 "split": "f32 storage; products as bf16x3 split (6 bf16 MFMA, fp32 accumulate)",
+                 "f32": "f32 (fp32 MFMA)"}
+
+
+def dtype_label(w):
+    d = DTYPE_OF_PATH[w.fp32_gemm]
+    if w.dtype == "bf16":
+        d += "; bf16 gradients and parameters, their statistics on the bf16 MFMA"
+    return d
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, grad_sets, budget_s=15.0, max_blocks=32, seed=0):
+def cpu_baseline(w, grad_sets, budget_s=15.0, max_blocks=32, seed=0, one_thread=False):
     """Time the oracle (as it stands) on a sample of blocks: one refresh step
     and one non-refresh step per block, extrapolated linearly to all blocks
-    over one root cycle (blocks are independent)."""
+    over one root cycle (blocks are independent). With one_thread, the same
+    timing again with the BLAS limited to one thread, reported beside it."""
     import numpy as np
+
+    single = None
+    if one_thread:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            single = cpu_baseline(w, grad_sets, budget_s / 2, max_blocks, seed)
 
     from oracle import ShampooOracle, block_table
     try:
@@ -113,6 +143,9 @@ def cpu_baseline(w, grad_sets, budget_s=15.0, max_blocks=32, seed=0):
                    f"linearly to all blocks over a {k}-step root cycle"),
         "blocks_per_s": steps_per_s * len(table),
         "cpu_seconds": t_ref + t_non,
+        "cpu_model": cpu_model(),
+        "one_thread": None if single is None else {
+            k: single[k] for k in ("value", "blocks_per_s", "cores", "sample")},
     }
 
 
@@ -161,6 +194,7 @@ def cpu_baseline_tensor(w, grad_sets, budget_s=15.0, max_blocks=16, seed=0):
                    f"linearly to all blocks over a {k}-step root cycle"),
         "blocks_per_s": steps_per_s * len(table),
         "cpu_seconds": t_ref + t_non,
+        "cpu_model": cpu_model(),
     }
 
 
@@ -269,7 +303,7 @@ def run_tensor(args, w, torch, S, synth):
         "ms_per_step": round(elapsed / args.steps * 1e3, 3),
         "ms_per_step_instrumented": round(elapsed_i / args.steps * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 gradients and parameters)",
+        "dtype": dtype_label(w),
         "data": "synthetic (seeded gradients with conv-filter shapes)",
         "config": {"workload": w.name, "tensors": len(w.shapes), "blocks": B,
                    "block": list(w.block_dims), "root_every": w.root_every,
@@ -280,6 +314,61 @@ def run_tensor(args, w, torch, S, synth):
     }
     sh.close()
     print(json.dumps(out), flush=True)
+
+
+def measure_matrix(args, w, torch, S, params, grad_sets):
+    """Warmup, the timed pass and the instrumented pass of one matrix
+    workload on a fresh handle; returns what the JSON line reports."""
+    n_sets = len(grad_sets)
+    sh = S.Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
+                   root_every=w.root_every, newton_max_iters=w.newton_max_iters,
+                   newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype,
+                   momentum=w.momentum, root_method=w.root_method, cheb_degree=w.cheb_degree,
+                   fp32_gemm=w.fp32_gemm)
+    B = sh.n_blocks
+    log(f"{B} blocks, workspace {sh.workspace.numel() / 2**30:.1f} GiB, products {w.fp32_gemm}")
+    for t in range(args.warmup):
+        sh.step(params, grad_sets[t % n_sets])
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    stream = torch.cuda.current_stream()
+    # the measured pass: no per-launch events
+    elapsed, wall = timed_steps(torch, sh, params, grad_sets, args.warmup, args.steps, stream)
+    # the instrumented pass over as many further steps (as many refreshes):
+    # per-class times, the Newton statistics and the roofline
+    sh.set_timing(True)
+    elapsed_i, _ = timed_steps(torch, sh, params, grad_sets, args.warmup + args.steps,
+                               args.steps, stream)
+    tm = sh.timing()
+    sh.set_timing(False)
+    n_div = sh.n_diverged()
+    st, it, _ = sh.newton_info()
+    iters = it.cpu().tolist()
+    status = st.cpu().tolist()
+    resid = sh.newton_residual().cpu()
+    B_ = len(iters) // 2
+    newton_stats = {
+        "status_counts": {name: status.count(code) for code, name in
+                          ((1, "converged"), (2, "stalled"), (3, "diverged"), (4, "capped"))},
+        "iters_left_mean": sum(iters[:B_]) / max(1, B_),
+        "iters_right_mean": sum(iters[B_:]) / max(1, B_),
+        "iters_min": min(iters) if iters else 0, "iters_max": max(iters) if iters else 0,
+        "residual_median": float(resid.median()) if len(resid) else 0.0,
+        "residual_max": float(resid.max()) if len(resid) else 0.0,
+        "n_diverged": n_div,
+    }
+    log(f"timed {args.steps} steps: {elapsed * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms); "
+        f"instrumented: {elapsed_i * 1e3:.1f} ms")
+    sh.close()
+    del sh
+    torch.cuda.empty_cache()
+    # statistics of bf16 gradients take the bf16 MFMA; the other products
+    # the configured fp32 path
+    paths = {"stats": "bf16" if w.dtype == "bf16" else w.fp32_gemm,
+             "newton_gemm": w.fp32_gemm, "apply": w.fp32_gemm}
+    return {"B": B, "elapsed": elapsed, "elapsed_i": elapsed_i, "tm": tm, "newton": newton_stats,
+            "kernels": class_table(tm, paths)}
 
 
 def newton_traffic(workload, gemm):
@@ -359,6 +448,8 @@ def main():
                     help="instead of the step, time the vendor library's batched GEMM "
                          "(torch.bmm on hipBLASLt) at the workload's block shape in fp16, bf16 "
                          "and fp32: the practical ceiling of a plain product on this chip")
+    ap.add_argument("--no-f32-pass", action="store_true",
+                    help="skip the second timed pass with every fp32 product on the fp32 MFMA")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one plain 1 GiB device copy (a known-size kernel that "
                          "calibrates the HBM traffic counters)")
@@ -408,52 +499,9 @@ def main():
         if t % 10 == 0 or t == n_sets:
             torch.cuda.synchronize()
             log(f"gradient sets generated: {t}/{n_sets}")
-    sh = S.Shampoo(w.shapes, w.block_rows, w.block_cols, beta2=w.beta2, eps=w.eps, lr=w.lr,
-                   root_every=w.root_every, newton_max_iters=w.newton_max_iters,
-                   newton_tol=w.newton_tol, newton_scale_mode=w.newton_scale_mode, dtype=w.dtype,
-                   momentum=w.momentum, root_method=w.root_method, cheb_degree=w.cheb_degree,
-                   fp32_gemm=w.fp32_gemm)
-    B = sh.n_blocks
-    log(f"{B} blocks, workspace {sh.workspace.numel() / 2**30:.1f} GiB")
-    for t in range(args.warmup):
-        sh.step(params, grad_sets[t % n_sets])
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
-
-    stream = torch.cuda.current_stream()
-    # the measured pass: no per-launch events
-    elapsed, wall = timed_steps(torch, sh, params, grad_sets, args.warmup, args.steps, stream)
-    # the instrumented pass over as many further steps (as many refreshes):
-    # per-class times, the Newton statistics and the roofline
-    sh.set_timing(True)
-    elapsed_i, _ = timed_steps(torch, sh, params, grad_sets, args.warmup + args.steps,
-                               args.steps, stream)
-    tm = sh.timing()
-    sh.set_timing(False)
-    n_div = sh.n_diverged()
-    st, it, _ = sh.newton_info()
-    iters = it.cpu().tolist()
-    status = st.cpu().tolist()
-    resid = sh.newton_residual().cpu()
-    B_ = len(iters) // 2
-    newton_stats = {
-        "status_counts": {name: status.count(code) for code, name in
-                          ((1, "converged"), (2, "stalled"), (3, "diverged"), (4, "capped"))},
-        "iters_left_mean": sum(iters[:B_]) / max(1, B_),
-        "iters_right_mean": sum(iters[B_:]) / max(1, B_),
-        "iters_min": min(iters) if iters else 0, "iters_max": max(iters) if iters else 0,
-        "residual_median": float(resid.median()) if len(resid) else 0.0,
-        "residual_max": float(resid.max()) if len(resid) else 0.0,
-    }
-    log(f"timed {args.steps} steps: {elapsed * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms); "
-        f"instrumented: {elapsed_i * 1e3:.1f} ms")
-
+    r = measure_matrix(args, w, torch, S, params, grad_sets)
+    B, elapsed, elapsed_i, tm, kernels = r["B"], r["elapsed"], r["elapsed_i"], r["tm"], r["kernels"]
     steps_per_s = args.steps / elapsed
-    # statistics of bf16 gradients take the bf16 MFMA; the other products
-    # the configured fp32 path
-    paths = {"stats": "bf16" if w.dtype == "bf16" else w.fp32_gemm,
-             "newton_gemm": w.fp32_gemm, "apply": w.fp32_gemm}
-    kernels = class_table(tm, paths)
     nw = tm["newton_gemm"]
     achieved = nw["flops"] / (nw["ms"] * 1e-3) / 1e12 if nw["ms"] > 0 else 0.0
     traffic = newton_traffic(w.name, w.fp32_gemm)
@@ -467,19 +515,37 @@ def main():
         "launches": nw["launches"],
         "flops_per_launch": nw["flops"] / max(1, nw["launches"]),
         "avg_launch_ms": nw["ms"] / max(1, nw["launches"]),
-        # the same fp32 flops against the fp32 MFMA, for comparison with the other path
-        "frac_of_fp32_mfma_peak": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+        # the same fp32 flops over the fp32 MFMA's peak: not a roofline fraction
+        # (the split products do not run on the fp32 MFMA), a comparison of rates
+        "fp32_equiv_vs_fp32_mfma_peak": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
     }
+    # the same workload with every fp32 product on the fp32 MFMA, timed the
+    # same way in the same run (its roofline is the fp32 MFMA's own peak)
+    f32_pass = None
+    if w.fp32_gemm != "f32" and not args.no_f32_pass:
+        wf = dataclasses.replace(w, fp32_gemm="f32")
+        rf = measure_matrix(args, wf, torch, S, params, grad_sets)
+        kf = rf["kernels"]
+        f32_pass = {
+            "value": round(args.steps / rf["elapsed"], 4), "unit": "steps/s",
+            "ms_per_step": round(rf["elapsed"] / args.steps * 1e3, 3),
+            "dtype": dtype_label(wf),
+            "gemm": {k: {"tflops": kf[k].get("tflops"), "frac_mfma": kf[k].get("frac_mfma"),
+                         "mfma_path": kf[k].get("mfma_path")}
+                     for k in ("stats", "newton_gemm", "apply") if k in kf},
+            "newton": {k: rf["newton"][k] for k in ("iters_left_mean", "iters_right_mean",
+                                                    "n_diverged")},
+        }
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
-        cpu = cpu_baseline(w, grad_sets)
+        cpu = cpu_baseline(w, grad_sets, one_thread=w.name in ("single_64x32", "gpt_small_b256"))
     out = {
         "metric": METRIC, "value": round(steps_per_s, 4), "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 3),
         "ms_per_step_instrumented": round(elapsed_i / args.steps * 1e3, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 gradients and parameters)",
+        "dtype": dtype_label(w),
         "data": "synthetic (seeded gradients with transformer-layer shapes)",
         "config": {"workload": w.name, "matrices": len(w.shapes), "blocks": B,
                    "block": [w.block_rows, w.block_cols], "root_every": w.root_every,
@@ -491,11 +557,11 @@ def main():
         "blocks_per_s": round(steps_per_s * B, 1),
         "gemm_tflops": {k: kernels[k].get("tflops") for k in ("stats", "newton_gemm", "apply")},
         "kernels": kernels,
-        "newton": dict(newton_stats, n_diverged=n_div),
+        "newton": r["newton"],
         "roofline": roofline,
+        "fp32_mfma_pass": f32_pass,
         "cpu_baseline": cpu,
     }
-    sh.close()
     if args.copy_probe:
         n = 1 << 28  # 1 GiB of fp32
         src_t = torch.ones(n, dtype=torch.float32, device=dev)

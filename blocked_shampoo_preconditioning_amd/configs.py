@@ -1,4 +1,5 @@
-"""The five synthetic workloads the step is tested and measured on.
+"""The synthetic workloads the step is tested and measured on (five, plus one
+GPU's eighth share of the 1B-class set).
 
 Each workload is a set of weight matrices with transformer-layer shapes, a
 block shape, the optimizer's hyper-parameters and the distribution of the
@@ -71,6 +72,11 @@ WORKLOADS = {
         name="decoder_1b_b1024_f32", shapes=_layers(DECODER_1B_LAYER, 24), block_rows=1024,
         block_cols=1024, root_every=10, steps=50, grad="col_scaled", grad_std=1e-2,
         seed=1004, notes="24 1B-class decoder layers, 1152 blocks of 1024x1024, fp32"),
+    "decoder_1b_b1024_f32_shard8": Workload(
+        name="decoder_1b_b1024_f32_shard8", shapes=_layers(DECODER_1B_LAYER, 3), block_rows=1024,
+        block_cols=1024, root_every=10, steps=50, grad="col_scaled", grad_std=1e-2,
+        seed=1004, notes="one GPU's share of the 1B-class set split 8 ways by blocks: 3 of its "
+                         "24 layers, 144 blocks of 1024x1024, fp32"),
     "decoder_1b_b1024_bf16": Workload(
         name="decoder_1b_b1024_bf16", shapes=_layers(DECODER_1B_LAYER, 24), block_rows=1024,
         block_cols=1024, root_every=10, steps=50, dtype="bf16", grad="col_scaled",
