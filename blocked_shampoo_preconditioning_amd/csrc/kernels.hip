@@ -544,19 +544,22 @@ __device__ __forceinline__ void split_mma(floatx16 (&acc)[C::FM][C::FN], const u
 // phase earlier) is split into the other buffer and tile kt + 2 is loaded
 // into the freed stage, so every load has a full phase to land. F16: two
 // fp16 planes of A 2^ea and B 2^eb and three products instead (the caller
-// scales the sums back by 2^-(ea + eb)).
-template <class C, bool PCOLS, bool QCOLS, int MASK = -1, bool F16 = false>
+// scales the sums back by 2^-(ea + eb)). SAME: B is A (same rows, same
+// scale: a diagonal tile of a matrix times itself), so its rows are loaded,
+// split and stored once and read as both operands.
+template <class C, bool PCOLS, bool QCOLS, int MASK = -1, bool F16 = false, bool SAME = false>
 __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda,
                                             const float* __restrict__ B, int ldb, int K, int m0,
                                             int n0, int wm, int wn,
                                             floatx16 (&acc)[C::FM][C::FN], float* lds,
                                             int ea = 0, int eb = 0) {
+  static_assert(!SAME || (C::BM == C::BN && PCOLS == QCOLS), "a shared panel is square");
   constexpr int NPL = F16 ? 2 : 3;                          // planes per operand
   constexpr int PA = C::BM * C::LDX, PB = C::BN * C::LDX;  // one plane, in 16-bit words
   uint16_t* sA0 = reinterpret_cast<uint16_t*>(lds);  // [2][NPL][BM][LDX]
   uint16_t* sA1 = sA0 + NPL * PA;
-  uint16_t* sB0 = sA0 + 2 * NPL * PA;                 // [2][NPL][BN][LDX]
-  uint16_t* sB1 = sB0 + NPL * PB;
+  uint16_t* sB0 = SAME ? sA0 : sA0 + 2 * NPL * PA;    // [2][NPL][BN][LDX]
+  uint16_t* sB1 = SAME ? sA1 : sB0 + NPL * PB;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -567,30 +570,30 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
   SplitOperand<C, C::BM, PCOLS> a0, a1;
   SplitOperand<C, C::BN, QCOLS> b0, b1;
   split_load<C, C::BM, PCOLS>(a0, A, lda, m0, 0);
-  split_load<C, C::BN, QCOLS>(b0, B, ldb, n0, 0);
+  if constexpr (!SAME) split_load<C, C::BN, QCOLS>(b0, B, ldb, n0, 0);
   split_load<C, C::BM, PCOLS>(a1, A, lda, m0, 16);
-  split_load<C, C::BN, QCOLS>(b1, B, ldb, n0, 16);
+  if constexpr (!SAME) split_load<C, C::BN, QCOLS>(b1, B, ldb, n0, 16);
   split_store<C, C::BM, PCOLS, F16>(a0, sA0, ea);
-  split_store<C, C::BN, QCOLS, F16>(b0, sB0, eb);
+  if constexpr (!SAME) split_store<C, C::BN, QCOLS, F16>(b0, sB0, eb);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
     // tile kt from buffer 0; tile kt + 1 (stage 1) into buffer 1; tile kt + 2
     // into stage 0 (the last pair repeats tile nk - 1, in bounds and unused)
     const int k2 = min(kt + 2, nk - 1) * 16, k3 = min(kt + 3, nk - 1) * 16;
     split_load<C, C::BM, PCOLS>(a0, A, lda, m0, k2);
-    split_load<C, C::BN, QCOLS>(b0, B, ldb, n0, k2);
+    if constexpr (!SAME) split_load<C, C::BN, QCOLS>(b0, B, ldb, n0, k2);
     split_mma<C, MASK, F16>(acc, sA0, sB0, wm, wn);
     split_store<C, C::BM, PCOLS, F16>(a1, sA1, ea);
-    split_store<C, C::BN, QCOLS, F16>(b1, sB1, eb);
+    if constexpr (!SAME) split_store<C, C::BN, QCOLS, F16>(b1, sB1, eb);
     __syncthreads();
     // tile kt + 1 from buffer 1; tile kt + 2 (stage 0) into buffer 0; tile
     // kt + 3 into stage 1
     split_load<C, C::BM, PCOLS>(a1, A, lda, m0, k3);
-    split_load<C, C::BN, QCOLS>(b1, B, ldb, n0, k3);
+    if constexpr (!SAME) split_load<C, C::BN, QCOLS>(b1, B, ldb, n0, k3);
     split_mma<C, MASK, F16>(acc, sA1, sB1, wm, wn);
     if (kt + 2 < nk) {
       split_store<C, C::BM, PCOLS, F16>(a0, sA0, ea);
-      split_store<C, C::BN, QCOLS, F16>(b0, sB0, eb);
+      if constexpr (!SAME) split_store<C, C::BN, QCOLS, F16>(b0, sB0, eb);
     }
     __syncthreads();
   }
@@ -635,11 +638,10 @@ constexpr int half_mask(bool bottom) {
 // takes 3 fragment times instead of 4 with 2 x 2 fragments per wave. The
 // choice is per wave (the wave index is uniform; readfirstlane tells the
 // compiler so) and made outside the K loop.
-template <class C>
+template <class C, bool SQUARE = (C::FM == C::FN && C::WM == C::WN)>
 struct SymWave {
   int wm, wn, mask;
   __device__ __forceinline__ SymWave(bool diag) {
-    static_assert(C::FM == C::FN && C::WM == C::WN, "symmetric tiles are square");
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     wm = wave % C::WM;
     wn = wave / C::WM;
@@ -657,6 +659,40 @@ struct SymWave {
       mask = below ? half_mask<C::FM, C::FN>(true) : half_mask<C::FM, C::FN>(false);
     } else if (wm > wn) {
       mask = 0;
+    }
+  }
+};
+
+// 256 x 256 tiles of eight waves of 128 x 64 (2 x 4 waves, 4 x 2 fragments
+// each). On a diagonal tile, of the 8 x 8 fragments the upper triangle (36)
+// is needed: the waves crossing the diagonal keep their fragments on or above
+// it (3 or 7), the two waves below it each take the bottom half of a full
+// block above it, whose own wave keeps the top half (4 and 4). With wave w on
+// SIMD w % 4 the busiest SIMD then runs 11 fragment products where a full
+// tile runs 16.
+template <class C>
+struct SymWave<C, false> {
+  static_assert(C::WM == 2 && C::WN == 4 && C::FM == 4 && C::FN == 2, "the 256-tile layout");
+  static constexpr int kCross0 = 0x0B;   // rows 0-3 x cols 0-1 on or above the diagonal
+  static constexpr int kCross1 = 0xBF;   // rows 0-3 x cols 2-3 on or above the diagonal
+  static constexpr int kTop = 0x0F, kBottom = 0xF0;
+  int wm, wn, mask;
+  __device__ __forceinline__ SymWave(bool diag) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wm = wave % C::WM;
+    wn = wave / C::WM;
+    mask = -1;
+    if (!diag) return;
+    if (wm == 0 && wn < 2) {
+      mask = wn == 0 ? kCross0 : kCross1;
+    } else if (wm == 1 && wn >= 2) {
+      mask = wn == 2 ? kCross0 : kCross1;
+    } else if (wm == 1) {  // below the diagonal: the bottom half of block (0, wn + 2)
+      wm = 0;
+      wn += 2;
+      mask = kBottom;
+    } else {
+      mask = kTop;
     }
   }
 };
@@ -707,6 +743,32 @@ __device__ __forceinline__ void mainloop_sym_x6(const float* __restrict__ A,
                                                 int n0, floatx16 (&acc)[C::FM][C::FN],
                                                 float* lds, const SymWave<C>& sw, int ea = 0,
                                                 int eb = 0) {
+  if constexpr (C::FM != C::FN) {
+    using W = SymWave<C>;
+    const int ld = COLS ? M : K;
+    // a diagonal tile of a matrix times itself: one panel serves both operands
+    const bool same = A == B && ea == eb;
+    if (sw.mask == -1)
+      mainloop_x6<C, COLS, COLS, -1, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
+    else if (same) {
+      if (sw.mask == W::kCross0)
+        mainloop_x6<C, COLS, COLS, W::kCross0, F16, true>(A, ld, A, ld, K, m0, m0, sw.wm, sw.wn, acc, lds, ea, ea);
+      else if (sw.mask == W::kCross1)
+        mainloop_x6<C, COLS, COLS, W::kCross1, F16, true>(A, ld, A, ld, K, m0, m0, sw.wm, sw.wn, acc, lds, ea, ea);
+      else if (sw.mask == W::kTop)
+        mainloop_x6<C, COLS, COLS, W::kTop, F16, true>(A, ld, A, ld, K, m0, m0, sw.wm, sw.wn, acc, lds, ea, ea);
+      else
+        mainloop_x6<C, COLS, COLS, W::kBottom, F16, true>(A, ld, A, ld, K, m0, m0, sw.wm, sw.wn, acc, lds, ea, ea);
+    } else if (sw.mask == W::kCross0)
+      mainloop_x6<C, COLS, COLS, W::kCross0, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
+    else if (sw.mask == W::kCross1)
+      mainloop_x6<C, COLS, COLS, W::kCross1, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
+    else if (sw.mask == W::kTop)
+      mainloop_x6<C, COLS, COLS, W::kTop, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
+    else
+      mainloop_x6<C, COLS, COLS, W::kBottom, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
+    return;
+  } else {
   constexpr int kUpper = upper_mask<C::FM, C::FN>();
   constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
   const int ld = COLS ? M : K;
@@ -720,6 +782,7 @@ __device__ __forceinline__ void mainloop_sym_x6(const float* __restrict__ A,
     mainloop_x6<C, COLS, COLS, kBottom, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
   else
     mainloop_x6<C, COLS, COLS, 0, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
+  }
 }
 
 // Row / column of accumulator register r of fragment (i, j) of the wave's
@@ -2091,6 +2154,18 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
     }                                                                                          \
     break;                                                                                     \
   }
+    case 256: {
+      // 256-tiles: fp16 split only
+      if (mode != kGemmSplitF16) return hipErrorInvalidValue;
+      const int gx = grid_sym<Cfg256>(g);
+      if (!gx) break;
+      if (cols)
+        hipLaunchKernelGGL((syrk_ema_kernel<Cfg256, kPathSplitHCols>), dim3(gx, g.n_problems),
+                           dim3(Cfg256::NT), 0, s, g);
+      else
+        SHP_SYM_LAUNCH(Cfg256, kPathSplitH)
+      break;
+    }
     SHP_SYM_CASE(128, Cfg128)
     SHP_SYM_CASE(64, Cfg64)
     SHP_SYM_CASE(32, Cfg32)

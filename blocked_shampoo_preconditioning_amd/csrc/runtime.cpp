@@ -104,8 +104,12 @@ Plan make_plan(const shampoo_config_t* c, const shampoo_matrix_desc_t* m, int32_
   for (int i = 0; i < n; ++i)
     p.B += ((m[i].rows + p.br - 1) / p.br) * ((m[i].cols + p.bc - 1) / p.bc);
   p.tile = pick_tile(p.br, p.bc);
-  p.ntiles_l = shp::sym_tiles(p.br, p.tile);
-  p.ntiles_r = shp::sym_tiles(p.bc, p.tile);
+  // (a 256-wide block would be one diagonal tile: 128-tiles balance it better)
+  p.sym_tile = c->fp32_gemm == SHAMPOO_GEMM_SPLIT_F16 && p.br % 256 == 0 && p.bc % 256 == 0 &&
+                       p.br >= 512 && p.bc >= 512
+                   ? 256 : p.tile;
+  p.ntiles_l = shp::sym_tiles(p.br, p.sym_tile);
+  p.ntiles_r = shp::sym_tiles(p.bc, p.sym_tile);
   p.resid_stride = std::max(p.ntiles_l, p.ntiles_r);
   p.fl = p.B * p.br * p.br;
   p.fr = p.B * p.bc * p.bc;
@@ -353,7 +357,7 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
                                       4.0 * (2.0 * (double)p.br * p.br + 2.0 * (double)p.bc * p.bc));
   return timed(h, kStats, flops, bytes, s, [&] {
     return hb ? shp::launch_gemm_sym_bf16(g, p.tile, s)
-              : shp::launch_gemm_sym(g, p.tile, false, h->cfg.fp32_gemm, s);
+              : shp::launch_gemm_sym(g, p.sym_tile, false, h->cfg.fp32_gemm, s);
   });
 }
 
@@ -373,7 +377,7 @@ int do_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
   j.xalt = m_xalt(h);
   for (int i = 0; i < 3; ++i) j.s[i] = m_s(h, i);
   j.s[3] = p.off_s3 >= 0 ? h->at<float>(p.off_s3) : nullptr;
-  j.tile[0] = j.tile[1] = p.tile;
+  j.tile[0] = j.tile[1] = p.sym_tile;
   j.gemm_mode = h->cfg.fp32_gemm;
   for (int i = 0; i < 6; ++i) j.mx[i] = m_mx(h, i);
   for (const auto& b : h->blocks)

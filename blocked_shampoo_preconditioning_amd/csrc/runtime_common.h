@@ -47,6 +47,9 @@ struct Carver {
 struct Plan {
   int64_t B = 0;
   int br = 0, bc = 0, n_mats = 0, tile = 32, max_iters = 1;
+  // tile of the symmetric products (statistics of fp32 gradients, roots):
+  // 256 on the fp16 split when both block sides allow it, else `tile`
+  int sym_tile = 32;
   int ntiles_l = 0, ntiles_r = 0, resid_stride = 0;
   int64_t fl = 0, fr = 0;  // elements of all left / right factors
   int64_t off_blocks, off_mats, off_umats, off_nreal, off_status, off_final, off_scale, off_rprev,
