@@ -304,6 +304,16 @@ hipError_t launch_rebase_words(uint64_t* w, int64_t n, uint64_t ver, hipStream_t
 // waits for a copy from pageable memory.
 hipError_t launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t s);
 
+// Library-held scratch for callers that cannot allocate: a static device
+// array of kScratchBytes per GPU, alive until the process ends. Its device
+// address on the current device (hipGetSymbolAddress, fetched once per
+// device; host code must use this address, never the array's name). Every
+// call that uses it on one GPU shares it: calls that overlap there race.
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+hipError_t scratch_address(void** ptr);
+// w[0 .. n) = 0 by a kernel (no memset node, so it can be captured).
+hipError_t launch_zero_words(uint64_t* w, int64_t n, hipStream_t s);
+
 // Tiles written by a symmetric product of side n with square tile t.
 inline int32_t sym_tiles(int32_t n, int32_t t) {
   int32_t T = n / t;

@@ -23,6 +23,7 @@
 
 #include <math.h>
 #include <cstring>
+#include <mutex>
 
 #include <type_traits>
 
@@ -2331,6 +2332,29 @@ __global__ __launch_bounds__(kUploadWords) void upload_kernel(uint64_t* __restri
   if (i < n) dst[i] = c.w[i];
 }
 
+// The scratch of the entry points that allocate nothing (file scope, one
+// copy per GPU).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+
+hipError_t scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t s) {
   const int64_t words = (bytes + 7) / 8;
   for (int64_t o = 0; o < words; o += kUploadWords) {
@@ -2343,6 +2367,19 @@ hipError_t launch_upload(void* dst, const void* src, int64_t bytes, hipStream_t 
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint64_t* __restrict__ w, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    w[i] = 0;
+}
+
+hipError_t launch_zero_words(uint64_t* w, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, s, w, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_rebase_words(uint64_t* w, int64_t n, uint64_t ver, hipStream_t s) {

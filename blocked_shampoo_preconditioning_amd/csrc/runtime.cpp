@@ -389,9 +389,14 @@ int do_refresh(shampoo_ctx* h, hipStream_t s, int64_t t_stats) {
   return SHAMPOO_OK;
 }
 
-int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
+// tmp / tmp_words: where the intermediate X_L G (or its transpose on the
+// fp32 MFMA path) and its per-block maximum words go; NULL: the workspace's
+int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed, float* tmp = nullptr,
+             uint64_t* tmp_words = nullptr) {
   const Plan& p = h->plan;
   if (p.B == 0) return SHAMPOO_OK;
+  if (tmp == nullptr) tmp = m_tmpT(h);
+  if (tmp_words == nullptr && m_f16(h)) tmp_words = m_mx(h, 8);
   // the preconditioned matrix: the packed gradient, or the momentum buffer
   const float* G = p.momentum ? m_mom(h) : m_gp(h);
   const bool split = h->cfg.fp32_gemm != SHAMPOO_GEMM_F32;
@@ -417,7 +422,7 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
     a.M = p.bc;
     a.N = p.br;
   }
-  a.C = m_tmpT(h);
+  a.C = tmp;
   a.sC = (int64_t)p.bc * p.br;
   a.K = p.br;
   a.batch = (int)p.B;
@@ -425,7 +430,7 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   if (m_f16(h)) {  // maxima: left roots, the preconditioned blocks; raises Tmp's
     a.mP = m_mx(h, 0);
     a.mQ = m_mx(h, p.momentum ? 7 : 6);
-    a.mC = m_mx(h, 8);
+    a.mC = tmp_words;
     a.ver = h->next_ver();
   }
   g1.p[0] = a;
@@ -434,7 +439,7 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   // split: U[m][n] = sum_k Tmp[m][k] X_R[n][k] (X_R symmetric)
   shp::GemmLaunch g2{};
   shp::GemmProblem b{};
-  b.P = m_tmpT(h);
+  b.P = tmp;
   b.sP = (int64_t)p.bc * p.br;
   b.Q = m_xroot(h) + p.fl;
   b.sQ = (int64_t)p.bc * p.bc;
@@ -445,7 +450,7 @@ int do_apply(shampoo_ctx* h, hipStream_t s, float* out_packed) {
   b.batch = (int)p.B;
   b.alpha = 1.f;
   if (m_f16(h)) {  // maxima: Tmp, right roots
-    b.mP = m_mx(h, 8);
+    b.mP = tmp_words;
     b.mQ = m_mx(h, 0) + p.B;
   }
   g2.p[0] = b;
@@ -583,6 +588,10 @@ int shampoo_init(const shampoo_config_t* cfg, const shampoo_matrix_desc_t* mats,
     if (e == hipSuccess)
       e = shp::launch_init_state(m_lr(h), plan.fl, plan.br, plan.fr, plan.bc, (int32_t)plan.B,
                                  (float)cfg->eps, s);
+    // the address of the library's scratch on this device (set-up of
+    // shampoo_precondition_noalloc; fetched once per device)
+    void* scratch = nullptr;
+    if (e == hipSuccess) e = shp::scratch_address(&scratch);
   }
   if (e != hipSuccess) return cleanup(hip_fail(e, "shampoo_init"));
   *out = h;
@@ -726,6 +735,37 @@ int shampoo_precondition(shampoo_t h, void* out, void* hip_stream) {
   if (h->tensor)
     return tensor_precondition(h, static_cast<float*>(out), static_cast<hipStream_t>(hip_stream));
   return do_apply(h, static_cast<hipStream_t>(hip_stream), static_cast<float*>(out));
+}
+
+int shampoo_precondition_noalloc(shampoo_t h, void* out, void* hip_stream) {
+  if (!h) return fail(SHAMPOO_ERR_INVALID_ARG, "handle is NULL");
+  if (h->tensor)
+    return fail(SHAMPOO_ERR_UNSUPPORTED, "shampoo_precondition_noalloc takes matrix handles only");
+  const Plan& p = h->plan;
+  if (!out && p.B) return fail(SHAMPOO_ERR_INVALID_ARG, "out is NULL");
+  if (reinterpret_cast<uintptr_t>(out) % 16) return fail(SHAMPOO_ERR_MISALIGNED, "out not 16-byte aligned");
+  if (!h->roots_valid) return fail(SHAMPOO_ERR_NO_ROOTS, "no roots yet");
+  // the intermediate, then its maximum words (fp16 split), in the library's scratch
+  const int64_t tmp_bytes = (p.B * (int64_t)p.br * p.bc * 4 + 255) / 256 * 256;
+  const int64_t need = tmp_bytes + (m_f16(h) ? 8 * p.B : 0);
+  if (need > shp::kScratchBytes)
+    return fail(SHAMPOO_ERR_UNSUPPORTED,
+                "shampoo_precondition_noalloc: the intermediate needs " + std::to_string(need) +
+                    " bytes of scratch, more than the " + std::to_string(shp::kScratchBytes) +
+                    " the library holds per GPU (use shampoo_precondition)");
+  if (p.B == 0) return SHAMPOO_OK;
+  void* base = nullptr;
+  HIP_CHECK(shp::scratch_address(&base));
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  float* tmp = static_cast<float*>(base);
+  uint64_t* words = nullptr;
+  if (m_f16(h)) {
+    // words left by an earlier call (of any handle) carry other versions:
+    // clear them so this call's writes define them
+    words = reinterpret_cast<uint64_t*>(static_cast<char*>(base) + tmp_bytes);
+    HIP_CHECK(shp::launch_zero_words(words, p.B, s));
+  }
+  return do_apply(h, s, static_cast<float*>(out), tmp, words);
 }
 
 int shampoo_get_status(shampoo_t h, void* hip_stream, int32_t* n_diverged_out) {

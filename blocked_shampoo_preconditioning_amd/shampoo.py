@@ -102,6 +102,7 @@ _SIGNATURES = {
     "shampoo_pack": [_P, _PP, _P],
     "shampoo_unpack": [_P, _PP, _P],
     "shampoo_precondition": [_P, _P, _P],
+    "shampoo_precondition_noalloc": [_P, _P, _P],
     "shampoo_get_status": [_P, _P, ctypes.POINTER(ctypes.c_int32)],
     "shampoo_set_timing": [_P, ctypes.c_int32, _P],
     "shampoo_get_timing": [_P, ctypes.POINTER(Timing)],
@@ -239,6 +240,11 @@ def shampoo_precondition(h, out_ptr, stream):
     _check(load_library().shampoo_precondition(h, ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)))
 
 
+def shampoo_precondition_noalloc(h, out_ptr, stream):
+    _check(load_library().shampoo_precondition_noalloc(h, ctypes.c_void_p(out_ptr),
+                                                       ctypes.c_void_p(stream)))
+
+
 def shampoo_get_status(h, stream):
     n = ctypes.c_int32()
     _check(load_library().shampoo_get_status(h, ctypes.c_void_p(stream), ctypes.byref(n)))
@@ -374,6 +380,9 @@ class Shampoo:
 
     def precondition(self, out):
         shampoo_precondition(self.handle, out.data_ptr(), self._stream())
+
+    def precondition_noalloc(self, out):
+        shampoo_precondition_noalloc(self.handle, out.data_ptr(), self._stream())
 
     def n_diverged(self):
         return shampoo_get_status(self.handle, self._stream())

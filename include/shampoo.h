@@ -311,6 +311,20 @@ int shampoo_unpack(shampoo_t h, void* const* dst, void* hip_stream);
  * touched. */
 int shampoo_precondition(shampoo_t h, void* out, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * result as shampoo_precondition, bit for bit, with the intermediate X_L Gp
+ * (and its per-block maximum words on the fp16 split) kept in scratch memory
+ * the library holds instead of in the workspace: a static device array of 64
+ * MiB per GPU, alive until the process ends. Matrix handles only
+ * (SHAMPOO_ERR_UNSUPPORTED for a tensor handle, and for a handle whose
+ * intermediate, 4 * n_blocks * block_rows * block_cols bytes rounded up to
+ * 256 plus 8 * n_blocks, exceeds 64 MiB). Calls no hipMalloc or other
+ * allocating routine. Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (other streams, other threads) race; calls
+ * on one stream are ordered. */
+int shampoo_precondition_noalloc(shampoo_t h, void* out, void* hip_stream);
+
 /* Number of factors whose last Newton run diverged (non-finite or growing
  * residual). Synchronises hip_stream. */
 int shampoo_get_status(shampoo_t h, void* hip_stream, int32_t* n_diverged_out);
