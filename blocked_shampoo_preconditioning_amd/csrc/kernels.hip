@@ -721,6 +721,20 @@ template <class C>
 __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X, int K, int m0,
                                                   int n0, floatx16 (&acc)[C::FM][C::FN],
                                                   float* lds, const SymWave<C>& sw) {
+  if constexpr (C::FM != C::FN) {
+    using W = SymWave<C>;
+    if (sw.mask == -1)
+      mainloop_bf16<C>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    else if (sw.mask == W::kCross0)
+      mainloop_bf16<C, W::kCross0>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    else if (sw.mask == W::kCross1)
+      mainloop_bf16<C, W::kCross1>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    else if (sw.mask == W::kTop)
+      mainloop_bf16<C, W::kTop>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    else
+      mainloop_bf16<C, W::kBottom>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+    return;
+  } else {
   constexpr int kUpper = upper_mask<C::FM, C::FN>();
   constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
   if (sw.mask == -1)
@@ -733,6 +747,7 @@ __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X
     mainloop_bf16<C, kBottom>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
   else
     mainloop_bf16<C, 0>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  }
 }
 
 // COLS: both operands stored [K][M] (m contiguous, row stride M), as the
@@ -1010,7 +1025,7 @@ __global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void syrk_ema_kern
 // Statistics from bf16 packed gradients: L <- beta2 L + g Gp Gp^T reads GpH
 // (rows of Gp), R <- beta2 R + g Gp^T Gp reads GpTH (rows of Gp^T).
 template <class C>
-__global__ __launch_bounds__(C::NT, 3) void syrk_bf16_kernel(GemmLaunch g) {
+__global__ __launch_bounds__(C::NT, C::NT == 512 ? 2 : 3) void syrk_bf16_kernel(GemmLaunch g) {
   sym_product<C, kPathBF16>(g);
 }
 
@@ -2188,6 +2203,7 @@ hipError_t launch_gemm_sym_bf16(const GemmLaunch& g, int tile, hipStream_t s) {
       hipLaunchKernelGGL(syrk_bf16_kernel<CFG>, dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g);  \
     break;                                                                                       \
   }
+    SHP_SYMH_CASE(256, Cfg256)
     SHP_SYMH_CASE(128, Cfg128)
     SHP_SYMH_CASE(64, Cfg64)
     SHP_SYMH_CASE(32, Cfg32)

@@ -108,6 +108,7 @@ Plan make_plan(const shampoo_config_t* c, const shampoo_matrix_desc_t* m, int32_
   p.sym_tile = c->fp32_gemm == SHAMPOO_GEMM_SPLIT_F16 && p.br % 256 == 0 && p.bc % 256 == 0 &&
                        p.br >= 512 && p.bc >= 512
                    ? 256 : p.tile;
+  p.bf16_tile = p.br % 256 == 0 && p.bc % 256 == 0 && p.br >= 512 && p.bc >= 512 ? 256 : p.tile;
   p.ntiles_l = shp::sym_tiles(p.br, p.sym_tile);
   p.ntiles_r = shp::sym_tiles(p.bc, p.sym_tile);
   p.resid_stride = std::max(p.ntiles_l, p.ntiles_r);
@@ -356,7 +357,7 @@ int do_stats(shampoo_ctx* h, hipStream_t s) {
   const double bytes = (double)p.B * ((hb ? 2.0 : 4.0) * 2.0 * p.br * p.bc +
                                       4.0 * (2.0 * (double)p.br * p.br + 2.0 * (double)p.bc * p.bc));
   return timed(h, kStats, flops, bytes, s, [&] {
-    return hb ? shp::launch_gemm_sym_bf16(g, p.tile, s)
+    return hb ? shp::launch_gemm_sym_bf16(g, p.bf16_tile, s)
               : shp::launch_gemm_sym(g, p.sym_tile, false, h->cfg.fp32_gemm, s);
   });
 }

@@ -50,6 +50,9 @@ struct Plan {
   // tile of the symmetric products (statistics of fp32 gradients, roots):
   // 256 on the fp16 split when both block sides allow it, else `tile`
   int sym_tile = 32;
+  // tile of the statistics of bf16 gradients (bf16 MFMA): 256 when both block
+  // sides are multiples of 256 of at least 512, else `tile`
+  int bf16_tile = 32;
   int ntiles_l = 0, ntiles_r = 0, resid_stride = 0;
   int64_t fl = 0, fr = 0;  // elements of all left / right factors
   int64_t off_blocks, off_mats, off_umats, off_nreal, off_status, off_final, off_scale, off_rprev,
