@@ -294,6 +294,14 @@ hipError_t launch_cheb_combine(const float* Ahat, const float* T2, float* out, F
 // mo: maxima of Ybuf0 (a) and Z0buf (b) per factor.
 hipError_t launch_db_stage2_init(float* Ybuf0, const float* Ybuf1, float* Z0buf, FactorSet fs,
                                  NewtonCtl c, hipStream_t s, MaxOut mo = MaxOut{});
+// Coupled Newton for factor sets whose sides are all <= kSmallSide: every
+// iteration in one launch (one workgroup per factor, iterates in LDS, fp32
+// FMA products), from M0 and X1 of launch_newton_init to the kept root in
+// Xroot, with the status, iteration, residual and scaling records of the
+// per-iteration kernels and the roots' maximum words (mo.a).
+constexpr int kSmallSide = 64;
+hipError_t launch_newton_small(const float* M0, const float* X1, float* Xroot, FactorSet fs,
+                               NewtonCtl c, hipStream_t s, MaxOut mo = MaxOut{});
 // Maximum words w[0 .. n) keep their exponents and take version ver (after a
 // restore wrote words of another handle's versions).
 hipError_t launch_rebase_words(uint64_t* w, int64_t n, uint64_t ver, hipStream_t s);

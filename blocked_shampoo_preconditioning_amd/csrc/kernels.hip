@@ -1904,6 +1904,229 @@ __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ X
   if (mo.a != nullptr) raise_max(mo.a + f, mx, mo.ver);
 }
 
+// ---------------------------------------------------------------------------
+// Coupled Newton for factors of side <= 64 in one launch: one workgroup per
+// factor runs every iteration with its iterates in LDS, the products as fp32
+// FMAs (exact fp32 products, fp32 sums; no operand split). Small blocks would
+// otherwise spend their step launching the per-iteration kernels, most of
+// them with nothing left to do. The iteration, its scaling (mode 3), stop
+// rules, final-step X-only iteration and records are those of the
+// newton_sym / newton_check / newton_final chain; it starts from M_0 and X_1
+// of newton_init and writes the kept iterate to Xroot (with its maximum word).
+// ---------------------------------------------------------------------------
+// C = alpha P Q + beta D + gamma I for n x n matrices in LDS (row stride n, n
+// a multiple of 32; P symmetric, read by rows). The 4 x 4 blocks on and above
+// the diagonal are computed and mirrored, so C is exactly symmetric. Returns
+// this thread's share of ||C - I||_F^2 when want_resid.
+__device__ __forceinline__ float small_product(float* __restrict__ C, const float* __restrict__ P,
+                                               const float* __restrict__ Q,
+                                               const float* __restrict__ D, float alpha,
+                                               float beta, float gamma, int n, bool want_resid) {
+  const int nb = n / 4;
+  float rs = 0.f;
+  for (int t = threadIdx.x; t < nb * nb; t += blockDim.x) {
+    const int bi = t / nb, bj = t - bi * nb;
+    if (bi > bj) continue;
+    const int r0 = 4 * bi, c0 = 4 * bj;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int k = 0; k < n; ++k) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(P + k * n + r0);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(Q + k * n + c0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = r0 + i, col = c0 + j;
+        if (row > col) continue;
+        float x = alpha * acc[i][j];
+        if (D != nullptr) x += beta * D[row * n + col];
+        if (row == col) x += gamma;
+        C[row * n + col] = x;
+        C[col * n + row] = x;
+        if (want_resid) {
+          const float d = x - (row == col ? 1.f : 0.f);
+          rs += (row == col ? 1.f : 2.f) * d * d;
+        }
+      }
+  }
+  return rs;
+}
+
+// Sum over the workgroup (256 threads), the same value in every thread.
+__device__ __forceinline__ float small_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void newton_small_kernel(const float* __restrict__ Mbuf,
+                                                           const float* __restrict__ Xbuf,
+                                                           float* __restrict__ Xroot, FactorSet fs,
+                                                           NewtonCtl c, MaxOut mo) {
+  __shared__ __align__(16) float sm[6][kSmallSide * kSmallSide];
+  __shared__ float red[4];
+  const int f = blockIdx.x;
+  int n;
+  const float* mf = factor_ptr(Mbuf, fs, f, n);
+  const int64_t base = mf - Mbuf;
+  const int nn = n * n;
+  const int p = c.p;
+  const bool scaled = c.scale_mode == 3 && c.coef != nullptr;
+  float* rec = scaled ? c.coef + (size_t)f * kCoefRecord : nullptr;
+  // the coefficients of the next iteration (scale mode 3: the record's)
+  const double pp = (double)p * p, q = p + 1.0;
+  float t2a = (float)(1.0 / pp), t2b = (float)(-2.0 * q / pp), t2g = (float)(q * q / pp);
+  float xa = (float)(-1.0 / p), xb = (float)(q / p), ma = 1.f, mu_prev = 1.f;
+  if (scaled) {
+    t2a = rec[kCoefT2 + 0];
+    t2b = rec[kCoefT2 + 1];
+    t2g = rec[kCoefT2 + 3];
+    xa = rec[kCoefXT + 0];
+    xb = rec[kCoefXT + 1];
+    ma = rec[kCoefM + 0];
+    mu_prev = rec[kCoefPrevMu];
+  }
+  int st = c.status[f], fin = c.final_iter[f];
+  float rprev = c.rprev[f];
+  float lo = scaled ? c.lo[f] : 0.f;
+  // slots: the accepted M and X, the new ones, T^2, T^4 (for p = 6, 8, T^p
+  // goes to the new-M slot and M' to T^2's)
+  int iM = 0, iMn = 1, iX = 2, iXn = 3;
+  float* T2 = sm[4];
+  float* T4 = sm[5];
+  for (int e = threadIdx.x; e < nn; e += blockDim.x) {
+    sm[iM][e] = mf[e];
+    sm[iXn][e] = Xbuf[base + e];  // X_1, formed by the init kernel
+  }
+  __syncthreads();
+  const double cube = (double)n * n * (n + 1.0);
+  const int per_iter = p == 4 ? 4 : 5;
+  double flops = 0.0;
+  for (int k = 0; k < c.max_iters && (st == 0 || st == kStatusFinalX); ++k) {
+    const int cur = k + 1;
+    float* M = sm[iM];
+    float* X = sm[iX];
+    float* Xn = sm[iXn];
+    if (k > 0) small_product(Xn, X, M, X, xa, xb, 0.f, n, false);  // X' = mu^(1/p) X T
+    __syncthreads();
+    if (st == kStatusFinalX) {  // the iteration forms only X, which is the result
+      flops += cube;
+      st = 1;
+      fin = cur;
+      const int t = iX;
+      iX = iXn;
+      iXn = t;
+      break;
+    }
+    small_product(T2, M, M, M, t2a, t2b, t2g, n, false);
+    __syncthreads();
+    small_product(T4, T2, T2, nullptr, 1.f, 0.f, 0.f, n, false);
+    __syncthreads();
+    float* Tp = T4;
+    if (p == 6 || p == 8) {
+      // T^6 = T^4 T^2, T^8 = T^4 T^4, into the new-M slot, then M' into T^2's
+      small_product(sm[iMn], T4, p == 6 ? T2 : T4, nullptr, 1.f, 0.f, 0.f, n, false);
+      __syncthreads();
+      Tp = sm[iMn];
+    }
+    float* Mn = (p == 6 || p == 8) ? T2 : sm[iMn];
+    const float part = small_product(Mn, Tp, M, nullptr, ma, 0.f, 0.f, n, true);  // T^p (mu M)
+    const float s = small_sum(part, red);
+    flops += (k == 0 ? per_iter - 1 : per_iter) * cube;
+    const float r = sqrtf(s) / sqrtf((float)fs.nreal[f]);
+    // the stopping rule of newton_check_kernel
+    const float mu = ma;
+    const float rp = mu_prev > 1.f ? INFINITY : rprev;
+    const bool monotone = c.tol > 0.f && mu == 1.f;
+    bool accept = false;
+    if (!isfinite(r)) {
+      st = 3;
+    } else if (monotone && r > 1.2f * rp && rp > kFloorGuard) {
+      st = 3;
+    } else if (monotone && r >= rp) {
+      st = 2;
+    } else {
+      accept = true;
+      rprev = r;
+      fin = cur;
+      if (c.tol > 0.f && r <= c.tol)
+        st = 1;
+      else if (cur >= c.max_iters)
+        st = 4;
+    }
+    if (accept) {
+      if (p == 6 || p == 8) {
+        // M' sits in T^2's slot: copy it into the new-M slot
+        for (int e = threadIdx.x; e < nn; e += blockDim.x) sm[iMn][e] = T2[e];
+        __syncthreads();
+      }
+      int t = iM;
+      iM = iMn;
+      iMn = t;
+      t = iX;
+      iX = iXn;
+      iXn = t;
+    }
+    if (st == 0) {
+      double mun = 1.0;
+      if (scaled) {
+        const double a = lo;
+        mun = a < kScaledPhaseEnd ? newton_balance(a, p) : 1.0;
+        lo = (float)newton_map(a, p, mun);
+        const double mr = pow(mun, 1.0 / p);
+        t2a = (float)(mun * mun / pp);
+        t2b = (float)(-2.0 * q * mun / pp);
+        t2g = (float)(q * q / pp);
+        xa = (float)(-mun * mr / p);
+        xb = (float)(q * mr / p);
+        ma = (float)mun;
+        mu_prev = mu;
+      }
+      if (c.tol > 0.f && mu == 1.f && mun == 1.0 && cur < c.max_iters) {
+        const float bound = (float)((p + 1) / (2.0 * p) * sqrt((double)fs.nreal[f]) * (double)r * r);
+        if (fmaxf(bound, kRoundingFloor) <= c.tol) {
+          st = kStatusFinalX;
+          rprev = bound;
+        }
+      }
+    }
+  }
+  // the kept iterate: X_fin (X_0 = s^(-1/p) I is never stored)
+  const float* X = sm[iX];
+  const float cf = c.cfac[f];
+  float mx = 0.f;
+  for (int e = threadIdx.x; e < nn; e += blockDim.x) {
+    const int row = e / n, col = e - row * n;
+    const float x = fin == 0 ? (row == col ? cf : 0.f) : X[e];
+    Xroot[base + e] = x;
+    mx = fmaxf(mx, fabsf(x));
+  }
+  if (mo.a != nullptr) raise_max2_wg<256>(mo.a + f, mx, nullptr, 0.f, mo.ver);
+  if (threadIdx.x == 0) {
+    c.status[f] = st;
+    c.final_iter[f] = fin;
+    c.rprev[f] = rprev;
+    if (scaled) {
+      c.lo[f] = lo;
+      write_newton_coefs(rec, ma, p);
+      rec[kCoefPrevMu] = mu_prev;
+    }
+    if (flops > 0.0) atomicAdd(c.flops_acc, flops);
+  }
+}
+
 // Stage 1's kept Y (index final_iter, Ybuf0 for even, Ybuf1 for odd) becomes
 // stage 2's Y0 in Ybuf0, and Z0 = I goes to Z0buf. A factor whose stage 1
 // diverged keeps its status and gets no stage 2 (its root becomes s^(-1/p) I).
@@ -2395,6 +2618,14 @@ hipError_t launch_zero_words(uint64_t* w, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
   hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, s, w, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_newton_small(const float* M0, const float* X1, float* Xroot, FactorSet fs,
+                               NewtonCtl c, hipStream_t s, MaxOut mo) {
+  if (fs.B == 0) return hipSuccess;
+  if (fs.max_side() > kSmallSide || c.solver != kCoupledNewton) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(newton_small_kernel, dim3(fs.count()), dim3(256), 0, s, M0, X1, Xroot, fs, c, mo);
   return hipGetLastError();
 }
 

@@ -144,6 +144,14 @@ int newton(shampoo_ctx* h, const RootJob& j, hipStream_t s) {
     return shp::launch_newton_init(j.A, j.s[0], j.xalt, fs, c, s, max_out(h, j, j.s[0], j.xalt));
   });
   if (rc) return rc;
+  if (fs.max_side() <= shp::kSmallSide) {
+    // small factors: the whole iteration in one launch (its flops are counted
+    // on the device)
+    return timed(h, kNewtonGemm, 0.0, 0.0, s, [&] {
+      return shp::launch_newton_small(j.s[0], j.xalt, j.xroot, fs, c, s,
+                                      max_out(h, j, j.xroot, nullptr));
+    });
+  }
   const double p = c.p;
   const float a2 = (float)(1.0 / (p * p)), b2 = (float)(-2.0 * (p + 1.0) / (p * p)),
               g2 = (float)((p + 1.0) * (p + 1.0) / (p * p));
