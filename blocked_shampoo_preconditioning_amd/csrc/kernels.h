@@ -187,8 +187,11 @@ struct FactorSet {
   }
 };
 
-// Power-iteration products of scale mode 2 (the first shares the norm pass).
-constexpr int kPowerIters = 16;
+// Power-iteration products of scale modes 2 and 3 (the first shares the norm
+// pass); the Chebyshev interval, which must contain the whole spectrum, takes
+// more.
+constexpr int kPowerIters = 8;
+constexpr int kPowerItersCheb = 16;
 constexpr int kMaxSide = 4096;
 
 enum RootSolver { kCoupledNewton = 0, kNewtonDB = 1, kChebyshev = 2 };

@@ -1403,13 +1403,13 @@ __device__ __forceinline__ const float* factor_ptr(const float* base, const Fact
 //           every step (newton_check_kernel), starting from an estimate of the
 //           spectrum's bottom made here
 //   mode 2: s = lam / 2, lam the power-iteration estimate ||A v_k|| of the
-//           largest eigenvalue after kPowerIters (16) products from
+//           largest eigenvalue after kPowerIters (8) products from
 //           v_0 = 1 / sqrt(n). For symmetric A the ratios ||A^(j+1) v|| /
-//           ||A^j v|| never decrease, so lam >= lam_max |c_1|^(1/16) with c_1
+//           ||A^j v|| never decrease, so lam >= lam_max |c_1|^(1/8) with c_1
 //           the component of v_0 on the top eigenvector: the spectrum of A / s
 //           stays inside the iteration's convergence region (0, p + 1)
-//           unless |c_1| < 2^-16 (p + 1)^-16 (4.3e-7 for p = 4). lam = 0 falls
-//           back to mode 1.
+//           unless |c_1| < (2 / (p + 1))^8 (6.6e-4 for p = 4). lam = 0 falls
+//           back to mode 1. The Chebyshev interval takes kPowerItersCheb (16).
 // Only the real extent of a factor enters.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double block_sum(double v, double* red) {
@@ -1651,7 +1651,8 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
     // Top power iteration from v_0 = 1 / sqrt(n); in mode 3 the bottom one
     // runs beside it on lam_j I - A from u_0 (one pass over A per step serves
     // both): q_j = u_j^T A u_j, u_(j+1) = normalised lam_j u_j - A u_j.
-    for (int it = 0; it < kPowerIters; ++it) {
+    const int steps = cheb ? kPowerItersCheb : kPowerIters;
+    for (int it = 0; it < steps; ++it) {
       if (it > 0) {
         if (scaled)
           sym_matvec<true>(Af, n, nr, v, u, w, wu);

@@ -188,7 +188,7 @@ def inverse_root_eigh(A, p=4):
     return (Q * lam ** (-1.0 / p)) @ Q.T
 
 
-def _power_lambda(A, power_iters=16):
+def _power_lambda(A, power_iters=8):
     """||A v_k|| after power_iters products from v_0 = 1 / sqrt(n) (0 if A v = 0).
 
     Pinned by: test_newton_scale_mode2_power_iteration (closed form on a diagonal matrix).
@@ -204,7 +204,7 @@ def _power_lambda(A, power_iters=16):
     return lam
 
 
-def newton_scale(A, p=4, mode=1, power_iters=16):
+def newton_scale(A, p=4, mode=1, power_iters=8):
     """Norm used to scale A before the coupled Newton iteration.
 
     mode 0: s = ||A||_F, which puts the spectrum of A/s in (0, 1].
@@ -217,11 +217,11 @@ def newton_scale(A, p=4, mode=1, power_iters=16):
             (see newton_balance).
     mode 2: s = lam / 2, where lam is the power-iteration estimate of the
             largest eigenvalue: from v_0 = (1, ..., 1) / sqrt(n), repeat
-            w = A v, lam = ||w||, v = w / lam, power_iters (16) times. For a
+            w = A v, lam = ||w||, v = w / lam, power_iters (8) times. For a
             symmetric A the ratios ||A^(j+1) v|| / ||A^j v|| never decrease, so
-            lam >= lam_max * |c_1|^(1/16), c_1 the component of v_0 along the top
+            lam >= lam_max * |c_1|^(1/8), c_1 the component of v_0 along the top
             eigenvector: the spectrum of A / s stays below 5 (the iteration's
-            convergence region) unless |c_1| < 0.4^16 = 4.3e-7. If lam is 0,
+            convergence region) unless |c_1| < 0.4^8 = 6.6e-4. If lam is 0,
             s falls back to min(||A||_F, ||A||_inf) * 2 / (p + 1).
 
     Pinned by: test_newton_scale_bounds_spectrum, test_newton_scale_mode2_power_iteration.
@@ -263,7 +263,7 @@ SCALED_PHASE_END = 0.75
 BALANCE_STEPS = 40
 
 
-def power_pair(A, power_iters=16):
+def power_pair(A, power_iters=8):
     """Top and bottom power iterations run side by side (one pass over A per
     step serves both): v_0 = (1, ..., 1) / sqrt(n) for the top, u_0 = (1, -1,
     1, ...) / sqrt(n) for the bottom; step j forms A v_j and A u_j, takes
@@ -295,7 +295,7 @@ def power_pair(A, power_iters=16):
     return lam, q
 
 
-def spectrum_floor_estimate(A, power_iters=16):
+def spectrum_floor_estimate(A, power_iters=8):
     """Estimate of the smallest eigenvalue of a symmetric A that is never
     below it: the smaller of the smallest diagonal entry and power_pair's
     Rayleigh quotient (both are Rayleigh quotients of A).
@@ -450,7 +450,7 @@ def inverse_root_coupled_newton(A, p=4, max_iters=25, tol=0.0, scale_mode=1,
     return X, info
 
 
-def db_scale(A, mode=2, power_iters=16):
+def db_scale(A, mode=2, power_iters=8):
     """Scale for the Denman-Beavers stages: the iteration converges for a
     spectrum inside (0, 2), so the spectral target is 1 instead of Newton's:
     mode 0 ||A||_F, mode 1 min(||A||_F, ||A||_inf), mode 2 the power estimate
