@@ -196,7 +196,7 @@ struct Bf16Stage {
   u32x4 a[PA], b[PB];
 };
 
-template <class C>
+template <class C, bool SAME = false>
 __device__ __forceinline__ void bf16_load(Bf16Stage<C>& st, const uint16_t* __restrict__ X, int K,
                                           int m0, int n0, int kt) {
   using S = Bf16Stage<C>;
@@ -207,16 +207,18 @@ __device__ __forceinline__ void bf16_load(Bf16Stage<C>& st, const uint16_t* __re
     st.a[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(m0 + c / S::CPR) * K + k0 +
                                               (c % S::CPR) * 8);
   }
+  if constexpr (!SAME) {
 #pragma unroll
-  for (int i = 0; i < S::PB; ++i) {
-    const int c = tid + i * C::NT;
-    st.b[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(n0 + c / S::CPR) * K + k0 +
-                                              (c % S::CPR) * 8);
+    for (int i = 0; i < S::PB; ++i) {
+      const int c = tid + i * C::NT;
+      st.b[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(n0 + c / S::CPR) * K + k0 +
+                                                (c % S::CPR) * 8);
+    }
   }
 }
 
 // Into LDS buffer buf: [BM][LDKH] of A then [BN][LDKH] of B per buffer.
-template <class C>
+template <class C, bool SAME = false>
 __device__ __forceinline__ void bf16_store(const Bf16Stage<C>& st, uint16_t* sA, uint16_t* sB,
                                            int buf) {
   using S = Bf16Stage<C>;
@@ -229,10 +231,12 @@ __device__ __forceinline__ void bf16_store(const Bf16Stage<C>& st, uint16_t* sA,
     const int c = tid + i * C::NT;
     *reinterpret_cast<u32x4*>(dA + (c / S::CPR) * LD + (c % S::CPR) * 8) = st.a[i];
   }
+  if constexpr (!SAME) {
 #pragma unroll
-  for (int i = 0; i < S::PB; ++i) {
-    const int c = tid + i * C::NT;
-    *reinterpret_cast<u32x4*>(dB + (c / S::CPR) * LD + (c % S::CPR) * 8) = st.b[i];
+    for (int i = 0; i < S::PB; ++i) {
+      const int c = tid + i * C::NT;
+      *reinterpret_cast<u32x4*>(dB + (c / S::CPR) * LD + (c % S::CPR) * 8) = st.b[i];
+    }
   }
 }
 
@@ -268,12 +272,15 @@ __device__ __forceinline__ void bf16_mma(floatx16 (&acc)[C::FM][C::FN], const ui
 // while the MFMAs run on K-tile kt, tile kt + 1 (loaded one phase earlier)
 // goes to the other buffer and tile kt + 2 is loaded into the freed stage, so
 // every load has a full phase to land; an odd last tile runs alone.
-template <class C, int MASK = -1>
+// SAME: a diagonal tile (n0 == m0): the rows are loaded once and read as
+// both operands.
+template <class C, int MASK = -1, bool SAME = false>
 __device__ __forceinline__ void mainloop_bf16(const uint16_t* __restrict__ X, int K, int m0, int n0,
                                               int wm, int wn, floatx16 (&acc)[C::FM][C::FN],
                                               float* lds) {
-  uint16_t* sA = reinterpret_cast<uint16_t*>(lds);  // [2][BM][LDKH]
-  uint16_t* sB = sA + 2 * C::BM * C::LDKH;           // [2][BN][LDKH]
+  static_assert(!SAME || C::BM == C::BN, "a shared panel is square");
+  uint16_t* sA = reinterpret_cast<uint16_t*>(lds);           // [2][BM][LDKH]
+  uint16_t* sB = SAME ? sA : sA + 2 * C::BM * C::LDKH;      // [2][BN][LDKH]
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -282,19 +289,19 @@ __device__ __forceinline__ void mainloop_bf16(const uint16_t* __restrict__ X, in
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = K / C::BKH;
   Bf16Stage<C> s0, s1;
-  bf16_load<C>(s0, X, K, m0, n0, 0);
-  if (nk > 1) bf16_load<C>(s1, X, K, m0, n0, 1);
-  bf16_store<C>(s0, sA, sB, 0);
+  bf16_load<C, SAME>(s0, X, K, m0, n0, 0);
+  if (nk > 1) bf16_load<C, SAME>(s1, X, K, m0, n0, 1);
+  bf16_store<C, SAME>(s0, sA, sB, 0);
   __syncthreads();
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    if (kt + 2 < nk) bf16_load<C>(s0, X, K, m0, n0, kt + 2);
+    if (kt + 2 < nk) bf16_load<C, SAME>(s0, X, K, m0, n0, kt + 2);
     bf16_mma<C, MASK>(acc, sA, sB, 0, wm, wn);
-    bf16_store<C>(s1, sA, sB, 1);
+    bf16_store<C, SAME>(s1, sA, sB, 1);
     __syncthreads();
-    if (kt + 3 < nk) bf16_load<C>(s1, X, K, m0, n0, kt + 3);
+    if (kt + 3 < nk) bf16_load<C, SAME>(s1, X, K, m0, n0, kt + 3);
     bf16_mma<C, MASK>(acc, sA, sB, 1, wm, wn);
-    if (kt + 2 < nk) bf16_store<C>(s0, sA, sB, 0);
+    if (kt + 2 < nk) bf16_store<C, SAME>(s0, sA, sB, 0);
     __syncthreads();
   }
   if (kt < nk) bf16_mma<C, MASK>(acc, sA, sB, 0, wm, wn);
@@ -665,12 +672,12 @@ struct SymWave {
 };
 
 // 256 x 256 tiles of eight waves of 128 x 64 (2 x 4 waves, 4 x 2 fragments
-// each). On a diagonal tile, of the 8 x 8 fragments the upper triangle (36)
-// is needed: the waves crossing the diagonal keep their fragments on or above
-// it (3 or 7), the two waves below it each take the bottom half of a full
-// block above it, whose own wave keeps the top half (4 and 4). With wave w on
-// SIMD w % 4 the busiest SIMD then runs 11 fragment products where a full
-// tile runs 16.
+// each). On a diagonal tile only the upper triangle of the 8 x 8 fragments
+// (36) is needed: the blocks crossing the diagonal take 3 or 7 fragments, the
+// two full blocks above it are split in halves of 4, the two blocks below it
+// are not computed. Wave w runs on SIMD w % 4, so the roles are dealt to pair
+// a 3 with a 7 and a 4 with a 4 on every SIMD: the busiest SIMD runs 10
+// fragment products where a full tile runs 16.
 template <class C>
 struct SymWave<C, false> {
   static_assert(C::WM == 2 && C::WN == 4 && C::FM == 4 && C::FN == 2, "the 256-tile layout");
@@ -684,17 +691,12 @@ struct SymWave<C, false> {
     wn = wave / C::WM;
     mask = -1;
     if (!diag) return;
-    if (wm == 0 && wn < 2) {
-      mask = wn == 0 ? kCross0 : kCross1;
-    } else if (wm == 1 && wn >= 2) {
-      mask = wn == 2 ? kCross0 : kCross1;
-    } else if (wm == 1) {  // below the diagonal: the bottom half of block (0, wn + 2)
-      wm = 0;
-      wn += 2;
-      mask = kBottom;
-    } else {
-      mask = kTop;
-    }
+    // role of wave 0..7: block (wm, wn) and its fragment mask
+    constexpr int kWm = 0x22;        // bits: waves 1 and 5 take blocks of row 1
+    constexpr int kWn = 0xEDE8;      // two bits per wave: 0, 2, 2, 3, 1, 3, 2, 3
+    wm = (kWm >> wave) & 1;
+    wn = (kWn >> (2 * wave)) & 3;
+    mask = (wave & 3) < 2 ? ((wave & 4) ? kCross1 : kCross0) : ((wave & 4) ? kBottom : kTop);
   }
 };
 
@@ -723,16 +725,17 @@ __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X
                                                   float* lds, const SymWave<C>& sw) {
   if constexpr (C::FM != C::FN) {
     using W = SymWave<C>;
+    // a diagonal tile (every wave's mask is not -1 there) reads one panel
     if (sw.mask == -1)
       mainloop_bf16<C>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
     else if (sw.mask == W::kCross0)
-      mainloop_bf16<C, W::kCross0>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+      mainloop_bf16<C, W::kCross0, true>(X, K, m0, m0, sw.wm, sw.wn, acc, lds);
     else if (sw.mask == W::kCross1)
-      mainloop_bf16<C, W::kCross1>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+      mainloop_bf16<C, W::kCross1, true>(X, K, m0, m0, sw.wm, sw.wn, acc, lds);
     else if (sw.mask == W::kTop)
-      mainloop_bf16<C, W::kTop>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+      mainloop_bf16<C, W::kTop, true>(X, K, m0, m0, sw.wm, sw.wn, acc, lds);
     else
-      mainloop_bf16<C, W::kBottom>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+      mainloop_bf16<C, W::kBottom, true>(X, K, m0, m0, sw.wm, sw.wn, acc, lds);
     return;
   } else {
   constexpr int kUpper = upper_mask<C::FM, C::FN>();
