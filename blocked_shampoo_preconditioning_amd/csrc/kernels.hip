@@ -196,22 +196,34 @@ struct Bf16Stage {
   u32x4 a[PA], b[PB];
 };
 
+// Row of 16-byte chunk c of a bf16 K-tile (four chunks per row, chunk c % 4
+// within it): the 16 lanes of one LDS write group take rows {0, 4, 8, 12}
+// (plus 0..3 by group) of a 16-row band, so at the 80-byte row pitch their
+// 64-byte row segments start 0, 20, 40 and 60 banks apart (mod 64; 0, 4 mod
+// 8-lane groups of 32 banks) and the group writes every bank once; four
+// consecutive lanes still load one row's 64 contiguous bytes.
+__device__ __forceinline__ int bf16_row(int c) {
+  const int g = c >> 4, w = c & 15;
+  return ((g >> 2) << 4) + (g & 3) + ((w >> 2) << 2);
+}
+
 template <class C, bool SAME = false>
 __device__ __forceinline__ void bf16_load(Bf16Stage<C>& st, const uint16_t* __restrict__ X, int K,
                                           int m0, int n0, int kt) {
   using S = Bf16Stage<C>;
+  static_assert(S::CPR == 4 && C::BM % 16 == 0 && C::BN % 16 == 0, "chunk layout");
   const int tid = threadIdx.x, k0 = kt * C::BKH;
 #pragma unroll
   for (int i = 0; i < S::PA; ++i) {
     const int c = tid + i * C::NT;
-    st.a[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(m0 + c / S::CPR) * K + k0 +
+    st.a[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(m0 + bf16_row(c)) * K + k0 +
                                               (c % S::CPR) * 8);
   }
   if constexpr (!SAME) {
 #pragma unroll
     for (int i = 0; i < S::PB; ++i) {
       const int c = tid + i * C::NT;
-      st.b[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(n0 + c / S::CPR) * K + k0 +
+      st.b[i] = *reinterpret_cast<const u32x4*>(X + (size_t)(n0 + bf16_row(c)) * K + k0 +
                                                 (c % S::CPR) * 8);
     }
   }
@@ -229,13 +241,13 @@ __device__ __forceinline__ void bf16_store(const Bf16Stage<C>& st, uint16_t* sA,
 #pragma unroll
   for (int i = 0; i < S::PA; ++i) {
     const int c = tid + i * C::NT;
-    *reinterpret_cast<u32x4*>(dA + (c / S::CPR) * LD + (c % S::CPR) * 8) = st.a[i];
+    *reinterpret_cast<u32x4*>(dA + bf16_row(c) * LD + (c % S::CPR) * 8) = st.a[i];
   }
   if constexpr (!SAME) {
 #pragma unroll
     for (int i = 0; i < S::PB; ++i) {
       const int c = tid + i * C::NT;
-      *reinterpret_cast<u32x4*>(dB + (c / S::CPR) * LD + (c % S::CPR) * 8) = st.b[i];
+      *reinterpret_cast<u32x4*>(dB + bf16_row(c) * LD + (c % S::CPR) * 8) = st.b[i];
     }
   }
 }
