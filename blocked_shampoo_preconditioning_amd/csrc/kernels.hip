@@ -556,6 +556,179 @@ __device__ __forceinline__ void split_mma(floatx16 (&acc)[C::FM][C::FN], const u
                                                               acc[i][j], 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Staggered main loop of the fp16 split on 256 x 256 tiles of eight waves.
+// The waves of a workgroup run on SIMD w % 4, so waves 0-3 (group 0) and 4-7
+// (group 1) put one wave of each group on every SIMD. Each group loads,
+// splits and stores its half of the rows of every K-tile, and the groups run
+// half a K-step apart: in every slot between two barriers one group runs the
+// MFMAs of a K-tile on fragments already in registers, while the other reads
+// the fragments of its next K-tile from LDS, splits its share of the tile
+// after next into the other LDS buffer and issues the loads of the tile after
+// that. On every SIMD the matrix work of one wave then overlaps the operand
+// work of the other, where the lockstep loop (all waves in the same phase)
+// serialises them. Each accumulator sees the same MFMAs in the same order as
+// in the lockstep loop, so the results are bit-identical.
+// ---------------------------------------------------------------------------
+// One group's half (128 rows) of one operand of a K-tile of 16 (256 threads):
+// rows mode: two 4-value chunks, row split_row(c) and chunk c % 4 for
+// c = tg + 256 i; columns mode: 8 consecutive k of row tg % 128.
+template <bool COLS>
+struct HalfOperand {
+  f32x4 r[COLS ? 1 : 2];
+  float c[COLS ? 8 : 1];
+};
+
+template <bool COLS>
+__device__ __forceinline__ void half_load(HalfOperand<COLS>& o, const float* __restrict__ X, int ld,
+                                          int r0, int k0, int tg) {
+  if constexpr (COLS) {
+    const int row = tg & 127, kq = (tg >> 7) * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o.c[q] = X[(size_t)(k0 + kq + q) * ld + r0 + row];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tg + i * 256;
+      o.r[i] = *reinterpret_cast<const f32x4*>(X + (size_t)(r0 + split_row(c)) * ld + k0 + (c % 4) * 4);
+    }
+  }
+}
+
+// The two fp16 planes (scaled by 2^e) of a group's half at d, the group's
+// first row in plane 0; planes P 16-bit words apart, rows of LDX.
+template <class C, bool COLS>
+__device__ __forceinline__ void half_store(const HalfOperand<COLS>& o, uint16_t* d, int P, int e,
+                                           int tg) {
+  constexpr int LD = C::LDX;
+  if constexpr (COLS) {
+    uint16_t* dr = d + (tg & 127) * LD + (tg >> 7) * 8;
+    const Split2 s0 = split2h(o.c[0], o.c[1], e), s1 = split2h(o.c[2], o.c[3], e);
+    const Split2 s2 = split2h(o.c[4], o.c[5], e), s3 = split2h(o.c[6], o.c[7], e);
+    *reinterpret_cast<u32x4*>(dr) = (u32x4){s0.h, s1.h, s2.h, s3.h};
+    *reinterpret_cast<u32x4*>(dr + P) = (u32x4){s0.l, s1.l, s2.l, s3.l};
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tg + i * 256;
+      store_split4h(d + split_row(c) * LD + (c % 4) * 4, P, o.r[i], e);
+    }
+  }
+}
+
+// A wave's fp16 fragments of one K-tile (both planes of A and of B), in the
+// operand layout of split_mma.
+template <class C>
+struct HalfFrags {
+  f16x8 a[2][C::FM], b[2][C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ void half_frag_read(HalfFrags<C>& f, const uint16_t* sA,
+                                               const uint16_t* sB, int wm, int wn) {
+  constexpr int LD = C::LDX, PA = C::BM * LD, PB = C::BN * LD;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const uint16_t* a0 = sA + (wm * 32 * C::FM + l32) * LD + half * 8;
+  const uint16_t* b0 = sB + (wn * 32 * C::FN + l32) * LD + half * 8;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) f.a[p][i] = *reinterpret_cast<const f16x8*>(a0 + p * PA + i * 32 * LD);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) f.b[p][j] = *reinterpret_cast<const f16x8*>(b0 + p * PB + j * 32 * LD);
+  }
+}
+
+// The three fp16 products (lh, hl, hh) of one K-tile, product-major.
+template <class C, int MASK>
+__device__ __forceinline__ void half_frag_mma(floatx16 (&acc)[C::FM][C::FN], const HalfFrags<C>& f) {
+  constexpr int PP[3][2] = {{1, 0}, {0, 1}, {0, 0}};
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        if (MASK & (1 << (i * C::FN + j)))
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[PP[q][0]][i], f.b[PP[q][1]][j],
+                                                             acc[i][j], 0, 0, 0);
+}
+
+// A workgroup barrier that the scheduler does not move instructions across
+// (left alone, it sinks MFMAs below an s_barrier, which undoes the stagger).
+__device__ __forceinline__ void slot_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Slots: group 0 runs the MFMAs of tile q in slot 2q and its operand work in
+// slot 2q + 1; group 1 one slot later. Tile q + 2 goes into the buffer of
+// tile q, whose last fragment reads (group 1, slot 2q) precede its first
+// store (group 0, slot 2q + 1); tile q is complete after slot 2q - 2 and
+// first read in slot 2q - 1. Both groups pass 2 nk + 1 barriers.
+template <class C, bool PCOLS, bool QCOLS, int MASK, bool SAME>
+__device__ __forceinline__ void mainloop_stagger(const float* __restrict__ A, int lda,
+                                                 const float* __restrict__ B, int ldb, int K,
+                                                 int m0, int n0, int wm, int wn,
+                                                 floatx16 (&acc)[C::FM][C::FN], float* lds,
+                                                 int ea, int eb) {
+  static_assert(C::NT == 512 && C::BM == 256 && C::BN == 256, "256-tiles of eight waves");
+  constexpr int PA = C::BM * C::LDX, PB = C::BN * C::LDX;
+  uint16_t* sA0 = reinterpret_cast<uint16_t*>(lds);  // [2][2][BM][LDX]
+  uint16_t* sA1 = sA0 + 2 * PA;
+  uint16_t* sB0 = SAME ? sA0 : sA0 + 4 * PA;          // [2][2][BN][LDX]
+  uint16_t* sB1 = SAME ? sA1 : sB0 + 2 * PB;
+  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+  const int tg = threadIdx.x & 255;
+  const int ra = m0 + grp * 128, rb = n0 + grp * 128;
+  const int oa = grp * 128 * C::LDX;  // the group's first row in a plane
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int nk = K / 16;  // >= 2
+  HalfOperand<PCOLS> a;
+  HalfOperand<QCOLS> b;
+  HalfFrags<C> fr;
+  half_load<PCOLS>(a, A, lda, ra, 0, tg);
+  if constexpr (!SAME) half_load<QCOLS>(b, B, ldb, rb, 0, tg);
+  half_store<C, PCOLS>(a, sA0 + oa, PA, ea, tg);
+  if constexpr (!SAME) half_store<C, QCOLS>(b, sB0 + oa, PB, eb, tg);
+  half_load<PCOLS>(a, A, lda, ra, 16, tg);
+  if constexpr (!SAME) half_load<QCOLS>(b, B, ldb, rb, 16, tg);
+  half_store<C, PCOLS>(a, sA1 + oa, PA, ea, tg);
+  if constexpr (!SAME) half_store<C, QCOLS>(b, sB1 + oa, PB, eb, tg);
+  __syncthreads();
+  if (nk > 2) {
+    half_load<PCOLS>(a, A, lda, ra, 32, tg);
+    if constexpr (!SAME) half_load<QCOLS>(b, B, ldb, rb, 32, tg);
+  }
+  half_frag_read<C>(fr, sA0, sB0, wm, wn);
+  if (grp == 1) slot_barrier();  // group 1 runs one slot behind
+  for (int q = 0; q < nk; ++q) {
+    half_frag_mma<C, MASK>(acc, fr);
+    slot_barrier();
+    // operand slot: the fragments of tile q + 1 first (their LDS latency
+    // then overlaps the split), then tile q + 2 where tile q was, then the
+    // loads of tile q + 3
+    const bool odd = q & 1;
+    if (q + 1 < nk) half_frag_read<C>(fr, odd ? sA0 : sA1, odd ? sB0 : sB1, wm, wn);
+    if (q + 2 < nk) {
+      half_store<C, PCOLS>(a, (odd ? sA1 : sA0) + oa, PA, ea, tg);
+      if constexpr (!SAME) half_store<C, QCOLS>(b, (odd ? sB1 : sB0) + oa, PB, eb, tg);
+      if (q + 3 < nk) {
+        half_load<PCOLS>(a, A, lda, ra, (q + 3) * 16, tg);
+        if constexpr (!SAME) half_load<QCOLS>(b, B, ldb, rb, (q + 3) * 16, tg);
+      }
+    }
+    if (grp == 0 || q + 1 < nk) slot_barrier();
+  }
+}
+
 // acc[fm][fn] = sum over K of A[m0 + ...][k] * B[n0 + ...][k]: A is [M][K]
 // with row stride lda (k contiguous), or with PCOLS its transpose [K][M] (row
 // stride lda, m contiguous); B likewise [N][K] or, with QCOLS, [K][N]. K is a
@@ -574,6 +747,10 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
                                             floatx16 (&acc)[C::FM][C::FN], float* lds,
                                             int ea = 0, int eb = 0) {
   static_assert(!SAME || (C::BM == C::BN && PCOLS == QCOLS), "a shared panel is square");
+  if constexpr (F16 && C::NT == 512 && C::BM == 256 && C::BN == 256) {
+    mainloop_stagger<C, PCOLS, QCOLS, MASK, SAME>(A, lda, B, ldb, K, m0, n0, wm, wn, acc, lds, ea, eb);
+    return;
+  }
   constexpr int NPL = F16 ? 2 : 3;                          // planes per operand
   constexpr int PA = C::BM * C::LDX, PB = C::BN * C::LDX;  // one plane, in 16-bit words
   uint16_t* sA0 = reinterpret_cast<uint16_t*>(lds);  // [2][NPL][BM][LDX]
