@@ -570,49 +570,30 @@ __device__ __forceinline__ void split_mma(floatx16 (&acc)[C::FM][C::FN], const u
 // serialises them. Each accumulator sees the same MFMAs in the same order as
 // in the lockstep loop, so the results are bit-identical.
 // ---------------------------------------------------------------------------
-// One group's half (128 rows) of one operand of a K-tile of 16 (256 threads):
-// rows mode: two 4-value chunks, row split_row(c) and chunk c % 4 for
-// c = tg + 256 i; columns mode: 8 consecutive k of row tg % 128.
-template <bool COLS>
+// One group's half (128 rows) of one row operand ([rows][K], k contiguous)
+// of a K-tile of 16, 256 threads: two 4-value chunks, row split_row(c) and
+// chunk c % 4 for c = tg + 256 i.
 struct HalfOperand {
-  f32x4 r[COLS ? 1 : 2];
-  float c[COLS ? 8 : 1];
+  f32x4 r[2];
 };
 
-template <bool COLS>
-__device__ __forceinline__ void half_load(HalfOperand<COLS>& o, const float* __restrict__ X, int ld,
+__device__ __forceinline__ void half_load(HalfOperand& o, const float* __restrict__ X, int ld,
                                           int r0, int k0, int tg) {
-  if constexpr (COLS) {
-    const int row = tg & 127, kq = (tg >> 7) * 8;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) o.c[q] = X[(size_t)(k0 + kq + q) * ld + r0 + row];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tg + i * 256;
-      o.r[i] = *reinterpret_cast<const f32x4*>(X + (size_t)(r0 + split_row(c)) * ld + k0 + (c % 4) * 4);
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int c = tg + i * 256;
+    o.r[i] = *reinterpret_cast<const f32x4*>(X + (size_t)(r0 + split_row(c)) * ld + k0 + (c % 4) * 4);
   }
 }
 
 // The two fp16 planes (scaled by 2^e) of a group's half at d, the group's
 // first row in plane 0; planes P 16-bit words apart, rows of LDX.
-template <class C, bool COLS>
-__device__ __forceinline__ void half_store(const HalfOperand<COLS>& o, uint16_t* d, int P, int e,
-                                           int tg) {
-  constexpr int LD = C::LDX;
-  if constexpr (COLS) {
-    uint16_t* dr = d + (tg & 127) * LD + (tg >> 7) * 8;
-    const Split2 s0 = split2h(o.c[0], o.c[1], e), s1 = split2h(o.c[2], o.c[3], e);
-    const Split2 s2 = split2h(o.c[4], o.c[5], e), s3 = split2h(o.c[6], o.c[7], e);
-    *reinterpret_cast<u32x4*>(dr) = (u32x4){s0.h, s1.h, s2.h, s3.h};
-    *reinterpret_cast<u32x4*>(dr + P) = (u32x4){s0.l, s1.l, s2.l, s3.l};
-  } else {
+template <class C>
+__device__ __forceinline__ void half_store(const HalfOperand& o, uint16_t* d, int P, int e, int tg) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tg + i * 256;
-      store_split4h(d + split_row(c) * LD + (c % 4) * 4, P, o.r[i], e);
-    }
+  for (int i = 0; i < 2; ++i) {
+    const int c = tg + i * 256;
+    store_split4h(d + split_row(c) * C::LDX + (c % 4) * 4, P, o.r[i], e);
   }
 }
 
@@ -663,12 +644,14 @@ __device__ __forceinline__ void slot_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Slots: group 0 runs the MFMAs of tile q in slot 2q and its operand work in
-// slot 2q + 1; group 1 one slot later. Tile q + 2 goes into the buffer of
-// tile q, whose last fragment reads (group 1, slot 2q) precede its first
-// store (group 0, slot 2q + 1); tile q is complete after slot 2q - 2 and
-// first read in slot 2q - 1. Both groups pass 2 nk + 1 barriers.
-template <class C, bool PCOLS, bool QCOLS, int MASK, bool SAME>
+// C = A B^T with both operands by rows ([rows][K], k contiguous), K a
+// multiple of 16 and at least 32. Slots: group 0 runs the MFMAs of tile q in
+// slot 2q and its operand work in slot 2q + 1; group 1 one slot later. Tile
+// q + 2 goes into the buffer of tile q, whose last fragment reads (group 1,
+// slot 2q) precede its first store (group 0, slot 2q + 1); tile q is
+// complete after slot 2q - 2 and first read in slot 2q - 1. Both groups pass
+// 2 nk + 1 barriers.
+template <class C, int MASK, bool SAME>
 __device__ __forceinline__ void mainloop_stagger(const float* __restrict__ A, int lda,
                                                  const float* __restrict__ B, int ldb, int K,
                                                  int m0, int n0, int wm, int wn,
@@ -691,21 +674,20 @@ __device__ __forceinline__ void mainloop_stagger(const float* __restrict__ A, in
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int nk = K / 16;  // >= 2
-  HalfOperand<PCOLS> a;
-  HalfOperand<QCOLS> b;
+  HalfOperand a, b;
   HalfFrags<C> fr;
-  half_load<PCOLS>(a, A, lda, ra, 0, tg);
-  if constexpr (!SAME) half_load<QCOLS>(b, B, ldb, rb, 0, tg);
-  half_store<C, PCOLS>(a, sA0 + oa, PA, ea, tg);
-  if constexpr (!SAME) half_store<C, QCOLS>(b, sB0 + oa, PB, eb, tg);
-  half_load<PCOLS>(a, A, lda, ra, 16, tg);
-  if constexpr (!SAME) half_load<QCOLS>(b, B, ldb, rb, 16, tg);
-  half_store<C, PCOLS>(a, sA1 + oa, PA, ea, tg);
-  if constexpr (!SAME) half_store<C, QCOLS>(b, sB1 + oa, PB, eb, tg);
+  half_load(a, A, lda, ra, 0, tg);
+  if constexpr (!SAME) half_load(b, B, ldb, rb, 0, tg);
+  half_store<C>(a, sA0 + oa, PA, ea, tg);
+  if constexpr (!SAME) half_store<C>(b, sB0 + oa, PB, eb, tg);
+  half_load(a, A, lda, ra, 16, tg);
+  if constexpr (!SAME) half_load(b, B, ldb, rb, 16, tg);
+  half_store<C>(a, sA1 + oa, PA, ea, tg);
+  if constexpr (!SAME) half_store<C>(b, sB1 + oa, PB, eb, tg);
   __syncthreads();
   if (nk > 2) {
-    half_load<PCOLS>(a, A, lda, ra, 32, tg);
-    if constexpr (!SAME) half_load<QCOLS>(b, B, ldb, rb, 32, tg);
+    half_load(a, A, lda, ra, 32, tg);
+    if constexpr (!SAME) half_load(b, B, ldb, rb, 32, tg);
   }
   half_frag_read<C>(fr, sA0, sB0, wm, wn);
   if (grp == 1) slot_barrier();  // group 1 runs one slot behind
@@ -718,11 +700,11 @@ __device__ __forceinline__ void mainloop_stagger(const float* __restrict__ A, in
     const bool odd = q & 1;
     if (q + 1 < nk) half_frag_read<C>(fr, odd ? sA0 : sA1, odd ? sB0 : sB1, wm, wn);
     if (q + 2 < nk) {
-      half_store<C, PCOLS>(a, (odd ? sA1 : sA0) + oa, PA, ea, tg);
-      if constexpr (!SAME) half_store<C, QCOLS>(b, (odd ? sB1 : sB0) + oa, PB, eb, tg);
+      half_store<C>(a, (odd ? sA1 : sA0) + oa, PA, ea, tg);
+      if constexpr (!SAME) half_store<C>(b, (odd ? sB1 : sB0) + oa, PB, eb, tg);
       if (q + 3 < nk) {
-        half_load<PCOLS>(a, A, lda, ra, (q + 3) * 16, tg);
-        if constexpr (!SAME) half_load<QCOLS>(b, B, ldb, rb, (q + 3) * 16, tg);
+        half_load(a, A, lda, ra, (q + 3) * 16, tg);
+        if constexpr (!SAME) half_load(b, B, ldb, rb, (q + 3) * 16, tg);
       }
     }
     if (grp == 0 || q + 1 < nk) slot_barrier();
@@ -747,8 +729,11 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
                                             floatx16 (&acc)[C::FM][C::FN], float* lds,
                                             int ea = 0, int eb = 0) {
   static_assert(!SAME || (C::BM == C::BN && PCOLS == QCOLS), "a shared panel is square");
-  if constexpr (F16 && C::NT == 512 && C::BM == 256 && C::BN == 256) {
-    mainloop_stagger<C, PCOLS, QCOLS, MASK, SAME>(A, lda, B, ldb, K, m0, n0, wm, wn, acc, lds, ea, eb);
+  // the staggered loop for row operands; with a column operand (one scalar
+  // load per value) it measured slower than the lockstep loop's two register
+  // stages (statistics of columns 5.63 -> 5.85 ms per launch at 1152 blocks of 1024^2)
+  if constexpr (F16 && C::NT == 512 && C::BM == 256 && C::BN == 256 && !PCOLS && !QCOLS) {
+    mainloop_stagger<C, MASK, SAME>(A, lda, B, ldb, K, m0, n0, wm, wn, acc, lds, ea, eb);
     return;
   }
   constexpr int NPL = F16 ? 2 : 3;                          // planes per operand
