@@ -1599,6 +1599,99 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+// sym_matvec for a factor of at most 256 columns (a single column chunk,
+// which would leave three waves idle): each wave runs down a quarter of the
+// rows (a lane: four consecutive columns, the loads of eight rows issued
+// together), and wave 0 adds the four partial columns in wave order from
+// part ([2][4][64] float4 in LDS). Every thread of the workgroup calls it.
+template <bool TWO>
+__device__ __forceinline__ void sym_matvec_small(const float* __restrict__ Af, int n, int nr,
+                                                 const float* x, const float* xu, float* y,
+                                                 float* yu, float4* part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane * 4;
+  const int rq = (nr + 3) / 4;
+  const int r0 = min(nr, wave * rq), r1 = min(nr, r0 + rq);
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f), t = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (j + 3 < nr) {
+    const float* col = Af + j;
+    int r = r0;
+    for (; r + 8 <= r1; r += 8) {
+      float4 a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = *reinterpret_cast<const float4*>(col + (int64_t)(r + u) * n);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float xr = x[r + u];
+        s.x += a[u].x * xr;
+        s.y += a[u].y * xr;
+        s.z += a[u].z * xr;
+        s.w += a[u].w * xr;
+        if constexpr (TWO) {
+          const float ur = xu[r + u];
+          t.x += a[u].x * ur;
+          t.y += a[u].y * ur;
+          t.z += a[u].z * ur;
+          t.w += a[u].w * ur;
+        }
+      }
+    }
+    for (; r < r1; ++r) {
+      const float4 a = *reinterpret_cast<const float4*>(col + (int64_t)r * n);
+      const float xr = x[r];
+      s.x += a.x * xr;
+      s.y += a.y * xr;
+      s.z += a.z * xr;
+      s.w += a.w * xr;
+      if constexpr (TWO) {
+        const float ur = xu[r];
+        t.x += a.x * ur;
+        t.y += a.y * ur;
+        t.z += a.z * ur;
+        t.w += a.w * ur;
+      }
+    }
+  } else if (j < nr) {
+    // the ragged last columns one by one
+    for (int r = r0; r < r1; ++r) {
+      const float* a = Af + (int64_t)r * n + j;
+      const float xr = x[r], ur = TWO ? xu[r] : 0.f;
+      s.x += a[0] * xr;
+      if (j + 1 < nr) s.y += a[1] * xr;
+      if (j + 2 < nr) s.z += a[2] * xr;
+      if constexpr (TWO) {
+        t.x += a[0] * ur;
+        if (j + 1 < nr) t.y += a[1] * ur;
+        if (j + 2 < nr) t.z += a[2] * ur;
+      }
+    }
+  }
+  part[wave * 64 + lane] = s;
+  if constexpr (TWO) part[256 + wave * 64 + lane] = t;
+  __syncthreads();
+  if (wave == 0 && j < nr) {
+    const float4 p0 = part[lane], p1 = part[64 + lane], p2 = part[128 + lane], p3 = part[192 + lane];
+    const float sv[4] = {(p0.x + p1.x) + (p2.x + p3.x), (p0.y + p1.y) + (p2.y + p3.y),
+                         (p0.z + p1.z) + (p2.z + p3.z), (p0.w + p1.w) + (p2.w + p3.w)};
+    float tv[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (TWO) {
+      const float4 q0 = part[256 + lane], q1 = part[320 + lane], q2 = part[384 + lane],
+                   q3 = part[448 + lane];
+      tv[0] = (q0.x + q1.x) + (q2.x + q3.x);
+      tv[1] = (q0.y + q1.y) + (q2.y + q3.y);
+      tv[2] = (q0.z + q1.z) + (q2.z + q3.z);
+      tv[3] = (q0.w + q1.w) + (q2.w + q3.w);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (j + k < nr) {
+        y[j + k] = sv[k];
+        if (TWO) yu[j + k] = tv[k];
+      }
+    }
+  }
+}
+
 // y = A x and, with TWO, yu = A xu for a symmetric factor A (row stride n,
 // real extent nr; x, xu, y, yu in LDS). Wave w owns the 256-column chunks
 // w, w + 4, ... (four consecutive columns a lane) and runs down every row, so
@@ -1698,6 +1791,12 @@ __device__ __forceinline__ void sym_matvec(const float* __restrict__ Af, int n, 
 // Scalar map of one coupled Newton iteration on an eigenvalue m of M scaled
 // by mu: f(mu m) = mu m ((p + 1 - mu m) / p)^p.
 __device__ __forceinline__ double newton_map(double m, int p, double mu) {
+  if (p == 4) {
+    // the same value without a division (dividing by 4 is exact): the
+    // bisection of the scale runs 80 of these in a dependent chain
+    const double y = mu * m, t = (5.0 - y) * 0.25;
+    return y * (((t * t) * t) * t);
+  }
   const double y = mu * m, t = (p + 1 - y) / p;
   double tp = 1.0;
   for (int i = 0; i < p; ++i) tp *= t;
@@ -1744,6 +1843,7 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
   __shared__ double red[4];
   __shared__ double red_inf[4];
   __shared__ double red_min[4];
+  __shared__ float4 part[2 * 4 * 64];  // partial products of factors of <= 256 columns
   // four vectors of the largest side (dynamic LDS, sized at launch): the top
   // power iteration's vector and product, the bottom one's (scale mode 3)
   extern __shared__ float4 vecs4[];  // float4: 16-byte aligned for the vector loads
@@ -1831,10 +1931,16 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ A,
     const int steps = cheb ? kPowerItersCheb : kPowerIters;
     for (int it = 0; it < steps; ++it) {
       if (it > 0) {
-        if (scaled)
+        if (nr <= 256) {
+          if (scaled)
+            sym_matvec_small<true>(Af, n, nr, v, u, w, wu, part);
+          else
+            sym_matvec_small<false>(Af, n, nr, v, nullptr, w, nullptr, part);
+        } else if (scaled) {
           sym_matvec<true>(Af, n, nr, v, u, w, wu);
-        else
+        } else {
           sym_matvec<false>(Af, n, nr, v, nullptr, w, nullptr);
+        }
       }
       __syncthreads();
       double nn = 0.0;
@@ -2111,13 +2217,21 @@ __device__ __forceinline__ float small_product(float* __restrict__ C, const floa
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-    for (int k = 0; k < n; ++k) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(P + k * n + r0);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(Q + k * n + c0);
+    // the LDS loads of eight k are issued together, then their FMAs (one k
+    // at a time waited on every load: 9 us per 64^3 product); n % 32 == 0
+    for (int k0 = 0; k0 < n; k0 += 8) {
+      f32x4 a[8], b[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int u = 0; u < 8; ++u) {
+        a[u] = *reinterpret_cast<const f32x4*>(P + (k0 + u) * n + r0);
+        b[u] = *reinterpret_cast<const f32x4*>(Q + (k0 + u) * n + c0);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[u][i], b[u][j], acc[i][j]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
