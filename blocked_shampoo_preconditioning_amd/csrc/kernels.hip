@@ -729,10 +729,14 @@ __device__ __forceinline__ void mainloop_x6(const float* __restrict__ A, int lda
                                             floatx16 (&acc)[C::FM][C::FN], float* lds,
                                             int ea = 0, int eb = 0) {
   static_assert(!SAME || (C::BM == C::BN && PCOLS == QCOLS), "a shared panel is square");
-  // the staggered loop for row operands; with a column operand (one scalar
-  // load per value) it measured slower than the lockstep loop's two register
-  // stages (statistics of columns 5.63 -> 5.85 ms per launch at 1152 blocks of 1024^2)
-  if constexpr (F16 && C::NT == 512 && C::BM == 256 && C::BN == 256 && !PCOLS && !QCOLS) {
+  // the staggered loop for row operands on full tiles. With a column operand
+  // (one scalar load per value) it measured slower than the lockstep loop's
+  // two register stages (statistics of columns 5.63 -> 5.85 ms per launch at
+  // 1152 blocks of 1024^2). On a diagonal tile (every wave masked) a slot
+  // lasts as long as the busiest role of its group, 4 + 7 fragments of MFMAs
+  // per K-tile, where lockstep pays the busiest SIMD's pair, 3 + 7.
+  if constexpr (F16 && C::NT == 512 && C::BM == 256 && C::BN == 256 && !PCOLS && !QCOLS &&
+                MASK == -1) {
     mainloop_stagger<C, MASK, SAME>(A, lda, B, ldb, K, m0, n0, wm, wn, acc, lds, ea, eb);
     return;
   }
