@@ -34,6 +34,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -67,6 +68,23 @@ def dtype_label(w):
     if w.dtype == "bf16":
         d += "; bf16 gradients and parameters, their statistics on the bf16 MFMA"
     return d
+
+
+def newton_kernel_desc(w):
+    """The Newton product kernel and tile the library's plan picks for the
+    workload: factors of side <= 64 iterate in one launch; otherwise the
+    symmetric products take 256x256 tiles on the fp16 split when both block
+    sides are multiples of 256 and at least 512, else the largest of 128, 64,
+    32 that divides both sides."""
+    br, bc = w.block_rows, w.block_cols
+    if max(br, bc) <= 64:
+        return "newton_small_kernel (one workgroup per factor, every iteration in one launch)"
+    if w.fp32_gemm == "split16" and br % 256 == 0 and bc % 256 == 0 and min(br, bc) >= 512:
+        tile = 256
+    else:
+        g = math.gcd(br, bc)
+        tile = 128 if g % 128 == 0 else 64 if g % 64 == 0 else 32
+    return f"newton_sym_kernel ({tile}x{tile} tiles, symmetric outputs)"
 
 
 def cpu_model():
@@ -510,8 +528,7 @@ def main():
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
         "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-        "kernel": f"newton_sym_kernel ({how}, 128x128 tiles, symmetric outputs; "
-                  f"{w.root_method} root products)",
+        "kernel": f"{newton_kernel_desc(w)} ({how}; {w.root_method} root products)",
         "launches": nw["launches"],
         "flops_per_launch": nw["flops"] / max(1, nw["launches"]),
         "avg_launch_ms": nw["ms"] / max(1, nw["launches"]),
