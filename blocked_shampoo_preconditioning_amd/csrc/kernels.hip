@@ -878,14 +878,17 @@ struct SymWave<C, false> {
   }
 };
 
-template <class C>
+// The symmetric products' main-loop dispatch by the wave's fragment mask
+// (-1 off the diagonal, the roles of a diagonal tile on it). FULL: known to
+// be an off-diagonal tile.
+template <class C, bool FULL>
 __device__ __forceinline__ void mainloop_sym(const float* __restrict__ P,
                                              const float* __restrict__ Q, int M, int N, int K,
                                              int m0, int n0, floatx16 (&acc)[C::FM][C::FN],
                                              float* lds, const SymWave<C>& sw) {
   constexpr int kUpper = upper_mask<C::FM, C::FN>();
   constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
-  if (sw.mask == -1)
+  if (FULL || sw.mask == -1)
     mainloop_w<C>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
   else if (sw.mask == kUpper)
     mainloop_w<C, kUpper>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
@@ -897,16 +900,16 @@ __device__ __forceinline__ void mainloop_sym(const float* __restrict__ P,
     mainloop_w<C, 0>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
 }
 
-template <class C>
+template <class C, bool FULL>
 __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X, int K, int m0,
                                                   int n0, floatx16 (&acc)[C::FM][C::FN],
                                                   float* lds, const SymWave<C>& sw) {
-  if constexpr (C::FM != C::FN) {
+  if (FULL || sw.mask == -1) {
+    mainloop_bf16<C>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
+  } else if constexpr (C::FM != C::FN) {
     using W = SymWave<C>;
-    // a diagonal tile (every wave's mask is not -1 there) reads one panel
-    if (sw.mask == -1)
-      mainloop_bf16<C>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
-    else if (sw.mask == W::kCross0)
+    // a diagonal tile reads one panel
+    if (sw.mask == W::kCross0)
       mainloop_bf16<C, W::kCross0, true>(X, K, m0, m0, sw.wm, sw.wn, acc, lds);
     else if (sw.mask == W::kCross1)
       mainloop_bf16<C, W::kCross1, true>(X, K, m0, m0, sw.wm, sw.wn, acc, lds);
@@ -918,9 +921,7 @@ __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X
   } else {
   constexpr int kUpper = upper_mask<C::FM, C::FN>();
   constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
-  if (sw.mask == -1)
-    mainloop_bf16<C>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
-  else if (sw.mask == kUpper)
+  if (sw.mask == kUpper)
     mainloop_bf16<C, kUpper>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
   else if (C::FM >= 2 && sw.mask == kTop)
     mainloop_bf16<C, kTop>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
@@ -934,20 +935,20 @@ __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X
 // COLS: both operands stored [K][M] (m contiguous, row stride M), as the
 // statistics of a matrix's columns read the packed block; otherwise rows
 // with k contiguous (row stride K).
-template <class C, bool COLS, bool F16 = false>
+template <class C, bool COLS, bool FULL, bool F16 = false>
 __device__ __forceinline__ void mainloop_sym_x6(const float* __restrict__ A,
                                                 const float* __restrict__ B, int M, int K, int m0,
                                                 int n0, floatx16 (&acc)[C::FM][C::FN],
                                                 float* lds, const SymWave<C>& sw, int ea = 0,
                                                 int eb = 0) {
-  if constexpr (C::FM != C::FN) {
+  const int ld = COLS ? M : K;
+  if (FULL || sw.mask == -1) {
+    mainloop_x6<C, COLS, COLS, -1, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
+  } else if constexpr (C::FM != C::FN) {
     using W = SymWave<C>;
-    const int ld = COLS ? M : K;
     // a diagonal tile of a matrix times itself: one panel serves both operands
     const bool same = A == B && ea == eb;
-    if (sw.mask == -1)
-      mainloop_x6<C, COLS, COLS, -1, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
-    else if (same) {
+    if (same) {
       if (sw.mask == W::kCross0)
         mainloop_x6<C, COLS, COLS, W::kCross0, F16, true>(A, ld, A, ld, K, m0, m0, sw.wm, sw.wn, acc, lds, ea, ea);
       else if (sw.mask == W::kCross1)
@@ -968,10 +969,7 @@ __device__ __forceinline__ void mainloop_sym_x6(const float* __restrict__ A,
   } else {
   constexpr int kUpper = upper_mask<C::FM, C::FN>();
   constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
-  const int ld = COLS ? M : K;
-  if (sw.mask == -1)
-    mainloop_x6<C, COLS, COLS, -1, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
-  else if (sw.mask == kUpper)
+  if (sw.mask == kUpper)
     mainloop_x6<C, COLS, COLS, kUpper, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
   else if (C::FM >= 2 && sw.mask == kTop)
     mainloop_x6<C, COLS, COLS, kTop, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
@@ -1028,6 +1026,166 @@ constexpr int lds_floats() {
   return path_f16(PATH) ? C::LDS_SPLITH : path_split(PATH) ? C::LDS_SPLIT : C::LDS_FLOATS;
 }
 
+// The main loop of one tile of a symmetric product on its operand path;
+// FULL: an off-diagonal tile.
+template <class C, int PATH, bool FULL>
+__device__ __forceinline__ void sym_mainloop(const GemmProblem& pb, int f, int m0, int n0,
+                                             floatx16 (&acc)[C::FM][C::FN], float* lds,
+                                             const SymWave<C>& sw) {
+  if constexpr (PATH == kPathBF16) {
+    mainloop_sym_bf16<C, FULL>(pb.Xh + (size_t)f * pb.sXh, pb.K, m0, n0, acc, lds, sw);
+  } else if constexpr (path_f16(PATH)) {
+    const int ea = f16_exp(pb.mP[f]), eb = f16_exp(pb.mQ[f]);
+    mainloop_sym_x6<C, path_cols(PATH), FULL, true>(pb.P + (size_t)f * pb.sP,
+                                                    pb.Q + (size_t)f * pb.sQ, pb.M, pb.K, m0, n0,
+                                                    acc, lds, sw, ea, eb);
+    unscale_acc<C>(acc, -(ea + eb));
+  } else if constexpr (path_split(PATH)) {
+    // operands by rows, or (statistics of a matrix's columns) by columns
+    mainloop_sym_x6<C, path_cols(PATH), FULL>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ,
+                                              pb.M, pb.K, m0, n0, acc, lds, sw);
+  } else {
+    mainloop_sym<C, FULL>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0,
+                          n0, acc, lds, sw);
+  }
+}
+
+// The symmetric epilogue over a wave's fragments (see sym_product): C =
+// alpha acc + beta D + beta2 D2 (+ the Chebyshev terms) + gamma I on and
+// above the diagonal and the mirror below it. diag: the tile holds the
+// diagonal (elements below it are not stored, the identity term applies on
+// it); off the diagonal every element lies strictly above it, and a branch
+// per fragment takes stores without per-element tests (two instantiations
+// of the whole epilogue, one per kind of tile, ran out of registers). Offsets
+// are 32-bit (a factor has at most 4096^2 elements): one 32-bit offset per
+// element instead of 64-bit index arithmetic.
+// Adds this lane's share of ||C - I||_F^2 to rs and of max |C| to mx, in the
+// order of the elements.
+template <class C, int PATH, bool TERMS>
+__device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN],
+                                             const SymWave<C>& sw, bool diag, int m0, int n0, int N,
+                                             float* Cb, const float* Db, const float* D2b,
+                                             const float* E1b, const float* E2b, float e_alpha,
+                                             float e_beta, float e_beta2, float e_gamma,
+                                             float e_t1, float e_t2, float& rs, float& mx) {
+  constexpr bool BATCH = PATH == kPathSplit || PATH == kPathSplitH;
+  constexpr int NF = C::FM * C::FN;
+  constexpr int GF = BATCH && NF >= 2 ? 2 : 1;  // fragments per batch
+  constexpr int HOIST = BATCH ? 16 : 4;
+  // The affine terms are loaded before their stores: the stores may alias
+  // them as far as the compiler knows (the statistics update in place), which
+  // would otherwise hold every load behind the store before it. No store
+  // below targets an element another lane reads here. The split paths with
+  // row operands have the registers for two whole fragments per batch (one
+  // memory round trip per two fragments); the others load HOIST registers of
+  // one fragment at a time.
+#pragma unroll
+  for (int q0 = 0; q0 < NF; q0 += GF) {
+    float dv[GF][HOIST], d2v[GF][HOIST], ev[GF][TERMS ? HOIST : 1];
+    if constexpr (BATCH) {
+#pragma unroll
+      for (int q = 0; q < GF; ++q) {
+        const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
+        if (!((sw.mask >> (i * C::FN + j)) & 1)) continue;  // wave-uniform
+        const int col = frag_col_w<C>(n0, sw.wn, j);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t o = (uint32_t)(frag_row_w<C>(m0, sw.wm, i, r) * N + col);
+          dv[q][r] = Db != nullptr ? Db[o] : 0.f;
+          d2v[q][r] = D2b != nullptr ? D2b[o] : 0.f;
+          if constexpr (TERMS)
+            ev[q][r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) + (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < GF; ++q) {
+      const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
+      if (!((sw.mask >> (i * C::FN + j)) & 1)) continue;  // wave-uniform
+      const int col = frag_col_w<C>(n0, sw.wn, j);
+      // off the diagonal (a uniform test per fragment) every element is stored
+      // and mirrored, the identity term never applies: the same arithmetic
+      // without the per-element tests of a diagonal tile
+      if (!TERMS && !diag) {  // (the Chebyshev products' registers keep them on one path)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          if constexpr (!BATCH) {
+            if ((4 * g4) % HOIST == 0) {
+#pragma unroll
+              for (int r = 0; r < HOIST; ++r) {
+                const uint32_t o = (uint32_t)(frag_row_w<C>(m0, sw.wm, i, 4 * g4 + r) * N + col);
+                dv[q][r] = Db != nullptr ? Db[o] : 0.f;
+                d2v[q][r] = D2b != nullptr ? D2b[o] : 0.f;
+                if constexpr (TERMS)
+                  ev[q][r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) +
+                             (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
+              }
+            }
+          }
+          const int row0 = frag_row_w<C>(m0, sw.wm, i, 4 * g4);
+          f32x4 v;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int h = (4 * g4 + qq) % HOIST;
+            float x = e_alpha * acc[i][j][4 * g4 + qq];
+            x += e_beta * dv[q][h];
+            x += e_beta2 * d2v[q][h];
+            if constexpr (TERMS) x += ev[q][h];
+            v[qq] = x;
+            Cb[(uint32_t)((row0 + qq) * N + col)] = x;
+            rs += 2.f * x * x;
+            if constexpr (path_f16(PATH)) mx = fmaxf(mx, fabsf(x));
+          }
+          *reinterpret_cast<f32x4*>(Cb + (uint32_t)(col * N + row0)) = v;
+        }
+        continue;
+      }
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        if constexpr (!BATCH) {
+          if ((4 * g4) % HOIST == 0) {
+#pragma unroll
+            for (int r = 0; r < HOIST; ++r) {
+              const uint32_t o = (uint32_t)(frag_row_w<C>(m0, sw.wm, i, 4 * g4 + r) * N + col);
+              dv[q][r] = Db != nullptr ? Db[o] : 0.f;
+              d2v[q][r] = D2b != nullptr ? D2b[o] : 0.f;
+              if constexpr (TERMS)
+                ev[q][r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) +
+                           (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
+            }
+          }
+        }
+        const int row0 = frag_row_w<C>(m0, sw.wm, i, 4 * g4);
+        f32x4 v;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int row = row0 + qq;
+          const int h = (4 * g4 + qq) % HOIST;
+          float x = e_alpha * acc[i][j][4 * g4 + qq];
+          x += e_beta * dv[q][h];
+          x += e_beta2 * d2v[q][h];
+          if constexpr (TERMS) x += ev[q][h];
+          if (diag && row == col) x += e_gamma;
+          v[qq] = x;
+          if (!diag || row <= col) {
+            Cb[(uint32_t)(row * N + col)] = x;
+            const float d = x - (diag && row == col ? 1.f : 0.f);
+            rs += (diag && row == col ? 1.f : 2.f) * d * d;
+            if constexpr (path_f16(PATH)) mx = fmaxf(mx, fabsf(x));
+          }
+        }
+        if (!diag || row0 + 3 < col) {
+          *reinterpret_cast<f32x4*>(Cb + (uint32_t)(col * N + row0)) = v;
+        } else {
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            if (row0 + qq < col) Cb[(uint32_t)(col * N + row0 + qq)] = v[qq];
+        }
+      }
+    }
+  }
+}
+
 // TERMS: the epilogue also adds coef[4] E1 + coef[5] E2 (the Chebyshev giant
 // steps); a separate instantiation, so the other products keep their registers.
 template <class C, int PATH = kPathF32, bool TERMS = false>
@@ -1061,25 +1219,8 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const bool diag = (ti == tj);
   const SymWave<C> sw(diag);
   floatx16 acc[C::FM][C::FN];
-  if constexpr (PATH == kPathBF16) {
-    mainloop_sym_bf16<C>(pb.Xh + (size_t)f * pb.sXh, pb.K, m0, n0, acc, lds, sw);
-  } else if constexpr (path_f16(PATH)) {
-    const int ea = f16_exp(pb.mP[f]), eb = f16_exp(pb.mQ[f]);
-    mainloop_sym_x6<C, path_cols(PATH), true>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ,
-                                              pb.M, pb.K, m0, n0, acc, lds, sw, ea, eb);
-    unscale_acc<C>(acc, -(ea + eb));
-  } else if constexpr (path_split(PATH)) {
-    // operands by rows, or (statistics of a matrix's columns) by columns
-    mainloop_sym_x6<C, path_cols(PATH)>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ,
-                                        pb.M, pb.K, m0, n0, acc, lds, sw);
-  } else
-    mainloop_sym<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0, n0,
-                    acc, lds, sw);
+  sym_mainloop<C, PATH, false>(pb, f, m0, n0, acc, lds, sw);
 
-  // Epilogue: C = alpha acc + beta D + gamma I on and above the diagonal, and
-  // the mirror below it. The four registers 4g..4g+3 of a lane hold four
-  // consecutive rows of one column, i.e. four consecutive columns of the
-  // mirrored row, written as one 16-byte store.
   float* Cb = pb.C + (size_t)f * pb.sC;
   const float* Db = pb.D != nullptr ? pb.D + (size_t)f * pb.sD : nullptr;
   const float* D2b = pb.D2 != nullptr ? pb.D2 + (size_t)f * pb.sD2 : nullptr;
@@ -1101,85 +1242,8 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const int N = pb.N;
   float rs = 0.f;
   float mx = 0.f;  // largest |value| stored (fp16 split: the result's maximum)
-  // The affine terms are loaded before their stores: the stores may alias
-  // them as far as the compiler knows (the statistics update in place), which
-  // would otherwise hold every load behind the store before it. No store
-  // below targets an element another lane reads here. The split paths with
-  // row operands have the registers for two whole fragments per batch (one
-  // memory round trip per two fragments); the others load HOIST registers of
-  // one fragment at a time.
-  constexpr bool BATCH = PATH == kPathSplit || PATH == kPathSplitH;
-  constexpr int NF = C::FM * C::FN;
-  constexpr int GF = BATCH && NF >= 2 ? 2 : 1;  // fragments per batch
-  constexpr int HOIST = BATCH ? 16 : 4;
-#pragma unroll
-  for (int q0 = 0; q0 < NF; q0 += GF) {
-    float dv[GF][HOIST], d2v[GF][HOIST], ev[GF][TERMS ? HOIST : 1];
-    if constexpr (BATCH) {
-#pragma unroll
-      for (int q = 0; q < GF; ++q) {
-        const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
-        if (!((sw.mask >> (i * C::FN + j)) & 1)) continue;  // wave-uniform
-        const int col = frag_col_w<C>(n0, sw.wn, j);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const size_t o = (size_t)frag_row_w<C>(m0, sw.wm, i, r) * N + col;
-          dv[q][r] = Db != nullptr ? Db[o] : 0.f;
-          d2v[q][r] = D2b != nullptr ? D2b[o] : 0.f;
-          if constexpr (TERMS)
-            ev[q][r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) + (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < GF; ++q) {
-      const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
-      if (!((sw.mask >> (i * C::FN + j)) & 1)) continue;  // wave-uniform
-      const int col = frag_col_w<C>(n0, sw.wn, j);
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        if constexpr (!BATCH) {
-          if ((4 * g4) % HOIST == 0) {
-#pragma unroll
-            for (int r = 0; r < HOIST; ++r) {
-              const size_t o = (size_t)frag_row_w<C>(m0, sw.wm, i, 4 * g4 + r) * N + col;
-              dv[q][r] = Db != nullptr ? Db[o] : 0.f;
-              d2v[q][r] = D2b != nullptr ? D2b[o] : 0.f;
-              if constexpr (TERMS)
-                ev[q][r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) +
-                           (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
-            }
-          }
-        }
-        const int row0 = frag_row_w<C>(m0, sw.wm, i, 4 * g4);
-        f32x4 v;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int row = row0 + qq;
-          const int h = (4 * g4 + qq) % HOIST;
-          float x = e_alpha * acc[i][j][4 * g4 + qq];
-          x += e_beta * dv[q][h];
-          x += e_beta2 * d2v[q][h];
-          if constexpr (TERMS) x += ev[q][h];
-          if (row == col) x += e_gamma;
-          v[qq] = x;
-          if (!diag || row <= col) {
-            Cb[(size_t)row * N + col] = x;
-            const float d = x - (row == col ? 1.f : 0.f);
-            rs += (row == col ? 1.f : 2.f) * d * d;
-            if constexpr (path_f16(PATH)) mx = fmaxf(mx, fabsf(x));
-          }
-        }
-        if (!diag || row0 + 3 < col) {
-          *reinterpret_cast<f32x4*>(Cb + (size_t)col * N + row0) = v;
-        } else {
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq)
-            if (row0 + qq < col) Cb[(size_t)col * N + row0 + qq] = v[qq];
-        }
-      }
-    }
-  }
+  sym_epilogue<C, PATH, TERMS>(acc, sw, diag, m0, n0, N, Cb, Db, D2b, E1b, E2b, e_alpha, e_beta,
+                               e_beta2, e_gamma, e_t1, e_t2, rs, mx);
   if constexpr (path_f16(PATH))
     if (pb.mC != nullptr) raise_max(pb.mC + f, mx, pb.ver);
   if (pb.resid != nullptr) {
