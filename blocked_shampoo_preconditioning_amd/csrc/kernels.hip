@@ -879,16 +879,15 @@ struct SymWave<C, false> {
 };
 
 // The symmetric products' main-loop dispatch by the wave's fragment mask
-// (-1 off the diagonal, the roles of a diagonal tile on it). FULL: known to
-// be an off-diagonal tile.
-template <class C, bool FULL>
+// (-1 off the diagonal, the roles of a diagonal tile on it).
+template <class C>
 __device__ __forceinline__ void mainloop_sym(const float* __restrict__ P,
                                              const float* __restrict__ Q, int M, int N, int K,
                                              int m0, int n0, floatx16 (&acc)[C::FM][C::FN],
                                              float* lds, const SymWave<C>& sw) {
   constexpr int kUpper = upper_mask<C::FM, C::FN>();
   constexpr int kTop = half_mask<C::FM, C::FN>(false), kBottom = half_mask<C::FM, C::FN>(true);
-  if (FULL || sw.mask == -1)
+  if (sw.mask == -1)
     mainloop_w<C>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
   else if (sw.mask == kUpper)
     mainloop_w<C, kUpper>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
@@ -900,11 +899,11 @@ __device__ __forceinline__ void mainloop_sym(const float* __restrict__ P,
     mainloop_w<C, 0>(P, Q, M, N, K, m0, n0, sw.wm, sw.wn, acc, lds);
 }
 
-template <class C, bool FULL>
+template <class C>
 __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X, int K, int m0,
                                                   int n0, floatx16 (&acc)[C::FM][C::FN],
                                                   float* lds, const SymWave<C>& sw) {
-  if (FULL || sw.mask == -1) {
+  if (sw.mask == -1) {
     mainloop_bf16<C>(X, K, m0, n0, sw.wm, sw.wn, acc, lds);
   } else if constexpr (C::FM != C::FN) {
     using W = SymWave<C>;
@@ -935,14 +934,14 @@ __device__ __forceinline__ void mainloop_sym_bf16(const uint16_t* __restrict__ X
 // COLS: both operands stored [K][M] (m contiguous, row stride M), as the
 // statistics of a matrix's columns read the packed block; otherwise rows
 // with k contiguous (row stride K).
-template <class C, bool COLS, bool FULL, bool F16 = false>
+template <class C, bool COLS, bool F16 = false>
 __device__ __forceinline__ void mainloop_sym_x6(const float* __restrict__ A,
                                                 const float* __restrict__ B, int M, int K, int m0,
                                                 int n0, floatx16 (&acc)[C::FM][C::FN],
                                                 float* lds, const SymWave<C>& sw, int ea = 0,
                                                 int eb = 0) {
   const int ld = COLS ? M : K;
-  if (FULL || sw.mask == -1) {
+  if (sw.mask == -1) {
     mainloop_x6<C, COLS, COLS, -1, F16>(A, ld, B, ld, K, m0, n0, sw.wm, sw.wn, acc, lds, ea, eb);
   } else if constexpr (C::FM != C::FN) {
     using W = SymWave<C>;
@@ -1026,26 +1025,25 @@ constexpr int lds_floats() {
   return path_f16(PATH) ? C::LDS_SPLITH : path_split(PATH) ? C::LDS_SPLIT : C::LDS_FLOATS;
 }
 
-// The main loop of one tile of a symmetric product on its operand path;
-// FULL: an off-diagonal tile.
-template <class C, int PATH, bool FULL>
+// The main loop of one tile of a symmetric product on its operand path.
+template <class C, int PATH>
 __device__ __forceinline__ void sym_mainloop(const GemmProblem& pb, int f, int m0, int n0,
                                              floatx16 (&acc)[C::FM][C::FN], float* lds,
                                              const SymWave<C>& sw) {
   if constexpr (PATH == kPathBF16) {
-    mainloop_sym_bf16<C, FULL>(pb.Xh + (size_t)f * pb.sXh, pb.K, m0, n0, acc, lds, sw);
+    mainloop_sym_bf16<C>(pb.Xh + (size_t)f * pb.sXh, pb.K, m0, n0, acc, lds, sw);
   } else if constexpr (path_f16(PATH)) {
     const int ea = f16_exp(pb.mP[f]), eb = f16_exp(pb.mQ[f]);
-    mainloop_sym_x6<C, path_cols(PATH), FULL, true>(pb.P + (size_t)f * pb.sP,
+    mainloop_sym_x6<C, path_cols(PATH), true>(pb.P + (size_t)f * pb.sP,
                                                     pb.Q + (size_t)f * pb.sQ, pb.M, pb.K, m0, n0,
                                                     acc, lds, sw, ea, eb);
     unscale_acc<C>(acc, -(ea + eb));
   } else if constexpr (path_split(PATH)) {
     // operands by rows, or (statistics of a matrix's columns) by columns
-    mainloop_sym_x6<C, path_cols(PATH), FULL>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ,
+    mainloop_sym_x6<C, path_cols(PATH)>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ,
                                               pb.M, pb.K, m0, n0, acc, lds, sw);
   } else {
-    mainloop_sym<C, FULL>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0,
+    mainloop_sym<C>(pb.P + (size_t)f * pb.sP, pb.Q + (size_t)f * pb.sQ, pb.M, pb.N, pb.K, m0,
                           n0, acc, lds, sw);
   }
 }
@@ -1219,7 +1217,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const bool diag = (ti == tj);
   const SymWave<C> sw(diag);
   floatx16 acc[C::FM][C::FN];
-  sym_mainloop<C, PATH, false>(pb, f, m0, n0, acc, lds, sw);
+  sym_mainloop<C, PATH>(pb, f, m0, n0, acc, lds, sw);
 
   float* Cb = pb.C + (size_t)f * pb.sC;
   const float* Db = pb.D != nullptr ? pb.D + (size_t)f * pb.sD : nullptr;
