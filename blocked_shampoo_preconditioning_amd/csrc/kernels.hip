@@ -1061,7 +1061,8 @@ __device__ __forceinline__ void sym_mainloop(const GemmProblem& pb, int f, int m
 // order of the elements.
 template <class C, int PATH, bool TERMS>
 __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN],
-                                             const SymWave<C>& sw, bool diag, int m0, int n0, int N,
+                                             const SymWave<C>& sw, bool diag, float* lds, int m0,
+                                             int n0, int N,
                                              float* Cb, const float* Db, const float* D2b,
                                              const float* E1b, const float* E2b, float e_alpha,
                                              float e_beta, float e_beta2, float e_gamma,
@@ -1070,6 +1071,15 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
   constexpr int NF = C::FM * C::FN;
   constexpr int GF = BATCH && NF >= 2 ? 2 : 1;  // fragments per batch
   constexpr int HOIST = BATCH ? 16 : 4;
+  // Off-diagonal mirrors pass through a wave-private 32 x 32 transpose buffer
+  // (rows of kTP floats: the 16-byte writes of 16 lanes cover the 64 banks
+  // once) and leave as whole 128-byte row segments instead of 16 bytes in
+  // each of 64 rows. Every main loop ends with a barrier after its last LDS
+  // read; the buffers start after the residual partials (lds[0..7]).
+  constexpr int kTP = 36;
+  static_assert(64 + (C::NT / 64) * 32 * kTP <= lds_floats<C, PATH>(), "LDS of the transpose buffers");
+  const int lane = threadIdx.x & 63;
+  float* tw = lds + 64 + (threadIdx.x >> 6) * 32 * kTP;
   // The affine terms are loaded before their stores: the stores may alias
   // them as far as the compiler knows (the statistics update in place), which
   // would otherwise hold every load behind the store before it. No store
@@ -1134,7 +1144,15 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
             rs += 2.f * x * x;
             if constexpr (path_f16(PATH)) mx = fmaxf(mx, fabsf(x));
           }
-          *reinterpret_cast<f32x4*>(Cb + (uint32_t)(col * N + row0)) = v;
+          *reinterpret_cast<f32x4*>(tw + (lane & 31) * kTP + g4 * 8 + (lane >> 5) * 4) = v;
+        }
+        // the mirror: row cbase + rr of the result, columns rbase + cc..+3
+        const int rbase = m0 + sw.wm * 32 * C::FM + i * 32, cbase = col - (lane & 31);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int rr = it * 8 + (lane >> 3), cc = (lane & 7) * 4;
+          *reinterpret_cast<f32x4*>(Cb + (uint32_t)((cbase + rr) * N + rbase + cc)) =
+              *reinterpret_cast<const f32x4*>(tw + rr * kTP + cc);
         }
         continue;
       }
@@ -1240,8 +1258,8 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   const int N = pb.N;
   float rs = 0.f;
   float mx = 0.f;  // largest |value| stored (fp16 split: the result's maximum)
-  sym_epilogue<C, PATH, TERMS>(acc, sw, diag, m0, n0, N, Cb, Db, D2b, E1b, E2b, e_alpha, e_beta,
-                               e_beta2, e_gamma, e_t1, e_t2, rs, mx);
+  sym_epilogue<C, PATH, TERMS>(acc, sw, diag, lds, m0, n0, N, Cb, Db, D2b, E1b, E2b, e_alpha,
+                               e_beta, e_beta2, e_gamma, e_t1, e_t2, rs, mx);
   if constexpr (path_f16(PATH))
     if (pb.mC != nullptr) raise_max(pb.mC + f, mx, pb.ver);
   if (pb.resid != nullptr) {
