@@ -602,6 +602,38 @@ def test_fp32_gemm_paths_every_block(gemm, block, shapes):
         sh.close()
 
 
+@pytest.mark.parametrize("gemm", ["f32", "split", "split16"])
+@pytest.mark.parametrize("block,shapes,dtype", [
+    ((1024, 1024), ((1024, 2048),), "f32"),  # 256-tiles on the fp16 split: staggered full tiles, diagonal roles
+    ((512, 512), ((1100, 600),), "f32"),     # 256-tiles with ragged tails
+    ((256, 256), ((300, 520),), "f32"),      # 128-tiles
+    ((64, 32), ((70, 45),), "f32"),          # 32-tiles and the one-launch Newton
+    ((512, 512), ((1100, 600),), "bf16"),    # bf16 statistics on 256-tiles
+])
+def test_statistics_and_roots_exactly_symmetric(gemm, block, shapes, dtype):
+    """Every symmetric product stores the upper triangle of its result and
+    mirrors it (off-diagonal fragments through the epilogue's LDS transpose,
+    diagonal tiles element by element), so the statistics and the roots are
+    symmetric bit for bit: after three steps with two refreshes, L, R, X_L and
+    X_R of every block (padding included) equal their transposes exactly."""
+    w = workload("gpt_small_b256", shapes=shapes, block_rows=block[0], block_cols=block[1],
+                 root_every=2, steps=3, seed=7, fp32_gemm=gemm, dtype=dtype)
+    log(f"exact symmetry: gemm {gemm} block {block} {dtype}")
+    src = synth.GradientSource(w, device="cuda")
+    params = src.init_params()
+    sh = make_shampoo(w)
+    for t in range(1, 4):
+        sh.step(params, src.grads(t))
+    torch.cuda.synchronize()
+    for name, (A, B) in (("statistics", sh.stats()), ("roots", sh.roots())):
+        for X, side in ((A, "left"), (B, "right")):
+            assert bool(torch.isfinite(X).all()), (name, side)
+            bad = (X != X.transpose(1, 2)).flatten(1).sum(1)
+            assert int(bad.sum()) == 0, (name, side, bad.nonzero().flatten().tolist()[:8])
+    assert sh.n_diverged() == 0
+    sh.close()
+
+
 def test_split_products_have_fp32_accuracy():
     """One step with roots on both product paths, same gradients (rows scaled
     over two decades, so the statistics span four): the statistics against
