@@ -1202,28 +1202,10 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
   }
 }
 
-// TERMS: the epilogue also adds coef[4] E1 + coef[5] E2 (the Chebyshev giant
-// steps); a separate instantiation, so the other products keep their registers.
-template <class C, int PATH = kPathF32, bool TERMS = false>
-__device__ __forceinline__ void sym_product(const GemmLaunch& g) {
-  __shared__ float lds[lds_floats<C, PATH>()];
-  float* red = lds;  // residual partials reuse the operand tiles after the K loop
-  const GemmProblem& pb = g.p[blockIdx.y];
-  const int T = pb.M / C::BM;
-  const int ntile = T * (T + 1) / 2;
-  // Matrices are dealt to the XCDs round-robin (matrix f on XCD f % 8) and
-  // each XCD runs the tiles of its matrices one matrix after the other, so an
-  // L2 serves all tiles of a matrix and, when converged factors drop out of a
-  // Newton launch, every XCD keeps its share of the remaining ones.
-  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-  const int j = idx / ntile;
-  const int tile = idx - j * ntile;
-  const int f = j * 8 + xcd;
-  if (f >= pb.batch) return;
-  if (pb.status != nullptr) {
-    const int st = pb.status[pb.f0 + f];
-    if (st != 0 && !(pb.also_status != 0 && st == pb.also_status)) return;
-  }
+// One tile (ti <= tj) of a symmetric product for factor f.
+template <class C, int PATH, bool TERMS>
+__device__ __forceinline__ void sym_tile(const GemmProblem& pb, int f, int tile, int T, float* lds,
+                                         float* red) {
   int t = tile, ti = 0;
   while (t >= T - ti) {
     t -= T - ti;
@@ -1275,6 +1257,85 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   }
 }
 
+
+// Live-factor table of a persistent symmetric launch, one byte per factor
+// slot of the workgroup's XCD; problems with more slots read the status words
+// per tile instead.
+constexpr int kMaxSlots = 4096;
+
+// Persistent Newton products on 256-tiles only: they hold one workgroup per
+// CU and the whole register file either way, while the loop's extra live
+// values would cost the smaller tiles a wave per SIMD.
+template <class C>
+constexpr bool kPersistSym = C::NT == 512;
+
+// TERMS: the epilogue also adds coef[4] E1 + coef[5] E2 (the Chebyshev giant
+// steps); a separate instantiation, so the other products keep their registers.
+//
+// Matrices are dealt to the XCDs round-robin (matrix f on XCD f % 8; the XCD
+// workgroup b runs on is b % 8) and each XCD runs the units (matrix slot j,
+// tile) of its matrices in order, so an L2 serves all tiles of a matrix and,
+// when converged factors drop out of a Newton launch, every XCD keeps its
+// share of the remaining ones. Without PERSIST a workgroup takes one unit.
+// PERSIST (the Newton products, whose launches lose factors as they
+// converge): the grid holds at most as
+// many workgroups as the device runs at once, each taking every (gridDim.x /
+// 8)-th unit of its XCD, so a launch whose factors have all stopped costs one
+// status read per factor instead of the dispatch of every tile.
+template <class C, int PATH = kPathF32, bool TERMS = false, bool PERSIST = false>
+__device__ __forceinline__ void sym_product(const GemmLaunch& g) {
+  __shared__ float lds[lds_floats<C, PATH>()];
+  float* red = lds;  // residual partials reuse the operand tiles after the K loop
+  const GemmProblem& pb = g.p[blockIdx.y];
+  const int T = pb.M / C::BM;
+  const int ntile = T * (T + 1) / 2;
+  const int xcd = blockIdx.x & 7;
+  if constexpr (!PERSIST) {
+    const int u = blockIdx.x >> 3;
+    const int j = u / ntile;
+    const int tile = u - j * ntile;
+    const int f = j * 8 + xcd;
+    if (f >= pb.batch) return;
+    if (pb.status != nullptr) {
+      const int st = pb.status[pb.f0 + f];
+      if (st != 0 && !(pb.also_status != 0 && st == pb.also_status)) return;
+    }
+    sym_tile<C, PATH, TERMS>(pb, f, tile, T, lds, red);
+  } else {
+    // live-factor table, one byte per slot of this XCD; problems with more
+    // slots read the status words per tile instead
+    __shared__ uint8_t live[kMaxSlots];
+    const int nslot = (pb.batch - xcd + 7) / 8;  // slots j: factor f = 8 j + xcd < batch
+    if (nslot <= 0) return;
+    const bool filter = pb.status != nullptr;
+    const bool table = filter && nslot <= kMaxSlots;
+    if (table) {
+      int n = 0;
+      for (int j = threadIdx.x; j < nslot; j += C::NT) {
+        const int st = pb.status[pb.f0 + j * 8 + xcd];
+        const int a = st == 0 || (pb.also_status != 0 && st == pb.also_status);
+        live[j] = (uint8_t)a;
+        n += a;
+      }
+      if (!__syncthreads_or(n)) return;
+    }
+    const int units = nslot * ntile;
+    for (int u = blockIdx.x >> 3; u < units; u += gridDim.x >> 3) {
+      const int j = u / ntile;
+      const int tile = u - j * ntile;
+      const int f = j * 8 + xcd;
+      if (table && !live[j]) continue;
+      if (filter && !table) {
+        const int st = pb.status[pb.f0 + f];
+        if (st != 0 && !(pb.also_status != 0 && st == pb.also_status)) continue;
+      }
+      // the previous tile's last LDS uses (transpose buffers, partials) end here
+      __syncthreads();
+      sym_tile<C, PATH, TERMS>(pb, f, tile, T, lds, red);
+    }
+  }
+}
+
 // Statistics: L <- beta2 L + g Gp Gp^T, R <- beta2 R + g Gp^T Gp (fp32 path:
 // P = Q = GpT for L, Gp for R; split path: the row operands, Gp for L and
 // GpT for R).
@@ -1294,7 +1355,7 @@ __global__ __launch_bounds__(C::NT, C::NT == 512 ? 2 : 3) void syrk_bf16_kernel(
 // operand is symmetric, so P and Q serve as row operands as they are.
 template <class C, int PATH>
 __global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void newton_sym_kernel(GemmLaunch g) {
-  sym_product<C, PATH>(g);
+  sym_product<C, PATH, false, kPersistSym<C>>(g);
 }
 
 // The product's main loop on either path: fp32 (C = P^T Q, P [K][M] and
@@ -2658,6 +2719,43 @@ int grid_sym(const GemmLaunch& g) {
   }
   return mx;
 }
+// Workgroups of a kernel that the current device holds at once, rounded down
+// to a multiple of the 8 XCDs (0 if the runtime cannot tell); cached per
+// kernel and device.
+int resident_grid(const void* kernel, int nt) {
+  static std::mutex mu;
+  struct Entry {
+    const void* k;
+    int dev, cap;
+  };
+  static Entry cache[256];
+  static int n = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (cache[i].k == kernel && cache[i].dev == dev) return cache[i].cap;
+  int cus = 0, occ = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, nt, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int cap = occ * cus / 8 * 8;
+  if (n < 256) cache[n++] = Entry{kernel, dev, cap};
+  return cap;
+}
+
+// Grid of a persistent symmetric launch: one workgroup per unit (slot, tile)
+// when the device holds them all, else as many as it holds.
+template <class C>
+int grid_persist(const GemmLaunch& g, const void* kernel) {
+  const int gx = grid_sym<C>(g);
+  if (!kPersistSym<C>) return gx;
+  const int cap = resident_grid(kernel, C::NT);
+  return cap >= 8 && cap < gx ? cap : gx;
+}
+
 template <class C>
 int grid_full(const GemmLaunch& g) {
   int mx = 0;
@@ -2720,6 +2818,7 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
     // symmetric problems read both operands the same way; columns on the
     // split path, for the statistics only
     if ((g.p[i].p_cols != 0) != (g.p[i].q_cols != 0)) return hipErrorInvalidValue;
+    if (g.p[i].M != g.p[i].N) return hipErrorInvalidValue;  // square results only
     if (g.p[i].p_cols != 0 && (mode == kGemmF32 || newton)) return hipErrorInvalidValue;
     ncols += g.p[i].p_cols != 0;
   }
@@ -2743,23 +2842,27 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
   }
   if (nterms != 0 && nterms != g.n_problems) return hipErrorInvalidValue;
   switch (tile) {
+#define SHP_SYM_KERNEL(KERNEL, CFG)                                                            \
+  hipLaunchKernelGGL(KERNEL, dim3(grid_persist<CFG>(g, reinterpret_cast<const void*>(KERNEL)),  \
+                                  g.n_problems),                                               \
+                     dim3(CFG::NT), 0, s, g);
+#define SHP_SYM_PLAIN(KERNEL, CFG)                                                             \
+  hipLaunchKernelGGL(KERNEL, dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g);
 #define SHP_SYM_LAUNCH(CFG, PATH)                                                              \
   if (nterms)                                                                                  \
-    hipLaunchKernelGGL((cheb_sym_kernel<CFG, PATH>), dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g); \
+    SHP_SYM_PLAIN((cheb_sym_kernel<CFG, PATH>), CFG)                                           \
   else if (newton)                                                                             \
-    hipLaunchKernelGGL((newton_sym_kernel<CFG, PATH>), dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g); \
+    SHP_SYM_KERNEL((newton_sym_kernel<CFG, PATH>), CFG)                                        \
   else                                                                                         \
-    hipLaunchKernelGGL((syrk_ema_kernel<CFG, PATH>), dim3(gx, g.n_problems), dim3(CFG::NT), 0, s, g);
+    SHP_SYM_PLAIN((syrk_ema_kernel<CFG, PATH>), CFG)
 #define SHP_SYM_CASE(T, CFG)                                                                   \
   case T: {                                                                                    \
     const int gx = grid_sym<CFG>(g);                                                           \
     if (!gx) break;                                                                            \
     if (cols && mode == kGemmSplitF16) {                                                       \
-      hipLaunchKernelGGL((syrk_ema_kernel<CFG, kPathSplitHCols>), dim3(gx, g.n_problems),     \
-                         dim3(CFG::NT), 0, s, g);                                              \
+      SHP_SYM_PLAIN((syrk_ema_kernel<CFG, kPathSplitHCols>), CFG)                              \
     } else if (cols) {                                                                         \
-      hipLaunchKernelGGL((syrk_ema_kernel<CFG, kPathSplitCols>), dim3(gx, g.n_problems),      \
-                         dim3(CFG::NT), 0, s, g);                                              \
+      SHP_SYM_PLAIN((syrk_ema_kernel<CFG, kPathSplitCols>), CFG)                               \
     } else if (mode == kGemmSplitF16) {                                                        \
       SHP_SYM_LAUNCH(CFG, kPathSplitH)                                                         \
     } else if (mode == kGemmSplit) {                                                           \
@@ -2774,11 +2877,11 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
       if (mode != kGemmSplitF16) return hipErrorInvalidValue;
       const int gx = grid_sym<Cfg256>(g);
       if (!gx) break;
-      if (cols)
-        hipLaunchKernelGGL((syrk_ema_kernel<Cfg256, kPathSplitHCols>), dim3(gx, g.n_problems),
-                           dim3(Cfg256::NT), 0, s, g);
-      else
+      if (cols) {
+        SHP_SYM_PLAIN((syrk_ema_kernel<Cfg256, kPathSplitHCols>), Cfg256)
+      } else {
         SHP_SYM_LAUNCH(Cfg256, kPathSplitH)
+      }
       break;
     }
     SHP_SYM_CASE(128, Cfg128)
@@ -2786,6 +2889,8 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
     SHP_SYM_CASE(32, Cfg32)
 #undef SHP_SYM_CASE
 #undef SHP_SYM_LAUNCH
+#undef SHP_SYM_KERNEL
+#undef SHP_SYM_PLAIN
     default:
       return hipErrorInvalidValue;
   }
