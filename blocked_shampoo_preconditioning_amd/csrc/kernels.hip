@@ -1059,7 +1059,7 @@ __device__ __forceinline__ void sym_mainloop(const GemmProblem& pb, int f, int m
 // element instead of 64-bit index arithmetic.
 // Adds this lane's share of ||C - I||_F^2 to rs and of max |C| to mx, in the
 // order of the elements.
-template <class C, int PATH, bool TERMS>
+template <class C, int PATH, bool TERMS, bool AFF2 = true>
 __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN],
                                              const SymWave<C>& sw, bool diag, float* lds, int m0,
                                              int n0, int N,
@@ -1067,9 +1067,18 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
                                              const float* E1b, const float* E2b, float e_alpha,
                                              float e_beta, float e_beta2, float e_gamma,
                                              float e_t1, float e_t2, float& rs, float& mx) {
-  constexpr bool BATCH = PATH == kPathSplit || PATH == kPathSplitH;
+  // AFF2: the second affine term may be present (the Chebyshev products'
+  // Clenshaw term). The statistics have only the EMA term; where the split
+  // rows paths do not already load two whole fragments per round trip, the
+  // registers of the second term let one whole fragment load per round trip
+  // (a wait for a load also waits for every store before it, so fewer round
+  // trips mean fewer waits on the stores: R statistics -5%, bf16 statistics
+  // -3% per launch on the 1B set; on the rows path dropping the second term
+  // changed its register allocation and cost 4%, so it keeps it).
+  constexpr bool WIDE = PATH == kPathSplit || PATH == kPathSplitH;
+  constexpr bool BATCH = WIDE || !AFF2;
   constexpr int NF = C::FM * C::FN;
-  constexpr int GF = BATCH && NF >= 2 ? 2 : 1;  // fragments per batch
+  constexpr int GF = WIDE && NF >= 2 ? 2 : 1;  // fragments per batch
   constexpr int HOIST = BATCH ? 16 : 4;
   // Off-diagonal mirrors pass through a wave-private 32 x 32 transpose buffer
   // (rows of kTP floats: the 16-byte writes of 16 lanes cover the 64 banks
@@ -1100,7 +1109,7 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
         for (int r = 0; r < 16; ++r) {
           const uint32_t o = (uint32_t)(frag_row_w<C>(m0, sw.wm, i, r) * N + col);
           dv[q][r] = Db != nullptr ? Db[o] : 0.f;
-          d2v[q][r] = D2b != nullptr ? D2b[o] : 0.f;
+          d2v[q][r] = AFF2 && D2b != nullptr ? D2b[o] : 0.f;
           if constexpr (TERMS)
             ev[q][r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) + (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
         }
@@ -1123,7 +1132,7 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
               for (int r = 0; r < HOIST; ++r) {
                 const uint32_t o = (uint32_t)(frag_row_w<C>(m0, sw.wm, i, 4 * g4 + r) * N + col);
                 dv[q][r] = Db != nullptr ? Db[o] : 0.f;
-                d2v[q][r] = D2b != nullptr ? D2b[o] : 0.f;
+                d2v[q][r] = AFF2 && D2b != nullptr ? D2b[o] : 0.f;
                 if constexpr (TERMS)
                   ev[q][r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) +
                              (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
@@ -1164,7 +1173,7 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
             for (int r = 0; r < HOIST; ++r) {
               const uint32_t o = (uint32_t)(frag_row_w<C>(m0, sw.wm, i, 4 * g4 + r) * N + col);
               dv[q][r] = Db != nullptr ? Db[o] : 0.f;
-              d2v[q][r] = D2b != nullptr ? D2b[o] : 0.f;
+              d2v[q][r] = AFF2 && D2b != nullptr ? D2b[o] : 0.f;
               if constexpr (TERMS)
                 ev[q][r] = (E1b != nullptr ? e_t1 * E1b[o] : 0.f) +
                            (E2b != nullptr ? e_t2 * E2b[o] : 0.f);
@@ -1203,7 +1212,7 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
 }
 
 // One tile (ti <= tj) of a symmetric product for factor f.
-template <class C, int PATH, bool TERMS>
+template <class C, int PATH, bool TERMS, bool AFF2>
 __device__ __forceinline__ void sym_tile(const GemmProblem& pb, int f, int tile, int T, float* lds,
                                          float* red) {
   int t = tile, ti = 0;
@@ -1240,8 +1249,8 @@ __device__ __forceinline__ void sym_tile(const GemmProblem& pb, int f, int tile,
   const int N = pb.N;
   float rs = 0.f;
   float mx = 0.f;  // largest |value| stored (fp16 split: the result's maximum)
-  sym_epilogue<C, PATH, TERMS>(acc, sw, diag, lds, m0, n0, N, Cb, Db, D2b, E1b, E2b, e_alpha,
-                               e_beta, e_beta2, e_gamma, e_t1, e_t2, rs, mx);
+  sym_epilogue<C, PATH, TERMS, AFF2>(acc, sw, diag, lds, m0, n0, N, Cb, Db, D2b, E1b, E2b,
+                                     e_alpha, e_beta, e_beta2, e_gamma, e_t1, e_t2, rs, mx);
   if constexpr (path_f16(PATH))
     if (pb.mC != nullptr) raise_max(pb.mC + f, mx, pb.ver);
   if (pb.resid != nullptr) {
@@ -1282,7 +1291,8 @@ constexpr bool kPersistSym = C::NT == 512;
 // many workgroups as the device runs at once, each taking every (gridDim.x /
 // 8)-th unit of its XCD, so a launch whose factors have all stopped costs one
 // status read per factor instead of the dispatch of every tile.
-template <class C, int PATH = kPathF32, bool TERMS = false, bool PERSIST = false>
+// AFF2 = false (the statistics): no second affine term.
+template <class C, int PATH = kPathF32, bool TERMS = false, bool PERSIST = false, bool AFF2 = true>
 __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   __shared__ float lds[lds_floats<C, PATH>()];
   float* red = lds;  // residual partials reuse the operand tiles after the K loop
@@ -1300,7 +1310,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
       const int st = pb.status[pb.f0 + f];
       if (st != 0 && !(pb.also_status != 0 && st == pb.also_status)) return;
     }
-    sym_tile<C, PATH, TERMS>(pb, f, tile, T, lds, red);
+    sym_tile<C, PATH, TERMS, AFF2>(pb, f, tile, T, lds, red);
   } else {
     // live-factor table, one byte per slot of this XCD; problems with more
     // slots read the status words per tile instead
@@ -1331,7 +1341,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
       }
       // the previous tile's last LDS uses (transpose buffers, partials) end here
       __syncthreads();
-      sym_tile<C, PATH, TERMS>(pb, f, tile, T, lds, red);
+      sym_tile<C, PATH, TERMS, AFF2>(pb, f, tile, T, lds, red);
     }
   }
 }
@@ -1341,14 +1351,14 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
 // GpT for R).
 template <class C, int PATH>
 __global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void syrk_ema_kernel(GemmLaunch g) {
-  sym_product<C, PATH>(g);
+  sym_product<C, PATH, false, false, PATH == kPathSplit || PATH == kPathSplitH>(g);
 }
 
 // Statistics from bf16 packed gradients: L <- beta2 L + g Gp Gp^T reads GpH
 // (rows of Gp), R <- beta2 R + g Gp^T Gp reads GpTH (rows of Gp^T).
 template <class C>
 __global__ __launch_bounds__(C::NT, C::NT == 512 ? 2 : 3) void syrk_bf16_kernel(GemmLaunch g) {
-  sym_product<C, kPathBF16>(g);
+  sym_product<C, kPathBF16, false, false, false>(g);
 }
 
 // One product of the coupled Newton chain (T T, X T, T2 T2 or T4 M); every
