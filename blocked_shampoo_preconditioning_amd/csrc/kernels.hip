@@ -1048,6 +1048,24 @@ __device__ __forceinline__ void sym_mainloop(const GemmProblem& pb, int f, int m
   }
 }
 
+// The affine terms D of fragments q0 .. q0 + GF - 1 of a wave's block (zero
+// for masked fragments, or without D).
+template <class C, int GF>
+__device__ __forceinline__ void sym_load_terms(float (&d)[GF][16], int q0, const SymWave<C>& sw,
+                                               int m0, int n0, int N, const float* Db) {
+#pragma unroll
+  for (int q = 0; q < GF; ++q) {
+    const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
+    if (!((sw.mask >> (i * C::FN + j)) & 1)) continue;  // wave-uniform
+    const int col = frag_col_w<C>(n0, sw.wn, j);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t o = (uint32_t)(frag_row_w<C>(m0, sw.wm, i, r) * N + col);
+      d[q][r] = Db != nullptr ? Db[o] : 0.f;
+    }
+  }
+}
+
 // The symmetric epilogue over a wave's fragments (see sym_product): C =
 // alpha acc + beta D + beta2 D2 (+ the Chebyshev terms) + gamma I on and
 // above the diagonal and the mirror below it. diag: the tile holds the
@@ -1080,6 +1098,13 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
   constexpr int NF = C::FM * C::FN;
   constexpr int GF = WIDE && NF >= 2 ? 2 : 1;  // fragments per batch
   constexpr int HOIST = BATCH ? 16 : 4;
+  // PIPE (split rows paths with the EMA or Newton term only): the terms of
+  // the next batch are loaded before this batch's stores, so the wait for
+  // them does not cover those stores; one batch of terms in flight while
+  // another is consumed takes the registers of the second term.
+  constexpr bool PIPE = WIDE && !AFF2 && !TERMS;
+  float nxt[GF][16];
+  if constexpr (PIPE) sym_load_terms<C, GF>(nxt, 0, sw, m0, n0, N, Db);
   // Off-diagonal mirrors pass through a wave-private 32 x 32 transpose buffer
   // (rows of kTP floats: the 16-byte writes of 16 lanes cover the 64 banks
   // once) and leave as whole 128-byte row segments instead of 16 bytes in
@@ -1099,7 +1124,16 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
 #pragma unroll
   for (int q0 = 0; q0 < NF; q0 += GF) {
     float dv[GF][HOIST], d2v[GF][HOIST], ev[GF][TERMS ? HOIST : 1];
-    if constexpr (BATCH) {
+    if constexpr (PIPE) {
+#pragma unroll
+      for (int q = 0; q < GF; ++q)
+#pragma unroll
+        for (int r = 0; r < HOIST; ++r) {
+          dv[q][r] = nxt[q][r];
+          d2v[q][r] = 0.f;
+        }
+      if (q0 + GF < NF) sym_load_terms<C, GF>(nxt, q0 + GF, sw, m0, n0, N, Db);
+    } else if constexpr (BATCH) {
 #pragma unroll
       for (int q = 0; q < GF; ++q) {
         const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
@@ -1365,12 +1399,19 @@ __global__ __launch_bounds__(C::NT, C::NT == 512 ? 2 : 3) void syrk_bf16_kernel(
 // operand is symmetric, so P and Q serve as row operands as they are.
 template <class C, int PATH>
 __global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void newton_sym_kernel(GemmLaunch g) {
-  sym_product<C, PATH, false, kPersistSym<C>>(g);
+  sym_product<C, PATH, false, kPersistSym<C>, false>(g);
 }
 
 // The product's main loop on either path: fp32 (C = P^T Q, P [K][M] and
 // Q [K][N]) or split (C = A B^T with A = P [M][K], or with PCOLS P = A^T
 // [K][M]; B = Q [N][K], or with QCOLS Q = B^T [K][N]).
+// Root products with a second affine term (the Chebyshev recurrence's
+// B_(k+2)), one tile per workgroup.
+template <class C, int PATH>
+__global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void sym_d2_kernel(GemmLaunch g) {
+  sym_product<C, PATH>(g);
+}
+
 template <class C, int PATH, bool PCOLS, bool QCOLS>
 __device__ __forceinline__ void full_mainloop(const GemmProblem& pb, int f, int m0, int n0,
                                               floatx16 (&acc)[C::FM][C::FN], float* lds) {
@@ -2851,6 +2892,11 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
     nterms += t;
   }
   if (nterms != 0 && nterms != g.n_problems) return hipErrorInvalidValue;
+  // a second affine term: root products only (the Newton kernel is compiled
+  // without it; such launches take their own kernel)
+  int nd2 = 0;
+  for (int i = 0; i < g.n_problems; ++i) nd2 += g.p[i].D2 != nullptr;
+  if (nd2 != 0 && !newton) return hipErrorInvalidValue;
   switch (tile) {
 #define SHP_SYM_KERNEL(KERNEL, CFG)                                                            \
   hipLaunchKernelGGL(KERNEL, dim3(grid_persist<CFG>(g, reinterpret_cast<const void*>(KERNEL)),  \
@@ -2861,6 +2907,8 @@ hipError_t launch_gemm_sym(const GemmLaunch& g, int tile, bool newton, int mode,
 #define SHP_SYM_LAUNCH(CFG, PATH)                                                              \
   if (nterms)                                                                                  \
     SHP_SYM_PLAIN((cheb_sym_kernel<CFG, PATH>), CFG)                                           \
+  else if (newton && nd2)                                                                      \
+    SHP_SYM_PLAIN((sym_d2_kernel<CFG, PATH>), CFG)                                             \
   else if (newton)                                                                             \
     SHP_SYM_KERNEL((newton_sym_kernel<CFG, PATH>), CFG)                                        \
   else                                                                                         \
