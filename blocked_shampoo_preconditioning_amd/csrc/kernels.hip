@@ -1098,11 +1098,14 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
   constexpr int NF = C::FM * C::FN;
   constexpr int GF = WIDE && NF >= 2 ? 2 : 1;  // fragments per batch
   constexpr int HOIST = BATCH ? 16 : 4;
-  // PIPE (split rows paths with the EMA or Newton term only): the terms of
-  // the next batch are loaded before this batch's stores, so the wait for
-  // them does not cover those stores; one batch of terms in flight while
-  // another is consumed takes the registers of the second term.
-  constexpr bool PIPE = WIDE && !AFF2 && !TERMS;
+  // PIPE (whole-fragment batches with the EMA or Newton term only): the
+  // terms of the next batch are loaded before this batch's stores, so the
+  // wait for them does not cover those stores; one batch of terms in flight
+  // while another is consumed takes the registers of the second term (bf16
+  // statistics 5.75 -> 4.79 ms and statistics of columns 5.25 -> 5.15 ms per
+  // launch on the 1B sets; two fragments per batch with the bf16 statistics:
+  // 5.17).
+  constexpr bool PIPE = BATCH && !AFF2 && !TERMS;
   float nxt[GF][16];
   if constexpr (PIPE) sym_load_terms<C, GF>(nxt, 0, sw, m0, n0, N, Db);
   // Off-diagonal mirrors pass through a wave-private 32 x 32 transpose buffer
