@@ -1661,42 +1661,55 @@ __global__ __launch_bounds__(256) void pack_kernel(const BlockMeta* __restrict__
   // 4-element vector loads need ld % 4 == 0 and a 4-element-aligned base
   const bool vec = (mm.ld & 3) == 0 &&
                    (reinterpret_cast<uintptr_t>(mm.grad) & (bf16 ? 7u : 15u)) == 0;
+  // All four rows' loads (gradient, momentum) are issued before the first
+  // store: the compiler cannot tell the gradient from the outputs, so loads
+  // written after a store stay behind it, and a wait for them would also wait
+  // for the stores before them.
+  float4 v[4], mv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = tid / 16 + 16 * i;
     const int c = (tid % 16) * 4;
     const int pr = rr0 + row, pc = cc0 + c;  // position inside the packed block
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (pr < bm.m && pc < bm.n) {
       const int64_t off = (int64_t)(bm.r0 + pr) * mm.ld + bm.c0 + pc;
       if (vec && pc + 3 < bm.n) {
-        v = load4(mm.grad, off, bf16);
+        v[i] = load4(mm.grad, off, bf16);
       } else {
-        v.x = load1(mm.grad, off, bf16);
-        if (pc + 1 < bm.n) v.y = load1(mm.grad, off + 1, bf16);
-        if (pc + 2 < bm.n) v.z = load1(mm.grad, off + 2, bf16);
-        if (pc + 3 < bm.n) v.w = load1(mm.grad, off + 3, bf16);
+        v[i].x = load1(mm.grad, off, bf16);
+        if (pc + 1 < bm.n) v[i].y = load1(mm.grad, off + 1, bf16);
+        if (pc + 2 < bm.n) v[i].z = load1(mm.grad, off + 2, bf16);
+        if (pc + 3 < bm.n) v[i].w = load1(mm.grad, off + 3, bf16);
       }
     }
+    if (Mom != nullptr && pr < br && pc < bc)
+      mv[i] = *reinterpret_cast<const float4*>(Mom + ((size_t)b * br + pr) * bc + pc);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = tid / 16 + 16 * i;
+    const int c = (tid % 16) * 4;
+    const int pr = rr0 + row, pc = cc0 + c;
     if (pr < br && pc < bc) {
       const size_t o = ((size_t)b * br + pr) * bc + pc;
-      *reinterpret_cast<float4*>(Gp + o) = v;
-      mg = fmaxf(mg, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-      if (GpH != nullptr) *reinterpret_cast<uint2*>(GpH + o) = bf16_bits4(v);
+      *reinterpret_cast<float4*>(Gp + o) = v[i];
+      mg = fmaxf(mg, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+      if (GpH != nullptr) *reinterpret_cast<uint2*>(GpH + o) = bf16_bits4(v[i]);
       if (Mom != nullptr) {  // momentum folded in before preconditioning
-        float4 m = *reinterpret_cast<const float4*>(Mom + o);
-        m.x = momentum * m.x + v.x;
-        m.y = momentum * m.y + v.y;
-        m.z = momentum * m.z + v.z;
-        m.w = momentum * m.w + v.w;
+        float4 m = mv[i];
+        m.x = momentum * m.x + v[i].x;
+        m.y = momentum * m.y + v[i].y;
+        m.z = momentum * m.z + v[i].z;
+        m.w = momentum * m.w + v[i].w;
         *reinterpret_cast<float4*>(Mom + o) = m;
         mmom = fmaxf(mmom, fmaxf(fmaxf(fabsf(m.x), fabsf(m.y)), fmaxf(fabsf(m.z), fabsf(m.w))));
       }
     }
-    tile[row][c] = v.x;
-    tile[row][c + 1] = v.y;
-    tile[row][c + 2] = v.z;
-    tile[row][c + 3] = v.w;
+    tile[row][c] = v[i].x;
+    tile[row][c + 1] = v[i].y;
+    tile[row][c + 2] = v[i].z;
+    tile[row][c + 3] = v[i].w;
   }
   // one atomic per workgroup and word (a block's 64 x 64 tiles are many
   // workgroups raising the same word)
@@ -2213,24 +2226,37 @@ __global__ __launch_bounds__(256) void newton_init_kernel(const float* __restric
   const int nr = fs.nreal[f];
   const float s = c.scale[f], cf = c.cfac[f];
   const float ip = 1.f / (float)c.p, ip1 = (float)(c.p + 1) / (float)c.p;
-  // four consecutive elements of one row per step (sides are multiples of 32)
+  // four consecutive elements of one row per step (sides are multiples of
+  // 32); four steps' loads are issued before their stores (a load written
+  // after a store stays behind it, and the wait for it would cover the store)
   const int nn4 = n * n / 4;
-  for (int e4 = blockIdx.x * blockDim.x + threadIdx.x; e4 < nn4; e4 += gridDim.x * blockDim.x) {
-    const int e = 4 * e4, r = e / n, col = e - r * n;
-    const float4 a = *reinterpret_cast<const float4*>(Af + e);
-    const float av[4] = {a.x, a.y, a.z, a.w};
-    float m[4], x[4];
+  const int stride = gridDim.x * blockDim.x;
+  for (int e0 = blockIdx.x * blockDim.x + threadIdx.x; e0 < nn4; e0 += 4 * stride) {
+    float4 a4[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float id = (r == col + k) ? 1.f : 0.f;
-      m[k] = (r < nr && col + k < nr) ? av[k] / s : id;
-      mm = fmaxf(mm, fabsf(m[k]));
-      x[k] = c.solver == kNewtonDB ? id : cf * (ip1 * id - ip * m[k]);
+    for (int u = 0; u < 4; ++u) {
+      const int e4 = e0 + u * stride;
+      if (e4 < nn4) a4[u] = *reinterpret_cast<const float4*>(Af + 4 * e4);
     }
-    *reinterpret_cast<float4*>(M0 + base + e) = make_float4(m[0], m[1], m[2], m[3]);
-    if (c.solver != kChebyshev) {
-      *reinterpret_cast<float4*>(X1 + base + e) = make_float4(x[0], x[1], x[2], x[3]);
-      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e4 = e0 + u * stride;
+      if (e4 >= nn4) break;
+      const int e = 4 * e4, r = e / n, col = e - r * n;
+      const float av[4] = {a4[u].x, a4[u].y, a4[u].z, a4[u].w};
+      float m[4], x[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float id = (r == col + k) ? 1.f : 0.f;
+        m[k] = (r < nr && col + k < nr) ? av[k] / s : id;
+        mm = fmaxf(mm, fabsf(m[k]));
+        x[k] = c.solver == kNewtonDB ? id : cf * (ip1 * id - ip * m[k]);
+      }
+      *reinterpret_cast<float4*>(M0 + base + e) = make_float4(m[0], m[1], m[2], m[3]);
+      if (c.solver != kChebyshev) {
+        *reinterpret_cast<float4*>(X1 + base + e) = make_float4(x[0], x[1], x[2], x[3]);
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+      }
     }
   }
   if (mo.a != nullptr || mo.b != nullptr)
@@ -2361,28 +2387,44 @@ __global__ __launch_bounds__(256) void newton_final_kernel(float* __restrict__ X
   const float* xf = factor_ptr(Xroot, fs, f, n);
   const int64_t base = xf - Xroot;
   const float cf = c.cfac[f];
-  // four consecutive elements of one row per step (sides are multiples of 32)
+  // four consecutive elements of one row per step (sides are multiples of
+  // 32); four steps' loads are issued before their stores (a load written
+  // after a store stays behind it, and the wait for it would cover the store)
   const int nn4 = n * n / 4;
+  const int stride = gridDim.x * blockDim.x;
+  const bool copy = !dead && (scale || k > 0);
+  const float* src = (scale && !odd ? Xroot : Xalt) + base;
   float mx = 0.f;
-  for (int e4 = blockIdx.x * blockDim.x + threadIdx.x; e4 < nn4; e4 += gridDim.x * blockDim.x) {
-    const int e = 4 * e4, r = e / n, col = e - r * n;
-    float4 x;
-    if (dead) {
-      x = make_float4(0.f, 0.f, 0.f, 0.f);
-    } else if (scale || k > 0) {
-      x = *reinterpret_cast<const float4*>((scale && !odd ? Xroot : Xalt) + base + e);
-      if (scale) {
-        x.x *= cf;
-        x.y *= cf;
-        x.z *= cf;
-        x.w *= cf;
-      }
-    } else {  // X_0 = s^(-1/p) I
-      x = make_float4(r == col ? cf : 0.f, r == col + 1 ? cf : 0.f, r == col + 2 ? cf : 0.f,
-                      r == col + 3 ? cf : 0.f);
+  for (int e0 = blockIdx.x * blockDim.x + threadIdx.x; e0 < nn4; e0 += 4 * stride) {
+    float4 x4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e4 = e0 + u * stride;
+      if (copy && e4 < nn4) x4[u] = *reinterpret_cast<const float4*>(src + 4 * e4);
     }
-    *reinterpret_cast<float4*>(Xroot + base + e) = x;
-    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e4 = e0 + u * stride;
+      if (e4 >= nn4) break;
+      const int e = 4 * e4, r = e / n, col = e - r * n;
+      float4 x;
+      if (dead) {
+        x = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else if (copy) {
+        x = x4[u];
+        if (scale) {
+          x.x *= cf;
+          x.y *= cf;
+          x.z *= cf;
+          x.w *= cf;
+        }
+      } else {  // X_0 = s^(-1/p) I
+        x = make_float4(r == col ? cf : 0.f, r == col + 1 ? cf : 0.f, r == col + 2 ? cf : 0.f,
+                        r == col + 3 ? cf : 0.f);
+      }
+      *reinterpret_cast<float4*>(Xroot + base + e) = x;
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+    }
   }
   if (mo.a != nullptr) raise_max(mo.a + f, mx, mo.ver);
 }
