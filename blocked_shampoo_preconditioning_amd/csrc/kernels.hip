@@ -1497,41 +1497,52 @@ __device__ __forceinline__ void update_batched(const floatx16 (&acc)[C::FM][C::F
   typedef typename std::conditional<BF16, uint16_t, float>::type P;
   P* w = reinterpret_cast<P*>(mm.param) + (size_t)bm.r0 * mm.ld + bm.c0;
   constexpr int NF = C::FM * C::FN;
-  constexpr int G = NF > 2 ? 2 : NF;  // fragments per batch (32 registers)
+  const int lane = threadIdx.x & 63;
+  const int wm = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % C::WM);
+  const int wn = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) / C::WM);
+  const int ld = (int)mm.ld;  // <= 2^26 (checked at init): 31 ld + col fits in 32 bits
+  // The parameters of the next fragment are loaded before this fragment's
+  // stores (the stores may alias them as far as the compiler knows, so loads
+  // written after a store stay behind it, and the wait for them would cover
+  // the stores before them). Each fragment's rows start at a pointer common
+  // to the wave and its elements sit at 32-bit offsets under 32 rows, so the
+  // two fragments in flight hold no 64-bit addresses per element.
+  float wv[2][16];
 #pragma unroll
-  for (int q0 = 0; q0 < NF; q0 += G) {
-    float wv[G][16];
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-      const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
-      const int col = frag_col<C>(n0, j);
+  for (int q = 0; q <= NF; ++q) {
+    if (q < NF) {
+      const int i = q / C::FN, j = q % C::FN;
+      const int r0 = m0 + wm * 32 * C::FM + i * 32;  // the fragment's first row (uniform)
+      const int col = n0 + wn * 32 * C::FN + j * 32 + (lane & 31);
+      const P* wf = w + (size_t)r0 * ld;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = frag_row<C>(m0, i, r);
+        const int rl = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         float v = 0.f;
-        if (col < bm.n && row < bm.m) {
-          const P x = w[(size_t)row * mm.ld + col];
+        if (col < bm.n && r0 + rl < bm.m) {
+          const P x = wf[(uint32_t)(rl * ld + col)];
           if constexpr (BF16)
             v = bf16_to_f32(x);
           else
             v = x;
         }
-        wv[q][r] = v;
+        wv[q & 1][r] = v;
       }
     }
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-      const int i = (q0 + q) / C::FN, j = (q0 + q) % C::FN;
-      const int col = frag_col<C>(n0, j);
+    if (q > 0) {
+      const int i = (q - 1) / C::FN, j = (q - 1) % C::FN;
+      const int r0 = m0 + wm * 32 * C::FM + i * 32;
+      const int col = n0 + wn * 32 * C::FN + j * 32 + (lane & 31);
+      P* wf = w + (size_t)r0 * ld;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = frag_row<C>(m0, i, r);
-        if (col < bm.n && row < bm.m) {
-          const float v = wv[q][r] - lr * acc[i][j][r];
+        const int rl = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (col < bm.n && r0 + rl < bm.m) {
+          const float v = wv[(q - 1) & 1][r] - lr * acc[i][j][r];
           if constexpr (BF16)
-            w[(size_t)row * mm.ld + col] = f32_to_bf16(v);
+            wf[(uint32_t)(rl * ld + col)] = f32_to_bf16(v);
           else
-            w[(size_t)row * mm.ld + col] = v;
+            wf[(uint32_t)(rl * ld + col)] = v;
         }
       }
     }

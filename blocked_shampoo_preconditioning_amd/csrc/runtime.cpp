@@ -91,6 +91,10 @@ int validate_mats(const shampoo_matrix_desc_t* m, int32_t n) {
       return fail(SHAMPOO_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": bad shape");
     if (m[i].ld < m[i].cols || m[i].ld <= 0)
       return fail(SHAMPOO_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": ld < cols");
+    // the parameter update addresses 32 rows of a block from one base with
+    // 32-bit element offsets
+    if (m[i].ld > (int64_t{1} << 26))
+      return fail(SHAMPOO_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": ld > 2^26");
   }
   return SHAMPOO_OK;
 }

@@ -102,8 +102,9 @@ enum {
 };
 
 /* One registered matrix: rows x cols, row-major, leading dimension ld
- * (elements, >= cols). Parameters and gradients of a matrix share this shape
- * and ld. Pointers must be aligned to their element size; 16-byte aligned
+ * (elements, cols <= ld <= 2^26; shampoo_init rejects a larger ld with
+ * SHAMPOO_ERR_INVALID_ARG). Parameters and gradients of a matrix share this
+ * shape and ld. Pointers must be aligned to their element size; 16-byte aligned
  * matrices with ld % 4 == 0 are read with vector loads. */
 typedef struct {
   int64_t rows, cols, ld;

@@ -91,6 +91,8 @@ def test_config_validation(lib, field, value, code):
     ((64, 64), 60, S.SHAMPOO_ERR_INVALID_ARG),
     ((64, 62), 62, S.SHAMPOO_OK),
     ((-1, 4), 4, S.SHAMPOO_ERR_INVALID_ARG),
+    ((64, 64), 1 << 26, S.SHAMPOO_OK),              # the largest leading dimension
+    ((64, 64), (1 << 26) + 1, S.SHAMPOO_ERR_INVALID_ARG),
 ])
 def test_matrix_validation(lib, shape, ld, code):
     c = S.shampoo_config_default()
