@@ -1324,11 +1324,11 @@ constexpr bool kPersistSym = C::NT == 512;
 // when converged factors drop out of a Newton launch, every XCD keeps its
 // share of the remaining ones. Without PERSIST a workgroup takes one unit.
 // PERSIST (the Newton products, whose launches lose factors as they
-// converge): the grid holds at most as many workgroups as the device runs at
-// once, each taking every (gridDim.x / 8)-th unit of its XCD, so a launch
-// whose factors have all stopped costs one status read per factor instead of
-// the dispatch of every tile. AFF2 = false (the statistics, the Newton
-// products): no second affine term.
+// converge): the grid holds at most as
+// many workgroups as the device runs at once, each taking every (gridDim.x /
+// 8)-th unit of its XCD, so a launch whose factors have all stopped costs one
+// status read per factor instead of the dispatch of every tile.
+// AFF2 = false (the statistics): no second affine term.
 template <class C, int PATH = kPathF32, bool TERMS = false, bool PERSIST = false, bool AFF2 = true>
 __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
   __shared__ float lds[lds_floats<C, PATH>()];
