@@ -1086,25 +1086,22 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
                                              float e_beta, float e_beta2, float e_gamma,
                                              float e_t1, float e_t2, float& rs, float& mx) {
   // AFF2: the second affine term may be present (the Chebyshev products'
-  // Clenshaw term). The statistics have only the EMA term; where the split
-  // rows paths do not already load two whole fragments per round trip, the
-  // registers of the second term let one whole fragment load per round trip
-  // (a wait for a load also waits for every store before it, so fewer round
-  // trips mean fewer waits on the stores: R statistics -5%, bf16 statistics
-  // -3% per launch on the 1B set; on the rows path dropping the second term
-  // changed its register allocation and cost 4%, so it keeps it).
+  // Clenshaw term). The statistics (the EMA term) and the Newton products
+  // have one term at most, and its registers let one whole fragment load per
+  // round trip (a wait for a load also waits for every store before it, so
+  // fewer round trips mean fewer waits on the stores).
   constexpr bool WIDE = PATH == kPathSplit || PATH == kPathSplitH;
   constexpr bool BATCH = WIDE || !AFF2;
   constexpr int NF = C::FM * C::FN;
-  constexpr int GF = WIDE && NF >= 2 ? 2 : 1;  // fragments per batch
+  constexpr int GF = WIDE && NF >= 2 && AFF2 ? 2 : 1;  // fragments per batch
   constexpr int HOIST = BATCH ? 16 : 4;
   // PIPE (whole-fragment batches with the EMA or Newton term only): the
-  // terms of the next batch are loaded before this batch's stores, so the
-  // wait for them does not cover those stores; one batch of terms in flight
-  // while another is consumed takes the registers of the second term (bf16
-  // statistics 5.75 -> 4.79 ms and statistics of columns 5.25 -> 5.15 ms per
-  // launch on the 1B sets; two fragments per batch with the bf16 statistics:
-  // 5.17).
+  // terms of the next fragment are loaded before this fragment's stores, so
+  // the wait for them does not cover those stores; one fragment of terms in
+  // flight while another is consumed takes the registers of the second term
+  // (per launch on the 1B sets: bf16 statistics 5.75 -> 4.79 ms, statistics
+  // of columns 5.25 -> 5.15, of rows 4.52 -> 4.41; two fragments per batch
+  // measured slower, 5.17 for the bf16 statistics).
   constexpr bool PIPE = BATCH && !AFF2 && !TERMS;
   float nxt[GF][16];
   if constexpr (PIPE) sym_load_terms<C, GF>(nxt, 0, sw, m0, n0, N, Db);
@@ -1388,7 +1385,7 @@ __device__ __forceinline__ void sym_product(const GemmLaunch& g) {
 // GpT for R).
 template <class C, int PATH>
 __global__ __launch_bounds__(C::NT, path_split(PATH) ? 2 : 4) void syrk_ema_kernel(GemmLaunch g) {
-  sym_product<C, PATH, false, false, PATH == kPathSplit || PATH == kPathSplitH>(g);
+  sym_product<C, PATH, false, false, false>(g);
 }
 
 // Statistics from bf16 packed gradients: L <- beta2 L + g Gp Gp^T reads GpH
