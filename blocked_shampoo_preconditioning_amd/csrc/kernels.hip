@@ -1117,10 +1117,11 @@ __device__ __forceinline__ void sym_epilogue(const floatx16 (&acc)[C::FM][C::FN]
   // The affine terms are loaded before their stores: the stores may alias
   // them as far as the compiler knows (the statistics update in place), which
   // would otherwise hold every load behind the store before it. No store
-  // below targets an element another lane reads here. The split paths with
-  // row operands have the registers for two whole fragments per batch (one
-  // memory round trip per two fragments); the others load HOIST registers of
-  // one fragment at a time.
+  // below targets an element another lane reads here. With one term at most
+  // (PIPE) a whole fragment's terms load per round trip, the next fragment's
+  // before this one's stores; with two, the split rows paths load two whole
+  // fragments per batch and the others HOIST registers of one fragment at a
+  // time.
 #pragma unroll
   for (int q0 = 0; q0 < NF; q0 += GF) {
     float dv[GF][HOIST], d2v[GF][HOIST], ev[GF][TERMS ? HOIST : 1];
