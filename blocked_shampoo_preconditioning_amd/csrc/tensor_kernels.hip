@@ -119,31 +119,52 @@ __global__ __launch_bounds__(256) void tensor_pack_kernel(const TBlockMeta* __re
   const void* grad = tensors[bm.tensor].grad;
   if ((g.E & 3) == 0) {
     // four consecutive elements a thread: one index decomposition, 16-byte
-    // stores of the packed block (and momentum)
-    for (int e = (blockIdx.x * 256 + threadIdx.x) * 4; e < g.E; e += gridDim.x * 256 * 4) {
-      int idx[K];
-      geo.indices(e, idx);
-      float v[4];
+    // stores of the packed block (and momentum). Four grid-stride steps'
+    // loads are issued before their stores: a load written after a store
+    // stays behind it, and the wait for it would cover the store.
+    const int stride = gridDim.x * 256 * 4;
+    for (int e0 = (blockIdx.x * 256 + threadIdx.x) * 4; e0 < g.E; e0 += 4 * stride) {
+      float v[4][4], mv[4][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int64_t off;
-        v[q] = 0.f;
-        if (geo.at(idx, off))
-          v[q] = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(grad)[off])
-                      : reinterpret_cast<const float*>(grad)[off];
-        if (q < 3) geo.step(idx);
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * stride;
+        if (e >= g.E) break;
+        int idx[K];
+        geo.indices(e, idx);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int64_t off;
+          v[u][q] = 0.f;
+          if (geo.at(idx, off))
+            v[u][q] = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(grad)[off])
+                           : reinterpret_cast<const float*>(grad)[off];
+          if (q < 3) geo.step(idx);
+        }
+        if (Mom != nullptr) {
+          const float4 m = *reinterpret_cast<const float4*>(Mom + (size_t)b * g.E + e);
+          mv[u][0] = m.x;
+          mv[u][1] = m.y;
+          mv[u][2] = m.z;
+          mv[u][3] = m.w;
+        }
       }
-      const size_t o = (size_t)b * g.E + e;
-      *reinterpret_cast<float4*>(Gp + o) = make_float4(v[0], v[1], v[2], v[3]);
-      mg = fmaxf(mg, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-      if (Mom != nullptr) {
-        float4 m = *reinterpret_cast<const float4*>(Mom + o);
-        m.x = momentum * m.x + v[0];
-        m.y = momentum * m.y + v[1];
-        m.z = momentum * m.z + v[2];
-        m.w = momentum * m.w + v[3];
-        *reinterpret_cast<float4*>(Mom + o) = m;
-        mm = fmaxf(mm, fmaxf(fmaxf(fabsf(m.x), fabsf(m.y)), fmaxf(fabsf(m.z), fabsf(m.w))));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * stride;
+        if (e >= g.E) break;
+        const size_t o = (size_t)b * g.E + e;
+        *reinterpret_cast<float4*>(Gp + o) = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+        mg = fmaxf(mg, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])),
+                             fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+        if (Mom != nullptr) {
+          float4 m;
+          m.x = momentum * mv[u][0] + v[u][0];
+          m.y = momentum * mv[u][1] + v[u][1];
+          m.z = momentum * mv[u][2] + v[u][2];
+          m.w = momentum * mv[u][3] + v[u][3];
+          *reinterpret_cast<float4*>(Mom + o) = m;
+          mm = fmaxf(mm, fmaxf(fmaxf(fabsf(m.x), fabsf(m.y)), fmaxf(fabsf(m.z), fabsf(m.w))));
+        }
       }
     }
   } else {
@@ -460,17 +481,24 @@ __global__ __launch_bounds__(256) void mode_product_update_kernel(
   const int64_t st = geo.stride[K - 1];
   const int ext = geo.ext[K - 1];
   void* param = tensors[bm.tensor].param;
+  // every parameter loaded before the first store (a load written after a
+  // store stays behind it, and the wait for it would cover the store)
+  float wv[J];
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) {
+    wv[jj] = 0.f;
+    if (jj < ext)
+      wv[jj] = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(param)[off + jj * st])
+                    : reinterpret_cast<const float*>(param)[off + jj * st];
+  }
 #pragma unroll
   for (int jj = 0; jj < J; ++jj) {
     if (jj >= ext) break;
-    const int64_t o = off + jj * st;
-    if (bf16) {
-      uint16_t* w = reinterpret_cast<uint16_t*>(param) + o;
-      *w = f32_to_bf16(bf16_to_f32(*w) - lr * acc[jj]);
-    } else {
-      float* w = reinterpret_cast<float*>(param) + o;
-      *w = *w - lr * acc[jj];
-    }
+    const float v = wv[jj] - lr * acc[jj];
+    if (bf16)
+      reinterpret_cast<uint16_t*>(param)[off + jj * st] = f32_to_bf16(v);
+    else
+      reinterpret_cast<float*>(param)[off + jj * st] = v;
   }
 }
 
@@ -528,23 +556,33 @@ __global__ __launch_bounds__(256) void mode_product2_update_kernel(
   __syncthreads();
   // The update, element e of the workgroup's 256 N N values per thread step:
   // with the tensor's natural strides consecutive threads reach consecutive
-  // parameters.
+  // parameters. All N N parameters of a thread are loaded before the first
+  // store (a load written after a store stays behind it, and the wait for it
+  // would cover the store).
   const int64_t st2 = geo.stride[K - 2], st3 = geo.stride[K - 1];
   const int ext2 = geo.ext[K - 2], ext3 = geo.ext[K - 1];
   void* param = tensors[bm.tensor].param;
-  for (int e = threadIdx.x; e < 256 * NN; e += 256) {
+  int64_t po[NN];
+  float wv[NN];
+#pragma unroll
+  for (int k = 0; k < NN; ++k) {
+    const int e = threadIdx.x + 256 * k;
     const int rl = e / NN, jj = e - rl * NN, j2 = jj / N, j3 = jj - j2 * N;
     const int64_t o0 = soff[rl];
-    if (o0 < 0 || j2 >= ext2 || j3 >= ext3) continue;
-    const int64_t o = o0 + j2 * st2 + j3 * st3;
-    const float u = su[e];
-    if (bf16) {
-      uint16_t* w = reinterpret_cast<uint16_t*>(param) + o;
-      *w = f32_to_bf16(bf16_to_f32(*w) - lr * u);
-    } else {
-      float* w = reinterpret_cast<float*>(param) + o;
-      *w = *w - lr * u;
-    }
+    po[k] = (o0 < 0 || j2 >= ext2 || j3 >= ext3) ? -1 : o0 + j2 * st2 + j3 * st3;
+    wv[k] = 0.f;
+    if (po[k] >= 0)
+      wv[k] = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(param)[po[k]])
+                   : reinterpret_cast<const float*>(param)[po[k]];
+  }
+#pragma unroll
+  for (int k = 0; k < NN; ++k) {
+    if (po[k] < 0) continue;
+    const float v = wv[k] - lr * su[threadIdx.x + 256 * k];
+    if (bf16)
+      reinterpret_cast<uint16_t*>(param)[po[k]] = f32_to_bf16(v);
+    else
+      reinterpret_cast<float*>(param)[po[k]] = v;
   }
 }
 
